@@ -1,0 +1,197 @@
+"""CPU oracle for the sparse MoE decode layer (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It wraps ``moe_oracle.c`` (plain loops, fp64) through
+ctypes and shares no code with the HIP library; the only thing both sides
+share is the seeded input generator.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_SO = os.path.join(_HERE, "libmoe_oracle.so")
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC"]
+
+_lib = None
+
+
+class OrcDims(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("n_routed", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32), ("top_k", ctypes.c_int32), ("wfmt", ctypes.c_int32)]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (building the checker is not using it)."""
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_SO)
+        for name in ("orc_fp16", "orc_bf16"):
+            getattr(L, name).restype = ctypes.c_double
+            getattr(L, name).argtypes = [ctypes.c_uint16]
+        for name in ("orc_e4m3", "orc_e2m1"):
+            getattr(L, name).restype = ctypes.c_double
+            getattr(L, name).argtypes = [ctypes.c_uint8]
+        L.orc_expert_bytes.restype = ctypes.c_size_t
+        L.orc_expert_bytes.argtypes = [ctypes.POINTER(OrcDims)]
+        L.orc_layer_forward.restype = ctypes.c_int
+        L.orc_stack_forward.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def dims_struct(dims) -> OrcDims:
+    return OrcDims(dims.d_model, dims.d_ff, dims.n_routed, dims.n_shared, dims.top_k, dims.wfmt_code)
+
+
+# --------------------------------------------------------------------------- scalar decoders
+
+def fp16(bits: int) -> float:
+    return lib().orc_fp16(bits)
+
+
+def bf16(bits: int) -> float:
+    return lib().orc_bf16(bits)
+
+
+def e4m3(code: int) -> float:
+    return lib().orc_e4m3(code)
+
+
+def e2m1(code: int) -> float:
+    return lib().orc_e2m1(code)
+
+
+def bf16_array(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp64 through the oracle's decoder."""
+    flat = np.ascontiguousarray(bits, dtype=np.uint16).reshape(-1)
+    table = np.array([lib().orc_bf16(i) for i in range(65536)], dtype=np.float64)
+    return table[flat].reshape(np.shape(bits))
+
+
+def dequant_q4_1_block(block: bytes) -> np.ndarray:
+    buf = np.frombuffer(bytes(block), dtype=np.uint8).copy()
+    out = np.zeros(32, dtype=np.float64)
+    lib().orc_dequant_q4_1_block(_p(buf, ctypes.c_uint8), _p(out, ctypes.c_double))
+    return out
+
+
+def dequant_matrix(wfmt_code: int, blob: np.ndarray, rows: int, k: int, s_t: float = 1.0) -> np.ndarray:
+    buf = np.ascontiguousarray(blob, dtype=np.uint8)
+    out = np.zeros((rows, k), dtype=np.float64)
+    lib().orc_dequant_matrix(ctypes.c_int(wfmt_code), _p(buf, ctypes.c_uint8), ctypes.c_int(rows),
+                             ctypes.c_int(k), ctypes.c_double(s_t), _p(out, ctypes.c_double))
+    return out
+
+
+# --------------------------------------------------------------------------- routing pieces
+
+def softmax(logits: np.ndarray) -> np.ndarray:
+    l = np.ascontiguousarray(logits, dtype=np.float64)
+    p = np.zeros_like(l)
+    lib().orc_softmax(ctypes.c_int(l.size), _p(l, ctypes.c_double), _p(p, ctypes.c_double))
+    return p
+
+
+def sort_experts(logits: np.ndarray) -> np.ndarray:
+    l = np.ascontiguousarray(logits, dtype=np.float64)
+    order = np.zeros(l.size, dtype=np.int32)
+    lib().orc_sort_experts(ctypes.c_int(l.size), _p(l, ctypes.c_double), _p(order, ctypes.c_int32))
+    return order
+
+
+def route(dims, logits: np.ndarray, forced: Optional[np.ndarray] = None):
+    l = np.ascontiguousarray(logits, dtype=np.float64)
+    d = dims_struct(dims)
+    idx = np.zeros(dims.top_k, dtype=np.int32)
+    w = np.zeros(dims.top_k, dtype=np.float64)
+    probs = np.zeros(dims.n_routed, dtype=np.float64)
+    f = None if forced is None else _p(np.ascontiguousarray(forced, dtype=np.int32), ctypes.c_int32)
+    lib().orc_route(ctypes.byref(d), _p(l, ctypes.c_double), f, _p(idx, ctypes.c_int32), _p(w, ctypes.c_double),
+                    _p(probs, ctypes.c_double))
+    return idx, w, probs
+
+
+def rmsnorm(y: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.zeros_like(y)
+    lib().orc_rmsnorm(ctypes.c_int(y.size), _p(y, ctypes.c_double), ctypes.c_double(eps), _p(out, ctypes.c_double))
+    return out
+
+
+# --------------------------------------------------------------------------- layer / stack
+
+def _layer_arrays(layer):
+    wr = np.ascontiguousarray(layer.router.cpu().numpy().view(np.uint16))
+    ex = np.ascontiguousarray(layer.experts.cpu().numpy())
+    ts = None if layer.tensor_scale is None else np.ascontiguousarray(layer.tensor_scale.cpu().numpy(), dtype=np.float32)
+    bias = None if layer.router_bias is None else np.ascontiguousarray(layer.router_bias.cpu().numpy(), dtype=np.float64)
+    return wr, ex, ts, bias
+
+
+def layer_forward(layer, x: np.ndarray, forced: Optional[np.ndarray] = None, dense: bool = False):
+    """Returns (idx [T,k] int32, w [T,k] f64, logits [T,E] f64, y [T,d] f64)."""
+    dims = layer.dims
+    x = np.ascontiguousarray(x, dtype=np.float64).reshape(-1, dims.d_model)
+    T = x.shape[0]
+    wr, ex, ts, bias = _layer_arrays(layer)
+    idx = np.zeros((T, dims.top_k), dtype=np.int32)
+    w = np.zeros((T, dims.top_k), dtype=np.float64)
+    logits = np.zeros((T, dims.n_routed), dtype=np.float64)
+    y = np.zeros((T, dims.d_model), dtype=np.float64)
+    fz = None
+    if forced is not None:
+        fz = np.ascontiguousarray(forced, dtype=np.int32).reshape(T, dims.top_k)
+    d = dims_struct(dims)
+    rc = lib().orc_layer_forward(
+        ctypes.byref(d), ctypes.c_int32(T), _p(x, ctypes.c_double), _p(wr, ctypes.c_uint16),
+        None if bias is None else _p(bias, ctypes.c_double), _p(ex, ctypes.c_uint8),
+        None if ts is None else _p(ts, ctypes.c_float), None if fz is None else _p(fz, ctypes.c_int32),
+        ctypes.c_int32(1 if dense else 0), _p(idx, ctypes.c_int32), _p(w, ctypes.c_double),
+        _p(logits, ctypes.c_double), _p(y, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle rejected dims {dims}")
+    return idx, w, logits, y
+
+
+def stack_forward(layers: Sequence, x0: np.ndarray):
+    """Returns (y_last [T,d], y_trace [L,T,d], idx_trace [L,T,k])."""
+    dims = layers[0].dims
+    x0 = np.ascontiguousarray(x0, dtype=np.float64).reshape(-1, dims.d_model)
+    T, L = x0.shape[0], len(layers)
+    arrs = [_layer_arrays(l) for l in layers]
+    wr_ptrs = (ctypes.POINTER(ctypes.c_uint16) * L)(*[_p(a[0], ctypes.c_uint16) for a in arrs])
+    ex_ptrs = (ctypes.POINTER(ctypes.c_uint8) * L)(*[_p(a[1], ctypes.c_uint8) for a in arrs])
+    ts_ptrs = None
+    if arrs[0][2] is not None:
+        ts_ptrs = (ctypes.POINTER(ctypes.c_float) * L)(*[_p(a[2], ctypes.c_float) for a in arrs])
+    y = np.zeros((T, dims.d_model), dtype=np.float64)
+    y_trace = np.zeros((L, T, dims.d_model), dtype=np.float64)
+    idx_trace = np.zeros((L, T, dims.top_k), dtype=np.int32)
+    d = dims_struct(dims)
+    rc = lib().orc_stack_forward(ctypes.byref(d), ctypes.c_int32(L), ctypes.c_int32(T), _p(x0, ctypes.c_double),
+                                 wr_ptrs, ex_ptrs, ts_ptrs, _p(y, ctypes.c_double), _p(y_trace, ctypes.c_double),
+                                 _p(idx_trace, ctypes.c_int32))
+    if rc != 0:
+        raise ValueError("oracle rejected the stack")
+    return y, y_trace, idx_trace

@@ -1,0 +1,409 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself (format specifications, library routines with their own semantics,
+closed forms of special cases, brute force)."""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+from sparse_moe_decode_route_amd import inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for ln in f:
+            ln = ln.strip()
+            if ln and not ln.startswith("#"):
+                yield ln
+
+
+def _same(a, b):
+    return (math.isnan(a) and math.isnan(b)) or (a == b and math.copysign(1, a) == math.copysign(1, b))
+
+
+# --------------------------------------------------------------------------- scalar formats
+
+def test_fp16_all_codes_match_numpy(orc):
+    codes = np.arange(65536, dtype=np.uint16)
+    ref = codes.view(np.float16).astype(np.float64)
+    got = np.array([orc.fp16(int(c)) for c in codes])
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.all(both_nan | (ref == got))
+    assert np.all(np.signbit(ref[~both_nan]) == np.signbit(got[~both_nan]))
+
+
+def test_bf16_all_codes_match_torch(orc):
+    codes = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    ref = codes.view(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.bf16_array(np.arange(65536, dtype=np.uint16))
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.all(both_nan | (ref == got))
+
+
+def test_e4m3_all_codes_match_torch(orc):
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        assert _same(orc.e4m3(c), float(ref[c])), hex(c)
+
+
+def test_e4m3_spec_points(orc):
+    for ln in _lines("e4m3_points.txt"):
+        code, val = ln.split()
+        assert _same(orc.e4m3(int(code, 16)), float(val)), code
+
+
+def test_e2m1_spec_table(orc):
+    rows = [ln.split() for ln in _lines("e2m1_table.txt")]
+    assert len(rows) == 16
+    for code, val in rows:
+        assert _same(orc.e2m1(int(code)), float(val)), code
+
+
+# --------------------------------------------------------------------------- blocks
+
+def test_q4_1_hand_built_blocks(orc):
+    lines = list(_lines("q4_1_blocks.txt"))
+    assert len(lines) == 8
+    for blk_line, val_line in zip(lines[0::2], lines[1::2]):
+        hexs = "".join(blk_line.split()[1:])
+        blob = bytes.fromhex(hexs)
+        assert len(blob) == 20
+        want = np.array([float(v) for v in val_line.split()[1:]])
+        got = orc.dequant_q4_1_block(blob)
+        np.testing.assert_array_equal(got, want)
+        # the same block through the matrix path (1 row, K = 32)
+        got2 = orc.dequant_matrix(1, np.frombuffer(blob, dtype=np.uint8), 1, 32)
+        np.testing.assert_array_equal(got2[0], want)
+
+
+def test_nvfp4_hand_built_row(orc):
+    kv = {}
+    for ln in _lines("nvfp4_row.txt"):
+        k, *v = ln.split()
+        kv[k] = v
+    blob = np.frombuffer(bytes.fromhex(kv["nibbles"][0]) + bytes.fromhex(kv["scales"][0]), dtype=np.uint8)
+    want = np.array([float(v) for v in kv["values"]])
+    got = orc.dequant_matrix(2, blob, 1, 32, float(kv["tensor_scale"][0]))[0]
+    np.testing.assert_array_equal(got, want)
+    assert np.all(np.signbit(got) == np.signbit(want))
+
+
+def test_bf16_matrix_matches_torch(orc):
+    w = torch.randn(8, 64, generator=torch.Generator().manual_seed(3)) * 0.02
+    blob, _ = gen.encode_matrix(w, "bf16")
+    got = orc.dequant_matrix(0, blob.numpy(), 8, 64)
+    ref = w.to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_q4_1_round_trip_error_bound(orc):
+    """|x - decode(encode(x))| <= d/2 + (fp16 rounding of m) per block."""
+    w = torch.randn(16, 256, generator=torch.Generator().manual_seed(5)) * 0.02
+    blob = gen.encode_q4_1(w).numpy()
+    dq = orc.dequant_matrix(1, blob.reshape(-1), 16, 256)
+    x = w.double().numpy()
+    blocks = blob.reshape(16, 8, 20)
+    d = blocks[:, :, 0:2].copy().view(np.float16).astype(np.float64)[..., 0]
+    m = blocks[:, :, 2:4].copy().view(np.float16).astype(np.float64)[..., 0]
+    err = np.abs(dq - x).reshape(16, 8, 32)
+    mn = x.reshape(16, 8, 32).min(axis=2)
+    bound = d / 2 + np.abs(m - mn) + 1e-12
+    assert np.all(err <= bound[..., None] * (1 + 1e-6))
+    # the encoder's own blocks re-encode to themselves
+    blob2 = gen.encode_q4_1(torch.from_numpy(dq.astype(np.float32))).numpy()
+    assert np.array_equal(blob2, blob)
+
+
+def test_nvfp4_round_trip_error_bound(orc):
+    """|x - decode(encode(x))| <= half an E2M1 step times the block scale, plus E4M3 scale rounding."""
+    w = torch.randn(8, 128, generator=torch.Generator().manual_seed(6)) * 0.02
+    blob, s_t = gen.encode_nvfp4(w)
+    dq = orc.dequant_matrix(2, blob.numpy(), 8, 128, float(s_t))
+    x = w.double().numpy().reshape(8, 8, 16)
+    sc = blob.numpy()[8 * 64:].reshape(8, 8)
+    sb = np.array([[orc.e4m3(int(c)) for c in r] for r in sc]) * float(s_t)
+    amax_b = np.abs(x).max(axis=2)
+    # the largest E2M1 gap is 2 (between 4 and 6); rounding to nearest loses at most half of it,
+    # and a scale that rounded down can push |x|/s past 6 (saturation) by at most the scale's relative error
+    bound = sb * 1.0 + np.maximum(0.0, amax_b - 6 * sb)
+    err = np.abs(dq.reshape(8, 8, 16) - x)
+    assert np.all(err <= bound[..., None] * (1 + 1e-6) + 1e-12)
+    # and relative error on the whole matrix is what a 4-bit format gives (loose sanity)
+    assert np.linalg.norm(dq.reshape(-1) - x.reshape(-1)) / np.linalg.norm(x) < 0.2
+
+
+# --------------------------------------------------------------------------- sizes
+
+def test_packed_sizes_and_page_file_sizes():
+    d2 = gen.LayerDims(2048, 512, wfmt="q4_1")
+    d4 = gen.LayerDims(2048, 512, wfmt="nvfp4")
+    assert gen.expert_bytes(d2) == 1_966_080            # 5.0 bits per weight
+    assert gen.expert_bytes(d4) == 1_769_472            # 4.5 bits per weight
+    n = 3 * 2048 * 512
+    assert gen.expert_bytes(d2) * 8 == 5 * n * 1 and gen.expert_bytes(d4) * 8 == 4.5 * n
+    # "What shipped": BF16 79.59 GB, NVFP4 22.86 GB, q4_1 25.99 GB for 39.8 B params
+    params = 79.59e9 / 2
+    assert abs(params - 39.8e9) / 39.8e9 < 0.001
+    assert params * 4.5 / 8 <= 22.86e9 and params * 5.0 / 8 <= 25.99e9
+    assert 25.99 > 22.86  # the q4_1 file is larger than the NVFP4 file
+    assert round(1 - 22.86 / 79.59, 2) == 0.71  # "71% smaller"
+
+
+# --------------------------------------------------------------------------- routing
+
+def test_softmax_matches_scipy_and_invariants(orc):
+    rng = np.random.default_rng(1)
+    for _ in range(5):
+        l = rng.normal(size=256) * 3
+        p = orc.softmax(l)
+        np.testing.assert_allclose(p, scipy.special.softmax(l), rtol=1e-13, atol=0)
+        assert abs(p.sum() - 1) < 1e-13
+        np.testing.assert_allclose(orc.softmax(l + 7.25), p, rtol=1e-13)
+    np.testing.assert_array_equal(orc.softmax(np.zeros(256)), np.full(256, 1 / 256))
+
+
+def _masked_argmax_topk(l, k):
+    l = np.array(l, dtype=np.float64)
+    out = []
+    for _ in range(k):
+        i = int(np.argmax(l))  # first occurrence: lower index wins ties
+        out.append(i)
+        l[i] = -np.inf
+    return out
+
+
+def test_topk_equals_repeated_masked_argmax(orc):
+    rng = np.random.default_rng(2)
+    for trial in range(50):
+        l = rng.normal(size=256)
+        if trial % 3 == 0:  # inject exact ties around the cut
+            srt = np.sort(l)[::-1]
+            l[l == srt[6]] = srt[5]
+            l[rng.integers(0, 256, 4)] = srt[5]
+        order = orc.sort_experts(l)
+        assert list(order[:6]) == _masked_argmax_topk(l, 6)
+        sel = order[:6]
+        rest = np.setdiff1d(np.arange(256), sel)
+        assert l[sel].min() >= l[rest].max()
+        assert len(set(sel.tolist())) == 6
+
+
+def test_equal_logits_pick_lowest_indices(orc):
+    dims = gen.LayerDims(512, 128, wfmt="bf16")
+    idx, w, _ = orc.route(dims, np.zeros(256))
+    assert list(idx) == [0, 1, 2, 3, 4, 5]
+    np.testing.assert_allclose(w, np.full(6, 1 / 6), rtol=1e-15)
+
+
+def test_renormalised_weights_equal_softmax_over_selected(orc):
+    dims = gen.LayerDims(512, 128, wfmt="bf16")
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        l = rng.normal(size=256) * 2
+        idx, w, p = orc.route(dims, l)
+        assert abs(w.sum() - 1) < 1e-14
+        np.testing.assert_allclose(w, scipy.special.softmax(l[idx]), rtol=1e-12)
+        assert np.all(np.diff(l[idx]) <= 0)  # slot order = logit descending
+
+
+def test_router_logits_match_numpy_matmul(orc):
+    dims = gen.LayerDims(512, 128, wfmt="bf16")
+    layer = gen.make_layer(dims, cfg_id=1)
+    x = gen.make_hidden(1, 4, 512).double().numpy()
+    idx, w, logits, _ = orc.layer_forward(layer, x)
+    wr = layer.router.view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_allclose(logits, x @ wr.T, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- expert FFN / layer
+
+def _torch_decode(layer, e, m):
+    """Expert matrix via torch's own bf16 widening (bf16 layers only)."""
+    dims = layer.dims
+    eb = gen.expert_bytes(dims)
+    offs = gen.matrix_offsets(dims)
+    rows, k = dims.matrix_shapes()[m]
+    blob = layer.experts[e * eb + offs[m]: e * eb + offs[m] + rows * k * 2]
+    return blob.view(torch.bfloat16).reshape(rows, k).to(torch.float64)
+
+
+def test_bf16_layer_matches_torch_library_routines(orc):
+    """Whole layer through torch's matmul / softmax / topk / silu on bf16-widened weights."""
+    dims = gen.LayerDims(512, 128, wfmt="bf16")
+    layer = gen.make_layer(dims, cfg_id=1)
+    x = gen.make_hidden(1, 4, 512).double()
+    idx, w, logits, y = orc.layer_forward(layer, x.numpy())
+    wr = layer.router.view(torch.bfloat16).to(torch.float64)
+    lg = x @ wr.T
+    p = torch.softmax(lg, dim=-1)
+    tv, ti = torch.topk(lg, 6, dim=-1)
+    for t in range(4):
+        assert sorted(ti[t].tolist()) == sorted(idx[t].tolist())
+    yref = torch.zeros(4, 512, dtype=torch.float64)
+    for t in range(4):
+        sel = ti[t]
+        wt = p[t, sel] / p[t, sel].sum()
+        experts = [(256, 1.0)] + [(int(e), float(wi)) for e, wi in zip(sel, wt)]
+        for e, we in experts:
+            wg, wu, wd = (_torch_decode(layer, e, m) for m in range(3))
+            h = F.silu(x[t] @ wg.T) * (x[t] @ wu.T)
+            yref[t] += we * (h @ wd.T)
+    np.testing.assert_allclose(y, yref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def _const_q4_1_layer(dims, consts):
+    """Every weight of expert e's matrix m equals consts[e][m] (d = 0, m = const), router zero."""
+    eb = gen.expert_bytes(dims)
+    buf = np.zeros(dims.n_experts * eb, dtype=np.uint8)
+    offs = gen.matrix_offsets(dims)
+    for e in range(dims.n_experts):
+        for m, (rows, k) in enumerate(dims.matrix_shapes()):
+            blocks = np.zeros((rows * k // 32, 20), dtype=np.uint8)
+            blocks[:, 2:4] = np.frombuffer(np.float16(consts[e][m]).tobytes(), dtype=np.uint8)
+            blocks[:, 4:] = 0x5A  # codes are ignored when d = 0
+            o = e * eb + offs[m]
+            buf[o:o + blocks.size] = blocks.reshape(-1)
+    return gen.Layer(dims, torch.zeros((dims.n_routed, dims.d_model), dtype=torch.int16), None,
+                     torch.from_numpy(buf), None)
+
+
+def test_constant_expert_closed_form(orc):
+    """All weights of an expert's gate/up/down equal cg, cu, cd: with S = sum(x),
+    h_f = silu(cg*S) * cu*S for every f, o_r = cd * d_ff * h; the zero router selects
+    experts 0..5 with weight 1/6 each; y = o_shared + sum_i o_i / 6."""
+    dims = gen.LayerDims(64, 32, n_routed=8, n_shared=1, top_k=6, wfmt="q4_1")
+    rng = np.random.default_rng(9)
+    consts = [[float(np.float16(v)) for v in rng.uniform(-0.05, 0.05, 3)] for _ in range(9)]
+    layer = _const_q4_1_layer(dims, consts)
+    x = rng.normal(size=(3, 64))
+    idx, w, _, y = orc.layer_forward(layer, x)
+    assert np.all(idx == np.arange(6))
+    for t in range(3):
+        S = x[t].sum()
+
+        def out(e):
+            cg, cu, cd = consts[e]
+            g, u = cg * S, cu * S
+            return cd * 32 * (g / (1 + math.exp(-g)) * u)
+
+        want = out(8) + sum(out(e) for e in range(6)) / 6
+        np.testing.assert_allclose(y[t], np.full(64, want), rtol=1e-12)
+
+
+@pytest.mark.parametrize("wfmt", ["bf16", "q4_1", "nvfp4"])
+def test_sparse_equals_dense_masked_bit_exact(orc, wfmt):
+    dims = gen.LayerDims(64, 32, n_routed=16, n_shared=1, top_k=6, wfmt=wfmt)
+    layer = gen.make_layer(dims, cfg_id=77)
+    x = gen.make_hidden(77, 3, 64).double().numpy()
+    i1, w1, _, y1 = orc.layer_forward(layer, x)
+    i2, w2, _, y2 = orc.layer_forward(layer, x, dense=True)
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(y1, y2)
+
+
+def test_sparse_equals_dense_masked_small_layer(orc):
+    """The CPU-sized layer (d 512, d_ff 128, 256+1 bf16 experts), every token."""
+    w = gen.WORKLOADS["c1_small_bf16"]
+    layer = gen.make_layer(w["dims"], cfg_id=w["cfg_id"])
+    x = gen.make_hidden(w["cfg_id"], w["tokens"], 512).double().numpy()
+    _, _, _, y1 = orc.layer_forward(layer, x)
+    _, _, _, y2 = orc.layer_forward(layer, x, dense=True)
+    assert np.array_equal(y1, y2)
+
+
+def test_selection_touches_exactly_k_plus_shared(orc):
+    dims = gen.LayerDims(64, 32, n_routed=16, n_shared=1, top_k=6, wfmt="q4_1")
+    layer = gen.make_layer(dims, cfg_id=78)
+    x = gen.make_hidden(78, 5, 64).double().numpy()
+    idx, w, _, y = orc.layer_forward(layer, x)
+    for t in range(5):
+        assert len(set(idx[t].tolist())) == 6 and np.all((idx[t] >= 0) & (idx[t] < 16))
+        assert abs(w[t].sum() - 1) < 1e-14 and np.all(w[t] > 0)
+    # poisoning every unselected routed expert leaves y unchanged
+    eb = gen.expert_bytes(dims)
+    ex = layer.experts.clone()
+    used = set(idx.reshape(-1).tolist())
+    for e in range(16):
+        if e not in used:
+            ex[e * eb:(e + 1) * eb] = 0xFF
+    l2 = gen.Layer(dims, layer.router, None, ex, None)
+    _, _, _, y2 = orc.layer_forward(l2, x)
+    assert np.array_equal(y, y2)
+
+
+def test_forced_routing_with_own_choice_is_identity(orc):
+    dims = gen.LayerDims(64, 32, n_routed=16, n_shared=1, top_k=6, wfmt="nvfp4")
+    layer = gen.make_layer(dims, cfg_id=79)
+    x = gen.make_hidden(79, 2, 64).double().numpy()
+    idx, w, _, y = orc.layer_forward(layer, x)
+    idx2, w2, _, y2 = orc.layer_forward(layer, x, forced=idx)
+    assert np.array_equal(idx, idx2) and np.array_equal(y, y2) and np.array_equal(w, w2)
+
+
+def test_down_scaling_by_power_of_two_is_exact(orc):
+    """Doubling every down-projection scale/min (q4_1) doubles y exactly."""
+    dims = gen.LayerDims(64, 32, n_routed=16, n_shared=1, top_k=6, wfmt="q4_1")
+    layer = gen.make_layer(dims, cfg_id=80)
+    x = gen.make_hidden(80, 2, 64).double().numpy()
+    _, _, _, y = orc.layer_forward(layer, x)
+    eb = gen.expert_bytes(dims)
+    off = gen.matrix_offsets(dims)[2]
+    ex = layer.experts.clone().numpy()
+    for e in range(17):
+        blk = ex[e * eb + off: e * eb + eb].reshape(-1, 20)
+        for c in (0, 2):
+            v = blk[:, c:c + 2].copy().view(np.float16) * np.float16(2)
+            blk[:, c:c + 2] = v.view(np.uint8)
+    l2 = gen.Layer(dims, layer.router, None, torch.from_numpy(ex), None)
+    _, _, _, y2 = orc.layer_forward(l2, x)
+    np.testing.assert_array_equal(y2, 2 * y)
+
+
+def test_router_bias_shifts_logits(orc):
+    dims = gen.LayerDims(64, 32, n_routed=16, n_shared=1, top_k=6, wfmt="q4_1")
+    base = gen.make_layer(dims, cfg_id=81)
+    bias = torch.from_numpy(np.linspace(-1, 1, 16).astype(np.float32))
+    biased = gen.Layer(dims, base.router, bias, base.experts, None)
+    x = gen.make_hidden(81, 2, 64).double().numpy()
+    _, _, l0, _ = orc.layer_forward(base, x)
+    _, _, l1, _ = orc.layer_forward(biased, x)
+    np.testing.assert_allclose(l1 - l0, np.broadcast_to(bias.double().numpy(), l0.shape), atol=1e-15)
+
+
+def test_zipf_bias_is_log_zipf_pmf():
+    b = gen.zipf_bias(256, 1.1, cfg_id=5, layer=0).double().numpy()
+    p = np.exp(b)
+    assert abs(p.sum() - 1) < 1e-5
+    srt = np.sort(p)[::-1]
+    ranks = np.arange(1, 257)
+    np.testing.assert_allclose(srt / srt[0], ranks ** -1.1, rtol=1e-5)
+
+
+# --------------------------------------------------------------------------- stack
+
+def test_rmsnorm_closed_form(orc):
+    y = np.full(2048, 3.0)
+    np.testing.assert_allclose(orc.rmsnorm(y), np.full(2048, 3.0 / math.sqrt(9.0 + 1e-6)), rtol=1e-15)
+    r = np.random.default_rng(4).normal(size=2048) * 5
+    x = orc.rmsnorm(r)
+    assert abs(np.mean(x * x) - 1) < 1e-6
+
+
+def test_stack_is_layer_composition(orc):
+    dims = gen.LayerDims(64, 32, n_routed=16, n_shared=1, top_k=6, wfmt="q4_1")
+    layers = [gen.make_layer(dims, cfg_id=82, layer=l) for l in range(3)]
+    x0 = gen.make_hidden(82, 1, 64).double().numpy()
+    y, trace, itrace = orc.stack_forward(layers, x0)
+    x = x0
+    for l in range(3):
+        idx, _, _, yl = orc.layer_forward(layers[l], x)
+        np.testing.assert_array_equal(trace[l], yl)
+        np.testing.assert_array_equal(itrace[l], idx)
+        x = orc.rmsnorm(yl[0])[None]
+    np.testing.assert_array_equal(y, trace[-1])
