@@ -1,0 +1,185 @@
+/*
+ * moe.h - C ABI of libmoe, the MI355X (gfx950) sparse mixture-of-experts FFN
+ * layer for token decode and prefill.
+ *
+ * What the layer computes is set by the Flint 40B-A2.5B pages:
+ *   - "Recursive Flint 40B-A2.5B" (orcarouter.ai blog), section "The
+ *     architecture is a memory-bandwidth argument", sparsity bullet: each
+ *     MoE layer has 256 routed experts, 6 are chosen per token, and one
+ *     shared expert is always active; decode is bound by moving weights, so
+ *     only the chosen experts' weights are read.
+ *   - same page, sections "What shipped" and "The quantisation recipe is
+ *     the most transferable part": weights ship as 4-bit q4_1 and NVFP4.
+ * Readings taken where the pages are open (gating, activation, layouts):
+ *   logits l = x Wr^T (+ bias); p = softmax(l) over all routed experts;
+ *   S = top_k experts by (logit descending, index ascending);
+ *   w_i = p_i / sum_{j in S} p_j;
+ *   expert(x) = Wd (silu(Wg x) * (Wu x)),  silu(z) = z / (1 + e^-z);
+ *   y = sum_shared expert(x) + sum_{i in S} w_i expert_i(x).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless marked (host).  The caller owns
+ *     every buffer; the library never allocates or frees device memory.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue
+ *     work and return without synchronising the host.
+ *   - Arguments are checked on the host before anything is enqueued; a
+ *     failed check returns a negative status, enqueues nothing, and leaves a
+ *     message for moe_last_error().  A launch failure returns
+ *     MOE_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - Device pointers must be 16-byte aligned (256 recommended).
+ *   - Dims: d_model and d_ff multiples of 32 in [32, 8192]; 1 <= top_k <= 8;
+ *     top_k <= n_routed <= 256;
+ *     0 <= n_shared <= 4.
+ *   - Matrices use the [out, in] (nn.Linear) convention; quantisation
+ *     blocks run along the input dimension.  Experts are numbered
+ *     0..n_routed-1 (routed) then n_routed.. (shared).
+ *   - Results do not depend on run-to-run scheduling: no floating-point
+ *     atomics; every sum has a fixed order.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* bad dims, NULL pointer, n_tokens out of range */
+    MOE_ERR_UNSUPPORTED = -2, /* format/activation combination not built */
+    MOE_ERR_WORKSPACE = -3,   /* ws NULL or smaller than moe_workspace_size() */
+    MOE_ERR_ALIGNMENT = -4,   /* a device pointer not 16-byte aligned */
+    MOE_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_W_BF16 = 0, MOE_W_Q4_1 = 1, MOE_W_NVFP4 = 2 } moe_wfmt;
+typedef enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act;
+
+/* (host) layer shape and weight format */
+typedef struct {
+    int32_t d_model;  /* hidden size D */
+    int32_t d_ff;     /* expert intermediate size F */
+    int32_t n_routed; /* routed experts E */
+    int32_t n_shared; /* always-active experts */
+    int32_t top_k;    /* experts chosen per token */
+    int32_t wfmt;     /* moe_wfmt */
+} moe_dims;
+
+/* (host) struct of device pointers for one layer */
+typedef struct {
+    const void *router;        /* bf16 [n_routed, d_model] */
+    const float *router_bias;  /* fp32 [n_routed] or NULL */
+    const void *experts;       /* n_routed + n_shared experts in the device layout
+                                  written by moe_repack_weights */
+    const float *tensor_scale; /* NVFP4: fp32 [(n_routed + n_shared) * 3]
+                                  (gate, up, down per expert); otherwise NULL */
+} moe_layer_weights;
+
+/*
+ * Canonical expert layout (input of moe_repack_weights), per expert the
+ * matrices gate [F, D], up [F, D], down [D, F] back to back:
+ *   bf16:  row-major 16-bit values.
+ *   q4_1:  rows x (K/32) blocks of 20 bytes {fp16 d, fp16 m, u8 q[16]};
+ *          element j in the low nibble of q[j], element j+16 in the high
+ *          nibble; value = d*q + m.
+ *   NVFP4: nibbles [rows, K/2] (element 2i low nibble, 2i+1 high nibble of
+ *          byte i), then E4M3 block-16 scales [rows, K/16]; value =
+ *          e2m1(q) * e4m3(scale) * tensor_scale.
+ * The device layout has the same size (moe_packed_expert_bytes).  For q4_1
+ * each matrix becomes a code plane [rows, K/2] followed by a scale plane
+ * [rows, K/32] of {fp16 d, fp16 m}; bf16 and NVFP4 are unchanged.
+ */
+
+/* (host) bytes of one expert (gate + up + down), canonical or device
+   layout; 0 if dims are invalid. */
+size_t moe_packed_expert_bytes(const moe_dims *dims);
+
+/* (host) workspace bytes needed by moe_expert_ffn_q4 / moe_layer_forward /
+   moe_stack_decode / moe_layer_forward_prefill for n_tokens tokens. */
+moe_status moe_workspace_size(const moe_dims *dims, int32_t n_tokens, size_t *bytes);
+
+/* Convert n_experts experts from the canonical layout to the device layout.
+   canonical and packed are device buffers of n_experts *
+   moe_packed_expert_bytes() bytes and must not overlap. */
+moe_status moe_repack_weights(const moe_dims *dims, const void *canonical, void *packed, int32_t n_experts,
+                              void *stream);
+
+/*
+ * Router and selection (rows a1-a2 of the path).  For each token:
+ * logits = x Wr^T (+ bias) in fp32; softmax over n_routed; the top_k
+ * experts by (logit descending, index ascending); renormalised weights.
+ *   x          [n_tokens, d_model], fp32 (act = MOE_ACT_F32) or bf16
+ *   router     bf16 [n_routed, d_model]; router_bias fp32 [n_routed] or NULL
+ *   topk_idx   out int32 [n_tokens, top_k], slots in selection order
+ *   topk_w     out fp32 [n_tokens, top_k], summing to 1 per token
+ *   logits_out out fp32 [n_tokens, n_routed], or NULL
+ *   ws, ws_bytes workspace of at least moe_workspace_size(dims, n_tokens)
+ * 1 <= n_tokens <= 65536.
+ */
+moe_status moe_route_topk(const moe_dims *dims, const void *x, int32_t act, int32_t n_tokens, const void *router,
+                          const float *router_bias, int32_t *topk_idx, float *topk_w, float *logits_out, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/*
+ * Expert FFN over given routing (rows a3-a5): for each token
+ * y = sum_shared expert_s(x) + sum_i topk_w[i] * expert_{topk_idx[i]}(x),
+ * streaming each distinct expert's 4-bit (or bf16) weights once per call and
+ * applying it to all tokens that chose it.  Decode sizes: 1 <= n_tokens <= 8.
+ *   experts      device layout; tensor_scale as in moe_layer_weights
+ *   topk_idx     int32 [n_tokens, top_k], each in [0, n_routed), distinct per token
+ *   topk_w       fp32 [n_tokens, top_k]
+ *   y            out fp32 [n_tokens, d_model]
+ *   ws, ws_bytes workspace of at least moe_workspace_size(dims, n_tokens)
+ * Indices outside [0, n_routed) select nothing (their slot contributes 0);
+ * a repeated index counts once, with the weight of its last slot.
+ */
+moe_status moe_expert_ffn_q4(const moe_dims *dims, const void *x, int32_t act, int32_t n_tokens,
+                             const void *experts, const float *tensor_scale, const int32_t *topk_idx,
+                             const float *topk_w, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Whole layer: route + expert FFN.  n_tokens <= 8 takes the decode path
+ * (grouped GEMV over the union of chosen experts); larger n_tokens take the
+ * prefill path (moe_layer_forward_prefill).  topk_idx_out / topk_w_out may be
+ * NULL.  1 <= n_tokens <= 65536.
+ */
+moe_status moe_layer_forward(const moe_dims *dims, const moe_layer_weights *w, const void *x, int32_t act,
+                             int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/*
+ * Prefill path for any n_tokens (rows a8-a10): route all tokens, permute
+ * (token, slot) pairs by expert (histogram, scan, scatter), run the experts
+ * as a grouped GEMM on the matrix cores (fp16 operands, fp32 accumulate),
+ * and combine each token's slots in a fixed order.
+ */
+moe_status moe_layer_forward_prefill(const moe_dims *dims, const moe_layer_weights *w, const void *x,
+                                     int32_t act, int32_t n_tokens, float *y, int32_t *topk_idx_out,
+                                     float *topk_w_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * A stack of n_layers layers (row a6): x_0 = x0 (fp32 [n_tokens, d_model]),
+ * y_l = layer_l(x_l), x_{l+1} = y_l / sqrt(mean(y_l^2) + 1e-6) per token;
+ * y receives y_{n_layers-1}.  layers is a host array of n_layers structs.
+ * y_trace fp32 [n_layers, n_tokens, d_model] and idx_trace int32
+ * [n_layers, n_tokens, top_k] receive every layer's output and selection, or
+ * are NULL.  1 <= n_tokens <= 8.
+ */
+moe_status moe_stack_decode(const moe_dims *dims, int32_t n_layers, const moe_layer_weights *layers,
+                            const float *x0, int32_t n_tokens, float *y, float *y_trace, int32_t *idx_trace,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* (host) static description of a status code. */
+const char *moe_status_string(moe_status s);
+
+/* (host) detail of the last non-OK status on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

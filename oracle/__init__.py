@@ -174,6 +174,22 @@ def layer_forward(layer, x: np.ndarray, forced: Optional[np.ndarray] = None, den
     return idx, w, logits, y
 
 
+def experts_given(layer, x: np.ndarray, idx: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y = shared experts + sum_i w[t, i] * expert_{idx[t, i]}(x_t), in fp64."""
+    dims = layer.dims
+    x = np.ascontiguousarray(x, dtype=np.float64).reshape(-1, dims.d_model)
+    T = x.shape[0]
+    _, ex, ts, _ = _layer_arrays(layer)
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(T, dims.top_k)
+    w = np.ascontiguousarray(w, dtype=np.float64).reshape(T, dims.top_k)
+    y = np.zeros((T, dims.d_model), dtype=np.float64)
+    d = dims_struct(dims)
+    lib().orc_experts_given(ctypes.byref(d), ctypes.c_int32(T), _p(x, ctypes.c_double), _p(ex, ctypes.c_uint8),
+                            None if ts is None else _p(ts, ctypes.c_float), _p(idx, ctypes.c_int32),
+                            _p(w, ctypes.c_double), _p(y, ctypes.c_double))
+    return y
+
+
 def stack_forward(layers: Sequence, x0: np.ndarray):
     """Returns (y_last [T,d], y_trace [L,T,d], idx_trace [L,T,k])."""
     dims = layers[0].dims

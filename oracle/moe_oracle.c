@@ -305,6 +305,31 @@ int orc_layer_forward(const orc_dims *dm, int32_t T, const double *x, const uint
     return 0;
 }
 
+/*
+ * Expert FFN over a given routing: y = sum_shared expert_s(x) +
+ * sum_i w[i] * expert_{idx[i]}(x), slots taken in the order given.
+ */
+int orc_experts_given(const orc_dims *dm, int32_t T, const double *x, const uint8_t *experts, const float *tscale,
+                      const int32_t *idx, const double *w, double *y) {
+    int D = dm->d_model, K = dm->top_k;
+    double *o = (double *)malloc(sizeof(double) * D);
+    for (int t = 0; t < T; t++) {
+        const double *xt = x + (size_t)t * D;
+        double *yt = y + (size_t)t * D;
+        for (int r = 0; r < D; r++) yt[r] = 0.0;
+        for (int s = 0; s < dm->n_shared; s++) {
+            orc_expert_ffn(dm, experts, tscale, dm->n_routed + s, xt, o);
+            for (int r = 0; r < D; r++) yt[r] += o[r];
+        }
+        for (int i = 0; i < K; i++) {
+            orc_expert_ffn(dm, experts, tscale, idx[(size_t)t * K + i], xt, o);
+            for (int r = 0; r < D; r++) yt[r] += w[(size_t)t * K + i] * o[r];
+        }
+    }
+    free(o);
+    return 0;
+}
+
 /* x_next = y / sqrt(mean(y^2) + eps), one token of length n. */
 void orc_rmsnorm(int n, const double *y, double eps, double *out) {
     double ss = 0.0;

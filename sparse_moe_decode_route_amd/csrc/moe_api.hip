@@ -1,0 +1,390 @@
+// C ABI of libmoe: argument checks on the host, workspace layout, and the
+// enqueueing of the decode, prefill and stack paths.  Nothing here touches
+// the device before every check has passed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+#include "moe_prefill.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const std::string &msg) {
+    g_err = msg;
+    return s;
+}
+
+moe_status ok() {
+    g_err.clear();
+    return MOE_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t mat_bytes(int fmt, size_t rows, size_t k) {
+    if (fmt == MOE_W_BF16) return rows * k * 2;
+    if (fmt == MOE_W_Q4_1) return rows * (k / 32) * 20;
+    return rows * (k / 2) + rows * (k / 16);
+}
+
+moe_status check_dims(const moe_dims *d) {
+    if (!d) return fail(MOE_ERR_INVALID_ARG, "dims is NULL");
+    if (d->wfmt != MOE_W_BF16 && d->wfmt != MOE_W_Q4_1 && d->wfmt != MOE_W_NVFP4)
+        return fail(MOE_ERR_UNSUPPORTED, "unknown weight format " + std::to_string(d->wfmt));
+    if (d->d_model < 32 || d->d_model > 8192 || d->d_model % 32)
+        return fail(MOE_ERR_INVALID_ARG, "d_model must be a multiple of 32 in [32, 8192]");
+    if (d->d_ff < 32 || d->d_ff > 8192 || d->d_ff % 32)
+        return fail(MOE_ERR_INVALID_ARG, "d_ff must be a multiple of 32 in [32, 8192]");
+    if (d->n_routed < 1 || d->n_routed > 256) return fail(MOE_ERR_INVALID_ARG, "n_routed must be in [1, 256]");
+    if (d->top_k < 1 || d->top_k > 8 || d->top_k > d->n_routed)
+        return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, min(8, n_routed)]");
+    if (d->n_shared < 0 || d->n_shared > 4) return fail(MOE_ERR_INVALID_ARG, "n_shared must be in [0, 4]");
+    return MOE_OK;
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Decode-path workspace (n_tokens <= 8).
+struct DecodeWs {
+    size_t logits, idx, w, xbuf, xconv, meta, act_expert, act_mask, act_w, h, ybuf0, ybuf1, total;
+    int amax;
+};
+
+DecodeWs decode_ws(const moe_dims &d, int T) {
+    DecodeWs L{};
+    L.amax = std::min(d.n_routed, T * d.top_k) + d.n_shared;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o += align_up(bytes);
+        return at;
+    };
+    L.logits = take((size_t)T * d.n_routed * 4);
+    L.idx = take((size_t)T * d.top_k * 4);
+    L.w = take((size_t)T * d.top_k * 4);
+    L.xbuf = take((size_t)T * d.d_model * 4);
+    L.xconv = take((size_t)T * d.d_model * 4);
+    L.meta = take(256);
+    L.act_expert = take((size_t)L.amax * 4);
+    L.act_mask = take((size_t)L.amax * 4);
+    L.act_w = take((size_t)L.amax * T * 4);
+    L.h = take((size_t)L.amax * T * d.d_ff * 4);
+    L.ybuf0 = take((size_t)T * d.d_model * 4);
+    L.ybuf1 = take((size_t)T * d.d_model * 4);
+    L.total = o;
+    return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+moe::DecodeParams base_params(const moe_dims &d, int T, void *ws, const DecodeWs &L) {
+    moe::DecodeParams p{};
+    p.D = d.d_model;
+    p.F = d.d_ff;
+    p.E = d.n_routed;
+    p.S = d.n_shared;
+    p.K = d.top_k;
+    p.T = T;
+    p.fmt = d.wfmt;
+    p.amax = L.amax;
+    p.expert_bytes = moe_packed_expert_bytes(&d);
+    p.logits = at<float>(ws, L.logits);
+    p.idx = at<int32_t>(ws, L.idx);
+    p.w = at<float>(ws, L.w);
+    p.xbuf = at<float>(ws, L.xbuf);
+    p.meta = at<int32_t>(ws, L.meta);
+    p.act_expert = at<int32_t>(ws, L.act_expert);
+    p.act_mask = at<uint32_t>(ws, L.act_mask);
+    p.act_w = at<float>(ws, L.act_w);
+    p.h = at<float>(ws, L.h);
+    return p;
+}
+
+moe_status hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+    return ok();
+}
+
+moe_status check_ptr(const void *p, const char *name, bool required = true) {
+    if (!p) return required ? fail(MOE_ERR_INVALID_ARG, std::string(name) + " is NULL") : MOE_OK;
+    if (!aligned16(p)) return fail(MOE_ERR_ALIGNMENT, std::string(name) + " is not 16-byte aligned");
+    return MOE_OK;
+}
+
+#define MOE_TRY(expr)                   \
+    do {                                \
+        moe_status _s = (expr);         \
+        if (_s != MOE_OK) return _s;    \
+    } while (0)
+
+moe_status check_ws(const moe_dims *d, int T, const void *ws, size_t ws_bytes) {
+    size_t need = 0;
+    MOE_TRY(moe_workspace_size(d, T, &need));
+    if (!ws || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
+                                           std::to_string(ws ? ws_bytes : 0));
+    return check_ptr(ws, "ws");
+}
+
+// fp32 view of the decode input (bf16 inputs are widened into ws first).
+moe_status decode_input(const moe_dims &d, const void *x, int act, int T, void *ws, const DecodeWs &L,
+                        hipStream_t st, const float **out) {
+    if (act == MOE_ACT_F32) {
+        *out = static_cast<const float *>(x);
+        return MOE_OK;
+    }
+    float *xc = at<float>(ws, L.xconv);
+    MOE_TRY(hip_status(moe::launch_bf16_to_f32(static_cast<const uint16_t *>(x), xc, T * d.d_model, st),
+                       "bf16 widening launch"));
+    *out = xc;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_packed_expert_bytes(const moe_dims *d) {
+    if (check_dims(d) != MOE_OK) return 0;
+    return 2 * mat_bytes(d->wfmt, d->d_ff, d->d_model) + mat_bytes(d->wfmt, d->d_model, d->d_ff);
+}
+
+moe_status moe_workspace_size(const moe_dims *d, int32_t n_tokens, size_t *bytes) {
+    MOE_TRY(check_dims(d));
+    if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    if (n_tokens < 1 || n_tokens > 65536) return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, 65536]");
+    size_t need = 0;
+    if (n_tokens <= moe::MAX_DECODE_T) need = decode_ws(*d, n_tokens).total;
+    need = std::max(need, moe::prefill_ws_bytes(d->d_model, d->d_ff, d->n_routed, d->n_shared, d->top_k, n_tokens));
+    *bytes = need;
+    return ok();
+}
+
+moe_status moe_repack_weights(const moe_dims *d, const void *canonical, void *packed, int32_t n_experts,
+                              void *stream) {
+    MOE_TRY(check_dims(d));
+    MOE_TRY(check_ptr(canonical, "canonical"));
+    MOE_TRY(check_ptr(packed, "packed"));
+    if (n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts must be >= 1");
+    const size_t eb = moe_packed_expert_bytes(d);
+    const char *c0 = static_cast<const char *>(canonical), *p0 = static_cast<const char *>(packed);
+    if (c0 < p0 + eb * n_experts && p0 < c0 + eb * n_experts)
+        return fail(MOE_ERR_INVALID_ARG, "canonical and packed overlap");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (d->wfmt != MOE_W_Q4_1)
+        return hip_status(hipMemcpyAsync(packed, canonical, eb * n_experts, hipMemcpyDeviceToDevice, st),
+                          "repack copy");
+    return hip_status(moe::launch_repack_q4_1(static_cast<const uint8_t *>(canonical), static_cast<uint8_t *>(packed),
+                                              n_experts, d->d_model, d->d_ff, st),
+                      "repack launch");
+}
+
+moe_status moe_route_topk(const moe_dims *d, const void *x, int32_t act, int32_t n_tokens, const void *router,
+                          const float *router_bias, int32_t *topk_idx, float *topk_w, float *logits_out, void *ws,
+                          size_t ws_bytes, void *stream) {
+    MOE_TRY(check_dims(d));
+    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown activation type");
+    if (n_tokens < 1 || n_tokens > 65536) return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, 65536]");
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(router, "router"));
+    MOE_TRY(check_ptr(router_bias, "router_bias", false));
+    MOE_TRY(check_ptr(topk_idx, "topk_idx"));
+    MOE_TRY(check_ptr(topk_w, "topk_w"));
+    MOE_TRY(check_ptr(logits_out, "logits_out", false));
+    MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n_tokens > moe::MAX_DECODE_T) {
+        float *logits = logits_out ? logits_out : moe::prefill_logits_buffer(ws, *d, n_tokens);
+        MOE_TRY(hip_status(moe::launch_router_gemm(x, act, n_tokens, d->d_model, d->n_routed,
+                                                   static_cast<const uint16_t *>(router), router_bias, logits, st),
+                           "router launch"));
+        return hip_status(moe::launch_topk(logits, n_tokens, d->n_routed, d->top_k, topk_idx, topk_w, st),
+                          "top-k launch");
+    }
+    const DecodeWs L = decode_ws(*d, n_tokens);
+    moe::DecodeParams p = base_params(*d, n_tokens, ws, L);
+    MOE_TRY(decode_input(*d, x, act, n_tokens, ws, L, st, &p.x));
+    p.router = static_cast<const uint16_t *>(router);
+    p.bias = router_bias;
+    if (logits_out) p.logits = logits_out;
+    p.idx_out = topk_idx;
+    p.w_out = topk_w;
+    p.want_router = 1;
+    p.want_shared = 0;
+    return hip_status(moe::launch_route_only(p, st), "route launch");
+}
+
+moe_status moe_expert_ffn_q4(const moe_dims *d, const void *x, int32_t act, int32_t n_tokens, const void *experts,
+                             const float *tensor_scale, const int32_t *topk_idx, const float *topk_w, float *y,
+                             void *ws, size_t ws_bytes, void *stream) {
+    MOE_TRY(check_dims(d));
+    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown activation type");
+    if (n_tokens < 1 || n_tokens > moe::MAX_DECODE_T)
+        return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, 8] for the expert FFN");
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(experts, "experts"));
+    MOE_TRY(check_ptr(tensor_scale, "tensor_scale", d->wfmt == MOE_W_NVFP4));
+    MOE_TRY(check_ptr(topk_idx, "topk_idx"));
+    MOE_TRY(check_ptr(topk_w, "topk_w"));
+    MOE_TRY(check_ptr(y, "y"));
+    MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const DecodeWs L = decode_ws(*d, n_tokens);
+    moe::DecodeParams p = base_params(*d, n_tokens, ws, L);
+    MOE_TRY(decode_input(*d, x, act, n_tokens, ws, L, st, &p.x));
+    p.experts = static_cast<const uint8_t *>(experts);
+    p.tscale = d->wfmt == MOE_W_NVFP4 ? tensor_scale : nullptr;
+    p.route_given = 1;
+    p.idx = const_cast<int32_t *>(topk_idx);
+    p.w = const_cast<float *>(topk_w);
+    p.want_router = 0;
+    p.want_shared = 1;
+    p.y = y;
+    return hip_status(moe::launch_decode(p, st), "expert FFN launch");
+}
+
+static moe_status check_layer(const moe_dims *d, const moe_layer_weights *w) {
+    if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+    MOE_TRY(check_ptr(w->router, "router"));
+    MOE_TRY(check_ptr(w->router_bias, "router_bias", false));
+    MOE_TRY(check_ptr(w->experts, "experts"));
+    MOE_TRY(check_ptr(w->tensor_scale, "tensor_scale", d->wfmt == MOE_W_NVFP4));
+    return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_dims *d, const moe_layer_weights *w, const void *x, int32_t act,
+                             int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                             size_t ws_bytes, void *stream) {
+    MOE_TRY(check_dims(d));
+    if (n_tokens > moe::MAX_DECODE_T)
+        return moe_layer_forward_prefill(d, w, x, act, n_tokens, y, topk_idx_out, topk_w_out, ws, ws_bytes, stream);
+    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown activation type");
+    if (n_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "n_tokens must be >= 1");
+    MOE_TRY(check_layer(d, w));
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(y, "y"));
+    MOE_TRY(check_ptr(topk_idx_out, "topk_idx_out", false));
+    MOE_TRY(check_ptr(topk_w_out, "topk_w_out", false));
+    MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const DecodeWs L = decode_ws(*d, n_tokens);
+    moe::DecodeParams p = base_params(*d, n_tokens, ws, L);
+    MOE_TRY(decode_input(*d, x, act, n_tokens, ws, L, st, &p.x));
+    p.router = static_cast<const uint16_t *>(w->router);
+    p.bias = w->router_bias;
+    p.experts = static_cast<const uint8_t *>(w->experts);
+    p.tscale = d->wfmt == MOE_W_NVFP4 ? w->tensor_scale : nullptr;
+    p.idx_out = topk_idx_out;
+    p.w_out = topk_w_out;
+    p.want_router = 1;
+    p.want_shared = 1;
+    p.y = y;
+    return hip_status(moe::launch_decode(p, st), "layer launch");
+}
+
+moe_status moe_layer_forward_prefill(const moe_dims *d, const moe_layer_weights *w, const void *x, int32_t act,
+                                     int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                                     size_t ws_bytes, void *stream) {
+    MOE_TRY(check_dims(d));
+    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown activation type");
+    if (n_tokens < 1 || n_tokens > 65536) return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, 65536]");
+    if (d->wfmt != MOE_W_Q4_1 && d->wfmt != MOE_W_NVFP4 && d->wfmt != MOE_W_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "prefill format");
+    MOE_TRY(check_layer(d, w));
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(y, "y"));
+    MOE_TRY(check_ptr(topk_idx_out, "topk_idx_out", false));
+    MOE_TRY(check_ptr(topk_w_out, "topk_w_out", false));
+    MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
+    moe::PrefillArgs a{};
+    a.D = d->d_model;
+    a.F = d->d_ff;
+    a.E = d->n_routed;
+    a.S = d->n_shared;
+    a.K = d->top_k;
+    a.T = n_tokens;
+    a.fmt = d->wfmt;
+    a.act = act;
+    a.expert_bytes = moe_packed_expert_bytes(d);
+    a.x = x;
+    a.router = static_cast<const uint16_t *>(w->router);
+    a.bias = w->router_bias;
+    a.experts = static_cast<const uint8_t *>(w->experts);
+    a.tscale = d->wfmt == MOE_W_NVFP4 ? w->tensor_scale : nullptr;
+    a.y = y;
+    a.idx_out = topk_idx_out;
+    a.w_out = topk_w_out;
+    a.ws = ws;
+    return hip_status(moe::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+moe_status moe_stack_decode(const moe_dims *d, int32_t n_layers, const moe_layer_weights *layers, const float *x0,
+                            int32_t n_tokens, float *y, float *y_trace, int32_t *idx_trace, void *ws,
+                            size_t ws_bytes, void *stream) {
+    MOE_TRY(check_dims(d));
+    if (n_layers < 1) return fail(MOE_ERR_INVALID_ARG, "n_layers must be >= 1");
+    if (n_tokens < 1 || n_tokens > moe::MAX_DECODE_T)
+        return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, 8] for stack decode");
+    if (!layers) return fail(MOE_ERR_INVALID_ARG, "layers is NULL");
+    for (int l = 0; l < n_layers; l++) MOE_TRY(check_layer(d, &layers[l]));
+    MOE_TRY(check_ptr(x0, "x0"));
+    MOE_TRY(check_ptr(y, "y"));
+    MOE_TRY(check_ptr(y_trace, "y_trace", false));
+    MOE_TRY(check_ptr(idx_trace, "idx_trace", false));
+    MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const DecodeWs L = decode_ws(*d, n_tokens);
+    const size_t TD = (size_t)n_tokens * d->d_model;
+    const float *prev = nullptr;
+    for (int l = 0; l < n_layers; l++) {
+        moe::DecodeParams p = base_params(*d, n_tokens, ws, L);
+        p.x = l == 0 ? x0 : nullptr;
+        p.x_prev = l == 0 ? nullptr : prev;
+        p.router = static_cast<const uint16_t *>(layers[l].router);
+        p.bias = layers[l].router_bias;
+        p.experts = static_cast<const uint8_t *>(layers[l].experts);
+        p.tscale = d->wfmt == MOE_W_NVFP4 ? layers[l].tensor_scale : nullptr;
+        p.idx_out = idx_trace ? idx_trace + (size_t)l * n_tokens * d->top_k : nullptr;
+        p.want_router = 1;
+        p.want_shared = 1;
+        float *out;
+        if (l == n_layers - 1)
+            out = y;
+        else if (y_trace)
+            out = y_trace + (size_t)l * TD;
+        else
+            out = at<float>(ws, (l & 1) ? L.ybuf1 : L.ybuf0);
+        p.y = out;
+        MOE_TRY(hip_status(moe::launch_decode(p, st), "stack layer launch"));
+        prev = out;
+    }
+    if (y_trace)
+        MOE_TRY(hip_status(hipMemcpyAsync(y_trace + (size_t)(n_layers - 1) * TD, y, TD * 4, hipMemcpyDeviceToDevice, st),
+                           "trace copy"));
+    return ok();
+}
+
+const char *moe_status_string(moe_status s) {
+    switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_ALIGNMENT: return "misaligned pointer";
+    case MOE_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

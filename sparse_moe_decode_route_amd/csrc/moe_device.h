@@ -1,0 +1,180 @@
+// Device helpers for libmoe (gfx950, wave64): weight-unit decoding and
+// wave reductions.  Formats as defined by the device layout in moe.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_WAVE 64
+
+namespace moe {
+
+enum { FMT_BF16 = 0, FMT_Q4_1 = 1, FMT_NVFP4 = 2 };
+
+// Hide a value's provenance from the optimiser so that byte extraction after
+// a nibble mask maps onto v_cvt_f32_ubyteN (one VALU op per weight) instead of
+// a bit-field extract followed by a conversion.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    return __half2float(__ushort_as_half((unsigned short)(h & 0xFFFFu)));
+}
+
+// OCP E4M3 (FN) byte -> fp32, by fields (the NaN code is not produced by
+// encoders and is not special-cased).
+__device__ __forceinline__ float e4m3_to_float(uint32_t c) {
+    uint32_t s = (c & 0x80u) << 24, e = (c >> 3) & 15u, m = c & 7u;
+    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+// ---- elements per weight unit (one lane's share of a row per step) ----
+template <int FMT> struct Unit;
+template <> struct Unit<FMT_BF16> { static constexpr int E = 8; };
+template <> struct Unit<FMT_Q4_1> { static constexpr int E = 32; };
+template <> struct Unit<FMT_NVFP4> { static constexpr int E = 32; };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream16(const void *p) {
+    u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Raw bytes of one unit of one row, as loaded from HBM.
+struct WUnit {
+    uint4 c;     // 16 bytes of codes (bf16: 8 values)
+    uint32_t s;  // q4_1: {fp16 d, fp16 m}; NVFP4: two E4M3 scale bytes; bf16: unused
+};
+
+// Matrix view in the device layout: [rows, K].
+struct Mat {
+    const uint8_t *base;
+    int rows, k;
+    float ts;  // NVFP4 tensor scale (1 otherwise)
+};
+
+template <int FMT>
+__device__ __forceinline__ size_t mat_bytes(int rows, int k) {
+    if (FMT == FMT_BF16) return (size_t)rows * k * 2;
+    if (FMT == FMT_Q4_1) return (size_t)rows * (k / 2) + (size_t)rows * (k / 32) * 4;
+    return (size_t)rows * (k / 2) + (size_t)rows * (k / 16);
+}
+
+template <int FMT>
+__device__ __forceinline__ WUnit load_unit(const Mat &m, int row, int u) {
+    WUnit w;
+    if (FMT == FMT_BF16) {
+        w.c = ld_stream16((const uint4 *)(m.base + (size_t)row * m.k * 2) + u);
+        w.s = 0;
+    } else if (FMT == FMT_Q4_1) {
+        w.c = ld_stream16((const uint4 *)(m.base + (size_t)row * (m.k / 2)) + u);
+        const uint32_t *sp = (const uint32_t *)(m.base + (size_t)m.rows * (m.k / 2) + (size_t)row * (m.k / 32) * 4);
+        w.s = __builtin_nontemporal_load(sp + u);
+    } else {
+        w.c = ld_stream16((const uint4 *)(m.base + (size_t)row * (m.k / 2)) + u);
+        const uint16_t *sp = (const uint16_t *)(m.base + (size_t)m.rows * (m.k / 2) + (size_t)row * (m.k / 16));
+        w.s = __builtin_nontemporal_load(sp + u);
+    }
+    return w;
+}
+
+// Activation unit in registers: the unit's elements and (4-bit formats) their sum.
+template <int FMT> struct XUnit {
+    float v[Unit<FMT>::E];
+    float sum;
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_x(XUnit<FMT> &x, const float *src, int u) {
+    const float4 *p = (const float4 *)(src + (size_t)u * Unit<FMT>::E);
+#pragma unroll
+    for (int i = 0; i < Unit<FMT>::E / 4; i++) {
+        float4 f = p[i];
+        x.v[4 * i + 0] = f.x;
+        x.v[4 * i + 1] = f.y;
+        x.v[4 * i + 2] = f.z;
+        x.v[4 * i + 3] = f.w;
+    }
+    if (FMT == FMT_Q4_1) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < Unit<FMT>::E; i++) s += x.v[i];
+        x.sum = s;
+    } else {
+        x.sum = 0.f;
+    }
+}
+
+// dot(unit weights, unit activations) in fp32.
+template <int FMT>
+__device__ __forceinline__ float unit_dot(const WUnit &w, const XUnit<FMT> &x, float ts) {
+    if (FMT == FMT_BF16) {
+        uint32_t a[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            acc = __builtin_fmaf(bf16lo(a[i]), x.v[2 * i], acc);
+            acc = __builtin_fmaf(bf16hi(a[i]), x.v[2 * i + 1], acc);
+        }
+        return acc;
+    } else if (FMT == FMT_Q4_1) {
+        // sum_i (d q_i + m) x_i = d * sum_i q_i x_i + m * sum_i x_i
+        uint32_t a[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint32_t lo = opaque(a[i] & 0x0F0F0F0Fu);
+            uint32_t hi = opaque((a[i] >> 4) & 0x0F0F0F0Fu);
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                acc0 = __builtin_fmaf((float)((lo >> (8 * b)) & 0xFFu), x.v[4 * i + b], acc0);
+                acc1 = __builtin_fmaf((float)((hi >> (8 * b)) & 0xFFu), x.v[16 + 4 * i + b], acc1);
+            }
+        }
+        float d = half_bits_to_float(w.s), m = half_bits_to_float(w.s >> 16);
+        return __builtin_fmaf(d, acc0 + acc1, m * x.sum);
+    } else {
+        // two blocks of 16: e2m1 codes decoded by the hardware converter
+        // (scale 1.0: exact), each block scaled by its E4M3 scale.
+        uint32_t a[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
+        float acc[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(a[i], 1.0f, 0);
+            auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(a[i], 1.0f, 1);
+            auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(a[i], 1.0f, 2);
+            auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(a[i], 1.0f, 3);
+            float s = acc[i >> 1];
+            s = __builtin_fmaf(p0[0], x.v[8 * i + 0], s);
+            s = __builtin_fmaf(p0[1], x.v[8 * i + 1], s);
+            s = __builtin_fmaf(p1[0], x.v[8 * i + 2], s);
+            s = __builtin_fmaf(p1[1], x.v[8 * i + 3], s);
+            s = __builtin_fmaf(p2[0], x.v[8 * i + 4], s);
+            s = __builtin_fmaf(p2[1], x.v[8 * i + 5], s);
+            s = __builtin_fmaf(p3[0], x.v[8 * i + 6], s);
+            s = __builtin_fmaf(p3[1], x.v[8 * i + 7], s);
+            acc[i >> 1] = s;
+        }
+        float s0 = e4m3_to_float(w.s & 0xFFu), s1 = e4m3_to_float((w.s >> 8) & 0xFFu);
+        return ts * __builtin_fmaf(s0, acc[0], s1 * acc[1]);
+    }
+}
+
+// Sum over groups of LPR consecutive lanes (LPR a power of two <= 64); every
+// lane of a group ends with the same value.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+    return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+}  // namespace moe

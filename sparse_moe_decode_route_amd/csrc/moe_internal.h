@@ -1,0 +1,46 @@
+// Internal host/device interface of libmoe (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int MAX_DECODE_T = 8;
+
+// Everything a decode-path kernel reads or writes (device pointers).
+struct DecodeParams {
+    int D, F, E, S, K, T, fmt;
+    int amax;            // slots in the active-expert list (shared + routed union bound)
+    int route_given;     // 1: idx/w come from the caller (no router, no top-k)
+    int want_router;     // phase A computes router logits
+    int want_shared;     // phase A computes shared experts' h
+    size_t expert_bytes;
+    const float *x;      // [T, D] fp32 input, or nullptr when x_prev is used
+    const float *x_prev; // previous layer output to RMS-normalise (stacks), or nullptr
+    float *xbuf;         // normalised input [T, D] written by phase A when x_prev is set
+    const uint16_t *router;
+    const float *bias;
+    const uint8_t *experts;
+    const float *tscale;
+    float *logits;       // [T, E]
+    int32_t *idx;        // [T, K]
+    float *w;            // [T, K]
+    int32_t *idx_out;    // optional copies for the caller
+    float *w_out;
+    int32_t *meta;       // meta[0] = number of active slots
+    int32_t *act_expert; // [amax]
+    uint32_t *act_mask;  // [amax] token bitmask
+    float *act_w;        // [amax, T] combine weight of each token (0 if absent)
+    float *h;            // [amax, T, F]
+    float *y;            // [T, D]
+};
+
+hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
+hipError_t launch_route_only(const DecodeParams &p, hipStream_t st);
+hipError_t launch_bf16_to_f32(const uint16_t *in, float *out, int n, hipStream_t st);
+hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *idx, float *w, hipStream_t st);
+hipError_t launch_router_gemm(const void *x, int act, int T, int D, int E, const uint16_t *router,
+                              const float *bias, float *logits, hipStream_t st);
+
+}  // namespace moe

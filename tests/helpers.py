@@ -1,0 +1,68 @@
+"""Comparison helpers shared by the GPU parity tests and the smoke check.
+
+Routing: the GPU takes its top-k decision on fp32 logits, the oracle on fp64
+logits.  Both are correct selections whenever no two logits around the cut
+are closer than the fp32 rounding error of the GPU's dot products, so the GPU
+set is checked for validity against the fp64 logits with a band derived from
+that error bound; outside the band the sets must be identical.  Outputs are
+compared with the oracle run on the GPU's own selection (teacher forcing),
+which equals the oracle's own result whenever the sets match.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+REL_L2_TOL = 2e-3  # layer-output tolerance on the relative L2 error per token
+U32 = 2.0 ** -24
+
+
+def router_band(x: np.ndarray, router_f64: np.ndarray) -> np.ndarray:
+    """Per-token bound on |fp32 logit - exact logit|, doubled (two logits compared).
+
+    The router kernel gives each lane d_model/512 units of 8 products,
+    accumulated in order by FMA, then a 6-level butterfly: every product
+    passes through at most n = d_model/64 + 8 roundings, so
+    |err| <= n * 2^-24 * sum_k |x_k W_ek| (first order).
+    """
+    d = x.shape[1]
+    n = d / 64 + 8
+    mag = np.abs(x) @ np.abs(router_f64).T  # [T, E]
+    return 2.0 * n * U32 * mag.max(axis=1) * 1.01
+
+
+def check_routing(gpu_idx: np.ndarray, gpu_w: np.ndarray, logits64: np.ndarray, orc_idx: np.ndarray,
+                  orc_w: np.ndarray, band: np.ndarray, w_atol: float = 2e-6):
+    """Returns (n_exact, n_ambiguous).  Raises AssertionError on an invalid selection."""
+    T, K = gpu_idx.shape
+    E = logits64.shape[1]
+    n_exact = n_amb = 0
+    for t in range(T):
+        sg = gpu_idx[t].tolist()
+        assert len(set(sg)) == K, f"token {t}: repeated experts {sg}"
+        assert all(0 <= e < E for e in sg), f"token {t}: index out of range {sg}"
+        rest = np.setdiff1d(np.arange(E), sg)
+        lo_sel = logits64[t, sg].min()
+        hi_rest = logits64[t, rest].max() if rest.size else -np.inf
+        assert lo_sel >= hi_rest - band[t], (
+            f"token {t}: selection {sg} invalid: min selected {lo_sel} < max unselected {hi_rest} - {band[t]}")
+        srt = np.sort(logits64[t])[::-1]
+        gap = srt[K - 1] - srt[K] if E > K else np.inf
+        if gap > band[t]:
+            assert sorted(sg) == sorted(orc_idx[t].tolist()), f"token {t}: {sg} vs oracle {orc_idx[t]}"
+            if gpu_w is not None:
+                ow = dict(zip(orc_idx[t].tolist(), orc_w[t].tolist()))
+                for e, wv in zip(sg, gpu_w[t].tolist()):
+                    assert abs(wv - ow[e]) <= w_atol, f"token {t} expert {e}: w {wv} vs {ow[e]}"
+            n_exact += 1
+        else:
+            n_amb += 1
+        if gpu_w is not None:
+            assert abs(float(np.sum(gpu_w[t])) - 1.0) < 1e-5
+    return n_exact, n_amb
+
+
+def rel_l2(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Per-row relative L2 error of a against reference b."""
+    a = np.asarray(a, dtype=np.float64).reshape(len(b), -1)
+    b = np.asarray(b, dtype=np.float64).reshape(len(b), -1)
+    return np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-300)

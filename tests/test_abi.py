@@ -1,0 +1,119 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point declared in include/moe.h, and rejects bad arguments on the host with
+the documented status codes before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_decode_route_amd import binding as B
+from sparse_moe_decode_route_amd import inputs as gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, ALIGNMENT = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.SO_PATH):
+        from sparse_moe_decode_route_amd import build
+        build.build()
+    return B.lib()
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ("moe_route_topk", "moe_expert_ffn_q4", "moe_layer_forward"):
+        assert required in names
+    assert set(names) == set(B.ENTRY_POINTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def _d(**kw):
+    base = dict(d_model=2048, d_ff=512, n_routed=256, n_shared=1, top_k=6, wfmt=1)
+    base.update(kw)
+    return B.CDims(**base)
+
+
+def test_sizes(L):
+    d = _d()
+    assert L.moe_packed_expert_bytes(ctypes.byref(d)) == 1_966_080
+    d4 = _d(wfmt=2)
+    assert L.moe_packed_expert_bytes(ctypes.byref(d4)) == 1_769_472
+    db = _d(d_model=512, d_ff=128, wfmt=0)
+    assert L.moe_packed_expert_bytes(ctypes.byref(db)) == 393_216
+    n = ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n)) == OK and n.value > 0
+    assert L.moe_workspace_size(ctypes.byref(d), 4096, ctypes.byref(n)) == OK
+
+
+@pytest.mark.parametrize("bad", [dict(d_model=48), dict(d_model=0), dict(d_ff=8200), dict(n_routed=300),
+                                 dict(top_k=0), dict(top_k=9), dict(n_routed=4, top_k=6), dict(n_shared=5)])
+def test_bad_dims_rejected(L, bad):
+    d = _d(**bad)
+    n = ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n)) == INVALID
+    assert L.moe_packed_expert_bytes(ctypes.byref(d)) == 0
+    assert L.moe_last_error()
+
+
+def test_unknown_format_rejected(L):
+    d = _d(wfmt=7)
+    n = ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(n)) == UNSUPPORTED
+
+
+def test_entry_points_validate_before_enqueue(L):
+    d = _d()
+    fake = ctypes.c_void_p(0x10000)       # never dereferenced: every call below fails validation
+    odd = ctypes.c_void_p(0x10004)        # misaligned
+    w = B.CLayerWeights(0x10000, 0, 0x20000, 0)
+    wnull = B.CLayerWeights(0, 0, 0x20000, 0)
+    # NULL x
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), None, 0, 1, fake, None, None, fake, 1 << 30, None) == INVALID
+    # NULL router
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(wnull), fake, 0, 1, fake, None, None, fake, 1 << 30, None) == INVALID
+    # misaligned y
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, 0, 1, odd, None, None, fake, 1 << 30, None) == ALIGNMENT
+    # workspace too small / missing
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, 0, 1, fake, None, None, fake, 16, None) == WORKSPACE
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, 0, 1, fake, None, None, None, 0, None) == WORKSPACE
+    # bad token counts and activation type
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, 0, 0, fake, None, None, fake, 1 << 30, None) == INVALID
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, 5, 1, fake, None, None, fake, 1 << 30, None) == UNSUPPORTED
+    assert L.moe_expert_ffn_q4(ctypes.byref(d), fake, 0, 9, fake, None, fake, fake, fake, fake, 1 << 30, None) == INVALID
+    # NVFP4 needs tensor scales
+    d4 = _d(wfmt=2)
+    assert L.moe_expert_ffn_q4(ctypes.byref(d4), fake, 0, 1, fake, None, fake, fake, fake, fake, 1 << 30, None) == INVALID
+    assert L.moe_route_topk(ctypes.byref(d), fake, 0, 70000, fake, None, fake, fake, None, fake, 1 << 30, None) == INVALID
+    assert L.moe_stack_decode(ctypes.byref(d), 0, ctypes.byref(w), fake, 1, fake, None, None, fake, 1 << 30, None) == INVALID
+    assert L.moe_stack_decode(ctypes.byref(d), 1, ctypes.byref(w), fake, 9, fake, None, None, fake, 1 << 30, None) == INVALID
+    # overlapping repack buffers
+    assert L.moe_repack_weights(ctypes.byref(d), fake, fake, 1, None) == INVALID
+    assert L.moe_repack_weights(ctypes.byref(d), fake, ctypes.c_void_p(0x90000000), 0, None) == INVALID
+    assert b"n_experts" in L.moe_last_error()
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.moe_status_string(s)
+
+
+def test_binding_error_carries_message(L):
+    dims = gen.LayerDims(48, 64)
+    with pytest.raises(B.MoeError) as e:
+        B.workspace_size(dims, 1)
+    assert "d_model" in str(e.value)

@@ -407,3 +407,31 @@ def test_stack_is_layer_composition(orc):
         np.testing.assert_array_equal(itrace[l], idx)
         x = orc.rmsnorm(yl[0])[None]
     np.testing.assert_array_equal(y, trace[-1])
+
+
+def test_experts_given_matches_layer_on_own_routing(orc):
+    dims = gen.LayerDims(64, 32, n_routed=16, n_shared=1, top_k=6, wfmt="nvfp4")
+    layer = gen.make_layer(dims, cfg_id=83)
+    x = gen.make_hidden(83, 3, 64).double().numpy()
+    idx, w, _, y = orc.layer_forward(layer, x)
+    y2 = orc.experts_given(layer, x, idx, w)
+    np.testing.assert_allclose(y2, y, rtol=1e-12, atol=1e-15)
+
+
+def test_experts_given_constant_closed_form(orc):
+    dims = gen.LayerDims(64, 32, n_routed=8, n_shared=1, top_k=2, wfmt="q4_1")
+    rng = np.random.default_rng(10)
+    consts = [[float(np.float16(v)) for v in rng.uniform(-0.05, 0.05, 3)] for _ in range(9)]
+    layer = _const_q4_1_layer(dims, consts)
+    x = rng.normal(size=(1, 64))
+    idx = np.array([[7, 2]])
+    w = np.array([[0.75, -0.5]])
+    y = orc.experts_given(layer, x, idx, w)
+    S = x[0].sum()
+
+    def out(e):
+        cg, cu, cd = consts[e]
+        g, u = cg * S, cu * S
+        return cd * 32 * (g / (1 + math.exp(-g)) * u)
+
+    np.testing.assert_allclose(y[0], np.full(64, out(8) + 0.75 * out(7) - 0.5 * out(2)), rtol=1e-12)
