@@ -149,6 +149,13 @@ moe_status decode_input(const moe_dims &d, const void *x, int act, int T, void *
     return MOE_OK;
 }
 
+// The batch-1 path when the shape fits it, the general decode path otherwise.
+hipError_t launch_any(const moe::DecodeParams &p, hipStream_t st) {
+    hipError_t e = moe::launch_decode_b1(p, st);
+    if (e == hipErrorNotSupported) return moe::launch_decode(p, st);
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,7 +295,7 @@ moe_status moe_layer_forward(const moe_dims *d, const moe_layer_weights *w, cons
     p.want_router = 1;
     p.want_shared = 1;
     p.y = y;
-    return hip_status(moe::launch_decode(p, st), "layer launch");
+    return hip_status(launch_any(p, st), "layer launch");
 }
 
 moe_status moe_layer_forward_prefill(const moe_dims *d, const moe_layer_weights *w, const void *x, int32_t act,
@@ -364,7 +371,13 @@ moe_status moe_stack_decode(const moe_dims *d, int32_t n_layers, const moe_layer
         else
             out = at<float>(ws, (l & 1) ? L.ybuf1 : L.ybuf0);
         p.y = out;
-        MOE_TRY(hip_status(moe::launch_decode(p, st), "stack layer launch"));
+        if (l + 1 < n_layers) {
+            p.next_router = static_cast<const uint8_t *>(layers[l + 1].router);
+            p.next_router_bytes = (size_t)d->n_routed * d->d_model * 2;
+            p.next_shared = static_cast<const uint8_t *>(layers[l + 1].experts) + (size_t)d->n_routed * p.expert_bytes;
+            p.next_shared_bytes = (size_t)d->n_shared * p.expert_bytes;
+        }
+        MOE_TRY(hip_status(launch_any(p, st), "stack layer launch"));
         prev = out;
     }
     if (y_trace)

@@ -147,54 +147,6 @@ __global__ void __launch_bounds__(MOE_WAVE) phase_a_kernel(DecodeParams p) {
     }
 }
 
-// Top-k of one token's logits by one wave: (value descending, index
-// ascending); weights w_i = exp(l_i - l_0) / sum_j exp(l_j - l_0), which is
-// the softmax over all experts renormalised over the chosen ones.  Lane i < K
-// returns slot i in *e_out / *w_out.
-__device__ void wave_topk(const float *l, int E, int K, int *e_out, float *w_out) {
-    const int lane = threadIdx.x & (MOE_WAVE - 1);
-    float v[4];
-    int ix[4];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        ix[k] = lane + 64 * k;
-        v[k] = ix[k] < E ? l[ix[k]] : -INFINITY;
-    }
-    float lsel = 0.f, l0 = 0.f;
-    int esel = 0;
-    for (int i = 0; i < K; i++) {
-        float bv = v[0];
-        int bi = ix[0];
-#pragma unroll
-        for (int k = 1; k < 4; k++)
-            if (v[k] > bv) {  // strict: the lower index keeps ties
-                bv = v[k];
-                bi = ix[k];
-            }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            float ov = __shfl_xor(bv, o, MOE_WAVE);
-            int oi = __shfl_xor(bi, o, MOE_WAVE);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if (i == 0) l0 = bv;
-        if (lane == i) {
-            lsel = bv;
-            esel = bi;
-        }
-#pragma unroll
-        for (int k = 0; k < 4; k++)
-            if (ix[k] == bi) v[k] = -INFINITY;
-    }
-    float ev = lane < K ? __expf(lsel - l0) : 0.f;
-    float den = group_sum<MOE_WAVE>(ev);
-    *e_out = esel;
-    *w_out = ev / den;
-}
-
 // Decode selection (T <= 8, one block): top-k per token (or the caller's
 // routing), then the union of chosen experts: shared experts first, then
 // routed experts in ascending index with a bitmask of the tokens using them.

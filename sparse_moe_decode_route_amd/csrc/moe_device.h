@@ -1,6 +1,7 @@
 // Device helpers for libmoe (gfx950, wave64): weight-unit decoding and
 // wave reductions.  Formats as defined by the device layout in moe.h.
 #pragma once
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -166,15 +167,115 @@ __device__ __forceinline__ float unit_dot(const WUnit &w, const XUnit<FMT> &x, f
     }
 }
 
-// Sum over groups of LPR consecutive lanes (LPR a power of two <= 64); every
-// lane of a group ends with the same value.
+// DPP lane exchange within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+constexpr int DPP_XOR1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within each 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within each 16
+
+// Sum over groups of LPR consecutive lanes (LPR a power of two <= 64).  Each
+// step pairs every lane with one partner of the same group and adds, so all
+// lanes of a group end with the same value, in a fixed order.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+    if (LPR >= 2) v += dpp_f<DPP_XOR1>(v);
+    if (LPR >= 4) v += dpp_f<DPP_XOR2>(v);
+    if (LPR >= 8) v += dpp_f<DPP_HALF_MIRROR>(v);
+    if (LPR >= 16) v += dpp_f<DPP_MIRROR>(v);
+    if (LPR >= 32) v += __shfl_xor(v, 16, MOE_WAVE);
+    if (LPR >= 64) v += __shfl_xor(v, 32, MOE_WAVE);
     return v;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key, -0 is
+// folded into +0 first so that the two compare equal as floats do); key 0
+// is below every float key, including -inf.
+__device__ __forceinline__ uint32_t f2key(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// max with a DPP-exchanged copy (lanes whose source is invalid read 0).
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true));
+}
+// rows enabled in ROW_MASK take the max with lane 15 (0x142) or lane 31
+// (0x143) of the wave; other rows keep their value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t max_bcast(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false));
+}
+
+// Largest key of the wave, valid in every lane (read back from lane 63).
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
+    v = max_dpp<DPP_XOR1>(v);
+    v = max_dpp<DPP_XOR2>(v);
+    v = max_dpp<DPP_HALF_MIRROR>(v);
+    v = max_dpp<DPP_MIRROR>(v);
+    v = max_bcast<0x142, 0xA>(v);
+    v = max_bcast<0x143, 0xC>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top-k of one token's logits by one wave: (value descending, index
+// ascending), decided on the fp32 logits; weights w_i = exp(l_i - l_0) /
+// sum_j exp(l_j - l_0), the softmax over all experts renormalised over the
+// chosen ones.  Lane i < K returns slot i (its expert in *e_out, its weight
+// in *w_out); other lanes return expert 0, weight 0.  Each round takes the
+// wave's largest key, then the lowest expert index holding it (ballots over
+// index = lane + 64k, k ascending).  No per-thread arrays: an array indexed
+// by the lane would be moved to LDS and need the dispatch packet (in host
+// memory) to compute thread offsets.
+__device__ __forceinline__ void wave_topk(const float *l, int E, int K, int *e_out, float *w_out) {
+    const int lane = threadIdx.x & (MOE_WAVE - 1);
+    // four loads issued back to back; the opaque copy keeps the compiler from
+    // sinking a load into the (ix < E) branch, which would serialise them
+    float lv[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) lv[k] = l[min(lane + 64 * k, E - 1)];
+    uint32_t key[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const int ix = lane + 64 * k;
+        const float v = __uint_as_float(opaque(__float_as_uint(lv[k])));
+        key[k] = ix < E ? f2key(v) : 0u;
+    }
+    int my_e = 0;
+    uint32_t my_key = 0, first_key = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const uint32_t m = wave_max_key(max(max(key[0], key[1]), max(key[2], key[3])));
+        int gi = 0;
+#pragma unroll
+        for (int k = 3; k >= 0; k--) {
+            const uint64_t b = __ballot(key[k] == m);
+            gi = b ? 64 * k + (int)__builtin_ctzll(b) : gi;
+        }
+        if (i == 0) first_key = m;
+        my_e = (lane == i) ? gi : my_e;
+        my_key = (lane == i) ? m : my_key;
+#pragma unroll
+        for (int k = 0; k < 4; k++) key[k] = (lane + 64 * k == gi) ? 0u : key[k];
+        if (i + 1 >= K) break;
+    }
+    const float ev = lane < K ? __expf(key2f(my_key) - key2f(first_key)) : 0.f;
+    const float den = group_sum<MOE_WAVE>(ev);
+    *e_out = lane < K ? my_e : 0;
+    *w_out = ev / den;
+}
 
 }  // namespace moe

@@ -34,9 +34,19 @@ struct DecodeParams {
     float *act_w;        // [amax, T] combine weight of each token (0 if absent)
     float *h;            // [amax, T, F]
     float *y;            // [T, D]
+    // weights of the next layer (stacks), touched during this layer's down
+    // projection so that they are on chip when the next layer starts
+    const uint8_t *next_router;
+    size_t next_router_bytes;
+    const uint8_t *next_shared;
+    size_t next_shared_bytes;
+    int32_t sink_flag;   // always 0: keeps prefetch loads alive
 };
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
+// Batch-1 path (three kernels per layer); hipErrorNotSupported if the shape
+// is outside what it was built for (the caller then takes launch_decode).
+hipError_t launch_decode_b1(const DecodeParams &p, hipStream_t st);
 hipError_t launch_route_only(const DecodeParams &p, hipStream_t st);
 hipError_t launch_bf16_to_f32(const uint16_t *in, float *out, int n, hipStream_t st);
 hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *idx, float *w, hipStream_t st);

@@ -194,3 +194,58 @@ def test_stack_teacher_forced_and_end_to_end():
         err = rel_l2(y, oy_end)
         print(f"[stack] end-to-end rel-L2 {err.max():.3e}")
         assert err.max() <= REL_L2_TOL
+
+
+# --------------------------------------------------------------------------- batch-1 path variants
+
+@pytest.mark.parametrize("dims", [
+    gen.LayerDims(512, 128, wfmt="bf16"),                                  # bf16 units, 16 lanes per down row
+    gen.LayerDims(4096, 256, n_routed=64, n_shared=1, top_k=6, wfmt="q4_1"),  # two units per lane, 8 lanes per row
+    gen.LayerDims(2048, 1024, n_routed=32, n_shared=0, top_k=4, wfmt="nvfp4"),  # no shared expert, 32 lanes per row
+    gen.LayerDims(1024, 2048, n_routed=48, n_shared=2, top_k=6, wfmt="q4_1"),   # two shared experts, 64 lanes per row
+], ids=["bf16", "q4_1-upl2", "nvfp4-noshared", "q4_1-2shared"])
+def test_batch1_path_shapes(dims):
+    host, dl = _layer(dims, 43)
+    for draw in range(3):
+        x = gen.make_hidden(43, 1, dims.d_model, draw=draw)
+        err, _, _ = _run_layer_case(host, dl, x, f"b1 {dims}")
+        assert err.max() <= FP32_PATH_TOL
+
+
+def test_batch1_equal_logits_choose_lowest_indices():
+    dims = gen.LayerDims(2048, 512, n_routed=64, n_shared=1, top_k=6, wfmt="q4_1")
+    host, dl = _layer(dims, 44, router_zero=True)
+    x = gen.make_hidden(44, 1, 2048)
+    y, idx, w = B.layer_forward(dl, x.to(_dev()))
+    torch.cuda.synchronize()
+    assert idx.cpu().numpy().tolist() == [[0, 1, 2, 3, 4, 5]]
+    np.testing.assert_allclose(w.cpu().numpy(), np.full((1, 6), 1 / 6), rtol=1e-6)
+    _, _, _, oy = oracle.layer_forward(host, x.double().numpy())
+    assert rel_l2(y.cpu().numpy(), oy).max() <= FP32_PATH_TOL
+
+
+def test_stack_graph_replays_match_eager():
+    """A captured stack step replayed several times equals the eager call each time."""
+    dims = gen.LayerDims(1024, 256, n_routed=32, n_shared=1, top_k=6, wfmt="q4_1")
+    devs = [_layer(dims, 45, layer=l)[1] for l in range(3)]
+    stack = B.StackHandle(devs)
+    xs = gen.make_hidden(45, 4, 1024, device=_dev())
+    x_static = torch.empty((1, 1024), device=_dev())
+    y_static = torch.empty((1, 1024), device=_dev())
+    ws = B.workspace(dims, 1)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.stack_decode(stack, x_static, ws=ws, y=y_static)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.stack_decode(stack, x_static, ws=ws, y=y_static)
+    for i in range(4):
+        x_static.copy_(xs[i:i + 1])
+        g.replay()
+        torch.cuda.synchronize()
+        got = y_static.clone()
+        ref, _, _ = B.stack_decode(stack, xs[i:i + 1].contiguous(), ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), i
