@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=47)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=47, help="layers in the CPU baseline sample")
+    ap.add_argument("--timed-calls", type=int, default=20,
+                    help="eager stack calls with per-kernel dispatch events (the roofline's kernel timing)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy five times (reference kernel for HBM counters)")
     return ap.parse_args()
 
 
@@ -72,6 +76,76 @@ def union_bytes(idx_trace: np.ndarray, dims, expert_bytes: int) -> float:
     for l in range(idx_trace.shape[0]):
         tot += len(set(idx_trace[l].reshape(-1).tolist())) + dims.n_shared
     return tot / idx_trace.shape[0] * expert_bytes
+
+
+def source_digest() -> str:
+    """Digest of the decode kernels' sources: stored counter readings apply only to this source."""
+    import hashlib
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_decode_route_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("moe_decode_b1.hip", "moe_decode.hip", "moe_device.h", "moe_internal.h"):
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# HBM traffic per launch read from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
+# script (one run per counter), each scaled by the same counter's reading for a
+# plain device copy of known size; keyed by (workload, kernel) and valid only for
+# the kernel source digest it was taken on.
+COUNTER_TRAFFIC = {}
+
+
+def kernel_algo_bytes(dims, T: int, routed_union: float):
+    """Algorithmic bytes one launch of each decode kernel must move.
+
+    Weights: packed bytes of the matrices the kernel reads (router bf16; gate
+    and up of the shared experts in the first kernel, of the routed union in
+    the gate/up kernel; down of every active expert in the last).  Activations:
+    fp32 x in, logits, h and y as produced and consumed between kernels."""
+    from sparse_moe_decode_route_amd import inputs as gen
+    D, F, E, S = dims.d_model, dims.d_ff, dims.n_routed, dims.n_shared
+    gu = gen.matrix_bytes(F, D, dims.wfmt)
+    dn = gen.matrix_bytes(D, F, dims.wfmt)
+    U = routed_union
+    a = E * D * 2 + S * 2 * gu + T * D * 4 + T * E * 4 + S * T * F * 4
+    b = T * E * 4 + U * 2 * gu + T * D * 4 + U * T * F * 4
+    c = (U + S) * dn + (U + S) * T * F * 4 + T * D * 4
+    return {"b1_route_shared": a, "b1_topk_gateup": b, "b1_down": c,
+            "phase_a_kernel": a, "select_kernel": T * E * 4, "gateup_kernel": b, "down_kernel": c}
+
+
+def time_kernels(args, stack, xs, ws, dims, T):
+    """Per-kernel mean dispatch durations over --timed-calls eager stack calls (fresh token each)."""
+    from sparse_moe_decode_route_amd import binding as B
+    n = max(1, args.timed_calls)
+    tot, unions = {}, []
+    for i in range(n):
+        _, itr, us = B.stack_decode_timed(stack, xs[i % xs.shape[0]].contiguous(), ws=ws, trace=True)
+        for k, v in us.items():
+            tot[k] = tot.get(k, 0.0) + v
+        it = itr.cpu().numpy()
+        unions.append(np.mean([len(set(it[l].reshape(-1).tolist())) for l in range(it.shape[0])]))
+    return {k: v / n for k, v in tot.items()}, float(np.mean(unions))
+
+
+def roofline(workload, dims, T, kernel_us, routed_union):
+    algo = kernel_algo_bytes(dims, T, routed_union)
+    dom = max(kernel_us, key=lambda k: kernel_us[k])
+    us = kernel_us[dom]
+    achieved = algo[dom] / (us * 1e-6) / 1e9
+    tr = COUNTER_TRAFFIC.get((workload, dom))
+    traffic = None
+    if tr is not None and tr["source_digest"] == source_digest():
+        traffic = tr["fetch_bytes"] + tr["write_bytes"]
+    kernels = {k: dict(us_per_launch=round(v, 3), algo_bytes_per_launch=round(algo[k]),
+                       gbs=round(algo[k] / (v * 1e-6) / 1e9, 1)) for k, v in kernel_us.items()}
+    return dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                algo_bytes_per_launch=round(algo[dom]), us_per_launch=round(us, 3),
+                timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream, "
+                       "mean over every launch of the eager timed calls",
+                per_kernel=kernels)
 
 
 def bench_stack(args, wfmt: str, T: int):
@@ -134,8 +208,11 @@ def bench_stack(args, wfmt: str, T: int):
 
     router_b = dims.n_routed * dims.d_model * 2
     algo_bytes_step = L * (bytes_per_layer + router_b)
-    achieved = algo_bytes_step / (ms * 1e-3) / 1e9
+    step_gbs = algo_bytes_step / (ms * 1e-3) / 1e9
     expert_gbs = L * bytes_per_layer / (ms * 1e-3) / 1e9
+    workload = f"stack_{wfmt}_b{T}"
+    kernel_us, routed_union = time_kernels(args, stack, xs, ws, dims, T)
+    log(f"per-kernel us: {kernel_us}, routed union {routed_union:.2f}")
     out = dict(
         metric="MoE-layer decode tokens/s + achieved HBM GB/s (% of peak), 4-bit, batch 1",
         value=round(layer_tok_s, 1), unit="MoE-layer tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -147,9 +224,9 @@ def bench_stack(args, wfmt: str, T: int):
                     layers=L, stack_tok_s=round(T / (ms * 1e-3), 2),
                     expert_bytes_per_layer=round(bytes_per_layer), router_bytes_per_layer=router_b,
                     expert_gbs=round(expert_gbs, 1), expert_frac_of_peak=round(expert_gbs / HBM_PEAK_GBS, 4),
-                    graph_matches_eager=graph_matches_eager),
-        roofline=dict(bound="hbm", kernel="moe_stack_decode (all kernels of one step)", achieved=round(achieved, 1),
-                      peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None),
+                    step_gbs_incl_router=round(step_gbs, 1), graph_matches_eager=graph_matches_eager,
+                    kernel_source_digest=source_digest()),
+        roofline=roofline(workload, dims, T, kernel_us, routed_union),
     )
     if want_cpu:
         out["cpu_baseline"] = cpu_baseline_stack(args, hosts, xs, dims, stack, ws)
@@ -166,17 +243,36 @@ def cpu_baseline_stack(args, hosts, xs, dims, stack, ws):
     t0 = time.time()
     y, ytr, itr = oracle.stack_forward(hosts[:n], x0)
     dt = time.time() - t0
-    # parity of this sample: GPU stack over the same layers and token
+    # parity of this sample: GPU stack over the same layers and token, end to end,
+    # and at the first layer whose selection differs, the oracle's fp64 logit gap
+    # between the k-th and (k+1)-th expert on the GPU's own input to that layer
     sub = B.StackHandle(stack.layers[:n])
-    yg, _, ig = B.stack_decode(sub, xs[0].contiguous(), ws=ws, trace=True)
+    yg, ytr_g, ig = B.stack_decode(sub, xs[0].contiguous(), ws=ws, trace=True)
     torch.cuda.synchronize()
-    same_route = bool(np.array_equal(ig.cpu().numpy(), itr))
+    ig = ig.cpu().numpy()
+    same = [bool(np.array_equal(np.sort(ig[l], axis=-1), np.sort(itr[l], axis=-1))) for l in range(n)]
+    first_diff = next((l for l in range(n) if not same[l]), None)
     yg = yg.cpu().double().numpy()
-    err = float(np.linalg.norm(yg - y) / np.linalg.norm(y)) if same_route else None
+    err = float(np.linalg.norm(yg - y) / np.linalg.norm(y)) if first_diff is None else None
+    gap, tf_match = None, None
+    ytr_g = ytr_g.cpu().double().numpy()
+    # relative difference of the two chains' layer outputs (fp32 GPU vs fp64 oracle): how far
+    # the hidden states have drifted apart by the time a selection differs
+    drift = [float(np.linalg.norm(ytr_g[l] - ytr[l]) / np.linalg.norm(ytr[l])) for l in range(n)]
+    if first_diff is not None:
+        xin = x0 if first_diff == 0 else oracle.rmsnorm(ytr_g[first_diff - 1])
+        oi, _, lg, _ = oracle.layer_forward(hosts[first_diff], xin)
+        srt = np.sort(lg[0])[::-1]
+        gap = float(srt[dims.top_k - 1] - srt[dims.top_k])
+        tf_match = bool(np.array_equal(np.sort(oi[0]), np.sort(ig[first_diff][0])))
     return dict(value=round(n / dt, 3), unit="MoE-layer tok/s", cores=1, kind="oracle",
                 sample=f"1 token through {n} q4_1 layers (d_model 2048, d_ff 512, 256+1 experts), fp64 C, "
                        f"one thread, {dt:.1f}s",
-                gpu_vs_oracle=dict(same_routing_all_layers=same_route, rel_l2_final=err))
+                gpu_vs_oracle=dict(layers_same_routing=int(sum(same)), layers=n, first_divergent_layer=first_diff,
+                                   oracle_topk_gap_at_divergence=gap,
+                                   teacher_forced_selection_matches_at_divergence=tf_match,
+                                   hidden_drift_by_layer=[float(f"{v:.2e}") for v in drift[:(first_diff or n) + 1]],
+                                   rel_l2_final=err))
 
 
 def bench_prefill(args):
@@ -203,7 +299,21 @@ def main():
         out = bench_stack(args, "nvfp4", 8)
     else:
         out = bench_prefill(args)
+    if args.copy_calibration:
+        copy_calibration()
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration():
+    """A plain device copy of 256 MiB, five times: the reference kernel whose
+    FETCH_SIZE / WRITE_SIZE readings scale the counters of the decode kernels."""
+    n = 64 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 5 x {n * 4} bytes read and written")
 
 
 if __name__ == "__main__":

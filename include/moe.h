@@ -109,7 +109,7 @@ moe_status moe_repack_weights(const moe_dims *dims, const void *canonical, void 
                               void *stream);
 
 /*
- * Router and selection (rows a1-a2 of the path).  For each token:
+ * Router and selection.  For each token:
  * logits = x Wr^T (+ bias) in fp32; softmax over n_routed; the top_k
  * experts by (logit descending, index ascending); renormalised weights.
  *   x          [n_tokens, d_model], fp32 (act = MOE_ACT_F32) or bf16
@@ -125,7 +125,7 @@ moe_status moe_route_topk(const moe_dims *dims, const void *x, int32_t act, int3
                           size_t ws_bytes, void *stream);
 
 /*
- * Expert FFN over given routing (rows a3-a5): for each token
+ * Expert FFN over given routing: for each token
  * y = sum_shared expert_s(x) + sum_i topk_w[i] * expert_{topk_idx[i]}(x),
  * streaming each distinct expert's 4-bit (or bf16) weights once per call and
  * applying it to all tokens that chose it.  Decode sizes: 1 <= n_tokens <= 8.
@@ -152,7 +152,7 @@ moe_status moe_layer_forward(const moe_dims *dims, const moe_layer_weights *w, c
                              size_t ws_bytes, void *stream);
 
 /*
- * Prefill path for any n_tokens (rows a8-a10): route all tokens, permute
+ * Prefill path for any n_tokens: route all tokens, permute
  * (token, slot) pairs by expert (histogram, scan, scatter), run the experts
  * as a grouped GEMM on the matrix cores (fp16 operands, fp32 accumulate),
  * and combine each token's slots in a fixed order.
@@ -162,7 +162,7 @@ moe_status moe_layer_forward_prefill(const moe_dims *dims, const moe_layer_weigh
                                      float *topk_w_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * A stack of n_layers layers (row a6): x_0 = x0 (fp32 [n_tokens, d_model]),
+ * A stack of n_layers layers: x_0 = x0 (fp32 [n_tokens, d_model]),
  * y_l = layer_l(x_l), x_{l+1} = y_l / sqrt(mean(y_l^2) + 1e-6) per token;
  * y receives y_{n_layers-1}.  layers is a host array of n_layers structs.
  * y_trace fp32 [n_layers, n_tokens, d_model] and idx_trace int32
@@ -172,6 +172,28 @@ moe_status moe_layer_forward_prefill(const moe_dims *dims, const moe_layer_weigh
 moe_status moe_stack_decode(const moe_dims *dims, int32_t n_layers, const moe_layer_weights *layers,
                             const float *x0, int32_t n_tokens, float *y, float *y_trace, int32_t *idx_trace,
                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Measurement variant of moe_stack_decode (no y_trace): the same kernels,
+ * each launched with a start/stop event pair that takes the dispatch's own
+ * begin and end timestamps, so the durations match a kernel trace.  The
+ * pages time whole-model decode only (tokens/s on the two named machines);
+ * this call gives the per-kernel split of the decode step that those
+ * figures are made of.  Blocks the calling thread until the stack is done.
+ *   kernel_us  (host) float [4]: mean duration in microseconds of each
+ *              kernel slot of a layer, averaged over the n_layers layers
+ *              (-1 for a slot that did not run).
+ *   n_kernels  (host) receives the number of slots used (3 on the batch-1
+ *              path, 4 on the general path).
+ *   names      (host, optional) receives the slots' kernel names separated
+ *              by ';' (truncated to names_cap bytes, NUL-terminated).
+ * Creates and destroys 8 * n_layers HIP events (n_layers <= 4096); not for
+ * use under stream capture.
+ */
+moe_status moe_stack_decode_timed(const moe_dims *dims, int32_t n_layers, const moe_layer_weights *layers,
+                                  const float *x0, int32_t n_tokens, float *y, int32_t *idx_trace, void *ws,
+                                  size_t ws_bytes, float *kernel_us, int32_t *n_kernels, char *names,
+                                  size_t names_cap, void *stream);
 
 /* (host) static description of a status code. */
 const char *moe_status_string(moe_status s);

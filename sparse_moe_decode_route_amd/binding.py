@@ -23,7 +23,7 @@ ACT_F32, ACT_BF16 = 0, 1
 ENTRY_POINTS = (
     "moe_packed_expert_bytes", "moe_workspace_size", "moe_repack_weights", "moe_route_topk",
     "moe_expert_ffn_q4", "moe_layer_forward", "moe_layer_forward_prefill", "moe_stack_decode",
-    "moe_status_string", "moe_last_error",
+    "moe_stack_decode_timed", "moe_status_string", "moe_last_error",
 )
 
 
@@ -71,6 +71,10 @@ def lib():
         L.moe_layer_forward_prefill.argtypes = L.moe_layer_forward.argtypes
         L.moe_stack_decode.restype = ctypes.c_int
         L.moe_stack_decode.argtypes = [pd, i32, ctypes.POINTER(CLayerWeights), vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_stack_decode_timed.restype = ctypes.c_int
+        L.moe_stack_decode_timed.argtypes = [pd, i32, ctypes.POINTER(CLayerWeights), vp, i32, vp, vp, vp, sz,
+                                             ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32), ctypes.c_char_p,
+                                             sz, vp]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_last_error.restype = ctypes.c_char_p
@@ -228,3 +232,25 @@ def stack_decode(stack: StackHandle, x0: torch.Tensor, ws: Optional[torch.Tensor
     _check(lib().moe_stack_decode(ctypes.byref(d), L, stack.carr, _ptr(x0), T, _ptr(y), _ptr(y_trace),
                                   _ptr(idx_trace), _ptr(ws), ws.numel(), _stream(stream)))
     return y, y_trace, idx_trace
+
+
+def stack_decode_timed(stack: StackHandle, x0: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                       y: Optional[torch.Tensor] = None, trace: bool = False, stream=None):
+    """moe_stack_decode_timed: returns (y, idx_trace or None, {kernel name: mean us per launch}).
+
+    Synchronises the stream (the call waits for its own events)."""
+    dims = stack.dims
+    T = x0.shape[0]
+    L = len(stack.layers)
+    dev = x0.device
+    y = y if y is not None else torch.empty((T, dims.d_model), dtype=torch.float32, device=dev)
+    idx_trace = torch.empty((L, T, dims.top_k), dtype=torch.int32, device=dev) if trace else None
+    ws = ws if ws is not None else workspace(dims, T, dev)
+    d = cdims(dims)
+    us = (ctypes.c_float * 4)()
+    nk = ctypes.c_int32(0)
+    names = ctypes.create_string_buffer(256)
+    _check(lib().moe_stack_decode_timed(ctypes.byref(d), L, stack.carr, _ptr(x0), T, _ptr(y), _ptr(idx_trace),
+                                        _ptr(ws), ws.numel(), us, ctypes.byref(nk), names, 256, _stream(stream)))
+    keys = names.value.decode().split(";")
+    return y, idx_trace, {keys[k]: float(us[k]) for k in range(nk.value)}

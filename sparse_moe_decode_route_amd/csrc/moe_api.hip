@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
@@ -150,11 +151,20 @@ moe_status decode_input(const moe_dims &d, const void *x, int act, int T, void *
 }
 
 // The batch-1 path when the shape fits it, the general decode path otherwise.
-hipError_t launch_any(const moe::DecodeParams &p, hipStream_t st) {
+// *path (optional) receives 1 for the batch-1 path, 2 for the general one.
+hipError_t launch_any(const moe::DecodeParams &p, hipStream_t st, int *path = nullptr) {
     hipError_t e = moe::launch_decode_b1(p, st);
-    if (e == hipErrorNotSupported) return moe::launch_decode(p, st);
+    if (path) *path = 1;
+    if (e == hipErrorNotSupported) {
+        if (path) *path = 2;
+        return moe::launch_decode(p, st);
+    }
     return e;
 }
+
+// Kernel names of one layer's slots, per path (slot order of MOE_LAUNCH).
+const char *const kB1Names = "b1_route_shared;b1_topk_gateup;b1_down";
+const char *const kGenericNames = "phase_a_kernel;select_kernel;gateup_kernel;down_kernel";
 
 }  // namespace
 
@@ -334,9 +344,15 @@ moe_status moe_layer_forward_prefill(const moe_dims *d, const moe_layer_weights 
     return hip_status(moe::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
-moe_status moe_stack_decode(const moe_dims *d, int32_t n_layers, const moe_layer_weights *layers, const float *x0,
-                            int32_t n_tokens, float *y, float *y_trace, int32_t *idx_trace, void *ws,
-                            size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the stack entry points; ev (optional) holds
+// n_layers * 2 * MAX_KERNEL_SLOTS events, *path receives the decode path.
+moe_status stack_impl(const moe_dims *d, int32_t n_layers, const moe_layer_weights *layers, const float *x0,
+                      int32_t n_tokens, float *y, float *y_trace, int32_t *idx_trace, void *ws, size_t ws_bytes,
+                      hipStream_t st, hipEvent_t *ev, int *path) {
     MOE_TRY(check_dims(d));
     if (n_layers < 1) return fail(MOE_ERR_INVALID_ARG, "n_layers must be >= 1");
     if (n_tokens < 1 || n_tokens > moe::MAX_DECODE_T)
@@ -348,7 +364,6 @@ moe_status moe_stack_decode(const moe_dims *d, int32_t n_layers, const moe_layer
     MOE_TRY(check_ptr(y_trace, "y_trace", false));
     MOE_TRY(check_ptr(idx_trace, "idx_trace", false));
     MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
-    hipStream_t st = static_cast<hipStream_t>(stream);
     const DecodeWs L = decode_ws(*d, n_tokens);
     const size_t TD = (size_t)n_tokens * d->d_model;
     const float *prev = nullptr;
@@ -363,6 +378,7 @@ moe_status moe_stack_decode(const moe_dims *d, int32_t n_layers, const moe_layer
         p.idx_out = idx_trace ? idx_trace + (size_t)l * n_tokens * d->top_k : nullptr;
         p.want_router = 1;
         p.want_shared = 1;
+        p.ev = ev ? ev + (size_t)l * 2 * moe::MAX_KERNEL_SLOTS : nullptr;
         float *out;
         if (l == n_layers - 1)
             out = y;
@@ -371,18 +387,74 @@ moe_status moe_stack_decode(const moe_dims *d, int32_t n_layers, const moe_layer
         else
             out = at<float>(ws, (l & 1) ? L.ybuf1 : L.ybuf0);
         p.y = out;
-        if (l + 1 < n_layers) {
-            p.next_router = static_cast<const uint8_t *>(layers[l + 1].router);
-            p.next_router_bytes = (size_t)d->n_routed * d->d_model * 2;
-            p.next_shared = static_cast<const uint8_t *>(layers[l + 1].experts) + (size_t)d->n_routed * p.expert_bytes;
-            p.next_shared_bytes = (size_t)d->n_shared * p.expert_bytes;
-        }
-        MOE_TRY(hip_status(launch_any(p, st), "stack layer launch"));
+        MOE_TRY(hip_status(launch_any(p, st, path), "stack layer launch"));
         prev = out;
     }
     if (y_trace)
         MOE_TRY(hip_status(hipMemcpyAsync(y_trace + (size_t)(n_layers - 1) * TD, y, TD * 4, hipMemcpyDeviceToDevice, st),
                            "trace copy"));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_stack_decode(const moe_dims *d, int32_t n_layers, const moe_layer_weights *layers, const float *x0,
+                            int32_t n_tokens, float *y, float *y_trace, int32_t *idx_trace, void *ws,
+                            size_t ws_bytes, void *stream) {
+    return stack_impl(d, n_layers, layers, x0, n_tokens, y, y_trace, idx_trace, ws, ws_bytes,
+                      static_cast<hipStream_t>(stream), nullptr, nullptr);
+}
+
+moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe_layer_weights *layers,
+                                  const float *x0, int32_t n_tokens, float *y, int32_t *idx_trace, void *ws,
+                                  size_t ws_bytes, float *kernel_us, int32_t *n_kernels, char *names,
+                                  size_t names_cap, void *stream) {
+    if (!kernel_us || !n_kernels) return fail(MOE_ERR_INVALID_ARG, "kernel_us / n_kernels is NULL");
+    if (n_layers < 1 || n_layers > 4096) return fail(MOE_ERR_INVALID_ARG, "n_layers must be in [1, 4096]");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t n_ev = (size_t)n_layers * 2 * moe::MAX_KERNEL_SLOTS;
+    std::vector<hipEvent_t> ev(n_ev, nullptr);
+    auto destroy = [&]() {
+        for (hipEvent_t e : ev)
+            if (e) (void)hipEventDestroy(e);
+    };
+    for (size_t i = 0; i < n_ev; i++) {
+        if (hipEventCreate(&ev[i]) != hipSuccess) {
+            destroy();
+            return fail(MOE_ERR_HIP, "hipEventCreate failed");
+        }
+    }
+    int path = 0;
+    moe_status s = stack_impl(d, n_layers, layers, x0, n_tokens, y, nullptr, idx_trace, ws, ws_bytes, st,
+                              ev.data(), &path);
+    if (s == MOE_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(MOE_ERR_HIP, "stream synchronize failed");
+    if (s != MOE_OK) {
+        destroy();
+        return s;
+    }
+    const int slots = path == 1 ? 3 : moe::MAX_KERNEL_SLOTS;
+    for (int k = 0; k < slots; k++) {
+        double tot = 0.0;
+        int cnt = 0;
+        for (int l = 0; l < n_layers; l++) {
+            float ms = 0.f;
+            const size_t b = (size_t)l * 2 * moe::MAX_KERNEL_SLOTS + 2 * k;
+            if (hipEventElapsedTime(&ms, ev[b], ev[b + 1]) == hipSuccess) {
+                tot += ms;
+                cnt++;
+            }
+        }
+        kernel_us[k] = cnt ? (float)(tot / cnt * 1e3) : -1.f;
+    }
+    (void)hipGetLastError();  // elapsed-time queries of slots a layer did not launch
+    destroy();
+    *n_kernels = slots;
+    if (names && names_cap) {
+        const char *src = path == 1 ? kB1Names : kGenericNames;
+        snprintf(names, names_cap, "%s", src);
+    }
     return ok();
 }
 

@@ -305,15 +305,15 @@ static hipError_t launch_decode_t(const DecodeParams &p, hipStream_t st, bool ro
     const int per_expert = (p.F + GD * RG_GATEUP - 1) / (GD * RG_GATEUP);
     const int grid_a = (p.want_router ? p.E : 0) + (p.want_shared ? p.S * per_expert : 0);
     if (grid_a > 0)
-        hipLaunchKernelGGL((phase_a_kernel<FMT, LPR_D, RG_GATEUP, MAXT>), dim3(grid_a), dim3(MOE_WAVE), 0, st, p);
-    hipLaunchKernelGGL(select_kernel, dim3(1), dim3(512), 0, st, p);
+        MOE_LAUNCH(0, (phase_a_kernel<FMT, LPR_D, RG_GATEUP, MAXT>), dim3(grid_a), dim3(MOE_WAVE), st, p);
+    MOE_LAUNCH(1, select_kernel, dim3(1), dim3(512), st, p);
     if (route_only) return hipGetLastError();
     const int routed_slots = p.amax - p.S;
     if (routed_slots > 0)
-        hipLaunchKernelGGL((gateup_kernel<FMT, LPR_D, RG_GATEUP, MAXT>), dim3(routed_slots * per_expert),
-                           dim3(MOE_WAVE), 0, st, p);
+        MOE_LAUNCH(2, (gateup_kernel<FMT, LPR_D, RG_GATEUP, MAXT>), dim3(routed_slots * per_expert),
+                   dim3(MOE_WAVE), st, p);
     const int grid_d = (p.D + GF * RR_DOWN - 1) / (GF * RR_DOWN);
-    hipLaunchKernelGGL((down_kernel<FMT, LPR_F, RR_DOWN, MAXT>), dim3(grid_d), dim3(MOE_WAVE), 0, st, p);
+    MOE_LAUNCH(3, (down_kernel<FMT, LPR_F, RR_DOWN, MAXT>), dim3(grid_d), dim3(MOE_WAVE), st, p);
     return hipGetLastError();
 }
 

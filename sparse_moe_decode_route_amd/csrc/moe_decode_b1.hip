@@ -341,11 +341,11 @@ template <int FMT, int UPLD>
 hipError_t launch_fmt(const DecodeParams &p, hipStream_t st, int uplr, int lpr_f) {
     const int per_expert = p.F / B1_RG;
     const int grid_a = p.E + p.S * per_expert;
-#define MOE_A(U)                                                                                           \
-    if (p.x_prev)                                                                                          \
-        hipLaunchKernelGGL((b1_route_shared<FMT, U, UPLD, true>), dim3(grid_a), dim3(MOE_WAVE), 0, st, p); \
-    else                                                                                                   \
-        hipLaunchKernelGGL((b1_route_shared<FMT, U, UPLD, false>), dim3(grid_a), dim3(MOE_WAVE), 0, st, p);
+#define MOE_A(U)                                                                          \
+    if (p.x_prev)                                                                         \
+        MOE_LAUNCH(0, (b1_route_shared<FMT, U, UPLD, true>), dim3(grid_a), dim3(MOE_WAVE), st, p); \
+    else                                                                                  \
+        MOE_LAUNCH(0, (b1_route_shared<FMT, U, UPLD, false>), dim3(grid_a), dim3(MOE_WAVE), st, p);
     switch (uplr) {
     case 1: MOE_A(1) break;
     case 2: MOE_A(2) break;
@@ -355,13 +355,13 @@ hipError_t launch_fmt(const DecodeParams &p, hipStream_t st, int uplr, int lpr_f
 #undef MOE_A
     const int waves_b = p.K * per_expert;
     const int grid_b = (waves_b + B1_WAVES_B - 1) / B1_WAVES_B;
-    hipLaunchKernelGGL((b1_topk_gateup<FMT, UPLD>), dim3(grid_b), dim3(MOE_WAVE * B1_WAVES_B), 0, st, p);
+    MOE_LAUNCH(1, (b1_topk_gateup<FMT, UPLD>), dim3(grid_b), dim3(MOE_WAVE * B1_WAVES_B), st, p);
     const int rows_per_block = (MOE_WAVE / lpr_f) * B1_RR;
     const int grid_c = (p.D + rows_per_block - 1) / rows_per_block;
     switch (lpr_f) {
-    case 8: hipLaunchKernelGGL((b1_down<FMT, 8>), dim3(grid_c), dim3(MOE_WAVE * B1_WAVES_C), 0, st, p); break;
-    case 16: hipLaunchKernelGGL((b1_down<FMT, 16>), dim3(grid_c), dim3(MOE_WAVE * B1_WAVES_C), 0, st, p); break;
-    default: hipLaunchKernelGGL((b1_down<FMT, 32>), dim3(grid_c), dim3(MOE_WAVE * B1_WAVES_C), 0, st, p); break;
+    case 8: MOE_LAUNCH(2, (b1_down<FMT, 8>), dim3(grid_c), dim3(MOE_WAVE * B1_WAVES_C), st, p); break;
+    case 16: MOE_LAUNCH(2, (b1_down<FMT, 16>), dim3(grid_c), dim3(MOE_WAVE * B1_WAVES_C), st, p); break;
+    default: MOE_LAUNCH(2, (b1_down<FMT, 32>), dim3(grid_c), dim3(MOE_WAVE * B1_WAVES_C), st, p); break;
     }
     return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 // Internal host/device interface of libmoe (not part of the C ABI).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -41,7 +42,23 @@ struct DecodeParams {
     const uint8_t *next_shared;
     size_t next_shared_bytes;
     int32_t sink_flag;   // always 0: keeps prefetch loads alive
+    // optional kernel timing: start/stop event pairs, pair s for the layer's
+    // kernel slot s; the kernel is then launched with hipExtLaunchKernelGGL,
+    // whose events take the dispatch's own begin and end timestamps
+    hipEvent_t *ev;
 };
+
+// Launch `kern(p)` on `st`, timed into event pair `slot` when p.ev is set.
+#define MOE_LAUNCH(slot, kern, grid, block, st, p)                                                   \
+    do {                                                                                             \
+        if ((p).ev)                                                                                  \
+            hipExtLaunchKernelGGL(kern, grid, block, 0, st, (p).ev[2 * (slot)], (p).ev[2 * (slot) + 1], 0, p); \
+        else                                                                                         \
+            hipLaunchKernelGGL(kern, grid, block, 0, st, p);                                         \
+    } while (0)
+
+// Kernel slots of one layer, per decode path (names as reported by the timing entry point).
+constexpr int MAX_KERNEL_SLOTS = 4;
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
 // Batch-1 path (three kernels per layer); hipErrorNotSupported if the shape
