@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=47)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=47, help="layers in the CPU baseline sample")
+    ap.add_argument("--cpu-tokens", type=int, default=8, help="tokens in the CPU baseline sample")
     ap.add_argument("--timed-calls", type=int, default=20,
                     help="eager stack calls with per-kernel dispatch events (the roofline's kernel timing)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -238,11 +239,15 @@ def cpu_baseline_stack(args, hosts, xs, dims, stack, ws):
     import oracle
     from sparse_moe_decode_route_amd import binding as B
     n = min(args.cpu_layers, len(hosts))
-    x0 = xs[0].cpu().double().numpy()
+    nt = max(1, args.cpu_tokens)
+    xa = xs[:nt].reshape(nt, -1).cpu().double().numpy()
     oracle.lib()
     t0 = time.time()
-    y, ytr, itr = oracle.stack_forward(hosts[:n], x0)
+    y_all, ytr_all, itr_all = oracle.stack_forward(hosts[:n], xa)
     dt = time.time() - t0
+    # parity below on the first token (the GPU chain of xs[0])
+    x0 = xa[:1]
+    y, ytr, itr = y_all[:1], ytr_all[:, :1], itr_all[:, :1]
     # parity of this sample: GPU stack over the same layers and token, end to end,
     # and at the first layer whose selection differs, the oracle's fp64 logit gap
     # between the k-th and (k+1)-th expert on the GPU's own input to that layer
@@ -265,9 +270,9 @@ def cpu_baseline_stack(args, hosts, xs, dims, stack, ws):
         srt = np.sort(lg[0])[::-1]
         gap = float(srt[dims.top_k - 1] - srt[dims.top_k])
         tf_match = bool(np.array_equal(np.sort(oi[0]), np.sort(ig[first_diff][0])))
-    return dict(value=round(n / dt, 3), unit="MoE-layer tok/s", cores=1, kind="oracle",
-                sample=f"1 token through {n} q4_1 layers (d_model 2048, d_ff 512, 256+1 experts), fp64 C, "
-                       f"one thread, {dt:.1f}s",
+    return dict(value=round(n * nt / dt, 3), unit="MoE-layer tok/s", cores=1, kind="oracle",
+                sample=f"{nt} tokens (independent chains) through {n} q4_1 layers (d_model 2048, d_ff 512, "
+                       f"256+1 experts), fp64 C, one thread, {dt:.1f}s",
                 gpu_vs_oracle=dict(layers_same_routing=int(sum(same)), layers=n, first_divergent_layer=first_diff,
                                    oracle_topk_gap_at_divergence=gap,
                                    teacher_forced_selection_matches_at_divergence=tf_match,
@@ -276,7 +281,72 @@ def cpu_baseline_stack(args, hosts, xs, dims, stack, ws):
 
 
 def bench_prefill(args):
-    raise SystemExit("prefill workload not built yet")
+    """4096 bf16 tokens through one q4_1 layer with a Zipf(1.1) router prior."""
+    from sparse_moe_decode_route_amd import binding as B
+    from sparse_moe_decode_route_amd import inputs as gen
+    dims = gen.LayerDims(2048, 512, wfmt="q4_1")
+    T = 4096
+    lay = gen.make_layer(dims, cfg_id=5, layer=0, zipf_s=1.1, device="cuda")
+    packed = torch.empty_like(lay.experts)
+    B.repack_weights(dims, lay.experts, packed, dims.n_experts)
+    torch.cuda.synchronize()
+    dev = B.DeviceLayer(dims, lay.router, lay.router_bias, packed, None)
+    del lay
+    x = gen.to_bf16(gen.make_hidden(5, T, 2048, draw=0, device="cuda"))
+    ws = B.workspace(dims, T)
+    y = torch.empty((T, 2048), dtype=torch.float32, device="cuda")
+    _, idx, _ = B.layer_forward(dev, x, ws=ws, y=y, prefill=True)
+    torch.cuda.synchronize()
+    loads = np.bincount(idx.cpu().numpy().reshape(-1), minlength=dims.n_routed)
+    for _ in range(args.warmup):
+        B.layer_forward(dev, x, ws=ws, y=y, want_routing=False, prefill=True)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        B.layer_forward(dev, x, ws=ws, y=y, want_routing=False, prefill=True)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    # per-kernel dispatch timings
+    n_timed = max(1, min(args.timed_calls, 20))
+    tot = {}
+    for _ in range(n_timed):
+        _, us = B.layer_forward_prefill_timed(dev, x, ws=ws, y=y)
+        for k, v in us.items():
+            tot[k] = tot.get(k, 0.0) + v
+    kus = {k: v / n_timed for k, v in tot.items()}
+    log(f"prefill per-kernel us: {kus}")
+    D, F, E, S, K = dims.d_model, dims.d_ff, dims.n_routed, dims.n_shared, dims.top_k
+    rows = T * (K + S)
+    fl_gu = rows * 2 * F * D * 2
+    fl_dn = rows * D * F * 2
+    fl_rt = 2 * T * E * D
+    fl_all = fl_gu + fl_dn + fl_rt
+    dom = "pf_gemm_gateup"
+    ach = fl_gu / (kus[dom] * 1e-6) / 1e12
+    per_kernel = {k: dict(us_per_launch=round(v, 2)) for k, v in kus.items()}
+    per_kernel["pf_gemm_gateup"]["tflops"] = round(fl_gu / (kus["pf_gemm_gateup"] * 1e-6) / 1e12, 1)
+    per_kernel["pf_gemm_down"]["tflops"] = round(fl_dn / (kus["pf_gemm_down"] * 1e-6) / 1e12, 1)
+    per_kernel["pf_router"]["tflops"] = round(fl_rt / (kus["pf_router"] * 1e-6) / 1e12, 1)
+    return dict(
+        metric="MoE-layer prefill tokens/s (grouped GEMM on MFMA), 4-bit weights",
+        value=round(T / (ms * 1e-3), 1), unit="tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f16",
+        data="synthetic",
+        config=dict(workload="moe_prefill_q4_1_t4096: 4096 bf16 tokens (N(0,1) rounded) through one layer, d_model "
+                             "2048, d_ff 512, 256 routed + 1 shared, top-6, q4_1 experts, Zipf(1.1) router prior; "
+                             "MFMA operands fp16, fp32 accumulate",
+                    global_batch=T, seq_len=T, parallelism="single-gpu",
+                    flops_per_step=fl_all, layer_tflops=round(fl_all / (ms * 1e-3) / 1e12, 1),
+                    layer_mfma_frac=round(fl_all / (ms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+                    experts_hit=int(np.count_nonzero(loads)), max_expert_load=int(loads.max())),
+        roofline=dict(bound="mfma", kernel=dom, achieved=round(ach, 1), peak=MFMA_FP16_PEAK_TFLOPS,
+                      unit="TFLOP/s", frac=round(ach / MFMA_FP16_PEAK_TFLOPS, 4), traffic=None,
+                      flops_per_launch=fl_gu, us_per_launch=round(kus[dom], 2),
+                      timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream",
+                      per_kernel=per_kernel),
+    )
 
 
 def main():

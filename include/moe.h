@@ -195,6 +195,22 @@ moe_status moe_stack_decode_timed(const moe_dims *dims, int32_t n_layers, const 
                                   size_t ws_bytes, float *kernel_us, int32_t *n_kernels, char *names,
                                   size_t names_cap, void *stream);
 
+/*
+ * Measurement variant of moe_layer_forward_prefill (no routing outputs): the
+ * same kernels, each launched with a start/stop event pair on its dispatch.
+ * Blocks the calling thread until the layer is done.
+ *   kernel_us  (host) float [6]: duration in microseconds of each kernel, in
+ *              launch order (router, scan, scatter, gate/up GEMM, down GEMM,
+ *              combine); -1 for a kernel that did not run.
+ *   n_kernels  (host) receives 6.
+ *   names      (host, optional) receives the kernel names separated by ';'.
+ * Creates and destroys 12 HIP events; not for use under stream capture.
+ */
+moe_status moe_layer_forward_prefill_timed(const moe_dims *dims, const moe_layer_weights *w, const void *x,
+                                           int32_t act, int32_t n_tokens, float *y, void *ws, size_t ws_bytes,
+                                           float *kernel_us, int32_t *n_kernels, char *names, size_t names_cap,
+                                           void *stream);
+
 /* (host) static description of a status code. */
 const char *moe_status_string(moe_status s);
 

@@ -149,6 +149,20 @@ def _layer_arrays(layer):
     return wr, ex, ts, bias
 
 
+def router_logits(layer, x: np.ndarray) -> np.ndarray:
+    """Router logits only, [T, E] fp64 (x W_r^T + bias), token by token."""
+    dims = layer.dims
+    x = np.ascontiguousarray(x, dtype=np.float64).reshape(-1, dims.d_model)
+    wr, _, _, bias = _layer_arrays(layer)
+    out = np.zeros((x.shape[0], dims.n_routed), dtype=np.float64)
+    d = dims_struct(dims)
+    bp = None if bias is None else _p(bias, ctypes.c_double)
+    for t in range(x.shape[0]):
+        lib().orc_router_logits(ctypes.byref(d), _p(x[t], ctypes.c_double), _p(wr, ctypes.c_uint16), bp,
+                                _p(out[t], ctypes.c_double))
+    return out
+
+
 def layer_forward(layer, x: np.ndarray, forced: Optional[np.ndarray] = None, dense: bool = False):
     """Returns (idx [T,k] int32, w [T,k] f64, logits [T,E] f64, y [T,d] f64)."""
     dims = layer.dims

@@ -23,7 +23,7 @@ ACT_F32, ACT_BF16 = 0, 1
 ENTRY_POINTS = (
     "moe_packed_expert_bytes", "moe_workspace_size", "moe_repack_weights", "moe_route_topk",
     "moe_expert_ffn_q4", "moe_layer_forward", "moe_layer_forward_prefill", "moe_stack_decode",
-    "moe_stack_decode_timed", "moe_status_string", "moe_last_error",
+    "moe_stack_decode_timed", "moe_layer_forward_prefill_timed", "moe_status_string", "moe_last_error",
 )
 
 
@@ -75,6 +75,10 @@ def lib():
         L.moe_stack_decode_timed.argtypes = [pd, i32, ctypes.POINTER(CLayerWeights), vp, i32, vp, vp, vp, sz,
                                              ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32), ctypes.c_char_p,
                                              sz, vp]
+        L.moe_layer_forward_prefill_timed.restype = ctypes.c_int
+        L.moe_layer_forward_prefill_timed.argtypes = [pd, ctypes.POINTER(CLayerWeights), vp, i32, i32, vp, vp, sz,
+                                                      ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32),
+                                                      ctypes.c_char_p, sz, vp]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_last_error.restype = ctypes.c_char_p
@@ -254,3 +258,22 @@ def stack_decode_timed(stack: StackHandle, x0: torch.Tensor, ws: Optional[torch.
                                         _ptr(ws), ws.numel(), us, ctypes.byref(nk), names, 256, _stream(stream)))
     keys = names.value.decode().split(";")
     return y, idx_trace, {keys[k]: float(us[k]) for k in range(nk.value)}
+
+
+def layer_forward_prefill_timed(layer: DeviceLayer, x: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                                y: Optional[torch.Tensor] = None, stream=None):
+    """moe_layer_forward_prefill_timed: returns (y, {kernel name: us}).  Synchronises the stream."""
+    dims = layer.dims
+    T = x.shape[0]
+    y = y if y is not None else torch.empty((T, dims.d_model), dtype=torch.float32, device=x.device)
+    ws = ws if ws is not None else workspace(dims, T, x.device)
+    d = cdims(dims)
+    cw = layer.cstruct()
+    us = (ctypes.c_float * 8)()
+    nk = ctypes.c_int32(0)
+    names = ctypes.create_string_buffer(256)
+    _check(lib().moe_layer_forward_prefill_timed(ctypes.byref(d), ctypes.byref(cw), _ptr(x), _act(x), T, _ptr(y),
+                                                 _ptr(ws), ws.numel(), us, ctypes.byref(nk), names, 256,
+                                                 _stream(stream)))
+    keys = names.value.decode().split(";")
+    return y, {keys[k]: float(us[k]) for k in range(nk.value)}

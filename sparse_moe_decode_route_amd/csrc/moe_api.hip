@@ -151,6 +151,22 @@ moe_status decode_input(const moe_dims &d, const void *x, int act, int T, void *
 }
 
 // The batch-1 path when the shape fits it, the general decode path otherwise.
+moe::PrefillArgs prefill_args(const moe_dims &d, const void *x, int act, int T, void *ws) {
+    moe::PrefillArgs a{};
+    a.D = d.d_model;
+    a.F = d.d_ff;
+    a.E = d.n_routed;
+    a.S = d.n_shared;
+    a.K = d.top_k;
+    a.T = T;
+    a.fmt = d.wfmt;
+    a.act = act;
+    a.expert_bytes = moe_packed_expert_bytes(&d);
+    a.x = x;
+    a.ws = ws;
+    return a;
+}
+
 // *path (optional) receives 1 for the batch-1 path, 2 for the general one.
 hipError_t launch_any(const moe::DecodeParams &p, hipStream_t st, int *path = nullptr) {
     hipError_t e = moe::launch_decode_b1(p, st);
@@ -219,13 +235,15 @@ moe_status moe_route_topk(const moe_dims *d, const void *x, int32_t act, int32_t
     MOE_TRY(check_ptr(logits_out, "logits_out", false));
     MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (n_tokens > moe::MAX_DECODE_T) {
-        float *logits = logits_out ? logits_out : moe::prefill_logits_buffer(ws, *d, n_tokens);
-        MOE_TRY(hip_status(moe::launch_router_gemm(x, act, n_tokens, d->d_model, d->n_routed,
-                                                   static_cast<const uint16_t *>(router), router_bias, logits, st),
-                           "router launch"));
-        return hip_status(moe::launch_topk(logits, n_tokens, d->n_routed, d->top_k, topk_idx, topk_w, st),
-                          "top-k launch");
+    if (n_tokens > moe::MAX_DECODE_T) {  // many tokens: the prefill router (MFMA) with its top-k
+        moe::PrefillArgs a = prefill_args(*d, x, act, n_tokens, ws);
+        a.router = static_cast<const uint16_t *>(router);
+        a.bias = router_bias;
+        a.idx_out = topk_idx;
+        a.w_out = topk_w;
+        a.logits_out = logits_out;
+        a.route_only = 1;
+        return hip_status(moe::launch_prefill(a, st), "prefill route launch");
     }
     const DecodeWs L = decode_ws(*d, n_tokens);
     moe::DecodeParams p = base_params(*d, n_tokens, ws, L);
@@ -245,8 +263,7 @@ moe_status moe_expert_ffn_q4(const moe_dims *d, const void *x, int32_t act, int3
                              void *ws, size_t ws_bytes, void *stream) {
     MOE_TRY(check_dims(d));
     if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown activation type");
-    if (n_tokens < 1 || n_tokens > moe::MAX_DECODE_T)
-        return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, 8] for the expert FFN");
+    if (n_tokens < 1 || n_tokens > 65536) return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, 65536]");
     MOE_TRY(check_ptr(x, "x"));
     MOE_TRY(check_ptr(experts, "experts"));
     MOE_TRY(check_ptr(tensor_scale, "tensor_scale", d->wfmt == MOE_W_NVFP4));
@@ -255,6 +272,15 @@ moe_status moe_expert_ffn_q4(const moe_dims *d, const void *x, int32_t act, int3
     MOE_TRY(check_ptr(y, "y"));
     MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n_tokens > moe::MAX_DECODE_T) {  // many tokens: grouped GEMM over the given routing
+        moe::PrefillArgs a = prefill_args(*d, x, act, n_tokens, ws);
+        a.experts = static_cast<const uint8_t *>(experts);
+        a.tscale = d->wfmt == MOE_W_NVFP4 ? tensor_scale : nullptr;
+        a.given_idx = topk_idx;
+        a.given_w = topk_w;
+        a.y = y;
+        return hip_status(moe::launch_prefill(a, st), "prefill expert FFN launch");
+    }
     const DecodeWs L = decode_ws(*d, n_tokens);
     moe::DecodeParams p = base_params(*d, n_tokens, ws, L);
     MOE_TRY(decode_input(*d, x, act, n_tokens, ws, L, st, &p.x));
@@ -308,9 +334,9 @@ moe_status moe_layer_forward(const moe_dims *d, const moe_layer_weights *w, cons
     return hip_status(launch_any(p, st), "layer launch");
 }
 
-moe_status moe_layer_forward_prefill(const moe_dims *d, const moe_layer_weights *w, const void *x, int32_t act,
-                                     int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws,
-                                     size_t ws_bytes, void *stream) {
+static moe_status prefill_impl(const moe_dims *d, const moe_layer_weights *w, const void *x, int32_t act,
+                               int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                               size_t ws_bytes, hipStream_t st, hipEvent_t *ev) {
     MOE_TRY(check_dims(d));
     if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown activation type");
     if (n_tokens < 1 || n_tokens > 65536) return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, 65536]");
@@ -322,17 +348,7 @@ moe_status moe_layer_forward_prefill(const moe_dims *d, const moe_layer_weights 
     MOE_TRY(check_ptr(topk_idx_out, "topk_idx_out", false));
     MOE_TRY(check_ptr(topk_w_out, "topk_w_out", false));
     MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
-    moe::PrefillArgs a{};
-    a.D = d->d_model;
-    a.F = d->d_ff;
-    a.E = d->n_routed;
-    a.S = d->n_shared;
-    a.K = d->top_k;
-    a.T = n_tokens;
-    a.fmt = d->wfmt;
-    a.act = act;
-    a.expert_bytes = moe_packed_expert_bytes(d);
-    a.x = x;
+    moe::PrefillArgs a = prefill_args(*d, x, act, n_tokens, ws);
     a.router = static_cast<const uint16_t *>(w->router);
     a.bias = w->router_bias;
     a.experts = static_cast<const uint8_t *>(w->experts);
@@ -340,8 +356,15 @@ moe_status moe_layer_forward_prefill(const moe_dims *d, const moe_layer_weights 
     a.y = y;
     a.idx_out = topk_idx_out;
     a.w_out = topk_w_out;
-    a.ws = ws;
-    return hip_status(moe::launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill launch");
+    a.ev = ev;
+    return hip_status(moe::launch_prefill(a, st), "prefill launch");
+}
+
+moe_status moe_layer_forward_prefill(const moe_dims *d, const moe_layer_weights *w, const void *x, int32_t act,
+                                     int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                                     size_t ws_bytes, void *stream) {
+    return prefill_impl(d, w, x, act, n_tokens, y, topk_idx_out, topk_w_out, ws, ws_bytes,
+                        static_cast<hipStream_t>(stream), nullptr);
 }
 
 }  // extern "C"
@@ -456,6 +479,35 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
         snprintf(names, names_cap, "%s", src);
     }
     return ok();
+}
+
+moe_status moe_layer_forward_prefill_timed(const moe_dims *d, const moe_layer_weights *w, const void *x, int32_t act,
+                                           int32_t n_tokens, float *y, void *ws, size_t ws_bytes, float *kernel_us,
+                                           int32_t *n_kernels, char *names, size_t names_cap, void *stream) {
+    if (!kernel_us || !n_kernels) return fail(MOE_ERR_INVALID_ARG, "kernel_us / n_kernels is NULL");
+    hipEvent_t ev[2 * moe::PREFILL_SLOTS] = {};
+    for (auto &e : ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (auto &f : ev)
+                if (f) (void)hipEventDestroy(f);
+            return fail(MOE_ERR_HIP, "hipEventCreate failed");
+        }
+    }
+    moe_status s = prefill_impl(d, w, x, act, n_tokens, y, nullptr, nullptr, ws, ws_bytes,
+                                static_cast<hipStream_t>(stream), ev);
+    if (s == MOE_OK && hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+        s = fail(MOE_ERR_HIP, "stream synchronize failed");
+    if (s == MOE_OK) {
+        for (int k = 0; k < moe::PREFILL_SLOTS; k++) {
+            float ms = 0.f;
+            kernel_us[k] = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1]) == hipSuccess ? ms * 1e3f : -1.f;
+        }
+        (void)hipGetLastError();
+        *n_kernels = moe::PREFILL_SLOTS;
+        if (names && names_cap) snprintf(names, names_cap, "%s", moe::kPrefillNames);
+    }
+    for (auto &e : ev) (void)hipEventDestroy(e);
+    return s == MOE_OK ? ok() : s;
 }
 
 const char *moe_status_string(moe_status s) {

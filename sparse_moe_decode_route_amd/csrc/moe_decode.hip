@@ -210,21 +210,6 @@ __global__ void __launch_bounds__(512) select_kernel(DecodeParams p) {
     }
 }
 
-// Top-k for any number of tokens: one wave per token.
-__global__ void __launch_bounds__(256) topk_kernel(const float *logits, int T, int E, int K, int32_t *idx,
-                                                   float *w) {
-    const int t = blockIdx.x * 4 + threadIdx.x / MOE_WAVE;
-    const int lane = threadIdx.x % MOE_WAVE;
-    if (t >= T) return;
-    int e;
-    float wi;
-    wave_topk(logits + (size_t)t * E, E, K, &e, &wi);
-    if (lane < K) {
-        idx[(size_t)t * K + lane] = e;
-        w[(size_t)t * K + lane] = wi;
-    }
-}
-
 // Routed gate/up: one wave per (active slot, feature group).
 template <int FMT, int LPR_D, int RG, int MAXT>
 __global__ void __launch_bounds__(MOE_WAVE) gateup_kernel(DecodeParams p) {
@@ -360,9 +345,5 @@ hipError_t launch_bf16_to_f32(const uint16_t *in, float *out, int n, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *idx, float *w, hipStream_t st) {
-    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, K, idx, w);
-    return hipGetLastError();
-}
 
 }  // namespace moe

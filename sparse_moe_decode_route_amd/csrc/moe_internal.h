@@ -66,8 +66,4 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
 hipError_t launch_decode_b1(const DecodeParams &p, hipStream_t st);
 hipError_t launch_route_only(const DecodeParams &p, hipStream_t st);
 hipError_t launch_bf16_to_f32(const uint16_t *in, float *out, int n, hipStream_t st);
-hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *idx, float *w, hipStream_t st);
-hipError_t launch_router_gemm(const void *x, int act, int T, int D, int E, const uint16_t *router,
-                              const float *bias, float *logits, hipStream_t st);
-
 }  // namespace moe

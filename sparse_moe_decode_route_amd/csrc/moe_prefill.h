@@ -20,11 +20,19 @@ struct PrefillArgs {
     float *y;
     int32_t *idx_out;
     float *w_out;
+    float *logits_out;        // optional [T, E]
+    const int32_t *given_idx; // caller routing [T, K] (router skipped), or nullptr
+    const float *given_w;
+    int route_only;           // stop after routing (idx_out / w_out / logits_out)
     void *ws;
+    hipEvent_t *ev;           // optional start/stop pairs per kernel slot (PREFILL_SLOTS)
 };
 
+// Kernel slots of the prefill path, in launch order (timing entry point).
+constexpr int PREFILL_SLOTS = 6;
+extern const char *const kPrefillNames;
+
 size_t prefill_ws_bytes(int D, int F, int E, int S, int K, int T);
-float *prefill_logits_buffer(void *ws, const moe_dims &d, int T);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);
 hipError_t launch_repack_q4_1(const uint8_t *canonical, uint8_t *packed, int n_experts, int D, int F, hipStream_t st);
 

@@ -1,17 +1,702 @@
-// Prefill path (placeholder until the grouped GEMM lands): reports
-// unsupported so callers fail loudly.
+// Prefill path of the MoE layer: route every token, group the (token, slot)
+// pairs by expert, run each expert as a grouped GEMM on the matrix cores, and
+// combine each token's rows in a fixed order.
+//
+// What is computed is the same layer as the decode path ("Recursive Flint
+// 40B-A2.5B", section "The architecture is a memory-bandwidth argument": 256
+// routed experts, 6 chosen per token, one always-on shared expert), applied to
+// many tokens at once.  With thousands of tokens each active expert sees a
+// matrix of tokens, so the expert projections become dense contractions and
+// run on MFMA (fp16 operands, fp32 accumulation).
+//
+// Kernels (one stream, in order):
+//   pf_router   logits = x Wr^T (+bias) by bf16 MFMA, per-token top-k,
+//               per-expert 64-token bitmasks, fp16 copy of x
+//   pf_scan     per-expert counts and word prefixes of the masks, row
+//               offsets, tile table
+//   pf_scatter  position of every (token, slot) pair in its expert's rows
+//   pf_gemm<0>  H = silu(X Wg^T) * (X Wu^T) per expert (fp16 H)
+//   pf_gemm<1>  O = coef * (H Wd^T) per expert (fp32 O)
+//   pf_combine  y[t] = sum of t's rows of O in slot order
+// No floating-point atomics: integer/bitwise atomics only, so results do not
+// depend on scheduling.
 #include <hip/hip_runtime.h>
 
+#include "moe_device.h"
 #include "moe_internal.h"
 #include "moe_prefill.h"
 
 namespace moe {
+namespace {
 
-size_t prefill_ws_bytes(int, int, int, int, int, int) { return 0; }
-float *prefill_logits_buffer(void *ws, const moe_dims &, int) { return static_cast<float *>(ws); }
-hipError_t launch_prefill(const PrefillArgs &, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_router_gemm(const void *, int, int, int, int, const uint16_t *, const float *, float *, hipStream_t) {
-    return hipErrorNotSupported;
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int PF_BM = 128;          // rows (token slots) per GEMM tile
+constexpr int PF_THREADS = 256;     // 4 waves
+constexpr int PF_RT = 64;           // tokens per router block
+constexpr int PF_LDS_ROW = 40;      // halfs per staged row (32 data + 8 pad)
+constexpr int PF_MAX_TOPK = 8;
+
+struct PfTile {
+    int e, row0, rows;
+};
+
+// Workspace layout (byte offsets), shared by the host sizing and the launcher.
+struct PfWs {
+    size_t x16, idx, w, mask, wp, off, tiles, meta, perm_tok, perm_w, pos, h, o, total;
+    int NW, R, tiles_max;
+};
+
+size_t al(size_t v) { return (v + 255) & ~(size_t)255; }
+
+PfWs pf_layout(int D, int F, int E, int S, int K, int T) {
+    PfWs L{};
+    L.NW = (T + 63) / 64;
+    L.R = T * (K + S);
+    L.tiles_max = (L.R + PF_BM - 1) / PF_BM + E + S;
+    size_t o = 0;
+    L.x16 = o; o = al(o + (size_t)T * D * 2);
+    L.idx = o; o = al(o + (size_t)T * K * 4);
+    L.w = o; o = al(o + (size_t)T * K * 4);
+    L.mask = o; o = al(o + (size_t)E * L.NW * 8);
+    L.wp = o; o = al(o + (size_t)E * L.NW * 4);
+    L.off = o; o = al(o + (size_t)(E + S + 1) * 4);
+    L.tiles = o; o = al(o + (size_t)L.tiles_max * sizeof(PfTile));
+    L.meta = o; o = al(o + 16 * 4);
+    L.perm_tok = o; o = al(o + (size_t)L.R * 4);
+    L.perm_w = o; o = al(o + (size_t)L.R * 4);
+    L.pos = o; o = al(o + (size_t)T * (K + S) * 4);
+    L.h = o; o = al(o + (size_t)L.R * F * 2);
+    L.o = o; o = al(o + (size_t)L.R * D * 4);
+    L.total = o;
+    return L;
 }
+
+template <typename T>
+T *wsp(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+struct PfParams {
+    int D, F, E, S, K, T, act, NW, R, tiles_max, want_x16;
+    hipEvent_t *ev;
+    size_t expert_bytes;
+    const void *x;
+    const uint16_t *router;
+    const float *bias;
+    const uint8_t *experts;
+    const float *tscale;
+    float *y;
+    int32_t *idx_out;
+    float *w_out;
+    float *logits_out;
+    _Float16 *x16;
+    int32_t *idx;
+    float *w;
+    unsigned long long *mask;
+    int32_t *wp;
+    int32_t *off;
+    PfTile *tiles;
+    int32_t *meta;
+    int32_t *perm_tok;
+    float *perm_w;
+    int32_t *pos;
+    _Float16 *h;
+    float *o;
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// fp32 -> (hi, lo) bf16 pair with hi + lo = x up to 2^-16 |x| (both rounded to nearest)
+__device__ __forceinline__ uint32_t f2bf_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// pf_router: one block = 64 tokens x all experts; wave w owns experts
+// [64w, 64w + 64) as two 32-row MFMA tiles, both 32-token halves.
+// ---------------------------------------------------------------------------
+template <int ACT>
+__global__ void __launch_bounds__(PF_THREADS) pf_router(PfParams p) {
+    __shared__ float lg[32][256];
+    __shared__ unsigned long long smask[256];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t0 = blockIdx.x * PF_RT;
+    const int D = p.D, E = p.E, T = p.T;
+    if (tid < 256) smask[tid] = 0ull;
+
+    // fp16 copy of this block's tokens (operand of the expert GEMMs)
+    if (p.want_x16) {
+        const int nt = min(PF_RT, T - t0);
+        const int n8 = nt * D / 8;
+        for (int i = tid; i < n8; i += PF_THREADS) {
+            const size_t e0 = (size_t)t0 * D + (size_t)i * 8;
+            half8_t hv;
+            if (ACT == 0) {
+                const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.x) + e0);
+                const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.x) + e0 + 4);
+                hv[0] = (_Float16)a.x; hv[1] = (_Float16)a.y; hv[2] = (_Float16)a.z; hv[3] = (_Float16)a.w;
+                hv[4] = (_Float16)b.x; hv[5] = (_Float16)b.y; hv[6] = (_Float16)b.z; hv[7] = (_Float16)b.w;
+            } else {
+                const uint4 r = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + e0);
+                const uint32_t ww[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    hv[2 * j] = (_Float16)bf16lo(ww[j]);
+                    hv[2 * j + 1] = (_Float16)bf16hi(ww[j]);
+                }
+            }
+            *reinterpret_cast<half8_t *>(p.x16 + e0) = hv;
+        }
+    }
+
+    // router GEMM: D[m = expert][n = token]
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int j = 0; j < 16; j++) acc[a][b][j] = 0.f;
+    const int g = lane >> 5, l32 = lane & 31;
+    const uint16_t *wrow[2];
+#pragma unroll
+    for (int a = 0; a < 2; a++) wrow[a] = p.router + (size_t)min(64 * wave + 32 * a + l32, E - 1) * D + 8 * g;
+    int trow[2];
+#pragma unroll
+    for (int b = 0; b < 2; b++) trow[b] = min(t0 + 32 * b + l32, T - 1);
+    for (int k0 = 0; k0 < D; k0 += 16) {
+        bf16x8_t af[2];
+#pragma unroll
+        for (int a = 0; a < 2; a++) af[a] = as_bf16x8(*reinterpret_cast<const uint4 *>(wrow[a] + k0));
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            if (ACT == 0) {
+                const float *xs = static_cast<const float *>(p.x) + (size_t)trow[b] * D + k0 + 8 * g;
+                const float4 u0 = *reinterpret_cast<const float4 *>(xs);
+                const float4 u1 = *reinterpret_cast<const float4 *>(xs + 4);
+                const float xv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t h0 = f2bf_rne(xv[2 * j]), h1 = f2bf_rne(xv[2 * j + 1]);
+                    const uint32_t l0 = f2bf_rne(xv[2 * j] - __uint_as_float(h0 << 16));
+                    const uint32_t l1 = f2bf_rne(xv[2 * j + 1] - __uint_as_float(h1 << 16));
+                    hi[j] = h0 | (h1 << 16);
+                    lo[j] = l0 | (l1 << 16);
+                }
+                const bf16x8_t bh = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                const bf16x8_t bl = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+                for (int a = 0; a < 2; a++) {
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bh, acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bl, acc[a][b], 0, 0, 0);
+                }
+            } else {
+                const uint16_t *xs = static_cast<const uint16_t *>(p.x) + (size_t)trow[b] * D + k0 + 8 * g;
+                const bf16x8_t bx = as_bf16x8(*reinterpret_cast<const uint4 *>(xs));
+#pragma unroll
+                for (int a = 0; a < 2; a++)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bx, acc[a][b], 0, 0, 0);
+            }
+        }
+    }
+    // per 32-token half: logits (+ bias) to LDS [token][expert], then top-k
+    // (wave w takes tokens w, w + 4, ...)
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+        if (b) __syncthreads();  // the previous half's top-k has read lg
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const int e = 64 * wave + 32 * a + 8 * (j >> 2) + 4 * g + (j & 3);
+                if (e < E) lg[l32][e] = acc[a][b][j] + (p.bias ? p.bias[e] : 0.f);
+            }
+        __syncthreads();
+        for (int tl = wave; tl < 32; tl += 4) {
+            const int t = t0 + 32 * b + tl;
+            if (t >= T) break;
+            int e;
+            float wi;
+            wave_topk(lg[tl], E, p.K, &e, &wi);
+            if (lane < p.K) {
+                p.idx[(size_t)t * p.K + lane] = e;
+                p.w[(size_t)t * p.K + lane] = wi;
+                if (p.idx_out) p.idx_out[(size_t)t * p.K + lane] = e;
+                if (p.w_out) p.w_out[(size_t)t * p.K + lane] = wi;
+                atomicOr(&smask[e], 1ull << (32 * b + tl));
+            }
+            if (p.logits_out)
+                for (int e2 = lane; e2 < E; e2 += 64) p.logits_out[(size_t)t * E + e2] = lg[tl][e2];
+        }
+    }
+    __syncthreads();
+    if (tid < E) p.mask[(size_t)tid * p.NW + blockIdx.x] = smask[tid];
+}
+
+// ---------------------------------------------------------------------------
+// pf_x16: fp16 copy of x (the router kernel makes it otherwise)
+// ---------------------------------------------------------------------------
+template <int ACT>
+__global__ void __launch_bounds__(PF_THREADS) pf_x16(PfParams p) {
+    const size_t i = (size_t)blockIdx.x * PF_THREADS + threadIdx.x;
+    if (i >= (size_t)p.T * p.D / 8) return;
+    half8_t hv;
+    if (ACT == 0) {
+        const float4 a = reinterpret_cast<const float4 *>(p.x)[2 * i];
+        const float4 b = reinterpret_cast<const float4 *>(p.x)[2 * i + 1];
+        hv[0] = (_Float16)a.x; hv[1] = (_Float16)a.y; hv[2] = (_Float16)a.z; hv[3] = (_Float16)a.w;
+        hv[4] = (_Float16)b.x; hv[5] = (_Float16)b.y; hv[6] = (_Float16)b.z; hv[7] = (_Float16)b.w;
+    } else {
+        const uint4 r = reinterpret_cast<const uint4 *>(p.x)[i];
+        const uint32_t ww[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            hv[2 * j] = (_Float16)bf16lo(ww[j]);
+            hv[2 * j + 1] = (_Float16)bf16hi(ww[j]);
+        }
+    }
+    reinterpret_cast<half8_t *>(p.x16)[i] = hv;
+}
+
+// ---------------------------------------------------------------------------
+// pf_mask_given: per-expert token bitmasks from a caller-given routing (one
+// block per 64 tokens); indices outside [0, E) select nothing.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(PF_THREADS) pf_mask_given(PfParams p) {
+    __shared__ unsigned long long smask[256];
+    const int tid = threadIdx.x;
+    smask[tid] = 0ull;
+    __syncthreads();
+    const int t0 = blockIdx.x * 64;
+    for (int i = tid; i < 64 * p.K; i += PF_THREADS) {
+        const int tl = i / p.K, j = i % p.K, t = t0 + tl;
+        if (t >= p.T) continue;
+        const int e = p.idx[(size_t)t * p.K + j];
+        if (e >= 0 && e < p.E) atomicOr(&smask[e], 1ull << tl);
+    }
+    __syncthreads();
+    if (tid < p.E) p.mask[(size_t)tid * p.NW + blockIdx.x] = smask[tid];
+}
+
+// ---------------------------------------------------------------------------
+// pf_scan: one block.  Rows are ordered routed expert 0..E-1, then shared.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(PF_THREADS) pf_scan(PfParams p) {
+    __shared__ int cnt[PF_THREADS + 8];
+    const int tid = threadIdx.x;
+    const int n_exp = p.E + p.S;
+    for (int e = tid; e < n_exp; e += PF_THREADS) {
+        int c = 0;
+        if (e < p.E) {
+            for (int w = 0; w < p.NW; w++) {
+                p.wp[(size_t)e * p.NW + w] = c;
+                c += __popcll(p.mask[(size_t)e * p.NW + w]);
+            }
+        } else {
+            c = p.T;
+        }
+        cnt[e] = c;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int off = 0, tiles = 0;
+        for (int e = 0; e < n_exp; e++) {
+            const int c = cnt[e];
+            p.off[e] = off;
+            cnt[e] = tiles;  // becomes the expert's first tile index
+            off += c;
+            tiles += (c + PF_BM - 1) / PF_BM;
+        }
+        p.off[n_exp] = off;
+        p.meta[0] = tiles;
+        p.meta[1] = off;
+    }
+    __syncthreads();
+    for (int e = tid; e < n_exp; e += PF_THREADS) {
+        const int n = p.off[e + 1] - p.off[e];
+        const int first = cnt[e];
+        for (int i = 0; i * PF_BM < n; i++) {
+            PfTile t;
+            t.e = e;
+            t.row0 = p.off[e] + i * PF_BM;
+            t.rows = min(PF_BM, n - i * PF_BM);
+            p.tiles[first + i] = t;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// pf_scatter: one thread per token.  The rank of token t in expert e's rows
+// is the number of tokens before t that chose e (prefix popcount).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(PF_THREADS) pf_scatter(PfParams p) {
+    const int t = blockIdx.x * PF_THREADS + threadIdx.x;
+    if (t >= p.T) return;
+    const int KS = p.K + p.S;
+    const int w = t >> 6;
+    const unsigned long long below = (t & 63) ? ((1ull << (t & 63)) - 1ull) : 0ull;
+    for (int j = 0; j < p.K; j++) {
+        const int e = p.idx[(size_t)t * p.K + j];
+        if (e < 0 || e >= p.E) {  // caller routing may hold invalid indices: no row
+            p.pos[(size_t)t * KS + j] = -1;
+            continue;
+        }
+        const size_t mi = (size_t)e * p.NW + w;
+        const int r = p.off[e] + p.wp[mi] + __popcll(p.mask[mi] & below);
+        p.perm_tok[r] = t;
+        p.perm_w[r] = p.w[(size_t)t * p.K + j];
+        p.pos[(size_t)t * KS + j] = r;
+    }
+    for (int s = 0; s < p.S; s++) {
+        const int r = p.off[p.E + s] + t;
+        p.perm_tok[r] = t;
+        p.perm_w[r] = 1.f;
+        p.pos[(size_t)t * KS + p.K + s] = r;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Weight fragments for v_mfma_f32_32x32x16_f16.  One call covers 32 inputs of
+// one weight row (one q4_1 block): lane group g = lane / 32 holds, for MFMA
+// step s (0, 1), the 8 inputs [16 s + 8 g, 16 s + 8 g + 8).  The token operand
+// is staged with the same input order, so the reduction is unchanged.
+// ---------------------------------------------------------------------------
+template <int FMT> struct WRaw;
+template <> struct WRaw<FMT_Q4_1> { uint2 c; uint32_t dm; };
+template <> struct WRaw<FMT_NVFP4> { uint32_t c0, c1; uint32_t s; };
+template <> struct WRaw<FMT_BF16> { uint4 v0, v1; };
+
+// base: matrix start; rows x K; row r, block b (32 inputs), lane group g
+template <int FMT>
+__device__ __forceinline__ WRaw<FMT> load_wraw(const uint8_t *base, int rows, int K, int r, int b, int g) {
+    WRaw<FMT> w;
+    if constexpr (FMT == FMT_Q4_1) {
+        const uint8_t *c = base + (size_t)r * (K / 2) + b * 16 + g * 8;
+        w.c = *reinterpret_cast<const uint2 *>(c);
+        w.dm = *reinterpret_cast<const uint32_t *>(base + (size_t)rows * (K / 2) + ((size_t)r * (K / 32) + b) * 4);
+    } else if constexpr (FMT == FMT_NVFP4) {
+        const uint8_t *c = base + (size_t)r * (K / 2) + b * 16 + g * 4;
+        w.c0 = *reinterpret_cast<const uint32_t *>(c);
+        w.c1 = *reinterpret_cast<const uint32_t *>(c + 8);
+        w.s = *reinterpret_cast<const uint16_t *>(base + (size_t)rows * (K / 2) + (size_t)r * (K / 16) + b * 2);
+    } else {
+        const uint16_t *v = reinterpret_cast<const uint16_t *>(base) + (size_t)r * K + b * 32 + g * 8;
+        w.v0 = *reinterpret_cast<const uint4 *>(v);
+        w.v1 = *reinterpret_cast<const uint4 *>(v + 16);
+    }
+    return w;
+}
+
+// 4 nibbles (bytes of t, each < 16) -> two fp16 pairs holding the integers
+__device__ __forceinline__ void nib4_to_h(uint32_t t, half2_t &a, half2_t &b) {
+    const uint32_t p01 = (t & 0xFFu) | ((t & 0xFF00u) << 8) | 0x64006400u;
+    const uint32_t p23 = ((t >> 16) & 0xFFu) | ((t >> 8) & 0xFF0000u) | 0x64006400u;
+    const half2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
+    a = __builtin_bit_cast(half2_t, p01) - k1024;  // exact: 1024 + q - 1024
+    b = __builtin_bit_cast(half2_t, p23) - k1024;
+}
+
+// E2M1 code (4 bits) -> fp16 bits: sign, and the high byte of the fp16
+// encodings of {0, .5, 1, 1.5, 2, 3, 4, 6} packed in a 64-bit table
+__device__ __forceinline__ uint32_t e2m1_h(uint32_t c) {
+    constexpr unsigned long long kHi = 0x464442403E3C3800ull;
+    const uint32_t hi = (uint32_t)(kHi >> (8 * (c & 7u))) & 0xFFu;
+    return (hi << 8) | ((c & 8u) << 12);
+}
+
+// fragments for steps 0 and 1; NVFP4 values exclude the tensor scale
+// (applied to the accumulator), and are exact in fp16.
+template <int FMT>
+__device__ __forceinline__ void dequant_frag(const WRaw<FMT> &w, half8_t &s0, half8_t &s1) {
+    if constexpr (FMT == FMT_Q4_1) {
+        const half2_t d2 = __builtin_bit_cast(half2_t, (w.dm & 0xFFFFu) * 0x10001u);
+        const half2_t m2 = __builtin_bit_cast(half2_t, (w.dm >> 16) * 0x10001u);
+        const uint32_t wl[2] = {w.c.x, w.c.y};
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            half2_t a, b;
+            nib4_to_h(wl[i] & 0x0F0F0F0Fu, a, b);
+            a = a * d2 + m2;
+            b = b * d2 + m2;
+            s0[4 * i + 0] = a[0]; s0[4 * i + 1] = a[1]; s0[4 * i + 2] = b[0]; s0[4 * i + 3] = b[1];
+            nib4_to_h((wl[i] >> 4) & 0x0F0F0F0Fu, a, b);
+            a = a * d2 + m2;
+            b = b * d2 + m2;
+            s1[4 * i + 0] = a[0]; s1[4 * i + 1] = a[1]; s1[4 * i + 2] = b[0]; s1[4 * i + 3] = b[1];
+        }
+    } else if constexpr (FMT == FMT_NVFP4) {
+        const _Float16 sc0 = (_Float16)e4m3_to_float(w.s & 0xFFu);
+        const _Float16 sc1 = (_Float16)e4m3_to_float(w.s >> 8);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            s0[j] = __builtin_bit_cast(_Float16, (uint16_t)e2m1_h((w.c0 >> (4 * j)) & 0xFu)) * sc0;
+            s1[j] = __builtin_bit_cast(_Float16, (uint16_t)e2m1_h((w.c1 >> (4 * j)) & 0xFu)) * sc1;
+        }
+    } else {
+        const uint32_t a[4] = {w.v0.x, w.v0.y, w.v0.z, w.v0.w};
+        const uint32_t b[4] = {w.v1.x, w.v1.y, w.v1.z, w.v1.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            s0[2 * j] = (_Float16)bf16lo(a[j]);
+            s0[2 * j + 1] = (_Float16)bf16hi(a[j]);
+            s1[2 * j] = (_Float16)bf16lo(b[j]);
+            s1[2 * j + 1] = (_Float16)bf16hi(b[j]);
+        }
+    }
+}
+
+// Tile decode with an XCD-aware order: blocks go round-robin to the 8 XCDs,
+// so consecutive logical tiles (same expert's weights, same token rows) are
+// given to blocks on one XCD and share its L2.
+__device__ __forceinline__ int xcd_logical(int b, int n) {
+    const int q = n / 8, r = n % 8, x = b % 8;
+    return x * q + min(x, r) + b / 8;
+}
+
+// ---------------------------------------------------------------------------
+// pf_gemm<MODE>: one block = one tile of <= 128 rows of one expert x 128
+// (gate/up: features; MODE 0) or 256 (down: outputs; MODE 1) weight rows.
+// Wave w owns 2 A-operand row groups of 32 (gate and up of the same 32
+// features, or 2 x 32 down rows) against all 128 tile rows (4 x 32).
+// ---------------------------------------------------------------------------
+template <int FMT, int MODE>
+__global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfParams p) {
+    __shared__ __attribute__((aligned(16))) _Float16 bt[2][PF_BM * PF_LDS_ROW];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    const int MT = MODE == 0 ? (p.F + 127) / 128 : (p.D + 255) / 256;
+    const int n_tiles = p.meta[0];
+    const int n_blk = n_tiles * MT;
+    if ((int)blockIdx.x >= n_blk) return;
+    const int L = xcd_logical(blockIdx.x, n_blk);
+    const int ti = L / MT, mt = L % MT;
+    const PfTile tile = p.tiles[ti];
+    const int K = MODE == 0 ? p.D : p.F;           // reduction length
+    const int ROWS_A = MODE == 0 ? p.F : p.D;      // rows of the weight matrix
+    const uint8_t *eb = p.experts + (size_t)tile.e * p.expert_bytes;
+    const size_t mb_gu = mat_bytes<FMT>(p.F, p.D);
+    const uint8_t *mA0 = MODE == 0 ? eb : eb + 2 * mb_gu;             // gate | down
+    const uint8_t *mA1 = MODE == 0 ? eb + mb_gu : eb + 2 * mb_gu;     // up   | down
+    int r0 = MODE == 0 ? mt * 128 + 32 * wave : mt * 256 + 64 * wave; // first A row of sub 0
+    int ra[2];
+    ra[0] = r0 + l32;
+    ra[1] = MODE == 0 ? r0 + l32 : r0 + 32 + l32;
+    const bool sub_ok[2] = {r0 < ROWS_A, (MODE == 0 ? r0 : r0 + 32) < ROWS_A};
+    ra[0] = min(ra[0], ROWS_A - 1);
+    ra[1] = min(ra[1], ROWS_A - 1);
+
+    // staging: thread stages rows (tid >> 2) and (tid >> 2) + 64, part tid & 3
+    const int part = tid & 3;
+    const _Float16 *srow[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int rr = min((tid >> 2) + 64 * i, tile.rows - 1);
+        if (MODE == 0)
+            srow[i] = p.x16 + (size_t)p.perm_tok[tile.row0 + rr] * p.D + 8 * part;
+        else
+            srow[i] = p.h + (size_t)(tile.row0 + rr) * p.F + 8 * part;
+    }
+    const int sdst[2] = {((tid >> 2)) * PF_LDS_ROW + 8 * part, ((tid >> 2) + 64) * PF_LDS_ROW + 8 * part};
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int j = 0; j < 16; j++) acc[a][b][j] = 0.f;
+
+    const int NK = K / 32;
+    // prologue: step 0
+    uint4 xr[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) xr[i] = *reinterpret_cast<const uint4 *>(srow[i]);
+    WRaw<FMT> wr[2];
+    wr[0] = load_wraw<FMT>(mA0, ROWS_A, K, ra[0], 0, g);
+    wr[1] = load_wraw<FMT>(mA1, ROWS_A, K, ra[1], 0, g);
+#pragma unroll
+    for (int i = 0; i < 2; i++) *reinterpret_cast<uint4 *>(&bt[0][sdst[i]]) = xr[i];
+    __syncthreads();
+
+    for (int kb = 0; kb < NK; kb++) {
+        const int cur = kb & 1;
+        // prefetch step kb + 1 (the last step re-reads itself: no branch, so
+        // the loads stay in flight across the MFMAs below)
+        const int kn = min(kb + 1, NK - 1);
+        WRaw<FMT> wn[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) xr[i] = *reinterpret_cast<const uint4 *>(srow[i] + 32 * kn);
+        wn[0] = load_wraw<FMT>(mA0, ROWS_A, K, ra[0], kn, g);
+        wn[1] = load_wraw<FMT>(mA1, ROWS_A, K, ra[1], kn, g);
+        half8_t af[2][2];
+        dequant_frag<FMT>(wr[0], af[0][0], af[0][1]);
+        dequant_frag<FMT>(wr[1], af[1][0], af[1][1]);
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+#pragma unroll
+            for (int s = 0; s < 2; s++) {
+                const half8_t bf =
+                    *reinterpret_cast<const half8_t *>(&bt[cur][(32 * b + l32) * PF_LDS_ROW + 16 * s + 8 * g]);
+                acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0][s], bf, acc[0][b], 0, 0, 0);
+                acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[1][s], bf, acc[1][b], 0, 0, 0);
+            }
+        }
+        // stage step kb + 1 into the other buffer (read by nobody during step
+        // kb; after the last step nobody reads it at all)
+#pragma unroll
+        for (int i = 0; i < 2; i++) *reinterpret_cast<uint4 *>(&bt[cur ^ 1][sdst[i]]) = xr[i];
+        wr[0] = wn[0];
+        wr[1] = wn[1];
+        __syncthreads();
+    }
+
+    // epilogue.  acc[a][b][j] = out[row m][token n], m = 8 (j/4) + 4 g + j%4, n = 32 b + l32
+    if (MODE == 0) {
+        if (!sub_ok[0]) return;
+        const float ts_g = p.tscale ? p.tscale[3 * tile.e + 0] : 1.f;
+        const float ts_u = p.tscale ? p.tscale[3 * tile.e + 1] : 1.f;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int n = 32 * b + l32;
+            if (n >= tile.rows) continue;
+            _Float16 *hrow = p.h + (size_t)(tile.row0 + n) * p.F + r0 + 4 * g;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                uint32_t pk[2];
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    const float g0 = acc[0][b][4 * q + 2 * i] * ts_g, u0 = acc[1][b][4 * q + 2 * i] * ts_u;
+                    const float g1 = acc[0][b][4 * q + 2 * i + 1] * ts_g, u1 = acc[1][b][4 * q + 2 * i + 1] * ts_u;
+                    const _Float16 h0 = (_Float16)silu_mul(g0, u0), h1 = (_Float16)silu_mul(g1, u1);
+                    pk[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                }
+                *reinterpret_cast<uint2 *>(hrow + 8 * q) = make_uint2(pk[0], pk[1]);
+            }
+        }
+    } else {
+        const float ts_d = p.tscale ? p.tscale[3 * tile.e + 2] : 1.f;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int n = 32 * b + l32;
+            if (n >= tile.rows) continue;
+            const float c = p.perm_w[tile.row0 + n] * ts_d;
+            float *orow = p.o + (size_t)(tile.row0 + n) * p.D;
+#pragma unroll
+            for (int a = 0; a < 2; a++) {
+                if (!sub_ok[a]) continue;
+                const int dr = r0 + 32 * a + 4 * g;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    float4 v;
+                    v.x = acc[a][b][4 * q + 0] * c;
+                    v.y = acc[a][b][4 * q + 1] * c;
+                    v.z = acc[a][b][4 * q + 2] * c;
+                    v.w = acc[a][b][4 * q + 3] * c;
+                    *reinterpret_cast<float4 *>(orow + dr + 8 * q) = v;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// pf_combine: y[t, 4i..4i+3] = sum over t's slots (routed in top-k order,
+// then shared) of O[pos] (already scaled by the slot's weight).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(PF_THREADS) pf_combine(PfParams p) {
+    const size_t i = (size_t)blockIdx.x * PF_THREADS + threadIdx.x;
+    const int D4 = p.D / 4;
+    if (i >= (size_t)p.T * D4) return;
+    const int t = (int)(i / D4), c = (int)(i % D4);
+    const int KS = p.K + p.S;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < KS; j++) {
+        const int r = p.pos[(size_t)t * KS + j];
+        if (r < 0) continue;
+        const float4 v = reinterpret_cast<const float4 *>(p.o + (size_t)r * p.D)[c];
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    reinterpret_cast<float4 *>(p.y)[i] = s;
+}
+
+template <int FMT>
+void launch_gemms(const PfParams &p, hipStream_t st) {
+    const int mt0 = (p.F + 127) / 128, mt1 = (p.D + 255) / 256;
+    MOE_LAUNCH(3, (pf_gemm<FMT, 0>), dim3(p.tiles_max * mt0), dim3(PF_THREADS), st, p);
+    MOE_LAUNCH(4, (pf_gemm<FMT, 1>), dim3(p.tiles_max * mt1), dim3(PF_THREADS), st, p);
+}
+
+}  // namespace
+
+const char *const kPrefillNames = "pf_router;pf_scan;pf_scatter;pf_gemm_gateup;pf_gemm_down;pf_combine";
+
+size_t prefill_ws_bytes(int D, int F, int E, int S, int K, int T) { return pf_layout(D, F, E, S, K, T).total; }
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
+    if (a.E > 256 || a.K > PF_MAX_TOPK || a.D % 32 || a.F % 32) return hipErrorNotSupported;
+    const PfWs L = pf_layout(a.D, a.F, a.E, a.S, a.K, a.T);
+    PfParams p{};
+    p.D = a.D; p.F = a.F; p.E = a.E; p.S = a.S; p.K = a.K; p.T = a.T; p.act = a.act;
+    p.NW = L.NW; p.R = L.R; p.tiles_max = L.tiles_max;
+    p.want_x16 = a.route_only ? 0 : 1;
+    p.ev = a.ev;
+    p.expert_bytes = a.expert_bytes;
+    p.x = a.x; p.router = a.router; p.bias = a.bias; p.experts = a.experts; p.tscale = a.tscale;
+    p.y = a.y; p.idx_out = a.idx_out; p.w_out = a.w_out; p.logits_out = a.logits_out;
+    p.x16 = wsp<_Float16>(a.ws, L.x16);
+    p.idx = wsp<int32_t>(a.ws, L.idx);
+    p.w = wsp<float>(a.ws, L.w);
+    p.mask = wsp<unsigned long long>(a.ws, L.mask);
+    p.wp = wsp<int32_t>(a.ws, L.wp);
+    p.off = wsp<int32_t>(a.ws, L.off);
+    p.tiles = wsp<PfTile>(a.ws, L.tiles);
+    p.meta = wsp<int32_t>(a.ws, L.meta);
+    p.perm_tok = wsp<int32_t>(a.ws, L.perm_tok);
+    p.perm_w = wsp<float>(a.ws, L.perm_w);
+    p.pos = wsp<int32_t>(a.ws, L.pos);
+    p.h = wsp<_Float16>(a.ws, L.h);
+    p.o = wsp<float>(a.ws, L.o);
+    const int nb64 = (a.T + 63) / 64;
+    if (!a.given_idx) {
+        if (a.act == MOE_ACT_F32)
+            MOE_LAUNCH(0, (pf_router<0>), dim3(nb64), dim3(PF_THREADS), st, p);
+        else
+            MOE_LAUNCH(0, (pf_router<1>), dim3(nb64), dim3(PF_THREADS), st, p);
+        if (a.route_only) return hipGetLastError();
+    } else {
+        p.idx = const_cast<int32_t *>(a.given_idx);
+        p.w = const_cast<float *>(a.given_w);
+        const size_t n8 = (size_t)a.T * a.D / 8;
+        const dim3 gx((unsigned)((n8 + PF_THREADS - 1) / PF_THREADS));
+        if (a.act == MOE_ACT_F32)
+            hipLaunchKernelGGL((pf_x16<0>), gx, dim3(PF_THREADS), 0, st, p);
+        else
+            hipLaunchKernelGGL((pf_x16<1>), gx, dim3(PF_THREADS), 0, st, p);
+        MOE_LAUNCH(0, pf_mask_given, dim3(nb64), dim3(PF_THREADS), st, p);
+    }
+    MOE_LAUNCH(1, pf_scan, dim3(1), dim3(PF_THREADS), st, p);
+    MOE_LAUNCH(2, pf_scatter, dim3((a.T + PF_THREADS - 1) / PF_THREADS), dim3(PF_THREADS), st, p);
+    if (a.fmt == FMT_Q4_1)
+        launch_gemms<FMT_Q4_1>(p, st);
+    else if (a.fmt == FMT_NVFP4)
+        launch_gemms<FMT_NVFP4>(p, st);
+    else
+        launch_gemms<FMT_BF16>(p, st);
+    const size_t n4 = (size_t)a.T * a.D / 4;
+    MOE_LAUNCH(5, pf_combine, dim3((unsigned)((n4 + PF_THREADS - 1) / PF_THREADS)), dim3(PF_THREADS), st, p);
+    return hipGetLastError();
+}
+
 
 }  // namespace moe

@@ -94,7 +94,7 @@ def test_entry_points_validate_before_enqueue(L):
     # bad token counts and activation type
     assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, 0, 0, fake, None, None, fake, 1 << 30, None) == INVALID
     assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), fake, 5, 1, fake, None, None, fake, 1 << 30, None) == UNSUPPORTED
-    assert L.moe_expert_ffn_q4(ctypes.byref(d), fake, 0, 9, fake, None, fake, fake, fake, fake, 1 << 30, None) == INVALID
+    assert L.moe_expert_ffn_q4(ctypes.byref(d), fake, 0, 70000, fake, None, fake, fake, fake, fake, 1 << 30, None) == INVALID
     # NVFP4 needs tensor scales
     d4 = _d(wfmt=2)
     assert L.moe_expert_ffn_q4(ctypes.byref(d4), fake, 0, 1, fake, None, fake, fake, fake, fake, 1 << 30, None) == INVALID

@@ -221,6 +221,17 @@ def test_router_logits_match_numpy_matmul(orc):
     np.testing.assert_allclose(logits, x @ wr.T, rtol=1e-12, atol=1e-12)
 
 
+def test_router_logits_only_match_numpy_matmul_with_bias(orc):
+    # the logits-only entry (used for many-token routing checks) against a
+    # library matmul, with a Zipf router prior
+    dims = gen.LayerDims(256, 64, n_routed=32, n_shared=1, top_k=6, wfmt="q4_1")
+    layer = gen.make_layer(dims, cfg_id=82, zipf_s=1.1)
+    x = gen.make_hidden(82, 5, 256).double().numpy()
+    wr = layer.router.view(torch.bfloat16).to(torch.float64).numpy()
+    ref = x @ wr.T + layer.router_bias.double().numpy()
+    np.testing.assert_allclose(orc.router_logits(layer, x), ref, rtol=1e-12, atol=1e-12)
+
+
 # --------------------------------------------------------------------------- expert FFN / layer
 
 def _torch_decode(layer, e, m):
