@@ -37,7 +37,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int PF_BM = 128;          // rows (token slots) per GEMM tile
 constexpr int PF_THREADS = 256;     // 4 waves
 constexpr int PF_RT = 64;           // tokens per router block
-constexpr int PF_LDS_ROW = 40;      // halfs per staged row (32 data + 8 pad)
 constexpr int PF_MAX_TOPK = 8;
 
 struct PfTile {
@@ -362,6 +361,11 @@ __global__ void __launch_bounds__(PF_THREADS) pf_scatter(PfParams p) {
     }
 }
 
+// The grouped-GEMM helpers use device-only types (buffer resources) and are
+// compiled for the device side of the build only; the host side sees the
+// kernels' launch stubs.
+#if defined(__HIP_DEVICE_COMPILE__)
+
 // ---------------------------------------------------------------------------
 // Weight fragments for v_mfma_f32_32x32x16_f16.  One call covers 32 inputs of
 // one weight row (one q4_1 block): lane group g = lane / 32 holds, for MFMA
@@ -373,25 +377,9 @@ template <> struct WRaw<FMT_Q4_1> { uint2 c; uint32_t dm; };
 template <> struct WRaw<FMT_NVFP4> { uint32_t c0, c1; uint32_t s; };
 template <> struct WRaw<FMT_BF16> { uint4 v0, v1; };
 
-// base: matrix start; rows x K; row r, block b (32 inputs), lane group g
-template <int FMT>
-__device__ __forceinline__ WRaw<FMT> load_wraw(const uint8_t *base, int rows, int K, int r, int b, int g) {
-    WRaw<FMT> w;
-    if constexpr (FMT == FMT_Q4_1) {
-        const uint8_t *c = base + (size_t)r * (K / 2) + b * 16 + g * 8;
-        w.c = *reinterpret_cast<const uint2 *>(c);
-        w.dm = *reinterpret_cast<const uint32_t *>(base + (size_t)rows * (K / 2) + ((size_t)r * (K / 32) + b) * 4);
-    } else if constexpr (FMT == FMT_NVFP4) {
-        const uint8_t *c = base + (size_t)r * (K / 2) + b * 16 + g * 4;
-        w.c0 = *reinterpret_cast<const uint32_t *>(c);
-        w.c1 = *reinterpret_cast<const uint32_t *>(c + 8);
-        w.s = *reinterpret_cast<const uint16_t *>(base + (size_t)rows * (K / 2) + (size_t)r * (K / 16) + b * 2);
-    } else {
-        const uint16_t *v = reinterpret_cast<const uint16_t *>(base) + (size_t)r * K + b * 32 + g * 8;
-        w.v0 = *reinterpret_cast<const uint4 *>(v);
-        w.v1 = *reinterpret_cast<const uint4 *>(v + 16);
-    }
-    return w;
+// Raw buffer resource over [base, base + bytes): loads past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // 4 nibbles (bytes of t, each < 16) -> two fp16 pairs holding the integers
@@ -460,15 +448,130 @@ __device__ __forceinline__ int xcd_logical(int b, int n) {
     return x * q + min(x, r) + b / 8;
 }
 
+// LDS bytes between consecutive lanes of a 2-byte buffer-to-LDS copy: each
+// lane's value lands zero-extended in a dword of its own (measured on gfx950)
+constexpr int NV_DMA16_STRIDE = 4;
+
+// Weight stage of pf_gemm: the raw fragments of the block's 256 weight rows
+// for one 32-input step, copied to LDS as they are stored in HBM
+//   q4_1:  codes [256][16 B], then {d, m} [256][4 B]
+//   NVFP4: codes [256][16 B], then E4M3 pairs [256][2 B]
+//   bf16:  values [256][64 B]
+template <int FMT> struct WStage;
+template <> struct WStage<FMT_Q4_1> { static constexpr int BYTES = 256 * 20, SCALE_OFF = 4096, DMA = 2; };
+// (the NVFP4 scale region is sized for 4 bytes per row so that the 2-byte
+// DMA stays inside it whichever lane stride the hardware uses)
+template <> struct WStage<FMT_NVFP4> {
+    static constexpr int BYTES = 256 * 20, SCALE_OFF = 4096, DMA = 2, SCALE_STRIDE = NV_DMA16_STRIDE;
+};
+template <> struct WStage<FMT_BF16> { static constexpr int BYTES = 256 * 64, DMA = 4; };
+
+// DMA copies issued per thread per K-step (2 token chunks + the weight stage);
+// the wait for a stage three steps back relies on this count
+template <int FMT> constexpr int pf_loads_per_step() { return 2 + WStage<FMT>::DMA; }
+
+// s_waitcnt with vmcnt(n) only (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr int PF_NS = 4;       // LDS stages in flight
+constexpr int PF_UNROLL = 16;  // K-steps per loop trip (multiple of PF_NS)
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release
+// half waits for every outstanding load, which would drain the prefetch
+// pipeline).  Callers order the LDS traffic themselves: an explicit vmcnt
+// wait for the DMA writes, and every LDS read of a stage is consumed before
+// the barrier that lets it be overwritten.  The signal fences keep the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void pf_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// slot of (row, 16-byte chunk) in a token stage: chunks XOR-swizzled by row
+// so the fragment reads of 8 consecutive rows hit distinct banks
+__device__ __forceinline__ int pf_slot(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// fragment of weight row `row` of a weight stage (lane group g)
+template <int FMT>
+__device__ __forceinline__ WRaw<FMT> wraw_from_lds(const uint8_t *ws, int row, int g) {
+    WRaw<FMT> w;
+    if constexpr (FMT == FMT_Q4_1) {
+        w.c = *reinterpret_cast<const uint2 *>(ws + row * 16 + 8 * g);
+        w.dm = *reinterpret_cast<const uint32_t *>(ws + WStage<FMT>::SCALE_OFF + row * 4);
+    } else if constexpr (FMT == FMT_NVFP4) {
+        w.c0 = *reinterpret_cast<const uint32_t *>(ws + row * 16 + 4 * g);
+        w.c1 = *reinterpret_cast<const uint32_t *>(ws + row * 16 + 8 + 4 * g);
+        w.s = *reinterpret_cast<const uint16_t *>(ws + WStage<FMT>::SCALE_OFF + row * WStage<FMT>::SCALE_STRIDE);
+    } else {
+        w.v0 = *reinterpret_cast<const uint4 *>(ws + row * 64 + 16 * g);
+        w.v1 = *reinterpret_cast<const uint4 *>(ws + row * 64 + 32 + 16 * g);
+    }
+    return w;
+}
+
+// DMA sources of one thread in pf_gemm: token buffer and weight matrices
+// (buffer resources) with this thread's byte offsets at step 0
+template <int FMT> struct PfDma {
+    __amdgpu_buffer_rsrc_t rx;
+    uint32_t xo[2];
+    __amdgpu_buffer_rsrc_t rw[WStage<FMT>::DMA];
+    uint32_t wo[WStage<FMT>::DMA];
+    int wave;
+};
+
+// copy step ks of the token tile and of the weight fragments into one stage
+template <int FMT>
+__device__ __forceinline__ void pf_issue(const PfDma<FMT> &d, uint4 *xs, uint8_t *wsb, int ks) {
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rx, (lds_void *)(xs + i * 256 + 64 * d.wave), 16, d.xo[i], 64 * ks,
+                                                 0, 0);
+    if constexpr (FMT == FMT_BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw[i], (lds_void *)(wsb + 16 * (i * 256 + 64 * d.wave)), 16,
+                                                     d.wo[i], 64 * ks, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw[0], (lds_void *)(wsb + 16 * 64 * d.wave), 16, d.wo[0], 16 * ks,
+                                                 0, 0);
+        if constexpr (FMT == FMT_Q4_1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw[1], (lds_void *)(wsb + WStage<FMT>::SCALE_OFF + 4 * 64 * d.wave),
+                                                     4, d.wo[1], 4 * ks, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                d.rw[1], (lds_void *)(wsb + WStage<FMT>::SCALE_OFF + WStage<FMT>::SCALE_STRIDE * 64 * d.wave), 2,
+                d.wo[1], 2 * ks, 0, 0);
+    }
+}
+#endif  // __HIP_DEVICE_COMPILE__ (helpers of pf_gemm)
+
 // ---------------------------------------------------------------------------
 // pf_gemm<MODE>: one block = one tile of <= 128 rows of one expert x 128
 // (gate/up: features; MODE 0) or 256 (down: outputs; MODE 1) weight rows.
 // Wave w owns 2 A-operand row groups of 32 (gate and up of the same 32
 // features, or 2 x 32 down rows) against all 128 tile rows (4 x 32).
+// Pipeline: the token tile and the block's raw weight fragments of step k
+// are copied to LDS stage k % 4 by buffer-to-LDS DMA three steps ahead; the
+// weights are dequantised from LDS into MFMA operands.
 // ---------------------------------------------------------------------------
 template <int FMT, int MODE>
 __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfParams p) {
-    __shared__ __attribute__((aligned(16))) _Float16 bt[2][PF_BM * PF_LDS_ROW];
+#if defined(__HIP_DEVICE_COMPILE__)
+    // one LDS object per stage: stage indices are compile-time after
+    // unrolling, so alias analysis separates a stage's DMA writes from the
+    // reads of the others (no conservative vmcnt waits before ds_read)
+    __shared__ uint4 x0s[PF_BM * 4], x1s[PF_BM * 4], x2s[PF_BM * 4], x3s[PF_BM * 4];
+    __shared__ __attribute__((aligned(16))) uint8_t w0s[WStage<FMT>::BYTES], w1s[WStage<FMT>::BYTES],
+        w2s[WStage<FMT>::BYTES], w3s[WStage<FMT>::BYTES];
+#define PF_XST(st) ((st) == 0 ? x0s : (st) == 1 ? x1s : (st) == 2 ? x2s : x3s)
+#define PF_WST(st) ((st) == 0 ? w0s : (st) == 1 ? w1s : (st) == 2 ? w2s : w3s)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
@@ -483,28 +586,57 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfParams p) {
     const int ROWS_A = MODE == 0 ? p.F : p.D;      // rows of the weight matrix
     const uint8_t *eb = p.experts + (size_t)tile.e * p.expert_bytes;
     const size_t mb_gu = mat_bytes<FMT>(p.F, p.D);
-    const uint8_t *mA0 = MODE == 0 ? eb : eb + 2 * mb_gu;             // gate | down
-    const uint8_t *mA1 = MODE == 0 ? eb + mb_gu : eb + 2 * mb_gu;     // up   | down
-    int r0 = MODE == 0 ? mt * 128 + 32 * wave : mt * 256 + 64 * wave; // first A row of sub 0
-    int ra[2];
-    ra[0] = r0 + l32;
-    ra[1] = MODE == 0 ? r0 + l32 : r0 + 32 + l32;
-    const bool sub_ok[2] = {r0 < ROWS_A, (MODE == 0 ? r0 : r0 + 32) < ROWS_A};
-    ra[0] = min(ra[0], ROWS_A - 1);
-    ra[1] = min(ra[1], ROWS_A - 1);
+    const uint32_t mbytes = (uint32_t)mat_bytes<FMT>(ROWS_A, K);
+    const int r0 = MODE == 0 ? mt * 128 + 32 * wave : mt * 256 + 64 * wave;  // first A row of sub 0
+    const int r1 = MODE == 0 ? r0 : r0 + 32;
+    const bool sub_ok[2] = {r0 < ROWS_A, r1 < ROWS_A};
+    // this wave's two row groups inside a weight stage
+    const int lrow0 = MODE == 0 ? 32 * wave + l32 : 64 * wave + l32;
+    const int lrow1 = MODE == 0 ? 128 + 32 * wave + l32 : 64 * wave + 32 + l32;
 
-    // staging: thread stages rows (tid >> 2) and (tid >> 2) + 64, part tid & 3
-    const int part = tid & 3;
-    const _Float16 *srow[2];
+    // token DMA: this thread fills slots (i * 256 + 64 * wave + lane) of a
+    // stage, i = 0, 1, i.e. rows 64 i + 16 wave + lane / 4, one chunk each;
+    // byte offsets inside the token buffer, the step goes in the scalar offset
+    const __amdgpu_buffer_rsrc_t rx =
+        MODE == 0 ? buf_rsrc(p.x16, (uint32_t)((size_t)p.T * p.D * 2))
+                  : buf_rsrc(p.h + (size_t)tile.row0 * p.F, (uint32_t)tile.rows * p.F * 2);
+    uint32_t xo[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        const int rr = min((tid >> 2) + 64 * i, tile.rows - 1);
-        if (MODE == 0)
-            srow[i] = p.x16 + (size_t)p.perm_tok[tile.row0 + rr] * p.D + 8 * part;
-        else
-            srow[i] = p.h + (size_t)(tile.row0 + rr) * p.F + 8 * part;
+        const int r = 64 * i + 16 * wave + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 1) & 3);
+        const int rr = min(r, tile.rows - 1);
+        const uint32_t row = MODE == 0 ? (uint32_t)p.perm_tok[tile.row0 + rr] * p.D : (uint32_t)rr * p.F;
+        xo[i] = 2 * row + 16 * c;
     }
-    const int sdst[2] = {((tid >> 2)) * PF_LDS_ROW + 8 * part, ((tid >> 2) + 64) * PF_LDS_ROW + 8 * part};
+    // weight DMA: stage row q of the block -> weight row, matrix
+    //   MODE 0: q < 128 gate row mt*128 + q, else up row mt*128 + q - 128
+    //   MODE 1: down row mt*256 + q
+    PfDma<FMT> dma;
+    dma.rx = rx;
+    dma.xo[0] = xo[0];
+    dma.xo[1] = xo[1];
+    dma.wave = wave;
+    if constexpr (FMT == FMT_BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int j = i * 256 + 64 * wave + lane;  // 16-byte chunk of the stage
+            const int q = j >> 2;                       // row of the stage (uniform matrix per wave)
+            const int qw = 64 * i + 16 * wave;          // first row of the wave's chunks
+            const int rowA = min(MODE == 0 ? mt * 128 + (q & 127) : mt * 256 + q, ROWS_A - 1);
+            const uint8_t *mat = MODE == 0 ? (qw < 128 ? eb : eb + mb_gu) : eb + 2 * mb_gu;
+            dma.rw[i] = buf_rsrc(mat, mbytes);
+            dma.wo[i] = (uint32_t)rowA * K * 2 + 16 * (j & 3);
+        }
+    } else {
+        const int q = 64 * wave + lane;
+        const int rowA = min(MODE == 0 ? mt * 128 + (q & 127) : mt * 256 + q, ROWS_A - 1);
+        const uint8_t *mat = MODE == 0 ? (64 * wave < 128 ? eb : eb + mb_gu) : eb + 2 * mb_gu;
+        dma.rw[0] = dma.rw[1] = buf_rsrc(mat, mbytes);
+        dma.wo[0] = (uint32_t)rowA * (K / 2);
+        dma.wo[1] = (uint32_t)ROWS_A * (K / 2) + (uint32_t)rowA * (FMT == FMT_Q4_1 ? (K / 32) * 4 : K / 16);
+    }
+    const int NK = K / 32;
 
     f32x16_t acc[2][4];
 #pragma unroll
@@ -514,48 +646,38 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfParams p) {
 #pragma unroll
             for (int j = 0; j < 16; j++) acc[a][b][j] = 0.f;
 
-    const int NK = K / 32;
-    // prologue: step 0
-    uint4 xr[2];
 #pragma unroll
-    for (int i = 0; i < 2; i++) xr[i] = *reinterpret_cast<const uint4 *>(srow[i]);
-    WRaw<FMT> wr[2];
-    wr[0] = load_wraw<FMT>(mA0, ROWS_A, K, ra[0], 0, g);
-    wr[1] = load_wraw<FMT>(mA1, ROWS_A, K, ra[1], 0, g);
-#pragma unroll
-    for (int i = 0; i < 2; i++) *reinterpret_cast<uint4 *>(&bt[0][sdst[i]]) = xr[i];
-    __syncthreads();
+    for (int s = 0; s < PF_NS - 1; s++) pf_issue<FMT>(dma, PF_XST(s), PF_WST(s), min(s, NK - 1));
 
-    for (int kb = 0; kb < NK; kb++) {
-        const int cur = kb & 1;
-        // prefetch step kb + 1 (the last step re-reads itself: no branch, so
-        // the loads stay in flight across the MFMAs below)
-        const int kn = min(kb + 1, NK - 1);
-        WRaw<FMT> wn[2];
+    // 16 steps per loop trip: the wait-count analysis is exact inside the
+    // unrolled body but drains every load at a loop header
+    for (int kb0 = 0; kb0 < NK; kb0 += PF_UNROLL) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) xr[i] = *reinterpret_cast<const uint4 *>(srow[i] + 32 * kn);
-        wn[0] = load_wraw<FMT>(mA0, ROWS_A, K, ra[0], kn, g);
-        wn[1] = load_wraw<FMT>(mA1, ROWS_A, K, ra[1], kn, g);
-        half8_t af[2][2];
-        dequant_frag<FMT>(wr[0], af[0][0], af[0][1]);
-        dequant_frag<FMT>(wr[1], af[1][0], af[1][1]);
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
+        for (int u = 0; u < PF_UNROLL; u++) {
+            const int kb = kb0 + u;
+            if (kb >= NK) break;
+            // stage kb (issued 3 steps back) has landed for this wave; after
+            // the barrier, for every wave, and stage kb - 1 is free
+            wait_vmcnt<2 * pf_loads_per_step<FMT>()>();
+            pf_barrier();
+            // past the end: reload the last step (never read)
+            pf_issue<FMT>(dma, PF_XST((u + PF_NS - 1) % PF_NS), PF_WST((u + PF_NS - 1) % PF_NS),
+                          min(kb + PF_NS - 1, NK - 1));
+            const uint8_t *wsb = PF_WST(u % PF_NS);
+            half8_t af[2][2];
+            dequant_frag<FMT>(wraw_from_lds<FMT>(wsb, lrow0, g), af[0][0], af[0][1]);
+            dequant_frag<FMT>(wraw_from_lds<FMT>(wsb, lrow1, g), af[1][0], af[1][1]);
+            const _Float16 *stg = reinterpret_cast<const _Float16 *>(PF_XST(u % PF_NS));
 #pragma unroll
             for (int s = 0; s < 2; s++) {
-                const half8_t bf =
-                    *reinterpret_cast<const half8_t *>(&bt[cur][(32 * b + l32) * PF_LDS_ROW + 16 * s + 8 * g]);
-                acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0][s], bf, acc[0][b], 0, 0, 0);
-                acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[1][s], bf, acc[1][b], 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    const half8_t bf = *reinterpret_cast<const half8_t *>(stg + 8 * pf_slot(32 * b + l32, 2 * s + g));
+                    acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0][s], bf, acc[0][b], 0, 0, 0);
+                    acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[1][s], bf, acc[1][b], 0, 0, 0);
+                }
             }
         }
-        // stage step kb + 1 into the other buffer (read by nobody during step
-        // kb; after the last step nobody reads it at all)
-#pragma unroll
-        for (int i = 0; i < 2; i++) *reinterpret_cast<uint4 *>(&bt[cur ^ 1][sdst[i]]) = xr[i];
-        wr[0] = wn[0];
-        wr[1] = wn[1];
-        __syncthreads();
     }
 
     // epilogue.  acc[a][b][j] = out[row m][token n], m = 8 (j/4) + 4 g + j%4, n = 32 b + l32
@@ -605,7 +727,11 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfParams p) {
             }
         }
     }
+
+#endif  // __HIP_DEVICE_COMPILE__
 }
+#undef PF_XST
+#undef PF_WST
 
 // ---------------------------------------------------------------------------
 // pf_combine: y[t, 4i..4i+3] = sum over t's slots (routed in top-k order,
