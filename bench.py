@@ -112,8 +112,15 @@ def kernel_algo_bytes(dims, T: int, routed_union: float):
     a = E * D * 2 + S * 2 * gu + T * D * 4 + T * E * 4 + S * T * F * 4
     b = T * E * 4 + U * 2 * gu + T * D * 4 + U * T * F * 4
     c = (U + S) * dn + (U + S) * T * F * 4 + T * D * 4
+    K = dims.top_k
+    pairs = T * K + S * T  # (expert, token) rows of h
+    bn = {"bn_norm": 2 * T * D * 4,
+          "pf_logits": E * D * 2 + T * D * 4 + T * E * 4,
+          "bn_select": T * E * 4,
+          "bn_gateup": (U + S) * 2 * gu + T * D * 4 + pairs * F * 4,
+          "bn_down": (U + S) * dn + pairs * F * 4 + T * D * 4}
     return {"b1_route_shared": a, "b1_topk_gateup": b, "b1_down": c,
-            "phase_a_kernel": a, "select_kernel": T * E * 4, "gateup_kernel": b, "down_kernel": c}
+            "phase_a_kernel": a, "select_kernel": T * E * 4, "gateup_kernel": b, "down_kernel": c, **bn}
 
 
 def time_kernels(args, stack, xs, ws, dims, T):
@@ -328,7 +335,7 @@ def bench_prefill(args):
     per_kernel = {k: dict(us_per_launch=round(v, 2)) for k, v in kus.items()}
     per_kernel["pf_gemm_gateup"]["tflops"] = round(fl_gu / (kus["pf_gemm_gateup"] * 1e-6) / 1e12, 1)
     per_kernel["pf_gemm_down"]["tflops"] = round(fl_dn / (kus["pf_gemm_down"] * 1e-6) / 1e12, 1)
-    per_kernel["pf_router"]["tflops"] = round(fl_rt / (kus["pf_router"] * 1e-6) / 1e12, 1)
+    per_kernel["pf_logits"]["tflops"] = round(fl_rt / (kus["pf_logits"] * 1e-6) / 1e12, 1)
     return dict(
         metric="MoE-layer prefill tokens/s (grouped GEMM on MFMA), 4-bit weights",
         value=round(T / (ms * 1e-3), 1), unit="tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,

@@ -180,14 +180,14 @@ moe_status moe_stack_decode(const moe_dims *dims, int32_t n_layers, const moe_la
  * pages time whole-model decode only (tokens/s on the two named machines);
  * this call gives the per-kernel split of the decode step that those
  * figures are made of.  Blocks the calling thread until the stack is done.
- *   kernel_us  (host) float [4]: mean duration in microseconds of each
- *              kernel slot of a layer, averaged over the n_layers layers
- *              (-1 for a slot that did not run).
+ *   kernel_us  (host) float [5]: mean duration in microseconds of each
+ *              kernel slot of a layer, averaged over the layers that ran it
+ *              (-1 for a slot that never ran).
  *   n_kernels  (host) receives the number of slots used (3 on the batch-1
- *              path, 4 on the general path).
+ *              path, 5 on the small-batch path, 4 on the general path).
  *   names      (host, optional) receives the slots' kernel names separated
  *              by ';' (truncated to names_cap bytes, NUL-terminated).
- * Creates and destroys 8 * n_layers HIP events (n_layers <= 4096); not for
+ * Creates and destroys 10 * n_layers HIP events (n_layers <= 4096); not for
  * use under stream capture.
  */
 moe_status moe_stack_decode_timed(const moe_dims *dims, int32_t n_layers, const moe_layer_weights *layers,
@@ -199,12 +199,12 @@ moe_status moe_stack_decode_timed(const moe_dims *dims, int32_t n_layers, const 
  * Measurement variant of moe_layer_forward_prefill (no routing outputs): the
  * same kernels, each launched with a start/stop event pair on its dispatch.
  * Blocks the calling thread until the layer is done.
- *   kernel_us  (host) float [6]: duration in microseconds of each kernel, in
- *              launch order (router, scan, scatter, gate/up GEMM, down GEMM,
- *              combine); -1 for a kernel that did not run.
- *   n_kernels  (host) receives 6.
+ *   kernel_us  (host) float [7]: duration in microseconds of each kernel, in
+ *              launch order (router logits, top-k, scan, scatter, gate/up
+ *              GEMM, down GEMM, combine); -1 for a kernel that did not run.
+ *   n_kernels  (host) receives 7.
  *   names      (host, optional) receives the kernel names separated by ';'.
- * Creates and destroys 12 HIP events; not for use under stream capture.
+ * Creates and destroys 14 HIP events; not for use under stream capture.
  */
 moe_status moe_layer_forward_prefill_timed(const moe_dims *dims, const moe_layer_weights *w, const void *x,
                                            int32_t act, int32_t n_tokens, float *y, void *ws, size_t ws_bytes,

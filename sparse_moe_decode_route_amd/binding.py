@@ -251,7 +251,7 @@ def stack_decode_timed(stack: StackHandle, x0: torch.Tensor, ws: Optional[torch.
     idx_trace = torch.empty((L, T, dims.top_k), dtype=torch.int32, device=dev) if trace else None
     ws = ws if ws is not None else workspace(dims, T, dev)
     d = cdims(dims)
-    us = (ctypes.c_float * 4)()
+    us = (ctypes.c_float * 8)()
     nk = ctypes.c_int32(0)
     names = ctypes.create_string_buffer(256)
     _check(lib().moe_stack_decode_timed(ctypes.byref(d), L, stack.carr, _ptr(x0), T, _ptr(y), _ptr(idx_trace),

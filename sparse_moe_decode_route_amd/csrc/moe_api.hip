@@ -53,7 +53,7 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Decode-path workspace (n_tokens <= 8).
 struct DecodeWs {
-    size_t logits, idx, w, xbuf, xconv, meta, act_expert, act_mask, act_w, h, ybuf0, ybuf1, total;
+    size_t logits, idx, w, xbuf, xconv, meta, act_expert, act_mask, act_w, h, ybuf0, ybuf1, work, pairs, total;
     int amax;
 };
 
@@ -78,6 +78,8 @@ DecodeWs decode_ws(const moe_dims &d, int T) {
     L.h = take((size_t)L.amax * T * d.d_ff * 4);
     L.ybuf0 = take((size_t)T * d.d_model * 4);
     L.ybuf1 = take((size_t)T * d.d_model * 4);
+    L.work = take((size_t)(d.n_shared * ((T + 1) / 2) + T * d.top_k) * 16);
+    L.pairs = take((size_t)(d.n_shared * T + T * d.top_k) * 16);
     L.total = o;
     return L;
 }
@@ -107,6 +109,8 @@ moe::DecodeParams base_params(const moe_dims &d, int T, void *ws, const DecodeWs
     p.act_mask = at<uint32_t>(ws, L.act_mask);
     p.act_w = at<float>(ws, L.act_w);
     p.h = at<float>(ws, L.h);
+    p.work = at<int32_t>(ws, L.work);
+    p.pairs = at<int32_t>(ws, L.pairs);
     return p;
 }
 
@@ -167,20 +171,24 @@ moe::PrefillArgs prefill_args(const moe_dims &d, const void *x, int act, int T, 
     return a;
 }
 
-// *path (optional) receives 1 for the batch-1 path, 2 for the general one.
+// The batch-1 path, else the small-batch path, else the general one (any
+// shape).  *path (optional) receives 1, 3 or 2 respectively.  Each launcher
+// checks its shape before enqueueing anything.
 hipError_t launch_any(const moe::DecodeParams &p, hipStream_t st, int *path = nullptr) {
     hipError_t e = moe::launch_decode_b1(p, st);
     if (path) *path = 1;
-    if (e == hipErrorNotSupported) {
-        if (path) *path = 2;
-        return moe::launch_decode(p, st);
-    }
-    return e;
+    if (e != hipErrorNotSupported) return e;
+    e = moe::launch_decode_bn(p, st);
+    if (path) *path = 3;
+    if (e != hipErrorNotSupported) return e;
+    if (path) *path = 2;
+    return moe::launch_decode(p, st);
 }
 
 // Kernel names of one layer's slots, per path (slot order of MOE_LAUNCH).
 const char *const kB1Names = "b1_route_shared;b1_topk_gateup;b1_down";
 const char *const kGenericNames = "phase_a_kernel;select_kernel;gateup_kernel;down_kernel";
+const char *const kBnNames = "bn_norm;pf_logits;bn_select;bn_gateup;bn_down";
 
 }  // namespace
 
@@ -457,7 +465,7 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
         destroy();
         return s;
     }
-    const int slots = path == 1 ? 3 : moe::MAX_KERNEL_SLOTS;
+    const int slots = path == 1 ? 3 : path == 3 ? 5 : 4;
     for (int k = 0; k < slots; k++) {
         double tot = 0.0;
         int cnt = 0;
@@ -475,7 +483,7 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
     destroy();
     *n_kernels = slots;
     if (names && names_cap) {
-        const char *src = path == 1 ? kB1Names : kGenericNames;
+        const char *src = path == 1 ? kB1Names : path == 3 ? kBnNames : kGenericNames;
         snprintf(names, names_cap, "%s", src);
     }
     return ok();

@@ -1,0 +1,391 @@
+// Decode path for a small batch (1 <= T <= 8 tokens) of regular shape.
+//
+// The layer is the same as on the batch-1 path (the Flint 40B-A2.5B pages,
+// "Recursive Flint 40B-A2.5B", orcarouter.ai blog, section "The architecture
+// is a memory-bandwidth argument": 256 routed experts, 6 chosen per token,
+// one shared expert; decode time is weight traffic).  With T tokens the
+// union of their chosen experts is read once per layer: expert e's weights
+// serve every token that chose it.
+//
+//   bn_norm     (stacks) x_t = y_t / rms(y_t) for every token, once
+//   pf_logits   router logits for all tokens (bf16 MFMA, from the prefill path)
+//   bn_select   per-token top-k, the expert union with token masks, and two
+//               work lists: (slot, token pair) items for gate/up and
+//               (slot, token) pairs for the down projection
+//   bn_gateup   one wave per (item, 2-4 features): weights and both tokens' x
+//               loaded before any arithmetic
+//   bn_down     8 output rows per block; the waves take (slot, token) pairs
+//               in batches of 4 with every load of a batch in flight; the
+//               per-token partial sums are added in a fixed order
+// No floating-point atomics; every sum has a fixed order.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+#include "moe_prefill.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int BN_WAVES = 4;     // waves per block (gate/up and down)
+constexpr int BN_RR = 2;        // output rows per lane group in down
+constexpr int BN_PB = 4;        // (slot, token) pairs per load batch in down
+constexpr int BN_SEL_THREADS = 512;
+
+// ---------------------------------------------------------------------------
+// bn_norm: one block per token; xbuf[t] = y[t] / sqrt(mean(y[t]^2) + 1e-6).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bn_norm(DecodeParams p) {
+    __shared__ float red[4];
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float4 *y = reinterpret_cast<const float4 *>(p.x_prev + (size_t)t * p.D);
+    const int n4 = p.D / 4;
+    float ss = 0.f;
+    for (int i = tid; i < n4; i += 256) {
+        const float4 v = y[i];
+        ss = __builtin_fmaf(v.x, v.x, ss);
+        ss = __builtin_fmaf(v.y, v.y, ss);
+        ss = __builtin_fmaf(v.z, v.z, ss);
+        ss = __builtin_fmaf(v.w, v.w, ss);
+    }
+    ss = group_sum<MOE_WAVE>(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+    const float inv = 1.0f / sqrtf(tot / (float)p.D + 1e-6f);
+    float4 *xo = reinterpret_cast<float4 *>(p.xbuf + (size_t)t * p.D);
+    for (int i = tid; i < n4; i += 256) {
+        const float4 v = y[i];
+        xo[i] = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bn_select: one block.  Wave t takes token t's top-k (or reads the given
+// routing); the union of routed experts is compacted in ascending order after
+// the shared experts.  Work lists:
+//   work[i]  = {slot, token a, token b (or -1), expert}  for gate/up
+//   pairs[j] = {slot, token, coef bits, expert}         for down
+// meta = {active slots, items, pairs}.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
+    __shared__ int sel_e[MAX_DECODE_T][8];
+    __shared__ float sel_w[MAX_DECODE_T][8];
+    __shared__ uint32_t emask[256];
+    __shared__ int wcnt[4];
+    __shared__ int act_e[256 + 4];
+    __shared__ uint32_t act_m[256 + 4];
+    __shared__ int n_items_s[256 + 4 + 1];
+    __shared__ int n_pairs_s[256 + 4 + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = p.T, K = p.K, E = p.E, S = p.S;
+    if (tid < 256) emask[tid] = 0u;
+    __syncthreads();
+    if (wave < T) {
+        int e;
+        float wi;
+        if (p.route_given) {
+            e = lane < K ? p.idx[wave * K + lane] : 0;
+            wi = lane < K ? p.w[wave * K + lane] : 0.f;
+        } else {
+            wave_topk(p.logits + (size_t)wave * E, E, K, &e, &wi);
+            if (lane < K) {
+                p.idx[wave * K + lane] = e;
+                p.w[wave * K + lane] = wi;
+                if (p.idx_out) p.idx_out[wave * K + lane] = e;
+                if (p.w_out) p.w_out[wave * K + lane] = wi;
+            }
+        }
+        if (lane < K) {
+            const bool ok = e >= 0 && e < E;  // invalid given indices select nothing
+            sel_e[wave][lane] = ok ? e : -1;
+            sel_w[wave][lane] = wi;
+            if (ok) atomicOr(&emask[e], 1u << wave);
+        }
+    }
+    __syncthreads();
+    // compaction of the routed union (threads 0..255 = experts, ascending)
+    const uint32_t m = tid < E ? emask[tid] : 0u;
+    const uint64_t bal = __ballot(m != 0u);
+    if (tid < 256 && lane == 0) wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int base = 0;
+    for (int w2 = 0; w2 < wave && w2 < 4; w2++) base += wcnt[w2];
+    const int n_routed = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    const int n_act = S + n_routed;
+    if (tid < 256 && m != 0u) {
+        const int pos = S + base + __popcll(bal & ((1ull << lane) - 1ull));
+        act_e[pos] = tid;
+        act_m[pos] = m;
+    }
+    if (tid < S) {
+        act_e[tid] = E + tid;
+        act_m[tid] = (T >= 32) ? 0xFFFFFFFFu : ((1u << T) - 1u);
+    }
+    __syncthreads();
+    // per-slot work counts, then exclusive scans (one thread, <= 260 slots)
+    if (tid < n_act) {
+        const int c = __popc(act_m[tid]);
+        n_items_s[tid] = (c + 1) / 2;
+        n_pairs_s[tid] = c;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int a = 0, b = 0;
+        for (int i = 0; i < n_act; i++) {
+            const int ci = n_items_s[i], cp = n_pairs_s[i];
+            n_items_s[i] = a;
+            n_pairs_s[i] = b;
+            a += ci;
+            b += cp;
+        }
+        n_items_s[n_act] = a;
+        n_pairs_s[n_act] = b;
+        p.meta[0] = n_act;
+        p.meta[1] = a;
+        p.meta[2] = b;
+    }
+    __syncthreads();
+    if (tid < n_act) {
+        const int slot = tid, e = act_e[slot];
+        const uint32_t mk = act_m[slot];
+        p.act_expert[slot] = e;
+        p.act_mask[slot] = mk;
+        int it = n_items_s[slot], pr = n_pairs_s[slot];
+        int pend = -1;
+        for (int t = 0; t < T; t++) {
+            float c = 0.f;
+            if (slot < S) {
+                c = 1.f;
+            } else {
+                // a repeated index adds its weights (the expert counted twice)
+                for (int k = 0; k < K; k++)
+                    if (sel_e[t][k] == e) c += sel_w[t][k];
+            }
+            p.act_w[slot * T + t] = ((mk >> t) & 1u) ? c : 0.f;
+            if (!((mk >> t) & 1u)) continue;
+            int4 q;
+            q.x = slot; q.y = t; q.z = __float_as_int(c); q.w = e;
+            reinterpret_cast<int4 *>(p.pairs)[pr++] = q;
+            if (pend < 0) {
+                pend = t;
+            } else {
+                reinterpret_cast<int4 *>(p.work)[it++] = make_int4(slot, pend, t, e);
+                pend = -1;
+            }
+        }
+        if (pend >= 0) reinterpret_cast<int4 *>(p.work)[it++] = make_int4(slot, pend, -1, e);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bn_gateup: wave gw -> item gw / (F / RG), features f0 .. f0 + RG - 1.
+// h[(slot * T + t) * F + f] = silu(Wg x_t)[f] * (Wu x_t)[f] for both tokens.
+// ---------------------------------------------------------------------------
+template <int FMT, int UPLD, int RG>
+__global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int per_item = p.F / RG;
+    const int gw = blockIdx.x * BN_WAVES + wave;
+    const int item = gw / per_item, f0 = (gw % per_item) * RG;
+    if (item >= p.meta[1]) return;
+    const int4 wk = reinterpret_cast<const int4 *>(p.work)[item];
+    const int slot = wk.x, ta = wk.y, tb = wk.z < 0 ? wk.y : wk.z, expert = wk.w;
+    const uint8_t *eb = p.experts + (size_t)expert * p.expert_bytes;
+    Mat mg{eb, p.F, p.D, p.tscale ? p.tscale[3 * expert + 0] : 1.f};
+    Mat mu{eb + mat_bytes<FMT>(p.F, p.D), p.F, p.D, p.tscale ? p.tscale[3 * expert + 1] : 1.f};
+    const float *xin = p.x_prev ? p.xbuf : p.x;
+    WUnit wg[RG][UPLD], wu[RG][UPLD];
+    XUnit<FMT> xa[UPLD], xb[UPLD];
+#pragma unroll
+    for (int r = 0; r < RG; r++)
+#pragma unroll
+        for (int i = 0; i < UPLD; i++) {
+            wg[r][i] = load_unit<FMT>(mg, f0 + r, lane + MOE_WAVE * i);
+            wu[r][i] = load_unit<FMT>(mu, f0 + r, lane + MOE_WAVE * i);
+        }
+#pragma unroll
+    for (int i = 0; i < UPLD; i++) {
+        load_x<FMT>(xa[i], xin + (size_t)ta * p.D, lane + MOE_WAVE * i);
+        load_x<FMT>(xb[i], xin + (size_t)tb * p.D, lane + MOE_WAVE * i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float ag[RG][2], au[RG][2];
+#pragma unroll
+    for (int r = 0; r < RG; r++) {
+        ag[r][0] = ag[r][1] = au[r][0] = au[r][1] = 0.f;
+#pragma unroll
+        for (int i = 0; i < UPLD; i++) {
+            ag[r][0] += unit_dot<FMT>(wg[r][i], xa[i], mg.ts);
+            au[r][0] += unit_dot<FMT>(wu[r][i], xa[i], mu.ts);
+            ag[r][1] += unit_dot<FMT>(wg[r][i], xb[i], mg.ts);
+            au[r][1] += unit_dot<FMT>(wu[r][i], xb[i], mu.ts);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RG; r++) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const float gs = group_sum<MOE_WAVE>(ag[r][j]);
+            const float us = group_sum<MOE_WAVE>(au[r][j]);
+            const int t = j == 0 ? ta : tb;
+            if (lane == 2 * r + j && (j == 0 || wk.z >= 0))
+                p.h[((size_t)slot * p.T + t) * p.F + f0 + r] = silu_mul(gs, us);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bn_down: block = 4 waves over the same 8 output rows (LPR_F lanes per row
+// group, 2 rows per group); wave w takes pairs w, w + 4, ... in batches.
+// y[t, row] = sum over pairs (slot, t) of coef * Wd_slot[row] . h[slot, t].
+// ---------------------------------------------------------------------------
+template <int FMT, int LPR_F, int TT>
+__global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_down(DecodeParams p) {
+    constexpr int UE = Unit<FMT>::E;
+    constexpr int G = MOE_WAVE / LPR_F;  // row groups per wave
+    constexpr int ROWS = G * BN_RR;      // rows per block
+    __shared__ float part[BN_WAVES][TT][ROWS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane / LPR_F, sub = lane % LPR_F;
+    const int D = p.D, F = p.F;
+    const int rb = blockIdx.x * ROWS;
+    const int r0 = rb + grp * BN_RR;
+    const int n_pairs = p.meta[2];
+    float acc[BN_RR][TT];
+#pragma unroll
+    for (int r = 0; r < BN_RR; r++)
+#pragma unroll
+        for (int t = 0; t < TT; t++) acc[r][t] = 0.f;
+    for (int pb = wave; pb < n_pairs; pb += BN_WAVES * BN_PB) {
+        // one batch: BN_PB pairs (clamped to the last pair; extras weigh 0)
+        WUnit wd[BN_PB][BN_RR];
+        XUnit<FMT> hv[BN_PB];
+        float coef[BN_PB], ts[BN_PB];
+        int tok[BN_PB];
+#pragma unroll
+        for (int q = 0; q < BN_PB; q++) {
+            const int pi = pb + BN_WAVES * q;
+            const int4 pr = reinterpret_cast<const int4 *>(p.pairs)[min(pi, n_pairs - 1)];
+            coef[q] = pi < n_pairs ? __int_as_float(pr.z) : 0.f;
+            tok[q] = pr.y;
+            const uint8_t *eb = p.experts + (size_t)pr.w * p.expert_bytes;
+            Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, p.tscale ? p.tscale[3 * pr.w + 2] : 1.f};
+            ts[q] = md.ts;
+#pragma unroll
+            for (int r = 0; r < BN_RR; r++) wd[q][r] = load_unit<FMT>(md, min(r0 + r, D - 1), sub);
+            const float *hsrc = p.h + ((size_t)pr.x * p.T + pr.y) * F;
+#pragma unroll
+            for (int i = 0; i < UE / 4; i++) {
+                const float4 f = reinterpret_cast<const float4 *>(hsrc + sub * UE)[i];
+                hv[q].v[4 * i + 0] = f.x;
+                hv[q].v[4 * i + 1] = f.y;
+                hv[q].v[4 * i + 2] = f.z;
+                hv[q].v[4 * i + 3] = f.w;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < BN_PB; q++) {
+            float sum = 0.f;
+            if (FMT == FMT_Q4_1) {
+#pragma unroll
+                for (int i = 0; i < UE; i++) sum += hv[q].v[i];
+            }
+            hv[q].sum = sum;
+#pragma unroll
+            for (int r = 0; r < BN_RR; r++) {
+                const float v = coef[q] * unit_dot<FMT>(wd[q][r], hv[q], ts[q]);
+#pragma unroll
+                for (int t = 0; t < TT; t++) acc[r][t] += tok[q] == t ? v : 0.f;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < BN_RR; r++)
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+            const float s = group_sum<LPR_F>(acc[r][t]);
+            if (sub == 0) part[wave][t][grp * BN_RR + r] = s;
+        }
+    __syncthreads();
+    // fixed-order sum of the waves' partials
+    for (int i = tid; i < TT * ROWS; i += MOE_WAVE * BN_WAVES) {
+        const int t = i / ROWS, rr = i % ROWS;
+        if (t >= p.T || rb + rr >= D) continue;
+        float y = part[0][t][rr];
+#pragma unroll
+        for (int w = 1; w < BN_WAVES; w++) y += part[w][t][rr];
+        p.y[(size_t)t * D + rb + rr] = y;
+    }
+}
+
+template <int FMT, int UPLD, int LPR_F>
+hipError_t launch_bn_fmt(const DecodeParams &p, hipStream_t st) {
+    const int S = p.S;
+    constexpr int RG = UPLD == 1 ? 4 : 2;  // features per wave (register budget)
+    const int max_items = S * ((p.T + 1) / 2) + p.T * p.K;
+    const int waves_g = max_items * (p.F / RG);
+    MOE_LAUNCH(3, (bn_gateup<FMT, UPLD, RG>), dim3((waves_g + BN_WAVES - 1) / BN_WAVES), dim3(MOE_WAVE * BN_WAVES),
+               st, p);
+    const int rows = (MOE_WAVE / LPR_F) * BN_RR;
+    const dim3 gd((p.D + rows - 1) / rows);
+    if (p.T <= 2)
+        MOE_LAUNCH(4, (bn_down<FMT, LPR_F, 2>), gd, dim3(MOE_WAVE * BN_WAVES), st, p);
+    else if (p.T <= 4)
+        MOE_LAUNCH(4, (bn_down<FMT, LPR_F, 4>), gd, dim3(MOE_WAVE * BN_WAVES), st, p);
+    else
+        MOE_LAUNCH(4, (bn_down<FMT, LPR_F, 8>), gd, dim3(MOE_WAVE * BN_WAVES), st, p);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_bn_shape(const DecodeParams &p, hipStream_t st) {
+    constexpr int UE = Unit<FMT>::E;
+    if (p.D % (MOE_WAVE * UE)) return hipErrorNotSupported;
+    const int upld = p.D / (MOE_WAVE * UE), lpr_f = p.F / UE;
+    if (p.F % UE || p.F % 4) return hipErrorNotSupported;
+    if (upld == 1 && lpr_f == 16) return launch_bn_fmt<FMT, 1, 16>(p, st);
+    if (upld == 1 && lpr_f == 32) return launch_bn_fmt<FMT, 1, 32>(p, st);
+    if (upld == 2 && lpr_f == 16) return launch_bn_fmt<FMT, 2, 16>(p, st);
+    if (upld == 2 && lpr_f == 32) return launch_bn_fmt<FMT, 2, 32>(p, st);
+    return hipErrorNotSupported;
+}
+
+template <int FMT>
+bool bn_shape_ok(const DecodeParams &p) {
+    constexpr int UE = Unit<FMT>::E;
+    if (p.D % (MOE_WAVE * UE) || p.F % UE || p.F % 4) return false;
+    const int upld = p.D / (MOE_WAVE * UE), lpr_f = p.F / UE;
+    return (upld == 1 || upld == 2) && (lpr_f == 16 || lpr_f == 32);
+}
+
+}  // namespace
+
+// Kernel slots: 0 norm, 1 logits, 2 select, 3 gate/up, 4 down.
+hipError_t launch_decode_bn(const DecodeParams &p, hipStream_t st) {
+    if (p.T < 1 || p.T > MAX_DECODE_T || p.E > 256 || p.S > 4 || !p.want_shared) return hipErrorNotSupported;
+    if (!p.work || !p.pairs) return hipErrorNotSupported;
+    const bool ok = p.fmt == FMT_Q4_1 ? bn_shape_ok<FMT_Q4_1>(p)
+                    : p.fmt == FMT_NVFP4 ? bn_shape_ok<FMT_NVFP4>(p)
+                                         : bn_shape_ok<FMT_BF16>(p);
+    if (!ok) return hipErrorNotSupported;
+    if (p.x_prev) MOE_LAUNCH(0, bn_norm, dim3(p.T), dim3(256), st, p);
+    if (!p.route_given) {
+        if (!p.want_router) return hipErrorNotSupported;
+        const float *xin = p.x_prev ? p.xbuf : p.x;
+        const hipError_t e = launch_router_logits(xin, p.T, p.D, p.E, p.router, p.bias, p.logits,
+                                                  p.ev ? p.ev + 2 : nullptr, st);
+        if (e != hipSuccess) return e;
+    }
+    MOE_LAUNCH(2, bn_select, dim3(1), dim3(BN_SEL_THREADS), st, p);
+    if (p.fmt == FMT_Q4_1) return launch_bn_shape<FMT_Q4_1>(p, st);
+    if (p.fmt == FMT_NVFP4) return launch_bn_shape<FMT_NVFP4>(p, st);
+    return launch_bn_shape<FMT_BF16>(p, st);
+}
+
+}  // namespace moe

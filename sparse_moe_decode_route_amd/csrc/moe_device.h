@@ -240,13 +240,10 @@ __device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
 // index = lane + 64k, k ascending).  No per-thread arrays: an array indexed
 // by the lane would be moved to LDS and need the dispatch packet (in host
 // memory) to compute thread offsets.
-__device__ __forceinline__ void wave_topk(const float *l, int E, int K, int *e_out, float *w_out) {
+// The selection on logits already in registers: lv[k] = logit of expert
+// lane + 64 k (any value for indices >= E).
+__device__ __forceinline__ void wave_topk_regs(const float lv[4], int E, int K, int *e_out, float *w_out) {
     const int lane = threadIdx.x & (MOE_WAVE - 1);
-    // four loads issued back to back; the opaque copy keeps the compiler from
-    // sinking a load into the (ix < E) branch, which would serialise them
-    float lv[4];
-#pragma unroll
-    for (int k = 0; k < 4; k++) lv[k] = l[min(lane + 64 * k, E - 1)];
     uint32_t key[4];
 #pragma unroll
     for (int k = 0; k < 4; k++) {
@@ -276,6 +273,21 @@ __device__ __forceinline__ void wave_topk(const float *l, int E, int K, int *e_o
     const float den = group_sum<MOE_WAVE>(ev);
     *e_out = lane < K ? my_e : 0;
     *w_out = ev / den;
+}
+
+// Loads of one token's logits for wave_topk_regs (clamped in-bounds indices).
+__device__ __forceinline__ void wave_topk_load(const float *l, int E, float lv[4]) {
+    const int lane = threadIdx.x & (MOE_WAVE - 1);
+#pragma unroll
+    for (int k = 0; k < 4; k++) lv[k] = l[min(lane + 64 * k, E - 1)];
+}
+
+__device__ __forceinline__ void wave_topk(const float *l, int E, int K, int *e_out, float *w_out) {
+    // four loads issued back to back; the opaque copy in wave_topk_regs keeps
+    // the compiler from sinking a load into the (ix < E) branch
+    float lv[4];
+    wave_topk_load(l, E, lv);
+    wave_topk_regs(lv, E, K, e_out, w_out);
 }
 
 }  // namespace moe

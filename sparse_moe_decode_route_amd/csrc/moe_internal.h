@@ -46,6 +46,8 @@ struct DecodeParams {
     // kernel slot s; the kernel is then launched with hipExtLaunchKernelGGL,
     // whose events take the dispatch's own begin and end timestamps
     hipEvent_t *ev;
+    int32_t *work;       // small-batch path: gate/up items {slot, token a, token b, expert}
+    int32_t *pairs;      // small-batch path: down pairs {slot, token, coef bits, expert}
 };
 
 // Launch `kern(p)` on `st`, timed into event pair `slot` when p.ev is set.
@@ -58,12 +60,15 @@ struct DecodeParams {
     } while (0)
 
 // Kernel slots of one layer, per decode path (names as reported by the timing entry point).
-constexpr int MAX_KERNEL_SLOTS = 4;
+constexpr int MAX_KERNEL_SLOTS = 5;
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
 // Batch-1 path (three kernels per layer); hipErrorNotSupported if the shape
 // is outside what it was built for (the caller then takes launch_decode).
 hipError_t launch_decode_b1(const DecodeParams &p, hipStream_t st);
+// Small-batch path (1 <= T <= 8, regular shapes: d_model a multiple of 64
+// units, d_ff of 16 or 32 units); hipErrorNotSupported otherwise.
+hipError_t launch_decode_bn(const DecodeParams &p, hipStream_t st);
 hipError_t launch_route_only(const DecodeParams &p, hipStream_t st);
 hipError_t launch_bf16_to_f32(const uint16_t *in, float *out, int n, hipStream_t st);
 }  // namespace moe

@@ -10,8 +10,9 @@
 // run on MFMA (fp16 operands, fp32 accumulation).
 //
 // Kernels (one stream, in order):
-//   pf_router   logits = x Wr^T (+bias) by bf16 MFMA, per-token top-k,
-//               per-expert 64-token bitmasks, fp16 copy of x
+//   pf_logits   logits = x Wr^T (+bias) by bf16 MFMA (split reduction),
+//               fp16 copy of x
+//   pf_topk     per-token top-k, per-expert 64-token bitmasks
 //   pf_scan     per-expert counts and word prefixes of the masks, row
 //               offsets, tile table
 //   pf_scatter  position of every (token, slot) pair in its expert's rows
@@ -45,7 +46,7 @@ struct PfTile {
 
 // Workspace layout (byte offsets), shared by the host sizing and the launcher.
 struct PfWs {
-    size_t x16, idx, w, mask, wp, off, tiles, meta, perm_tok, perm_w, pos, h, o, total;
+    size_t x16, logits, idx, w, mask, wp, off, tiles, meta, perm_tok, perm_w, pos, h, o, total;
     int NW, R, tiles_max;
 };
 
@@ -58,6 +59,7 @@ PfWs pf_layout(int D, int F, int E, int S, int K, int T) {
     L.tiles_max = (L.R + PF_BM - 1) / PF_BM + E + S;
     size_t o = 0;
     L.x16 = o; o = al(o + (size_t)T * D * 2);
+    L.logits = o; o = al(o + (size_t)T * E * 4);
     L.idx = o; o = al(o + (size_t)T * K * 4);
     L.w = o; o = al(o + (size_t)T * K * 4);
     L.mask = o; o = al(o + (size_t)E * L.NW * 8);
@@ -92,6 +94,7 @@ struct PfParams {
     int32_t *idx_out;
     float *w_out;
     float *logits_out;
+    float *logits;       // [T, E]: logits_out, or workspace
     _Float16 *x16;
     int32_t *idx;
     float *w;
@@ -116,71 +119,45 @@ __device__ __forceinline__ uint32_t f2bf_rne(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// pf_router: one block = 64 tokens x all experts; wave w owns experts
-// [64w, 64w + 64) as two 32-row MFMA tiles, both 32-token halves.
+// pf_logits: logits[t, e] = x[t] . Wr[e] (+ bias[e]) by bf16 MFMA.  One block
+// = 32 experts x 32 tokens; its 4 waves split the reduction into quarters,
+// summed in wave order through LDS.  Blocks of the first expert column also
+// write the fp16 copy of x (operand of the expert GEMMs).  An fp32 input is
+// split x = hi + lo into two bf16 parts, both accumulated.
 // ---------------------------------------------------------------------------
+constexpr int PF_LG_CH = 8;  // reduction steps of 16 per load batch
+
 template <int ACT>
-__global__ void __launch_bounds__(PF_THREADS) pf_router(PfParams p) {
-    __shared__ float lg[32][256];
-    __shared__ unsigned long long smask[256];
+__global__ void __launch_bounds__(PF_THREADS) pf_logits(PfParams p) {
+    __shared__ float red[4][32][33];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t0 = blockIdx.x * PF_RT;
-    const int D = p.D, E = p.E, T = p.T;
-    if (tid < 256) smask[tid] = 0ull;
-
-    // fp16 copy of this block's tokens (operand of the expert GEMMs)
-    if (p.want_x16) {
-        const int nt = min(PF_RT, T - t0);
-        const int n8 = nt * D / 8;
-        for (int i = tid; i < n8; i += PF_THREADS) {
-            const size_t e0 = (size_t)t0 * D + (size_t)i * 8;
-            half8_t hv;
-            if (ACT == 0) {
-                const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.x) + e0);
-                const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.x) + e0 + 4);
-                hv[0] = (_Float16)a.x; hv[1] = (_Float16)a.y; hv[2] = (_Float16)a.z; hv[3] = (_Float16)a.w;
-                hv[4] = (_Float16)b.x; hv[5] = (_Float16)b.y; hv[6] = (_Float16)b.z; hv[7] = (_Float16)b.w;
-            } else {
-                const uint4 r = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + e0);
-                const uint32_t ww[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    hv[2 * j] = (_Float16)bf16lo(ww[j]);
-                    hv[2 * j + 1] = (_Float16)bf16hi(ww[j]);
-                }
-            }
-            *reinterpret_cast<half8_t *>(p.x16 + e0) = hv;
-        }
-    }
-
-    // router GEMM: D[m = expert][n = token]
-    f32x16_t acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-            for (int j = 0; j < 16; j++) acc[a][b][j] = 0.f;
     const int g = lane >> 5, l32 = lane & 31;
-    const uint16_t *wrow[2];
+    const int D = p.D, E = p.E, T = p.T;
+    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+    const int NKS = D / 16;                                   // reduction steps
+    const int ks0 = wave * NKS / 4, ks1 = (wave + 1) * NKS / 4;  // this wave's quarter
+    const uint16_t *wrow = p.router + (size_t)min(e0 + l32, E - 1) * D + 8 * g;
+    const int trow = min(t0 + l32, T - 1);
+    const bool write_x16 = p.want_x16 && blockIdx.y == 0 && t0 + l32 < T;
+    f32x16_t acc;
 #pragma unroll
-    for (int a = 0; a < 2; a++) wrow[a] = p.router + (size_t)min(64 * wave + 32 * a + l32, E - 1) * D + 8 * g;
-    int trow[2];
+    for (int j = 0; j < 16; j++) acc[j] = 0.f;
+    for (int kc = ks0; kc < ks1; kc += PF_LG_CH) {
+        // one batch: every load first, then the MFMAs
+        uint4 av[PF_LG_CH];
+        bf16x8_t bh[PF_LG_CH], bl[PF_LG_CH];
 #pragma unroll
-    for (int b = 0; b < 2; b++) trow[b] = min(t0 + 32 * b + l32, T - 1);
-    for (int k0 = 0; k0 < D; k0 += 16) {
-        bf16x8_t af[2];
-#pragma unroll
-        for (int a = 0; a < 2; a++) af[a] = as_bf16x8(*reinterpret_cast<const uint4 *>(wrow[a] + k0));
-#pragma unroll
-        for (int b = 0; b < 2; b++) {
+        for (int c = 0; c < PF_LG_CH; c++) {
+            const int k0 = 16 * min(kc + c, ks1 - 1);
+            av[c] = *reinterpret_cast<const uint4 *>(wrow + k0);
             if (ACT == 0) {
-                const float *xs = static_cast<const float *>(p.x) + (size_t)trow[b] * D + k0 + 8 * g;
+                const float *xs = static_cast<const float *>(p.x) + (size_t)trow * D + k0 + 8 * g;
                 const float4 u0 = *reinterpret_cast<const float4 *>(xs);
                 const float4 u1 = *reinterpret_cast<const float4 *>(xs + 4);
                 const float xv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
                 uint32_t hi[4], lo[4];
+                half8_t hv;
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
                     const uint32_t h0 = f2bf_rne(xv[2 * j]), h1 = f2bf_rne(xv[2 * j + 1]);
@@ -188,55 +165,87 @@ __global__ void __launch_bounds__(PF_THREADS) pf_router(PfParams p) {
                     const uint32_t l1 = f2bf_rne(xv[2 * j + 1] - __uint_as_float(h1 << 16));
                     hi[j] = h0 | (h1 << 16);
                     lo[j] = l0 | (l1 << 16);
+                    hv[2 * j] = (_Float16)xv[2 * j];
+                    hv[2 * j + 1] = (_Float16)xv[2 * j + 1];
                 }
-                const bf16x8_t bh = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-                const bf16x8_t bl = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-#pragma unroll
-                for (int a = 0; a < 2; a++) {
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bh, acc[a][b], 0, 0, 0);
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bl, acc[a][b], 0, 0, 0);
-                }
+                bh[c] = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                bl[c] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+                if (write_x16 && kc + c < ks1)
+                    *reinterpret_cast<half8_t *>(p.x16 + (size_t)trow * D + k0 + 8 * g) = hv;
             } else {
-                const uint16_t *xs = static_cast<const uint16_t *>(p.x) + (size_t)trow[b] * D + k0 + 8 * g;
-                const bf16x8_t bx = as_bf16x8(*reinterpret_cast<const uint4 *>(xs));
+                const uint4 r = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + (size_t)trow * D +
+                                                                 k0 + 8 * g);
+                bh[c] = as_bf16x8(r);
+                if (write_x16 && kc + c < ks1) {
+                    const uint32_t ww[4] = {r.x, r.y, r.z, r.w};
+                    half8_t hv;
 #pragma unroll
-                for (int a = 0; a < 2; a++)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bx, acc[a][b], 0, 0, 0);
+                    for (int j = 0; j < 4; j++) {
+                        hv[2 * j] = (_Float16)bf16lo(ww[j]);
+                        hv[2 * j + 1] = (_Float16)bf16hi(ww[j]);
+                    }
+                    *reinterpret_cast<half8_t *>(p.x16 + (size_t)trow * D + k0 + 8 * g) = hv;
+                }
             }
         }
+#pragma unroll
+        for (int c = 0; c < PF_LG_CH; c++) {
+            if (kc + c >= ks1) break;
+            const bf16x8_t a = as_bf16x8(av[c]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[c], acc, 0, 0, 0);
+            if (ACT == 0) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[c], acc, 0, 0, 0);
+        }
     }
-    // per 32-token half: logits (+ bias) to LDS [token][expert], then top-k
-    // (wave w takes tokens w, w + 4, ...)
+    // acc[j] = partial logit of expert e0 + 8 (j/4) + 4 g + j%4, token t0 + l32
 #pragma unroll
-    for (int b = 0; b < 2; b++) {
-        if (b) __syncthreads();  // the previous half's top-k has read lg
+    for (int j = 0; j < 16; j++) red[wave][8 * (j >> 2) + 4 * g + (j & 3)][l32] = acc[j];
+    __syncthreads();
+    for (int i = tid; i < 32 * 32; i += PF_THREADS) {
+        const int el = i >> 5, tl = i & 31;
+        const int e = e0 + el, t = t0 + tl;
+        if (e >= E || t >= T) continue;
+        float v = red[0][el][tl];
+        v += red[1][el][tl];
+        v += red[2][el][tl];
+        v += red[3][el][tl];
+        p.logits[(size_t)t * E + e] = v + (p.bias ? p.bias[e] : 0.f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// pf_topk: one block = 64 tokens (one mask word); wave w takes tokens w,
+// w + 4, ...: top-k and renormalised weights, per-expert token bitmask.
+// ---------------------------------------------------------------------------
+constexpr int PF_TOPK_THREADS = 1024;  // 16 waves x 4 tokens
+
+__global__ void __launch_bounds__(PF_TOPK_THREADS) pf_topk(PfParams p) {
+    __shared__ unsigned long long smask[256];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t0 = blockIdx.x * 64;
+    if (tid < 256) smask[tid] = 0ull;
+    // the wave's 4 tokens' logits, all loads in flight together
+    float lv[4][4];
 #pragma unroll
-        for (int a = 0; a < 2; a++)
+    for (int i = 0; i < 4; i++) wave_topk_load(p.logits + (size_t)min(t0 + wave + 16 * i, p.T - 1) * p.E, p.E, lv[i]);
+    __syncthreads();
 #pragma unroll
-            for (int j = 0; j < 16; j++) {
-                const int e = 64 * wave + 32 * a + 8 * (j >> 2) + 4 * g + (j & 3);
-                if (e < E) lg[l32][e] = acc[a][b][j] + (p.bias ? p.bias[e] : 0.f);
-            }
-        __syncthreads();
-        for (int tl = wave; tl < 32; tl += 4) {
-            const int t = t0 + 32 * b + tl;
-            if (t >= T) break;
-            int e;
-            float wi;
-            wave_topk(lg[tl], E, p.K, &e, &wi);
-            if (lane < p.K) {
-                p.idx[(size_t)t * p.K + lane] = e;
-                p.w[(size_t)t * p.K + lane] = wi;
-                if (p.idx_out) p.idx_out[(size_t)t * p.K + lane] = e;
-                if (p.w_out) p.w_out[(size_t)t * p.K + lane] = wi;
-                atomicOr(&smask[e], 1ull << (32 * b + tl));
-            }
-            if (p.logits_out)
-                for (int e2 = lane; e2 < E; e2 += 64) p.logits_out[(size_t)t * E + e2] = lg[tl][e2];
+    for (int i = 0; i < 4; i++) {
+        const int tl = wave + 16 * i, t = t0 + tl;
+        if (t >= p.T) break;
+        int e;
+        float wi;
+        wave_topk_regs(lv[i], p.E, p.K, &e, &wi);
+        if (lane < p.K) {
+            p.idx[(size_t)t * p.K + lane] = e;
+            p.w[(size_t)t * p.K + lane] = wi;
+            if (p.idx_out) p.idx_out[(size_t)t * p.K + lane] = e;
+            if (p.w_out) p.w_out[(size_t)t * p.K + lane] = wi;
+            atomicOr(&smask[e], 1ull << tl);
         }
     }
     __syncthreads();
-    if (tid < E) p.mask[(size_t)tid * p.NW + blockIdx.x] = smask[tid];
+    if (tid < p.E) p.mask[(size_t)tid * p.NW + blockIdx.x] = smask[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -285,48 +294,76 @@ __global__ void __launch_bounds__(PF_THREADS) pf_mask_given(PfParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// pf_scan: one block.  Rows are ordered routed expert 0..E-1, then shared.
+// pf_scan: one block of 1024.  Rows are ordered routed expert 0..E-1, then
+// shared.  Per routed expert (one wave each): prefix popcounts of its mask
+// words; then block-wide exclusive scans of the row counts and tile counts.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(PF_THREADS) pf_scan(PfParams p) {
-    __shared__ int cnt[PF_THREADS + 8];
-    const int tid = threadIdx.x;
+constexpr int PF_SCAN_THREADS = 1024;
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        v += lane >= o ? u : 0;
+    }
+    return v;
+}
+
+// exclusive scan over the block (one value per thread, 1024 threads)
+__device__ __forceinline__ int block_excl_scan(int v, int *tmp16, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63) tmp16[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const int t = lane < 16 ? tmp16[lane] : 0;
+        const int ti = wave_incl_scan(t);
+        if (lane < 16) tmp16[lane] = ti - t;  // exclusive wave offsets
+        if (lane == 15) *total = ti;
+    }
+    __syncthreads();
+    const int r = tmp16[wave] + incl - v;
+    __syncthreads();
+    return r;
+}
+
+__global__ void __launch_bounds__(PF_SCAN_THREADS) pf_scan(PfParams p) {
+    __shared__ int cnt[PF_SCAN_THREADS];
+    __shared__ int tmp16[16];
+    __shared__ int tot_rows, tot_tiles;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_exp = p.E + p.S;
-    for (int e = tid; e < n_exp; e += PF_THREADS) {
-        int c = 0;
-        if (e < p.E) {
-            for (int w = 0; w < p.NW; w++) {
-                p.wp[(size_t)e * p.NW + w] = c;
-                c += __popcll(p.mask[(size_t)e * p.NW + w]);
-            }
-        } else {
-            c = p.T;
+    // per routed expert: word prefixes (64 words per pass)
+    for (int e = wave; e < p.E; e += 16) {
+        int carry = 0;
+        for (int w0 = 0; w0 < p.NW; w0 += 64) {
+            const int w = w0 + lane;
+            const int c = w < p.NW ? __popcll(p.mask[(size_t)e * p.NW + w]) : 0;
+            const int incl = wave_incl_scan(c);
+            if (w < p.NW) p.wp[(size_t)e * p.NW + w] = carry + incl - c;
+            carry += __shfl(incl, 63, 64);
         }
-        cnt[e] = c;
+        if (lane == 0) cnt[e] = carry;
     }
     __syncthreads();
+    const int my_n = tid < p.E ? cnt[tid] : (tid < n_exp ? p.T : 0);
+    const int my_tiles = (my_n + PF_BM - 1) / PF_BM;
+    const int off = block_excl_scan(my_n, tmp16, &tot_rows);
+    const int toff = block_excl_scan(my_tiles, tmp16, &tot_tiles);
+    if (tid < n_exp) p.off[tid] = off;
     if (tid == 0) {
-        int off = 0, tiles = 0;
-        for (int e = 0; e < n_exp; e++) {
-            const int c = cnt[e];
-            p.off[e] = off;
-            cnt[e] = tiles;  // becomes the expert's first tile index
-            off += c;
-            tiles += (c + PF_BM - 1) / PF_BM;
-        }
-        p.off[n_exp] = off;
-        p.meta[0] = tiles;
-        p.meta[1] = off;
+        p.off[n_exp] = tot_rows;
+        p.meta[0] = tot_tiles;
+        p.meta[1] = tot_rows;
     }
-    __syncthreads();
-    for (int e = tid; e < n_exp; e += PF_THREADS) {
-        const int n = p.off[e + 1] - p.off[e];
-        const int first = cnt[e];
-        for (int i = 0; i * PF_BM < n; i++) {
+    if (tid < n_exp) {
+        for (int i = 0; i < my_tiles; i++) {
             PfTile t;
-            t.e = e;
-            t.row0 = p.off[e] + i * PF_BM;
-            t.rows = min(PF_BM, n - i * PF_BM);
-            p.tiles[first + i] = t;
+            t.e = tid;
+            t.row0 = off + i * PF_BM;
+            t.rows = min(PF_BM, my_n - i * PF_BM);
+            p.tiles[toff + i] = t;
         }
     }
 }
@@ -759,15 +796,27 @@ __global__ void __launch_bounds__(PF_THREADS) pf_combine(PfParams p) {
 template <int FMT>
 void launch_gemms(const PfParams &p, hipStream_t st) {
     const int mt0 = (p.F + 127) / 128, mt1 = (p.D + 255) / 256;
-    MOE_LAUNCH(3, (pf_gemm<FMT, 0>), dim3(p.tiles_max * mt0), dim3(PF_THREADS), st, p);
-    MOE_LAUNCH(4, (pf_gemm<FMT, 1>), dim3(p.tiles_max * mt1), dim3(PF_THREADS), st, p);
+    MOE_LAUNCH(4, (pf_gemm<FMT, 0>), dim3(p.tiles_max * mt0), dim3(PF_THREADS), st, p);
+    MOE_LAUNCH(5, (pf_gemm<FMT, 1>), dim3(p.tiles_max * mt1), dim3(PF_THREADS), st, p);
 }
 
 }  // namespace
 
-const char *const kPrefillNames = "pf_router;pf_scan;pf_scatter;pf_gemm_gateup;pf_gemm_down;pf_combine";
+const char *const kPrefillNames = "pf_logits;pf_topk;pf_scan;pf_scatter;pf_gemm_gateup;pf_gemm_down;pf_combine";
 
 size_t prefill_ws_bytes(int D, int F, int E, int S, int K, int T) { return pf_layout(D, F, E, S, K, T).total; }
+
+hipError_t launch_router_logits(const float *x, int T, int D, int E, const uint16_t *router, const float *bias,
+                                float *logits, hipEvent_t *ev, hipStream_t st) {
+    if (E > 256 || D % 16) return hipErrorNotSupported;
+    PfParams p{};
+    p.D = D; p.E = E; p.T = T;
+    p.x = x; p.router = router; p.bias = bias; p.logits = logits;
+    p.want_x16 = 0;
+    p.ev = ev;
+    MOE_LAUNCH(0, (pf_logits<0>), dim3((T + 31) / 32, (E + 31) / 32), dim3(PF_THREADS), st, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     if (a.E > 256 || a.K > PF_MAX_TOPK || a.D % 32 || a.F % 32) return hipErrorNotSupported;
@@ -780,6 +829,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     p.expert_bytes = a.expert_bytes;
     p.x = a.x; p.router = a.router; p.bias = a.bias; p.experts = a.experts; p.tscale = a.tscale;
     p.y = a.y; p.idx_out = a.idx_out; p.w_out = a.w_out; p.logits_out = a.logits_out;
+    p.logits = a.logits_out ? a.logits_out : wsp<float>(a.ws, L.logits);
     p.x16 = wsp<_Float16>(a.ws, L.x16);
     p.idx = wsp<int32_t>(a.ws, L.idx);
     p.w = wsp<float>(a.ws, L.w);
@@ -795,10 +845,12 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     p.o = wsp<float>(a.ws, L.o);
     const int nb64 = (a.T + 63) / 64;
     if (!a.given_idx) {
+        const dim3 gl((a.T + 31) / 32, (a.E + 31) / 32);
         if (a.act == MOE_ACT_F32)
-            MOE_LAUNCH(0, (pf_router<0>), dim3(nb64), dim3(PF_THREADS), st, p);
+            MOE_LAUNCH(0, (pf_logits<0>), gl, dim3(PF_THREADS), st, p);
         else
-            MOE_LAUNCH(0, (pf_router<1>), dim3(nb64), dim3(PF_THREADS), st, p);
+            MOE_LAUNCH(0, (pf_logits<1>), gl, dim3(PF_THREADS), st, p);
+        MOE_LAUNCH(1, pf_topk, dim3(nb64), dim3(PF_TOPK_THREADS), st, p);
         if (a.route_only) return hipGetLastError();
     } else {
         p.idx = const_cast<int32_t *>(a.given_idx);
@@ -809,10 +861,10 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
             hipLaunchKernelGGL((pf_x16<0>), gx, dim3(PF_THREADS), 0, st, p);
         else
             hipLaunchKernelGGL((pf_x16<1>), gx, dim3(PF_THREADS), 0, st, p);
-        MOE_LAUNCH(0, pf_mask_given, dim3(nb64), dim3(PF_THREADS), st, p);
+        MOE_LAUNCH(1, pf_mask_given, dim3(nb64), dim3(PF_THREADS), st, p);
     }
-    MOE_LAUNCH(1, pf_scan, dim3(1), dim3(PF_THREADS), st, p);
-    MOE_LAUNCH(2, pf_scatter, dim3((a.T + PF_THREADS - 1) / PF_THREADS), dim3(PF_THREADS), st, p);
+    MOE_LAUNCH(2, pf_scan, dim3(1), dim3(PF_SCAN_THREADS), st, p);
+    MOE_LAUNCH(3, pf_scatter, dim3((a.T + PF_THREADS - 1) / PF_THREADS), dim3(PF_THREADS), st, p);
     if (a.fmt == FMT_Q4_1)
         launch_gemms<FMT_Q4_1>(p, st);
     else if (a.fmt == FMT_NVFP4)
@@ -820,7 +872,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     else
         launch_gemms<FMT_BF16>(p, st);
     const size_t n4 = (size_t)a.T * a.D / 4;
-    MOE_LAUNCH(5, pf_combine, dim3((unsigned)((n4 + PF_THREADS - 1) / PF_THREADS)), dim3(PF_THREADS), st, p);
+    MOE_LAUNCH(6, pf_combine, dim3((unsigned)((n4 + PF_THREADS - 1) / PF_THREADS)), dim3(PF_THREADS), st, p);
     return hipGetLastError();
 }
 

@@ -66,3 +66,27 @@ def rel_l2(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     a = np.asarray(a, dtype=np.float64).reshape(len(b), -1)
     b = np.asarray(b, dtype=np.float64).reshape(len(b), -1)
     return np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-300)
+
+
+def router_band_mfma(x: np.ndarray, router_f64: np.ndarray, f32_input: bool) -> np.ndarray:
+    """Per-token bound on |GPU logit - exact logit| for the matrix-core router, doubled.
+
+    Products of bf16 operands are exact in fp32.  Each MFMA instruction adds
+    16 products into the fp32 accumulator; over d_model/16 instructions a
+    product passes through at most n = d_model/16 + 16 roundings.  An fp32
+    input is split x = hi + lo into two bf16 parts (residual <= 2^-18 |x|)
+    and both halves are accumulated, doubling n."""
+    d = x.shape[1]
+    n = d / 16 + 16
+    rel = 2 * n * U32 + 2.0 ** -18 if f32_input else n * U32
+    mag = np.abs(x) @ np.abs(router_f64).T
+    return 2.0 * rel * mag.max(axis=1) * 1.01
+
+
+def decode_band(x: np.ndarray, router_f64: np.ndarray) -> np.ndarray:
+    """Band for a decode call: one token takes the fp32 router GEMV, several
+    tokens may take the matrix-core router (fp32 input split in two)."""
+    b = router_band(x, router_f64)
+    if x.shape[0] > 1:
+        b = np.maximum(b, router_band_mfma(x, router_f64, True))
+    return b

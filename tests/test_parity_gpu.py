@@ -12,7 +12,7 @@ import torch
 import oracle
 from sparse_moe_decode_route_amd import binding as B
 from sparse_moe_decode_route_amd import inputs as gen
-from tests.helpers import REL_L2_TOL, check_routing, rel_l2, router_band
+from tests.helpers import REL_L2_TOL, check_routing, decode_band, rel_l2, router_band
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,7 @@ def _run_layer_case(host, dev_layer, x32: torch.Tensor, label: str, prefill=Fals
     y, idx, w = y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
     x64 = x32.double().numpy()
     oi, ow, ol, oy = oracle.layer_forward(host, x64)
-    band = router_band(x64, _router64(host)) + band_extra
+    band = decode_band(x64, _router64(host)) + band_extra
     n_exact, n_amb = check_routing(idx, w, ol, oi, ow, band)
     # outputs against the oracle on the GPU's own selection
     _, _, _, oy_forced = oracle.layer_forward(host, x64, forced=idx)
@@ -249,3 +249,71 @@ def test_stack_graph_replays_match_eager():
         ref, _, _ = B.stack_decode(stack, xs[i:i + 1].contiguous(), ws=ws)
         torch.cuda.synchronize()
         assert torch.equal(got, ref), i
+
+
+# --------------------------------------------------------------------------- small-batch path (2-8 tokens)
+
+@pytest.mark.parametrize("dims,T", [
+    (gen.LayerDims(2048, 512, wfmt="q4_1"), 2),
+    (gen.LayerDims(2048, 512, wfmt="q4_1"), 5),
+    (gen.LayerDims(2048, 512, wfmt="q4_1"), 8),
+    (gen.LayerDims(512, 128, wfmt="bf16"), 3),
+    (gen.LayerDims(2048, 1024, n_routed=32, n_shared=0, top_k=4, wfmt="nvfp4"), 4),
+    (gen.LayerDims(4096, 512, n_routed=64, n_shared=2, top_k=6, wfmt="q4_1"), 7),
+], ids=["q4_1-t2", "q4_1-t5", "q4_1-t8", "bf16-t3", "nvfp4-noshared-t4", "q4_1-upl2-2shared-t7"])
+def test_small_batch_path_shapes(dims, T):
+    host, dl = _layer(dims, 46)
+    x = gen.make_hidden(46, T, dims.d_model, draw=T)
+    err, _, _ = _run_layer_case(host, dl, x, f"bn {dims} T={T}")
+    assert err.max() <= FP32_PATH_TOL
+
+
+def test_small_batch_given_routing_with_invalid_indices():
+    dims = gen.LayerDims(2048, 512, n_routed=64, n_shared=1, top_k=6, wfmt="q4_1")
+    host, dl = _layer(dims, 47)
+    T = 4
+    x = gen.make_hidden(47, T, 2048, draw=3)
+    rng = np.random.default_rng(11)
+    idx = np.stack([rng.choice(64, 6, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, 6)).astype(np.float32)
+    idx[1, 2] = -1
+    idx[3, 5] = 64  # out of range: selects nothing
+    y = B.expert_ffn_q4(dims, x.to(_dev()), dl.experts, None, torch.from_numpy(idx).to(_dev()),
+                        torch.from_numpy(w).to(_dev()))
+    torch.cuda.synchronize()
+    valid = (idx >= 0) & (idx < 64)
+    # "select nothing" = a zero-weight term (adds an exact +0.0 in the oracle)
+    oy = oracle.experts_given(host, x.double().numpy(), np.where(valid, idx, 0),
+                              np.where(valid, w, 0.0).astype(np.float64))
+    assert np.all(rel_l2(y.cpu().numpy(), oy) <= FP32_PATH_TOL)
+
+
+def test_small_batch_deterministic():
+    host, dl = _layer(gen.LayerDims(2048, 512, wfmt="q4_1"), 46)
+    x = gen.make_hidden(46, 8, 2048, draw=77).to(_dev())
+    y1, i1, w1 = B.layer_forward(dl, x)
+    y2, i2, w2 = B.layer_forward(dl, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(i1, i2) and torch.equal(w1, w2)
+
+
+def test_stack_small_batch_teacher_forced():
+    """3 tokens through 3 full-size NVFP4 layers (RMSNorm between layers on the device)."""
+    dims = gen.LayerDims(2048, 512, wfmt="nvfp4")
+    L, T = 3, 3
+    hosts = [gen.make_layer(dims, cfg_id=48, layer=l) for l in range(L)]
+    devs = [B.upload_layer(h, _dev()) for h in hosts]
+    stack = B.StackHandle(devs)
+    x0 = gen.make_hidden(48, T, 2048)
+    y, ytr, itr = B.stack_decode(stack, x0.to(_dev()), trace=True)
+    torch.cuda.synchronize()
+    ytr, itr = ytr.cpu().numpy(), itr.cpu().numpy()
+    x = x0.double().numpy()
+    for l in range(L):
+        oi, ow, ol, _ = oracle.layer_forward(hosts[l], x)
+        check_routing(itr[l], None, ol, oi, ow, decode_band(x, _router64(hosts[l])) + 1e-5)
+        _, _, _, oy = oracle.layer_forward(hosts[l], x, forced=itr[l])
+        err = rel_l2(ytr[l], oy)
+        print(f"[stack T={T}] layer {l} teacher-forced rel-L2 {err.max():.3e}")
+        assert err.max() <= FP32_PATH_TOL
+        x = np.stack([oracle.rmsnorm(ytr[l][t]) for t in range(T)])

@@ -15,7 +15,7 @@ import torch
 import oracle
 from sparse_moe_decode_route_amd import binding as B
 from sparse_moe_decode_route_amd import inputs as gen
-from tests.helpers import REL_L2_TOL, U32, check_routing, rel_l2
+from tests.helpers import REL_L2_TOL, check_routing, rel_l2, router_band_mfma
 
 pytestmark = pytest.mark.gpu
 
@@ -39,23 +39,6 @@ def _layer(dims, cfg_id, layer=0, zipf_s=None):
 
 def _router64(host):
     return oracle.bf16_array(host.router.numpy().view(np.uint16))
-
-
-def router_band_mfma(x64: np.ndarray, router64: np.ndarray, f32_input: bool) -> np.ndarray:
-    """Per-token bound on |GPU logit - exact logit|, doubled (two logits compared).
-
-    Products of bf16 operands are exact in fp32.  Each MFMA instruction adds
-    16 products into the fp32 accumulator; over d_model/16 instructions a
-    product passes through at most n = d_model/16 + 16 roundings.  An fp32
-    input is split x = hi + lo into two bf16 parts (residual <= 2^-18 |x|)
-    and both halves are accumulated, doubling n."""
-    d = x64.shape[1]
-    n = d / 16 + 16
-    rel = n * U32
-    if f32_input:
-        rel = 2 * n * U32 + 2.0 ** -18
-    mag = np.abs(x64) @ np.abs(router64).T
-    return 2.0 * rel * mag.max(axis=1) * 1.01
 
 
 def _x(T, D, draw, bf16: bool):
