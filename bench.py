@@ -94,7 +94,13 @@ def source_digest() -> str:
 # script (one run per counter), each scaled by the same counter's reading for a
 # plain device copy of known size; keyed by (workload, kernel) and valid only for
 # the kernel source digest it was taken on.
-COUNTER_TRAFFIC = {}
+_FETCH_SCALE = 262144.0 / 131085.2  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
+_WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE KiB
+COUNTER_TRAFFIC = {
+    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="89c5f0cfd958d7bc",
+                                              fetch_bytes=round(3935.0 * _FETCH_SCALE * 1024),
+                                              write_bytes=round(12.2 * _WRITE_SCALE * 1024)),
+}
 
 
 def kernel_algo_bytes(dims, T: int, routed_union: float):
