@@ -180,14 +180,14 @@ moe_status moe_stack_decode(const moe_dims *dims, int32_t n_layers, const moe_la
  * pages time whole-model decode only (tokens/s on the two named machines);
  * this call gives the per-kernel split of the decode step that those
  * figures are made of.  Blocks the calling thread until the stack is done.
- *   kernel_us  (host) float [5]: mean duration in microseconds of each
+ *   kernel_us  (host) float [4]: mean duration in microseconds of each
  *              kernel slot of a layer, averaged over the layers that ran it
  *              (-1 for a slot that never ran).
  *   n_kernels  (host) receives the number of slots used (3 on the batch-1
- *              path, 5 on the small-batch path, 4 on the general path).
+ *              path, 4 on the small-batch and general paths).
  *   names      (host, optional) receives the slots' kernel names separated
  *              by ';' (truncated to names_cap bytes, NUL-terminated).
- * Creates and destroys 10 * n_layers HIP events (n_layers <= 4096); not for
+ * Creates and destroys 8 * n_layers HIP events (n_layers <= 4096); not for
  * use under stream capture.
  */
 moe_status moe_stack_decode_timed(const moe_dims *dims, int32_t n_layers, const moe_layer_weights *layers,

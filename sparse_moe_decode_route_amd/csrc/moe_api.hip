@@ -188,7 +188,7 @@ hipError_t launch_any(const moe::DecodeParams &p, hipStream_t st, int *path = nu
 // Kernel names of one layer's slots, per path (slot order of MOE_LAUNCH).
 const char *const kB1Names = "b1_route_shared;b1_topk_gateup;b1_down";
 const char *const kGenericNames = "phase_a_kernel;select_kernel;gateup_kernel;down_kernel";
-const char *const kBnNames = "bn_norm;pf_logits;bn_select;bn_gateup;bn_down";
+const char *const kBnNames = "pf_logits;bn_select;bn_gateup;bn_down";
 
 }  // namespace
 
@@ -465,7 +465,7 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
         destroy();
         return s;
     }
-    const int slots = path == 1 ? 3 : path == 3 ? 5 : 4;
+    const int slots = path == 1 ? 3 : 4;
     for (int k = 0; k < slots; k++) {
         double tot = 0.0;
         int cnt = 0;

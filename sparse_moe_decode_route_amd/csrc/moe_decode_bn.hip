@@ -7,14 +7,16 @@
 // union of their chosen experts is read once per layer: expert e's weights
 // serve every token that chose it.
 //
-//   bn_norm     (stacks) x_t = y_t / rms(y_t) for every token, once
-//   pf_logits   router logits for all tokens (bf16 MFMA, from the prefill path)
+//   pf_logits   router logits for all tokens (bf16 MFMA, from the prefill
+//               path); in a stack x_t = y_t / rms(y_t) is never written: the
+//               router and gate/up kernels scale their dot products by each
+//               token's 1/rms, computed from the loads they already make
 //   bn_select   per-token top-k, the expert union with token masks, and two
 //               work lists: (slot, token pair) items for gate/up and
 //               (slot, token) pairs for the down projection
 //   bn_gateup   one wave per (item, 2-4 features): weights and both tokens' x
 //               loaded before any arithmetic
-//   bn_down     8 output rows per block; the waves take (slot, token) pairs
+//   bn_down     8 output rows per block; its 8 waves take (slot, token) pairs
 //               in batches of 4 with every load of a batch in flight; the
 //               per-token partial sums are added in a fixed order
 // No floating-point atomics; every sum has a fixed order.
@@ -29,38 +31,11 @@ namespace moe {
 
 namespace {
 
-constexpr int BN_WAVES = 4;     // waves per block (gate/up and down)
+constexpr int BN_WAVES = 4;     // waves per block in gate/up
+constexpr int BN_DWAVES = 8;    // waves per block in down
 constexpr int BN_RR = 2;        // output rows per lane group in down
 constexpr int BN_PB = 4;        // (slot, token) pairs per load batch in down
 constexpr int BN_SEL_THREADS = 512;
-
-// ---------------------------------------------------------------------------
-// bn_norm: one block per token; xbuf[t] = y[t] / sqrt(mean(y[t]^2) + 1e-6).
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) bn_norm(DecodeParams p) {
-    __shared__ float red[4];
-    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float4 *y = reinterpret_cast<const float4 *>(p.x_prev + (size_t)t * p.D);
-    const int n4 = p.D / 4;
-    float ss = 0.f;
-    for (int i = tid; i < n4; i += 256) {
-        const float4 v = y[i];
-        ss = __builtin_fmaf(v.x, v.x, ss);
-        ss = __builtin_fmaf(v.y, v.y, ss);
-        ss = __builtin_fmaf(v.z, v.z, ss);
-        ss = __builtin_fmaf(v.w, v.w, ss);
-    }
-    ss = group_sum<MOE_WAVE>(ss);
-    if (lane == 0) red[wave] = ss;
-    __syncthreads();
-    const float tot = ((red[0] + red[1]) + red[2]) + red[3];
-    const float inv = 1.0f / sqrtf(tot / (float)p.D + 1e-6f);
-    float4 *xo = reinterpret_cast<float4 *>(p.xbuf + (size_t)t * p.D);
-    for (int i = tid; i < n4; i += 256) {
-        const float4 v = y[i];
-        xo[i] = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
-    }
-}
 
 // ---------------------------------------------------------------------------
 // bn_select: one block.  Wave t takes token t's top-k (or reads the given
@@ -79,6 +54,7 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
     __shared__ uint32_t act_m[256 + 4];
     __shared__ int n_items_s[256 + 4 + 1];
     __shared__ int n_pairs_s[256 + 4 + 1];
+    __shared__ int wtot_i[BN_SEL_THREADS / 64], wtot_p[BN_SEL_THREADS / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = p.T, K = p.K, E = p.E, S = p.S;
     if (tid < 256) emask[tid] = 0u;
@@ -125,28 +101,37 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
         act_m[tid] = (T >= 32) ? 0xFFFFFFFFu : ((1u << T) - 1u);
     }
     __syncthreads();
-    // per-slot work counts, then exclusive scans (one thread, <= 260 slots)
-    if (tid < n_act) {
-        const int c = __popc(act_m[tid]);
-        n_items_s[tid] = (c + 1) / 2;
-        n_pairs_s[tid] = c;
+    // per-slot work counts and their exclusive scans (8 waves x 64 slots)
+    const int c_slot = tid < n_act ? __popc(act_m[tid]) : 0;
+    const int ci = (c_slot + 1) / 2;
+    const int inc_i = wave_incl_scan(ci), inc_p = wave_incl_scan(c_slot);
+    if (lane == 63) {
+        wtot_i[wave] = inc_i;
+        wtot_p[wave] = inc_p;
     }
     __syncthreads();
-    if (tid == 0) {
-        int a = 0, b = 0;
-        for (int i = 0; i < n_act; i++) {
-            const int ci = n_items_s[i], cp = n_pairs_s[i];
-            n_items_s[i] = a;
-            n_pairs_s[i] = b;
-            a += ci;
-            b += cp;
-        }
-        n_items_s[n_act] = a;
-        n_pairs_s[n_act] = b;
-        p.meta[0] = n_act;
-        p.meta[1] = a;
-        p.meta[2] = b;
+    int off_i = 0, off_p = 0, tot_i = 0, tot_p = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < BN_SEL_THREADS / 64; w2++) {
+        off_i += w2 < wave ? wtot_i[w2] : 0;
+        off_p += w2 < wave ? wtot_p[w2] : 0;
+        tot_i += wtot_i[w2];
+        tot_p += wtot_p[w2];
     }
+    if (tid < n_act) {
+        n_items_s[tid] = off_i + inc_i - ci;
+        n_pairs_s[tid] = off_p + inc_p - c_slot;
+    }
+    if (tid == 0) {
+        p.meta[0] = n_act;
+        p.meta[1] = tot_i;
+        p.meta[2] = tot_p;
+    }
+    // gate/up items past the last are marked empty (slot -1), so the gate/up
+    // kernel needs no count
+    const int max_items = S * ((T + 1) / 2) + T * K;
+    for (int i = tot_i + tid; i < max_items; i += BN_SEL_THREADS)
+        reinterpret_cast<int4 *>(p.work)[i] = make_int4(-1, 0, 0, 0);
     __syncthreads();
     if (tid < n_act) {
         const int slot = tid, e = act_e[slot];
@@ -191,13 +176,14 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
     const int per_item = p.F / RG;
     const int gw = blockIdx.x * BN_WAVES + wave;
     const int item = gw / per_item, f0 = (gw % per_item) * RG;
-    if (item >= p.meta[1]) return;
     const int4 wk = reinterpret_cast<const int4 *>(p.work)[item];
+    if (wk.x < 0) return;  // past the last item
     const int slot = wk.x, ta = wk.y, tb = wk.z < 0 ? wk.y : wk.z, expert = wk.w;
     const uint8_t *eb = p.experts + (size_t)expert * p.expert_bytes;
     Mat mg{eb, p.F, p.D, p.tscale ? p.tscale[3 * expert + 0] : 1.f};
     Mat mu{eb + mat_bytes<FMT>(p.F, p.D), p.F, p.D, p.tscale ? p.tscale[3 * expert + 1] : 1.f};
-    const float *xin = p.x_prev ? p.xbuf : p.x;
+    const bool scaled = p.x_prev != nullptr;  // stack: x is the previous output, normalised here
+    const float *xin = scaled ? p.x_prev : p.x;
     WUnit wg[RG][UPLD], wu[RG][UPLD];
     XUnit<FMT> xa[UPLD], xb[UPLD];
 #pragma unroll
@@ -213,6 +199,22 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
         load_x<FMT>(xb[i], xin + (size_t)tb * p.D, lane + MOE_WAVE * i);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // the wave holds both tokens' whole rows: 1/rms from them (1 without a stack)
+    float inv[2] = {1.f, 1.f};
+    if (scaled) {
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int i = 0; i < UPLD; i++)
+#pragma unroll
+            for (int k = 0; k < Unit<FMT>::E; k++) {
+                sa = __builtin_fmaf(xa[i].v[k], xa[i].v[k], sa);
+                sb = __builtin_fmaf(xb[i].v[k], xb[i].v[k], sb);
+            }
+        sa = group_sum<MOE_WAVE>(sa);
+        sb = group_sum<MOE_WAVE>(sb);
+        inv[0] = 1.0f / sqrtf(sa / (float)p.D + 1e-6f);
+        inv[1] = 1.0f / sqrtf(sb / (float)p.D + 1e-6f);
+    }
     float ag[RG][2], au[RG][2];
 #pragma unroll
     for (int r = 0; r < RG; r++) {
@@ -229,8 +231,8 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
     for (int r = 0; r < RG; r++) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const float gs = group_sum<MOE_WAVE>(ag[r][j]);
-            const float us = group_sum<MOE_WAVE>(au[r][j]);
+            const float gs = group_sum<MOE_WAVE>(ag[r][j]) * inv[j];
+            const float us = group_sum<MOE_WAVE>(au[r][j]) * inv[j];
             const int t = j == 0 ? ta : tb;
             if (lane == 2 * r + j && (j == 0 || wk.z >= 0))
                 p.h[((size_t)slot * p.T + t) * p.F + f0 + r] = silu_mul(gs, us);
@@ -239,16 +241,16 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// bn_down: block = 4 waves over the same 8 output rows (LPR_F lanes per row
-// group, 2 rows per group); wave w takes pairs w, w + 4, ... in batches.
+// bn_down: block = 8 waves over the same output rows (LPR_F lanes per row
+// group, 2 rows per group); wave w takes pairs w, w + 8, ... in batches.
 // y[t, row] = sum over pairs (slot, t) of coef * Wd_slot[row] . h[slot, t].
 // ---------------------------------------------------------------------------
 template <int FMT, int LPR_F, int TT>
-__global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_down(DecodeParams p) {
+__global__ void __launch_bounds__(MOE_WAVE *BN_DWAVES) bn_down(DecodeParams p) {
     constexpr int UE = Unit<FMT>::E;
     constexpr int G = MOE_WAVE / LPR_F;  // row groups per wave
     constexpr int ROWS = G * BN_RR;      // rows per block
-    __shared__ float part[BN_WAVES][TT][ROWS];
+    __shared__ float part[BN_DWAVES][TT][ROWS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = lane / LPR_F, sub = lane % LPR_F;
@@ -261,7 +263,7 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_down(DecodeParams p) {
     for (int r = 0; r < BN_RR; r++)
 #pragma unroll
         for (int t = 0; t < TT; t++) acc[r][t] = 0.f;
-    for (int pb = wave; pb < n_pairs; pb += BN_WAVES * BN_PB) {
+    for (int pb = wave; pb < n_pairs; pb += BN_DWAVES * BN_PB) {
         // one batch: BN_PB pairs (clamped to the last pair; extras weigh 0)
         WUnit wd[BN_PB][BN_RR];
         XUnit<FMT> hv[BN_PB];
@@ -269,7 +271,7 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_down(DecodeParams p) {
         int tok[BN_PB];
 #pragma unroll
         for (int q = 0; q < BN_PB; q++) {
-            const int pi = pb + BN_WAVES * q;
+            const int pi = pb + BN_DWAVES * q;
             const int4 pr = reinterpret_cast<const int4 *>(p.pairs)[min(pi, n_pairs - 1)];
             coef[q] = pi < n_pairs ? __int_as_float(pr.z) : 0.f;
             tok[q] = pr.y;
@@ -314,12 +316,12 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_down(DecodeParams p) {
         }
     __syncthreads();
     // fixed-order sum of the waves' partials
-    for (int i = tid; i < TT * ROWS; i += MOE_WAVE * BN_WAVES) {
+    for (int i = tid; i < TT * ROWS; i += MOE_WAVE * BN_DWAVES) {
         const int t = i / ROWS, rr = i % ROWS;
         if (t >= p.T || rb + rr >= D) continue;
         float y = part[0][t][rr];
 #pragma unroll
-        for (int w = 1; w < BN_WAVES; w++) y += part[w][t][rr];
+        for (int w = 1; w < BN_DWAVES; w++) y += part[w][t][rr];
         p.y[(size_t)t * D + rb + rr] = y;
     }
 }
@@ -330,16 +332,16 @@ hipError_t launch_bn_fmt(const DecodeParams &p, hipStream_t st) {
     constexpr int RG = UPLD == 1 ? 4 : 2;  // features per wave (register budget)
     const int max_items = S * ((p.T + 1) / 2) + p.T * p.K;
     const int waves_g = max_items * (p.F / RG);
-    MOE_LAUNCH(3, (bn_gateup<FMT, UPLD, RG>), dim3((waves_g + BN_WAVES - 1) / BN_WAVES), dim3(MOE_WAVE * BN_WAVES),
+    MOE_LAUNCH(2, (bn_gateup<FMT, UPLD, RG>), dim3((waves_g + BN_WAVES - 1) / BN_WAVES), dim3(MOE_WAVE * BN_WAVES),
                st, p);
     const int rows = (MOE_WAVE / LPR_F) * BN_RR;
     const dim3 gd((p.D + rows - 1) / rows);
     if (p.T <= 2)
-        MOE_LAUNCH(4, (bn_down<FMT, LPR_F, 2>), gd, dim3(MOE_WAVE * BN_WAVES), st, p);
+        MOE_LAUNCH(3, (bn_down<FMT, LPR_F, 2>), gd, dim3(MOE_WAVE * BN_DWAVES), st, p);
     else if (p.T <= 4)
-        MOE_LAUNCH(4, (bn_down<FMT, LPR_F, 4>), gd, dim3(MOE_WAVE * BN_WAVES), st, p);
+        MOE_LAUNCH(3, (bn_down<FMT, LPR_F, 4>), gd, dim3(MOE_WAVE * BN_DWAVES), st, p);
     else
-        MOE_LAUNCH(4, (bn_down<FMT, LPR_F, 8>), gd, dim3(MOE_WAVE * BN_WAVES), st, p);
+        MOE_LAUNCH(3, (bn_down<FMT, LPR_F, 8>), gd, dim3(MOE_WAVE * BN_DWAVES), st, p);
     return hipGetLastError();
 }
 
@@ -366,7 +368,7 @@ bool bn_shape_ok(const DecodeParams &p) {
 
 }  // namespace
 
-// Kernel slots: 0 norm, 1 logits, 2 select, 3 gate/up, 4 down.
+// Kernel slots: 0 logits, 1 select, 2 gate/up, 3 down.
 hipError_t launch_decode_bn(const DecodeParams &p, hipStream_t st) {
     if (p.T < 1 || p.T > MAX_DECODE_T || p.E > 256 || p.S > 4 || !p.want_shared) return hipErrorNotSupported;
     if (!p.work || !p.pairs) return hipErrorNotSupported;
@@ -374,15 +376,14 @@ hipError_t launch_decode_bn(const DecodeParams &p, hipStream_t st) {
                     : p.fmt == FMT_NVFP4 ? bn_shape_ok<FMT_NVFP4>(p)
                                          : bn_shape_ok<FMT_BF16>(p);
     if (!ok) return hipErrorNotSupported;
-    if (p.x_prev) MOE_LAUNCH(0, bn_norm, dim3(p.T), dim3(256), st, p);
     if (!p.route_given) {
         if (!p.want_router) return hipErrorNotSupported;
-        const float *xin = p.x_prev ? p.xbuf : p.x;
+        const float *xin = p.x_prev ? p.x_prev : p.x;
         const hipError_t e = launch_router_logits(xin, p.T, p.D, p.E, p.router, p.bias, p.logits,
-                                                  p.ev ? p.ev + 2 : nullptr, st);
+                                                  p.x_prev ? 1 : 0, p.ev, st);
         if (e != hipSuccess) return e;
     }
-    MOE_LAUNCH(2, bn_select, dim3(1), dim3(BN_SEL_THREADS), st, p);
+    MOE_LAUNCH(1, bn_select, dim3(1), dim3(BN_SEL_THREADS), st, p);
     if (p.fmt == FMT_Q4_1) return launch_bn_shape<FMT_Q4_1>(p, st);
     if (p.fmt == FMT_NVFP4) return launch_bn_shape<FMT_NVFP4>(p, st);
     return launch_bn_shape<FMT_BF16>(p, st);

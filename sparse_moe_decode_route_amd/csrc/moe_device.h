@@ -275,6 +275,17 @@ __device__ __forceinline__ void wave_topk_regs(const float lv[4], int E, int K, 
     *w_out = ev / den;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & (MOE_WAVE - 1);
+#pragma unroll
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+        const int u = __shfl_up(v, o, MOE_WAVE);
+        v += lane >= o ? u : 0;
+    }
+    return v;
+}
+
 // Loads of one token's logits for wave_topk_regs (clamped in-bounds indices).
 __device__ __forceinline__ void wave_topk_load(const float *l, int E, float lv[4]) {
     const int lane = threadIdx.x & (MOE_WAVE - 1);

@@ -60,7 +60,7 @@ struct DecodeParams {
     } while (0)
 
 // Kernel slots of one layer, per decode path (names as reported by the timing entry point).
-constexpr int MAX_KERNEL_SLOTS = 5;
+constexpr int MAX_KERNEL_SLOTS = 4;
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
 // Batch-1 path (three kernels per layer); hipErrorNotSupported if the shape

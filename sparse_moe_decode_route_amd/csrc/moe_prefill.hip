@@ -37,7 +37,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int PF_BM = 128;          // rows (token slots) per GEMM tile
 constexpr int PF_THREADS = 256;     // 4 waves
-constexpr int PF_RT = 64;           // tokens per router block
 constexpr int PF_MAX_TOPK = 8;
 
 struct PfTile {
@@ -83,6 +82,7 @@ T *wsp(void *ws, size_t off) {
 
 struct PfParams {
     int D, F, E, S, K, T, act, NW, R, tiles_max, want_x16;
+    int rms_in;          // pf_logits: x is un-normalised, scale each token by 1/rms(x)
     hipEvent_t *ev;
     size_t expert_bytes;
     const void *x;
@@ -120,29 +120,34 @@ __device__ __forceinline__ uint32_t f2bf_rne(float f) {
 
 // ---------------------------------------------------------------------------
 // pf_logits: logits[t, e] = x[t] . Wr[e] (+ bias[e]) by bf16 MFMA.  One block
-// = 32 experts x 32 tokens; its 4 waves split the reduction into quarters,
+// = 32 experts x 32 tokens; its KS waves split the reduction into KS parts,
 // summed in wave order through LDS.  Blocks of the first expert column also
 // write the fp16 copy of x (operand of the expert GEMMs).  An fp32 input is
-// split x = hi + lo into two bf16 parts, both accumulated.
+// split x = hi + lo into two bf16 parts, both accumulated.  With rms_in, x is
+// the previous layer's output and each token's logits are scaled by
+// 1 / sqrt(mean(x^2) + 1e-6) (the dot product is linear in x); the sum of
+// squares comes from the same loads, in a fixed order.
 // ---------------------------------------------------------------------------
 constexpr int PF_LG_CH = 8;  // reduction steps of 16 per load batch
 
-template <int ACT>
-__global__ void __launch_bounds__(PF_THREADS) pf_logits(PfParams p) {
-    __shared__ float red[4][32][33];
+template <int ACT, int KS>
+__global__ void __launch_bounds__(64 * KS) pf_logits(PfParams p) {
+    __shared__ float red[KS][32][33];
+    __shared__ float ssq[KS][32];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int D = p.D, E = p.E, T = p.T;
     const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
-    const int NKS = D / 16;                                   // reduction steps
-    const int ks0 = wave * NKS / 4, ks1 = (wave + 1) * NKS / 4;  // this wave's quarter
+    const int NKS = D / 16;                                     // reduction steps
+    const int ks0 = wave * NKS / KS, ks1 = (wave + 1) * NKS / KS;  // this wave's part
     const uint16_t *wrow = p.router + (size_t)min(e0 + l32, E - 1) * D + 8 * g;
     const int trow = min(t0 + l32, T - 1);
     const bool write_x16 = p.want_x16 && blockIdx.y == 0 && t0 + l32 < T;
     f32x16_t acc;
 #pragma unroll
     for (int j = 0; j < 16; j++) acc[j] = 0.f;
+    float ss = 0.f;
     for (int kc = ks0; kc < ks1; kc += PF_LG_CH) {
         // one batch: every load first, then the MFMAs
         uint4 av[PF_LG_CH];
@@ -150,6 +155,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_logits(PfParams p) {
 #pragma unroll
         for (int c = 0; c < PF_LG_CH; c++) {
             const int k0 = 16 * min(kc + c, ks1 - 1);
+            const bool live = kc + c < ks1;
             av[c] = *reinterpret_cast<const uint4 *>(wrow + k0);
             if (ACT == 0) {
                 const float *xs = static_cast<const float *>(p.x) + (size_t)trow * D + k0 + 8 * g;
@@ -168,15 +174,18 @@ __global__ void __launch_bounds__(PF_THREADS) pf_logits(PfParams p) {
                     hv[2 * j] = (_Float16)xv[2 * j];
                     hv[2 * j + 1] = (_Float16)xv[2 * j + 1];
                 }
+                if (live) {
+#pragma unroll
+                    for (int j = 0; j < 8; j++) ss = __builtin_fmaf(xv[j], xv[j], ss);
+                }
                 bh[c] = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
                 bl[c] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-                if (write_x16 && kc + c < ks1)
-                    *reinterpret_cast<half8_t *>(p.x16 + (size_t)trow * D + k0 + 8 * g) = hv;
+                if (write_x16 && live) *reinterpret_cast<half8_t *>(p.x16 + (size_t)trow * D + k0 + 8 * g) = hv;
             } else {
                 const uint4 r = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + (size_t)trow * D +
                                                                  k0 + 8 * g);
                 bh[c] = as_bf16x8(r);
-                if (write_x16 && kc + c < ks1) {
+                if (write_x16 && live) {
                     const uint32_t ww[4] = {r.x, r.y, r.z, r.w};
                     half8_t hv;
 #pragma unroll
@@ -199,15 +208,24 @@ __global__ void __launch_bounds__(PF_THREADS) pf_logits(PfParams p) {
     // acc[j] = partial logit of expert e0 + 8 (j/4) + 4 g + j%4, token t0 + l32
 #pragma unroll
     for (int j = 0; j < 16; j++) red[wave][8 * (j >> 2) + 4 * g + (j & 3)][l32] = acc[j];
+    if (ACT == 0) {
+        ss += __shfl_xor(ss, 32, 64);  // the two lane groups of token l32
+        if (g == 0) ssq[wave][l32] = ss;
+    }
     __syncthreads();
-    for (int i = tid; i < 32 * 32; i += PF_THREADS) {
+    for (int i = tid; i < 32 * 32; i += 64 * KS) {
         const int el = i >> 5, tl = i & 31;
         const int e = e0 + el, t = t0 + tl;
         if (e >= E || t >= T) continue;
         float v = red[0][el][tl];
-        v += red[1][el][tl];
-        v += red[2][el][tl];
-        v += red[3][el][tl];
+#pragma unroll
+        for (int w = 1; w < KS; w++) v += red[w][el][tl];
+        if (ACT == 0 && p.rms_in) {
+            float q = ssq[0][tl];
+#pragma unroll
+            for (int w = 1; w < KS; w++) q += ssq[w][tl];
+            v *= 1.0f / sqrtf(q / (float)D + 1e-6f);
+        }
         p.logits[(size_t)t * E + e] = v + (p.bias ? p.bias[e] : 0.f);
     }
 }
@@ -299,16 +317,6 @@ __global__ void __launch_bounds__(PF_THREADS) pf_mask_given(PfParams p) {
 // words; then block-wide exclusive scans of the row counts and tile counts.
 // ---------------------------------------------------------------------------
 constexpr int PF_SCAN_THREADS = 1024;
-
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(v, o, 64);
-        v += lane >= o ? u : 0;
-    }
-    return v;
-}
 
 // exclusive scan over the block (one value per thread, 1024 threads)
 __device__ __forceinline__ int block_excl_scan(int v, int *tmp16, int *total) {
@@ -807,14 +815,16 @@ const char *const kPrefillNames = "pf_logits;pf_topk;pf_scan;pf_scatter;pf_gemm_
 size_t prefill_ws_bytes(int D, int F, int E, int S, int K, int T) { return pf_layout(D, F, E, S, K, T).total; }
 
 hipError_t launch_router_logits(const float *x, int T, int D, int E, const uint16_t *router, const float *bias,
-                                float *logits, hipEvent_t *ev, hipStream_t st) {
+                                float *logits, int rms_in, hipEvent_t *ev, hipStream_t st) {
     if (E > 256 || D % 16) return hipErrorNotSupported;
     PfParams p{};
     p.D = D; p.E = E; p.T = T;
     p.x = x; p.router = router; p.bias = bias; p.logits = logits;
     p.want_x16 = 0;
+    p.rms_in = rms_in;
     p.ev = ev;
-    MOE_LAUNCH(0, (pf_logits<0>), dim3((T + 31) / 32, (E + 31) / 32), dim3(PF_THREADS), st, p);
+    // few tokens: an 8-way split of the reduction keeps 8 waves per block busy
+    MOE_LAUNCH(0, (pf_logits<0, 8>), dim3((T + 31) / 32, (E + 31) / 32), dim3(64 * 8), st, p);
     return hipGetLastError();
 }
 
@@ -847,9 +857,9 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     if (!a.given_idx) {
         const dim3 gl((a.T + 31) / 32, (a.E + 31) / 32);
         if (a.act == MOE_ACT_F32)
-            MOE_LAUNCH(0, (pf_logits<0>), gl, dim3(PF_THREADS), st, p);
+            MOE_LAUNCH(0, (pf_logits<0, 4>), gl, dim3(PF_THREADS), st, p);
         else
-            MOE_LAUNCH(0, (pf_logits<1>), gl, dim3(PF_THREADS), st, p);
+            MOE_LAUNCH(0, (pf_logits<1, 4>), gl, dim3(PF_THREADS), st, p);
         MOE_LAUNCH(1, pf_topk, dim3(nb64), dim3(PF_TOPK_THREADS), st, p);
         if (a.route_only) return hipGetLastError();
     } else {
