@@ -53,7 +53,8 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Decode-path workspace (n_tokens <= 8).
 struct DecodeWs {
-    size_t logits, idx, w, xbuf, xconv, meta, act_expert, act_mask, act_w, h, ybuf0, ybuf1, work, pairs, total;
+    size_t logits, idx, w, xbuf, xconv, meta, act_expert, act_mask, act_w, h, ybuf0, ybuf1, work, pairs, b1_list,
+        total;
     int amax;
 };
 
@@ -80,6 +81,7 @@ DecodeWs decode_ws(const moe_dims &d, int T) {
     L.ybuf1 = take((size_t)T * d.d_model * 4);
     L.work = take((size_t)(d.n_shared * ((T + 1) / 2) + T * d.top_k) * 16);
     L.pairs = take((size_t)(d.n_shared * T + T * d.top_k) * 16);
+    L.b1_list = take(8 * 16 * 4);
     L.total = o;
     return L;
 }
@@ -111,6 +113,7 @@ moe::DecodeParams base_params(const moe_dims &d, int T, void *ws, const DecodeWs
     p.h = at<float>(ws, L.h);
     p.work = at<int32_t>(ws, L.work);
     p.pairs = at<int32_t>(ws, L.pairs);
+    p.b1_list = at<int32_t>(ws, L.b1_list);
     return p;
 }
 

@@ -18,6 +18,7 @@
 // indices, so that the compiler counts outstanding loads exactly), and
 // reductions use DPP lane exchanges.
 #include <hip/hip_fp16.h>
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include "moe_device.h"
@@ -48,7 +49,7 @@ __device__ __forceinline__ float inv_rms_from(const float4 (&y)[2 * UPLR]) {
         ss = __builtin_fmaf(y[i].z, y[i].z, ss);
         ss = __builtin_fmaf(y[i].w, y[i].w, ss);
     }
-    ss = group_sum<MOE_WAVE>(ss);
+    ss = wave_sum(ss);
     return 1.0f / sqrtf(ss / (float)(UPLR * 512) + 1e-6f);
 }
 
@@ -104,8 +105,8 @@ __device__ __forceinline__ void gateup_finish(const GateUp<FMT, UPLD, RG> &g, co
     }
 #pragma unroll
     for (int r = 0; r < RG; r++) {
-        const float gs = group_sum<MOE_WAVE>(ag[r]);
-        const float us = group_sum<MOE_WAVE>(au[r]);
+        const float gs = wave_sum(ag[r]);
+        const float us = wave_sum(au[r]);
         if (lane == r) p.h[(size_t)slot * p.F + f0 + r] = silu_mul(gs, us);
     }
 }
@@ -153,7 +154,7 @@ __global__ void __launch_bounds__(MOE_WAVE) b1_route_shared(DecodeParams p) {
             xv.sum = 0.f;
             acc += unit_dot<FMT_BF16>(w[i], xv, 1.f);
         }
-        const float s = group_sum<MOE_WAVE>(acc);
+        const float s = wave_sum(acc);
         if (lane == 0) p.logits[e] = p.bias ? s + p.bias[e] : s;
         return;
     }
@@ -195,6 +196,19 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_B) b1_topk_gateup(DecodePar
         float wi;
         wave_topk(p.logits, p.E, p.K, &e, &wi);
         if (lane < 8) s_sel[lane] = e;
+        if ((int)blockIdx.x < p.b1_ncopy) {
+            // one copy of the active list per XCD (block b runs on XCD b % 8),
+            // read by the down kernel's blocks of the same XCD
+            int32_t *cp = p.b1_list + 16 * blockIdx.x;
+            if (lane < p.S) {
+                cp[lane] = p.E + lane;
+                cp[8 + lane] = __float_as_int(1.f);
+            }
+            if (lane < p.K) {
+                cp[p.S + lane] = e;
+                cp[8 + p.S + lane] = __float_as_int(wi);
+            }
+        }
         if (blockIdx.x == 0) {
             if (lane < p.K) {
                 p.idx[lane] = e;
@@ -211,7 +225,13 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_B) b1_topk_gateup(DecodePar
             if (lane == 0) p.meta[0] = p.S + p.K;
         }
     }
-    __syncthreads();
+    // only s_sel (LDS) is shared: wait for the LDS write, then a barrier
+    // without the global release fence of __syncthreads (which would hold
+    // block 0 until its routing stores were acknowledged)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const int per_expert = p.F / B1_RG;
     const int gw = blockIdx.x * B1_WAVES_B + wave;
     const int j = gw / per_expert, f0 = (gw % per_expert) * B1_RG;
@@ -254,10 +274,12 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_C) b1_down(DecodeParams p) 
     const int n_active = p.S + p.K;
     const int rb = blockIdx.x * ROWS;
     const int r0 = rb + grp * B1_RR;
-    // 1) the active list (one load per lane), read back per slot below
+    // 1) the active list (one load per lane) from this XCD's copy, read back
+    //    per slot below
     const int la = min(lane, n_active - 1);
-    const int my_e = p.act_expert[la];
-    const float my_c = p.act_w[la];
+    const int32_t *lst = p.b1_list + 16 * (blockIdx.x % p.b1_ncopy);
+    const int my_e = lst[la];
+    const float my_c = __int_as_float(lst[8 + la]);
     // 2) every slot's h straight into LDS (global_load_lds: lane L of a wave
     //    instruction writes 16 bytes at the instruction's LDS base + 16 L, so
     //    each lane gathers the source for its padded position; pad positions
@@ -338,7 +360,9 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_C) b1_down(DecodeParams p) 
 }
 
 template <int FMT, int UPLD>
-hipError_t launch_fmt(const DecodeParams &p, hipStream_t st, int uplr, int lpr_f) {
+hipError_t launch_fmt(const DecodeParams &pin, hipStream_t st, int uplr, int lpr_f) {
+    DecodeParams p = pin;
+    p.b1_ncopy = std::min(8, (p.K * (p.F / B1_RG) + B1_WAVES_B - 1) / B1_WAVES_B);
     const int per_expert = p.F / B1_RG;
     const int grid_a = p.E + p.S * per_expert;
 #define MOE_A(U)                                                                          \

@@ -210,8 +210,8 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
                 sa = __builtin_fmaf(xa[i].v[k], xa[i].v[k], sa);
                 sb = __builtin_fmaf(xb[i].v[k], xb[i].v[k], sb);
             }
-        sa = group_sum<MOE_WAVE>(sa);
-        sb = group_sum<MOE_WAVE>(sb);
+        sa = wave_sum(sa);
+        sb = wave_sum(sb);
         inv[0] = 1.0f / sqrtf(sa / (float)p.D + 1e-6f);
         inv[1] = 1.0f / sqrtf(sb / (float)p.D + 1e-6f);
     }
@@ -231,8 +231,8 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
     for (int r = 0; r < RG; r++) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const float gs = group_sum<MOE_WAVE>(ag[r][j]) * inv[j];
-            const float us = group_sum<MOE_WAVE>(au[r][j]) * inv[j];
+            const float gs = wave_sum(ag[r][j]) * inv[j];
+            const float us = wave_sum(au[r][j]) * inv[j];
             const int t = j == 0 ? ta : tb;
             if (lane == 2 * r + j && (j == 0 || wk.z >= 0))
                 p.h[((size_t)slot * p.T + t) * p.F + f0 + r] = silu_mul(gs, us);

@@ -195,6 +195,20 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Sum over the whole wave, returned uniform (an SGPR value): rows of 16
+// reduced by DPP, then row 1 += row 0 and row 3 += row 2 (row_bcast:15),
+// rows 2-3 += row 1 (row_bcast:31), and lane 63 read back.  Fixed order, and
+// no LDS round trip (unlike a shuffle through ds_bpermute).
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    v += dpp_f<DPP_HALF_MIRROR>(v);
+    v += dpp_f<DPP_MIRROR>(v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key, -0 is
@@ -270,7 +284,7 @@ __device__ __forceinline__ void wave_topk_regs(const float lv[4], int E, int K, 
         if (i + 1 >= K) break;
     }
     const float ev = lane < K ? __expf(key2f(my_key) - key2f(first_key)) : 0.f;
-    const float den = group_sum<MOE_WAVE>(ev);
+    const float den = wave_sum(ev);
     *e_out = lane < K ? my_e : 0;
     *w_out = ev / den;
 }

@@ -48,6 +48,8 @@ struct DecodeParams {
     hipEvent_t *ev;
     int32_t *work;       // small-batch path: gate/up items {slot, token a, token b, expert}
     int32_t *pairs;      // small-batch path: down pairs {slot, token, coef bits, expert}
+    int32_t *b1_list;    // batch-1 path: 8 copies (one per XCD) of {expert[8], coef bits[8]}
+    int b1_ncopy;        // copies written (gate/up blocks 0 .. b1_ncopy - 1)
 };
 
 // Launch `kern(p)` on `st`, timed into event pair `slot` when p.ev is set.
