@@ -35,6 +35,7 @@ constexpr int BN_WAVES = 4;     // waves per block in gate/up
 constexpr int BN_DWAVES = 8;    // waves per block in down
 constexpr int BN_RR = 2;        // output rows per lane group in down
 constexpr int BN_PB = 4;        // (slot, token) pairs per load batch in down
+constexpr int BN_MAXB = 3;      // batches per wave: 8 tokens x (8 + 4) pairs / (8 waves x 4)
 constexpr int BN_SEL_THREADS = 512;
 
 // ---------------------------------------------------------------------------
@@ -132,6 +133,10 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
     const int max_items = S * ((T + 1) / 2) + T * K;
     for (int i = tot_i + tid; i < max_items; i += BN_SEL_THREADS)
         reinterpret_cast<int4 *>(p.work)[i] = make_int4(-1, 0, 0, 0);
+    // down pairs past the last: token -1 (never accumulated), expert 0, h row 0
+    const int max_pairs = T * (K + S);
+    for (int i = tot_p + tid; i < max_pairs; i += BN_SEL_THREADS)
+        reinterpret_cast<int4 *>(p.pairs)[i] = make_int4(0, -1, 0, 0);
     __syncthreads();
     if (tid < n_act) {
         const int slot = tid, e = act_e[slot];
@@ -162,6 +167,59 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
             }
         }
         if (pend >= 0) reinterpret_cast<int4 *>(p.work)[it++] = make_int4(slot, pend, -1, e);
+    }
+}
+
+// h for one work item from weights and x in registers: the wave holds the
+// tokens' whole rows, so 1/rms comes from them (1 outside a stack).
+template <int FMT, int UPLD, int RG, bool TWO>
+__device__ __forceinline__ void bn_gateup_finish(const DecodeParams &p, const WUnit (&wg)[RG][UPLD],
+                                                 const WUnit (&wu)[RG][UPLD], const XUnit<FMT> (&xa)[UPLD],
+                                                 const XUnit<FMT> (&xb)[UPLD], float tsg, float tsu, bool scaled,
+                                                 int slot, int ta, int tb, int f0) {
+    const int lane = threadIdx.x & 63;
+    float inv[2] = {1.f, 1.f};
+    if (scaled) {
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int i = 0; i < UPLD; i++)
+#pragma unroll
+            for (int k = 0; k < Unit<FMT>::E; k++) {
+                sa = __builtin_fmaf(xa[i].v[k], xa[i].v[k], sa);
+                if (TWO) sb = __builtin_fmaf(xb[i].v[k], xb[i].v[k], sb);
+            }
+        inv[0] = 1.0f / sqrtf(wave_sum(sa) / (float)p.D + 1e-6f);
+        if (TWO) inv[1] = 1.0f / sqrtf(wave_sum(sb) / (float)p.D + 1e-6f);
+    }
+    float ag[RG][2], au[RG][2];
+#pragma unroll
+    for (int r = 0; r < RG; r++) {
+        ag[r][0] = ag[r][1] = au[r][0] = au[r][1] = 0.f;
+#pragma unroll
+        for (int i = 0; i < UPLD; i++) {
+            if (TWO) {
+                float g0, g1, u0, u1;
+                unit_dot2<FMT>(wg[r][i], xa[i], xb[i], tsg, g0, g1);
+                unit_dot2<FMT>(wu[r][i], xa[i], xb[i], tsu, u0, u1);
+                ag[r][0] += g0;
+                ag[r][1] += g1;
+                au[r][0] += u0;
+                au[r][1] += u1;
+            } else {
+                ag[r][0] += unit_dot<FMT>(wg[r][i], xa[i], tsg);
+                au[r][0] += unit_dot<FMT>(wu[r][i], xa[i], tsu);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RG; r++) {
+#pragma unroll
+        for (int j = 0; j < (TWO ? 2 : 1); j++) {
+            const float gs = wave_sum(ag[r][j]) * inv[j];
+            const float us = wave_sum(au[r][j]) * inv[j];
+            const int t = j == 0 ? ta : tb;
+            if (lane == 2 * r + j) p.h[((size_t)slot * p.T + t) * p.F + f0 + r] = silu_mul(gs, us);
+        }
     }
 }
 
@@ -199,45 +257,12 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
         load_x<FMT>(xb[i], xin + (size_t)tb * p.D, lane + MOE_WAVE * i);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // the wave holds both tokens' whole rows: 1/rms from them (1 without a stack)
-    float inv[2] = {1.f, 1.f};
-    if (scaled) {
-        float sa = 0.f, sb = 0.f;
-#pragma unroll
-        for (int i = 0; i < UPLD; i++)
-#pragma unroll
-            for (int k = 0; k < Unit<FMT>::E; k++) {
-                sa = __builtin_fmaf(xa[i].v[k], xa[i].v[k], sa);
-                sb = __builtin_fmaf(xb[i].v[k], xb[i].v[k], sb);
-            }
-        sa = wave_sum(sa);
-        sb = wave_sum(sb);
-        inv[0] = 1.0f / sqrtf(sa / (float)p.D + 1e-6f);
-        inv[1] = 1.0f / sqrtf(sb / (float)p.D + 1e-6f);
-    }
-    float ag[RG][2], au[RG][2];
-#pragma unroll
-    for (int r = 0; r < RG; r++) {
-        ag[r][0] = ag[r][1] = au[r][0] = au[r][1] = 0.f;
-#pragma unroll
-        for (int i = 0; i < UPLD; i++) {
-            ag[r][0] += unit_dot<FMT>(wg[r][i], xa[i], mg.ts);
-            au[r][0] += unit_dot<FMT>(wu[r][i], xa[i], mu.ts);
-            ag[r][1] += unit_dot<FMT>(wg[r][i], xb[i], mg.ts);
-            au[r][1] += unit_dot<FMT>(wu[r][i], xb[i], mu.ts);
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < RG; r++) {
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const float gs = wave_sum(ag[r][j]) * inv[j];
-            const float us = wave_sum(au[r][j]) * inv[j];
-            const int t = j == 0 ? ta : tb;
-            if (lane == 2 * r + j && (j == 0 || wk.z >= 0))
-                p.h[((size_t)slot * p.T + t) * p.F + f0 + r] = silu_mul(gs, us);
-        }
-    }
+    // a routed expert usually serves one token of the batch: the second
+    // token's arithmetic only runs for items that have one (uniform branch)
+    if (wk.z >= 0)
+        bn_gateup_finish<FMT, UPLD, RG, true>(p, wg, wu, xa, xb, mg.ts, mu.ts, scaled, slot, ta, tb, f0);
+    else
+        bn_gateup_finish<FMT, UPLD, RG, false>(p, wg, wu, xa, xb, mg.ts, mu.ts, scaled, slot, ta, tb, f0);
 }
 
 // ---------------------------------------------------------------------------
@@ -257,13 +282,23 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_DWAVES) bn_down(DecodeParams p) {
     const int D = p.D, F = p.F;
     const int rb = blockIdx.x * ROWS;
     const int r0 = rb + grp * BN_RR;
-    const int n_pairs = p.meta[2];
+    // the pairs list is padded to its maximum (entries past the last have
+    // token -1 and add nothing), so no count is read; every entry this wave
+    // will use is loaded before the first weight load
+    const int max_pairs = p.T * (p.K + p.S);
+    int4 ent[BN_MAXB * BN_PB];
+#pragma unroll
+    for (int i = 0; i < BN_MAXB * BN_PB; i++)
+        ent[i] = reinterpret_cast<const int4 *>(p.pairs)[min(wave + BN_DWAVES * i, max_pairs - 1)];
     float acc[BN_RR][TT];
 #pragma unroll
     for (int r = 0; r < BN_RR; r++)
 #pragma unroll
         for (int t = 0; t < TT; t++) acc[r][t] = 0.f;
-    for (int pb = wave; pb < n_pairs; pb += BN_DWAVES * BN_PB) {
+#pragma unroll
+    for (int bt = 0; bt < BN_MAXB; bt++) {
+        const int pb = wave + BN_DWAVES * BN_PB * bt;
+        if (pb >= max_pairs) break;
         // one batch: BN_PB pairs (clamped to the last pair; extras weigh 0)
         WUnit wd[BN_PB][BN_RR];
         XUnit<FMT> hv[BN_PB];
@@ -272,15 +307,15 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_DWAVES) bn_down(DecodeParams p) {
 #pragma unroll
         for (int q = 0; q < BN_PB; q++) {
             const int pi = pb + BN_DWAVES * q;
-            const int4 pr = reinterpret_cast<const int4 *>(p.pairs)[min(pi, n_pairs - 1)];
-            coef[q] = pi < n_pairs ? __int_as_float(pr.z) : 0.f;
-            tok[q] = pr.y;
+            const int4 pr = ent[bt * BN_PB + q];
+            coef[q] = pi < max_pairs ? __int_as_float(pr.z) : 0.f;
+            tok[q] = pi < max_pairs ? pr.y : -1;
             const uint8_t *eb = p.experts + (size_t)pr.w * p.expert_bytes;
             Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, p.tscale ? p.tscale[3 * pr.w + 2] : 1.f};
             ts[q] = md.ts;
 #pragma unroll
             for (int r = 0; r < BN_RR; r++) wd[q][r] = load_unit<FMT>(md, min(r0 + r, D - 1), sub);
-            const float *hsrc = p.h + ((size_t)pr.x * p.T + pr.y) * F;
+            const float *hsrc = p.h + ((size_t)pr.x * p.T + max(pr.y, 0)) * F;
 #pragma unroll
             for (int i = 0; i < UE / 4; i++) {
                 const float4 f = reinterpret_cast<const float4 *>(hsrc + sub * UE)[i];

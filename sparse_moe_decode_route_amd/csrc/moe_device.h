@@ -167,6 +167,64 @@ __device__ __forceinline__ float unit_dot(const WUnit &w, const XUnit<FMT> &x, f
     }
 }
 
+// dot(unit weights, x) for two tokens at once: each weight is decoded once.
+template <int FMT>
+__device__ __forceinline__ void unit_dot2(const WUnit &w, const XUnit<FMT> &xa, const XUnit<FMT> &xb, float ts,
+                                          float &ra, float &rb) {
+    if (FMT == FMT_BF16) {
+        uint32_t a[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float lo = bf16lo(a[i]), hi = bf16hi(a[i]);
+            sa = __builtin_fmaf(lo, xa.v[2 * i], sa);
+            sb = __builtin_fmaf(lo, xb.v[2 * i], sb);
+            sa = __builtin_fmaf(hi, xa.v[2 * i + 1], sa);
+            sb = __builtin_fmaf(hi, xb.v[2 * i + 1], sb);
+        }
+        ra = sa;
+        rb = sb;
+    } else if (FMT == FMT_Q4_1) {
+        uint32_t a[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
+        float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint32_t lo = opaque(a[i] & 0x0F0F0F0Fu);
+            uint32_t hi = opaque((a[i] >> 4) & 0x0F0F0F0Fu);
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const float ql = (float)((lo >> (8 * b)) & 0xFFu), qh = (float)((hi >> (8 * b)) & 0xFFu);
+                a0 = __builtin_fmaf(ql, xa.v[4 * i + b], a0);
+                b0 = __builtin_fmaf(ql, xb.v[4 * i + b], b0);
+                a1 = __builtin_fmaf(qh, xa.v[16 + 4 * i + b], a1);
+                b1 = __builtin_fmaf(qh, xb.v[16 + 4 * i + b], b1);
+            }
+        }
+        const float d = half_bits_to_float(w.s), m = half_bits_to_float(w.s >> 16);
+        ra = __builtin_fmaf(d, a0 + a1, m * xa.sum);
+        rb = __builtin_fmaf(d, b0 + b1, m * xb.sum);
+    } else {
+        uint32_t a[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
+        float sa[2] = {0.f, 0.f}, sb[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(a[i], 1.0f, 0);
+            const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(a[i], 1.0f, 1);
+            const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(a[i], 1.0f, 2);
+            const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(a[i], 1.0f, 3);
+            const float v[8] = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                sa[i >> 1] = __builtin_fmaf(v[j], xa.v[8 * i + j], sa[i >> 1]);
+                sb[i >> 1] = __builtin_fmaf(v[j], xb.v[8 * i + j], sb[i >> 1]);
+            }
+        }
+        const float s0 = e4m3_to_float(w.s & 0xFFu), s1 = e4m3_to_float((w.s >> 8) & 0xFFu);
+        ra = ts * __builtin_fmaf(s0, sa[0], s1 * sa[1]);
+        rb = ts * __builtin_fmaf(s0, sb[0], s1 * sb[1]);
+    }
+}
+
 // DPP lane exchange within rows of 16 lanes.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
