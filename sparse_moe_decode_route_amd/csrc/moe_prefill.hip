@@ -427,12 +427,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// 4 nibbles (bytes of t, each < 16) -> two fp16 pairs holding the integers
+// 4 nibbles (bytes of t, each < 16) -> two fp16 pairs holding the integers:
+// v_perm_b32 places each byte under a 0x64 high byte, giving the fp16 value
+// 1024 + q exactly; subtracting 1024 is exact too.
 __device__ __forceinline__ void nib4_to_h(uint32_t t, half2_t &a, half2_t &b) {
-    const uint32_t p01 = (t & 0xFFu) | ((t & 0xFF00u) << 8) | 0x64006400u;
-    const uint32_t p23 = ((t >> 16) & 0xFFu) | ((t >> 8) & 0xFF0000u) | 0x64006400u;
+    const uint32_t p01 = __builtin_amdgcn_perm(0x64646464u, t, 0x04010400u);  // bytes t0, 64, t1, 64
+    const uint32_t p23 = __builtin_amdgcn_perm(0x64646464u, t, 0x04030402u);  // bytes t2, 64, t3, 64
     const half2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-    a = __builtin_bit_cast(half2_t, p01) - k1024;  // exact: 1024 + q - 1024
+    a = __builtin_bit_cast(half2_t, p01) - k1024;
     b = __builtin_bit_cast(half2_t, p23) - k1024;
 }
 
@@ -607,7 +609,7 @@ __device__ __forceinline__ void pf_issue(const PfDma<FMT> &d, uint4 *xs, uint8_t
 // weights are dequantised from LDS into MFMA operands.
 // ---------------------------------------------------------------------------
 template <int FMT, int MODE>
-__global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfParams p) {
+__global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm(PfParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     // one LDS object per stage: stage indices are compile-time after
     // unrolling, so alias analysis separates a stage's DMA writes from the
