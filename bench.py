@@ -340,7 +340,8 @@ def bench_prefill(args):
     per_kernel = {k: dict(us_per_launch=round(v, 2)) for k, v in kus.items()}
     per_kernel["pf_gemm_gateup"]["tflops"] = round(fl_gu / (kus["pf_gemm_gateup"] * 1e-6) / 1e12, 1)
     per_kernel["pf_gemm_down"]["tflops"] = round(fl_dn / (kus["pf_gemm_down"] * 1e-6) / 1e12, 1)
-    per_kernel["pf_logits"]["tflops"] = round(fl_rt / (kus["pf_logits"] * 1e-6) / 1e12, 1)
+    rname = "pf_router_gemm" if "pf_router_gemm" in kus else "pf_logits"
+    per_kernel[rname]["tflops"] = round(fl_rt / (kus[rname] * 1e-6) / 1e12, 1)
     return dict(
         metric="MoE-layer prefill tokens/s (grouped GEMM on MFMA), 4-bit weights",
         value=round(T / (ms * 1e-3), 1), unit="tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,

@@ -515,7 +515,7 @@ moe_status moe_layer_forward_prefill_timed(const moe_dims *d, const moe_layer_we
         }
         (void)hipGetLastError();
         *n_kernels = moe::PREFILL_SLOTS;
-        if (names && names_cap) snprintf(names, names_cap, "%s", moe::kPrefillNames);
+        if (names && names_cap) snprintf(names, names_cap, "%s", moe::prefill_names(act));
     }
     for (auto &e : ev) (void)hipEventDestroy(e);
     return s == MOE_OK ? ok() : s;

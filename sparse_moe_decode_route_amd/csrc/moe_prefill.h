@@ -28,9 +28,10 @@ struct PrefillArgs {
     hipEvent_t *ev;           // optional start/stop pairs per kernel slot (PREFILL_SLOTS)
 };
 
-// Kernel slots of the prefill path, in launch order (timing entry point).
+// Kernel slots of the prefill path, in launch order (timing entry point);
+// names of the slots' kernels for tokens of type act (MOE_ACT_*).
 constexpr int PREFILL_SLOTS = 7;
-extern const char *const kPrefillNames;
+const char *prefill_names(int act);
 
 size_t prefill_ws_bytes(int D, int F, int E, int S, int K, int T);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);

@@ -10,9 +10,12 @@
 // run on MFMA (fp16 operands, fp32 accumulation).
 //
 // Kernels (one stream, in order):
-//   pf_logits   logits = x Wr^T (+bias) by bf16 MFMA (split reduction),
-//               fp16 copy of x
-//   pf_topk     per-token top-k, per-expert 64-token bitmasks
+//   pf_router_gemm  (bf16 tokens) partial logits x Wr^T of ksplit reduction
+//               parts by a tiled bf16 MFMA GEMM, fp16 copy of x
+//   pf_logits   (fp32 tokens) logits = x Wr^T + bias by bf16 MFMA on a
+//               two-term bf16 split of x, fp16 copy of x
+//   pf_topk     logits (sum of the parts + bias), per-token top-k,
+//               per-expert 64-token bitmasks
 //   pf_scan     per-expert counts and word prefixes of the masks, row
 //               offsets, tile table
 //   pf_scatter  position of every (token, slot) pair in its expert's rows
@@ -45,20 +48,33 @@ struct PfTile {
 
 // Workspace layout (byte offsets), shared by the host sizing and the launcher.
 struct PfWs {
-    size_t x16, logits, idx, w, mask, wp, off, tiles, meta, perm_tok, perm_w, pos, h, o, total;
-    int NW, R, tiles_max;
+    size_t x16, logits, part, idx, w, mask, wp, off, tiles, meta, perm_tok, perm_w, pos, h, o, total;
+    int NW, R, tiles_max, ksplit;
 };
 
 size_t al(size_t v) { return (v + 255) & ~(size_t)255; }
+
+constexpr int RG_BT = 64;  // tokens per block of the bf16 router GEMM
+
+// Reduction parts of the bf16 router GEMM: the fewest (1, 2, 4 or 8: a
+// divisor of the 8 XCDs) that give 256 blocks, one 32-input step each at least.
+int pf_router_splits(int T, int D) {
+    const int ntt = (T + RG_BT - 1) / RG_BT, nk = D / 32;
+    int s = 1;
+    while (s < 8 && ntt * s < 256 && 2 * s <= nk) s *= 2;
+    return s;
+}
 
 PfWs pf_layout(int D, int F, int E, int S, int K, int T) {
     PfWs L{};
     L.NW = (T + 63) / 64;
     L.R = T * (K + S);
     L.tiles_max = (L.R + PF_BM - 1) / PF_BM + E + S;
+    L.ksplit = pf_router_splits(T, D);
     size_t o = 0;
     L.x16 = o; o = al(o + (size_t)T * D * 2);
     L.logits = o; o = al(o + (size_t)T * E * 4);
+    L.part = o; o = al(o + (size_t)L.ksplit * T * E * 4);
     L.idx = o; o = al(o + (size_t)T * K * 4);
     L.w = o; o = al(o + (size_t)T * K * 4);
     L.mask = o; o = al(o + (size_t)E * L.NW * 8);
@@ -83,6 +99,7 @@ T *wsp(void *ws, size_t off) {
 struct PfParams {
     int D, F, E, S, K, T, act, NW, R, tiles_max, want_x16;
     int rms_in;          // pf_logits: x is un-normalised, scale each token by 1/rms(x)
+    int ksplit;          // pf_router_gemm: reduction parts
     hipEvent_t *ev;
     size_t expert_bytes;
     const void *x;
@@ -95,6 +112,7 @@ struct PfParams {
     float *w_out;
     float *logits_out;
     float *logits;       // [T, E]: logits_out, or workspace
+    float *part;         // [ksplit, T, E]: partial logits of the bf16 router GEMM
     _Float16 *x16;
     int32_t *idx;
     float *w;
@@ -231,39 +249,79 @@ __global__ void __launch_bounds__(64 * KS) pf_logits(PfParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// pf_topk: one block = 64 tokens (one mask word); wave w takes tokens w,
-// w + 4, ...: top-k and renormalised weights, per-expert token bitmask.
+// pf_topk: one block = 16 tokens (a quarter of a 64-token mask word), each
+// wave PF_TOPK_TPW of them (tokens w, w + waves, ...).  Logits: NP = 0 reads finished ones
+// (bias included); NP > 0 sums the bf16 router GEMM's NP partials in part
+// order and adds the bias.  Then top-k with renormalised weights, and the
+// block's 16 bits of every expert's token bitmask (the grid covers whole
+// words, so tokens past T get zero bits).
 // ---------------------------------------------------------------------------
-constexpr int PF_TOPK_THREADS = 1024;  // 16 waves x 4 tokens
+constexpr int PF_TOPK_TOK = 16;
+constexpr int PF_TOPK_TPW = 1;                                 // tokens per wave
+constexpr int PF_TOPK_WAVES = PF_TOPK_TOK / PF_TOPK_TPW;
+constexpr int PF_TOPK_THREADS = 64 * PF_TOPK_WAVES;
 
+template <int NP>
 __global__ void __launch_bounds__(PF_TOPK_THREADS) pf_topk(PfParams p) {
-    __shared__ unsigned long long smask[256];
+    __shared__ uint32_t smask[256];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t0 = blockIdx.x * 64;
-    if (tid < 256) smask[tid] = 0ull;
-    // the wave's 4 tokens' logits, all loads in flight together
-    float lv[4][4];
+    const int t0 = blockIdx.x * PF_TOPK_TOK;
+    const int T = p.T, E = p.E;
+    for (int i = tid; i < 256; i += PF_TOPK_THREADS) smask[i] = 0u;
+    // the wave's tokens' logits, all loads in flight together
+    float lv[PF_TOPK_TPW][4];
+    if (NP == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) wave_topk_load(p.logits + (size_t)min(t0 + wave + 16 * i, p.T - 1) * p.E, p.E, lv[i]);
+        for (int i = 0; i < PF_TOPK_TPW; i++)
+            wave_topk_load(p.logits + (size_t)min(t0 + wave + PF_TOPK_WAVES * i, T - 1) * E, E, lv[i]);
+    } else {
+        float pv[PF_TOPK_TPW][NP][4];
+#pragma unroll
+        for (int i = 0; i < PF_TOPK_TPW; i++) {
+            const int t = min(t0 + wave + PF_TOPK_WAVES * i, T - 1);
+#pragma unroll
+            for (int j = 0; j < NP; j++)
+#pragma unroll
+                for (int k = 0; k < 4; k++) pv[i][j][k] = p.part[((size_t)j * T + t) * E + min(lane + 64 * k, E - 1)];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float bk = p.bias ? p.bias[min(lane + 64 * k, E - 1)] : 0.f;
+#pragma unroll
+            for (int i = 0; i < PF_TOPK_TPW; i++) {
+                float v = pv[i][0][k];
+#pragma unroll
+                for (int j = 1; j < NP; j++) v += pv[i][j][k];
+                lv[i][k] = v + bk;
+            }
+        }
+    }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int tl = wave + 16 * i, t = t0 + tl;
-        if (t >= p.T) break;
+    for (int i = 0; i < PF_TOPK_TPW; i++) {
+        const int tl = wave + PF_TOPK_WAVES * i, t = t0 + tl;
+        if (t >= T) break;
+        if (NP > 0 && p.logits_out) {
+#pragma unroll
+            for (int k = 0; k < 4; k++)
+                if (lane + 64 * k < E) p.logits_out[(size_t)t * E + lane + 64 * k] = lv[i][k];
+        }
         int e;
         float wi;
-        wave_topk_regs(lv[i], p.E, p.K, &e, &wi);
+        wave_topk_regs(lv[i], E, p.K, &e, &wi);
         if (lane < p.K) {
             p.idx[(size_t)t * p.K + lane] = e;
             p.w[(size_t)t * p.K + lane] = wi;
             if (p.idx_out) p.idx_out[(size_t)t * p.K + lane] = e;
             if (p.w_out) p.w_out[(size_t)t * p.K + lane] = wi;
-            atomicOr(&smask[e], 1ull << tl);
+            atomicOr(&smask[e], 1u << tl);
         }
     }
     __syncthreads();
-    if (tid < p.E) p.mask[(size_t)tid * p.NW + blockIdx.x] = smask[tid];
+    // 16-bit piece blockIdx.x % 4 of word blockIdx.x / 4 (little-endian words)
+    for (int e = tid; e < E; e += PF_TOPK_THREADS)
+        reinterpret_cast<uint16_t *>(p.mask)[(size_t)e * 4 * p.NW + blockIdx.x] = (uint16_t)smask[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -539,9 +597,12 @@ __device__ __forceinline__ void pf_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// slot of (row, 16-byte chunk) in a token stage: chunks XOR-swizzled by row
-// so the fragment reads of 8 consecutive rows hit distinct banks
-__device__ __forceinline__ int pf_slot(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
+// slot of (row, 16-byte chunk) in a stage of 64-byte rows: chunks XOR-
+// swizzled by (row >> 2) & 3, so that a 16-lane group of 16-byte fragment
+// reads (rows r .. r + 15, one chunk) covers all 64 banks (measured on
+// gfx950: as fast as a contiguous read; swizzling by (row >> 1) & 3 costs 1.8x)
+__device__ __forceinline__ int pf_swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int pf_slot(int r, int c) { return r * 4 + (c ^ pf_swz(r)); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -597,6 +658,76 @@ __device__ __forceinline__ void pf_issue(const PfDma<FMT> &d, uint4 *xs, uint8_t
                 d.wo[1], 2 * ks, 0, 0);
     }
 }
+// DMA of one 32-input step of pf_router_gemm: this thread's token chunk and
+// its 4 router chunks (offsets of step 0; the step goes in the scalar offset)
+struct RgDma {
+    __amdgpu_buffer_rsrc_t rx, rr;
+    uint32_t xo, ro[4];
+    int wave;
+};
+
+__device__ __forceinline__ void rg_issue(const RgDma &d, uint4 *xs, uint4 *rs, int k) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rx, (lds_void *)(xs + 64 * d.wave), 16, d.xo, 64 * k, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rr, (lds_void *)(rs + i * 256 + 64 * d.wave), 16, d.ro[i], 64 * k,
+                                                 0, 0);
+}
+// Epilogue of the grouped GEMMs.  acc[a][b][j] = out[row m][token n] of
+// the wave's row group a, m = 8 (j/4) + 4 g + j%4, n = 32 b + l32.
+//   MODE 0: h = silu(gate) * up (gate in a = 0, up in a = 1), fp16 rows of H
+//   MODE 1: O = coef * acc, fp32 rows of O
+template <int MODE>
+__device__ __forceinline__ void pf_epilogue(const PfParams &p, const PfTile &tile, const f32x16_t (&acc)[2][4], int r0,
+                                            const bool (&sub_ok)[2], int g, int l32) {
+    if (MODE == 0) {
+        if (!sub_ok[0]) return;
+        const float ts_g = p.tscale ? p.tscale[3 * tile.e + 0] : 1.f;
+        const float ts_u = p.tscale ? p.tscale[3 * tile.e + 1] : 1.f;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int n = 32 * b + l32;
+            if (n >= tile.rows) continue;
+            _Float16 *hrow = p.h + (size_t)(tile.row0 + n) * p.F + r0 + 4 * g;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                uint32_t pk[2];
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    const float g0 = acc[0][b][4 * q + 2 * i] * ts_g, u0 = acc[1][b][4 * q + 2 * i] * ts_u;
+                    const float g1 = acc[0][b][4 * q + 2 * i + 1] * ts_g, u1 = acc[1][b][4 * q + 2 * i + 1] * ts_u;
+                    const _Float16 h0 = (_Float16)silu_mul(g0, u0), h1 = (_Float16)silu_mul(g1, u1);
+                    pk[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                }
+                *reinterpret_cast<uint2 *>(hrow + 8 * q) = make_uint2(pk[0], pk[1]);
+            }
+        }
+    } else {
+        const float ts_d = p.tscale ? p.tscale[3 * tile.e + 2] : 1.f;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int n = 32 * b + l32;
+            if (n >= tile.rows) continue;
+            const float c = p.perm_w[tile.row0 + n] * ts_d;
+            float *orow = p.o + (size_t)(tile.row0 + n) * p.D;
+#pragma unroll
+            for (int a = 0; a < 2; a++) {
+                if (!sub_ok[a]) continue;
+                const int dr = r0 + 32 * a + 4 * g;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    float4 v;
+                    v.x = acc[a][b][4 * q + 0] * c;
+                    v.y = acc[a][b][4 * q + 1] * c;
+                    v.z = acc[a][b][4 * q + 2] * c;
+                    v.w = acc[a][b][4 * q + 3] * c;
+                    *reinterpret_cast<float4 *>(orow + dr + 8 * q) = v;
+                }
+            }
+        }
+    }
+}
+
 #endif  // __HIP_DEVICE_COMPILE__ (helpers of pf_gemm)
 
 // ---------------------------------------------------------------------------
@@ -651,7 +782,7 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm(PfParams p) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int r = 64 * i + 16 * wave + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 1) & 3);
+        const int c = (lane & 3) ^ pf_swz(r);
         const int rr = min(r, tile.rows - 1);
         const uint32_t row = MODE == 0 ? (uint32_t)p.perm_tok[tile.row0 + rr] * p.D : (uint32_t)rr * p.F;
         xo[i] = 2 * row + 16 * c;
@@ -727,58 +858,303 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm(PfParams p) {
         }
     }
 
-    // epilogue.  acc[a][b][j] = out[row m][token n], m = 8 (j/4) + 4 g + j%4, n = 32 b + l32
-    if (MODE == 0) {
-        if (!sub_ok[0]) return;
-        const float ts_g = p.tscale ? p.tscale[3 * tile.e + 0] : 1.f;
-        const float ts_u = p.tscale ? p.tscale[3 * tile.e + 1] : 1.f;
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const int n = 32 * b + l32;
-            if (n >= tile.rows) continue;
-            _Float16 *hrow = p.h + (size_t)(tile.row0 + n) * p.F + r0 + 4 * g;
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                uint32_t pk[2];
-#pragma unroll
-                for (int i = 0; i < 2; i++) {
-                    const float g0 = acc[0][b][4 * q + 2 * i] * ts_g, u0 = acc[1][b][4 * q + 2 * i] * ts_u;
-                    const float g1 = acc[0][b][4 * q + 2 * i + 1] * ts_g, u1 = acc[1][b][4 * q + 2 * i + 1] * ts_u;
-                    const _Float16 h0 = (_Float16)silu_mul(g0, u0), h1 = (_Float16)silu_mul(g1, u1);
-                    pk[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                }
-                *reinterpret_cast<uint2 *>(hrow + 8 * q) = make_uint2(pk[0], pk[1]);
-            }
-        }
-    } else {
-        const float ts_d = p.tscale ? p.tscale[3 * tile.e + 2] : 1.f;
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const int n = 32 * b + l32;
-            if (n >= tile.rows) continue;
-            const float c = p.perm_w[tile.row0 + n] * ts_d;
-            float *orow = p.o + (size_t)(tile.row0 + n) * p.D;
-#pragma unroll
-            for (int a = 0; a < 2; a++) {
-                if (!sub_ok[a]) continue;
-                const int dr = r0 + 32 * a + 4 * g;
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    float4 v;
-                    v.x = acc[a][b][4 * q + 0] * c;
-                    v.y = acc[a][b][4 * q + 1] * c;
-                    v.z = acc[a][b][4 * q + 2] * c;
-                    v.w = acc[a][b][4 * q + 3] * c;
-                    *reinterpret_cast<float4 *>(orow + dr + 8 * q) = v;
-                }
-            }
-        }
-    }
+    pf_epilogue<MODE>(p, tile, acc, r0, sub_ok, g, l32);
 
 #endif  // __HIP_DEVICE_COMPILE__
 }
 #undef PF_XST
 #undef PF_WST
+
+// ---------------------------------------------------------------------------
+// pf_gemm_q4<MODE>: pf_gemm for q4_1 weights, with the weight fragments of 4
+// consecutive 32-input steps copied at once (per row 64 B of codes and the
+// 16 B of 4 {d, m} pairs).  The address unit's cost of a wave-wide copy
+// grows with the cache lines it touches: 16 rows x 64 B costs well under
+// half of 64 rows x 16 B (measured on gfx950), and it dominated the
+// one-step weight copies.  Weight macro-stages are double-buffered and
+// copied one macro (4 steps) ahead; the token tile keeps pf_gemm's 4-stage
+// per-step ring, and the weights are dequantised from LDS the same way.
+// ---------------------------------------------------------------------------
+constexpr int PQ_MS = 4;  // steps per weight macro-stage
+
+// chunk swizzle of a row in the code macro-stage (64-byte rows)
+__device__ __forceinline__ int pq_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+template <int MODE>
+__global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm_q4(PfParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ uint4 x0s[PF_BM * 4], x1s[PF_BM * 4], x2s[PF_BM * 4], x3s[PF_BM * 4];
+    // codes: [256 rows][4 steps x 16 B], a row's step chunks XOR-swizzled by
+    // pq_swz(row) (the 8-byte fragment reads of 32 rows then spread over the
+    // banks with the least conflict measured); scales: [256 rows][4 steps x {d, m}]
+    __shared__ __attribute__((aligned(16))) uint8_t c0s[256 * 16 * PQ_MS], c1s[256 * 16 * PQ_MS];
+    __shared__ __attribute__((aligned(16))) uint8_t s0s[256 * 4 * PQ_MS], s1s[256 * 4 * PQ_MS];
+#define PQ_XST(st) ((st) == 0 ? x0s : (st) == 1 ? x1s : (st) == 2 ? x2s : x3s)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    const int MT = MODE == 0 ? (p.F + 127) / 128 : (p.D + 255) / 256;
+    const int n_tiles = p.meta[0];
+    const int n_blk = n_tiles * MT;
+    if ((int)blockIdx.x >= n_blk) return;
+    const int L = xcd_logical(blockIdx.x, n_blk);
+    const int ti = L / MT, mt = L % MT;
+    const PfTile tile = p.tiles[ti];
+    const int K = MODE == 0 ? p.D : p.F;
+    const int ROWS_A = MODE == 0 ? p.F : p.D;
+    const uint8_t *eb = p.experts + (size_t)tile.e * p.expert_bytes;
+    const uint32_t mb = (uint32_t)mat_bytes<FMT_Q4_1>(ROWS_A, K);  // bytes of one weight matrix
+    const int r0 = MODE == 0 ? mt * 128 + 32 * wave : mt * 256 + 64 * wave;
+    const int r1 = MODE == 0 ? r0 : r0 + 32;
+    const bool sub_ok[2] = {r0 < ROWS_A, r1 < ROWS_A};
+    const int lrow0 = MODE == 0 ? 32 * wave + l32 : 64 * wave + l32;
+    const int lrow1 = MODE == 0 ? 128 + 32 * wave + l32 : 64 * wave + 32 + l32;
+
+    // token DMA as in pf_gemm
+    PfDma<FMT_Q4_1> dx;
+    dx.wave = wave;
+    dx.rx = MODE == 0 ? buf_rsrc(p.x16, (uint32_t)((size_t)p.T * p.D * 2))
+                      : buf_rsrc(p.h + (size_t)tile.row0 * p.F, (uint32_t)tile.rows * p.F * 2);
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int r = 64 * i + 16 * wave + (lane >> 2);
+        const int c = (lane & 3) ^ pf_swz(r);
+        const int rr = min(r, tile.rows - 1);
+        const uint32_t row = MODE == 0 ? (uint32_t)p.perm_tok[tile.row0 + rr] * p.D : (uint32_t)rr * p.F;
+        dx.xo[i] = 2 * row + 16 * c;
+    }
+    // weight DMA over the block's matrices (gate then up, or down).  Stage
+    // row q: MODE 0 gate row mt*128 + q (q < 128) or up row mt*128 + q - 128,
+    // MODE 1 down row mt*256 + q.  Code slots i * 256 + tid hold row
+    // q = 64 i + tid / 4, step (tid & 3) ^ pq_swz(q) (= pq_swz(tid / 4)); scale
+    // slot tid holds row tid.
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(MODE == 0 ? eb : eb + 2 * (size_t)mb, MODE == 0 ? 2 * mb : mb);
+    auto wrow = [&](int q, uint32_t &mat) {
+        mat = (MODE == 0 && q >= 128) ? mb : 0u;
+        return (uint32_t)min(MODE == 0 ? mt * 128 + (q & 127) : mt * 256 + q, ROWS_A - 1);
+    };
+    uint32_t co[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        uint32_t mat;
+        const uint32_t ra = wrow(64 * i + (tid >> 2), mat);
+        co[i] = mat + ra * (uint32_t)(K / 2) + 16 * ((tid & 3) ^ pq_swz(tid >> 2));
+    }
+    uint32_t so;
+    {
+        uint32_t mat;
+        const uint32_t ra = wrow(tid, mat);
+        so = mat + (uint32_t)ROWS_A * (K / 2) + ra * (uint32_t)(K / 32) * 4;
+    }
+    const int NK = K / 32, NM = (NK + PQ_MS - 1) / PQ_MS;
+    uint32_t sc0[PQ_MS], sc1[PQ_MS];  // {d, m} of the current macro, rows lrow0 and lrow1
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int j = 0; j < 16; j++) acc[a][b][j] = 0.f;
+
+    // weight macro m into buffer b: 4 code copies and 1 scale copy per thread
+#define PQ_ISSUE_W(b, m)                                                                                           \
+    do {                                                                                                           \
+        uint8_t *cb_ = (b) == 0 ? c0s : c1s;                                                                       \
+        uint8_t *sb_ = (b) == 0 ? s0s : s1s;                                                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; i_++) __builtin_amdgcn_raw_ptr_buffer_load_lds(                 \
+            rw, (lds_void *)(cb_ + 16 * (i_ * 256 + 64 * wave)), 16, co[i_], 16 * PQ_MS * (m), 0, 0);              \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(sb_ + 16 * 64 * wave), 16, so, 4 * PQ_MS * (m), 0, \
+                                                 0);                                                               \
+    } while (0)
+#define PQ_ISSUE_X(st, ks)                                                                                         \
+    do {                                                                                                           \
+        _Pragma("unroll") for (int i_ = 0; i_ < 2; i_++) __builtin_amdgcn_raw_ptr_buffer_load_lds(                 \
+            dx.rx, (lds_void *)(PQ_XST(st) + i_ * 256 + 64 * wave), 16, dx.xo[i_], 64 * (ks), 0, 0);               \
+    } while (0)
+
+    PQ_ISSUE_W(0, 0);
+#pragma unroll
+    for (int s = 0; s < PF_NS - 1; s++) PQ_ISSUE_X(s, min(s, NK - 1));
+
+    static_assert(PF_UNROLL % (2 * PQ_MS) == 0 && PF_UNROLL % PF_NS == 0, "stage indices per trip");
+    for (int kb0 = 0; kb0 < NK; kb0 += PF_UNROLL) {
+#pragma unroll
+        for (int u = 0; u < PF_UNROLL; u++) {
+            const int kb = kb0 + u;
+            if (kb >= NK) break;
+            // token stage kb (and, issued before it, weight macro kb / 4) has
+            // landed once only the copies of the two later steps are
+            // pending: 2 token copies each, plus a weight macro (5) if one
+            // of those steps began a macro
+            if (u % PQ_MS == 1 || u % PQ_MS == 2)
+                wait_vmcnt<4 + 5>();
+            else
+                wait_vmcnt<4>();
+            pf_barrier();
+            if (u % PQ_MS == 0) PQ_ISSUE_W((u / PQ_MS + 1) % 2, min(kb / PQ_MS + 1, NM - 1));
+            PQ_ISSUE_X((u + PF_NS - 1) % PF_NS, min(kb + PF_NS - 1, NK - 1));
+            const uint8_t *cb = (u / PQ_MS) % 2 == 0 ? c0s : c1s;
+            const uint8_t *sb = (u / PQ_MS) % 2 == 0 ? s0s : s1s;
+            const int st = u % PQ_MS;
+            if (st == 0) {  // the macro's 4 {d, m} pairs of both rows, one 16-byte read each
+                const uint4 v0 = *reinterpret_cast<const uint4 *>(sb + lrow0 * 16);
+                const uint4 v1 = *reinterpret_cast<const uint4 *>(sb + lrow1 * 16);
+                sc0[0] = v0.x; sc0[1] = v0.y; sc0[2] = v0.z; sc0[3] = v0.w;
+                sc1[0] = v1.x; sc1[1] = v1.y; sc1[2] = v1.z; sc1[3] = v1.w;
+            }
+            WRaw<FMT_Q4_1> w0, w1;
+            w0.c = *reinterpret_cast<const uint2 *>(cb + lrow0 * 64 + 16 * (st ^ pq_swz(lrow0)) + 8 * g);
+            w0.dm = sc0[st];
+            w1.c = *reinterpret_cast<const uint2 *>(cb + lrow1 * 64 + 16 * (st ^ pq_swz(lrow1)) + 8 * g);
+            w1.dm = sc1[st];
+            half8_t af[2][2];
+            dequant_frag<FMT_Q4_1>(w0, af[0][0], af[0][1]);
+            dequant_frag<FMT_Q4_1>(w1, af[1][0], af[1][1]);
+            const _Float16 *stg = reinterpret_cast<const _Float16 *>(PQ_XST(u % PF_NS));
+#pragma unroll
+            for (int s = 0; s < 2; s++) {
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    const half8_t bf = *reinterpret_cast<const half8_t *>(stg + 8 * pf_slot(32 * b + l32, 2 * s + g));
+                    acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0][s], bf, acc[0][b], 0, 0, 0);
+                    acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[1][s], bf, acc[1][b], 0, 0, 0);
+                }
+            }
+        }
+    }
+#undef PQ_ISSUE_W
+#undef PQ_ISSUE_X
+    pf_epilogue<MODE>(p, tile, acc, r0, sub_ok, g, l32);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+#undef PQ_XST
+
+// ---------------------------------------------------------------------------
+// pf_router_gemm: router logits of bf16 tokens as a tiled GEMM on the matrix
+// cores.  One block = 64 tokens x all experts (<= 256) x one of ksplit parts
+// of the reduction; wave w owns experts 64w .. 64w + 63 (2 x 32) against the
+// 64 tokens (2 x 32).  The tokens and router rows of each 32-input step are
+// copied to a 4-stage LDS ring by buffer-to-LDS DMA three steps ahead, as in
+// pf_gemm.  bf16 x bf16 products are exact in the fp32 accumulator.  Output:
+// the part's partial logits (no bias; pf_topk sums the parts in order) and,
+// when the expert GEMMs follow, the fp16 copy of the block's slice of x.
+// The blocks of one part run on one XCD pair, whose L2 then holds only that
+// part of the router.  X16: write the fp16 copy of x.
+// ---------------------------------------------------------------------------
+constexpr int RG_NS = 4;       // LDS stages (at most 6)
+constexpr int RG_UNROLL = 16;  // steps per loop trip (multiple of RG_NS)
+static_assert(RG_NS <= 6 && RG_UNROLL % RG_NS == 0, "router GEMM pipeline shape");
+
+template <int X16>
+__global__ void __launch_bounds__(PF_THREADS) pf_router_gemm(PfParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // one LDS object per stage (unused ones are dropped)
+    __shared__ uint4 x0s[RG_BT * 4], x1s[RG_BT * 4], x2s[RG_BT * 4], x3s[RG_BT * 4], x4s[RG_BT * 4], x5s[RG_BT * 4];
+    __shared__ uint4 r0s[256 * 4], r1s[256 * 4], r2s[256 * 4], r3s[256 * 4], r4s[256 * 4], r5s[256 * 4];
+#define RG_XST(st) ((st) == 0 ? x0s : (st) == 1 ? x1s : (st) == 2 ? x2s : (st) == 3 ? x3s : (st) == 4 ? x4s : x5s)
+#define RG_RST(st) ((st) == 0 ? r0s : (st) == 1 ? r1s : (st) == 2 ? r2s : (st) == 3 ? r3s : (st) == 4 ? r4s : r5s)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    const int S = p.ksplit, T = p.T, D = p.D, E = p.E;
+    const int xcd = blockIdx.x % 8;
+    const int ks = xcd % S;
+    const int t0 = ((blockIdx.x / 8) * (8 / S) + xcd / S) * RG_BT;
+    if (t0 >= T) return;
+    const int NK = D / 32;
+    const int kb_lo = ks * NK / S, n = (ks + 1) * NK / S - kb_lo;
+
+    // stage slot j holds row j / 4, 16-byte chunk (j & 3) ^ pf_swz(row);
+    // this thread fills token slot tid and router slots i * 256 + tid, whose
+    // rows 64 i + tid / 4 share the swizzle of row tid / 4
+    const int xr = tid >> 2, xc = (tid & 3) ^ pf_swz(xr);
+    RgDma dma;
+    dma.wave = wave;
+    dma.rx = buf_rsrc(p.x, (uint32_t)((size_t)T * D * 2));
+    dma.rr = buf_rsrc(p.router, (uint32_t)E * D * 2);
+    dma.xo = (uint32_t)min(t0 + xr, T - 1) * D * 2 + 16 * xc + 64 * kb_lo;
+#pragma unroll
+    for (int i = 0; i < 4; i++) dma.ro[i] = (uint32_t)min(64 * i + xr, E - 1) * D * 2 + 16 * xc + 64 * kb_lo;
+    // rows past T hold row T - 1 (clamped DMA) and rewrite its identical values
+    _Float16 *x16p = p.x16 + (size_t)min(t0 + xr, T - 1) * D + 32 * kb_lo + 8 * xc;
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int j = 0; j < 16; j++) acc[a][b][j] = 0.f;
+
+#pragma unroll
+    for (int s = 0; s < RG_NS - 1; s++) rg_issue(dma, RG_XST(s), RG_RST(s), min(s, n - 1));
+
+    for (int kb0 = 0; kb0 < n; kb0 += RG_UNROLL) {
+        _Float16 *x16b = x16p + 32 * kb0;
+#pragma unroll
+        for (int u = 0; u < RG_UNROLL; u++) {
+            const int kb = kb0 + u;
+            if (kb >= n) break;
+            wait_vmcnt<(RG_NS - 2) * 5>();
+            pf_barrier();
+            rg_issue(dma, RG_XST((u + RG_NS - 1) % RG_NS), RG_RST((u + RG_NS - 1) % RG_NS), min(kb + RG_NS - 1, n - 1));
+            const uint4 *xs = RG_XST(u % RG_NS);
+            const uint4 *rs = RG_RST(u % RG_NS);
+            if (X16) {  // this thread's own token chunk of the step (packed by
+                        // hand: a half8 store here stops the unrolling)
+                const uint4 v = xs[tid];
+                const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+                uint32_t hh[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const half2_t h2 = {(_Float16)bf16lo(ww[j]), (_Float16)bf16hi(ww[j])};
+                    hh[j] = __builtin_bit_cast(uint32_t, h2);
+                }
+                *reinterpret_cast<uint4 *>(x16b + 32 * u) = make_uint4(hh[0], hh[1], hh[2], hh[3]);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; s++) {
+                const bf16x8_t a0 = as_bf16x8(rs[pf_slot(64 * wave + l32, 2 * s + g)]);
+                const bf16x8_t a1 = as_bf16x8(rs[pf_slot(64 * wave + 32 + l32, 2 * s + g)]);
+                const bf16x8_t b0 = as_bf16x8(xs[pf_slot(l32, 2 * s + g)]);
+                const bf16x8_t b1 = as_bf16x8(xs[pf_slot(32 + l32, 2 * s + g)]);
+                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+            }
+        }
+    }
+
+    // acc[a][b][j] = partial logit of expert 64 w + 32 a + 8 (j/4) + 4 g + j%4, token t0 + 32 b + l32
+    float *part = p.part + (size_t)ks * T * E;
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+        const int t = t0 + 32 * b + l32;
+        if (t >= T) continue;
+        float *prow = part + (size_t)t * E;
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int e = 64 * wave + 32 * a + 8 * q + 4 * g;
+                if ((E & 3) == 0) {
+                    if (e < E)
+                        *reinterpret_cast<float4 *>(prow + e) =
+                            make_float4(acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (e + i < E) prow[e + i] = acc[a][b][4 * q + i];
+                }
+            }
+        }
+    }
+#undef RG_XST
+#undef RG_RST
+#endif  // __HIP_DEVICE_COMPILE__
+}
 
 // ---------------------------------------------------------------------------
 // pf_combine: y[t, 4i..4i+3] = sum over t's slots (routed in top-k order,
@@ -806,13 +1182,21 @@ __global__ void __launch_bounds__(PF_THREADS) pf_combine(PfParams p) {
 template <int FMT>
 void launch_gemms(const PfParams &p, hipStream_t st) {
     const int mt0 = (p.F + 127) / 128, mt1 = (p.D + 255) / 256;
-    MOE_LAUNCH(4, (pf_gemm<FMT, 0>), dim3(p.tiles_max * mt0), dim3(PF_THREADS), st, p);
-    MOE_LAUNCH(5, (pf_gemm<FMT, 1>), dim3(p.tiles_max * mt1), dim3(PF_THREADS), st, p);
+    if constexpr (FMT == FMT_Q4_1) {
+        MOE_LAUNCH(4, pf_gemm_q4<0>, dim3(p.tiles_max * mt0), dim3(PF_THREADS), st, p);
+        MOE_LAUNCH(5, pf_gemm_q4<1>, dim3(p.tiles_max * mt1), dim3(PF_THREADS), st, p);
+    } else {
+        MOE_LAUNCH(4, (pf_gemm<FMT, 0>), dim3(p.tiles_max * mt0), dim3(PF_THREADS), st, p);
+        MOE_LAUNCH(5, (pf_gemm<FMT, 1>), dim3(p.tiles_max * mt1), dim3(PF_THREADS), st, p);
+    }
 }
 
 }  // namespace
 
-const char *const kPrefillNames = "pf_logits;pf_topk;pf_scan;pf_scatter;pf_gemm_gateup;pf_gemm_down;pf_combine";
+const char *prefill_names(int act) {
+    return act == MOE_ACT_F32 ? "pf_logits;pf_topk;pf_scan;pf_scatter;pf_gemm_gateup;pf_gemm_down;pf_combine"
+                              : "pf_router_gemm;pf_topk;pf_scan;pf_scatter;pf_gemm_gateup;pf_gemm_down;pf_combine";
+}
 
 size_t prefill_ws_bytes(int D, int F, int E, int S, int K, int T) { return pf_layout(D, F, E, S, K, T).total; }
 
@@ -842,6 +1226,8 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     p.x = a.x; p.router = a.router; p.bias = a.bias; p.experts = a.experts; p.tscale = a.tscale;
     p.y = a.y; p.idx_out = a.idx_out; p.w_out = a.w_out; p.logits_out = a.logits_out;
     p.logits = a.logits_out ? a.logits_out : wsp<float>(a.ws, L.logits);
+    p.part = wsp<float>(a.ws, L.part);
+    p.ksplit = L.ksplit;
     p.x16 = wsp<_Float16>(a.ws, L.x16);
     p.idx = wsp<int32_t>(a.ws, L.idx);
     p.w = wsp<float>(a.ws, L.w);
@@ -857,12 +1243,25 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     p.o = wsp<float>(a.ws, L.o);
     const int nb64 = (a.T + 63) / 64;
     if (!a.given_idx) {
-        const dim3 gl((a.T + 31) / 32, (a.E + 31) / 32);
-        if (a.act == MOE_ACT_F32)
-            MOE_LAUNCH(0, (pf_logits<0, 4>), gl, dim3(PF_THREADS), st, p);
-        else
-            MOE_LAUNCH(0, (pf_logits<1, 4>), gl, dim3(PF_THREADS), st, p);
-        MOE_LAUNCH(1, pf_topk, dim3(nb64), dim3(PF_TOPK_THREADS), st, p);
+        const dim3 gk(4 * L.NW);  // pf_topk: 16-token blocks over whole mask words
+        if (a.act == MOE_ACT_F32) {
+            // fp32 tokens: the two-term bf16 split needs the pf_logits kernel
+            MOE_LAUNCH(0, (pf_logits<0, 4>), dim3((a.T + 31) / 32, (a.E + 31) / 32), dim3(PF_THREADS), st, p);
+            MOE_LAUNCH(1, pf_topk<0>, gk, dim3(PF_TOPK_THREADS), st, p);
+        } else {
+            const int ntt = (a.T + RG_BT - 1) / RG_BT;
+            const dim3 gr((unsigned)((ntt * p.ksplit + 7) / 8 * 8));
+            if (p.want_x16)
+                MOE_LAUNCH(0, pf_router_gemm<1>, gr, dim3(PF_THREADS), st, p);
+            else
+                MOE_LAUNCH(0, pf_router_gemm<0>, gr, dim3(PF_THREADS), st, p);
+            switch (p.ksplit) {
+            case 1: MOE_LAUNCH(1, pf_topk<1>, gk, dim3(PF_TOPK_THREADS), st, p); break;
+            case 2: MOE_LAUNCH(1, pf_topk<2>, gk, dim3(PF_TOPK_THREADS), st, p); break;
+            case 4: MOE_LAUNCH(1, pf_topk<4>, gk, dim3(PF_TOPK_THREADS), st, p); break;
+            default: MOE_LAUNCH(1, pf_topk<8>, gk, dim3(PF_TOPK_THREADS), st, p); break;
+            }
+        }
         if (a.route_only) return hipGetLastError();
     } else {
         p.idx = const_cast<int32_t *>(a.given_idx);
