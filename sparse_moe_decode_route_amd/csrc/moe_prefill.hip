@@ -20,7 +20,7 @@
 //               offsets, tile table
 //   pf_scatter  position of every (token, slot) pair in its expert's rows
 //   pf_gemm<0>  H = silu(X Wg^T) * (X Wu^T) per expert (fp16 H)
-//   pf_gemm<1>  O = coef * (H Wd^T) per expert (fp32 O)
+//   pf_gemm<1>  O = coef * (H Wd^T) per expert (fp16 O, like H)
 //   pf_combine  y[t] = sum of t's rows of O in slot order
 // No floating-point atomics: integer/bitwise atomics only, so results do not
 // depend on scheduling.
@@ -86,7 +86,7 @@ PfWs pf_layout(int D, int F, int E, int S, int K, int T) {
     L.perm_w = o; o = al(o + (size_t)L.R * 4);
     L.pos = o; o = al(o + (size_t)T * (K + S) * 4);
     L.h = o; o = al(o + (size_t)L.R * F * 2);
-    L.o = o; o = al(o + (size_t)L.R * D * 4);
+    L.o = o; o = al(o + (size_t)L.R * D * 2);
     L.total = o;
     return L;
 }
@@ -125,7 +125,7 @@ struct PfParams {
     float *perm_w;
     int32_t *pos;
     _Float16 *h;
-    float *o;
+    _Float16 *o;         // [R, D] down-projection rows (coefficient applied), fp16
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -372,7 +372,8 @@ __global__ void __launch_bounds__(PF_THREADS) pf_mask_given(PfParams p) {
 // ---------------------------------------------------------------------------
 // pf_scan: one block of 1024.  Rows are ordered routed expert 0..E-1, then
 // shared.  Per routed expert (one wave each): prefix popcounts of its mask
-// words; then block-wide exclusive scans of the row counts and tile counts.
+// words; then block-wide exclusive scans of the row counts and tile counts
+// (the tile table lists every full 128-row tile, then the partial ones).
 // ---------------------------------------------------------------------------
 constexpr int PF_SCAN_THREADS = 1024;
 
@@ -414,22 +415,33 @@ __global__ void __launch_bounds__(PF_SCAN_THREADS) pf_scan(PfParams p) {
     }
     __syncthreads();
     const int my_n = tid < p.E ? cnt[tid] : (tid < n_exp ? p.T : 0);
-    const int my_tiles = (my_n + PF_BM - 1) / PF_BM;
+    // full tiles of every expert first, then the partial ones (expert order)
+    const int my_full = my_n / PF_BM, my_part = my_n % PF_BM ? 1 : 0;
     const int off = block_excl_scan(my_n, tmp16, &tot_rows);
-    const int toff = block_excl_scan(my_tiles, tmp16, &tot_tiles);
+    const int foff = block_excl_scan(my_full, tmp16, &tot_tiles);
+    const int n_full = tot_tiles;
+    __syncthreads();
+    const int poff = block_excl_scan(my_part, tmp16, &tot_tiles);
     if (tid < n_exp) p.off[tid] = off;
     if (tid == 0) {
         p.off[n_exp] = tot_rows;
-        p.meta[0] = tot_tiles;
+        p.meta[0] = n_full + tot_tiles;
         p.meta[1] = tot_rows;
     }
     if (tid < n_exp) {
-        for (int i = 0; i < my_tiles; i++) {
+        for (int i = 0; i < my_full; i++) {
             PfTile t;
             t.e = tid;
             t.row0 = off + i * PF_BM;
-            t.rows = min(PF_BM, my_n - i * PF_BM);
-            p.tiles[toff + i] = t;
+            t.rows = PF_BM;
+            p.tiles[foff + i] = t;
+        }
+        if (my_part) {
+            PfTile t;
+            t.e = tid;
+            t.row0 = off + my_full * PF_BM;
+            t.rows = my_n - my_full * PF_BM;
+            p.tiles[n_full + poff] = t;
         }
     }
 }
@@ -545,12 +557,16 @@ __device__ __forceinline__ void dequant_frag(const WRaw<FMT> &w, half8_t &s0, ha
     }
 }
 
-// Tile decode with an XCD-aware order: blocks go round-robin to the 8 XCDs,
-// so consecutive logical tiles (same expert's weights, same token rows) are
-// given to blocks on one XCD and share its L2.
-__device__ __forceinline__ int xcd_logical(int b, int n) {
-    const int q = n / 8, r = n % 8, x = b % 8;
-    return x * q + min(x, r) + b / 8;
+// Block -> (tile, weight-row block) with an XCD-aware order.  Blocks go
+// round-robin to the 8 XCDs (block b to XCD b % 8); XCD x takes tiles x,
+// x + 8, x + 16, ... in table order, the MT blocks of a tile back to back, so
+// they share the tile's token rows in that XCD's L2, every XCD gets the same
+// share of full and partial tiles, and the table's partial tiles (last) fill
+// each XCD's tail.  Returns ti * MT + mt, or -1 past the last tile.
+__device__ __forceinline__ int xcd_tile_block(int b, int MT, int n_tiles) {
+    const int x = b & 7, j = b >> 3;
+    const int ti = x + 8 * (j / MT);
+    return ti < n_tiles ? ti * MT + j % MT : -1;
 }
 
 // LDS bytes between consecutive lanes of a 2-byte buffer-to-LDS copy: each
@@ -676,7 +692,7 @@ __device__ __forceinline__ void rg_issue(const RgDma &d, uint4 *xs, uint4 *rs, i
 // Epilogue of the grouped GEMMs.  acc[a][b][j] = out[row m][token n] of
 // the wave's row group a, m = 8 (j/4) + 4 g + j%4, n = 32 b + l32.
 //   MODE 0: h = silu(gate) * up (gate in a = 0, up in a = 1), fp16 rows of H
-//   MODE 1: O = coef * acc, fp32 rows of O
+//   MODE 1: O = coef * acc, fp16 rows of O
 template <int MODE>
 __device__ __forceinline__ void pf_epilogue(const PfParams &p, const PfTile &tile, const f32x16_t (&acc)[2][4], int r0,
                                             const bool (&sub_ok)[2], int g, int l32) {
@@ -709,19 +725,17 @@ __device__ __forceinline__ void pf_epilogue(const PfParams &p, const PfTile &til
             const int n = 32 * b + l32;
             if (n >= tile.rows) continue;
             const float c = p.perm_w[tile.row0 + n] * ts_d;
-            float *orow = p.o + (size_t)(tile.row0 + n) * p.D;
+            _Float16 *orow = p.o + (size_t)(tile.row0 + n) * p.D;
 #pragma unroll
             for (int a = 0; a < 2; a++) {
                 if (!sub_ok[a]) continue;
                 const int dr = r0 + 32 * a + 4 * g;
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    float4 v;
-                    v.x = acc[a][b][4 * q + 0] * c;
-                    v.y = acc[a][b][4 * q + 1] * c;
-                    v.z = acc[a][b][4 * q + 2] * c;
-                    v.w = acc[a][b][4 * q + 3] * c;
-                    *reinterpret_cast<float4 *>(orow + dr + 8 * q) = v;
+                    const half2_t v01 = {(_Float16)(acc[a][b][4 * q + 0] * c), (_Float16)(acc[a][b][4 * q + 1] * c)};
+                    const half2_t v23 = {(_Float16)(acc[a][b][4 * q + 2] * c), (_Float16)(acc[a][b][4 * q + 3] * c)};
+                    *reinterpret_cast<uint2 *>(orow + dr + 8 * q) =
+                        make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
                 }
             }
         }
@@ -754,10 +768,8 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm(PfParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int MT = MODE == 0 ? (p.F + 127) / 128 : (p.D + 255) / 256;
-    const int n_tiles = p.meta[0];
-    const int n_blk = n_tiles * MT;
-    if ((int)blockIdx.x >= n_blk) return;
-    const int L = xcd_logical(blockIdx.x, n_blk);
+    const int L = xcd_tile_block(blockIdx.x, MT, p.meta[0]);
+    if (L < 0) return;
     const int ti = L / MT, mt = L % MT;
     const PfTile tile = p.tiles[ti];
     const int K = MODE == 0 ? p.D : p.F;           // reduction length
@@ -865,6 +877,24 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm(PfParams p) {
 #undef PF_XST
 #undef PF_WST
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// MFMAs of one 32-input step against the first NB 32-row token blocks of a
+// token stage (the tile's other blocks hold only padding rows)
+template <int NB>
+__device__ __forceinline__ void pf_mfma_tokens(const _Float16 *stg, const half8_t (&af)[2][2], f32x16_t (&acc)[2][4],
+                                               int l32, int g) {
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const half8_t bf = *reinterpret_cast<const half8_t *>(stg + 8 * pf_slot(32 * b + l32, 2 * s + g));
+            acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0][s], bf, acc[0][b], 0, 0, 0);
+            acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[1][s], bf, acc[1][b], 0, 0, 0);
+        }
+    }
+}
+#endif
+
 // ---------------------------------------------------------------------------
 // pf_gemm_q4<MODE>: pf_gemm for q4_1 weights, with the weight fragments of 4
 // consecutive 32-input steps copied at once (per row 64 B of codes and the
@@ -875,7 +905,10 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm(PfParams p) {
 // copied one macro (4 steps) ahead; the token tile keeps pf_gemm's 4-stage
 // per-step ring, and the weights are dequantised from LDS the same way.
 // ---------------------------------------------------------------------------
-constexpr int PQ_MS = 4;  // steps per weight macro-stage
+constexpr int PQ_MS = 4;                                        // steps per weight macro-stage
+constexpr int PQ_SOFF = 256 * 16 * PQ_MS;                       // scales inside a macro buffer
+constexpr int PQ_WBYTES = PQ_SOFF + 256 * 4 * PQ_MS;
+constexpr int PQ_UNROLL = 16;                                   // steps per loop trip
 
 // chunk swizzle of a row in the code macro-stage (64-byte rows)
 __device__ __forceinline__ int pq_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
@@ -887,23 +920,23 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm_q4(PfParams p) {
     // codes: [256 rows][4 steps x 16 B], a row's step chunks XOR-swizzled by
     // pq_swz(row) (the 8-byte fragment reads of 32 rows then spread over the
     // banks with the least conflict measured); scales: [256 rows][4 steps x {d, m}]
-    __shared__ __attribute__((aligned(16))) uint8_t c0s[256 * 16 * PQ_MS], c1s[256 * 16 * PQ_MS];
-    __shared__ __attribute__((aligned(16))) uint8_t s0s[256 * 4 * PQ_MS], s1s[256 * 4 * PQ_MS];
+    // (one LDS object per macro buffer: codes, then scales at PQ_SOFF)
+    __shared__ __attribute__((aligned(16))) uint8_t c0s[PQ_WBYTES], c1s[PQ_WBYTES];
 #define PQ_XST(st) ((st) == 0 ? x0s : (st) == 1 ? x1s : (st) == 2 ? x2s : x3s)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int MT = MODE == 0 ? (p.F + 127) / 128 : (p.D + 255) / 256;
-    const int n_tiles = p.meta[0];
-    const int n_blk = n_tiles * MT;
-    if ((int)blockIdx.x >= n_blk) return;
-    const int L = xcd_logical(blockIdx.x, n_blk);
+    const int L = xcd_tile_block(blockIdx.x, MT, p.meta[0]);
+    if (L < 0) return;
     const int ti = L / MT, mt = L % MT;
     const PfTile tile = p.tiles[ti];
     const int K = MODE == 0 ? p.D : p.F;
     const int ROWS_A = MODE == 0 ? p.F : p.D;
     const uint8_t *eb = p.experts + (size_t)tile.e * p.expert_bytes;
     const uint32_t mb = (uint32_t)mat_bytes<FMT_Q4_1>(ROWS_A, K);  // bytes of one weight matrix
+    // 32-row token blocks holding rows of the tile (the rest is padding)
+    const int nb = __builtin_amdgcn_readfirstlane((tile.rows + 31) >> 5);
     const int r0 = MODE == 0 ? mt * 128 + 32 * wave : mt * 256 + 64 * wave;
     const int r1 = MODE == 0 ? r0 : r0 + 32;
     const bool sub_ok[2] = {r0 < ROWS_A, r1 < ROWS_A};
@@ -957,74 +990,99 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm_q4(PfParams p) {
 #pragma unroll
             for (int j = 0; j < 16; j++) acc[a][b][j] = 0.f;
 
-    // weight macro m into buffer b: 4 code copies and 1 scale copy per thread
-#define PQ_ISSUE_W(b, m)                                                                                           \
+    // weight macro m into buffer b, in two parts: W1 = the scale copy and
+    // code copies 0, 1 (issued at the macro's first step), W2 = code copies
+    // 2, 3 (at its second step), so no step queues all five
+#define PQ_ISSUE_W1(b, m)                                                                                          \
     do {                                                                                                           \
         uint8_t *cb_ = (b) == 0 ? c0s : c1s;                                                                       \
-        uint8_t *sb_ = (b) == 0 ? s0s : s1s;                                                                       \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; i_++) __builtin_amdgcn_raw_ptr_buffer_load_lds(                 \
-            rw, (lds_void *)(cb_ + 16 * (i_ * 256 + 64 * wave)), 16, co[i_], 16 * PQ_MS * (m), 0, 0);              \
+        uint8_t *sb_ = ((b) == 0 ? c0s : c1s) + PQ_SOFF;                                                           \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(sb_ + 16 * 64 * wave), 16, so, 4 * PQ_MS * (m), 0, \
                                                  0);                                                               \
+        _Pragma("unroll") for (int i_ = 0; i_ < 2; i_++) __builtin_amdgcn_raw_ptr_buffer_load_lds(                 \
+            rw, (lds_void *)(cb_ + 16 * (i_ * 256 + 64 * wave)), 16, co[i_], 16 * PQ_MS * (m), 0, 0);              \
+    } while (0)
+#define PQ_ISSUE_W2(b, m)                                                                                          \
+    do {                                                                                                           \
+        uint8_t *cb_ = (b) == 0 ? c0s : c1s;                                                                       \
+        _Pragma("unroll") for (int i_ = 2; i_ < 4; i_++) __builtin_amdgcn_raw_ptr_buffer_load_lds(                 \
+            rw, (lds_void *)(cb_ + 16 * (i_ * 256 + 64 * wave)), 16, co[i_], 16 * PQ_MS * (m), 0, 0);              \
     } while (0)
 #define PQ_ISSUE_X(st, ks)                                                                                         \
     do {                                                                                                           \
         _Pragma("unroll") for (int i_ = 0; i_ < 2; i_++) __builtin_amdgcn_raw_ptr_buffer_load_lds(                 \
             dx.rx, (lds_void *)(PQ_XST(st) + i_ * 256 + 64 * wave), 16, dx.xo[i_], 64 * (ks), 0, 0);               \
     } while (0)
+#define PQ_READ_SC(b)                                                                                              \
+    do {                                                                                                           \
+        const uint8_t *sb_ = ((b) == 0 ? c0s : c1s) + PQ_SOFF;                                                     \
+        const uint4 v0_ = *reinterpret_cast<const uint4 *>(sb_ + lrow0 * 16);                                      \
+        const uint4 v1_ = *reinterpret_cast<const uint4 *>(sb_ + lrow1 * 16);                                      \
+        sc0[0] = v0_.x; sc0[1] = v0_.y; sc0[2] = v0_.z; sc0[3] = v0_.w;                                            \
+        sc1[0] = v1_.x; sc1[1] = v1_.y; sc1[2] = v1_.z; sc1[3] = v1_.w;                                            \
+    } while (0)
 
-    PQ_ISSUE_W(0, 0);
+    PQ_ISSUE_W1(0, 0);
+    PQ_ISSUE_W2(0, 0);
 #pragma unroll
     for (int s = 0; s < PF_NS - 1; s++) PQ_ISSUE_X(s, min(s, NK - 1));
+    // macro 0 has landed once only the 3 token stages are pending
+    wait_vmcnt<2 * (PF_NS - 1)>();
+    pf_barrier();
+    PQ_READ_SC(0);
 
-    static_assert(PF_UNROLL % (2 * PQ_MS) == 0 && PF_UNROLL % PF_NS == 0, "stage indices per trip");
-    for (int kb0 = 0; kb0 < NK; kb0 += PF_UNROLL) {
-#pragma unroll
-        for (int u = 0; u < PF_UNROLL; u++) {
-            const int kb = kb0 + u;
-            if (kb >= NK) break;
-            // token stage kb (and, issued before it, weight macro kb / 4) has
-            // landed once only the copies of the two later steps are
-            // pending: 2 token copies each, plus a weight macro (5) if one
-            // of those steps began a macro
-            if (u % PQ_MS == 1 || u % PQ_MS == 2)
-                wait_vmcnt<4 + 5>();
-            else
-                wait_vmcnt<4>();
-            pf_barrier();
-            if (u % PQ_MS == 0) PQ_ISSUE_W((u / PQ_MS + 1) % 2, min(kb / PQ_MS + 1, NM - 1));
-            PQ_ISSUE_X((u + PF_NS - 1) % PF_NS, min(kb + PF_NS - 1, NK - 1));
-            const uint8_t *cb = (u / PQ_MS) % 2 == 0 ? c0s : c1s;
-            const uint8_t *sb = (u / PQ_MS) % 2 == 0 ? s0s : s1s;
-            const int st = u % PQ_MS;
-            if (st == 0) {  // the macro's 4 {d, m} pairs of both rows, one 16-byte read each
-                const uint4 v0 = *reinterpret_cast<const uint4 *>(sb + lrow0 * 16);
-                const uint4 v1 = *reinterpret_cast<const uint4 *>(sb + lrow1 * 16);
-                sc0[0] = v0.x; sc0[1] = v0.y; sc0[2] = v0.z; sc0[3] = v0.w;
-                sc1[0] = v1.x; sc1[1] = v1.y; sc1[2] = v1.z; sc1[3] = v1.w;
-            }
-            WRaw<FMT_Q4_1> w0, w1;
-            w0.c = *reinterpret_cast<const uint2 *>(cb + lrow0 * 64 + 16 * (st ^ pq_swz(lrow0)) + 8 * g);
-            w0.dm = sc0[st];
-            w1.c = *reinterpret_cast<const uint2 *>(cb + lrow1 * 64 + 16 * (st ^ pq_swz(lrow1)) + 8 * g);
-            w1.dm = sc1[st];
-            half8_t af[2][2];
-            dequant_frag<FMT_Q4_1>(w0, af[0][0], af[0][1]);
-            dequant_frag<FMT_Q4_1>(w1, af[1][0], af[1][1]);
-            const _Float16 *stg = reinterpret_cast<const _Float16 *>(PQ_XST(u % PF_NS));
-#pragma unroll
-            for (int s = 0; s < 2; s++) {
-#pragma unroll
-                for (int b = 0; b < 4; b++) {
-                    const half8_t bf = *reinterpret_cast<const half8_t *>(stg + 8 * pf_slot(32 * b + l32, 2 * s + g));
-                    acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0][s], bf, acc[0][b], 0, 0, 0);
-                    acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[1][s], bf, acc[1][b], 0, 0, 0);
-                }
-            }
-        }
+    static_assert(PQ_UNROLL % (2 * PQ_MS) == 0 && PQ_UNROLL % PF_NS == 0 && PQ_MS == 4, "stage indices per trip");
+    // The main loop, instantiated for tiles with rows in all four 32-row
+    // token blocks and for tiles of at most 32 rows (the partial tiles of
+    // most experts): the token-block count fixes the MFMAs of a step.
+    // Step kb waits until token stage kb (and, issued before it, weight
+    // macro kb / 4) has landed: only the copies of the two later steps may
+    // be pending, 2 token copies each, plus W1 (3) after a macro's first
+    // step and W2 (2) after its second.  The next macro's scales are read
+    // at a macro's last step (its W1 copy precedes that step's token stage).
+#define PQ_MAIN_LOOP(NB_)                                                                                              \
+    for (int kb0 = 0; kb0 < NK; kb0 += PQ_UNROLL) {                                                                    \
+_Pragma("unroll")                                                                                                      \
+        for (int u = 0; u < PQ_UNROLL; u++) {                                                                          \
+            const int kb = kb0 + u;                                                                                    \
+            if (kb >= NK) break;                                                                                       \
+            const int st = u % PQ_MS;                                                                                  \
+            if (st == 0)                                                                                               \
+                wait_vmcnt<4>();                                                                                       \
+            else if (st == 1)                                                                                          \
+                wait_vmcnt<4 + 3>();                                                                                   \
+            else if (st == 2)                                                                                          \
+                wait_vmcnt<4 + 3 + 2>();                                                                               \
+            else                                                                                                       \
+                wait_vmcnt<4 + 2>();                                                                                   \
+            pf_barrier();                                                                                              \
+            if (st == 0) PQ_ISSUE_W1((u / PQ_MS + 1) % 2, min(kb / PQ_MS + 1, NM - 1));                                \
+            if (st == 1) PQ_ISSUE_W2((u / PQ_MS + 1) % 2, min(kb / PQ_MS + 1, NM - 1));                                \
+            PQ_ISSUE_X((u + PF_NS - 1) % PF_NS, min(kb + PF_NS - 1, NK - 1));                                          \
+            const uint8_t *cb = (u / PQ_MS) % 2 == 0 ? c0s : c1s;                                                      \
+            WRaw<FMT_Q4_1> w0, w1;                                                                                     \
+            w0.c = *reinterpret_cast<const uint2 *>(cb + lrow0 * 64 + 16 * (st ^ pq_swz(lrow0)) + 8 * g);              \
+            w0.dm = sc0[st];                                                                                           \
+            w1.c = *reinterpret_cast<const uint2 *>(cb + lrow1 * 64 + 16 * (st ^ pq_swz(lrow1)) + 8 * g);              \
+            w1.dm = sc1[st];                                                                                           \
+            half8_t af[2][2];                                                                                          \
+            dequant_frag<FMT_Q4_1>(w0, af[0][0], af[0][1]);                                                            \
+            dequant_frag<FMT_Q4_1>(w1, af[1][0], af[1][1]);                                                            \
+            if (st == PQ_MS - 1) PQ_READ_SC((u / PQ_MS + 1) % 2);                                                      \
+            const _Float16 *stg = reinterpret_cast<const _Float16 *>(PQ_XST(u % PF_NS));                               \
+            pf_mfma_tokens<NB_>(stg, af, acc, l32, g);                                                                 \
+        }                                                                                                              \
     }
-#undef PQ_ISSUE_W
+    if (nb == 1) {
+        PQ_MAIN_LOOP(1);
+    } else {
+        PQ_MAIN_LOOP(4);
+    }
+#undef PQ_MAIN_LOOP
+#undef PQ_ISSUE_W1
+#undef PQ_ISSUE_W2
 #undef PQ_ISSUE_X
+#undef PQ_READ_SC
     pf_epilogue<MODE>(p, tile, acc, r0, sub_ok, g, l32);
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -1157,37 +1215,47 @@ __global__ void __launch_bounds__(PF_THREADS) pf_router_gemm(PfParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// pf_combine: y[t, 4i..4i+3] = sum over t's slots (routed in top-k order,
-// then shared) of O[pos] (already scaled by the slot's weight).
+// pf_combine: y[t, 8i..8i+7] = sum over t's slots (routed in top-k order,
+// then shared) of O[pos] (fp16, already scaled by the slot's weight),
+// accumulated in fp32.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(PF_THREADS) pf_combine(PfParams p) {
     const size_t i = (size_t)blockIdx.x * PF_THREADS + threadIdx.x;
-    const int D4 = p.D / 4;
-    if (i >= (size_t)p.T * D4) return;
-    const int t = (int)(i / D4), c = (int)(i % D4);
+    const int D8 = p.D / 8;
+    if (i >= (size_t)p.T * D8) return;
+    const int t = (int)(i / D8), c = (int)(i % D8);
     const int KS = p.K + p.S;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < KS; j++) {
         const int r = p.pos[(size_t)t * KS + j];
         if (r < 0) continue;
-        const float4 v = reinterpret_cast<const float4 *>(p.o + (size_t)r * p.D)[c];
-        s.x += v.x;
-        s.y += v.y;
-        s.z += v.z;
-        s.w += v.w;
+        const uint4 v = reinterpret_cast<const uint4 *>(p.o + (size_t)r * p.D)[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const half2_t h2 = __builtin_bit_cast(half2_t, w[k]);
+            s[2 * k] += (float)h2[0];
+            s[2 * k + 1] += (float)h2[1];
+        }
     }
-    reinterpret_cast<float4 *>(p.y)[i] = s;
+    float4 *yo = reinterpret_cast<float4 *>(p.y) + 2 * i;
+    yo[0] = make_float4(s[0], s[1], s[2], s[3]);
+    yo[1] = make_float4(s[4], s[5], s[6], s[7]);
 }
+
+// grid of the grouped GEMMs for at most tiles_max tiles of MT blocks (the
+// block -> tile order of xcd_tile_block)
+unsigned pf_gemm_grid(int tiles_max, int MT) { return (unsigned)(8 * MT * ((tiles_max + 7) / 8)); }
 
 template <int FMT>
 void launch_gemms(const PfParams &p, hipStream_t st) {
     const int mt0 = (p.F + 127) / 128, mt1 = (p.D + 255) / 256;
     if constexpr (FMT == FMT_Q4_1) {
-        MOE_LAUNCH(4, pf_gemm_q4<0>, dim3(p.tiles_max * mt0), dim3(PF_THREADS), st, p);
-        MOE_LAUNCH(5, pf_gemm_q4<1>, dim3(p.tiles_max * mt1), dim3(PF_THREADS), st, p);
+        MOE_LAUNCH(4, pf_gemm_q4<0>, dim3(pf_gemm_grid(p.tiles_max, mt0)), dim3(PF_THREADS), st, p);
+        MOE_LAUNCH(5, pf_gemm_q4<1>, dim3(pf_gemm_grid(p.tiles_max, mt1)), dim3(PF_THREADS), st, p);
     } else {
-        MOE_LAUNCH(4, (pf_gemm<FMT, 0>), dim3(p.tiles_max * mt0), dim3(PF_THREADS), st, p);
-        MOE_LAUNCH(5, (pf_gemm<FMT, 1>), dim3(p.tiles_max * mt1), dim3(PF_THREADS), st, p);
+        MOE_LAUNCH(4, (pf_gemm<FMT, 0>), dim3(pf_gemm_grid(p.tiles_max, mt0)), dim3(PF_THREADS), st, p);
+        MOE_LAUNCH(5, (pf_gemm<FMT, 1>), dim3(pf_gemm_grid(p.tiles_max, mt1)), dim3(PF_THREADS), st, p);
     }
 }
 
@@ -1240,7 +1308,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     p.perm_w = wsp<float>(a.ws, L.perm_w);
     p.pos = wsp<int32_t>(a.ws, L.pos);
     p.h = wsp<_Float16>(a.ws, L.h);
-    p.o = wsp<float>(a.ws, L.o);
+    p.o = wsp<_Float16>(a.ws, L.o);
     const int nb64 = (a.T + 63) / 64;
     if (!a.given_idx) {
         const dim3 gk(4 * L.NW);  // pf_topk: 16-token blocks over whole mask words
@@ -1282,8 +1350,8 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
         launch_gemms<FMT_NVFP4>(p, st);
     else
         launch_gemms<FMT_BF16>(p, st);
-    const size_t n4 = (size_t)a.T * a.D / 4;
-    MOE_LAUNCH(6, pf_combine, dim3((unsigned)((n4 + PF_THREADS - 1) / PF_THREADS)), dim3(PF_THREADS), st, p);
+    const size_t n8 = (size_t)a.T * a.D / 8;
+    MOE_LAUNCH(6, pf_combine, dim3((unsigned)((n8 + PF_THREADS - 1) / PF_THREADS)), dim3(PF_THREADS), st, p);
     return hipGetLastError();
 }
 

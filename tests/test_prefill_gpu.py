@@ -20,9 +20,9 @@ from tests.helpers import REL_L2_TOL, check_routing, rel_l2, router_band_mfma
 pytestmark = pytest.mark.gpu
 
 # fp16 operands: x (exact for bf16 inputs, 2^-12 relative for fp32), the
-# dequantised weights and h are each rounded once to fp16 (2^-12 relative),
-# which puts the expected error near 3e-4; this guard sits between that and
-# the 2e-3 contract.
+# dequantised weights, h and the per-slot down rows O are each rounded once to
+# fp16 (2^-12 relative), which puts the expected error near 4e-4; this guard
+# sits between that and the 2e-3 contract.
 FP16_PATH_GUARD = 1e-3
 
 
