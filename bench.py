@@ -314,12 +314,35 @@ def bench_prefill(args):
         B.layer_forward(dev, x, ws=ws, y=y, want_routing=False, prefill=True)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # eager launches (host launch cost between the 7 kernels included), for context
     ev0.record()
     for _ in range(args.steps):
         B.layer_forward(dev, x, ws=ws, y=y, want_routing=False, prefill=True)
     ev1.record()
     torch.cuda.synchronize()
+    ms_eager = ev0.elapsed_time(ev1) / args.steps
+    y_eager = y.clone()
+    # the timed step: one layer forward captured in a HIP graph and replayed
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.layer_forward(dev, x, ws=ws, y=y, want_routing=False, prefill=True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.layer_forward(dev, x, ws=ws, y=y, want_routing=False, prefill=True)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    graph_matches_eager = bool(torch.equal(y, y_eager))
     # per-kernel dispatch timings
     n_timed = max(1, min(args.timed_calls, 20))
     tot = {}
@@ -353,7 +376,9 @@ def bench_prefill(args):
                     global_batch=T, seq_len=T, parallelism="single-gpu",
                     flops_per_step=fl_all, layer_tflops=round(fl_all / (ms * 1e-3) / 1e12, 1),
                     layer_mfma_frac=round(fl_all / (ms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
-                    experts_hit=int(np.count_nonzero(loads)), max_expert_load=int(loads.max())),
+                    experts_hit=int(np.count_nonzero(loads)), max_expert_load=int(loads.max()),
+                    timing="HIP graph replay of one layer forward", eager_ms_per_step=round(ms_eager, 4),
+                    graph_matches_eager=graph_matches_eager),
         roofline=dict(bound="mfma", kernel=dom, achieved=round(ach, 1), peak=MFMA_FP16_PEAK_TFLOPS,
                       unit="TFLOP/s", frac=round(ach / MFMA_FP16_PEAK_TFLOPS, 4), traffic=None,
                       flops_per_launch=fl_gu, us_per_launch=round(kus[dom], 2),

@@ -38,7 +38,8 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int PF_BM = 128;          // rows (token slots) per GEMM tile
+constexpr int PF_BM = 128;          // rows (token slots) per tile of pf_gemm (and the bound of the tile count)
+constexpr int PQ_BM = 128;          // rows per tile of pf_gemm_q4
 constexpr int PF_THREADS = 256;     // 4 waves
 constexpr int PF_MAX_TOPK = 8;
 
@@ -100,6 +101,7 @@ struct PfParams {
     int D, F, E, S, K, T, act, NW, R, tiles_max, want_x16;
     int rms_in;          // pf_logits: x is un-normalised, scale each token by 1/rms(x)
     int ksplit;          // pf_router_gemm: reduction parts
+    int BM;              // token rows per GEMM tile (tile table)
     hipEvent_t *ev;
     size_t expert_bytes;
     const void *x;
@@ -373,7 +375,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_mask_given(PfParams p) {
 // pf_scan: one block of 1024.  Rows are ordered routed expert 0..E-1, then
 // shared.  Per routed expert (one wave each): prefix popcounts of its mask
 // words; then block-wide exclusive scans of the row counts and tile counts
-// (the tile table lists every full 128-row tile, then the partial ones).
+// (the tile table lists every full tile of p.BM rows, then the partial ones).
 // ---------------------------------------------------------------------------
 constexpr int PF_SCAN_THREADS = 1024;
 
@@ -401,22 +403,39 @@ __global__ void __launch_bounds__(PF_SCAN_THREADS) pf_scan(PfParams p) {
     __shared__ int tot_rows, tot_tiles;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_exp = p.E + p.S;
-    // per routed expert: word prefixes (64 words per pass)
-    for (int e = wave; e < p.E; e += 16) {
-        int carry = 0;
+    // per routed expert (wave w: experts w, w + 16, ...): word prefixes, 64
+    // words per pass; the words of 4 of the wave's experts are loaded
+    // together (more spill at 1024 threads)
+    constexpr int EPW = 4;
+    for (int e0 = wave; e0 < p.E; e0 += 16 * EPW) {
+        int carry[EPW];
+#pragma unroll
+        for (int i = 0; i < EPW; i++) carry[i] = 0;
         for (int w0 = 0; w0 < p.NW; w0 += 64) {
             const int w = w0 + lane;
-            const int c = w < p.NW ? __popcll(p.mask[(size_t)e * p.NW + w]) : 0;
-            const int incl = wave_incl_scan(c);
-            if (w < p.NW) p.wp[(size_t)e * p.NW + w] = carry + incl - c;
-            carry += __shfl(incl, 63, 64);
+            int c[EPW];
+#pragma unroll
+            for (int i = 0; i < EPW; i++) {
+                const int e = e0 + 16 * i;
+                c[i] = (e < p.E && w < p.NW) ? __popcll(p.mask[(size_t)e * p.NW + w]) : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < EPW; i++) {
+                const int e = e0 + 16 * i;
+                const int incl = wave_incl_scan(c[i]);
+                if (e < p.E && w < p.NW) p.wp[(size_t)e * p.NW + w] = carry[i] + incl - c[i];
+                carry[i] += __shfl(incl, 63, 64);
+            }
         }
-        if (lane == 0) cnt[e] = carry;
+#pragma unroll
+        for (int i = 0; i < EPW; i++)
+            if (lane == 0 && e0 + 16 * i < p.E) cnt[e0 + 16 * i] = carry[i];
     }
     __syncthreads();
     const int my_n = tid < p.E ? cnt[tid] : (tid < n_exp ? p.T : 0);
     // full tiles of every expert first, then the partial ones (expert order)
-    const int my_full = my_n / PF_BM, my_part = my_n % PF_BM ? 1 : 0;
+    const int BM = p.BM;
+    const int my_full = my_n / BM, my_part = my_n % BM ? 1 : 0;
     const int off = block_excl_scan(my_n, tmp16, &tot_rows);
     const int foff = block_excl_scan(my_full, tmp16, &tot_tiles);
     const int n_full = tot_tiles;
@@ -432,48 +451,49 @@ __global__ void __launch_bounds__(PF_SCAN_THREADS) pf_scan(PfParams p) {
         for (int i = 0; i < my_full; i++) {
             PfTile t;
             t.e = tid;
-            t.row0 = off + i * PF_BM;
-            t.rows = PF_BM;
+            t.row0 = off + i * BM;
+            t.rows = BM;
             p.tiles[foff + i] = t;
         }
         if (my_part) {
             PfTile t;
             t.e = tid;
-            t.row0 = off + my_full * PF_BM;
-            t.rows = my_n - my_full * PF_BM;
+            t.row0 = off + my_full * BM;
+            t.rows = my_n - my_full * BM;
             p.tiles[n_full + poff] = t;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// pf_scatter: one thread per token.  The rank of token t in expert e's rows
-// is the number of tokens before t that chose e (prefix popcount).
+// pf_scatter: one thread per (token, slot) pair.  The rank of token t in
+// routed expert e's rows is the number of tokens before t that chose e
+// (prefix popcount); shared expert s takes row t of its block.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(PF_THREADS) pf_scatter(PfParams p) {
-    const int t = blockIdx.x * PF_THREADS + threadIdx.x;
-    if (t >= p.T) return;
     const int KS = p.K + p.S;
-    const int w = t >> 6;
-    const unsigned long long below = (t & 63) ? ((1ull << (t & 63)) - 1ull) : 0ull;
-    for (int j = 0; j < p.K; j++) {
+    const int i = blockIdx.x * PF_THREADS + threadIdx.x;
+    if (i >= p.T * KS) return;
+    const int t = i / KS, j = i % KS;
+    int r;
+    float wt;
+    if (j < p.K) {
         const int e = p.idx[(size_t)t * p.K + j];
         if (e < 0 || e >= p.E) {  // caller routing may hold invalid indices: no row
-            p.pos[(size_t)t * KS + j] = -1;
-            continue;
+            p.pos[i] = -1;
+            return;
         }
-        const size_t mi = (size_t)e * p.NW + w;
-        const int r = p.off[e] + p.wp[mi] + __popcll(p.mask[mi] & below);
-        p.perm_tok[r] = t;
-        p.perm_w[r] = p.w[(size_t)t * p.K + j];
-        p.pos[(size_t)t * KS + j] = r;
+        const size_t mi = (size_t)e * p.NW + (t >> 6);
+        const unsigned long long below = (t & 63) ? ((1ull << (t & 63)) - 1ull) : 0ull;
+        r = p.off[e] + p.wp[mi] + __popcll(p.mask[mi] & below);
+        wt = p.w[(size_t)t * p.K + j];
+    } else {
+        r = p.off[p.E + j - p.K] + t;
+        wt = 1.f;
     }
-    for (int s = 0; s < p.S; s++) {
-        const int r = p.off[p.E + s] + t;
-        p.perm_tok[r] = t;
-        p.perm_w[r] = 1.f;
-        p.pos[(size_t)t * KS + p.K + s] = r;
-    }
+    p.perm_tok[r] = t;
+    p.perm_w[r] = wt;
+    p.pos[i] = r;
 }
 
 // The grouped-GEMM helpers use device-only types (buffer resources) and are
@@ -693,15 +713,15 @@ __device__ __forceinline__ void rg_issue(const RgDma &d, uint4 *xs, uint4 *rs, i
 // the wave's row group a, m = 8 (j/4) + 4 g + j%4, n = 32 b + l32.
 //   MODE 0: h = silu(gate) * up (gate in a = 0, up in a = 1), fp16 rows of H
 //   MODE 1: O = coef * acc, fp16 rows of O
-template <int MODE>
-__device__ __forceinline__ void pf_epilogue(const PfParams &p, const PfTile &tile, const f32x16_t (&acc)[2][4], int r0,
+template <int MODE, int NBLK>
+__device__ __forceinline__ void pf_epilogue(const PfParams &p, const PfTile &tile, const f32x16_t (&acc)[2][NBLK], int r0,
                                             const bool (&sub_ok)[2], int g, int l32) {
     if (MODE == 0) {
         if (!sub_ok[0]) return;
         const float ts_g = p.tscale ? p.tscale[3 * tile.e + 0] : 1.f;
         const float ts_u = p.tscale ? p.tscale[3 * tile.e + 1] : 1.f;
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
+        for (int b = 0; b < NBLK; b++) {
             const int n = 32 * b + l32;
             if (n >= tile.rows) continue;
             _Float16 *hrow = p.h + (size_t)(tile.row0 + n) * p.F + r0 + 4 * g;
@@ -721,7 +741,7 @@ __device__ __forceinline__ void pf_epilogue(const PfParams &p, const PfTile &til
     } else {
         const float ts_d = p.tscale ? p.tscale[3 * tile.e + 2] : 1.f;
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
+        for (int b = 0; b < NBLK; b++) {
             const int n = 32 * b + l32;
             if (n >= tile.rows) continue;
             const float c = p.perm_w[tile.row0 + n] * ts_d;
@@ -870,7 +890,7 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm(PfParams p) {
         }
     }
 
-    pf_epilogue<MODE>(p, tile, acc, r0, sub_ok, g, l32);
+    pf_epilogue<MODE, 4>(p, tile, acc, r0, sub_ok, g, l32);
 
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -880,8 +900,8 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm(PfParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
 // MFMAs of one 32-input step against the first NB 32-row token blocks of a
 // token stage (the tile's other blocks hold only padding rows)
-template <int NB>
-__device__ __forceinline__ void pf_mfma_tokens(const _Float16 *stg, const half8_t (&af)[2][2], f32x16_t (&acc)[2][4],
+template <int NB, int NBLK>
+__device__ __forceinline__ void pf_mfma_tokens(const _Float16 *stg, const half8_t (&af)[2][2], f32x16_t (&acc)[2][NBLK],
                                                int l32, int g) {
 #pragma unroll
     for (int s = 0; s < 2; s++) {
@@ -896,7 +916,10 @@ __device__ __forceinline__ void pf_mfma_tokens(const _Float16 *stg, const half8_
 #endif
 
 // ---------------------------------------------------------------------------
-// pf_gemm_q4<MODE>: pf_gemm for q4_1 weights, with the weight fragments of 4
+// pf_gemm_q4<MODE, BM>: pf_gemm for q4_1 weights on tiles of up to BM token
+// rows (128: two blocks per CU; 256: one block per CU with the accumulators
+// of 8 token blocks, so each dequantised weight feeds twice the MFMAs), with
+// the weight fragments of 4
 // consecutive 32-input steps copied at once (per row 64 B of codes and the
 // 16 B of 4 {d, m} pairs).  The address unit's cost of a wave-wide copy
 // grows with the cache lines it touches: 16 rows x 64 B costs well under
@@ -913,10 +936,12 @@ constexpr int PQ_UNROLL = 16;                                   // steps per loo
 // chunk swizzle of a row in the code macro-stage (64-byte rows)
 __device__ __forceinline__ int pq_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
-template <int MODE>
-__global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm_q4(PfParams p) {
+template <int MODE, int BM>
+__global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __shared__ uint4 x0s[PF_BM * 4], x1s[PF_BM * 4], x2s[PF_BM * 4], x3s[PF_BM * 4];
+    constexpr int NBLK = BM / 32;  // 32-row token blocks of a tile
+    constexpr int XCH = BM / 64;   // token copies per thread per step
+    __shared__ uint4 x0s[BM * 4], x1s[BM * 4], x2s[BM * 4], x3s[BM * 4];
     // codes: [256 rows][4 steps x 16 B], a row's step chunks XOR-swizzled by
     // pq_swz(row) (the 8-byte fragment reads of 32 rows then spread over the
     // banks with the least conflict measured); scales: [256 rows][4 steps x {d, m}]
@@ -943,18 +968,18 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm_q4(PfParams p) {
     const int lrow0 = MODE == 0 ? 32 * wave + l32 : 64 * wave + l32;
     const int lrow1 = MODE == 0 ? 128 + 32 * wave + l32 : 64 * wave + 32 + l32;
 
-    // token DMA as in pf_gemm
-    PfDma<FMT_Q4_1> dx;
-    dx.wave = wave;
-    dx.rx = MODE == 0 ? buf_rsrc(p.x16, (uint32_t)((size_t)p.T * p.D * 2))
-                      : buf_rsrc(p.h + (size_t)tile.row0 * p.F, (uint32_t)tile.rows * p.F * 2);
+    // token DMA: this thread fills slots i * 256 + tid of a stage, i.e. rows
+    // 64 i + 16 wave + lane / 4, one chunk each (the step goes in the scalar offset)
+    const __amdgpu_buffer_rsrc_t rx = MODE == 0 ? buf_rsrc(p.x16, (uint32_t)((size_t)p.T * p.D * 2))
+                                                : buf_rsrc(p.h + (size_t)tile.row0 * p.F, (uint32_t)tile.rows * p.F * 2);
+    uint32_t xo[XCH];
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+    for (int i = 0; i < XCH; i++) {
         const int r = 64 * i + 16 * wave + (lane >> 2);
         const int c = (lane & 3) ^ pf_swz(r);
         const int rr = min(r, tile.rows - 1);
         const uint32_t row = MODE == 0 ? (uint32_t)p.perm_tok[tile.row0 + rr] * p.D : (uint32_t)rr * p.F;
-        dx.xo[i] = 2 * row + 16 * c;
+        xo[i] = 2 * row + 16 * c;
     }
     // weight DMA over the block's matrices (gate then up, or down).  Stage
     // row q: MODE 0 gate row mt*128 + q (q < 128) or up row mt*128 + q - 128,
@@ -982,11 +1007,11 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm_q4(PfParams p) {
     const int NK = K / 32, NM = (NK + PQ_MS - 1) / PQ_MS;
     uint32_t sc0[PQ_MS], sc1[PQ_MS];  // {d, m} of the current macro, rows lrow0 and lrow1
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[2][NBLK];
 #pragma unroll
     for (int a = 0; a < 2; a++)
 #pragma unroll
-        for (int b = 0; b < 4; b++)
+        for (int b = 0; b < NBLK; b++)
 #pragma unroll
             for (int j = 0; j < 16; j++) acc[a][b][j] = 0.f;
 
@@ -1010,8 +1035,8 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm_q4(PfParams p) {
     } while (0)
 #define PQ_ISSUE_X(st, ks)                                                                                         \
     do {                                                                                                           \
-        _Pragma("unroll") for (int i_ = 0; i_ < 2; i_++) __builtin_amdgcn_raw_ptr_buffer_load_lds(                 \
-            dx.rx, (lds_void *)(PQ_XST(st) + i_ * 256 + 64 * wave), 16, dx.xo[i_], 64 * (ks), 0, 0);               \
+        _Pragma("unroll") for (int i_ = 0; i_ < XCH; i_++) __builtin_amdgcn_raw_ptr_buffer_load_lds(               \
+            rx, (lds_void *)(PQ_XST(st) + i_ * 256 + 64 * wave), 16, xo[i_], 64 * (ks), 0, 0);                     \
     } while (0)
 #define PQ_READ_SC(b)                                                                                              \
     do {                                                                                                           \
@@ -1027,18 +1052,18 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm_q4(PfParams p) {
 #pragma unroll
     for (int s = 0; s < PF_NS - 1; s++) PQ_ISSUE_X(s, min(s, NK - 1));
     // macro 0 has landed once only the 3 token stages are pending
-    wait_vmcnt<2 * (PF_NS - 1)>();
+    wait_vmcnt<XCH * (PF_NS - 1)>();
     pf_barrier();
     PQ_READ_SC(0);
 
     static_assert(PQ_UNROLL % (2 * PQ_MS) == 0 && PQ_UNROLL % PF_NS == 0 && PQ_MS == 4, "stage indices per trip");
-    // The main loop, instantiated for tiles with rows in all four 32-row
-    // token blocks and for tiles of at most 32 rows (the partial tiles of
-    // most experts): the token-block count fixes the MFMAs of a step.
-    // Step kb waits until token stage kb (and, issued before it, weight
-    // macro kb / 4) has landed: only the copies of the two later steps may
-    // be pending, 2 token copies each, plus W1 (3) after a macro's first
-    // step and W2 (2) after its second.  The next macro's scales are read
+    // The main loop, instantiated for tiles of at most 32 rows (the partial
+    // tiles of most experts), of at most 128 and of up to BM rows: the
+    // token-block count fixes the MFMAs of a step.  Step kb waits until
+    // token stage kb (and, issued before it, weight macro kb / 4) has
+    // landed: only the copies of the two later steps may be pending, XCH
+    // token copies each, plus W1 (3) after a macro's first step and W2 (2)
+    // after its second.  The next macro's scales are read
     // at a macro's last step (its W1 copy precedes that step's token stage).
 #define PQ_MAIN_LOOP(NB_)                                                                                              \
     for (int kb0 = 0; kb0 < NK; kb0 += PQ_UNROLL) {                                                                    \
@@ -1048,13 +1073,13 @@ _Pragma("unroll")                                                               
             if (kb >= NK) break;                                                                                       \
             const int st = u % PQ_MS;                                                                                  \
             if (st == 0)                                                                                               \
-                wait_vmcnt<4>();                                                                                       \
+                wait_vmcnt<2 * XCH>();                                                                                 \
             else if (st == 1)                                                                                          \
-                wait_vmcnt<4 + 3>();                                                                                   \
+                wait_vmcnt<2 * XCH + 3>();                                                                             \
             else if (st == 2)                                                                                          \
-                wait_vmcnt<4 + 3 + 2>();                                                                               \
+                wait_vmcnt<2 * XCH + 3 + 2>();                                                                         \
             else                                                                                                       \
-                wait_vmcnt<4 + 2>();                                                                                   \
+                wait_vmcnt<2 * XCH + 2>();                                                                             \
             pf_barrier();                                                                                              \
             if (st == 0) PQ_ISSUE_W1((u / PQ_MS + 1) % 2, min(kb / PQ_MS + 1, NM - 1));                                \
             if (st == 1) PQ_ISSUE_W2((u / PQ_MS + 1) % 2, min(kb / PQ_MS + 1, NM - 1));                                \
@@ -1070,20 +1095,22 @@ _Pragma("unroll")                                                               
             dequant_frag<FMT_Q4_1>(w1, af[1][0], af[1][1]);                                                            \
             if (st == PQ_MS - 1) PQ_READ_SC((u / PQ_MS + 1) % 2);                                                      \
             const _Float16 *stg = reinterpret_cast<const _Float16 *>(PQ_XST(u % PF_NS));                               \
-            pf_mfma_tokens<NB_>(stg, af, acc, l32, g);                                                                 \
+            pf_mfma_tokens<NB_, NBLK>(stg, af, acc, l32, g);                                                           \
         }                                                                                                              \
     }
     if (nb == 1) {
         PQ_MAIN_LOOP(1);
-    } else {
+    } else if (BM == 128 || nb <= 4) {
         PQ_MAIN_LOOP(4);
+    } else {
+        PQ_MAIN_LOOP(NBLK);
     }
 #undef PQ_MAIN_LOOP
 #undef PQ_ISSUE_W1
 #undef PQ_ISSUE_W2
 #undef PQ_ISSUE_X
 #undef PQ_READ_SC
-    pf_epilogue<MODE>(p, tile, acc, r0, sub_ok, g, l32);
+    pf_epilogue<MODE, NBLK>(p, tile, acc, r0, sub_ok, g, l32);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 #undef PQ_XST
@@ -1251,8 +1278,8 @@ template <int FMT>
 void launch_gemms(const PfParams &p, hipStream_t st) {
     const int mt0 = (p.F + 127) / 128, mt1 = (p.D + 255) / 256;
     if constexpr (FMT == FMT_Q4_1) {
-        MOE_LAUNCH(4, pf_gemm_q4<0>, dim3(pf_gemm_grid(p.tiles_max, mt0)), dim3(PF_THREADS), st, p);
-        MOE_LAUNCH(5, pf_gemm_q4<1>, dim3(pf_gemm_grid(p.tiles_max, mt1)), dim3(PF_THREADS), st, p);
+        MOE_LAUNCH(4, (pf_gemm_q4<0, PQ_BM>), dim3(pf_gemm_grid(p.tiles_max, mt0)), dim3(PF_THREADS), st, p);
+        MOE_LAUNCH(5, (pf_gemm_q4<1, PQ_BM>), dim3(pf_gemm_grid(p.tiles_max, mt1)), dim3(PF_THREADS), st, p);
     } else {
         MOE_LAUNCH(4, (pf_gemm<FMT, 0>), dim3(pf_gemm_grid(p.tiles_max, mt0)), dim3(PF_THREADS), st, p);
         MOE_LAUNCH(5, (pf_gemm<FMT, 1>), dim3(pf_gemm_grid(p.tiles_max, mt1)), dim3(PF_THREADS), st, p);
@@ -1296,6 +1323,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     p.logits = a.logits_out ? a.logits_out : wsp<float>(a.ws, L.logits);
     p.part = wsp<float>(a.ws, L.part);
     p.ksplit = L.ksplit;
+    p.BM = a.fmt == FMT_Q4_1 ? PQ_BM : PF_BM;
     p.x16 = wsp<_Float16>(a.ws, L.x16);
     p.idx = wsp<int32_t>(a.ws, L.idx);
     p.w = wsp<float>(a.ws, L.w);
@@ -1343,7 +1371,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
         MOE_LAUNCH(1, pf_mask_given, dim3(nb64), dim3(PF_THREADS), st, p);
     }
     MOE_LAUNCH(2, pf_scan, dim3(1), dim3(PF_SCAN_THREADS), st, p);
-    MOE_LAUNCH(3, pf_scatter, dim3((a.T + PF_THREADS - 1) / PF_THREADS), dim3(PF_THREADS), st, p);
+    MOE_LAUNCH(3, pf_scatter, dim3((a.T * (a.K + a.S) + PF_THREADS - 1) / PF_THREADS), dim3(PF_THREADS), st, p);
     if (a.fmt == FMT_Q4_1)
         launch_gemms<FMT_Q4_1>(p, st);
     else if (a.fmt == FMT_NVFP4)
