@@ -79,15 +79,19 @@ def union_bytes(idx_trace: np.ndarray, dims, expert_bytes: int) -> float:
     return tot / idx_trace.shape[0] * expert_bytes
 
 
-def source_digest() -> str:
-    """Digest of the decode kernels' sources: stored counter readings apply only to this source."""
+def source_digest(files=("moe_decode_b1.hip", "moe_decode.hip", "moe_device.h", "moe_internal.h")) -> str:
+    """Digest of kernel sources (default: the decode kernels'): stored counter
+    readings apply only to the source they were taken on."""
     import hashlib
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_decode_route_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("moe_decode_b1.hip", "moe_decode.hip", "moe_device.h", "moe_internal.h"):
+    for f in files:
         with open(os.path.join(root, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_device.h", "moe_internal.h")
 
 
 # HBM traffic per launch read from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
@@ -97,9 +101,12 @@ def source_digest() -> str:
 _FETCH_SCALE = 262144.0 / 131085.2  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
 _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE KiB
 COUNTER_TRAFFIC = {
-    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="89c5f0cfd958d7bc",
-                                              fetch_bytes=round(3935.0 * _FETCH_SCALE * 1024),
-                                              write_bytes=round(12.2 * _WRITE_SCALE * 1024)),
+    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="0036dbe912b2656f",
+                                              fetch_bytes=round(3936.0 * _FETCH_SCALE * 1024),
+                                              write_bytes=round(12.7 * _WRITE_SCALE * 1024)),
+    ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="de119f1f3ef38691",
+                                             fetch_bytes=round(223913.3 * _FETCH_SCALE * 1024),
+                                             write_bytes=round(28684.6 * _WRITE_SCALE * 1024)),
 }
 
 
@@ -360,6 +367,9 @@ def bench_prefill(args):
     fl_all = fl_gu + fl_dn + fl_rt
     dom = "pf_gemm_gateup"
     ach = fl_gu / (kus[dom] * 1e-6) / 1e12
+    tr = COUNTER_TRAFFIC.get(("prefill_q4_1", dom))
+    pf_traffic = (tr["fetch_bytes"] + tr["write_bytes"]
+                  if tr is not None and tr["source_digest"] == source_digest(PREFILL_SOURCES) else None)
     per_kernel = {k: dict(us_per_launch=round(v, 2)) for k, v in kus.items()}
     per_kernel["pf_gemm_gateup"]["tflops"] = round(fl_gu / (kus["pf_gemm_gateup"] * 1e-6) / 1e12, 1)
     per_kernel["pf_gemm_down"]["tflops"] = round(fl_dn / (kus["pf_gemm_down"] * 1e-6) / 1e12, 1)
@@ -380,7 +390,7 @@ def bench_prefill(args):
                     timing="HIP graph replay of one layer forward", eager_ms_per_step=round(ms_eager, 4),
                     graph_matches_eager=graph_matches_eager),
         roofline=dict(bound="mfma", kernel=dom, achieved=round(ach, 1), peak=MFMA_FP16_PEAK_TFLOPS,
-                      unit="TFLOP/s", frac=round(ach / MFMA_FP16_PEAK_TFLOPS, 4), traffic=None,
+                      unit="TFLOP/s", frac=round(ach / MFMA_FP16_PEAK_TFLOPS, 4), traffic=pf_traffic,
                       flops_per_launch=fl_gu, us_per_launch=round(kus[dom], 2),
                       timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream",
                       per_kernel=per_kernel),
