@@ -127,7 +127,7 @@ def kernel_algo_bytes(dims, T: int, routed_union: float):
     c = (U + S) * dn + (U + S) * T * F * 4 + T * D * 4
     K = dims.top_k
     pairs = T * K + S * T  # (expert, token) rows of h
-    bn = {"pf_logits": E * D * 2 + T * D * 4 + T * E * 4,
+    bn = {"bn_router": E * D * 2 + T * D * 4 + T * E * 4,
           "bn_select": T * E * 4,
           "bn_gateup": (U + S) * 2 * gu + T * D * 4 + pairs * F * 4,
           "bn_down": (U + S) * dn + pairs * F * 4 + T * D * 4}

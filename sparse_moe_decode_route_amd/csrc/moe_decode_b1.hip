@@ -35,34 +35,6 @@ constexpr int B1_RR = 2;          // output rows per lane group in C
 constexpr int B1_MAX_ACTIVE = 8;  // shared + routed slots
 constexpr int B1_SLOTS_PER_WAVE = B1_MAX_ACTIVE / B1_WAVES_C;
 
-// 1 / sqrt(mean(y^2) + 1e-6), summed in the same order in every wave of
-// every kernel: lane l takes elements 8l + 512i + j (j < 8) for i < UPLR
-// (d_model = 512 * UPLR), in order, then the DPP/shuffle butterfly.  y holds
-// the 2*UPLR float4 at float4 indices 2l + 128i and 2l + 1 + 128i.
-template <int UPLR>
-__device__ __forceinline__ float inv_rms_from(const float4 (&y)[2 * UPLR]) {
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 2 * UPLR; i++) {
-        ss = __builtin_fmaf(y[i].x, y[i].x, ss);
-        ss = __builtin_fmaf(y[i].y, y[i].y, ss);
-        ss = __builtin_fmaf(y[i].z, y[i].z, ss);
-        ss = __builtin_fmaf(y[i].w, y[i].w, ss);
-    }
-    ss = wave_sum(ss);
-    return 1.0f / sqrtf(ss / (float)(UPLR * 512) + 1e-6f);
-}
-
-template <int UPLR>
-__device__ __forceinline__ void load_rms_part(float4 (&y)[2 * UPLR], const float *src) {
-    const int lane = threadIdx.x & (MOE_WAVE - 1);
-#pragma unroll
-    for (int i = 0; i < UPLR; i++) {
-        y[2 * i] = ((const float4 *)src)[2 * lane + 128 * i];
-        y[2 * i + 1] = ((const float4 *)src)[2 * lane + 1 + 128 * i];
-    }
-}
-
 // Gate/up rows f0..f0+RG-1 of one expert: loads issued first, used later.
 template <int FMT, int UPLD, int RG>
 struct GateUp {

@@ -7,10 +7,11 @@
 // union of their chosen experts is read once per layer: expert e's weights
 // serve every token that chose it.
 //
-//   pf_logits   router logits for all tokens (bf16 MFMA, from the prefill
-//               path); in a stack x_t = y_t / rms(y_t) is never written: the
-//               router and gate/up kernels scale their dot products by each
-//               token's 1/rms, computed from the loads they already make
+//   bn_router   router logits: one block per expert row, one wave per token
+//               (the batch-1 router's reduction per wave); in a stack
+//               x_t = y_t / rms(y_t) is never written: the router and gate/up
+//               kernels apply each token's 1/rms, computed from the loads they
+//               already make
 //   bn_select   per-token top-k, the expert union with token masks, and two
 //               work lists: (slot, token pair) items for gate/up and
 //               (slot, token) pairs for the down projection
@@ -25,7 +26,6 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
-#include "moe_prefill.h"
 
 namespace moe {
 
@@ -37,6 +37,47 @@ constexpr int BN_RR = 2;        // output rows per lane group in down
 constexpr int BN_PB = 4;        // (slot, token) pairs per load batch in down
 constexpr int BN_MAXB = 3;      // batches per wave: 8 tokens x (8 + 4) pairs / (8 waves x 4)
 constexpr int BN_SEL_THREADS = 512;
+
+// ---------------------------------------------------------------------------
+// bn_router: logits[t, e] = x_t . Wr[e] (+ bias[e]) for T <= 8 tokens.  One
+// block per expert row, wave t = token t; each wave sums its lane's units in
+// order and then across the wave (DPP butterfly), as the batch-1 router does,
+// so the same fp32 rounding band holds.  SCALED: x_t = y_t / rms(y_t) from
+// the previous layer's output, the sum of squares taken from the wave's own
+// loads of y_t.  d_model = 512 * UPLR.
+// ---------------------------------------------------------------------------
+template <int UPLR, bool SCALED>
+__global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_router(DecodeParams p) {
+    const int lane = threadIdx.x & (MOE_WAVE - 1), t = threadIdx.x / MOE_WAVE;
+    const int e = blockIdx.x;
+    const float *xin = (SCALED ? p.x_prev : p.x) + (size_t)t * p.D;
+    float4 yr[2 * UPLR];
+    load_rms_part<UPLR>(yr, xin);
+    Mat mr{(const uint8_t *)p.router, p.E, p.D, 1.f};
+    WUnit w[UPLR];
+#pragma unroll
+    for (int i = 0; i < UPLR; i++) w[i] = load_unit<FMT_BF16>(mr, e, lane + MOE_WAVE * i);
+    __builtin_amdgcn_sched_barrier(0);
+    const float xs = SCALED ? inv_rms_from<UPLR>(yr) : 1.f;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < UPLR; i++) {
+        XUnit<FMT_BF16> xv;
+        const float4 a = yr[2 * i], b = yr[2 * i + 1];
+        xv.v[0] = a.x * xs;
+        xv.v[1] = a.y * xs;
+        xv.v[2] = a.z * xs;
+        xv.v[3] = a.w * xs;
+        xv.v[4] = b.x * xs;
+        xv.v[5] = b.y * xs;
+        xv.v[6] = b.z * xs;
+        xv.v[7] = b.w * xs;
+        xv.sum = 0.f;
+        acc += unit_dot<FMT_BF16>(w[i], xv, 1.f);
+    }
+    const float sum = wave_sum(acc);
+    if (lane == 0) p.logits[(size_t)t * p.E + e] = p.bias ? sum + p.bias[e] : sum;
+}
 
 // ---------------------------------------------------------------------------
 // bn_select: one block.  Wave t takes token t's top-k (or reads the given
@@ -412,11 +453,21 @@ hipError_t launch_decode_bn(const DecodeParams &p, hipStream_t st) {
                                          : bn_shape_ok<FMT_BF16>(p);
     if (!ok) return hipErrorNotSupported;
     if (!p.route_given) {
-        if (!p.want_router) return hipErrorNotSupported;
-        const float *xin = p.x_prev ? p.x_prev : p.x;
-        const hipError_t e = launch_router_logits(xin, p.T, p.D, p.E, p.router, p.bias, p.logits,
-                                                  p.x_prev ? 1 : 0, p.ev, st);
-        if (e != hipSuccess) return e;
+        if (!p.want_router || p.D % 512) return hipErrorNotSupported;
+        const dim3 gr(p.E), br(MOE_WAVE * p.T);
+#define BN_ROUTER(U)                                                                  \
+    if (p.x_prev)                                                                     \
+        MOE_LAUNCH(0, (bn_router<U, true>), gr, br, st, p);                           \
+    else                                                                              \
+        MOE_LAUNCH(0, (bn_router<U, false>), gr, br, st, p);
+        switch (p.D / 512) {
+        case 1: BN_ROUTER(1) break;
+        case 2: BN_ROUTER(2) break;
+        case 4: BN_ROUTER(4) break;
+        case 8: BN_ROUTER(8) break;
+        default: return hipErrorNotSupported;
+        }
+#undef BN_ROUTER
     }
     MOE_LAUNCH(1, bn_select, dim3(1), dim3(BN_SEL_THREADS), st, p);
     if (p.fmt == FMT_Q4_1) return launch_bn_shape<FMT_Q4_1>(p, st);

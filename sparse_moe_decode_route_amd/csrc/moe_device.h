@@ -347,6 +347,34 @@ __device__ __forceinline__ void wave_topk_regs(const float lv[4], int E, int K, 
     *w_out = ev / den;
 }
 
+// 1 / sqrt(mean(y^2) + 1e-6), summed in the same order in every wave of
+// every kernel: lane l takes elements 8l + 512i + j (j < 8) for i < UPLR
+// (d_model = 512 * UPLR), in order, then the DPP/shuffle butterfly.  y holds
+// the 2*UPLR float4 at float4 indices 2l + 128i and 2l + 1 + 128i.
+template <int UPLR>
+__device__ __forceinline__ float inv_rms_from(const float4 (&y)[2 * UPLR]) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2 * UPLR; i++) {
+        ss = __builtin_fmaf(y[i].x, y[i].x, ss);
+        ss = __builtin_fmaf(y[i].y, y[i].y, ss);
+        ss = __builtin_fmaf(y[i].z, y[i].z, ss);
+        ss = __builtin_fmaf(y[i].w, y[i].w, ss);
+    }
+    ss = wave_sum(ss);
+    return 1.0f / sqrtf(ss / (float)(UPLR * 512) + 1e-6f);
+}
+
+template <int UPLR>
+__device__ __forceinline__ void load_rms_part(float4 (&y)[2 * UPLR], const float *src) {
+    const int lane = threadIdx.x & (MOE_WAVE - 1);
+#pragma unroll
+    for (int i = 0; i < UPLR; i++) {
+        y[2 * i] = ((const float4 *)src)[2 * lane + 128 * i];
+        y[2 * i + 1] = ((const float4 *)src)[2 * lane + 1 + 128 * i];
+    }
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
     const int lane = threadIdx.x & (MOE_WAVE - 1);

@@ -35,11 +35,6 @@ const char *prefill_names(int act);
 
 size_t prefill_ws_bytes(int D, int F, int E, int S, int K, int T);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);
-// logits[T, E] = x Wr^T (+ bias) for fp32 x by the prefill router kernel
-// (bf16 MFMA on a two-term bf16 split of x); rms_in: x is un-normalised and
-// each token's dot products are scaled by 1/rms(x); ev: optional start/stop pair.
-hipError_t launch_router_logits(const float *x, int T, int D, int E, const uint16_t *router, const float *bias,
-                                float *logits, int rms_in, hipEvent_t *ev, hipStream_t st);
 hipError_t launch_repack_q4_1(const uint8_t *canonical, uint8_t *packed, int n_experts, int D, int F, hipStream_t st);
 
 }  // namespace moe

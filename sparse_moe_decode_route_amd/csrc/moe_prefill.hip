@@ -99,7 +99,6 @@ T *wsp(void *ws, size_t off) {
 
 struct PfParams {
     int D, F, E, S, K, T, act, NW, R, tiles_max, want_x16;
-    int rms_in;          // pf_logits: x is un-normalised, scale each token by 1/rms(x)
     int ksplit;          // pf_router_gemm: reduction parts
     int BM;              // token rows per GEMM tile (tile table)
     hipEvent_t *ev;
@@ -143,17 +142,13 @@ __device__ __forceinline__ uint32_t f2bf_rne(float f) {
 // = 32 experts x 32 tokens; its KS waves split the reduction into KS parts,
 // summed in wave order through LDS.  Blocks of the first expert column also
 // write the fp16 copy of x (operand of the expert GEMMs).  An fp32 input is
-// split x = hi + lo into two bf16 parts, both accumulated.  With rms_in, x is
-// the previous layer's output and each token's logits are scaled by
-// 1 / sqrt(mean(x^2) + 1e-6) (the dot product is linear in x); the sum of
-// squares comes from the same loads, in a fixed order.
+// split x = hi + lo into two bf16 parts, both accumulated.
 // ---------------------------------------------------------------------------
 constexpr int PF_LG_CH = 8;  // reduction steps of 16 per load batch
 
 template <int ACT, int KS>
 __global__ void __launch_bounds__(64 * KS) pf_logits(PfParams p) {
     __shared__ float red[KS][32][33];
-    __shared__ float ssq[KS][32];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
@@ -167,7 +162,6 @@ __global__ void __launch_bounds__(64 * KS) pf_logits(PfParams p) {
     f32x16_t acc;
 #pragma unroll
     for (int j = 0; j < 16; j++) acc[j] = 0.f;
-    float ss = 0.f;
     for (int kc = ks0; kc < ks1; kc += PF_LG_CH) {
         // one batch: every load first, then the MFMAs
         uint4 av[PF_LG_CH];
@@ -193,10 +187,6 @@ __global__ void __launch_bounds__(64 * KS) pf_logits(PfParams p) {
                     lo[j] = l0 | (l1 << 16);
                     hv[2 * j] = (_Float16)xv[2 * j];
                     hv[2 * j + 1] = (_Float16)xv[2 * j + 1];
-                }
-                if (live) {
-#pragma unroll
-                    for (int j = 0; j < 8; j++) ss = __builtin_fmaf(xv[j], xv[j], ss);
                 }
                 bh[c] = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
                 bl[c] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
@@ -228,10 +218,6 @@ __global__ void __launch_bounds__(64 * KS) pf_logits(PfParams p) {
     // acc[j] = partial logit of expert e0 + 8 (j/4) + 4 g + j%4, token t0 + l32
 #pragma unroll
     for (int j = 0; j < 16; j++) red[wave][8 * (j >> 2) + 4 * g + (j & 3)][l32] = acc[j];
-    if (ACT == 0) {
-        ss += __shfl_xor(ss, 32, 64);  // the two lane groups of token l32
-        if (g == 0) ssq[wave][l32] = ss;
-    }
     __syncthreads();
     for (int i = tid; i < 32 * 32; i += 64 * KS) {
         const int el = i >> 5, tl = i & 31;
@@ -240,12 +226,6 @@ __global__ void __launch_bounds__(64 * KS) pf_logits(PfParams p) {
         float v = red[0][el][tl];
 #pragma unroll
         for (int w = 1; w < KS; w++) v += red[w][el][tl];
-        if (ACT == 0 && p.rms_in) {
-            float q = ssq[0][tl];
-#pragma unroll
-            for (int w = 1; w < KS; w++) q += ssq[w][tl];
-            v *= 1.0f / sqrtf(q / (float)D + 1e-6f);
-        }
         p.logits[(size_t)t * E + e] = v + (p.bias ? p.bias[e] : 0.f);
     }
 }
@@ -1294,20 +1274,6 @@ const char *prefill_names(int act) {
 }
 
 size_t prefill_ws_bytes(int D, int F, int E, int S, int K, int T) { return pf_layout(D, F, E, S, K, T).total; }
-
-hipError_t launch_router_logits(const float *x, int T, int D, int E, const uint16_t *router, const float *bias,
-                                float *logits, int rms_in, hipEvent_t *ev, hipStream_t st) {
-    if (E > 256 || D % 16) return hipErrorNotSupported;
-    PfParams p{};
-    p.D = D; p.E = E; p.T = T;
-    p.x = x; p.router = router; p.bias = bias; p.logits = logits;
-    p.want_x16 = 0;
-    p.rms_in = rms_in;
-    p.ev = ev;
-    // few tokens: an 8-way split of the reduction keeps 8 waves per block busy
-    MOE_LAUNCH(0, (pf_logits<0, 8>), dim3((T + 31) / 32, (E + 31) / 32), dim3(64 * 8), st, p);
-    return hipGetLastError();
-}
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     if (a.E > 256 || a.K > PF_MAX_TOPK || a.D % 32 || a.F % 32) return hipErrorNotSupported;

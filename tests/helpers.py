@@ -84,9 +84,6 @@ def router_band_mfma(x: np.ndarray, router_f64: np.ndarray, f32_input: bool) -> 
 
 
 def decode_band(x: np.ndarray, router_f64: np.ndarray) -> np.ndarray:
-    """Band for a decode call: one token takes the fp32 router GEMV, several
-    tokens may take the matrix-core router (fp32 input split in two)."""
-    b = router_band(x, router_f64)
-    if x.shape[0] > 1:
-        b = np.maximum(b, router_band_mfma(x, router_f64, True))
-    return b
+    """Band for a decode call (1 to 8 tokens): every decode path computes the
+    router as an fp32 GEMV, lane-sequential partial sums then a wave butterfly."""
+    return router_band(x, router_f64)
