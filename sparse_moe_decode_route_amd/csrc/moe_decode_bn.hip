@@ -88,8 +88,7 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_router(DecodeParams
 // meta = {active slots, items, pairs}.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
-    __shared__ int sel_e[MAX_DECODE_T][8];
-    __shared__ float sel_w[MAX_DECODE_T][8];
+    __shared__ float coef[256][MAX_DECODE_T];  // routed expert x token: summed selection weights
     __shared__ uint32_t emask[256];
     __shared__ int wcnt[4];
     __shared__ int act_e[256 + 4];
@@ -100,6 +99,7 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = p.T, K = p.K, E = p.E, S = p.S;
     if (tid < 256) emask[tid] = 0u;
+    for (int i = tid; i < 256 * MAX_DECODE_T; i += BN_SEL_THREADS) (&coef[0][0])[i] = 0.f;
     __syncthreads();
     if (wave < T) {
         int e;
@@ -116,11 +116,14 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
                 if (p.w_out) p.w_out[wave * K + lane] = wi;
             }
         }
-        if (lane < K) {
-            const bool ok = e >= 0 && e < E;  // invalid given indices select nothing
-            sel_e[wave][lane] = ok ? e : -1;
-            sel_w[wave][lane] = wi;
-            if (ok) atomicOr(&emask[e], 1u << wave);
+        const bool ok = lane < K && e >= 0 && e < E;  // invalid given indices select nothing
+        if (ok) atomicOr(&emask[e], 1u << wave);
+        // the token's weights per expert, added in selection order (a repeated
+        // given index adds its weights: the expert counted twice)
+        for (int k = 0; k < K; k++) {
+            const int ek = __shfl(e, k, 64);
+            const float wk = __shfl(wi, k, 64);
+            if (lane == 0 && ek >= 0 && ek < E) coef[ek][wave] += wk;
         }
     }
     __syncthreads();
@@ -163,6 +166,8 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
     if (tid < n_act) {
         n_items_s[tid] = off_i + inc_i - ci;
         n_pairs_s[tid] = off_p + inc_p - c_slot;
+        p.act_expert[tid] = act_e[tid];
+        p.act_mask[tid] = act_m[tid];
     }
     if (tid == 0) {
         p.meta[0] = n_act;
@@ -179,35 +184,24 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
     for (int i = tot_p + tid; i < max_pairs; i += BN_SEL_THREADS)
         reinterpret_cast<int4 *>(p.pairs)[i] = make_int4(0, -1, 0, 0);
     __syncthreads();
-    if (tid < n_act) {
-        const int slot = tid, e = act_e[slot];
+    // one thread per (slot, token): the pair of a selected token sits at its
+    // rank among the slot's tokens; an even rank starts a gate/up item with
+    // the slot's next selected token (or none)
+    for (int i = tid; i < n_act * T; i += BN_SEL_THREADS) {
+        const int slot = i / T, t = i % T;
+        const int e = act_e[slot];
         const uint32_t mk = act_m[slot];
-        p.act_expert[slot] = e;
-        p.act_mask[slot] = mk;
-        int it = n_items_s[slot], pr = n_pairs_s[slot];
-        int pend = -1;
-        for (int t = 0; t < T; t++) {
-            float c = 0.f;
-            if (slot < S) {
-                c = 1.f;
-            } else {
-                // a repeated index adds its weights (the expert counted twice)
-                for (int k = 0; k < K; k++)
-                    if (sel_e[t][k] == e) c += sel_w[t][k];
-            }
-            p.act_w[slot * T + t] = ((mk >> t) & 1u) ? c : 0.f;
-            if (!((mk >> t) & 1u)) continue;
-            int4 q;
-            q.x = slot; q.y = t; q.z = __float_as_int(c); q.w = e;
-            reinterpret_cast<int4 *>(p.pairs)[pr++] = q;
-            if (pend < 0) {
-                pend = t;
-            } else {
-                reinterpret_cast<int4 *>(p.work)[it++] = make_int4(slot, pend, t, e);
-                pend = -1;
-            }
+        const bool on = (mk >> t) & 1u;
+        const float c = !on ? 0.f : slot < S ? 1.f : coef[e][t];
+        p.act_w[slot * T + t] = c;
+        if (!on) continue;
+        const int rank = __popc(mk & ((1u << t) - 1u));
+        reinterpret_cast<int4 *>(p.pairs)[n_pairs_s[slot] + rank] = make_int4(slot, t, __float_as_int(c), e);
+        if ((rank & 1) == 0) {
+            const uint32_t later = mk & ~((2u << t) - 1u);
+            const int tb = later ? __builtin_ctz(later) : -1;
+            reinterpret_cast<int4 *>(p.work)[n_items_s[slot] + rank / 2] = make_int4(slot, t, tb, e);
         }
-        if (pend >= 0) reinterpret_cast<int4 *>(p.work)[it++] = make_int4(slot, pend, -1, e);
     }
 }
 
