@@ -261,9 +261,12 @@ __device__ __forceinline__ void bn_gateup_finish(const DecodeParams &p, const WU
 // ---------------------------------------------------------------------------
 // bn_gateup: wave gw -> item gw / (F / RG), features f0 .. f0 + RG - 1.
 // h[(slot * T + t) * F + f] = silu(Wg x_t)[f] * (Wu x_t)[f] for both tokens.
+// Weight loads first; the tokens' x rows go to LDS by contiguous loads of the
+// whole block and are read back per lane unit.
 // ---------------------------------------------------------------------------
 template <int FMT, int UPLD, int RG>
 __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) {
+    __shared__ uint4 xs[2][UPLD * MOE_WAVE * Unit<FMT>::E / 4];  // both tokens' x, 16-byte chunks
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int per_item = p.F / RG;
@@ -286,12 +289,19 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
             wg[r][i] = load_unit<FMT>(mg, f0 + r, lane + MOE_WAVE * i);
             wu[r][i] = load_unit<FMT>(mu, f0 + r, lane + MOE_WAVE * i);
         }
+    // the block's waves share the item (F / RG is a multiple of BN_WAVES):
+    // its tokens' x rows are loaded once, 1 KB contiguous per wave-wide load
+    const int nq = p.D / 4;  // 16-byte chunks per row
+    for (int q = threadIdx.x; q < nq; q += MOE_WAVE * BN_WAVES) {
+        xs[0][xs_slot<FMT>(q)] = *reinterpret_cast<const uint4 *>(xin + (size_t)ta * p.D + 4 * q);
+        xs[1][xs_slot<FMT>(q)] = *reinterpret_cast<const uint4 *>(xin + (size_t)tb * p.D + 4 * q);
+    }
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < UPLD; i++) {
-        load_x<FMT>(xa[i], xin + (size_t)ta * p.D, lane + MOE_WAVE * i);
-        load_x<FMT>(xb[i], xin + (size_t)tb * p.D, lane + MOE_WAVE * i);
+        load_x_lds<FMT>(xa[i], xs[0], lane + MOE_WAVE * i);
+        load_x_lds<FMT>(xb[i], xs[1], lane + MOE_WAVE * i);
     }
-    __builtin_amdgcn_sched_barrier(0);
     // a routed expert usually serves one token of the batch: the second
     // token's arithmetic only runs for items that have one (uniform branch)
     if (wk.z >= 0)
@@ -433,7 +443,8 @@ bool bn_shape_ok(const DecodeParams &p) {
     constexpr int UE = Unit<FMT>::E;
     if (p.D % (MOE_WAVE * UE) || p.F % UE || p.F % 4) return false;
     const int upld = p.D / (MOE_WAVE * UE), lpr_f = p.F / UE;
-    return (upld == 1 || upld == 2) && (lpr_f == 16 || lpr_f == 32);
+    const int rg = upld == 1 ? 4 : 2;  // features per gate/up wave: a block's waves share one item
+    return (upld == 1 || upld == 2) && (lpr_f == 16 || lpr_f == 32) && (p.F / rg) % BN_WAVES == 0;
 }
 
 }  // namespace

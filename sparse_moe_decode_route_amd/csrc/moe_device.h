@@ -112,6 +112,38 @@ __device__ __forceinline__ void load_x(XUnit<FMT> &x, const float *src, int u) {
     }
 }
 
+// Activations staged in LDS as 16-byte chunks, unit u's chunk c at slot
+// u * (E / 4) + (c ^ ((u >> 1) & (E / 4 - 1))): 16 lanes reading one chunk of
+// 16 consecutive units then hit distinct banks.
+template <int FMT>
+__device__ __forceinline__ int xs_slot(int q) {
+    constexpr int CPU = Unit<FMT>::E / 4;
+    const int u = q / CPU, c = q % CPU;
+    return u * CPU + (c ^ ((u >> 1) & (CPU - 1)));
+}
+
+// load_x from the LDS staging (same values, same sum order)
+template <int FMT>
+__device__ __forceinline__ void load_x_lds(XUnit<FMT> &x, const uint4 *xs, int u) {
+    constexpr int CPU = Unit<FMT>::E / 4;
+#pragma unroll
+    for (int i = 0; i < CPU; i++) {
+        const uint4 f = xs[u * CPU + (i ^ ((u >> 1) & (CPU - 1)))];
+        x.v[4 * i + 0] = __uint_as_float(f.x);
+        x.v[4 * i + 1] = __uint_as_float(f.y);
+        x.v[4 * i + 2] = __uint_as_float(f.z);
+        x.v[4 * i + 3] = __uint_as_float(f.w);
+    }
+    if (FMT == FMT_Q4_1) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < Unit<FMT>::E; i++) s += x.v[i];
+        x.sum = s;
+    } else {
+        x.sum = 0.f;
+    }
+}
+
 // dot(unit weights, unit activations) in fp32.
 template <int FMT>
 __device__ __forceinline__ float unit_dot(const WUnit &w, const XUnit<FMT> &x, float ts) {
