@@ -161,13 +161,20 @@ __global__ void __launch_bounds__(MOE_WAVE) b1_route_shared(DecodeParams p) {
 // ---------------------------------------------------------------------------
 template <int FMT, int UPLD>
 __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_B) b1_topk_gateup(DecodeParams p) {
-    __shared__ int s_sel[8];
     const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
-    if (wave == 0) {
-        int e;
+    const int per_expert = p.F / B1_RG;
+    const int gw = blockIdx.x * B1_WAVES_B + wave;
+    const int j = gw / per_expert, f0 = (gw % per_expert) * B1_RG;
+    float lv[4];
+    wave_topk_load(p.logits, p.E, lv);
+    int e = -1;
+    if (wave == 0 && ((int)blockIdx.x < p.b1_ncopy || blockIdx.x == 0)) {
+        // the full selection with weights, for the routing outputs and the
+        // down kernel
+        int es;
         float wi;
-        wave_topk(p.logits, p.E, p.K, &e, &wi);
-        if (lane < 8) s_sel[lane] = e;
+        wave_topk_regs(lv, p.E, p.K, &es, &wi);
+        if (j < p.K) e = __shfl(es, j, MOE_WAVE);
         if ((int)blockIdx.x < p.b1_ncopy) {
             // one copy of the active list per XCD (block b runs on XCD b % 8),
             // read by the down kernel's blocks of the same XCD
@@ -177,17 +184,17 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_B) b1_topk_gateup(DecodePar
                 cp[8 + lane] = __float_as_int(1.f);
             }
             if (lane < p.K) {
-                cp[p.S + lane] = e;
+                cp[p.S + lane] = es;
                 cp[8 + p.S + lane] = __float_as_int(wi);
             }
         }
         if (blockIdx.x == 0) {
             if (lane < p.K) {
-                p.idx[lane] = e;
+                p.idx[lane] = es;
                 p.w[lane] = wi;
-                p.act_expert[p.S + lane] = e;
+                p.act_expert[p.S + lane] = es;
                 p.act_w[p.S + lane] = wi;
-                if (p.idx_out) p.idx_out[lane] = e;
+                if (p.idx_out) p.idx_out[lane] = es;
                 if (p.w_out) p.w_out[lane] = wi;
             }
             if (lane < p.S) {
@@ -197,18 +204,10 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_B) b1_topk_gateup(DecodePar
             if (lane == 0) p.meta[0] = p.S + p.K;
         }
     }
-    // only s_sel (LDS) is shared: wait for the LDS write, then a barrier
-    // without the global release fence of __syncthreads (which would hold
-    // block 0 until its routing stores were acknowledged)
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const int per_expert = p.F / B1_RG;
-    const int gw = blockIdx.x * B1_WAVES_B + wave;
-    const int j = gw / per_expert, f0 = (gw % per_expert) * B1_RG;
     if (j >= p.K) return;
-    const int e = s_sel[j];
+    // every other wave finds its own expert (the j-th largest logit): no
+    // barrier between the selection and the weight loads
+    if (e < 0) e = wave_topk_nth(lv, p.E, j);
     GateUp<FMT, UPLD, B1_RG> g;
     gateup_issue<FMT, UPLD, B1_RG>(g, p, e, f0);
     // x in the same round trip as the weights (loaded before the top-k, a

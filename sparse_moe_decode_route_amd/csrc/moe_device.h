@@ -407,6 +407,33 @@ __device__ __forceinline__ void load_rms_part(float4 (&y)[2 * UPLR], const float
     }
 }
 
+// Index of the n-th largest logit (n = 0: the largest) by the same rounds as
+// wave_topk_regs, stopping after round n: the same expert that wave_topk
+// returns in lane n.
+__device__ __forceinline__ int wave_topk_nth(const float lv[4], int E, int n) {
+    const int lane = threadIdx.x & (MOE_WAVE - 1);
+    uint32_t key[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const int ix = lane + 64 * k;
+        const float v = __uint_as_float(opaque(__float_as_uint(lv[k])));
+        key[k] = ix < E ? f2key(v) : 0u;
+    }
+    int gi = 0;
+    for (int i = 0; i <= n; i++) {
+        const uint32_t m = wave_max_key(max(max(key[0], key[1]), max(key[2], key[3])));
+        gi = 0;
+#pragma unroll
+        for (int k = 3; k >= 0; k--) {
+            const uint64_t b = __ballot(key[k] == m);
+            gi = b ? 64 * k + (int)__builtin_ctzll(b) : gi;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) key[k] = (lane + 64 * k == gi) ? 0u : key[k];
+    }
+    return gi;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
     const int lane = threadIdx.x & (MOE_WAVE - 1);
