@@ -1035,16 +1035,29 @@ __global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfPa
     wait_vmcnt<XCH * (PF_NS - 1)>();
     pf_barrier();
     PQ_READ_SC(0);
+    // weights of step 0 in MFMA operand form; each step then dequantises the
+    // next step's weights while its own MFMAs run
+    half8_t af[2][2];
+    {
+        WRaw<FMT_Q4_1> w0, w1;
+        w0.c = *reinterpret_cast<const uint2 *>(c0s + lrow0 * 64 + 16 * pq_swz(lrow0) + 8 * g);
+        w0.dm = sc0[0];
+        w1.c = *reinterpret_cast<const uint2 *>(c0s + lrow1 * 64 + 16 * pq_swz(lrow1) + 8 * g);
+        w1.dm = sc1[0];
+        dequant_frag<FMT_Q4_1>(w0, af[0][0], af[0][1]);
+        dequant_frag<FMT_Q4_1>(w1, af[1][0], af[1][1]);
+    }
 
     static_assert(PQ_UNROLL % (2 * PQ_MS) == 0 && PQ_UNROLL % PF_NS == 0 && PQ_MS == 4, "stage indices per trip");
     // The main loop, instantiated for tiles of at most 32 rows (the partial
     // tiles of most experts), of at most 128 and of up to BM rows: the
     // token-block count fixes the MFMAs of a step.  Step kb waits until
-    // token stage kb (and, issued before it, weight macro kb / 4) has
-    // landed: only the copies of the two later steps may be pending, XCH
-    // token copies each, plus W1 (3) after a macro's first step and W2 (2)
-    // after its second.  The next macro's scales are read
-    // at a macro's last step (its W1 copy precedes that step's token stage).
+    // token stage kb has landed (only the copies of the two later steps may
+    // be pending: XCH token copies each, plus W1 (3) after a macro's first
+    // step and W2 (2) after its second); at a macro's last step it also waits
+    // for the next macro's W2, whose codes it dequantises for the next step.
+    // The next macro's scales are read at that step too (its W1 copy came
+    // before this step's token stage).
 #define PQ_MAIN_LOOP(NB_)                                                                                              \
     for (int kb0 = 0; kb0 < NK; kb0 += PQ_UNROLL) {                                                                    \
 _Pragma("unroll")                                                                                                      \
@@ -1059,23 +1072,23 @@ _Pragma("unroll")                                                               
             else if (st == 2)                                                                                          \
                 wait_vmcnt<2 * XCH + 3 + 2>();                                                                         \
             else                                                                                                       \
-                wait_vmcnt<2 * XCH + 2>();                                                                             \
+                wait_vmcnt<2 * XCH>();                                                                                 \
             pf_barrier();                                                                                              \
             if (st == 0) PQ_ISSUE_W1((u / PQ_MS + 1) % 2, min(kb / PQ_MS + 1, NM - 1));                                \
             if (st == 1) PQ_ISSUE_W2((u / PQ_MS + 1) % 2, min(kb / PQ_MS + 1, NM - 1));                                \
             PQ_ISSUE_X((u + PF_NS - 1) % PF_NS, min(kb + PF_NS - 1, NK - 1));                                          \
-            const uint8_t *cb = (u / PQ_MS) % 2 == 0 ? c0s : c1s;                                                      \
-            WRaw<FMT_Q4_1> w0, w1;                                                                                     \
-            w0.c = *reinterpret_cast<const uint2 *>(cb + lrow0 * 64 + 16 * (st ^ pq_swz(lrow0)) + 8 * g);              \
-            w0.dm = sc0[st];                                                                                           \
-            w1.c = *reinterpret_cast<const uint2 *>(cb + lrow1 * 64 + 16 * (st ^ pq_swz(lrow1)) + 8 * g);              \
-            w1.dm = sc1[st];                                                                                           \
-            half8_t af[2][2];                                                                                          \
-            dequant_frag<FMT_Q4_1>(w0, af[0][0], af[0][1]);                                                            \
-            dequant_frag<FMT_Q4_1>(w1, af[1][0], af[1][1]);                                                            \
-            if (st == PQ_MS - 1) PQ_READ_SC((u / PQ_MS + 1) % 2);                                                      \
             const _Float16 *stg = reinterpret_cast<const _Float16 *>(PQ_XST(u % PF_NS));                               \
             pf_mfma_tokens<NB_, NBLK>(stg, af, acc, l32, g);                                                           \
+            const int un = u + 1, stn = un % PQ_MS;                                                                    \
+            if (stn == 0) PQ_READ_SC((un / PQ_MS) % 2);                                                                \
+            const uint8_t *cb = (un / PQ_MS) % 2 == 0 ? c0s : c1s;                                                     \
+            WRaw<FMT_Q4_1> w0, w1;                                                                                     \
+            w0.c = *reinterpret_cast<const uint2 *>(cb + lrow0 * 64 + 16 * (stn ^ pq_swz(lrow0)) + 8 * g);             \
+            w0.dm = sc0[stn];                                                                                          \
+            w1.c = *reinterpret_cast<const uint2 *>(cb + lrow1 * 64 + 16 * (stn ^ pq_swz(lrow1)) + 8 * g);             \
+            w1.dm = sc1[stn];                                                                                          \
+            dequant_frag<FMT_Q4_1>(w0, af[0][0], af[0][1]);                                                            \
+            dequant_frag<FMT_Q4_1>(w1, af[1][0], af[1][1]);                                                            \
         }                                                                                                              \
     }
     if (nb == 1) {
