@@ -434,14 +434,18 @@ __device__ __forceinline__ int wave_topk_nth(const float lv[4], int E, int n) {
     return gi;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP only: row_shr
+// 1, 2, 4, 8 scan each 16-lane row (lanes shifted in from outside the row
+// read 0), then lane 15 of row 0 / 2 is added to rows 1 / 3 (row_bcast:15)
+// and lane 31 to rows 2 and 3 (row_bcast:31).  Rows outside a row mask keep
+// the old value 0, so they add nothing.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = threadIdx.x & (MOE_WAVE - 1);
-#pragma unroll
-    for (int o = 1; o < MOE_WAVE; o <<= 1) {
-        const int u = __shfl_up(v, o, MOE_WAVE);
-        v += lane >= o ? u : 0;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
     return v;
 }
 

@@ -384,9 +384,9 @@ __global__ void __launch_bounds__(PF_SCAN_THREADS) pf_scan(PfParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_exp = p.E + p.S;
     // per routed expert (wave w: experts w, w + 16, ...): word prefixes, 64
-    // words per pass; the words of 4 of the wave's experts are loaded
-    // together (more spill at 1024 threads)
-    constexpr int EPW = 4;
+    // words per pass; the words of the wave's 16 experts are loaded together
+    // (32-bit element offsets from the scalar base keep one register per address)
+    constexpr int EPW = 16;
     for (int e0 = wave; e0 < p.E; e0 += 16 * EPW) {
         int carry[EPW];
 #pragma unroll
@@ -397,13 +397,13 @@ __global__ void __launch_bounds__(PF_SCAN_THREADS) pf_scan(PfParams p) {
 #pragma unroll
             for (int i = 0; i < EPW; i++) {
                 const int e = e0 + 16 * i;
-                c[i] = (e < p.E && w < p.NW) ? __popcll(p.mask[(size_t)e * p.NW + w]) : 0;
+                c[i] = (e < p.E && w < p.NW) ? __popcll(p.mask[(uint32_t)(e * p.NW + w)]) : 0;
             }
 #pragma unroll
             for (int i = 0; i < EPW; i++) {
                 const int e = e0 + 16 * i;
                 const int incl = wave_incl_scan(c[i]);
-                if (e < p.E && w < p.NW) p.wp[(size_t)e * p.NW + w] = carry[i] + incl - c[i];
+                if (e < p.E && w < p.NW) p.wp[(uint32_t)(e * p.NW + w)] = carry[i] + incl - c[i];
                 carry[i] += __shfl(incl, 63, 64);
             }
         }
