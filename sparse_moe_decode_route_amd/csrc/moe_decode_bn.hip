@@ -17,9 +17,9 @@
 //               (slot, token) pairs for the down projection
 //   bn_gateup   one wave per (item, 2-4 features): weights and both tokens' x
 //               loaded before any arithmetic
-//   bn_down     8 output rows per block; its 8 waves take (slot, token) pairs
-//               in batches of 4 with every load of a batch in flight; the
-//               per-token partial sums are added in a fixed order
+//   bn_down     8 output rows per block; wave t sums token t's down terms
+//               (its shared slots, then its selections in top-k order) in
+//               batches of 4 with every load of a batch in flight
 // No floating-point atomics; every sum has a fixed order.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -32,10 +32,9 @@ namespace moe {
 namespace {
 
 constexpr int BN_WAVES = 4;     // waves per block in gate/up
-constexpr int BN_DWAVES = 8;    // waves per block in down
 constexpr int BN_RR = 2;        // output rows per lane group in down
-constexpr int BN_PB = 4;        // (slot, token) pairs per load batch in down
-constexpr int BN_MAXB = 3;      // batches per wave: 8 tokens x (8 + 4) pairs / (8 waves x 4)
+constexpr int BN_PB = 4;        // list entries per load batch in down
+constexpr int BN_MAXB = 3;      // batches per wave: a token's list has K + S <= 12 entries
 constexpr int BN_SEL_THREADS = 512;
 
 // ---------------------------------------------------------------------------
@@ -89,13 +88,15 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_router(DecodeParams
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
     __shared__ float coef[256][MAX_DECODE_T];  // routed expert x token: summed selection weights
+    __shared__ int sel_e[MAX_DECODE_T][8];     // token x selection: expert (-1: none)
+    __shared__ float sel_w[MAX_DECODE_T][8];
+    __shared__ int slot_of[256];               // routed expert -> active slot
     __shared__ uint32_t emask[256];
     __shared__ int wcnt[4];
     __shared__ int act_e[256 + 4];
     __shared__ uint32_t act_m[256 + 4];
     __shared__ int n_items_s[256 + 4 + 1];
-    __shared__ int n_pairs_s[256 + 4 + 1];
-    __shared__ int wtot_i[BN_SEL_THREADS / 64], wtot_p[BN_SEL_THREADS / 64];
+    __shared__ int wtot_i[BN_SEL_THREADS / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = p.T, K = p.K, E = p.E, S = p.S;
     if (tid < 256) emask[tid] = 0u;
@@ -118,6 +119,10 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
         }
         const bool ok = lane < K && e >= 0 && e < E;  // invalid given indices select nothing
         if (ok) atomicOr(&emask[e], 1u << wave);
+        if (lane < K) {
+            sel_e[wave][lane] = ok ? e : -1;
+            sel_w[wave][lane] = wi;
+        }
         // the token's weights per expert, added in selection order (a repeated
         // given index adds its weights: the expert counted twice)
         for (int k = 0; k < K; k++) {
@@ -140,53 +145,56 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
         const int pos = S + base + __popcll(bal & ((1ull << lane) - 1ull));
         act_e[pos] = tid;
         act_m[pos] = m;
+        slot_of[tid] = pos;
     }
     if (tid < S) {
         act_e[tid] = E + tid;
         act_m[tid] = (T >= 32) ? 0xFFFFFFFFu : ((1u << T) - 1u);
     }
     __syncthreads();
-    // per-slot work counts and their exclusive scans (8 waves x 64 slots)
+    // per-slot gate/up item counts and their exclusive scan (8 waves x 64 slots)
     const int c_slot = tid < n_act ? __popc(act_m[tid]) : 0;
     const int ci = (c_slot + 1) / 2;
-    const int inc_i = wave_incl_scan(ci), inc_p = wave_incl_scan(c_slot);
-    if (lane == 63) {
-        wtot_i[wave] = inc_i;
-        wtot_p[wave] = inc_p;
-    }
+    const int inc_i = wave_incl_scan(ci);
+    if (lane == 63) wtot_i[wave] = inc_i;
     __syncthreads();
-    int off_i = 0, off_p = 0, tot_i = 0, tot_p = 0;
+    int off_i = 0, tot_i = 0;
 #pragma unroll
     for (int w2 = 0; w2 < BN_SEL_THREADS / 64; w2++) {
         off_i += w2 < wave ? wtot_i[w2] : 0;
-        off_p += w2 < wave ? wtot_p[w2] : 0;
         tot_i += wtot_i[w2];
-        tot_p += wtot_p[w2];
     }
     if (tid < n_act) {
         n_items_s[tid] = off_i + inc_i - ci;
-        n_pairs_s[tid] = off_p + inc_p - c_slot;
         p.act_expert[tid] = act_e[tid];
         p.act_mask[tid] = act_m[tid];
     }
     if (tid == 0) {
         p.meta[0] = n_act;
         p.meta[1] = tot_i;
-        p.meta[2] = tot_p;
+        p.meta[2] = T * (K + S);
     }
     // gate/up items past the last are marked empty (slot -1), so the gate/up
     // kernel needs no count
     const int max_items = S * ((T + 1) / 2) + T * K;
     for (int i = tot_i + tid; i < max_items; i += BN_SEL_THREADS)
         reinterpret_cast<int4 *>(p.work)[i] = make_int4(-1, 0, 0, 0);
-    // down pairs past the last: token -1 (never accumulated), expert 0, h row 0
-    const int max_pairs = T * (K + S);
-    for (int i = tot_p + tid; i < max_pairs; i += BN_SEL_THREADS)
-        reinterpret_cast<int4 *>(p.pairs)[i] = make_int4(0, -1, 0, 0);
-    __syncthreads();
-    // one thread per (slot, token): the pair of a selected token sits at its
-    // rank among the slot's tokens; an even rank starts a gate/up item with
-    // the slot's next selected token (or none)
+    // down-projection list per token t: entries t * (K + S) + j = its shared
+    // slots, then its selections in top-k order {slot, t, weight bits, expert};
+    // an invalid given index gives token -1 (adds nothing)
+    for (int i = tid; i < T * (K + S); i += BN_SEL_THREADS) {
+        const int t = i / (K + S), j = i % (K + S);
+        int4 q;
+        if (j < S) {
+            q = make_int4(j, t, __float_as_int(1.f), E + j);
+        } else {
+            const int e = sel_e[t][j - S];
+            q = e < 0 ? make_int4(0, -1, 0, 0) : make_int4(slot_of[e], t, __float_as_int(sel_w[t][j - S]), e);
+        }
+        reinterpret_cast<int4 *>(p.pairs)[i] = q;
+    }
+    // one thread per (slot, token): an even rank among the slot's selected
+    // tokens starts a gate/up item with the slot's next selected token (or none)
     for (int i = tid; i < n_act * T; i += BN_SEL_THREADS) {
         const int slot = i / T, t = i % T;
         const int e = act_e[slot];
@@ -196,7 +204,6 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
         p.act_w[slot * T + t] = c;
         if (!on) continue;
         const int rank = __popc(mk & ((1u << t) - 1u));
-        reinterpret_cast<int4 *>(p.pairs)[n_pairs_s[slot] + rank] = make_int4(slot, t, __float_as_int(c), e);
         if ((rank & 1) == 0) {
             const uint32_t later = mk & ~((2u << t) - 1u);
             const int tb = later ? __builtin_ctz(later) : -1;
@@ -311,98 +318,85 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// bn_down: block = 8 waves over the same output rows (LPR_F lanes per row
-// group, 2 rows per group); wave w takes pairs w, w + 8, ... in batches.
-// y[t, row] = sum over pairs (slot, t) of coef * Wd_slot[row] . h[slot, t].
+// bn_down: y[t, r] = sum over token t's list (its shared slots, then its
+// selections in top-k order) of coef * (Wd[slot] row r . h[slot, t]).  One
+// block per ROWS output rows; wave t = token t, so each wave sums its own
+// token's terms in list order and writes its rows (no cross-wave reduction).
+// Lanes: LPR_F lanes per row (one unit each), row groups of BN_RR rows.
 // ---------------------------------------------------------------------------
-template <int FMT, int LPR_F, int TT>
-__global__ void __launch_bounds__(MOE_WAVE *BN_DWAVES) bn_down(DecodeParams p) {
+template <int FMT, int LPR_F>
+__global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p) {
     constexpr int UE = Unit<FMT>::E;
     constexpr int G = MOE_WAVE / LPR_F;  // row groups per wave
     constexpr int ROWS = G * BN_RR;      // rows per block
-    __shared__ float part[BN_DWAVES][TT][ROWS];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int HCH = LPR_F * UE / 4;  // 16-byte chunks of one h row (d_ff floats)
+    constexpr int HLD = (HCH + MOE_WAVE - 1) / MOE_WAVE;  // wave-wide loads per h row
+    // per wave: the h rows of one batch, each in the unit-swizzled chunk order
+    __shared__ uint4 hs[MAX_DECODE_T][BN_PB * HCH];
+    const int lane = threadIdx.x & 63;
+    const int t = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // the block has T waves
     const int grp = lane / LPR_F, sub = lane % LPR_F;
     const int D = p.D, F = p.F;
-    const int rb = blockIdx.x * ROWS;
-    const int r0 = rb + grp * BN_RR;
-    // the pairs list is padded to its maximum (entries past the last have
-    // token -1 and add nothing), so no count is read; every entry this wave
-    // will use is loaded before the first weight load
-    const int max_pairs = p.T * (p.K + p.S);
+    const int r0 = blockIdx.x * ROWS + grp * BN_RR;
+    const int KS = p.K + p.S;
+    // the token's list, loaded before any weight: lane j loads entry j, then
+    // every entry is read out as wave-uniform (scalar) values
+    const int4 mine = reinterpret_cast<const int4 *>(p.pairs)[t * KS + min(lane, KS - 1)];
     int4 ent[BN_MAXB * BN_PB];
 #pragma unroll
-    for (int i = 0; i < BN_MAXB * BN_PB; i++)
-        ent[i] = reinterpret_cast<const int4 *>(p.pairs)[min(wave + BN_DWAVES * i, max_pairs - 1)];
-    float acc[BN_RR][TT];
+    for (int i = 0; i < BN_MAXB * BN_PB; i++) {
+        const int j = min(i, KS - 1);
+        ent[i] = make_int4(__builtin_amdgcn_readlane(mine.x, j), __builtin_amdgcn_readlane(mine.y, j),
+                           __builtin_amdgcn_readlane(mine.z, j), __builtin_amdgcn_readlane(mine.w, j));
+    }
+    float acc[BN_RR];
 #pragma unroll
-    for (int r = 0; r < BN_RR; r++)
-#pragma unroll
-        for (int t = 0; t < TT; t++) acc[r][t] = 0.f;
+    for (int r = 0; r < BN_RR; r++) acc[r] = 0.f;
 #pragma unroll
     for (int bt = 0; bt < BN_MAXB; bt++) {
-        const int pb = wave + BN_DWAVES * BN_PB * bt;
-        if (pb >= max_pairs) break;
-        // one batch: BN_PB pairs (clamped to the last pair; extras weigh 0)
+        if (bt * BN_PB >= KS) break;
+        // one batch: BN_PB entries (past the list's end: weight 0)
         WUnit wd[BN_PB][BN_RR];
         XUnit<FMT> hv[BN_PB];
         float coef[BN_PB], ts[BN_PB];
-        int tok[BN_PB];
 #pragma unroll
         for (int q = 0; q < BN_PB; q++) {
-            const int pi = pb + BN_DWAVES * q;
-            const int4 pr = ent[bt * BN_PB + q];
-            coef[q] = pi < max_pairs ? __int_as_float(pr.z) : 0.f;
-            tok[q] = pi < max_pairs ? pr.y : -1;
+            const int j = bt * BN_PB + q;
+            const int4 pr = ent[j];
+            coef[q] = (j < KS && pr.y >= 0) ? __int_as_float(pr.z) : 0.f;
             const uint8_t *eb = p.experts + (size_t)pr.w * p.expert_bytes;
             Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, p.tscale ? p.tscale[3 * pr.w + 2] : 1.f};
             ts[q] = md.ts;
 #pragma unroll
             for (int r = 0; r < BN_RR; r++) wd[q][r] = load_unit<FMT>(md, min(r0 + r, D - 1), sub);
-            const float *hsrc = p.h + ((size_t)pr.x * p.T + max(pr.y, 0)) * F;
-#pragma unroll
-            for (int i = 0; i < UE / 4; i++) {
-                const float4 f = reinterpret_cast<const float4 *>(hsrc + sub * UE)[i];
-                hv[q].v[4 * i + 0] = f.x;
-                hv[q].v[4 * i + 1] = f.y;
-                hv[q].v[4 * i + 2] = f.z;
-                hv[q].v[4 * i + 3] = f.w;
-            }
         }
-        __builtin_amdgcn_sched_barrier(0);
+        // the batch's h rows: contiguous 16-byte loads (1 KB per wave-wide
+        // load) into this wave's LDS region, then per-lane units from LDS
+        uint4 hc[BN_PB][HLD];
 #pragma unroll
         for (int q = 0; q < BN_PB; q++) {
-            float sum = 0.f;
-            if (FMT == FMT_Q4_1) {
+            const uint4 *hsrc = reinterpret_cast<const uint4 *>(p.h + ((size_t)ent[bt * BN_PB + q].x * p.T + t) * F);
 #pragma unroll
-                for (int i = 0; i < UE; i++) sum += hv[q].v[i];
-            }
-            hv[q].sum = sum;
+            for (int i = 0; i < HLD; i++) hc[q][i] = hsrc[min(lane + MOE_WAVE * i, HCH - 1)];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the previous batch's LDS reads are done
 #pragma unroll
-            for (int r = 0; r < BN_RR; r++) {
-                const float v = coef[q] * unit_dot<FMT>(wd[q][r], hv[q], ts[q]);
+        for (int q = 0; q < BN_PB; q++)
 #pragma unroll
-                for (int t = 0; t < TT; t++) acc[r][t] += tok[q] == t ? v : 0.f;
-            }
+            for (int i = 0; i < HLD; i++)
+                if (lane + MOE_WAVE * i < HCH) hs[t][q * HCH + xs_slot<FMT>(lane + MOE_WAVE * i)] = hc[q][i];
+#pragma unroll
+        for (int q = 0; q < BN_PB; q++) {
+            load_x_lds<FMT>(hv[q], &hs[t][q * HCH], sub);
+#pragma unroll
+            for (int r = 0; r < BN_RR; r++) acc[r] += coef[q] * unit_dot<FMT>(wd[q][r], hv[q], ts[q]);
         }
     }
 #pragma unroll
-    for (int r = 0; r < BN_RR; r++)
-#pragma unroll
-        for (int t = 0; t < TT; t++) {
-            const float s = group_sum<LPR_F>(acc[r][t]);
-            if (sub == 0) part[wave][t][grp * BN_RR + r] = s;
-        }
-    __syncthreads();
-    // fixed-order sum of the waves' partials
-    for (int i = tid; i < TT * ROWS; i += MOE_WAVE * BN_DWAVES) {
-        const int t = i / ROWS, rr = i % ROWS;
-        if (t >= p.T || rb + rr >= D) continue;
-        float y = part[0][t][rr];
-#pragma unroll
-        for (int w = 1; w < BN_DWAVES; w++) y += part[w][t][rr];
-        p.y[(size_t)t * D + rb + rr] = y;
+    for (int r = 0; r < BN_RR; r++) {
+        const float y = group_sum<LPR_F>(acc[r]);
+        if (sub == 0 && r0 + r < D) p.y[(size_t)t * D + r0 + r] = y;
     }
 }
 
@@ -415,13 +409,7 @@ hipError_t launch_bn_fmt(const DecodeParams &p, hipStream_t st) {
     MOE_LAUNCH(2, (bn_gateup<FMT, UPLD, RG>), dim3((waves_g + BN_WAVES - 1) / BN_WAVES), dim3(MOE_WAVE * BN_WAVES),
                st, p);
     const int rows = (MOE_WAVE / LPR_F) * BN_RR;
-    const dim3 gd((p.D + rows - 1) / rows);
-    if (p.T <= 2)
-        MOE_LAUNCH(3, (bn_down<FMT, LPR_F, 2>), gd, dim3(MOE_WAVE * BN_DWAVES), st, p);
-    else if (p.T <= 4)
-        MOE_LAUNCH(3, (bn_down<FMT, LPR_F, 4>), gd, dim3(MOE_WAVE * BN_DWAVES), st, p);
-    else
-        MOE_LAUNCH(3, (bn_down<FMT, LPR_F, 8>), gd, dim3(MOE_WAVE * BN_DWAVES), st, p);
+    MOE_LAUNCH(3, (bn_down<FMT, LPR_F>), dim3((p.D + rows - 1) / rows), dim3(MOE_WAVE * p.T), st, p);
     return hipGetLastError();
 }
 
