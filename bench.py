@@ -101,12 +101,12 @@ PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_device.h", "moe_inte
 _FETCH_SCALE = 262144.0 / 131085.2  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
 _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE KiB
 COUNTER_TRAFFIC = {
-    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="0036dbe912b2656f",
-                                              fetch_bytes=round(3936.0 * _FETCH_SCALE * 1024),
+    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="f780e0e96407b4b4",
+                                              fetch_bytes=round(3940.7 * _FETCH_SCALE * 1024),
                                               write_bytes=round(12.7 * _WRITE_SCALE * 1024)),
-    ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="de119f1f3ef38691",
-                                             fetch_bytes=round(223913.3 * _FETCH_SCALE * 1024),
-                                             write_bytes=round(28684.6 * _WRITE_SCALE * 1024)),
+    ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="a96c28ed37160707",
+                                             fetch_bytes=round(227565.6 * _FETCH_SCALE * 1024),
+                                             write_bytes=round(28692.5 * _WRITE_SCALE * 1024)),
 }
 
 
