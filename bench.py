@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="stack_q4_1_b1",
-                    choices=["stack_q4_1_b1", "stack_nvfp4_b1", "stack_nvfp4_b8", "prefill_q4_1"])
+                    choices=["stack_q4_1_b1", "stack_nvfp4_b1", "stack_nvfp4_b8", "prefill_q4_1", "sweep_q4_1"])
     ap.add_argument("--layers", type=int, default=47)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=47, help="layers in the CPU baseline sample")
@@ -397,6 +397,76 @@ def bench_prefill(args):
     )
 
 
+def bench_sweep(args):
+    """Decode batch sweep: T tokens (fp32, N(0,1)) through 47 independent q4_1 layers, for
+    T = 1 .. 64, on the decode path (T <= 8: batch-1 or small-batch kernels) and on the
+    grouped-GEMM path (the prefill kernels, any T).  Each (T, path) is one HIP graph of
+    47 layer calls, replayed; every layer has its own weights, so the active experts
+    stream from HBM on every replay."""
+    from sparse_moe_decode_route_amd import binding as B
+    from sparse_moe_decode_route_amd import inputs as gen
+    dims = gen.LayerDims(2048, 512, wfmt="q4_1")
+    L = args.layers
+    devs, _ = build_stack(dims, 3, L, keep_host=False)
+    eb = B.packed_expert_bytes(dims)
+    rows = []
+    for T in (1, 2, 4, 8, 16, 32, 64):
+        x = gen.make_hidden(3, T, 2048, draw=900 + T, device="cuda")
+        for path in (("decode", "gemm") if T <= 8 else ("gemm",)):
+            prefill = path == "gemm"
+            ws = B.workspace(dims, T)
+            y = torch.empty((T, 2048), device="cuda")
+            # routing of every layer (for the distinct expert bytes)
+            union = 0
+            for d in devs:
+                _, idx, _ = B.layer_forward(d, x, ws=ws, y=y, prefill=prefill)
+                union += len(set(idx.cpu().numpy().reshape(-1).tolist())) + dims.n_shared
+
+            def step():
+                for d in devs:
+                    B.layer_forward(d, x, ws=ws, y=y, want_routing=False, prefill=prefill)
+
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                step()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            n = max(5, args.steps // 10)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            for _ in range(n):
+                g.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / n
+            del g
+            rows.append(dict(T=T, path=path, ms_per_step=round(ms, 4), us_per_layer=round(ms * 1000 / L, 2),
+                             layer_tok_s=round(L * T / (ms * 1e-3), 1),
+                             experts_per_layer=round(union / L, 1),
+                             expert_gbs=round(union * eb / (ms * 1e-3) / 1e9, 1)))
+            log(f"sweep T={T} {path}: {rows[-1]}")
+    best64 = max(r["layer_tok_s"] for r in rows if r["T"] == 64)
+    crossover = [r["T"] for r in rows if r["path"] == "gemm" and r["T"] <= 8 and
+                 r["layer_tok_s"] >= next(q["layer_tok_s"] for q in rows if q["T"] == r["T"] and q["path"] == "decode")]
+    return dict(
+        metric="MoE-layer decode tokens/s by batch size (q4_1, 47 independent layers)",
+        value=best64, unit="MoE-layer tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=next(r["ms_per_step"] for r in rows if r["T"] == 64), higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="f32", data="synthetic",
+        config=dict(workload="moe_decode_sweep_q4_1: d_model 2048, d_ff 512, 256 routed + 1 shared, top-6, q4_1 "
+                             "experts, 47 independent layers, T fp32 N(0,1) tokens per layer call, T = 1..64; "
+                             "value and ms_per_step at T = 64",
+                    global_batch=64, seq_len=1, parallelism="single-gpu", layers=L,
+                    gemm_path_not_slower_at_T=crossover, sweep=rows))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -413,6 +483,8 @@ def main():
         out = bench_stack(args, "q4_1", 1)
     elif args.workload == "stack_nvfp4_b1":
         out = bench_stack(args, "nvfp4", 1)
+    elif args.workload == "sweep_q4_1":
+        out = bench_sweep(args)
     elif args.workload == "stack_nvfp4_b8":
         out = bench_stack(args, "nvfp4", 8)
     else:

@@ -96,6 +96,15 @@ def test_prefill_q4_1_zipf_full_width():
     _prefill_case(host, dev, _x(192, dims.d_model, draw=3, bf16=True), "prefill q4_1 zipf T=192")
 
 
+@pytest.mark.parametrize("T", [1, 5, 8, 33, 64])
+def test_prefill_path_decode_batch_sizes(T):
+    # the grouped-GEMM path at the batch sizes of the decode sweep (1 .. 64
+    # fp32 tokens): a single tile per expert, mostly one or two rows each
+    dims = gen.WORKLOADS["c2_layer_q4_1"]["dims"]
+    host, dev = _layer(dims, cfg_id=3)
+    _prefill_case(host, dev, _x(T, dims.d_model, draw=40 + T, bf16=False), f"prefill path q4_1 T={T}")
+
+
 def test_prefill_nvfp4_full_width():
     dims = gen.WORKLOADS["c4_layer_nvfp4"]["dims"]
     host, dev = _layer(dims, cfg_id=4)
