@@ -52,6 +52,7 @@ def lib():
         L.orc_expert_bytes.argtypes = [ctypes.POINTER(OrcDims)]
         L.orc_layer_forward.restype = ctypes.c_int
         L.orc_stack_forward.restype = ctypes.c_int
+        L.orc_lm_head.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -225,3 +226,24 @@ def stack_forward(layers: Sequence, x0: np.ndarray):
     if rc != 0:
         raise ValueError("oracle rejected the stack")
     return y, y_trace, idx_trace
+
+
+# --------------------------------------------------------------------------- output layer
+
+def lm_head(wfmt_code: int, blob: np.ndarray, vocab: int, d: int, x: np.ndarray, s_t: float = 1.0,
+            rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Output-layer logits [T, n_rows] in fp64: x W^T over the listed rows of
+    the canonical [vocab, d] matrix (every row when rows is None)."""
+    buf = np.ascontiguousarray(blob, dtype=np.uint8).reshape(-1)
+    x = np.ascontiguousarray(x, dtype=np.float64).reshape(-1, d)
+    T = x.shape[0]
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32).reshape(-1)
+    n = vocab if r is None else r.size
+    out = np.zeros((T, n), dtype=np.float64)
+    rc = lib().orc_lm_head(ctypes.c_int(wfmt_code), _p(buf, ctypes.c_uint8), ctypes.c_int32(vocab),
+                           ctypes.c_int32(d), ctypes.c_double(s_t), ctypes.c_int32(T), _p(x, ctypes.c_double),
+                           None if r is None else _p(r, ctypes.c_int32), ctypes.c_int32(n),
+                           _p(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle: row index outside the vocabulary")
+    return out

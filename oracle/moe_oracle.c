@@ -369,3 +369,40 @@ int orc_stack_forward(const orc_dims *dm, int32_t n_layers, int32_t T, const dou
     free(w);
     return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* 4-bit output layer (lm_head)                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Output-layer logits: logits[t, i] = sum_k x[t, k] * W[rows[i], k] for the
+ * listed vocabulary rows (all rows 0..vocab-1 when rows is NULL and
+ * n_rows == vocab).  W is [vocab, d] in format fmt, canonical layout, with
+ * tensor scale s_t (NVFP4).  "Recursive Flint 40B-A2.5B" (orcarouter.ai
+ * blog), section "The quantisation recipe is the most transferable part":
+ * the output layer ships in 4 bits, since with 2.5 B active parameters it
+ * is a large part of the weights every decoded token reads.  Each row is
+ * decoded exactly into fp64 and summed over k in order.  logits is
+ * [T, n_rows].  Returns -1 on a row index outside [0, vocab).
+ */
+int orc_lm_head(int fmt, const uint8_t *w, int32_t vocab, int32_t d, double s_t, int32_t T, const double *x,
+                const int32_t *rows, int32_t n_rows, double *logits) {
+    double *wr = (double *)malloc(sizeof(double) * (size_t)d);
+    int rc = 0;
+    for (int i = 0; i < n_rows && rc == 0; i++) {
+        int r = rows ? rows[i] : i;
+        if (r < 0 || r >= vocab) {
+            rc = -1;
+            break;
+        }
+        orc_dequant_row(fmt, w, vocab, d, r, s_t, wr);
+        for (int t = 0; t < T; t++) {
+            const double *xt = x + (size_t)t * d;
+            double acc = 0.0;
+            for (int k = 0; k < d; k++) acc += xt[k] * wr[k];
+            logits[(size_t)t * n_rows + i] = acc;
+        }
+    }
+    free(wr);
+    return rc;
+}

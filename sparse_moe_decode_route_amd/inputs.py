@@ -12,6 +12,9 @@ Workload recipe (the pages print no layer values, so every input is synthetic):
 * expert e (0 <= e < n_routed routed, then the shared expert(s)) holds three
   matrices in the order gate [d_ff, d_model], up [d_ff, d_model],
   down [d_model, d_ff]; quantisation blocks run along the input dimension;
+* the output layer (lm_head) W [vocab, d_model] ~ N(0, 0.02), encoded in the
+  same block formats as the experts (blocks along d_model); its input is a
+  final-normed hidden state ~ N(0, 1);
 * a skewed router prior (prefill workload) adds bias_e = ln(Zipf(s) pmf at the
   expert's rank), ranks given by a seeded permutation.
 
@@ -28,7 +31,7 @@ Canonical byte layouts (what the generator writes and what both sides read):
 
 Random streams: numpy PCG64 seeded with SeedSequence([0xF1147, cfg_id, layer,
 tensor_id]); tensor_id 0 = router, 1 + 3*e + m = expert e matrix m,
-9998 = Zipf permutation, 9999 + draw = hidden states.  A device-side variant
+9997 = output layer, 9998 = Zipf permutation, 9999 + draw = hidden states.  A device-side variant
 (``device="cuda"``) draws the same shapes with torch's Philox generator seeded
 from the same SeedSequence, for workloads too large to draw on the host; its
 values differ from the host stream but follow the same recipe.
@@ -44,6 +47,7 @@ import torch
 WFMT_CODES = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 ROOT_SEED = 0xF1147
 TID_ROUTER = 0
+TID_LM_HEAD = 9997
 TID_ZIPF = 9998
 TID_HIDDEN = 9999
 
@@ -254,6 +258,18 @@ def make_layer(dims: LayerDims, cfg_id: int, layer: int = 0, zipf_s: Optional[fl
     return Layer(dims, router.contiguous(), bias, experts, tscale)
 
 
+def make_lm_head(vocab: int, d_model: int, wfmt: str, cfg_id: int, device=None):
+    """Canonical bytes of the output layer [vocab, d_model] and its tensor scale
+    (fp32 [1], NVFP4) or None.  Drawn in slabs of rows so that a full
+    vocabulary does not hold a second fp32 copy of the matrix."""
+    w = _normal((vocab, d_model), 0.02, cfg_id, 0, TID_LM_HEAD, device)
+    if wfmt == "nvfp4":
+        return encode_nvfp4(w)
+    slab = 16384
+    parts = [encode_matrix(w[r:r + slab], wfmt)[0] for r in range(0, vocab, slab)]
+    return torch.cat(parts), None
+
+
 def make_hidden(cfg_id: int, n_tokens: int, d_model: int, layer: int = 0, draw: int = 0,
                 device=None) -> torch.Tensor:
     """Hidden states ~ N(0, 1), fp32 [n_tokens, d_model]."""
@@ -278,3 +294,9 @@ WORKLOADS = {
     # prefill: 4096 bf16 tokens, Zipf(1.1) router prior, q4_1
     "c5_prefill_q4_1": dict(cfg_id=5, dims=LayerDims(2048, 512, wfmt="q4_1"), tokens=4096, zipf_s=1.1),
 }
+
+# Output layer at decode: the vocabulary is not on the pages; 0.3 B output
+# parameters over d_model 2048 gives 146,484 rows (a reading, not a figure
+# from the pages).  Not a multiple of any tile, so the last rows are ragged.
+LM_HEAD_VOCAB = 146_484
+LM_HEAD_CFG = 6

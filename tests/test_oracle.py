@@ -446,3 +446,68 @@ def test_experts_given_constant_closed_form(orc):
         return cd * 32 * (g / (1 + math.exp(-g)) * u)
 
     np.testing.assert_allclose(y[0], np.full(64, out(8) + 0.75 * out(7) - 0.5 * out(2)), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------- output layer (lm_head)
+
+def test_lm_head_q4_1_integer_matrix_is_exact_integer_product(orc):
+    # an integer matrix in [-8, 7] with both ends in every 32-block encodes with
+    # d = 1, m = -8 and exact codes, so the logits are the integer product
+    rng = np.random.default_rng(5)
+    V, D, T = 37, 96, 3
+    w = rng.integers(-8, 8, size=(V, D))
+    for b in range(D // 32):
+        w[:, 32 * b + rng.integers(0, 16)] = -8
+        w[:, 32 * b + 16 + rng.integers(0, 16)] = 7
+    x = rng.integers(-4, 5, size=(T, D))
+    blob = gen.encode_q4_1(torch.from_numpy(w.astype(np.float32))).reshape(-1).numpy()
+    got = orc.lm_head(1, blob, V, D, x.astype(np.float64))
+    assert np.array_equal(got, (x @ w.T).astype(np.float64))
+    rows = np.array([36, 0, 17, 17])
+    sub = orc.lm_head(1, blob, V, D, x.astype(np.float64), rows=rows)
+    assert np.array_equal(sub, got[:, rows])
+    with pytest.raises(ValueError):
+        orc.lm_head(1, blob, V, D, x.astype(np.float64), rows=np.array([V]))
+
+
+def test_lm_head_nvfp4_grid_matrix_is_exact_scaled_product(orc):
+    # values on the E2M1 grid with a +-6 in every 16-block: the block scale is
+    # e4m3(448) and the codes are exact, so every decoded weight is
+    # w * 448 * s_t with s_t the stored fp32 tensor scale
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6])
+    rng = np.random.default_rng(6)
+    V, D, T = 29, 64, 2
+    w = rng.choice(grid, size=(V, D))
+    for b in range(D // 16):
+        w[:, 16 * b + rng.integers(0, 16)] = rng.choice([6.0, -6.0])
+    x = rng.integers(-8, 9, size=(T, D)) / 4.0
+    blob, s_t = gen.encode_nvfp4(torch.from_numpy(w.astype(np.float32)))
+    s_t = float(s_t[0])
+    got = orc.lm_head(2, blob.numpy(), V, D, x, s_t=s_t)
+    want = (x @ w.T) * 448.0 * s_t
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("wfmt", ["bf16", "q4_1", "nvfp4"])
+def test_lm_head_one_hot_token_reads_one_column(orc, wfmt):
+    # x = e_k gives column k of the decoded matrix (orientation: rows are the
+    # vocabulary, columns the hidden size)
+    V, D = 50, 64
+    blob, s_t = gen.make_lm_head(V, D, wfmt, cfg_id=31)
+    s = 1.0 if s_t is None else float(s_t[0])
+    dec = orc.dequant_matrix(gen.WFMT_CODES[wfmt], blob.numpy(), V, D, s)
+    ks = [0, 31, 32, 63]
+    x = np.zeros((len(ks), D))
+    x[np.arange(len(ks)), ks] = 1.0
+    got = orc.lm_head(gen.WFMT_CODES[wfmt], blob.numpy(), V, D, x, s_t=s)
+    assert np.array_equal(got, dec[:, ks].T)
+
+
+def test_lm_head_is_linear_in_the_token(orc):
+    V, D = 40, 128
+    blob, s_t = gen.make_lm_head(V, D, "nvfp4", cfg_id=32)
+    s = float(s_t[0])
+    rng = np.random.default_rng(7)
+    x1, x2 = rng.standard_normal((2, D))
+    l1, l2, l12 = (orc.lm_head(2, blob.numpy(), V, D, v[None], s_t=s)[0] for v in (x1, x2, 0.5 * x1 - 3.0 * x2))
+    assert np.allclose(l12, 0.5 * l1 - 3.0 * l2, rtol=0, atol=1e-12)
