@@ -35,8 +35,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="stack_q4_1_b1",
-                    choices=["stack_q4_1_b1", "stack_nvfp4_b1", "stack_nvfp4_b8", "prefill_q4_1", "sweep_q4_1"])
+                    choices=["stack_q4_1_b1", "stack_nvfp4_b1", "stack_nvfp4_b8", "prefill_q4_1", "sweep_q4_1",
+                             "lm_head_q4_1", "lm_head_nvfp4", "lm_head_bf16"])
     ap.add_argument("--layers", type=int, default=47)
+    ap.add_argument("--lm-tokens", type=int, default=1, help="tokens per output-layer call (1..8)")
+    ap.add_argument("--lm-cpu-rows", type=int, default=146_484, help="vocabulary rows in the CPU baseline sample")
+    ap.add_argument("--lm-cpu-seconds", type=float, default=10.0, help="minimum CPU baseline time (whole passes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=47, help="layers in the CPU baseline sample")
     ap.add_argument("--cpu-tokens", type=int, default=8, help="tokens in the CPU baseline sample")
@@ -92,6 +96,7 @@ def source_digest(files=("moe_decode_b1.hip", "moe_decode.hip", "moe_device.h", 
 
 
 PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_device.h", "moe_internal.h")
+LM_HEAD_SOURCES = ("moe_lm_head.hip", "moe_device.h", "moe_internal.h")
 
 
 # HBM traffic per launch read from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
@@ -107,6 +112,9 @@ COUNTER_TRAFFIC = {
     ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="a96c28ed37160707",
                                              fetch_bytes=round(227565.6 * _FETCH_SCALE * 1024),
                                              write_bytes=round(28692.5 * _WRITE_SCALE * 1024)),
+    ("lm_head_q4_1_t1", "lm_head_kernel"): dict(source_digest="513bb84d9127ca42",
+                                                fetch_bytes=round(91655.9 * _FETCH_SCALE * 1024),
+                                                write_bytes=round(572.2 * _WRITE_SCALE * 1024)),
 }
 
 
@@ -467,6 +475,102 @@ def bench_sweep(args):
                     gemm_path_not_slower_at_T=crossover, sweep=rows))
 
 
+def bench_lm_head(args, wfmt: str):
+    """The output layer at decode: T tokens (fp32, N(0,1)) through W [146,484, 2048].
+
+    One step is one moe_lm_head call.  The weights exist in n_copies copies
+    (together larger than the chip's 256 MB last-level cache) and consecutive
+    calls rotate through them, so every call streams its matrix from HBM."""
+    from sparse_moe_decode_route_amd import binding as B
+    from sparse_moe_decode_route_amd import inputs as gen
+    import oracle
+    V, D, T = gen.LM_HEAD_VOCAB, 2048, args.lm_tokens
+    wbytes = B.lm_head_bytes(V, D, wfmt)
+    n_copies = max(2, -(-1024 * 2 ** 20 // wbytes))
+    t0 = time.time()
+    blob, s_t = gen.make_lm_head(V, D, wfmt, cfg_id=gen.LM_HEAD_CFG, device="cuda")
+    heads = [B.upload_lm_head(V, D, wfmt, blob, s_t, "cuda") for _ in range(n_copies)]
+    torch.cuda.synchronize()
+    log(f"output layer {wfmt}: {n_copies} copies of {wbytes / 1e6:.1f} MB ready in {time.time() - t0:.1f}s")
+    x = gen.make_hidden(gen.LM_HEAD_CFG, T, D, draw=500, device="cuda")
+    out = torch.empty((T, V), dtype=torch.float32, device="cuda")
+    ref = B.lm_head(heads[0], x)
+    torch.cuda.synchronize()
+
+    per_graph = n_copies * max(1, -(-24 // n_copies))  # >= 24 calls per replay: launch cost amortised
+
+    def step_all():
+        for i in range(per_graph):
+            B.lm_head(heads[i % n_copies], x, logits=out)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step_all()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_all()
+    reps = max(1, -(-args.steps // per_graph))
+    wreps = max(1, -(-args.warmup // per_graph))
+    for _ in range(wreps):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    steps = reps * per_graph
+    ms = ev0.elapsed_time(ev1) / steps
+    graph_matches_eager = bool(torch.equal(out, ref))
+    # per-launch dispatch durations (events on the launch stream), rotating copies
+    n_timed = max(1, min(args.timed_calls, 40))
+    kus = [B.lm_head_timed(heads[i % n_copies], x, logits=out)[1] for i in range(n_timed)]
+    us = float(np.mean(kus))
+    algo = wbytes + T * D * 4 + T * V * 4 + (4 if wfmt == "nvfp4" else 0)
+    ach = algo / (us * 1e-6) / 1e9
+    kname = "lm_head_kernel"
+    tr = COUNTER_TRAFFIC.get((f"lm_head_{wfmt}_t{T}", kname))
+    traffic = None
+    if tr is not None and tr["source_digest"] == source_digest(LM_HEAD_SOURCES):
+        traffic = tr["fetch_bytes"] + tr["write_bytes"]
+    cpu = None
+    if not args.no_cpu:
+        hb = blob.cpu().numpy()
+        xs = x.cpu().double().numpy()
+        rows = min(V, max(1, args.lm_cpu_rows))
+        st = 1.0 if s_t is None else float(s_t.reshape(-1)[0])
+        passes, c0 = 0, time.time()
+        while passes == 0 or time.time() - c0 < args.lm_cpu_seconds:
+            oracle.lm_head(gen.WFMT_CODES[wfmt], hb, V, D, xs, s_t=st, rows=np.arange(rows))
+            passes += 1
+        dt = (time.time() - c0) / passes
+        cpu = dict(value=round(T / (dt * V / rows), 3), unit="tok/s", cores=1, kind="oracle",
+                   sample=f"{passes} pass(es) over {rows} of {V} vocabulary rows for {T} token(s), fp64 C "
+                          f"oracle, one thread, {dt:.2f}s per pass; scaled to the full vocabulary")
+    return dict(
+        metric=f"output-layer (lm_head) decode tokens/s, {wfmt} weights",
+        value=round(T / (ms * 1e-3), 1), unit="tok/s", n_gpus=1, steps=steps, warmup=wreps * per_graph,
+        ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+        data="synthetic",
+        config=dict(workload=f"lm_head_{wfmt}: vocab {V} x d_model {D} {wfmt} output layer, {T} fp32 N(0,1) "
+                             f"token(s) per call, weights N(0, 0.02)",
+                    global_batch=T, seq_len=1, parallelism="single-gpu", weight_bytes=wbytes,
+                    weight_copies=n_copies,
+                    timing=f"HIP graph of {per_graph} calls rotating over the weight copies, replayed",
+                    graph_matches_eager=graph_matches_eager),
+        roofline=dict(bound="hbm", kernel=kname, achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic, algo_bytes_per_launch=algo,
+                      us_per_launch=round(us, 3),
+                      timing=f"HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream, mean of "
+                             f"{n_timed} calls over rotating weight copies"),
+        cpu_baseline=cpu,
+    )
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -485,6 +589,8 @@ def main():
         out = bench_stack(args, "nvfp4", 1)
     elif args.workload == "sweep_q4_1":
         out = bench_sweep(args)
+    elif args.workload.startswith("lm_head_"):
+        out = bench_lm_head(args, args.workload[len("lm_head_"):])
     elif args.workload == "stack_nvfp4_b8":
         out = bench_stack(args, "nvfp4", 8)
     else:

@@ -211,6 +211,54 @@ moe_status moe_layer_forward_prefill_timed(const moe_dims *dims, const moe_layer
                                            float *kernel_us, int32_t *n_kernels, char *names, size_t names_cap,
                                            void *stream);
 
+/*
+ * Output layer (lm_head) at decode.  "Recursive Flint 40B-A2.5B"
+ * (orcarouter.ai blog), section "The quantisation recipe is the most
+ * transferable part": the output layer is quantised to 4 bits, since with
+ * 2.5 B active parameters it is a large share of the weights every decoded
+ * token reads.  For each token t and vocabulary row v:
+ *   logits[t, v] = sum_k x[t, k] * W[v, k]     (fp32 accumulation)
+ * W is [vocab, d_model] in the formats of the experts (moe_wfmt; quantisation
+ * blocks along d_model): canonical layout as for one expert matrix, device
+ * layout as written by moe_lm_head_repack.  Limits: 1 <= vocab <=
+ * MOE_LM_HEAD_MAX_VOCAB; d_model a multiple of 32 in [32,
+ * MOE_LM_HEAD_MAX_D]; 1 <= n_tokens <= MOE_LM_HEAD_MAX_TOKENS.
+ */
+#define MOE_LM_HEAD_MAX_VOCAB 16777216
+#define MOE_LM_HEAD_MAX_D 4096
+#define MOE_LM_HEAD_MAX_TOKENS 8
+
+/* (host) bytes of W (canonical or device layout); 0 if the shape or format
+   is invalid. */
+size_t moe_lm_head_bytes(int32_t vocab, int32_t d_model, int32_t wfmt);
+
+/* Convert W from the canonical layout to the device layout (q4_1: code plane
+   [vocab, d_model/2] then scale plane [vocab, d_model/32] of {fp16 d, fp16 m};
+   bf16 and NVFP4: a copy).  canonical and packed are device buffers of
+   moe_lm_head_bytes() bytes and must not overlap. */
+moe_status moe_lm_head_repack(int32_t vocab, int32_t d_model, int32_t wfmt, const void *canonical, void *packed,
+                              void *stream);
+
+/*
+ *   weights      W in the device layout
+ *   tensor_scale NVFP4: fp32 [1] (4-byte aligned), the matrix's tensor scale;
+ *                otherwise ignored (may be NULL)
+ *   x            [n_tokens, d_model], fp32 (act = MOE_ACT_F32) or bf16
+ *   logits       out fp32 [n_tokens, vocab]; must not overlap an input
+ * Every row of W is read once per call (tokens beyond four per pass re-read
+ * it, mostly from L2).  Each logit is a fixed-order sum.
+ */
+moe_status moe_lm_head(int32_t vocab, int32_t d_model, int32_t wfmt, const void *weights, const float *tensor_scale,
+                       const void *x, int32_t act, int32_t n_tokens, float *logits, void *stream);
+
+/* Measurement variant of moe_lm_head: the same kernel launched with a
+   start/stop event pair on its dispatch; *kernel_us (host) receives its
+   duration in microseconds.  Blocks the calling thread until it is done;
+   not for use under stream capture. */
+moe_status moe_lm_head_timed(int32_t vocab, int32_t d_model, int32_t wfmt, const void *weights,
+                             const float *tensor_scale, const void *x, int32_t act, int32_t n_tokens, float *logits,
+                             float *kernel_us, void *stream);
+
 /* (host) static description of a status code. */
 const char *moe_status_string(moe_status s);
 

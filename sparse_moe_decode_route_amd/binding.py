@@ -23,7 +23,8 @@ ACT_F32, ACT_BF16 = 0, 1
 ENTRY_POINTS = (
     "moe_packed_expert_bytes", "moe_workspace_size", "moe_repack_weights", "moe_route_topk",
     "moe_expert_ffn_q4", "moe_layer_forward", "moe_layer_forward_prefill", "moe_stack_decode",
-    "moe_stack_decode_timed", "moe_layer_forward_prefill_timed", "moe_status_string", "moe_last_error",
+    "moe_stack_decode_timed", "moe_layer_forward_prefill_timed", "moe_lm_head_bytes", "moe_lm_head_repack",
+    "moe_lm_head", "moe_lm_head_timed", "moe_status_string", "moe_last_error",
 )
 
 
@@ -79,6 +80,14 @@ def lib():
         L.moe_layer_forward_prefill_timed.argtypes = [pd, ctypes.POINTER(CLayerWeights), vp, i32, i32, vp, vp, sz,
                                                       ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32),
                                                       ctypes.c_char_p, sz, vp]
+        L.moe_lm_head_bytes.restype = sz
+        L.moe_lm_head_bytes.argtypes = [i32, i32, i32]
+        L.moe_lm_head_repack.restype = ctypes.c_int
+        L.moe_lm_head_repack.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.moe_lm_head.restype = ctypes.c_int
+        L.moe_lm_head.argtypes = [i32, i32, i32, vp, vp, vp, i32, i32, vp, vp]
+        L.moe_lm_head_timed.restype = ctypes.c_int
+        L.moe_lm_head_timed.argtypes = [i32, i32, i32, vp, vp, vp, i32, i32, vp, ctypes.POINTER(ctypes.c_float), vp]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_last_error.restype = ctypes.c_char_p
@@ -277,3 +286,60 @@ def layer_forward_prefill_timed(layer: DeviceLayer, x: torch.Tensor, ws: Optiona
                                                  _stream(stream)))
     keys = names.value.decode().split(";")
     return y, {keys[k]: float(us[k]) for k in range(nk.value)}
+
+
+# --------------------------------------------------------------------------- output layer (lm_head)
+
+@dataclasses.dataclass
+class LmHead:
+    """Output-layer weights on the device: W [vocab, d_model] in the device layout."""
+    vocab: int
+    d_model: int
+    wfmt: str
+    weights: torch.Tensor                 # uint8, device layout
+    tensor_scale: Optional[torch.Tensor]  # fp32 [1] (NVFP4) or None
+
+    @property
+    def wfmt_code(self) -> int:
+        return gen.WFMT_CODES[self.wfmt]
+
+
+def lm_head_bytes(vocab: int, d_model: int, wfmt: str) -> int:
+    return int(lib().moe_lm_head_bytes(vocab, d_model, gen.WFMT_CODES[wfmt]))
+
+
+def lm_head_repack(vocab: int, d_model: int, wfmt: str, canonical: torch.Tensor, packed: torch.Tensor, stream=None):
+    _check(lib().moe_lm_head_repack(vocab, d_model, gen.WFMT_CODES[wfmt], _ptr(canonical), _ptr(packed),
+                                    _stream(stream)))
+
+
+def upload_lm_head(vocab: int, d_model: int, wfmt: str, canonical: torch.Tensor, tensor_scale: Optional[torch.Tensor],
+                   device="cuda") -> LmHead:
+    """Copy canonical output-layer bytes to the device and convert them to the device layout."""
+    canon = canonical.to(device)
+    packed = torch.empty_like(canon)
+    lm_head_repack(vocab, d_model, wfmt, canon, packed)
+    torch.cuda.current_stream().synchronize()
+    del canon
+    ts = None if tensor_scale is None else tensor_scale.to(device=device, dtype=torch.float32).reshape(1).contiguous()
+    return LmHead(vocab, d_model, wfmt, packed, ts)
+
+
+def lm_head(head: LmHead, x: torch.Tensor, logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_lm_head: fp32 logits [T, vocab] of the tokens x [T, d_model] (fp32 or bf16)."""
+    T = x.shape[0]
+    logits = logits if logits is not None else torch.empty((T, head.vocab), dtype=torch.float32, device=x.device)
+    _check(lib().moe_lm_head(head.vocab, head.d_model, head.wfmt_code, _ptr(head.weights), _ptr(head.tensor_scale),
+                             _ptr(x), _act(x), T, _ptr(logits), _stream(stream)))
+    return logits
+
+
+def lm_head_timed(head: LmHead, x: torch.Tensor, logits: Optional[torch.Tensor] = None, stream=None):
+    """moe_lm_head_timed: (logits, kernel microseconds).  Synchronises the stream."""
+    T = x.shape[0]
+    logits = logits if logits is not None else torch.empty((T, head.vocab), dtype=torch.float32, device=x.device)
+    us = ctypes.c_float(0.0)
+    _check(lib().moe_lm_head_timed(head.vocab, head.d_model, head.wfmt_code, _ptr(head.weights),
+                                   _ptr(head.tensor_scale), _ptr(x), _act(x), T, _ptr(logits), ctypes.byref(us),
+                                   _stream(stream)))
+    return logits, float(us.value)

@@ -521,6 +521,110 @@ moe_status moe_layer_forward_prefill_timed(const moe_dims *d, const moe_layer_we
     return s == MOE_OK ? ok() : s;
 }
 
+// ---- output layer (lm_head) ----
+
+static bool lm_head_fmt_ok(int32_t f) { return f == MOE_W_BF16 || f == MOE_W_Q4_1 || f == MOE_W_NVFP4; }
+
+size_t moe_lm_head_bytes(int32_t vocab, int32_t d_model, int32_t wfmt) {
+    if (vocab < 1 || vocab > MOE_LM_HEAD_MAX_VOCAB || d_model < 32 || d_model > MOE_LM_HEAD_MAX_D || d_model % 32 ||
+        !lm_head_fmt_ok(wfmt))
+        return 0;
+    return mat_bytes(wfmt, (size_t)vocab, (size_t)d_model);
+}
+
+static moe_status lm_head_check_shape(int32_t vocab, int32_t d_model, int32_t wfmt) {
+    if (!lm_head_fmt_ok(wfmt)) return fail(MOE_ERR_UNSUPPORTED, "unknown weight format " + std::to_string(wfmt));
+    if (vocab < 1 || vocab > MOE_LM_HEAD_MAX_VOCAB)
+        return fail(MOE_ERR_INVALID_ARG, "vocab must be in [1, " + std::to_string(MOE_LM_HEAD_MAX_VOCAB) + "]");
+    if (d_model < 32 || d_model > MOE_LM_HEAD_MAX_D || d_model % 32)
+        return fail(MOE_ERR_INVALID_ARG,
+                    "d_model must be a multiple of 32 in [32, " + std::to_string(MOE_LM_HEAD_MAX_D) + "]");
+    return MOE_OK;
+}
+
+moe_status moe_lm_head_repack(int32_t vocab, int32_t d_model, int32_t wfmt, const void *canonical, void *packed,
+                              void *stream) {
+    MOE_TRY(lm_head_check_shape(vocab, d_model, wfmt));
+    MOE_TRY(check_ptr(canonical, "canonical"));
+    MOE_TRY(check_ptr(packed, "packed"));
+    const size_t nb = moe_lm_head_bytes(vocab, d_model, wfmt);
+    const char *c0 = static_cast<const char *>(canonical), *p0 = static_cast<const char *>(packed);
+    if (c0 < p0 + nb && p0 < c0 + nb) return fail(MOE_ERR_INVALID_ARG, "canonical and packed overlap");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (wfmt != MOE_W_Q4_1)
+        return hip_status(hipMemcpyAsync(packed, canonical, nb, hipMemcpyDeviceToDevice, st), "lm_head copy");
+    return hip_status(moe::launch_repack_q4_1_matrix(static_cast<const uint8_t *>(canonical),
+                                                     static_cast<uint8_t *>(packed), vocab, d_model, st),
+                      "lm_head repack launch");
+}
+
+static moe_status lm_head_args(int32_t vocab, int32_t d_model, int32_t wfmt, const void *weights,
+                               const float *tensor_scale, const void *x, int32_t act, int32_t n_tokens,
+                               float *logits, moe::LmHeadArgs *a) {
+    MOE_TRY(lm_head_check_shape(vocab, d_model, wfmt));
+    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "unknown activation type " + std::to_string(act));
+    if (n_tokens < 1 || n_tokens > MOE_LM_HEAD_MAX_TOKENS)
+        return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, " + std::to_string(MOE_LM_HEAD_MAX_TOKENS) + "]");
+    MOE_TRY(check_ptr(weights, "weights"));
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(logits, "logits"));
+    if (wfmt == MOE_W_NVFP4) {
+        if (!tensor_scale) return fail(MOE_ERR_INVALID_ARG, "tensor_scale is NULL (NVFP4)");
+        if (reinterpret_cast<uintptr_t>(tensor_scale) & 3u)
+            return fail(MOE_ERR_ALIGNMENT, "tensor_scale is not 4-byte aligned");
+    }
+    const size_t out_bytes = (size_t)n_tokens * vocab * 4, x_bytes = (size_t)n_tokens * d_model * (act ? 2 : 4);
+    const size_t w_bytes = moe_lm_head_bytes(vocab, d_model, wfmt);
+    auto overlaps = [&](const void *p, size_t n) {
+        const char *a0 = reinterpret_cast<const char *>(logits), *b0 = static_cast<const char *>(p);
+        return a0 < b0 + n && b0 < a0 + out_bytes;
+    };
+    if (overlaps(x, x_bytes) || overlaps(weights, w_bytes) || (tensor_scale && overlaps(tensor_scale, 4)))
+        return fail(MOE_ERR_INVALID_ARG, "logits overlaps an input");
+    a->w = static_cast<const uint8_t *>(weights);
+    a->tscale = tensor_scale;
+    a->x = x;
+    a->logits = logits;
+    a->V = vocab;
+    a->D = d_model;
+    a->T = n_tokens;
+    a->act = act;
+    a->fmt = wfmt;
+    return MOE_OK;
+}
+
+moe_status moe_lm_head(int32_t vocab, int32_t d_model, int32_t wfmt, const void *weights, const float *tensor_scale,
+                       const void *x, int32_t act, int32_t n_tokens, float *logits, void *stream) {
+    moe::LmHeadArgs a{};
+    MOE_TRY(lm_head_args(vocab, d_model, wfmt, weights, tensor_scale, x, act, n_tokens, logits, &a));
+    return hip_status(moe::launch_lm_head(a, static_cast<hipStream_t>(stream)), "lm_head launch");
+}
+
+moe_status moe_lm_head_timed(int32_t vocab, int32_t d_model, int32_t wfmt, const void *weights,
+                             const float *tensor_scale, const void *x, int32_t act, int32_t n_tokens, float *logits,
+                             float *kernel_us, void *stream) {
+    if (!kernel_us) return fail(MOE_ERR_INVALID_ARG, "kernel_us is NULL");
+    moe::LmHeadArgs a{};
+    MOE_TRY(lm_head_args(vocab, d_model, wfmt, weights, tensor_scale, x, act, n_tokens, logits, &a));
+    if (hipEventCreate(&a.ev0) != hipSuccess) return fail(MOE_ERR_HIP, "hipEventCreate failed");
+    if (hipEventCreate(&a.ev1) != hipSuccess) {
+        (void)hipEventDestroy(a.ev0);
+        return fail(MOE_ERR_HIP, "hipEventCreate failed");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    moe_status s = hip_status(moe::launch_lm_head(a, st), "lm_head launch");
+    if (s == MOE_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(MOE_ERR_HIP, "stream synchronize failed");
+    if (s == MOE_OK) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, a.ev0, a.ev1) != hipSuccess) s = fail(MOE_ERR_HIP, "hipEventElapsedTime failed");
+        *kernel_us = ms * 1e3f;
+    }
+    (void)hipEventDestroy(a.ev0);
+    (void)hipEventDestroy(a.ev1);
+    return s == MOE_OK ? ok() : s;
+}
+
 const char *moe_status_string(moe_status s) {
     switch (s) {
     case MOE_OK: return "ok";

@@ -64,6 +64,21 @@ struct DecodeParams {
 // Kernel slots of one layer, per decode path (names as reported by the timing entry point).
 constexpr int MAX_KERNEL_SLOTS = 4;
 
+// Output layer (lm_head): logits [T, V] = x [T, D] . W [V, D]^T.
+struct LmHeadArgs {
+    const uint8_t *w;       // device layout of W
+    const float *tscale;    // NVFP4 tensor scale (1 float), else unused
+    const void *x;          // [T, D] fp32 (act 0) or bf16 (act 1)
+    float *logits;          // [T, V]
+    int V, D, T, act, fmt;
+    int n_tiles, n_groups;  // set by the launcher
+    hipEvent_t ev0, ev1;    // optional dispatch timing pair
+};
+hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st);
+// q4_1 canonical [rows, k] matrix -> code plane [rows, k/2] + scale plane [rows, k/32]
+hipError_t launch_repack_q4_1_matrix(const uint8_t *canonical, uint8_t *packed, long long rows, int k,
+                                     hipStream_t st);
+
 hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
 // Batch-1 path (three kernels per layer); hipErrorNotSupported if the shape
 // is outside what it was built for (the caller then takes launch_decode).

@@ -4,6 +4,7 @@
 // coalesced load.  Same bytes, same count.
 #include <hip/hip_runtime.h>
 
+#include "moe_internal.h"
 #include "moe_prefill.h"
 
 namespace moe {
@@ -39,6 +40,22 @@ hipError_t launch_repack_q4_1(const uint8_t *canonical, uint8_t *packed, int n_e
     const long long total = bpe * n_experts;
     const long long grid = (total + 255) / 256;
     hipLaunchKernelGGL(repack_q4_1_kernel, dim3((unsigned)grid), dim3(256), 0, st, canonical, packed, total, bpe, D, F);
+    return hipGetLastError();
+}
+
+__global__ void repack_q4_1_matrix_kernel(const uint8_t *canonical, uint8_t *packed, long long n_blocks) {
+    const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= n_blocks) return;
+    const uint32_t *s32 = (const uint32_t *)(canonical + b * 20);
+    ((uint4 *)packed)[b] = make_uint4(s32[1], s32[2], s32[3], s32[4]);
+    ((uint32_t *)(packed + n_blocks * 16))[b] = s32[0];
+}
+
+hipError_t launch_repack_q4_1_matrix(const uint8_t *canonical, uint8_t *packed, long long rows, int k,
+                                     hipStream_t st) {
+    const long long n_blocks = rows * (k / 32);
+    const long long grid = (n_blocks + 255) / 256;
+    hipLaunchKernelGGL(repack_q4_1_matrix_kernel, dim3((unsigned)grid), dim3(256), 0, st, canonical, packed, n_blocks);
     return hipGetLastError();
 }
 

@@ -87,3 +87,21 @@ def decode_band(x: np.ndarray, router_f64: np.ndarray) -> np.ndarray:
     """Band for a decode call (1 to 8 tokens): every decode path computes the
     router as an fp32 GEMV, lane-sequential partial sums then a wave butterfly."""
     return router_band(x, router_f64)
+
+
+def lm_head_band(x: np.ndarray, w_dec: np.ndarray, block: int = 32) -> np.ndarray:
+    """Bound on |fp32 logit - exact logit| for the output-layer kernel, [T, V].
+
+    A lane multiplies its columns' decoded weights into fp32 sums (at most
+    32 terms per unit of a 4-bit format, in order), scales and adds the unit
+    sums, and the wave adds its 64 lane sums in 6 levels: every product
+    passes through fewer than n = 48 roundings.  For q4_1 a unit's sum is
+    d * sum(q x) + m * sum(x), whose terms are bounded by |w| + 2 max|w| of
+    the block (m is itself a decoded value of the block, the one with
+    q = 0), so the bound uses that magnitude for every format."""
+    V, D = w_dec.shape
+    a = np.abs(w_dec)
+    bmax = a.reshape(V, D // block, block).max(axis=2)
+    mag = a + 2.0 * np.repeat(bmax, block, axis=1)
+    n = 48
+    return 2.0 * n * U32 * (np.abs(x) @ mag.T)

@@ -117,3 +117,38 @@ def test_binding_error_carries_message(L):
     with pytest.raises(B.MoeError) as e:
         B.workspace_size(dims, 1)
     assert "d_model" in str(e.value)
+
+
+def test_lm_head_sizes_and_checks(L):
+    V, D = 146_484, 2048
+    assert L.moe_lm_head_bytes(V, D, 1) == V * D // 32 * 20
+    assert L.moe_lm_head_bytes(V, D, 2) == V * D // 2 + V * D // 16
+    assert L.moe_lm_head_bytes(V, D, 0) == V * D * 2
+    assert B.lm_head_bytes(V, D, "q4_1") == gen.matrix_bytes(V, D, "q4_1")
+    for v, d, f in ((0, D, 1), (V, 48, 1), (V, 8192, 1), (V, D, 7), (1 << 25, D, 1)):
+        assert L.moe_lm_head_bytes(v, d, f) == 0
+    fake = ctypes.c_void_p(0x10000)
+    out = ctypes.c_void_p(0x90000000)
+    odd = ctypes.c_void_p(0x10004)
+    # shapes, formats, token counts
+    assert L.moe_lm_head(V, 48, 1, fake, None, fake, 0, 1, out, None) == INVALID
+    assert L.moe_lm_head(0, D, 1, fake, None, fake, 0, 1, out, None) == INVALID
+    assert L.moe_lm_head(V, D, 9, fake, None, fake, 0, 1, out, None) == UNSUPPORTED
+    assert L.moe_lm_head(V, D, 1, fake, None, fake, 3, 1, out, None) == UNSUPPORTED
+    assert L.moe_lm_head(V, D, 1, fake, None, fake, 0, 0, out, None) == INVALID
+    assert L.moe_lm_head(V, D, 1, fake, None, fake, 0, 9, out, None) == INVALID
+    # pointers: NULL, misaligned, NVFP4 tensor scale, overlap of logits with an input
+    assert L.moe_lm_head(V, D, 1, None, None, fake, 0, 1, out, None) == INVALID
+    assert L.moe_lm_head(V, D, 1, fake, None, odd, 0, 1, out, None) == ALIGNMENT
+    assert L.moe_lm_head(V, D, 2, fake, None, fake, 0, 1, out, None) == INVALID
+    assert b"tensor_scale" in L.moe_last_error()
+    assert L.moe_lm_head(V, D, 2, ctypes.c_void_p(0x20000000), ctypes.c_void_p(0x10002), fake, 0, 1, out, None) == ALIGNMENT
+    assert L.moe_lm_head(V, D, 1, fake, None, ctypes.c_void_p(0x90000400), 0, 1, out, None) == INVALID
+    assert b"overlap" in L.moe_last_error()
+    assert L.moe_lm_head(V, D, 1, ctypes.c_void_p(0x8F000000), None, fake, 0, 1, out, None) == INVALID
+    # repack: overlap and shape
+    assert L.moe_lm_head_repack(V, D, 1, fake, fake, None) == INVALID
+    assert L.moe_lm_head_repack(V, 40, 1, fake, out, None) == INVALID
+    kus = ctypes.c_float()
+    assert L.moe_lm_head_timed(V, D, 1, fake, None, fake, 0, 1, out, None, None) == INVALID
+    assert L.moe_lm_head_timed(V, D, 1, fake, None, fake, 0, 0, out, ctypes.byref(kus), None) == INVALID
