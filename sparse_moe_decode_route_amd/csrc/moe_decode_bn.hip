@@ -340,15 +340,15 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p
     const int r0 = blockIdx.x * ROWS + grp * BN_RR;
     const int KS = p.K + p.S;
     // the token's list, loaded before any weight: lane j loads entry j, then
-    // every entry is read out as wave-uniform (scalar) values
+    // every entry is read out as wave-uniform (scalar) values where it is used
+    // (no per-lane array of entries: indexed by the batch loop, it would live
+    // in scratch memory)
     const int4 mine = reinterpret_cast<const int4 *>(p.pairs)[t * KS + min(lane, KS - 1)];
-    int4 ent[BN_MAXB * BN_PB];
-#pragma unroll
-    for (int i = 0; i < BN_MAXB * BN_PB; i++) {
+    auto entry = [&](int i) {
         const int j = min(i, KS - 1);
-        ent[i] = make_int4(__builtin_amdgcn_readlane(mine.x, j), __builtin_amdgcn_readlane(mine.y, j),
-                           __builtin_amdgcn_readlane(mine.z, j), __builtin_amdgcn_readlane(mine.w, j));
-    }
+        return make_int4(__builtin_amdgcn_readlane(mine.x, j), __builtin_amdgcn_readlane(mine.y, j),
+                         __builtin_amdgcn_readlane(mine.z, j), __builtin_amdgcn_readlane(mine.w, j));
+    };
     float acc[BN_RR];
 #pragma unroll
     for (int r = 0; r < BN_RR; r++) acc[r] = 0.f;
@@ -362,7 +362,7 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p
 #pragma unroll
         for (int q = 0; q < BN_PB; q++) {
             const int j = bt * BN_PB + q;
-            const int4 pr = ent[j];
+            const int4 pr = entry(j);
             coef[q] = (j < KS && pr.y >= 0) ? __int_as_float(pr.z) : 0.f;
             const uint8_t *eb = p.experts + (size_t)pr.w * p.expert_bytes;
             Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, p.tscale ? p.tscale[3 * pr.w + 2] : 1.f};
@@ -375,12 +375,12 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p
         uint4 hc[BN_PB][HLD];
 #pragma unroll
         for (int q = 0; q < BN_PB; q++) {
-            const uint4 *hsrc = reinterpret_cast<const uint4 *>(p.h + ((size_t)ent[bt * BN_PB + q].x * p.T + t) * F);
+            const uint4 *hsrc = reinterpret_cast<const uint4 *>(p.h + ((size_t)entry(bt * BN_PB + q).x * p.T + t) * F);
 #pragma unroll
             for (int i = 0; i < HLD; i++) hc[q][i] = hsrc[min(lane + MOE_WAVE * i, HCH - 1)];
         }
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the previous batch's LDS reads are done
+        // (a wave's LDS accesses complete in issue order, so these writes do
+        // not overtake the previous batch's reads of the same region)
 #pragma unroll
         for (int q = 0; q < BN_PB; q++)
 #pragma unroll
