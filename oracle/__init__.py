@@ -53,6 +53,7 @@ def lib():
         L.orc_layer_forward.restype = ctypes.c_int
         L.orc_stack_forward.restype = ctypes.c_int
         L.orc_lm_head.restype = ctypes.c_int
+        L.orc_attn_decode.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -247,3 +248,35 @@ def lm_head(wfmt_code: int, blob: np.ndarray, vocab: int, d: int, x: np.ndarray,
     if rc != 0:
         raise ValueError("oracle: row index outside the vocabulary")
     return out
+
+
+# --------------------------------------------------------------------------- decode attention
+
+def attn_decode(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, qw: np.ndarray, kw: np.ndarray,
+                sinks: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos: np.ndarray, window: int,
+                rope_base: float = 10000.0, eps: float = 1e-6):
+    """One decode step of attention.  q [B, Hq, D], k_new / v_new [B, Hkv, D],
+    caches bf16 bits uint16 [B, Hkv, max_len, D] (copied, not modified), pos
+    [B].  Returns (out [B, Hq, D] fp64, k_cache, v_cache with the new entries)."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    k_new = np.ascontiguousarray(k_new, dtype=np.float64)
+    Hkv = k_new.shape[1]
+    v_new = np.ascontiguousarray(v_new, dtype=np.float64)
+    qw = np.ascontiguousarray(qw, dtype=np.float64)
+    kw = np.ascontiguousarray(kw, dtype=np.float64)
+    sinks = np.ascontiguousarray(sinks, dtype=np.float64)
+    kc = np.array(k_cache, dtype=np.uint16, copy=True, order="C")
+    vc = np.array(v_cache, dtype=np.uint16, copy=True, order="C")
+    max_len = kc.shape[2]
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    rc = lib().orc_attn_decode(
+        ctypes.c_int(Hq), ctypes.c_int(Hkv), ctypes.c_int(D), ctypes.c_int(window), ctypes.c_double(rope_base),
+        ctypes.c_double(eps), ctypes.c_int(B), _p(q, ctypes.c_double), _p(k_new, ctypes.c_double),
+        _p(v_new, ctypes.c_double), _p(qw, ctypes.c_double), _p(kw, ctypes.c_double), _p(sinks, ctypes.c_double),
+        _p(kc, ctypes.c_uint16), _p(vc, ctypes.c_uint16), ctypes.c_int(max_len), _p(pos, ctypes.c_int32),
+        _p(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle: position outside the cache")
+    return out, kc, vc

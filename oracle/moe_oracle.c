@@ -406,3 +406,114 @@ int orc_lm_head(int fmt, const uint8_t *w, int32_t vocab, int32_t d, double s_t,
     free(wr);
     return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* decode attention (the step before the MoE FFN in every layer)             */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16 bits of v as a 32-bit producer stores it: v cast to float, then
+ * rounded to nearest even (v finite). */
+static uint16_t orc_to_bf16(double v) {
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(r >> 16);
+}
+
+/* y = x / sqrt(mean(x^2) + eps) * w over one head of n values. */
+static void orc_head_rmsnorm(int n, const double *x, const double *w, double eps, double *y) {
+    double ss = 0.0;
+    for (int i = 0; i < n; i++) ss += x[i] * x[i];
+    double r = sqrt(ss / n + eps);
+    for (int i = 0; i < n; i++) y[i] = x[i] / r * w[i];
+}
+
+/* Rotary embedding at position p, pairs (i, i + n/2) rotated by the angle
+ * p * base^(-2i/n). */
+static void orc_rope(int n, double *x, int p, double base) {
+    int h = n / 2;
+    for (int i = 0; i < h; i++) {
+        double ang = (double)p * pow(base, -2.0 * i / n);
+        double c = cos(ang), s = sin(ang);
+        double a = x[i], b = x[i + h];
+        x[i] = a * c - b * s;
+        x[i + h] = a * s + b * c;
+    }
+}
+
+/*
+ * One decode step of attention for B sequences.  "Recursive Flint
+ * 40B-A2.5B" (orcarouter.ai blog), section "The architecture is a
+ * memory-bandwidth argument", attention and positional-encoding bullets:
+ * 32 query heads share 4 key/value heads (head size 128); sliding-window
+ * layers see the current token and the 512 before it and use rotary
+ * embeddings, full layers see every earlier token and use none; each head's
+ * queries and keys are RMS-normalised, and every head has a learned sink.
+ * For sequence b with new position P = pos[b]:
+ *   q_h = rope(rmsnorm(q[b,h]) * qw) (rope only when window > 0), likewise
+ *   k for each key/value head; k and v are stored in the caches at P in
+ *   bfloat16;
+ *   head h reads key/value head g = h / (Hq / Hkv) at positions
+ *   j in [max(0, P - window + 1), P] (all j <= P when window == 0);
+ *   s_j = q_h . K[j] / sqrt(D); the sink logit z_h joins the softmax
+ *   denominator only: out = sum_j e^{s_j} V[j] / (sum_j e^{s_j} + e^{z_h}).
+ * Caches are bfloat16 [B, Hkv, max_len, D]; q, out [B, Hq, D]; k_new, v_new
+ * [B, Hkv, D].  The stored k and v are rounded to bfloat16 from fp32 (the
+ * fp64 value cast to float, then round to nearest even).  Returns -1 on a
+ * position outside [0, max_len).
+ */
+int orc_attn_decode(int Hq, int Hkv, int D, int window, double rope_base, double eps, int B, const double *q,
+                    const double *k_new, const double *v_new, const double *qw, const double *kw,
+                    const double *sinks, uint16_t *k_cache, uint16_t *v_cache, int max_len, const int32_t *pos,
+                    double *out) {
+    double *qh = (double *)malloc(sizeof(double) * D);
+    double *kh = (double *)malloc(sizeof(double) * D);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)max_len);
+    int grp = Hq / Hkv, rc = 0;
+    for (int b = 0; b < B && rc == 0; b++) {
+        int P = pos[b];
+        if (P < 0 || P >= max_len) {
+            rc = -1;
+            break;
+        }
+        for (int g = 0; g < Hkv; g++) {
+            orc_head_rmsnorm(D, k_new + ((size_t)b * Hkv + g) * D, kw, eps, kh);
+            if (window > 0) orc_rope(D, kh, P, rope_base);
+            uint16_t *kc = k_cache + (((size_t)b * Hkv + g) * max_len + P) * D;
+            uint16_t *vc = v_cache + (((size_t)b * Hkv + g) * max_len + P) * D;
+            for (int d = 0; d < D; d++) {
+                kc[d] = orc_to_bf16(kh[d]);
+                vc[d] = orc_to_bf16(v_new[((size_t)b * Hkv + g) * D + d]);
+            }
+        }
+        int lo = window > 0 ? (P - window + 1 > 0 ? P - window + 1 : 0) : 0;
+        for (int h = 0; h < Hq; h++) {
+            int g = h / grp;
+            orc_head_rmsnorm(D, q + ((size_t)b * Hq + h) * D, qw, eps, qh);
+            if (window > 0) orc_rope(D, qh, P, rope_base);
+            const uint16_t *K = k_cache + ((size_t)b * Hkv + g) * max_len * D;
+            const uint16_t *V = v_cache + ((size_t)b * Hkv + g) * max_len * D;
+            double m = sinks[h];
+            for (int j = lo; j <= P; j++) {
+                double s = 0.0;
+                for (int d = 0; d < D; d++) s += qh[d] * orc_bf16(K[(size_t)j * D + d]);
+                s /= sqrt((double)D);
+                sc[j] = s;
+                if (s > m) m = s;
+            }
+            double den = exp(sinks[h] - m);
+            for (int j = lo; j <= P; j++) den += exp(sc[j] - m);
+            double *o = out + ((size_t)b * Hq + h) * D;
+            for (int d = 0; d < D; d++) o[d] = 0.0;
+            for (int j = lo; j <= P; j++) {
+                double w = exp(sc[j] - m) / den;
+                for (int d = 0; d < D; d++) o[d] += w * orc_bf16(V[(size_t)j * D + d]);
+            }
+        }
+    }
+    free(qh);
+    free(kh);
+    free(sc);
+    return rc;
+}

@@ -15,6 +15,9 @@ Workload recipe (the pages print no layer values, so every input is synthetic):
 * the output layer (lm_head) W [vocab, d_model] ~ N(0, 0.02), encoded in the
   same block formats as the experts (blocks along d_model); its input is a
   final-normed hidden state ~ N(0, 1);
+* decode attention: raw q, new k and v ~ N(0, 1); QK-norm gains 1 + 0.1 N(0, 1);
+  sink logits ~ N(0, 1); cached keys and values bf16(N(0, 1)) (a stored key is a
+  normalised vector, unit RMS);
 * a skewed router prior (prefill workload) adds bias_e = ln(Zipf(s) pmf at the
   expert's rank), ranks given by a seeded permutation.
 
@@ -47,6 +50,7 @@ import torch
 WFMT_CODES = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 ROOT_SEED = 0xF1147
 TID_ROUTER = 0
+TID_ATTN = 9000
 TID_LM_HEAD = 9997
 TID_ZIPF = 9998
 TID_HIDDEN = 9999
@@ -270,6 +274,33 @@ def make_lm_head(vocab: int, d_model: int, wfmt: str, cfg_id: int, device=None):
     return torch.cat(parts), None
 
 
+@dataclasses.dataclass
+class AttnInputs:
+    q: torch.Tensor        # fp32 [B, Hq, D]
+    k_new: torch.Tensor    # fp32 [B, Hkv, D]
+    v_new: torch.Tensor    # fp32 [B, Hkv, D]
+    q_norm_w: torch.Tensor  # fp32 [D]
+    k_norm_w: torch.Tensor  # fp32 [D]
+    sinks: torch.Tensor    # fp32 [Hq]
+    k_cache: torch.Tensor  # bf16 bits int16 [B, Hkv, max_len, D]
+    v_cache: torch.Tensor  # bf16 bits int16 [B, Hkv, max_len, D]
+
+
+def make_attn(B: int, Hq: int, Hkv: int, D: int, max_len: int, cfg_id: int, draw: int = 0,
+              device=None) -> AttnInputs:
+    """Inputs of one decode-attention step (seeded; tensor ids 9000 + 8 * draw + i)."""
+    t = TID_ATTN + 8 * draw
+    return AttnInputs(
+        q=_normal((B, Hq, D), 1.0, cfg_id, 0, t, device).contiguous(),
+        k_new=_normal((B, Hkv, D), 1.0, cfg_id, 0, t + 1, device).contiguous(),
+        v_new=_normal((B, Hkv, D), 1.0, cfg_id, 0, t + 2, device).contiguous(),
+        q_norm_w=(1.0 + _normal((D,), 0.1, cfg_id, 0, t + 3, device)).contiguous(),
+        k_norm_w=(1.0 + _normal((D,), 0.1, cfg_id, 0, t + 4, device)).contiguous(),
+        sinks=_normal((Hq,), 1.0, cfg_id, 0, t + 5, device).contiguous(),
+        k_cache=bf16_bits(_normal((B, Hkv, max_len, D), 1.0, cfg_id, 0, t + 6, device)).contiguous(),
+        v_cache=bf16_bits(_normal((B, Hkv, max_len, D), 1.0, cfg_id, 0, t + 7, device)).contiguous())
+
+
 def make_hidden(cfg_id: int, n_tokens: int, d_model: int, layer: int = 0, draw: int = 0,
                 device=None) -> torch.Tensor:
     """Hidden states ~ N(0, 1), fp32 [n_tokens, d_model]."""
@@ -300,3 +331,9 @@ WORKLOADS = {
 # from the pages).  Not a multiple of any tile, so the last rows are ragged.
 LM_HEAD_VOCAB = 146_484
 LM_HEAD_CFG = 6
+
+# Decode attention: 32 query heads over 4 key/value heads of 128; sliding
+# window of 513 positions (rotary embeddings) or full attention (none).
+ATTN_HQ, ATTN_HKV, ATTN_D, ATTN_WINDOW = 32, 4, 128, 513
+ATTN_ROPE_BASE = 10000.0  # not on the pages (a reading)
+ATTN_CFG = 7

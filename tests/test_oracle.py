@@ -511,3 +511,105 @@ def test_lm_head_is_linear_in_the_token(orc):
     x1, x2 = rng.standard_normal((2, D))
     l1, l2, l12 = (orc.lm_head(2, blob.numpy(), V, D, v[None], s_t=s)[0] for v in (x1, x2, 0.5 * x1 - 3.0 * x2))
     assert np.allclose(l12, 0.5 * l1 - 3.0 * l2, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- decode attention
+
+def _bf16_bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_vals(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_attn_reduces_to_library_sdpa(orc):
+    # unit-RMS +-1 tokens with eps 0 and unit gains pass the norms unchanged, a
+    # full layer has no rotary embedding, and a sink of -1e300 takes no mass:
+    # the step is grouped-query scaled-dot-product attention over positions <= P
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, D, L = 2, 8, 2, 16, 40
+    q = rng.choice([-1.0, 1.0], size=(B, Hq, D))
+    kn = rng.choice([-1.0, 1.0], size=(B, Hkv, D))
+    vn = rng.standard_normal((B, Hkv, D))
+    kc = _bf16_bits(rng.standard_normal((B, Hkv, L, D)))
+    vc = _bf16_bits(rng.standard_normal((B, Hkv, L, D)))
+    pos = np.array([17, 39])
+    out, kc2, vc2 = orc.attn_decode(q, kn, vn, np.ones(D), np.ones(D), np.full(Hq, -1e300), kc, vc, pos,
+                                    window=0, eps=0.0)
+    for b in range(B):
+        P = pos[b]
+        assert np.array_equal(_bf16_vals(kc2[b, :, P]), kn[b])
+        assert np.array_equal(kc2[b, :, :P], kc[b, :, :P]) and np.array_equal(kc2[b, :, P + 1:], kc[b, :, P + 1:])
+        K = torch.from_numpy(_bf16_vals(kc2[b, :, :P + 1]))
+        V = torch.from_numpy(_bf16_vals(vc2[b, :, :P + 1]))
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q[b])[:, None, :], K.repeat_interleave(Hq // Hkv, 0),
+                                             V.repeat_interleave(Hq // Hkv, 0))[:, 0, :].numpy()
+        assert np.allclose(out[b], ref, rtol=0, atol=1e-12)
+
+
+def test_attn_sink_closed_form(orc):
+    # every key equal: each position has the same score s, so the output is
+    # the mean of the values scaled by n e^s / (n e^s + e^z)
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, D, L = 1, 4, 1, 8, 12
+    P = 9
+    krow = rng.choice([-1.0, 1.0], size=D)
+    kc = _bf16_bits(np.broadcast_to(krow, (B, Hkv, L, D)))
+    vc = _bf16_bits(rng.standard_normal((B, Hkv, L, D)))
+    q = rng.choice([-1.0, 1.0], size=(B, Hq, D))
+    sinks = np.array([0.5, -2.0, 3.0, 0.0])
+    out, _, vc2 = orc.attn_decode(q, krow[None, None, :], np.zeros((B, Hkv, D)), np.ones(D), np.ones(D), sinks,
+                                  kc, vc, np.array([P]), window=0, eps=0.0)
+    V = _bf16_vals(vc2[0, 0, :P + 1])
+    for h in range(Hq):
+        s = q[0, h] @ krow / math.sqrt(D)
+        n = P + 1
+        want = V.mean(axis=0) * (n * math.exp(s) / (n * math.exp(s) + math.exp(sinks[h])))
+        assert np.allclose(out[0, h], want, rtol=1e-13, atol=1e-15)
+
+
+def test_attn_window_covers_exactly_513_positions(orc):
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, D, L = 1, 2, 1, 8, 700
+    P, W = 640, 513
+    q = rng.standard_normal((B, Hq, D))
+    kn, vn = rng.standard_normal((B, Hkv, D)), rng.standard_normal((B, Hkv, D))
+    kc = _bf16_bits(rng.standard_normal((B, Hkv, L, D)))
+    vc = _bf16_bits(rng.standard_normal((B, Hkv, L, D)))
+    base, _, _ = orc.attn_decode(q, kn, vn, np.ones(D), np.ones(D), np.zeros(Hq), kc, vc, np.array([P]), window=W)
+    outside = vc.copy()
+    outside[0, 0, :P - W + 1] = _bf16_bits(np.full(D, 1e4))        # positions 0 .. P - 513
+    o1, _, _ = orc.attn_decode(q, kn, vn, np.ones(D), np.ones(D), np.zeros(Hq), kc, outside, np.array([P]), window=W)
+    assert np.array_equal(o1, base)
+    inside = vc.copy()
+    inside[0, 0, P - W + 1] = _bf16_bits(np.full(D, 1e4))         # the oldest position in the window
+    o2, _, _ = orc.attn_decode(q, kn, vn, np.ones(D), np.ones(D), np.zeros(Hq), kc, inside, np.array([P]), window=W)
+    assert np.abs(o2 - base).max() > 1.0
+
+
+@pytest.mark.parametrize("i", [0, 1, 37])
+def test_attn_rope_rotates_dimension_pairs(orc, i):
+    # k = e_i with eps 0: the norm scales it to sqrt(D) e_i, and the rotary
+    # embedding at position P turns the pair (i, i + D/2) by P * base^(-2i/D)
+    D, P, base = 128, 301, 10000.0
+    kn = np.zeros((1, 1, D))
+    kn[0, 0, i] = 1.0
+    kc = np.zeros((1, 1, 400, D), dtype=np.uint16)
+    _, kc2, _ = orc.attn_decode(np.ones((1, 1, D)), kn, np.zeros((1, 1, D)), np.ones(D), np.ones(D), np.zeros(1),
+                                kc, kc.copy(), np.array([P]), window=513, rope_base=base, eps=0.0)
+    ang = P * base ** (-2.0 * i / D)
+    want = np.zeros(D)
+    want[i], want[i + D // 2] = math.sqrt(D) * math.cos(ang), math.sqrt(D) * math.sin(ang)
+    assert np.array_equal(_bf16_vals(kc2[0, 0, P]), _bf16_vals(_bf16_bits(want)))  # -0 == +0
+
+
+def test_attn_head_norm_closed_form(orc):
+    # a constant key c * 1 normalises to sign(c) * w (eps 0), with no rotation
+    # in a full layer
+    D = 16
+    w = np.linspace(0.5, 2.0, D)
+    kc = np.zeros((1, 1, 4, D), dtype=np.uint16)
+    _, kc2, _ = orc.attn_decode(np.ones((1, 1, D)), np.full((1, 1, D), -3.7), np.zeros((1, 1, D)), np.ones(D), w,
+                                np.zeros(1), kc, kc.copy(), np.array([2]), window=0, eps=0.0)
+    assert np.array_equal(_bf16_vals(kc2[0, 0, 2]), _bf16_vals(_bf16_bits(-w)))
