@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="stack_q4_1_b1",
                     choices=["stack_q4_1_b1", "stack_nvfp4_b1", "stack_nvfp4_b8", "prefill_q4_1", "sweep_q4_1",
-                             "lm_head_q4_1", "lm_head_nvfp4", "lm_head_bf16"])
+                             "lm_head_q4_1", "lm_head_nvfp4", "lm_head_bf16", "attn_swa", "attn_full128k"])
     ap.add_argument("--layers", type=int, default=47)
     ap.add_argument("--lm-tokens", type=int, default=1, help="tokens per output-layer call (1..8)")
     ap.add_argument("--lm-cpu-rows", type=int, default=146_484, help="vocabulary rows in the CPU baseline sample")
@@ -97,6 +97,7 @@ def source_digest(files=("moe_decode_b1.hip", "moe_decode.hip", "moe_device.h", 
 
 PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_device.h", "moe_internal.h")
 LM_HEAD_SOURCES = ("moe_lm_head.hip", "moe_device.h", "moe_internal.h")
+ATTN_SOURCES = ("moe_attn.hip", "moe_device.h", "moe_internal.h")
 
 
 # HBM traffic per launch read from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
@@ -571,6 +572,107 @@ def bench_lm_head(args, wfmt: str):
     )
 
 
+def bench_attn(args, kind: str):
+    """Decode attention for one token (batch 1).
+
+    attn_swa: the 35 sliding-window layers of one token, each with its own
+    cache (8192 positions, the token at 8000: a full window of 513); one step
+    is 35 calls.  attn_full128k: one full-attention layer at position 131,071
+    of a 131,072-position cache (268 MB of keys and values); two caches used
+    in turn so that every call streams from HBM."""
+    from sparse_moe_decode_route_amd import binding as B
+    from sparse_moe_decode_route_amd import inputs as gen
+    import oracle
+    Hq, Hkv, D = gen.ATTN_HQ, gen.ATTN_HKV, gen.ATTN_D
+    if kind == "swa":
+        window, max_len, P, n_layers = gen.ATTN_WINDOW, 8192, 8000, 35
+    else:
+        window, max_len, P, n_layers = 0, 131072, 131071, 2
+    dims = B.attn_dims(Hq, Hkv, window, gen.ATTN_ROPE_BASE, 1e-6)
+    layers = [gen.make_attn(1, Hq, Hkv, D, max_len, cfg_id=gen.ATTN_CFG, draw=l, device="cuda") for l in range(n_layers)]
+    pos = torch.tensor([P], dtype=torch.int32, device="cuda")
+    ws = B.attn_workspace(dims, 1, max_len)
+    out = torch.empty((1, Hq, D), device="cuda")
+    ref = B.attn_decode(dims, layers[0], pos, ws=ws).clone()
+    torch.cuda.synchronize()
+    per_graph = n_layers * max(1, -(-8 // n_layers))
+
+    def step_all():
+        for i in range(per_graph):
+            B.attn_decode(dims, layers[i % n_layers], pos, out=out, ws=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step_all()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_all()
+    reps = max(1, -(-args.steps // per_graph))
+    for _ in range(max(1, -(-args.warmup // per_graph))):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    calls = reps * per_graph
+    ms_call = ev0.elapsed_time(ev1) / calls
+    # the last replay's last call used layer (per_graph - 1) % n_layers
+    last = B.attn_decode(dims, layers[(per_graph - 1) % n_layers], pos, ws=ws)
+    graph_matches_eager = bool(torch.equal(out, last))
+    n_timed = max(1, min(args.timed_calls, 20))
+    kus = {}
+    for i in range(n_timed):
+        _, us = B.attn_decode_timed(dims, layers[i % n_layers], pos, ws=ws)
+        for k, v in us.items():
+            kus[k] = kus.get(k, 0.0) + v / n_timed
+    n_pos = min(P + 1, window) if window > 0 else P + 1
+    kv_bytes = n_pos * Hkv * D * 2 * 2
+    chunk = 64 if window > 0 else next(c for c in (64, 128, 256, 512, 1024) if c == 1024 or -(-max_len // c) * Hkv <= 1024)
+    nc = -(-(P + 1) // chunk) if window == 0 else -(-n_pos // chunk) + 1
+    part_bytes = Hq * nc * (D + 2) * 4
+    algo = kv_bytes + Hq * D * 4 + part_bytes  # keys, values, queries in, chunk partials out
+    ach = algo / (kus["attn_chunk"] * 1e-6) / 1e9
+    step_layers = n_layers if kind == "swa" else 1
+    ms_step = ms_call * step_layers
+    cpu = None
+    if not args.no_cpu:
+        l0 = layers[0]
+        c0 = time.time()
+        oracle.attn_decode(l0.q.cpu().numpy(), l0.k_new.cpu().numpy(), l0.v_new.cpu().numpy(),
+                           l0.q_norm_w.cpu().numpy(), l0.k_norm_w.cpu().numpy(), l0.sinks.cpu().numpy(),
+                           l0.k_cache.cpu().numpy().view(np.uint16), l0.v_cache.cpu().numpy().view(np.uint16),
+                           np.array([P]), window, gen.ATTN_ROPE_BASE, 1e-6)
+        dt = time.time() - c0
+        cpu = dict(value=round(1.0 / (dt * step_layers), 4), unit="tok/s", cores=1, kind="oracle",
+                   sample=f"one call of the fp64 C oracle ({dt:.2f}s, cache copy included), one thread; "
+                          f"x{step_layers} for the step")
+    name = "35 sliding-window layers" if kind == "swa" else "one full-attention layer at 128k context"
+    return dict(
+        metric=f"decode attention tokens/s ({name}, batch 1)",
+        value=round(1.0 / (ms_step * 1e-3), 1), unit="tok/s", n_gpus=1, steps=calls, warmup=per_graph,
+        ms_per_step=round(ms_step, 5), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+        data="synthetic",
+        config=dict(workload=f"attn_{kind}: 32 query / 4 key-value heads of 128, bf16 cache of {max_len} positions, "
+                             f"new token at {P}, " + ("window 513 with rotary embeddings, 35 layers with their own "
+                             "caches per step" if kind == "swa" else "full attention (no rotary embedding)"),
+                    global_batch=1, seq_len=P + 1, parallelism="single-gpu", us_per_call=round(ms_call * 1e3, 3),
+                    kernel_us={k: round(v, 3) for k, v in kus.items()},
+                    timing=f"HIP graph of {per_graph} calls over {n_layers} caches, replayed",
+                    graph_matches_eager=graph_matches_eager),
+        roofline=dict(bound="hbm", kernel="attn_chunk", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None, algo_bytes_per_launch=algo,
+                      us_per_launch=round(kus["attn_chunk"], 3),
+                      timing=f"HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream, mean of {n_timed} calls"),
+        cpu_baseline=cpu,
+    )
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -589,6 +691,8 @@ def main():
         out = bench_stack(args, "nvfp4", 1)
     elif args.workload == "sweep_q4_1":
         out = bench_sweep(args)
+    elif args.workload.startswith("attn_"):
+        out = bench_attn(args, args.workload[len("attn_"):])
     elif args.workload.startswith("lm_head_"):
         out = bench_lm_head(args, args.workload[len("lm_head_"):])
     elif args.workload == "stack_nvfp4_b8":

@@ -259,6 +259,68 @@ moe_status moe_lm_head_timed(int32_t vocab, int32_t d_model, int32_t wfmt, const
                              const float *tensor_scale, const void *x, int32_t act, int32_t n_tokens, float *logits,
                              float *kernel_us, void *stream);
 
+/*
+ * Decode attention, the step before the MoE FFN in every layer.
+ * "Recursive Flint 40B-A2.5B" (orcarouter.ai blog), section "The
+ * architecture is a memory-bandwidth argument", attention and
+ * positional-encoding bullets: 32 query heads share 4 key/value heads of
+ * size 128; sliding-window layers see the current token and the 512 before
+ * it and use rotary embeddings, full-attention layers see every earlier
+ * token and use none; queries and keys are RMS-normalised per head, and
+ * each head has a learned attention sink.  One new token per sequence b at
+ * position P = pos[b]:
+ *   qh = rope(rmsnorm(q[b,h]) * q_norm_w), kh likewise with k_norm_w
+ *     (rmsnorm over the 128 values with norm_eps; rope only when window > 0:
+ *     pairs (i, i + 64) turned by P * rope_base^(-2i/128));
+ *   the caches receive bf16(kh) and bf16(v_new) at P;
+ *   query head h reads key/value head h / (n_q_heads / n_kv_heads) at the
+ *   positions j in [max(0, P - window + 1), P] (every j <= P when window = 0):
+ *   s_j = qh . K[j] / sqrt(128),
+ *   out[b,h] = sum_j e^(s_j) V[j] / (sum_j e^(s_j) + e^(sinks[h])).
+ * Every sum has a fixed order.
+ */
+typedef struct {
+    int32_t n_q_heads;  /* query heads; a multiple of n_kv_heads, group of 1, 2, 4 or 8 */
+    int32_t n_kv_heads; /* key/value heads */
+    int32_t head_dim;   /* must be 128 */
+    int32_t window;     /* > 0: sliding window of this many positions, rotary embeddings; 0: full, none */
+    float rope_base;    /* rotary base (used when window > 0), > 0 */
+    float norm_eps;     /* RMSNorm epsilon, >= 0 */
+} moe_attn_dims;
+
+/* (host) workspace bytes moe_attn_decode needs for n_seqs sequences of
+   caches of max_len positions. */
+moe_status moe_attn_workspace_size(const moe_attn_dims *dims, int32_t n_seqs, int32_t max_len, size_t *bytes);
+
+/*
+ *   q          fp32 [n_seqs, n_q_heads, 128], the new tokens' query projections
+ *   k_new      fp32 [n_seqs, n_kv_heads, 128]; v_new likewise
+ *   q_norm_w   fp32 [128]; k_norm_w fp32 [128]; sinks fp32 [n_q_heads]
+ *   pos        int32 [n_seqs] (device): the new token's position; positions
+ *              0 .. P - 1 of the caches hold earlier tokens
+ *   k_cache    bf16 [n_seqs, n_kv_heads, max_len, 128], read and written at
+ *              P; v_cache likewise
+ *   out        fp32 [n_seqs, n_q_heads, 128]
+ *   ws         workspace of moe_attn_workspace_size() bytes
+ * 1 <= n_seqs <= 4096, 1 <= max_len <= 16777216.  A position outside
+ * [0, max_len) leaves that sequence's caches untouched and gives NaN
+ * outputs.  Buffers must not overlap.
+ */
+moe_status moe_attn_decode(const moe_attn_dims *dims, int32_t n_seqs, int32_t max_len, const float *q,
+                           const float *k_new, const float *v_new, const float *q_norm_w, const float *k_norm_w,
+                           const float *sinks, const int32_t *pos, uint16_t *k_cache, uint16_t *v_cache, float *out,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Measurement variant: the same three kernels, each launched with a
+   start/stop event pair on its dispatch; kernel_us (host) float [3]
+   receives their durations (prep, chunks, combine) in microseconds.
+   Blocks the calling thread; not for use under stream capture. */
+moe_status moe_attn_decode_timed(const moe_attn_dims *dims, int32_t n_seqs, int32_t max_len, const float *q,
+                                 const float *k_new, const float *v_new, const float *q_norm_w,
+                                 const float *k_norm_w, const float *sinks, const int32_t *pos, uint16_t *k_cache,
+                                 uint16_t *v_cache, float *out, void *ws, size_t ws_bytes, float *kernel_us,
+                                 void *stream);
+
 /* (host) static description of a status code. */
 const char *moe_status_string(moe_status s);
 

@@ -24,7 +24,8 @@ ENTRY_POINTS = (
     "moe_packed_expert_bytes", "moe_workspace_size", "moe_repack_weights", "moe_route_topk",
     "moe_expert_ffn_q4", "moe_layer_forward", "moe_layer_forward_prefill", "moe_stack_decode",
     "moe_stack_decode_timed", "moe_layer_forward_prefill_timed", "moe_lm_head_bytes", "moe_lm_head_repack",
-    "moe_lm_head", "moe_lm_head_timed", "moe_status_string", "moe_last_error",
+    "moe_lm_head", "moe_lm_head_timed", "moe_attn_workspace_size", "moe_attn_decode", "moe_attn_decode_timed",
+    "moe_status_string", "moe_last_error",
 )
 
 
@@ -32,6 +33,11 @@ class MoeError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"libmoe status {status}: {msg}")
         self.status = status
+
+
+class CAttnDims(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float)]
 
 
 class CDims(ctypes.Structure):
@@ -88,6 +94,13 @@ def lib():
         L.moe_lm_head.argtypes = [i32, i32, i32, vp, vp, vp, i32, i32, vp, vp]
         L.moe_lm_head_timed.restype = ctypes.c_int
         L.moe_lm_head_timed.argtypes = [i32, i32, i32, vp, vp, vp, i32, i32, vp, ctypes.POINTER(ctypes.c_float), vp]
+        pa = ctypes.POINTER(CAttnDims)
+        L.moe_attn_workspace_size.restype = ctypes.c_int
+        L.moe_attn_workspace_size.argtypes = [pa, i32, i32, ctypes.POINTER(sz)]
+        L.moe_attn_decode.restype = ctypes.c_int
+        L.moe_attn_decode.argtypes = [pa, i32, i32] + [vp] * 11 + [sz, vp]
+        L.moe_attn_decode_timed.restype = ctypes.c_int
+        L.moe_attn_decode_timed.argtypes = [pa, i32, i32] + [vp] * 11 + [sz, ctypes.POINTER(ctypes.c_float), vp]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_last_error.restype = ctypes.c_char_p
@@ -343,3 +356,45 @@ def lm_head_timed(head: LmHead, x: torch.Tensor, logits: Optional[torch.Tensor] 
                                    _ptr(head.tensor_scale), _ptr(x), _act(x), T, _ptr(logits), ctypes.byref(us),
                                    _stream(stream)))
     return logits, float(us.value)
+
+
+# --------------------------------------------------------------------------- decode attention
+
+def attn_dims(n_q_heads: int, n_kv_heads: int, window: int, rope_base: float = 10000.0,
+              norm_eps: float = 1e-6) -> CAttnDims:
+    return CAttnDims(n_q_heads, n_kv_heads, 128, window, rope_base, norm_eps)
+
+
+def attn_workspace(dims: CAttnDims, n_seqs: int, max_len: int, device="cuda") -> torch.Tensor:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_attn_workspace_size(ctypes.byref(dims), n_seqs, max_len, ctypes.byref(n)))
+    return torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device)
+
+
+def _attn_args(dims, a, pos, out, ws):
+    B, _, _ = a.q.shape
+    max_len = a.k_cache.shape[2]
+    out = out if out is not None else torch.empty_like(a.q)
+    ws = ws if ws is not None else attn_workspace(dims, B, max_len, a.q.device)
+    args = [ctypes.byref(dims), B, max_len, _ptr(a.q), _ptr(a.k_new), _ptr(a.v_new), _ptr(a.q_norm_w),
+            _ptr(a.k_norm_w), _ptr(a.sinks), _ptr(pos), _ptr(a.k_cache), _ptr(a.v_cache), _ptr(out), _ptr(ws),
+            ws.numel()]
+    return args, out
+
+
+def attn_decode(dims: CAttnDims, a: gen.AttnInputs, pos: torch.Tensor, out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_attn_decode: writes the new keys/values into a.k_cache / a.v_cache
+    (device tensors) and returns out [B, Hq, 128]."""
+    args, out = _attn_args(dims, a, pos, out, ws)
+    _check(lib().moe_attn_decode(*args, _stream(stream)))
+    return out
+
+
+def attn_decode_timed(dims: CAttnDims, a: gen.AttnInputs, pos: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None, stream=None):
+    """moe_attn_decode_timed: (out, {kernel: us}).  Synchronises the stream."""
+    args, out = _attn_args(dims, a, pos, out, ws)
+    us = (ctypes.c_float * 3)()
+    _check(lib().moe_attn_decode_timed(*args, us, _stream(stream)))
+    return out, dict(zip(("attn_prep", "attn_chunk", "attn_combine"), (float(v) for v in us)))

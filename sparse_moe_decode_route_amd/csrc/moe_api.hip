@@ -625,6 +625,154 @@ moe_status moe_lm_head_timed(int32_t vocab, int32_t d_model, int32_t wfmt, const
     return s == MOE_OK ? ok() : s;
 }
 
+// ---- decode attention ----
+
+struct AttnWs {
+    size_t q_prep, part_m, part_l, part_o, total;
+};
+
+static AttnWs attn_ws(const moe_attn_dims &d, int B, int max_len) {
+    AttnWs L{};
+    const size_t nc = (size_t)moe::attn_chunk_slots(d.window, max_len,
+                                                    moe::attn_chunk_size(d.window, max_len, B, d.n_kv_heads));
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o += align_up(bytes);
+        return at;
+    };
+    L.q_prep = take((size_t)B * d.n_q_heads * 128 * 4);
+    L.part_m = take((size_t)B * d.n_q_heads * nc * 4);
+    L.part_l = take((size_t)B * d.n_q_heads * nc * 4);
+    L.part_o = take((size_t)B * d.n_q_heads * nc * 128 * 4);
+    L.total = o;
+    return L;
+}
+
+static moe_status attn_check(const moe_attn_dims *d, int32_t B, int32_t max_len) {
+    if (!d) return fail(MOE_ERR_INVALID_ARG, "dims is NULL");
+    if (d->head_dim != 128) return fail(MOE_ERR_UNSUPPORTED, "head_dim must be 128");
+    if (d->n_kv_heads < 1 || d->n_q_heads < d->n_kv_heads || d->n_q_heads % d->n_kv_heads || d->n_q_heads > 1024)
+        return fail(MOE_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads (at most 1024)");
+    const int grp = d->n_q_heads / d->n_kv_heads;
+    if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
+        return fail(MOE_ERR_UNSUPPORTED, "query heads per key/value head must be 1, 2, 4 or 8");
+    if (d->window < 0) return fail(MOE_ERR_INVALID_ARG, "window must be >= 0");
+    if (d->window > 0 && !(d->rope_base > 0.f)) return fail(MOE_ERR_INVALID_ARG, "rope_base must be > 0");
+    if (!(d->norm_eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "norm_eps must be >= 0");
+    if (B < 1 || B > 4096) return fail(MOE_ERR_INVALID_ARG, "n_seqs must be in [1, 4096]");
+    if (max_len < 1 || max_len > 16777216) return fail(MOE_ERR_INVALID_ARG, "max_len must be in [1, 16777216]");
+    return MOE_OK;
+}
+
+moe_status moe_attn_workspace_size(const moe_attn_dims *d, int32_t n_seqs, int32_t max_len, size_t *bytes) {
+    MOE_TRY(attn_check(d, n_seqs, max_len));
+    if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = attn_ws(*d, n_seqs, max_len).total;
+    return ok();
+}
+
+// Host checks and the kernel arguments; nothing touches the device.
+static moe_status attn_prepare(const moe_attn_dims *d, int32_t B, int32_t max_len, const float *q, const float *k_new,
+                               const float *v_new, const float *q_norm_w, const float *k_norm_w, const float *sinks,
+                               const int32_t *pos, uint16_t *k_cache, uint16_t *v_cache, float *out, void *ws,
+                               size_t ws_bytes, moe::AttnArgs *args) {
+    MOE_TRY(attn_check(d, B, max_len));
+    const void *ins[] = {q, k_new, v_new, q_norm_w, k_norm_w, sinks, pos, k_cache, v_cache, out};
+    const char *names[] = {"q", "k_new", "v_new", "q_norm_w", "k_norm_w", "sinks", "pos", "k_cache", "v_cache", "out"};
+    for (int i = 0; i < 10; i++) MOE_TRY(check_ptr(ins[i], names[i]));
+    const AttnWs L = attn_ws(*d, B, max_len);
+    if (!ws || ws_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE, "workspace needs " + std::to_string(L.total) + " bytes, got " +
+                                           std::to_string(ws ? ws_bytes : 0));
+    MOE_TRY(check_ptr(ws, "ws"));
+    // the written buffers must not overlap anything else
+    const size_t cache_bytes = (size_t)B * d->n_kv_heads * max_len * 128 * 2;
+    const size_t out_bytes = (size_t)B * d->n_q_heads * 128 * 4;
+    struct R {
+        const void *p;
+        size_t n;
+    } rs[] = {{q, (size_t)B * d->n_q_heads * 512}, {k_new, (size_t)B * d->n_kv_heads * 512},
+              {v_new, (size_t)B * d->n_kv_heads * 512}, {q_norm_w, 512}, {k_norm_w, 512},
+              {sinks, (size_t)d->n_q_heads * 4}, {pos, (size_t)B * 4}, {k_cache, cache_bytes},
+              {v_cache, cache_bytes}, {out, out_bytes}, {ws, L.total}};
+    const int nr = sizeof(rs) / sizeof(rs[0]);
+    for (int i = 7; i < nr; i++)  // caches, out and ws against every other buffer
+        for (int j = 0; j < nr; j++) {
+            if (i == j || (j > 6 && j < i)) continue;
+            const char *a0 = static_cast<const char *>(rs[i].p), *b0 = static_cast<const char *>(rs[j].p);
+            if (a0 < b0 + rs[j].n && b0 < a0 + rs[i].n)
+                return fail(MOE_ERR_INVALID_ARG, std::string(names[i < 10 ? i : 0]) + " overlaps another buffer");
+        }
+    moe::AttnArgs a{};
+    a.B = B;
+    a.Hq = d->n_q_heads;
+    a.Hkv = d->n_kv_heads;
+    a.window = d->window;
+    a.max_len = max_len;
+    a.chunk = moe::attn_chunk_size(d->window, max_len, B, d->n_kv_heads);
+    a.n_chunks = moe::attn_chunk_slots(d->window, max_len, a.chunk);
+    a.rope_base = d->rope_base;
+    a.eps = d->norm_eps;
+    a.q = q;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.q_norm_w = q_norm_w;
+    a.k_norm_w = k_norm_w;
+    a.sinks = sinks;
+    a.pos = pos;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.out = out;
+    a.q_prep = at<float>(ws, L.q_prep);
+    a.part_m = at<float>(ws, L.part_m);
+    a.part_l = at<float>(ws, L.part_l);
+    a.part_o = at<float>(ws, L.part_o);
+    *args = a;
+    return MOE_OK;
+}
+
+moe_status moe_attn_decode(const moe_attn_dims *d, int32_t n_seqs, int32_t max_len, const float *q, const float *k_new,
+                           const float *v_new, const float *q_norm_w, const float *k_norm_w, const float *sinks,
+                           const int32_t *pos, uint16_t *k_cache, uint16_t *v_cache, float *out, void *ws,
+                           size_t ws_bytes, void *stream) {
+    moe::AttnArgs a{};
+    MOE_TRY(attn_prepare(d, n_seqs, max_len, q, k_new, v_new, q_norm_w, k_norm_w, sinks, pos, k_cache, v_cache, out,
+                         ws, ws_bytes, &a));
+    return hip_status(moe::launch_attn(a, static_cast<hipStream_t>(stream)), "attention launch");
+}
+
+moe_status moe_attn_decode_timed(const moe_attn_dims *d, int32_t n_seqs, int32_t max_len, const float *q,
+                                 const float *k_new, const float *v_new, const float *q_norm_w, const float *k_norm_w,
+                                 const float *sinks, const int32_t *pos, uint16_t *k_cache, uint16_t *v_cache,
+                                 float *out, void *ws, size_t ws_bytes, float *kernel_us, void *stream) {
+    if (!kernel_us) return fail(MOE_ERR_INVALID_ARG, "kernel_us is NULL");
+    moe::AttnArgs a{};
+    MOE_TRY(attn_prepare(d, n_seqs, max_len, q, k_new, v_new, q_norm_w, k_norm_w, sinks, pos, k_cache, v_cache, out,
+                         ws, ws_bytes, &a));
+    hipEvent_t ev[6] = {};
+    for (auto &e : ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (auto &f : ev)
+                if (f) (void)hipEventDestroy(f);
+            return fail(MOE_ERR_HIP, "hipEventCreate failed");
+        }
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    a.ev = ev;
+    moe_status s = hip_status(moe::launch_attn(a, st), "attention launch");
+    if (s == MOE_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(MOE_ERR_HIP, "stream synchronize failed");
+    if (s == MOE_OK) {
+        for (int k = 0; k < 3; k++) {
+            float ms = 0.f;
+            kernel_us[k] = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1]) == hipSuccess ? ms * 1e3f : -1.f;
+        }
+        (void)hipGetLastError();
+    }
+    for (auto &e : ev) (void)hipEventDestroy(e);
+    return s == MOE_OK ? ok() : s;
+}
+
 const char *moe_status_string(moe_status s) {
     switch (s) {
     case MOE_OK: return "ok";

@@ -79,6 +79,25 @@ hipError_t launch_lm_head(const LmHeadArgs &a, hipStream_t st);
 hipError_t launch_repack_q4_1_matrix(const uint8_t *canonical, uint8_t *packed, long long rows, int k,
                                      hipStream_t st);
 
+// Decode attention (one new token per sequence), head size 128.
+struct AttnArgs {
+    int B, Hq, Hkv, window, max_len;
+    int chunk;     // positions per chunk: attn_chunk_size(window, max_len, B, Hkv)
+    int n_chunks;  // chunk slots per (sequence, head): attn_chunk_slots(window, max_len, chunk)
+    float rope_base, eps;
+    const float *q, *k_new, *v_new, *q_norm_w, *k_norm_w, *sinks;
+    const int32_t *pos;
+    uint16_t *k_cache, *v_cache;  // bf16 [B, Hkv, max_len, 128]
+    float *out;                   // [B, Hq, 128]
+    float *q_prep;                // workspace [B, Hq, 128]
+    float *part_m, *part_l;       // workspace [B, Hq, n_chunks]
+    float *part_o;                // workspace [B, Hq, n_chunks, 128]
+    hipEvent_t *ev;               // optional start/stop pairs for the 3 kernels
+};
+int attn_chunk_size(int window, int max_len, int B, int Hkv);
+int attn_chunk_slots(int window, int max_len, int chunk);
+hipError_t launch_attn(const AttnArgs &a, hipStream_t st);
+
 hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
 // Batch-1 path (three kernels per layer); hipErrorNotSupported if the shape
 // is outside what it was built for (the caller then takes launch_decode).

@@ -152,3 +152,29 @@ def test_lm_head_sizes_and_checks(L):
     kus = ctypes.c_float()
     assert L.moe_lm_head_timed(V, D, 1, fake, None, fake, 0, 1, out, None, None) == INVALID
     assert L.moe_lm_head_timed(V, D, 1, fake, None, fake, 0, 0, out, ctypes.byref(kus), None) == INVALID
+
+
+def test_attn_checks(L):
+    d = B.attn_dims(32, 4, 513)
+    n = ctypes.c_size_t()
+    assert L.moe_attn_workspace_size(ctypes.byref(d), 1, 8192, ctypes.byref(n)) == OK and n.value > 0
+    full = B.attn_dims(32, 4, 0)
+    n2 = ctypes.c_size_t()
+    assert L.moe_attn_workspace_size(ctypes.byref(full), 1, 8192, ctypes.byref(n2)) == OK and n2.value > n.value
+    for bad, code in ((B.CAttnDims(32, 4, 64, 513, 1e4, 1e-6), UNSUPPORTED), (B.CAttnDims(30, 4, 128, 513, 1e4, 1e-6), INVALID),
+                      (B.CAttnDims(48, 4, 128, 513, 1e4, 1e-6), UNSUPPORTED), (B.CAttnDims(32, 4, 128, -1, 1e4, 1e-6), INVALID),
+                      (B.CAttnDims(32, 4, 128, 513, 0.0, 1e-6), INVALID), (B.CAttnDims(32, 4, 128, 513, 1e4, -1.0), INVALID)):
+        assert L.moe_attn_workspace_size(ctypes.byref(bad), 1, 8192, ctypes.byref(n)) == code
+    assert L.moe_attn_workspace_size(ctypes.byref(d), 0, 8192, ctypes.byref(n)) == INVALID
+    assert L.moe_attn_workspace_size(ctypes.byref(d), 1, 0, ctypes.byref(n)) == INVALID
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
+    ws = ctypes.c_void_p(0x40000000)
+    args = lambda **kw: [ctypes.byref(d), 1, 8192] + [kw.get(str(i), p[i]) for i in range(10)] + [kw.get("ws", ws), kw.get("wsb", 1 << 30), None]
+    assert L.moe_attn_decode(*args(**{"0": None})) == INVALID                         # NULL q
+    assert L.moe_attn_decode(*args(**{"6": ctypes.c_void_p(0x700004)})) == ALIGNMENT  # misaligned pos
+    assert L.moe_attn_decode(*args(wsb=16)) == WORKSPACE
+    # the k cache (2 MiB at 0x800000) overlapping the v cache
+    assert L.moe_attn_decode(*args(**{"8": ctypes.c_void_p(0x810000)})) == INVALID
+    assert b"overlaps" in L.moe_last_error()
+    kus = (ctypes.c_float * 3)()
+    assert L.moe_attn_decode_timed(*(args(**{"0": None})[:-1] + [kus, None])) == INVALID

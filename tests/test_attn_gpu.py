@@ -1,0 +1,132 @@
+"""GPU parity of decode attention against the CPU oracle.
+
+The oracle receives the generator's caches and writes the new key and value
+itself; the GPU writes them into its own copy.  Outputs are compared per
+(sequence, head) by relative L2 error; the stored new values must equal the
+oracle's, and the stored new keys may differ only where the fp32 and fp64
+keys round to neighbouring bfloat16 values."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_moe_decode_route_amd import binding as B
+from sparse_moe_decode_route_amd import inputs as gen
+from tests.helpers import rel_l2
+
+pytestmark = pytest.mark.gpu
+
+# fp32 sums over 128 products and over at most 256 positions per chunk, fp32
+# exponentials: relative errors near 1e-6.  A key that rounds to the
+# neighbouring bfloat16 shifts one score by ~2^-8 of its size; 1e-4 leaves
+# room for a few of those and catches any 16-bit arithmetic on the path.
+ATTN_TOL = 1e-4
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return torch.device("cuda:0")
+
+
+def _run(Hq, Hkv, window, max_len, pos, cfg_id, draw=0, base=gen.ATTN_ROPE_BASE, eps=1e-6, label=""):
+    Bn = len(pos)
+    a = gen.make_attn(Bn, Hq, Hkv, 128, max_len, cfg_id=cfg_id, draw=draw)
+    want, okc, ovc = oracle.attn_decode(a.q.numpy(), a.k_new.numpy(), a.v_new.numpy(), a.q_norm_w.numpy(),
+                                        a.k_norm_w.numpy(), a.sinks.numpy(), a.k_cache.numpy().view(np.uint16),
+                                        a.v_cache.numpy().view(np.uint16), np.array(pos), window, base, eps)
+    d = gen.AttnInputs(*(t.to(_dev()) for t in (a.q, a.k_new, a.v_new, a.q_norm_w, a.k_norm_w, a.sinks,
+                                                  a.k_cache, a.v_cache)))
+    dims = B.attn_dims(Hq, Hkv, window, base, eps)
+    out = B.attn_decode(dims, d, torch.tensor(pos, dtype=torch.int32, device=_dev()))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    err = rel_l2(got.reshape(-1, 128), want.reshape(-1, 128))
+    kc = d.k_cache.cpu().numpy().view(np.uint16)
+    vc = d.v_cache.cpu().numpy().view(np.uint16)
+    nflip = 0
+    for b, P in enumerate(pos):
+        if not 0 <= P < max_len:
+            continue
+        assert np.array_equal(vc[b, :, P], ovc[b, :, P])
+        diff = kc[b, :, P].astype(np.int32) - okc[b, :, P].astype(np.int32)
+        assert np.all(np.abs(diff) <= 1), diff
+        nflip += int(np.count_nonzero(diff))
+        # nothing else in the caches changed
+        keep = np.ones(max_len, bool)
+        keep[P] = False
+        assert np.array_equal(kc[b][:, keep], okc[b][:, keep]) and np.array_equal(vc[b][:, keep], ovc[b][:, keep])
+    print(f"[{label}] Hq={Hq} Hkv={Hkv} window={window} pos={pos} max rel-L2 {err.max():.3e} "
+          f"key bf16 neighbours {nflip}")
+    assert np.all(np.isfinite(got))
+    assert err.max() <= ATTN_TOL, err.max()
+    return got, want
+
+
+def test_attn_sliding_window_ragged_positions():
+    # first position only, a partial window, and a full window that starts
+    # inside a chunk (lo = 588) and spans three chunks
+    _run(32, 4, 513, 1200, [0, 300, 1100], cfg_id=71, label="swa")
+
+
+def test_attn_full_attention():
+    _run(32, 4, 0, 3000, [2999, 777, 255, 256], cfg_id=72, label="full")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (16, 4), (8, 1)])
+@pytest.mark.parametrize("window", [513, 0])
+def test_attn_group_sizes(Hq, Hkv, window):
+    _run(Hq, Hkv, window, 900, [899, 512, 17], cfg_id=73, label="groups")
+
+
+def test_attn_window_sizes_and_eps():
+    _run(32, 4, 1, 300, [0, 299], cfg_id=74, label="window 1")
+    _run(32, 4, 257, 1000, [999, 256, 257], cfg_id=74, eps=0.0, base=1e6, label="window 257")
+
+
+def test_attn_long_positions_rotary_accuracy():
+    # positions near 2^17: the rotary angle needs more than fp32 (reduced in fp64)
+    _run(32, 4, 513, 131072, [131071, 100003], cfg_id=75, label="long swa")
+
+
+def test_attn_full_128k_context():
+    _run(32, 4, 0, 131072, [131071], cfg_id=76, label="full 128k")
+
+
+def test_attn_invalid_position_gives_nan_and_keeps_caches():
+    a = gen.make_attn(2, 32, 4, 128, 64, cfg_id=77)
+    d = gen.AttnInputs(*(t.to(_dev()) for t in (a.q, a.k_new, a.v_new, a.q_norm_w, a.k_norm_w, a.sinks,
+                                                  a.k_cache, a.v_cache)))
+    kc0, vc0 = d.k_cache.clone(), d.v_cache.clone()
+    out = B.attn_decode(B.attn_dims(32, 4, 513), d, torch.tensor([64, 10], dtype=torch.int32, device=_dev()))
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0]).all() and torch.isfinite(out[1]).all()
+    assert torch.equal(d.k_cache[0], kc0[0]) and torch.equal(d.v_cache[0], vc0[0])
+
+
+def test_attn_deterministic_graph_and_timed():
+    a = gen.make_attn(2, 32, 4, 128, 4096, cfg_id=78)
+    d = gen.AttnInputs(*(t.to(_dev()) for t in (a.q, a.k_new, a.v_new, a.q_norm_w, a.k_norm_w, a.sinks,
+                                                  a.k_cache, a.v_cache)))
+    dims = B.attn_dims(32, 4, 0)
+    pos = torch.tensor([4095, 2000], dtype=torch.int32, device=_dev())
+    ws = B.attn_workspace(dims, 2, 4096)
+    r1 = B.attn_decode(dims, d, pos, ws=ws)
+    r2 = B.attn_decode(dims, d, pos, ws=ws)
+    out = torch.empty_like(r1)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.attn_decode(dims, d, pos, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.attn_decode(dims, d, pos, out=out, ws=ws)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, r1)
+    assert torch.equal(r1, r2)
+    r3, us = B.attn_decode_timed(dims, d, pos, ws=ws)
+    assert torch.equal(r3, r1) and all(v > 0 for v in us.values())
