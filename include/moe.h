@@ -311,9 +311,9 @@ moe_status moe_attn_decode(const moe_attn_dims *dims, int32_t n_seqs, int32_t ma
                            const float *sinks, const int32_t *pos, uint16_t *k_cache, uint16_t *v_cache, float *out,
                            void *ws, size_t ws_bytes, void *stream);
 
-/* Measurement variant: the same three kernels, each launched with a
-   start/stop event pair on its dispatch; kernel_us (host) float [3]
-   receives their durations (prep, chunks, combine) in microseconds.
+/* Measurement variant: the same two kernels, each launched with a
+   start/stop event pair on its dispatch; kernel_us (host) float [2]
+   receives their durations (chunks, combine) in microseconds.
    Blocks the calling thread; not for use under stream capture. */
 moe_status moe_attn_decode_timed(const moe_attn_dims *dims, int32_t n_seqs, int32_t max_len, const float *q,
                                  const float *k_new, const float *v_new, const float *q_norm_w,

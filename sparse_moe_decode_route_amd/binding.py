@@ -395,6 +395,6 @@ def attn_decode_timed(dims: CAttnDims, a: gen.AttnInputs, pos: torch.Tensor, out
                       ws: Optional[torch.Tensor] = None, stream=None):
     """moe_attn_decode_timed: (out, {kernel: us}).  Synchronises the stream."""
     args, out = _attn_args(dims, a, pos, out, ws)
-    us = (ctypes.c_float * 3)()
+    us = (ctypes.c_float * 2)()
     _check(lib().moe_attn_decode_timed(*args, us, _stream(stream)))
-    return out, dict(zip(("attn_prep", "attn_chunk", "attn_combine"), (float(v) for v in us)))
+    return out, dict(zip(("attn_chunk", "attn_combine"), (float(v) for v in us)))

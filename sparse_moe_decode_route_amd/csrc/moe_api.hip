@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <string>
 #include <vector>
@@ -628,7 +629,7 @@ moe_status moe_lm_head_timed(int32_t vocab, int32_t d_model, int32_t wfmt, const
 // ---- decode attention ----
 
 struct AttnWs {
-    size_t q_prep, part_m, part_l, part_o, total;
+    size_t part_m, part_l, part_o, total;
 };
 
 static AttnWs attn_ws(const moe_attn_dims &d, int B, int max_len) {
@@ -641,7 +642,6 @@ static AttnWs attn_ws(const moe_attn_dims &d, int B, int max_len) {
         o += align_up(bytes);
         return at;
     };
-    L.q_prep = take((size_t)B * d.n_q_heads * 128 * 4);
     L.part_m = take((size_t)B * d.n_q_heads * nc * 4);
     L.part_l = take((size_t)B * d.n_q_heads * nc * 4);
     L.part_o = take((size_t)B * d.n_q_heads * nc * 128 * 4);
@@ -714,6 +714,7 @@ static moe_status attn_prepare(const moe_attn_dims *d, int32_t B, int32_t max_le
     a.n_chunks = moe::attn_chunk_slots(d->window, max_len, a.chunk);
     a.rope_base = d->rope_base;
     a.eps = d->norm_eps;
+    for (int i = 0; i < 64; i++) a.rope_freq[i] = std::pow((double)d->rope_base, -2.0 * i / 128.0);
     a.q = q;
     a.k_new = k_new;
     a.v_new = v_new;
@@ -724,7 +725,6 @@ static moe_status attn_prepare(const moe_attn_dims *d, int32_t B, int32_t max_le
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     a.out = out;
-    a.q_prep = at<float>(ws, L.q_prep);
     a.part_m = at<float>(ws, L.part_m);
     a.part_l = at<float>(ws, L.part_l);
     a.part_o = at<float>(ws, L.part_o);
@@ -750,7 +750,7 @@ moe_status moe_attn_decode_timed(const moe_attn_dims *d, int32_t n_seqs, int32_t
     moe::AttnArgs a{};
     MOE_TRY(attn_prepare(d, n_seqs, max_len, q, k_new, v_new, q_norm_w, k_norm_w, sinks, pos, k_cache, v_cache, out,
                          ws, ws_bytes, &a));
-    hipEvent_t ev[6] = {};
+    hipEvent_t ev[4] = {};
     for (auto &e : ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             for (auto &f : ev)
@@ -763,7 +763,7 @@ moe_status moe_attn_decode_timed(const moe_attn_dims *d, int32_t n_seqs, int32_t
     moe_status s = hip_status(moe::launch_attn(a, st), "attention launch");
     if (s == MOE_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(MOE_ERR_HIP, "stream synchronize failed");
     if (s == MOE_OK) {
-        for (int k = 0; k < 3; k++) {
+        for (int k = 0; k < 2; k++) {
             float ms = 0.f;
             kernel_us[k] = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1]) == hipSuccess ? ms * 1e3f : -1.f;
         }

@@ -11,16 +11,17 @@
 // embedding turns the pairs (i, i + 64) by P * base^(-2i/128); the cache
 // holds bfloat16 keys (normalised and rotated) and values.
 //
-// Three kernels:
-//   attn_prep    per head: RMSNorm, rotary embedding (angle reduced in fp64,
-//                since P * freq needs more than fp32 at long positions), the
-//                query scaled by 1/sqrt(128) into the workspace, the new key
-//                and value rounded to bfloat16 into the caches at P;
+// Two kernels:
 //   attn_chunk   per (sequence, key/value head, chunk of positions): the
-//                group's query heads against the chunk's keys (scores to
-//                LDS), the chunk's max and exp-sum per head, then the values
-//                weighted by the exponentials; partial (max, sum, output)
-//                per chunk to the workspace;
+//                group's query heads normalised and rotated in registers
+//                (the 64 rotary angles reduced in fp64, since P * freq needs
+//                more than fp32 at long positions), against the chunk's keys
+//                (scores to LDS), the chunk's max and exp-sum per head, then
+//                the values weighted by the exponentials; partial (max, sum,
+//                output) per chunk to the workspace.  The block whose chunk
+//                holds P computes the new key (normalised, rotated) and value
+//                in bf16, uses them for row P and writes them to the caches;
+//                no other block reads row P;
 //   attn_combine per (sequence, query head): the chunks merged with the
 //                sink in a fixed order: out = sum_c e^(m_c - M) o_c /
 //                (e^(z - M) + sum_c e^(m_c - M) l_c), M = max(z, max_c m_c).
@@ -45,7 +46,6 @@ namespace {
 constexpr int AT_D = 128;       // head size
 constexpr int AT_CMAX = 1024;   // largest chunk (positions)
 constexpr int AT_UT = 4;        // tiles of 8 positions per load group
-constexpr int AT_PREP_WAVES = 8;
 constexpr int AT_COMB_WAVES = 16;
 
 __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
@@ -60,48 +60,6 @@ __device__ __forceinline__ int attn_lo(const AttnArgs &p, int P) {
 // First chunk a sequence reads.
 __device__ __forceinline__ int attn_first_chunk(const AttnArgs &p, int P) {
     return p.window > 0 ? attn_lo(p, P) / p.chunk : 0;
-}
-
-__global__ void __launch_bounds__(64 * AT_PREP_WAVES) attn_prep(AttnArgs p) {
-    const int lane = threadIdx.x & 63;
-    const int hi = blockIdx.y * AT_PREP_WAVES + (threadIdx.x >> 6);
-    const int b = blockIdx.x;
-    if (hi >= p.Hq + p.Hkv) return;
-    const int P = p.pos[b];
-    if (P < 0 || P >= p.max_len) return;  // invalid position: caches untouched, output NaN (combine)
-    const bool is_q = hi < p.Hq;
-    const float *src = is_q ? p.q + ((size_t)b * p.Hq + hi) * AT_D : p.k_new + ((size_t)b * p.Hkv + hi - p.Hq) * AT_D;
-    const float *w = is_q ? p.q_norm_w : p.k_norm_w;
-    float x0 = src[lane], x1 = src[lane + 64];
-    const float inv = 1.0f / sqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)AT_D + p.eps);
-    float y0 = x0 * inv * w[lane], y1 = x1 * inv * w[lane + 64];
-    if (p.window > 0) {
-        // angle P * base^(-2 lane / 128), reduced modulo 2 pi in fp64
-        const double freq = exp2(-2.0 * lane / AT_D * log2((double)p.rope_base));
-        const double two_pi = 6.283185307179586476925286766559;
-        double ang = (double)P * freq;
-        ang -= two_pi * floor(ang / two_pi);
-        double sd, cd;
-        sincos(ang, &sd, &cd);
-        const float c = (float)cd, s = (float)sd;
-        const float r0 = y0 * c - y1 * s, r1 = y0 * s + y1 * c;
-        y0 = r0;
-        y1 = r1;
-    }
-    if (is_q) {
-        const float sc = 0.08838834764831845f;  // 1 / sqrt(128)
-        float *dst = p.q_prep + ((size_t)b * p.Hq + hi) * AT_D;
-        dst[lane] = y0 * sc;
-        dst[lane + 64] = y1 * sc;
-    } else {
-        const int g = hi - p.Hq;
-        const size_t row = (((size_t)b * p.Hkv + g) * p.max_len + P) * AT_D;
-        p.k_cache[row + lane] = to_bf16_rne(y0);
-        p.k_cache[row + lane + 64] = to_bf16_rne(y1);
-        const float *vs = p.v_new + ((size_t)b * p.Hkv + g) * AT_D;
-        p.v_cache[row + lane] = to_bf16_rne(vs[lane]);
-        p.v_cache[row + lane + 64] = to_bf16_rne(vs[lane + 64]);
-    }
 }
 
 // v from lane ^ (1 << s), every lane active
@@ -132,6 +90,38 @@ __device__ __forceinline__ void unpack16(const uint4 &a, const uint4 &b, float (
 }
 
 // HW query heads per wave, WV waves per block (HW * WV = group size).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)to_bf16_rne(lo) | ((uint32_t)to_bf16_rne(hi) << 16);
+}
+
+// This lane's 16 values (dimensions 16 sub .. 16 sub + 15) of one head:
+// RMSNorm over the head's 128 values (the 8 lanes of a position hold them),
+// gain, and the rotary turn of the pairs (i, i + 64) with cos / sin from cs;
+// the partner of a lane's values sits in lane ^ 4.
+__device__ __forceinline__ void head_prep(float (&x)[16], const float *gain, const float (*cs)[64], bool rope,
+                                          float eps, int lane) {
+    const int sub = lane & 7;
+    float ss = 0.f;
+#pragma unroll
+    for (int d = 0; d < 16; d++) ss = __builtin_fmaf(x[d], x[d], ss);
+    ss += at_xor(ss, 0);
+    ss += at_xor(ss, 1);
+    ss += at_xor(ss, 2);
+    const float inv = 1.0f / sqrtf(ss / (float)AT_D + eps);
+#pragma unroll
+    for (int d = 0; d < 16; d++) x[d] = x[d] * inv * gain[16 * sub + d];
+    if (rope) {
+        const bool high = sub >= 4;
+        const int i0 = 16 * (sub & 3);
+#pragma unroll
+        for (int d = 0; d < 16; d++) {
+            const float y = at_xor(x[d], 2);  // the partner value
+            const float c = cs[0][i0 + d], s = cs[1][i0 + d];
+            x[d] = high ? y * s + x[d] * c : x[d] * c - y * s;
+        }
+    }
+}
+
 // Score partials of one tile (8 positions) for HW heads, summed over the
 // position's 8 lanes: each level halves the heads a lane carries, then the
 // remaining levels add; lanes with sub < HW end holding head sub.
@@ -179,25 +169,11 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
     const int start = max(c0, lo), end = min(c0 + p.chunk, P + 1);  // [start, end)
     if (start >= end) return;
     const int h0 = g * (HW * WV) + w * HW;
-    float qv[HW][16];
-#pragma unroll
-    for (int h = 0; h < HW; h++) {
-        const float4 *qs = reinterpret_cast<const float4 *>(p.q_prep + ((size_t)b * p.Hq + h0 + h) * AT_D + 16 * sub);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float4 f = qs[i];
-            qv[h][4 * i] = f.x;
-            qv[h][4 * i + 1] = f.y;
-            qv[h][4 * i + 2] = f.z;
-            qv[h][4 * i + 3] = f.w;
-        }
-    }
     const size_t base = ((size_t)b * p.Hkv + g) * p.max_len;
     const uint4 *K = reinterpret_cast<const uint4 *>(p.k_cache + base * AT_D) + 2 * sub;
     const uint4 *V = reinterpret_cast<const uint4 *>(p.v_cache + base * AT_D) + 2 * sub;
     const int n = end - start;
     const int ngrp = (n + 8 * AT_UT - 1) / (8 * AT_UT);  // load groups of AT_UT tiles
-
     // rows of group gi into (x, y); rows past the chunk's end re-read its last row
     auto issue = [&](const uint4 *M, uint4 (&x)[AT_UT], uint4 (&y)[AT_UT], int gi) {
 #pragma unroll
@@ -207,10 +183,110 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
             y[u] = ld_stream16(M + (size_t)j * 16 + 1);
         }
     };
+    // the first groups of keys and values are requested before anything else
+    uint4 xa[AT_UT], ya[AT_UT], va[AT_UT], vb[AT_UT];
+    issue(K, xa, ya, 0);
+    issue(V, va, vb, 0);
+
+    // cos / sin of the 64 rotary angles P * freq_i: the product and its
+    // reduction modulo 2 pi in fp64 (P * freq needs more than fp32 at long
+    // positions), the reduced angle's sine and cosine in fp32
+    __shared__ float cs[2][64];
+    const bool rope = p.window > 0;
+    if (rope) {
+        if (threadIdx.x < 64) {
+            const double two_pi = 6.283185307179586476925286766559;
+            double ang = (double)P * p.rope_freq[threadIdx.x];
+            ang -= two_pi * floor(ang / two_pi);
+            float sf, cf;
+            sincosf((float)ang, &sf, &cf);
+            cs[0][threadIdx.x] = cf;
+            cs[1][threadIdx.x] = sf;
+        }
+        __syncthreads();
+    }
+    // this wave's query heads: normalised, rotated, scaled by 1/sqrt(128)
+    float qv[HW][16];
+#pragma unroll
+    for (int h = 0; h < HW; h++) {
+        const float4 *qs = reinterpret_cast<const float4 *>(p.q + ((size_t)b * p.Hq + h0 + h) * AT_D + 16 * sub);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float4 f = qs[i];
+            qv[h][4 * i] = f.x;
+            qv[h][4 * i + 1] = f.y;
+            qv[h][4 * i + 2] = f.z;
+            qv[h][4 * i + 3] = f.w;
+        }
+        head_prep(qv[h], p.q_norm_w, cs, rope, p.eps, lane);
+#pragma unroll
+        for (int d = 0; d < 16; d++) qv[h][d] *= 0.08838834764831845f;  // 1 / sqrt(128)
+    }
+    // the chunk holding P: the new key (normalised, rotated) and value in
+    // bf16, used in place of the cache row P, which this block also writes
+    const bool hasP = end == P + 1;
+    uint4 kn0 = make_uint4(0, 0, 0, 0), kn1 = kn0, vn0 = kn0, vn1 = kn0;
+    if (hasP) {
+        float kx[16], vx[16];
+        const float4 *ks = reinterpret_cast<const float4 *>(p.k_new + ((size_t)b * p.Hkv + g) * AT_D + 16 * sub);
+        const float4 *vs = reinterpret_cast<const float4 *>(p.v_new + ((size_t)b * p.Hkv + g) * AT_D + 16 * sub);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float4 f = ks[i], e = vs[i];
+            kx[4 * i] = f.x;
+            kx[4 * i + 1] = f.y;
+            kx[4 * i + 2] = f.z;
+            kx[4 * i + 3] = f.w;
+            vx[4 * i] = e.x;
+            vx[4 * i + 1] = e.y;
+            vx[4 * i + 2] = e.z;
+            vx[4 * i + 3] = e.w;
+        }
+        head_prep(kx, p.k_norm_w, cs, rope, p.eps, lane);
+        kn0 = make_uint4(pack_bf16x2(kx[0], kx[1]), pack_bf16x2(kx[2], kx[3]), pack_bf16x2(kx[4], kx[5]),
+                         pack_bf16x2(kx[6], kx[7]));
+        kn1 = make_uint4(pack_bf16x2(kx[8], kx[9]), pack_bf16x2(kx[10], kx[11]), pack_bf16x2(kx[12], kx[13]),
+                         pack_bf16x2(kx[14], kx[15]));
+        vn0 = make_uint4(pack_bf16x2(vx[0], vx[1]), pack_bf16x2(vx[2], vx[3]), pack_bf16x2(vx[4], vx[5]),
+                         pack_bf16x2(vx[6], vx[7]));
+        vn1 = make_uint4(pack_bf16x2(vx[8], vx[9]), pack_bf16x2(vx[10], vx[11]), pack_bf16x2(vx[12], vx[13]),
+                         pack_bf16x2(vx[14], vx[15]));
+        if (w == 0 && pg == 0) {
+            const size_t row = (((size_t)b * p.Hkv + g) * p.max_len + P) * AT_D;
+            uint4 *kd = reinterpret_cast<uint4 *>(p.k_cache + row) + 2 * sub;
+            uint4 *vd = reinterpret_cast<uint4 *>(p.v_cache + row) + 2 * sub;
+            kd[0] = kn0;
+            kd[1] = kn1;
+            vd[0] = vn0;
+            vd[1] = vn1;
+        }
+    }
+    // row P of the first groups is the new key / value
+#pragma unroll
+    for (int u = 0; u < AT_UT; u++) {
+        if (start + min(u * 8 + pg, n - 1) == P) {
+            xa[u] = kn0;
+            ya[u] = kn1;
+            va[u] = vn0;
+            vb[u] = vn1;
+        }
+    }
+    // later groups: rows of group gi, row P replaced by (nx, ny)
+    auto issue_p = [&](const uint4 *M, uint4 (&x)[AT_UT], uint4 (&y)[AT_UT], int gi, const uint4 &nx,
+                       const uint4 &ny) {
+        issue(M, x, y, gi);
+#pragma unroll
+        for (int u = 0; u < AT_UT; u++) {
+            if (start + min((gi * AT_UT + u) * 8 + pg, n - 1) == P) {
+                x[u] = nx;
+                y[u] = ny;
+            }
+        }
+    };
 
     // scores, two load groups in registers
     {
-        uint4 xa[AT_UT], ya[AT_UT], xb[AT_UT], yb[AT_UT];
+        uint4 xb[AT_UT], yb[AT_UT];
         auto scores = [&](const uint4 (&x)[AT_UT], const uint4 (&y)[AT_UT], int gi) {
 #pragma unroll
             for (int u = 0; u < AT_UT; u++) {
@@ -219,11 +295,10 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
                 if (jj < n && sub < HW) sc[w][jj][sub] = s;
             }
         };
-        issue(K, xa, ya, 0);
         for (int gi = 0; gi < ngrp; gi += 2) {
-            if (gi + 1 < ngrp) issue(K, xb, yb, gi + 1);
+            if (gi + 1 < ngrp) issue_p(K, xb, yb, gi + 1, kn0, kn1);
             scores(xa, ya, gi);
-            if (gi + 2 < ngrp) issue(K, xa, ya, gi + 2);
+            if (gi + 2 < ngrp) issue_p(K, xa, ya, gi + 2, kn0, kn1);
             if (gi + 1 < ngrp) scores(xb, yb, gi + 1);
         }
     }
@@ -256,7 +331,7 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
 #pragma unroll
         for (int d = 0; d < 16; d++) o[h][d] = 0.f;
     {
-        uint4 xa[AT_UT], ya[AT_UT], xb[AT_UT], yb[AT_UT];
+        uint4 xb[AT_UT], yb[AT_UT];
         auto accum = [&](const uint4 (&x)[AT_UT], const uint4 (&y)[AT_UT], int gi) {
 #pragma unroll
             for (int u = 0; u < AT_UT; u++) {
@@ -272,11 +347,10 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
                 }
             }
         };
-        issue(V, xa, ya, 0);
         for (int gi = 0; gi < ngrp; gi += 2) {
-            if (gi + 1 < ngrp) issue(V, xb, yb, gi + 1);
-            accum(xa, ya, gi);
-            if (gi + 2 < ngrp) issue(V, xa, ya, gi + 2);
+            if (gi + 1 < ngrp) issue_p(V, xb, yb, gi + 1, vn0, vn1);
+            accum(va, vb, gi);
+            if (gi + 2 < ngrp) issue_p(V, va, vb, gi + 2, vn0, vn1);
             if (gi + 1 < ngrp) accum(xb, yb, gi + 1);
         }
     }
@@ -394,19 +468,20 @@ void launch_chunks(const AttnArgs &p, hipStream_t st) {
     const dim3 grid(p.n_chunks, p.Hkv, p.B);
     auto kern = attn_chunk<HW, WV>;
     if (p.ev)
-        hipExtLaunchKernelGGL(kern, grid, dim3(64 * WV), 0, st, p.ev[2], p.ev[3], 0, p);
+        hipExtLaunchKernelGGL(kern, grid, dim3(64 * WV), 0, st, p.ev[0], p.ev[1], 0, p);
     else
         hipLaunchKernelGGL(kern, grid, dim3(64 * WV), 0, st, p);
 }
 
 }  // namespace
 
-// Chunk size: 64 positions for a sliding window (its 513 positions then
-// spread over 9-10 blocks per key/value head); for full attention the
+// Chunk size: 32 positions for a sliding window (its 513 positions then
+// spread over 17-18 blocks per key/value head, each with one load group of
+// keys and one of values in flight); for full attention the
 // smallest power of two in [64, 1024] that keeps the blocks of a call to
 // about 1024 at the cache's full length.
 int attn_chunk_size(int window, int max_len, int B, int Hkv) {
-    if (window > 0) return 64;
+    if (window > 0) return 32;
     int c = 64;
     while (c < AT_CMAX && (long long)((max_len + c - 1) / c) * B * Hkv > 1024) c *= 2;
     return c;
@@ -421,11 +496,6 @@ int attn_chunk_slots(int window, int max_len, int chunk) {
 
 hipError_t launch_attn(const AttnArgs &a, hipStream_t st) {
     AttnArgs p = a;
-    const dim3 gp(p.B, (p.Hq + p.Hkv + AT_PREP_WAVES - 1) / AT_PREP_WAVES);
-    if (p.ev)
-        hipExtLaunchKernelGGL(attn_prep, gp, dim3(64 * AT_PREP_WAVES), 0, st, p.ev[0], p.ev[1], 0, p);
-    else
-        hipLaunchKernelGGL(attn_prep, gp, dim3(64 * AT_PREP_WAVES), 0, st, p);
     const int grp = p.Hq / p.Hkv;
     if (grp == 8)
         launch_chunks<4, 2>(p, st);
@@ -437,7 +507,7 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t st) {
         launch_chunks<1, 1>(p, st);
     const dim3 gc(p.B, p.Hq);
     if (p.ev)
-        hipExtLaunchKernelGGL(attn_combine, gc, dim3(64 * AT_COMB_WAVES), 0, st, p.ev[4], p.ev[5], 0, p);
+        hipExtLaunchKernelGGL(attn_combine, gc, dim3(64 * AT_COMB_WAVES), 0, st, p.ev[2], p.ev[3], 0, p);
     else
         hipLaunchKernelGGL(attn_combine, gc, dim3(64 * AT_COMB_WAVES), 0, st, p);
     return hipGetLastError();

@@ -85,14 +85,14 @@ struct AttnArgs {
     int chunk;     // positions per chunk: attn_chunk_size(window, max_len, B, Hkv)
     int n_chunks;  // chunk slots per (sequence, head): attn_chunk_slots(window, max_len, chunk)
     float rope_base, eps;
+    double rope_freq[64];  // base^(-2i/128), i < 64 (host-computed in fp64)
     const float *q, *k_new, *v_new, *q_norm_w, *k_norm_w, *sinks;
     const int32_t *pos;
     uint16_t *k_cache, *v_cache;  // bf16 [B, Hkv, max_len, 128]
     float *out;                   // [B, Hq, 128]
-    float *q_prep;                // workspace [B, Hq, 128]
     float *part_m, *part_l;       // workspace [B, Hq, n_chunks]
     float *part_o;                // workspace [B, Hq, n_chunks, 128]
-    hipEvent_t *ev;               // optional start/stop pairs for the 3 kernels
+    hipEvent_t *ev;               // optional start/stop pairs for the 2 kernels
 };
 int attn_chunk_size(int window, int max_len, int B, int Hkv);
 int attn_chunk_slots(int window, int max_len, int chunk);

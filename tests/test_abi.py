@@ -176,5 +176,5 @@ def test_attn_checks(L):
     # the k cache (2 MiB at 0x800000) overlapping the v cache
     assert L.moe_attn_decode(*args(**{"8": ctypes.c_void_p(0x810000)})) == INVALID
     assert b"overlaps" in L.moe_last_error()
-    kus = (ctypes.c_float * 3)()
+    kus = (ctypes.c_float * 2)()
     assert L.moe_attn_decode_timed(*(args(**{"0": None})[:-1] + [kus, None])) == INVALID
