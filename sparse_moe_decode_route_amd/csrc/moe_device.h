@@ -299,6 +299,45 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// v from lane ^ (1 << s) (every lane active)
+__device__ __forceinline__ float xor_lane(float v, int s) {
+    const int i = __float_as_int(v);
+    if (s == 0) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+    if (s == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+    if (s == 2) return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x101F));             // xor 4
+    if (s == 3) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, true)); // row_ror 8
+    if (s == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x401F));             // xor 16
+    return __shfl_xor(v, 32, 64);
+}
+
+// Sums of P values (P a power of two <= 64) over the 64 lanes; value j ends in
+// every lane l with l % P == j.  Level s pairs lane l with l ^ (1 << s): each
+// keeps the half of its values whose index has bit s equal to its own lane
+// bit and adds the partner's copy of that half, so after log2(P) levels one
+// value remains, and the last levels add it over the remaining lane bits.
+// Each sum has a fixed order.
+template <int P>
+__device__ __forceinline__ float wave_reduce_rows(float (&v)[P], int lane) {
+    float a[P];
+#pragma unroll
+    for (int j = 0; j < P; j++) a[j] = v[j];
+    int lev = 0;
+#pragma unroll
+    for (int n = P; n > 1; n >>= 1, lev++) {
+        const bool hi = (lane >> lev) & 1;
+#pragma unroll
+        for (int m = 0; m < n / 2; m++) {
+            const float keep = hi ? a[2 * m + 1] : a[2 * m];
+            const float send = hi ? a[2 * m] : a[2 * m + 1];
+            a[m] = keep + xor_lane(send, lev);
+        }
+    }
+    float r = a[0];
+#pragma unroll
+    for (int s = lev; s < 6; s++) r += xor_lane(r, s);
+    return r;
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key, -0 is

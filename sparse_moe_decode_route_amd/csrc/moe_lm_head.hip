@@ -136,45 +136,6 @@ __device__ __forceinline__ void unit_dot_multi(const WUnit &w, const XUnit<FMT> 
     }
 }
 
-// v from lane ^ (1 << s) (every lane active)
-__device__ __forceinline__ float lm_xor(float v, int s) {
-    const int i = __float_as_int(v);
-    if (s == 0) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
-    if (s == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
-    if (s == 2) return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x101F));             // xor 4
-    if (s == 3) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, true)); // row_ror 8
-    if (s == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x401F));             // xor 16
-    return __shfl_xor(v, 32, 64);
-}
-
-// Sums of P values (P a power of two <= 8) over the 64 lanes; value j ends in
-// every lane l with l % P == j.  Level s pairs lane l with l ^ (1 << s): each
-// keeps the half of its values whose index has bit s equal to its own lane
-// bit and adds the partner's copy of that half, so after log2(P) levels one
-// value remains, and the last levels add it over the remaining lane bits.
-// Each sum has a fixed order.
-template <int P>
-__device__ __forceinline__ float lm_wave_reduce(float (&v)[P], int lane) {
-    float a[P];
-#pragma unroll
-    for (int j = 0; j < P; j++) a[j] = v[j];
-    int lev = 0;
-#pragma unroll
-    for (int n = P; n > 1; n >>= 1, lev++) {
-        const bool hi = (lane >> lev) & 1;
-#pragma unroll
-        for (int m = 0; m < n / 2; m++) {
-            const float keep = hi ? a[2 * m + 1] : a[2 * m];
-            const float send = hi ? a[2 * m] : a[2 * m + 1];
-            a[m] = keep + lm_xor(send, lev);
-        }
-    }
-    float r = a[0];
-#pragma unroll
-    for (int s = lev; s < 6; s++) r += lm_xor(r, s);
-    return r;
-}
-
 template <int FMT> constexpr int lm_scale_bytes() { return FMT == FMT_Q4_1 ? 4 : FMT == FMT_NVFP4 ? 2 : 0; }
 
 // XR = activations per token per lane (32 or 64: D <= 2048 or <= 4096), TG =
@@ -273,7 +234,7 @@ __global__ __launch_bounds__(64) void lm_head_kernel(LmHeadArgs p) {
         const bool mine = lane / P == g;  // lane l keeps row l of the tile
 #pragma unroll
         for (int t = 0; t < TG; t++) {
-            const float s = lm_wave_reduce<P>(part[t], lane);
+            const float s = wave_reduce_rows<P>(part[t], lane);
             out[t] = mine ? s : out[t];
         }
     };
