@@ -107,15 +107,18 @@ ATTN_SOURCES = ("moe_attn.hip", "moe_device.h", "moe_internal.h")
 _FETCH_SCALE = 262144.0 / 131085.2  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
 _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE KiB
 COUNTER_TRAFFIC = {
-    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="f780e0e96407b4b4",
-                                              fetch_bytes=round(3940.7 * _FETCH_SCALE * 1024),
+    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="ee4985062332661a",
+                                              fetch_bytes=round(3939.9 * _FETCH_SCALE * 1024),
                                               write_bytes=round(12.7 * _WRITE_SCALE * 1024)),
-    ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="a96c28ed37160707",
-                                             fetch_bytes=round(227565.6 * _FETCH_SCALE * 1024),
-                                             write_bytes=round(28692.5 * _WRITE_SCALE * 1024)),
-    ("lm_head_q4_1_t1", "lm_head_kernel"): dict(source_digest="513bb84d9127ca42",
-                                                fetch_bytes=round(91655.9 * _FETCH_SCALE * 1024),
+    ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="d075cab14c744b5a",
+                                             fetch_bytes=round(227450.1 * _FETCH_SCALE * 1024),
+                                             write_bytes=round(28696.1 * _WRITE_SCALE * 1024)),
+    ("lm_head_q4_1_t1", "lm_head_kernel"): dict(source_digest="c45bdaa74bc3a5cb",
+                                                fetch_bytes=round(91654.2 * _FETCH_SCALE * 1024),
                                                 write_bytes=round(572.2 * _WRITE_SCALE * 1024)),
+    ("attn_full128k", "attn_chunk"): dict(source_digest="911d325de356f382",
+                                          fetch_bytes=round(152563.8 * _FETCH_SCALE * 1024),
+                                          write_bytes=round(4610.0 * _WRITE_SCALE * 1024)),
 }
 
 
@@ -638,6 +641,10 @@ def bench_attn(args, kind: str):
     part_bytes = Hq * nc * (D + 2) * 4
     algo = kv_bytes + Hq * D * 4 + part_bytes  # keys, values, queries in, chunk partials out
     ach = algo / (kus["attn_chunk"] * 1e-6) / 1e9
+    tr = COUNTER_TRAFFIC.get((f"attn_{kind}", "attn_chunk"))
+    traffic = None
+    if tr is not None and tr["source_digest"] == source_digest(ATTN_SOURCES):
+        traffic = tr["fetch_bytes"] + tr["write_bytes"]
     step_layers = n_layers if kind == "swa" else 1
     ms_step = ms_call * step_layers
     cpu = None
@@ -666,7 +673,7 @@ def bench_attn(args, kind: str):
                     timing=f"HIP graph of {per_graph} calls over {n_layers} caches, replayed",
                     graph_matches_eager=graph_matches_eager),
         roofline=dict(bound="hbm", kernel="attn_chunk", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None, algo_bytes_per_launch=algo,
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic, algo_bytes_per_launch=algo,
                       us_per_launch=round(kus["attn_chunk"], 3),
                       timing=f"HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream, mean of {n_timed} calls"),
         cpu_baseline=cpu,
