@@ -52,7 +52,15 @@ moe_status check_dims(const moe_dims *d) {
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Decode-path workspace (n_tokens <= 8).
+// Whether n_tokens runs on a decode path: up to 8 tokens always, up to 16 on
+// the small-batch path when the shape fits it.
+bool decode_tokens(const moe_dims &d, int T) {
+    if (T <= moe::MAX_DECODE_T) return true;
+    return T <= moe::MAX_BN_T && d.n_shared >= 1 &&
+           moe::decode_bn_supported(d.wfmt, d.d_model, d.d_ff, d.n_routed, d.n_shared);
+}
+
+// Decode-path workspace (n_tokens <= 16).
 struct DecodeWs {
     size_t logits, idx, w, xbuf, xconv, meta, act_expert, act_mask, act_w, h, ybuf0, ybuf1, work, pairs, b1_list,
         total;
@@ -208,7 +216,7 @@ moe_status moe_workspace_size(const moe_dims *d, int32_t n_tokens, size_t *bytes
     if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
     if (n_tokens < 1 || n_tokens > 65536) return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, 65536]");
     size_t need = 0;
-    if (n_tokens <= moe::MAX_DECODE_T) need = decode_ws(*d, n_tokens).total;
+    if (decode_tokens(*d, n_tokens)) need = decode_ws(*d, n_tokens).total;
     need = std::max(need, moe::prefill_ws_bytes(d->d_model, d->d_ff, d->n_routed, d->n_shared, d->top_k, n_tokens));
     *bytes = need;
     return ok();
@@ -320,7 +328,7 @@ moe_status moe_layer_forward(const moe_dims *d, const moe_layer_weights *w, cons
                              int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws,
                              size_t ws_bytes, void *stream) {
     MOE_TRY(check_dims(d));
-    if (n_tokens > moe::MAX_DECODE_T)
+    if (!decode_tokens(*d, n_tokens))
         return moe_layer_forward_prefill(d, w, x, act, n_tokens, y, topk_idx_out, topk_w_out, ws, ws_bytes, stream);
     if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown activation type");
     if (n_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "n_tokens must be >= 1");

@@ -337,7 +337,10 @@ static hipError_t dispatch(const DecodeParams &p, hipStream_t st, bool route_onl
 #undef MOE_T
 }
 
-hipError_t launch_decode(const DecodeParams &p, hipStream_t st) { return dispatch(p, st, false); }
+hipError_t launch_decode(const DecodeParams &p, hipStream_t st) {
+    if (p.T > MAX_DECODE_T) return hipErrorNotSupported;  // this path holds at most 8 tokens
+    return dispatch(p, st, false);
+}
 hipError_t launch_route_only(const DecodeParams &p, hipStream_t st) { return dispatch(p, st, true); }
 
 hipError_t launch_bf16_to_f32(const uint16_t *in, float *out, int n, hipStream_t st) {

@@ -1,4 +1,4 @@
-// Decode path for a small batch (1 <= T <= 8 tokens) of regular shape.
+// Decode path for a small batch (1 <= T <= 16 tokens) of regular shape.
 //
 // The layer is the same as on the batch-1 path (the Flint 40B-A2.5B pages,
 // "Recursive Flint 40B-A2.5B", orcarouter.ai blog, section "The architecture
@@ -38,7 +38,7 @@ constexpr int BN_MAXB = 3;      // batches per wave: a token's list has K + S <=
 constexpr int BN_SEL_THREADS = 512;
 
 // ---------------------------------------------------------------------------
-// bn_router: logits[t, e] = x_t . Wr[e] (+ bias[e]) for T <= 8 tokens.  One
+// bn_router: logits[t, e] = x_t . Wr[e] (+ bias[e]) for T <= 16 tokens.  One
 // block per expert row, wave t = token t; each wave sums its lane's units in
 // order and then across the wave (DPP butterfly), as the batch-1 router does,
 // so the same fp32 rounding band holds.  SCALED: x_t = y_t / rms(y_t) from
@@ -46,7 +46,7 @@ constexpr int BN_SEL_THREADS = 512;
 // loads of y_t.  d_model = 512 * UPLR.
 // ---------------------------------------------------------------------------
 template <int UPLR, bool SCALED>
-__global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_router(DecodeParams p) {
+__global__ void __launch_bounds__(MOE_WAVE *MAX_BN_T) bn_router(DecodeParams p) {
     const int lane = threadIdx.x & (MOE_WAVE - 1), t = threadIdx.x / MOE_WAVE;
     const int e = blockIdx.x;
     const float *xin = (SCALED ? p.x_prev : p.x) + (size_t)t * p.D;
@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_router(DecodeParams
 }
 
 // ---------------------------------------------------------------------------
-// bn_select: one block.  Wave t takes token t's top-k (or reads the given
+// bn_select: one block.  Wave w takes tokens w, w + 8, ... : their top-k (or reads the given
 // routing); the union of routed experts is compacted in ascending order after
 // the shared experts.  Work lists:
 //   work[i]  = {slot, token a, token b (or -1), expert}  for gate/up
@@ -87,9 +87,9 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_router(DecodeParams
 // meta = {active slots, items, pairs}.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
-    __shared__ float coef[256][MAX_DECODE_T];  // routed expert x token: summed selection weights
-    __shared__ int sel_e[MAX_DECODE_T][8];     // token x selection: expert (-1: none)
-    __shared__ float sel_w[MAX_DECODE_T][8];
+    __shared__ float coef[256][MAX_BN_T];  // routed expert x token: summed selection weights
+    __shared__ int sel_e[MAX_BN_T][8];     // token x selection: expert (-1: none)
+    __shared__ float sel_w[MAX_BN_T][8];
     __shared__ int slot_of[256];               // routed expert -> active slot
     __shared__ uint32_t emask[256];
     __shared__ int wcnt[4];
@@ -100,35 +100,35 @@ __global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = p.T, K = p.K, E = p.E, S = p.S;
     if (tid < 256) emask[tid] = 0u;
-    for (int i = tid; i < 256 * MAX_DECODE_T; i += BN_SEL_THREADS) (&coef[0][0])[i] = 0.f;
+    for (int i = tid; i < 256 * MAX_BN_T; i += BN_SEL_THREADS) (&coef[0][0])[i] = 0.f;
     __syncthreads();
-    if (wave < T) {
+    for (int t = wave; t < T; t += BN_SEL_THREADS / 64) {
         int e;
         float wi;
         if (p.route_given) {
-            e = lane < K ? p.idx[wave * K + lane] : 0;
-            wi = lane < K ? p.w[wave * K + lane] : 0.f;
+            e = lane < K ? p.idx[t * K + lane] : 0;
+            wi = lane < K ? p.w[t * K + lane] : 0.f;
         } else {
-            wave_topk(p.logits + (size_t)wave * E, E, K, &e, &wi);
+            wave_topk(p.logits + (size_t)t * E, E, K, &e, &wi);
             if (lane < K) {
-                p.idx[wave * K + lane] = e;
-                p.w[wave * K + lane] = wi;
-                if (p.idx_out) p.idx_out[wave * K + lane] = e;
-                if (p.w_out) p.w_out[wave * K + lane] = wi;
+                p.idx[t * K + lane] = e;
+                p.w[t * K + lane] = wi;
+                if (p.idx_out) p.idx_out[t * K + lane] = e;
+                if (p.w_out) p.w_out[t * K + lane] = wi;
             }
         }
         const bool ok = lane < K && e >= 0 && e < E;  // invalid given indices select nothing
-        if (ok) atomicOr(&emask[e], 1u << wave);
+        if (ok) atomicOr(&emask[e], 1u << t);
         if (lane < K) {
-            sel_e[wave][lane] = ok ? e : -1;
-            sel_w[wave][lane] = wi;
+            sel_e[t][lane] = ok ? e : -1;
+            sel_w[t][lane] = wi;
         }
         // the token's weights per expert, added in selection order (a repeated
         // given index adds its weights: the expert counted twice)
         for (int k = 0; k < K; k++) {
             const int ek = __shfl(e, k, 64);
             const float wk = __shfl(wi, k, 64);
-            if (lane == 0 && ek >= 0 && ek < E) coef[ek][wave] += wk;
+            if (lane == 0 && ek >= 0 && ek < E) coef[ek][t] += wk;
         }
     }
     __syncthreads();
@@ -320,8 +320,9 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
 // ---------------------------------------------------------------------------
 // bn_down: y[t, r] = sum over token t's list (its shared slots, then its
 // selections in top-k order) of coef * (Wd[slot] row r . h[slot, t]).  One
-// block per ROWS output rows; wave t = token t, so each wave sums its own
-// token's terms in list order and writes its rows (no cross-wave reduction).
+// block per (ROWS output rows, group of up to 8 tokens); wave w = token
+// 8 * blockIdx.y + w, so each wave sums its own token's terms in list order
+// and writes its rows (no cross-wave reduction).
 // Lanes: LPR_F lanes per row (one unit each), row groups of BN_RR rows.
 // ---------------------------------------------------------------------------
 template <int FMT, int LPR_F>
@@ -332,9 +333,11 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p
     constexpr int HCH = LPR_F * UE / 4;  // 16-byte chunks of one h row (d_ff floats)
     constexpr int HLD = (HCH + MOE_WAVE - 1) / MOE_WAVE;  // wave-wide loads per h row
     // per wave: the h rows of one batch, each in the unit-swizzled chunk order
-    __shared__ uint4 hs[MAX_DECODE_T][BN_PB * HCH];
+    __shared__ uint4 hs[MAX_DECODE_T][BN_PB * HCH];  // per wave
     const int lane = threadIdx.x & 63;
-    const int t = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // the block has T waves
+    const int tw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave within the block
+    const int t = blockIdx.y * MAX_DECODE_T + tw;
+    if (t >= p.T) return;  // a group's unused waves (no block-wide synchronisation below)
     const int grp = lane / LPR_F, sub = lane % LPR_F;
     const int D = p.D, F = p.F;
     const int r0 = blockIdx.x * ROWS + grp * BN_RR;
@@ -385,10 +388,10 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p
         for (int q = 0; q < BN_PB; q++)
 #pragma unroll
             for (int i = 0; i < HLD; i++)
-                if (lane + MOE_WAVE * i < HCH) hs[t][q * HCH + xs_slot<FMT>(lane + MOE_WAVE * i)] = hc[q][i];
+                if (lane + MOE_WAVE * i < HCH) hs[tw][q * HCH + xs_slot<FMT>(lane + MOE_WAVE * i)] = hc[q][i];
 #pragma unroll
         for (int q = 0; q < BN_PB; q++) {
-            load_x_lds<FMT>(hv[q], &hs[t][q * HCH], sub);
+            load_x_lds<FMT>(hv[q], &hs[tw][q * HCH], sub);
 #pragma unroll
             for (int r = 0; r < BN_RR; r++) acc[r] += coef[q] * unit_dot<FMT>(wd[q][r], hv[q], ts[q]);
         }
@@ -409,7 +412,9 @@ hipError_t launch_bn_fmt(const DecodeParams &p, hipStream_t st) {
     MOE_LAUNCH(2, (bn_gateup<FMT, UPLD, RG>), dim3((waves_g + BN_WAVES - 1) / BN_WAVES), dim3(MOE_WAVE * BN_WAVES),
                st, p);
     const int rows = (MOE_WAVE / LPR_F) * BN_RR;
-    MOE_LAUNCH(3, (bn_down<FMT, LPR_F>), dim3((p.D + rows - 1) / rows), dim3(MOE_WAVE * p.T), st, p);
+    const int tg = (p.T + MAX_DECODE_T - 1) / MAX_DECODE_T;  // token groups of up to 8 waves
+    MOE_LAUNCH(3, (bn_down<FMT, LPR_F>), dim3((p.D + rows - 1) / rows, tg), dim3(MOE_WAVE * min(p.T, MAX_DECODE_T)),
+               st, p);
     return hipGetLastError();
 }
 
@@ -437,9 +442,20 @@ bool bn_shape_ok(const DecodeParams &p) {
 
 }  // namespace
 
+bool decode_bn_supported(int fmt, int D, int F, int E, int S) {
+    DecodeParams p{};
+    p.D = D;
+    p.F = F;
+    const bool shape = fmt == FMT_Q4_1 ? bn_shape_ok<FMT_Q4_1>(p)
+                       : fmt == FMT_NVFP4 ? bn_shape_ok<FMT_NVFP4>(p)
+                                          : bn_shape_ok<FMT_BF16>(p);
+    const int u = D / 512;  // router units per lane
+    return shape && E <= 256 && S <= 4 && D % 512 == 0 && (u == 1 || u == 2 || u == 4 || u == 8);
+}
+
 // Kernel slots: 0 logits, 1 select, 2 gate/up, 3 down.
 hipError_t launch_decode_bn(const DecodeParams &p, hipStream_t st) {
-    if (p.T < 1 || p.T > MAX_DECODE_T || p.E > 256 || p.S > 4 || !p.want_shared) return hipErrorNotSupported;
+    if (p.T < 1 || p.T > MAX_BN_T || p.E > 256 || p.S > 4 || !p.want_shared) return hipErrorNotSupported;
     if (!p.work || !p.pairs) return hipErrorNotSupported;
     const bool ok = p.fmt == FMT_Q4_1 ? bn_shape_ok<FMT_Q4_1>(p)
                     : p.fmt == FMT_NVFP4 ? bn_shape_ok<FMT_NVFP4>(p)

@@ -7,7 +7,8 @@
 
 namespace moe {
 
-constexpr int MAX_DECODE_T = 8;
+constexpr int MAX_DECODE_T = 8;   // batch-1, general and stack decode paths
+constexpr int MAX_BN_T = 16;      // small-batch path (regular shapes)
 
 // Everything a decode-path kernel reads or writes (device pointers).
 struct DecodeParams {
@@ -102,9 +103,11 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
 // Batch-1 path (three kernels per layer); hipErrorNotSupported if the shape
 // is outside what it was built for (the caller then takes launch_decode).
 hipError_t launch_decode_b1(const DecodeParams &p, hipStream_t st);
-// Small-batch path (1 <= T <= 8, regular shapes: d_model a multiple of 64
+// Small-batch path (1 <= T <= MAX_BN_T, regular shapes: d_model a multiple of 64
 // units, d_ff of 16 or 32 units); hipErrorNotSupported otherwise.
 hipError_t launch_decode_bn(const DecodeParams &p, hipStream_t st);
 hipError_t launch_route_only(const DecodeParams &p, hipStream_t st);
+// Whether the small-batch path runs this shape (format, D, F, E, S), routing included.
+bool decode_bn_supported(int fmt, int D, int F, int E, int S);
 hipError_t launch_bf16_to_f32(const uint16_t *in, float *out, int n, hipStream_t st);
 }  // namespace moe

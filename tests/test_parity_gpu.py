@@ -260,7 +260,15 @@ def test_stack_graph_replays_match_eager():
     (gen.LayerDims(512, 128, wfmt="bf16"), 3),
     (gen.LayerDims(2048, 1024, n_routed=32, n_shared=0, top_k=4, wfmt="nvfp4"), 4),
     (gen.LayerDims(4096, 512, n_routed=64, n_shared=2, top_k=6, wfmt="q4_1"), 7),
-], ids=["q4_1-t2", "q4_1-t5", "q4_1-t8", "bf16-t3", "nvfp4-noshared-t4", "q4_1-upl2-2shared-t7"])
+    # 9-16 tokens: two token groups in the down projection, two tokens per
+    # selection wave
+    (gen.LayerDims(2048, 512, wfmt="q4_1"), 9),
+    (gen.LayerDims(2048, 512, wfmt="q4_1"), 16),
+    (gen.LayerDims(2048, 512, wfmt="nvfp4"), 12),
+    (gen.LayerDims(512, 128, wfmt="bf16"), 16),
+    (gen.LayerDims(4096, 512, n_routed=64, n_shared=2, top_k=6, wfmt="q4_1"), 13),
+], ids=["q4_1-t2", "q4_1-t5", "q4_1-t8", "bf16-t3", "nvfp4-noshared-t4", "q4_1-upl2-2shared-t7", "q4_1-t9",
+        "q4_1-t16", "nvfp4-t12", "bf16-t16", "q4_1-upl2-2shared-t13"])
 def test_small_batch_path_shapes(dims, T):
     host, dl = _layer(dims, 46)
     x = gen.make_hidden(46, T, dims.d_model, draw=T)
@@ -288,9 +296,10 @@ def test_small_batch_given_routing_with_invalid_indices():
     assert np.all(rel_l2(y.cpu().numpy(), oy) <= FP32_PATH_TOL)
 
 
-def test_small_batch_deterministic():
+@pytest.mark.parametrize("T", [8, 16])
+def test_small_batch_deterministic(T):
     host, dl = _layer(gen.LayerDims(2048, 512, wfmt="q4_1"), 46)
-    x = gen.make_hidden(46, 8, 2048, draw=77).to(_dev())
+    x = gen.make_hidden(46, T, 2048, draw=77).to(_dev())
     y1, i1, w1 = B.layer_forward(dl, x)
     y2, i2, w2 = B.layer_forward(dl, x)
     torch.cuda.synchronize()
