@@ -411,7 +411,7 @@ def bench_prefill(args):
 
 def bench_sweep(args):
     """Decode batch sweep: T tokens (fp32, N(0,1)) through 47 independent q4_1 layers, for
-    T = 1 .. 64, on the decode path (T <= 16: batch-1 or small-batch kernels) and on the
+    T = 1 .. 64, on the decode path (T <= 32: batch-1 or small-batch kernels) and on the
     grouped-GEMM path (the prefill kernels, any T).  Each (T, path) is one HIP graph of
     47 layer calls, replayed; every layer has its own weights, so the active experts
     stream from HBM on every replay."""
@@ -422,9 +422,9 @@ def bench_sweep(args):
     devs, _ = build_stack(dims, 3, L, keep_host=False)
     eb = B.packed_expert_bytes(dims)
     rows = []
-    for T in (1, 2, 4, 8, 12, 16, 32, 64):
+    for T in (1, 2, 4, 8, 12, 16, 24, 32, 64):
         x = gen.make_hidden(3, T, 2048, draw=900 + T, device="cuda")
-        for path in (("decode", "gemm") if T <= 16 else ("gemm",)):
+        for path in (("decode", "gemm") if T <= 32 else ("gemm",)):
             prefill = path == "gemm"
             ws = B.workspace(dims, T)
             y = torch.empty((T, 2048), device="cuda")
@@ -465,7 +465,7 @@ def bench_sweep(args):
                              expert_gbs=round(union * eb / (ms * 1e-3) / 1e9, 1)))
             log(f"sweep T={T} {path}: {rows[-1]}")
     best64 = max(r["layer_tok_s"] for r in rows if r["T"] == 64)
-    crossover = [r["T"] for r in rows if r["path"] == "gemm" and r["T"] <= 16 and
+    crossover = [r["T"] for r in rows if r["path"] == "gemm" and r["T"] <= 32 and
                  r["layer_tok_s"] >= next(q["layer_tok_s"] for q in rows if q["T"] == r["T"] and q["path"] == "decode")]
     return dict(
         metric="MoE-layer decode tokens/s by batch size (q4_1, 47 independent layers)",

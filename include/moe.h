@@ -143,7 +143,7 @@ moe_status moe_expert_ffn_q4(const moe_dims *dims, const void *x, int32_t act, i
 
 /*
  * Whole layer: route + expert FFN.  n_tokens <= 8 takes a decode path
- * (grouped GEMV over the union of chosen experts), and so does n_tokens <= 16
+ * (grouped GEMV over the union of chosen experts), and so does n_tokens <= 32
  * when the small-batch kernels fit the shape (d_model 2048 or 4096 with
  * 4-bit weights, 512 or 1024 with bf16; d_ff of 16 or 32 blocks, a multiple
  * of 64; at least one shared expert); larger n_tokens take the prefill path

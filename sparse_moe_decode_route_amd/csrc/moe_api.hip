@@ -52,7 +52,7 @@ moe_status check_dims(const moe_dims *d) {
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Whether n_tokens runs on a decode path: up to 8 tokens always, up to 16 on
+// Whether n_tokens runs on a decode path: up to 8 tokens always, up to 32 on
 // the small-batch path when the shape fits it.
 bool decode_tokens(const moe_dims &d, int T) {
     if (T <= moe::MAX_DECODE_T) return true;
@@ -60,7 +60,7 @@ bool decode_tokens(const moe_dims &d, int T) {
            moe::decode_bn_supported(d.wfmt, d.d_model, d.d_ff, d.n_routed, d.n_shared);
 }
 
-// Decode-path workspace (n_tokens <= 16).
+// Decode-path workspace (n_tokens <= 32).
 struct DecodeWs {
     size_t logits, idx, w, xbuf, xconv, meta, act_expert, act_mask, act_w, h, ybuf0, ybuf1, work, pairs, b1_list,
         total;

@@ -1,4 +1,4 @@
-// Decode path for a small batch (1 <= T <= 16 tokens) of regular shape.
+// Decode path for a small batch (1 <= T <= 32 tokens) of regular shape.
 //
 // The layer is the same as on the batch-1 path (the Flint 40B-A2.5B pages,
 // "Recursive Flint 40B-A2.5B", orcarouter.ai blog, section "The architecture
@@ -36,18 +36,22 @@ constexpr int BN_RR = 2;        // output rows per lane group in down
 constexpr int BN_PB = 4;        // list entries per load batch in down
 constexpr int BN_MAXB = 3;      // batches per wave: a token's list has K + S <= 12 entries
 constexpr int BN_SEL_THREADS = 512;
+constexpr int BN_ROUTER_WAVES = 16;  // tokens per router block
 
 // ---------------------------------------------------------------------------
-// bn_router: logits[t, e] = x_t . Wr[e] (+ bias[e]) for T <= 16 tokens.  One
-// block per expert row, wave t = token t; each wave sums its lane's units in
+// bn_router: logits[t, e] = x_t . Wr[e] (+ bias[e]) for T <= 32 tokens.  One
+// block per (expert row, group of up to 16 tokens), wave w = token
+// 16 * blockIdx.y + w; each wave sums its lane's units in
 // order and then across the wave (DPP butterfly), as the batch-1 router does,
 // so the same fp32 rounding band holds.  SCALED: x_t = y_t / rms(y_t) from
 // the previous layer's output, the sum of squares taken from the wave's own
 // loads of y_t.  d_model = 512 * UPLR.
 // ---------------------------------------------------------------------------
 template <int UPLR, bool SCALED>
-__global__ void __launch_bounds__(MOE_WAVE *MAX_BN_T) bn_router(DecodeParams p) {
-    const int lane = threadIdx.x & (MOE_WAVE - 1), t = threadIdx.x / MOE_WAVE;
+__global__ void __launch_bounds__(MOE_WAVE *BN_ROUTER_WAVES) bn_router(DecodeParams p) {
+    const int lane = threadIdx.x & (MOE_WAVE - 1);
+    const int t = blockIdx.y * BN_ROUTER_WAVES + threadIdx.x / MOE_WAVE;
+    if (t >= p.T) return;  // a group's unused waves
     const int e = blockIdx.x;
     const float *xin = (SCALED ? p.x_prev : p.x) + (size_t)t * p.D;
     float4 yr[2 * UPLR];
@@ -79,7 +83,7 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_BN_T) bn_router(DecodeParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// bn_select: one block.  Wave w takes tokens w, w + 8, ... : their top-k (or reads the given
+// bn_select: one block.  Wave w takes tokens w, w + 8, ...: their top-k (or reads the given
 // routing); the union of routed experts is compacted in ascending order after
 // the shared experts.  Work lists:
 //   work[i]  = {slot, token a, token b (or -1), expert}  for gate/up
@@ -463,7 +467,7 @@ hipError_t launch_decode_bn(const DecodeParams &p, hipStream_t st) {
     if (!ok) return hipErrorNotSupported;
     if (!p.route_given) {
         if (!p.want_router || p.D % 512) return hipErrorNotSupported;
-        const dim3 gr(p.E), br(MOE_WAVE * p.T);
+        const dim3 gr(p.E, (p.T + BN_ROUTER_WAVES - 1) / BN_ROUTER_WAVES), br(MOE_WAVE * min(p.T, BN_ROUTER_WAVES));
 #define BN_ROUTER(U)                                                                  \
     if (p.x_prev)                                                                     \
         MOE_LAUNCH(0, (bn_router<U, true>), gr, br, st, p);                           \

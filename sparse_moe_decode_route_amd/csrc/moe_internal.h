@@ -8,7 +8,7 @@
 namespace moe {
 
 constexpr int MAX_DECODE_T = 8;   // batch-1, general and stack decode paths
-constexpr int MAX_BN_T = 16;      // small-batch path (regular shapes)
+constexpr int MAX_BN_T = 32;      // small-batch path (regular shapes; token masks are 32 bits)
 
 // Everything a decode-path kernel reads or writes (device pointers).
 struct DecodeParams {

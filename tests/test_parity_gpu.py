@@ -267,8 +267,13 @@ def test_stack_graph_replays_match_eager():
     (gen.LayerDims(2048, 512, wfmt="nvfp4"), 12),
     (gen.LayerDims(512, 128, wfmt="bf16"), 16),
     (gen.LayerDims(4096, 512, n_routed=64, n_shared=2, top_k=6, wfmt="q4_1"), 13),
+    # 17-32 tokens: two router blocks per expert, four selection tokens per wave
+    (gen.LayerDims(2048, 512, wfmt="q4_1"), 32),
+    (gen.LayerDims(2048, 512, wfmt="nvfp4"), 21),
+    (gen.LayerDims(4096, 512, n_routed=64, n_shared=2, top_k=6, wfmt="q4_1"), 27),
 ], ids=["q4_1-t2", "q4_1-t5", "q4_1-t8", "bf16-t3", "nvfp4-noshared-t4", "q4_1-upl2-2shared-t7", "q4_1-t9",
-        "q4_1-t16", "nvfp4-t12", "bf16-t16", "q4_1-upl2-2shared-t13"])
+        "q4_1-t16", "nvfp4-t12", "bf16-t16", "q4_1-upl2-2shared-t13", "q4_1-t32", "nvfp4-t21",
+        "q4_1-upl2-2shared-t27"])
 def test_small_batch_path_shapes(dims, T):
     host, dl = _layer(dims, 46)
     x = gen.make_hidden(46, T, dims.d_model, draw=T)
@@ -296,7 +301,7 @@ def test_small_batch_given_routing_with_invalid_indices():
     assert np.all(rel_l2(y.cpu().numpy(), oy) <= FP32_PATH_TOL)
 
 
-@pytest.mark.parametrize("T", [8, 16])
+@pytest.mark.parametrize("T", [8, 16, 32])
 def test_small_batch_deterministic(T):
     host, dl = _layer(gen.LayerDims(2048, 512, wfmt="q4_1"), 46)
     x = gen.make_hidden(46, T, 2048, draw=77).to(_dev())
