@@ -157,20 +157,26 @@ __device__ __forceinline__ float unit_dot(const WUnit &w, const XUnit<FMT> &x, f
         }
         return acc;
     } else if (FMT == FMT_Q4_1) {
-        // sum_i (d q_i + m) x_i = d * sum_i q_i x_i + m * sum_i x_i
+        // sum_i (d q_i + m) x_i = d * sum_i q_i x_i + m * sum_i x_i.  A byte
+        // holding a code q < 16, read as an E4M3 float, is exactly q * 2^-9, so
+        // one packed conversion turns two codes into floats; every partial sum
+        // is then exactly 2^-9 of the integer-code one and d * 2^9 restores it
+        // (same roundings, same result).
         uint32_t a[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
         float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            uint32_t lo = opaque(a[i] & 0x0F0F0F0Fu);
-            uint32_t hi = opaque((a[i] >> 4) & 0x0F0F0F0Fu);
+            const uint32_t lo = a[i] & 0x0F0F0F0Fu, hi = (a[i] >> 4) & 0x0F0F0F0Fu;
+            const auto l01 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), l23 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+            const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+            const float ql[4] = {l01[0], l01[1], l23[0], l23[1]}, qh[4] = {h01[0], h01[1], h23[0], h23[1]};
 #pragma unroll
             for (int b = 0; b < 4; b++) {
-                acc0 = __builtin_fmaf((float)((lo >> (8 * b)) & 0xFFu), x.v[4 * i + b], acc0);
-                acc1 = __builtin_fmaf((float)((hi >> (8 * b)) & 0xFFu), x.v[16 + 4 * i + b], acc1);
+                acc0 = __builtin_fmaf(ql[b], x.v[4 * i + b], acc0);
+                acc1 = __builtin_fmaf(qh[b], x.v[16 + 4 * i + b], acc1);
             }
         }
-        float d = half_bits_to_float(w.s), m = half_bits_to_float(w.s >> 16);
+        float d = half_bits_to_float(w.s) * 512.0f, m = half_bits_to_float(w.s >> 16);
         return __builtin_fmaf(d, acc0 + acc1, m * x.sum);
     } else {
         // two blocks of 16: e2m1 codes decoded by the hardware converter
