@@ -26,13 +26,9 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return __half2float(__ushort_as_half((unsigned short)(h & 0xFFFFu)));
 }
 
-// OCP E4M3 (FN) byte -> fp32, by fields (the NaN code is not produced by
-// encoders and is not special-cased).
-__device__ __forceinline__ float e4m3_to_float(uint32_t c) {
-    uint32_t s = (c & 0x80u) << 24, e = (c >> 3) & 15u, m = c & 7u;
-    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-    return __uint_as_float(__float_as_uint(mag) | s);
-}
+// OCP E4M3 (FN) byte (the low 8 bits of c) -> fp32, exact, by the hardware
+// converter (the NaN code is not produced by encoders).
+__device__ __forceinline__ float e4m3_to_float(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
 
 // ---- elements per weight unit (one lane's share of a row per step) ----
 template <int FMT> struct Unit;
