@@ -107,18 +107,18 @@ ATTN_SOURCES = ("moe_attn.hip", "moe_device.h", "moe_internal.h")
 _FETCH_SCALE = 262144.0 / 131085.2  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
 _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE KiB
 COUNTER_TRAFFIC = {
-    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="ee4985062332661a",
-                                              fetch_bytes=round(3939.9 * _FETCH_SCALE * 1024),
+    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="3c400d9417aae1b3",
+                                              fetch_bytes=round(3939.4 * _FETCH_SCALE * 1024),
                                               write_bytes=round(12.7 * _WRITE_SCALE * 1024)),
-    ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="d075cab14c744b5a",
-                                             fetch_bytes=round(227450.1 * _FETCH_SCALE * 1024),
-                                             write_bytes=round(28696.1 * _WRITE_SCALE * 1024)),
-    ("lm_head_q4_1_t1", "lm_head_kernel"): dict(source_digest="c45bdaa74bc3a5cb",
-                                                fetch_bytes=round(91654.2 * _FETCH_SCALE * 1024),
+    ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="c0646f2761c21c42",
+                                             fetch_bytes=round(227273.3 * _FETCH_SCALE * 1024),
+                                             write_bytes=round(28692.8 * _WRITE_SCALE * 1024)),
+    ("lm_head_q4_1_t1", "lm_head_kernel"): dict(source_digest="a0621f359d9319a6",
+                                                fetch_bytes=round(91654.3 * _FETCH_SCALE * 1024),
                                                 write_bytes=round(572.2 * _WRITE_SCALE * 1024)),
-    ("attn_full128k", "attn_chunk"): dict(source_digest="911d325de356f382",
-                                          fetch_bytes=round(152563.8 * _FETCH_SCALE * 1024),
-                                          write_bytes=round(4610.0 * _WRITE_SCALE * 1024)),
+    ("attn_full128k", "attn_chunk"): dict(source_digest="b8d3f2684d475380",
+                                          fetch_bytes=round(152520.2 * _FETCH_SCALE * 1024),
+                                          write_bytes=round(4610.1 * _WRITE_SCALE * 1024)),
 }
 
 
