@@ -636,8 +636,10 @@ def bench_attn(args, kind: str):
             kus[k] = kus.get(k, 0.0) + v / n_timed
     n_pos = min(P + 1, window) if window > 0 else P + 1
     kv_bytes = n_pos * Hkv * D * 2 * 2
-    chunk = 64 if window > 0 else next(c for c in (64, 128, 256, 512, 1024) if c == 1024 or -(-max_len // c) * Hkv <= 1024)
-    nc = -(-(P + 1) // chunk) if window == 0 else -(-n_pos // chunk) + 1
+    # chunk partials written: one per chunk that holds positions of the range
+    chunk, _ = B.attn_chunk_plan(dims, 1, max_len)
+    lo = P + 1 - n_pos
+    nc = P // chunk - lo // chunk + 1
     part_bytes = Hq * nc * (D + 2) * 4
     algo = kv_bytes + Hq * D * 4 + part_bytes  # keys, values, queries in, chunk partials out
     ach = algo / (kus["attn_chunk"] * 1e-6) / 1e9

@@ -295,6 +295,15 @@ typedef struct {
    caches of max_len positions. */
 moe_status moe_attn_workspace_size(const moe_attn_dims *dims, int32_t n_seqs, int32_t max_len, size_t *bytes);
 
+/* (host) the chunk plan moe_attn_decode uses for these sizes: *chunk
+   positions per block of the first kernel, and *slots chunk partials per
+   (sequence, query head) in the workspace (the combine kernel merges the
+   slots a position range touches).  Sliding windows take 32-position
+   chunks; full layers the smallest power of two in [64, 1024] that keeps a
+   call near 1024 blocks.  Same argument checks as moe_attn_workspace_size. */
+moe_status moe_attn_chunk_plan(const moe_attn_dims *dims, int32_t n_seqs, int32_t max_len, int32_t *chunk,
+                               int32_t *slots);
+
 /*
  *   q          fp32 [n_seqs, n_q_heads, 128], the new tokens' query projections
  *   k_new      fp32 [n_seqs, n_kv_heads, 128]; v_new likewise

@@ -24,7 +24,7 @@ ENTRY_POINTS = (
     "moe_packed_expert_bytes", "moe_workspace_size", "moe_repack_weights", "moe_route_topk",
     "moe_expert_ffn_q4", "moe_layer_forward", "moe_layer_forward_prefill", "moe_stack_decode",
     "moe_stack_decode_timed", "moe_layer_forward_prefill_timed", "moe_lm_head_bytes", "moe_lm_head_repack",
-    "moe_lm_head", "moe_lm_head_timed", "moe_attn_workspace_size", "moe_attn_decode", "moe_attn_decode_timed",
+    "moe_lm_head", "moe_lm_head_timed", "moe_attn_workspace_size", "moe_attn_chunk_plan", "moe_attn_decode", "moe_attn_decode_timed",
     "moe_status_string", "moe_last_error",
 )
 
@@ -97,6 +97,8 @@ def lib():
         pa = ctypes.POINTER(CAttnDims)
         L.moe_attn_workspace_size.restype = ctypes.c_int
         L.moe_attn_workspace_size.argtypes = [pa, i32, i32, ctypes.POINTER(sz)]
+        L.moe_attn_chunk_plan.restype = ctypes.c_int
+        L.moe_attn_chunk_plan.argtypes = [pa, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.moe_attn_decode.restype = ctypes.c_int
         L.moe_attn_decode.argtypes = [pa, i32, i32] + [vp] * 11 + [sz, vp]
         L.moe_attn_decode_timed.restype = ctypes.c_int
@@ -369,6 +371,13 @@ def attn_workspace(dims: CAttnDims, n_seqs: int, max_len: int, device="cuda") ->
     n = ctypes.c_size_t(0)
     _check(lib().moe_attn_workspace_size(ctypes.byref(dims), n_seqs, max_len, ctypes.byref(n)))
     return torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device)
+
+
+def attn_chunk_plan(dims: CAttnDims, n_seqs: int, max_len: int) -> tuple[int, int]:
+    """(positions per chunk, chunk partial slots per query head) for these sizes."""
+    c, n = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().moe_attn_chunk_plan(ctypes.byref(dims), n_seqs, max_len, ctypes.byref(c), ctypes.byref(n)))
+    return int(c.value), int(n.value)
 
 
 def _attn_args(dims, a, pos, out, ws):

@@ -680,6 +680,15 @@ moe_status moe_attn_workspace_size(const moe_attn_dims *d, int32_t n_seqs, int32
     return ok();
 }
 
+moe_status moe_attn_chunk_plan(const moe_attn_dims *d, int32_t n_seqs, int32_t max_len, int32_t *chunk,
+                               int32_t *slots) {
+    MOE_TRY(attn_check(d, n_seqs, max_len));
+    if (!chunk || !slots) return fail(MOE_ERR_INVALID_ARG, "chunk or slots is NULL");
+    *chunk = moe::attn_chunk_size(d->window, max_len, n_seqs, d->n_kv_heads);
+    *slots = moe::attn_chunk_slots(d->window, max_len, *chunk);
+    return ok();
+}
+
 // Host checks and the kernel arguments; nothing touches the device.
 static moe_status attn_prepare(const moe_attn_dims *d, int32_t B, int32_t max_len, const float *q, const float *k_new,
                                const float *v_new, const float *q_norm_w, const float *k_norm_w, const float *sinks,

@@ -178,3 +178,21 @@ def test_attn_checks(L):
     assert b"overlaps" in L.moe_last_error()
     kus = (ctypes.c_float * 2)()
     assert L.moe_attn_decode_timed(*(args(**{"0": None})[:-1] + [kus, None])) == INVALID
+
+
+def test_attn_chunk_plan(L):
+    """Chunk plan: 32-position chunks for windows; for full layers the smallest
+    power of two in [64, 1024] keeping a call near 1024 blocks; the workspace
+    holds one (max, sum, 128-value) partial per slot and query head."""
+    cases = (((32, 4, 513), 1, 8192, 32, 17), ((32, 4, 513), 1, 100, 32, 4), ((32, 4, 0), 1, 131072, 512, 256),
+             ((32, 4, 0), 1, 8192, 64, 128), ((32, 4, 0), 8, 131072, 1024, 128), ((32, 4, 0), 1, 1, 64, 1))
+    for (hq, hkv, win), nseq, ml, chunk, slots in cases:
+        d = B.attn_dims(hq, hkv, win)
+        assert B.attn_chunk_plan(d, nseq, ml) == (chunk, slots)
+        n = ctypes.c_size_t()
+        assert L.moe_attn_workspace_size(ctypes.byref(d), nseq, ml, ctypes.byref(n)) == OK
+        need = nseq * hq * slots * 130 * 4
+        assert need <= n.value < need + 3 * 256
+    c = ctypes.c_int32()
+    assert L.moe_attn_chunk_plan(ctypes.byref(B.attn_dims(32, 4, 0)), 1, 8192, ctypes.byref(c), None) == INVALID
+    assert L.moe_attn_chunk_plan(ctypes.byref(B.attn_dims(32, 4, 0)), 0, 8192, ctypes.byref(c), ctypes.byref(c)) == INVALID
