@@ -47,7 +47,7 @@ typedef __bf16 at_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float at_f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int AT_D = 128;       // head size
-constexpr int AT_CMAX = 1024;   // largest chunk (positions)
+constexpr int AT_CMAX = 512;    // largest chunk (positions)
 constexpr int AT_UT = 4;        // tiles of 8 positions per load group
 constexpr int AT_COMB_WAVES = 16;
 
@@ -92,7 +92,6 @@ __device__ __forceinline__ void unpack16(const uint4 &a, const uint4 &b, float (
     }
 }
 
-// HW query heads per wave, WV waves per block (HW * WV = group size).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)to_bf16_rne(lo) | ((uint32_t)to_bf16_rne(hi) << 16);
 }
@@ -157,22 +156,69 @@ __device__ __forceinline__ float tile_scores(const float (&qv)[HW][16], const ui
     return s;
 }
 
-// HW query heads per wave, WV waves per block (HW * WV = group size).  MF
-// (group of 8 only): the scores on the matrix cores instead: A = the 8
-// queries split into bf16 high and low halves (rows 0-7 and 8-15, rows 16-31
-// zero), B = 32 positions' keys, 16 dimensions per v_mfma_f32_32x32x16_bf16;
-// head h's score is row h + row h + 8.  Each wave takes every other tile of
-// 32 positions for all 8 heads.
-template <int HW, int WV, bool MF>
+// This lane's 16 values (dimensions 16 sub .. 16 sub + 15) of a 128-value
+// fp32 row.
+__device__ __forceinline__ void load16(const float *row, int sub, float (&x)[16]) {
+    const float4 *s = reinterpret_cast<const float4 *>(row + 16 * sub);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float4 f = s[i];
+        x[4 * i] = f.x;
+        x[4 * i + 1] = f.y;
+        x[4 * i + 2] = f.z;
+        x[4 * i + 3] = f.w;
+    }
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&x)[16], int o) {
+    return make_uint4(pack_bf16x2(x[o], x[o + 1]), pack_bf16x2(x[o + 2], x[o + 3]), pack_bf16x2(x[o + 4], x[o + 5]),
+                      pack_bf16x2(x[o + 6], x[o + 7]));
+}
+
+// Query head h of sequence b, this lane's 16 values: normalised, rotated,
+// scaled by 1/sqrt(128).  Every lane of the wave takes part.
+__device__ __forceinline__ void query16(const AttnArgs &p, int b, int h, const float (*cs)[64], bool rope, int lane,
+                                        float (&x)[16]) {
+    load16(p.q + ((size_t)b * p.Hq + h) * AT_D, lane & 7, x);
+    head_prep(x, p.q_norm_w, cs, rope, p.eps, lane);
+#pragma unroll
+    for (int d = 0; d < 16; d++) x[d] *= 0.08838834764831845f;  // 1 / sqrt(128)
+}
+
+// The new token's key (normalised, rotated) and value for key/value head g
+// in bf16, this lane's 16 dimensions as two 16-byte chunks each; lanes with
+// write set store them to cache row P.  Every lane of the wave takes part.
+__device__ __forceinline__ void new_token(const AttnArgs &p, int b, int g, int P, const float (*cs)[64], bool rope,
+                                          int lane, bool write, uint4 &k0, uint4 &k1, uint4 &v0, uint4 &v1) {
+    const int sub = lane & 7;
+    float kx[16], vx[16];
+    load16(p.k_new + ((size_t)b * p.Hkv + g) * AT_D, sub, kx);
+    load16(p.v_new + ((size_t)b * p.Hkv + g) * AT_D, sub, vx);
+    head_prep(kx, p.k_norm_w, cs, rope, p.eps, lane);
+    k0 = pack8(kx, 0);
+    k1 = pack8(kx, 8);
+    v0 = pack8(vx, 0);
+    v1 = pack8(vx, 8);
+    if (write) {
+        const size_t row = (((size_t)b * p.Hkv + g) * p.max_len + P) * AT_D;
+        uint4 *kd = reinterpret_cast<uint4 *>(p.k_cache + row) + 2 * sub;
+        uint4 *vd = reinterpret_cast<uint4 *>(p.v_cache + row) + 2 * sub;
+        kd[0] = k0;
+        kd[1] = k1;
+        vd[0] = v0;
+        vd[1] = v1;
+    }
+}
+
+// Vector path (sliding windows; groups of 1, 2 and 4; 8 in windows): HW
+// query heads per wave, WV waves per block (HW * WV = group size).
+template <int HW, int WV>
 __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
-    static_assert(!MF || (HW == 4 && WV == 2), "matrix-core scores for a group of 8 heads");
     __shared__ float scb[WV * AT_CMAX * HW];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int sub = lane & 7, pg = lane >> 3;
     // score / exponential of position j for this wave's head h
-    auto sc = [&](int j, int h) -> float & {
-        return MF ? scb[j * 8 + 4 * w + h] : scb[(w * AT_CMAX + j) * HW + h];
-    };
+    auto sc = [&](int j, int h) -> float & { return scb[(w * AT_CMAX + j) * HW + h]; };
     const int b = blockIdx.z, g = blockIdx.y;
     const int P = p.pos[b];
     if (P < 0 || P >= p.max_len) return;
@@ -198,22 +244,7 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
     };
     // the first groups of keys and values are requested before anything else
     uint4 xa[AT_UT], ya[AT_UT], va[AT_UT], vb[AT_UT];
-    // matrix-core scores: this wave's 32-position tiles (w, w + 2, ...), lane
-    // (column l % 32, half l / 32) holding dimensions 16 s + 8 (l / 32) .. + 7
-    const int mc = lane & 31, mh2 = lane >> 5;
-    const int nt32 = (n + 31) / 32;
-    const uint4 *KM = reinterpret_cast<const uint4 *>(p.k_cache + base * AT_D) + mh2;
-    auto issue_mf = [&](uint4 (&bk)[8], int t) {
-        const int j = start + min(t * 32 + mc, n - 1);
-#pragma unroll
-        for (int st = 0; st < 8; st++) bk[st] = ld_stream16(KM + (size_t)j * 16 + 2 * st);
-    };
-    uint4 bk0[8], bk1[8];
-    if constexpr (MF) {
-        if (w < nt32) issue_mf(bk0, w);
-    } else {
-        issue(K, xa, ya, 0);
-    }
+    issue(K, xa, ya, 0);
     issue(V, va, vb, 0);
 
     // cos / sin of the 64 rotary angles P * freq_i: the product and its
@@ -233,70 +264,21 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
         }
         __syncthreads();
     }
-    // this wave's query heads: normalised, rotated, scaled by 1/sqrt(128)
+    // this wave's query heads
     float qv[HW][16];
 #pragma unroll
-    for (int h = 0; h < HW; h++) {
-        const float4 *qs = reinterpret_cast<const float4 *>(p.q + ((size_t)b * p.Hq + h0 + h) * AT_D + 16 * sub);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float4 f = qs[i];
-            qv[h][4 * i] = f.x;
-            qv[h][4 * i + 1] = f.y;
-            qv[h][4 * i + 2] = f.z;
-            qv[h][4 * i + 3] = f.w;
-        }
-        head_prep(qv[h], p.q_norm_w, cs, rope, p.eps, lane);
-#pragma unroll
-        for (int d = 0; d < 16; d++) qv[h][d] *= 0.08838834764831845f;  // 1 / sqrt(128)
-    }
-    // the chunk holding P: the new key (normalised, rotated) and value in
-    // bf16, used in place of the cache row P, which this block also writes
+    for (int h = 0; h < HW; h++) query16(p, b, h0 + h, cs, rope, lane, qv[h]);
+    // the chunk holding P: the new key and value used in place of the cache
+    // row P, which this block also writes
     const bool hasP = end == P + 1;
     uint4 kn0 = make_uint4(0, 0, 0, 0), kn1 = kn0, vn0 = kn0, vn1 = kn0;
-    if (hasP) {
-        float kx[16], vx[16];
-        const float4 *ks = reinterpret_cast<const float4 *>(p.k_new + ((size_t)b * p.Hkv + g) * AT_D + 16 * sub);
-        const float4 *vs = reinterpret_cast<const float4 *>(p.v_new + ((size_t)b * p.Hkv + g) * AT_D + 16 * sub);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float4 f = ks[i], e = vs[i];
-            kx[4 * i] = f.x;
-            kx[4 * i + 1] = f.y;
-            kx[4 * i + 2] = f.z;
-            kx[4 * i + 3] = f.w;
-            vx[4 * i] = e.x;
-            vx[4 * i + 1] = e.y;
-            vx[4 * i + 2] = e.z;
-            vx[4 * i + 3] = e.w;
-        }
-        head_prep(kx, p.k_norm_w, cs, rope, p.eps, lane);
-        kn0 = make_uint4(pack_bf16x2(kx[0], kx[1]), pack_bf16x2(kx[2], kx[3]), pack_bf16x2(kx[4], kx[5]),
-                         pack_bf16x2(kx[6], kx[7]));
-        kn1 = make_uint4(pack_bf16x2(kx[8], kx[9]), pack_bf16x2(kx[10], kx[11]), pack_bf16x2(kx[12], kx[13]),
-                         pack_bf16x2(kx[14], kx[15]));
-        vn0 = make_uint4(pack_bf16x2(vx[0], vx[1]), pack_bf16x2(vx[2], vx[3]), pack_bf16x2(vx[4], vx[5]),
-                         pack_bf16x2(vx[6], vx[7]));
-        vn1 = make_uint4(pack_bf16x2(vx[8], vx[9]), pack_bf16x2(vx[10], vx[11]), pack_bf16x2(vx[12], vx[13]),
-                         pack_bf16x2(vx[14], vx[15]));
-        if (w == 0 && pg == 0) {
-            const size_t row = (((size_t)b * p.Hkv + g) * p.max_len + P) * AT_D;
-            uint4 *kd = reinterpret_cast<uint4 *>(p.k_cache + row) + 2 * sub;
-            uint4 *vd = reinterpret_cast<uint4 *>(p.v_cache + row) + 2 * sub;
-            kd[0] = kn0;
-            kd[1] = kn1;
-            vd[0] = vn0;
-            vd[1] = vn1;
-        }
-    }
+    if (hasP) new_token(p, b, g, P, cs, rope, lane, w == 0 && pg == 0, kn0, kn1, vn0, vn1);
     // row P of the first groups is the new key / value
 #pragma unroll
     for (int u = 0; u < AT_UT; u++) {
         if (start + min(u * 8 + pg, n - 1) == P) {
-            if (!MF) {
-                xa[u] = kn0;
-                ya[u] = kn1;
-            }
+            xa[u] = kn0;
+            ya[u] = kn1;
             va[u] = vn0;
             vb[u] = vn1;
         }
@@ -314,68 +296,7 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
         }
     };
 
-    if constexpr (MF) {
-        // the 8 prepared queries and the new key through LDS into the
-        // matrix-core layout
-        __shared__ float qsh[8][AT_D];
-        __shared__ uint4 knsh[16];
-        if (pg == 0) {
-#pragma unroll
-            for (int h = 0; h < HW; h++)
-#pragma unroll
-                for (int d = 0; d < 16; d++) qsh[4 * w + h][16 * sub + d] = qv[h][d];
-            if (w == 0) {
-                knsh[2 * sub] = kn0;
-                knsh[2 * sub + 1] = kn1;
-            }
-        }
-        __syncthreads();
-        at_bf16x8 aq[8];
-#pragma unroll
-        for (int st = 0; st < 8; st++) {
-            uint32_t wd[4];
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                uint32_t pr = 0;
-                if (mc < 16) {
-                    const float *qr = &qsh[mc & 7][16 * st + 8 * mh2 + 2 * e];
-                    float v0 = qr[0], v1 = qr[1];
-                    if (mc >= 8) {  // low half: what the high half leaves
-                        v0 -= __uint_as_float((uint32_t)to_bf16_rne(v0) << 16);
-                        v1 -= __uint_as_float((uint32_t)to_bf16_rne(v1) << 16);
-                    }
-                    pr = pack_bf16x2(v0, v1);
-                }
-                wd[e] = pr;
-            }
-            aq[st] = __builtin_bit_cast(at_bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
-        }
-        auto scores_mf = [&](uint4 (&bk)[8], int t) {
-            const int j = start + min(t * 32 + mc, n - 1);
-            if (j == P) {
-#pragma unroll
-                for (int st = 0; st < 8; st++) bk[st] = knsh[2 * st + mh2];
-            }
-            at_f32x16 acc;
-#pragma unroll
-            for (int i = 0; i < 16; i++) acc[i] = 0.f;
-#pragma unroll
-            for (int st = 0; st < 8; st++)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[st], __builtin_bit_cast(at_bf16x8, bk[st]), acc, 0, 0, 0);
-            // acc[i] = row 4 * (l / 32) + i (high halves), acc[4 + i] = row 8 + 4 * (l / 32) + i (low halves)
-            const int jj = t * 32 + mc;
-            if (jj < n) {
-#pragma unroll
-                for (int i = 0; i < 4; i++) scb[jj * 8 + 4 * mh2 + i] = acc[i] + acc[4 + i];
-            }
-        };
-        for (int t = w; t < nt32; t += 4) {
-            if (t + 2 < nt32) issue_mf(bk1, t + 2);
-            scores_mf(bk0, t);
-            if (t + 4 < nt32) issue_mf(bk0, t + 4);
-            if (t + 2 < nt32) scores_mf(bk1, t + 2);
-        }
-    } else {
+    {
         // scores, two load groups in registers
         uint4 xb[AT_UT], yb[AT_UT];
         auto scores = [&](const uint4 (&x)[AT_UT], const uint4 (&y)[AT_UT], int gi) {
@@ -480,6 +401,266 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
     }
 }
 
+typedef short at_s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) at_s16x4 lds_s16x4;
+
+// Matrix-core path: full layers (no rotary embedding) with 8 query heads
+// per key/value head; the same partials as attn_chunk.  Two waves; wave w
+// takes the 32-position tiles w, w + 2, ... of the chunk for all 8 heads.
+//   scores  A = the 8 prepared queries split into bf16 high and low halves
+//           (rows 0-7 and 8-15; rows 16-31 zero), B = the tile's keys straight
+//           from the cache (lane l: position l % 32, dimensions
+//           16 s + 8 (l / 32) .. + 7 for step s), 8 v_mfma_f32_32x32x16_bf16
+//           over the 128 dimensions; head h's score is row h + row h + 8
+//           (the split leaves about 2^-18 of the query);
+//   values  O[h][d] += sum_j e_hj V[j][d]: A = the exponentials split the
+//           same way (lane l: head row l % 32, positions 8 (l / 32) .. + 7 of
+//           a 16-position half), B = 8 positions of one dimension per lane.
+//           The tile's 32 value rows arrive 1 KB per load instruction (four
+//           whole rows), go to a wave-private LDS tile, and come back
+//           transposed by ds_read_b64_tr_b16: within a 16-lane group, lane i
+//           receives element i % 4 of the 8-byte reads of lanes 4 j + i / 4,
+//           j = 0..3, so four lanes reading 4 dimensions each of 4 rows hand
+//           every lane one dimension at 4 positions.  Two such reads make a
+//           B operand; 8 MFMAs per tile (two halves x four 32-dimension
+//           blocks).  The 16-byte chunk c of tile row r sits at c ^ 2 (r % 4),
+//           so the 4 rows a 16-lane group reads fall in distinct banks.
+// The two waves' value sums are added in wave order at the end.
+__global__ void __launch_bounds__(128) attn_chunk_mf(AttnArgs p) {
+    __shared__ float pe[8 * AT_CMAX];  // head h, position j at h * AT_CMAX + j: score, then exponential
+    __shared__ uint4 vst[2][32 * 16];  // per wave: one tile of 32 value rows
+    __shared__ float qsh[8][AT_D];
+    __shared__ uint4 knsh[16], vnsh[16];  // the new key and value, bf16
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int sub = lane & 7, mc = lane & 31, mh2 = lane >> 5;
+    const int b = blockIdx.z, g = blockIdx.y;
+    const int P = p.pos[b];
+    if (P < 0 || P >= p.max_len) return;
+    const int start = blockIdx.x * p.chunk, end = min(start + p.chunk, P + 1);  // [start, end)
+    if (start >= end) return;
+    const int n = end - start, nt = (n + 31) / 32;
+    const size_t base = ((size_t)b * p.Hkv + g) * p.max_len;
+    const uint4 *Kc = reinterpret_cast<const uint4 *>(p.k_cache + base * AT_D);
+    const uint4 *Vc = reinterpret_cast<const uint4 *>(p.v_cache + base * AT_D);
+    // keys of tile t (B operands of the score MFMAs); rows past the chunk's
+    // end re-read its last row
+    auto issue_k = [&](uint4 (&bk)[8], int t) {
+        const int j = start + min(t * 32 + mc, n - 1);
+#pragma unroll
+        for (int st = 0; st < 8; st++) bk[st] = ld_stream16(Kc + (size_t)j * 16 + 2 * st + mh2);
+    };
+    // values of tile t: instruction i loads rows 4 i .. 4 i + 3 (lane l: row
+    // 4 i + l / 16, chunk l % 16); rows past the end re-read the last row
+    auto issue_v = [&](uint4 (&v)[8], int t) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int r = min(32 * t + 4 * i + (lane >> 4), n - 1);
+            v[i] = ld_stream16(Vc + (size_t)(start + r) * 16 + (lane & 15));
+        }
+    };
+    // the first tiles of keys and values are requested before anything else
+    uint4 bk0[8], bk1[8], va[8], vb[8];
+    if (w < nt) {
+        issue_k(bk0, w);
+        issue_v(va, w);
+    }
+    // the 8 prepared queries (wave w: heads 4 w .. 4 w + 3) and the new key
+    // and value through LDS
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        float x[16];
+        query16(p, b, g * 8 + 4 * w + h, nullptr, false, lane, x);
+        if (lane < 8) {
+#pragma unroll
+            for (int d = 0; d < 16; d++) qsh[4 * w + h][16 * sub + d] = x[d];
+        }
+    }
+    if (end == P + 1) {
+        uint4 k0, k1, v0, v1;
+        new_token(p, b, g, P, nullptr, false, lane, w == 0 && lane < 8, k0, k1, v0, v1);
+        if (w == 0 && lane < 8) {
+            knsh[2 * sub] = k0;
+            knsh[2 * sub + 1] = k1;
+            vnsh[2 * sub] = v0;
+            vnsh[2 * sub + 1] = v1;
+        }
+    }
+    __syncthreads();
+
+    // scores
+    at_bf16x8 aq[8];
+#pragma unroll
+    for (int st = 0; st < 8; st++) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            uint32_t pr = 0;
+            if (mc < 16) {
+                const float *qr = &qsh[mc & 7][16 * st + 8 * mh2 + 2 * e];
+                float v0 = qr[0], v1 = qr[1];
+                if (mc >= 8) {  // low half: what the high half leaves
+                    v0 -= __uint_as_float((uint32_t)to_bf16_rne(v0) << 16);
+                    v1 -= __uint_as_float((uint32_t)to_bf16_rne(v1) << 16);
+                }
+                pr = pack_bf16x2(v0, v1);
+            }
+            wd[e] = pr;
+        }
+        aq[st] = __builtin_bit_cast(at_bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+    }
+    auto scores = [&](uint4 (&bk)[8], int t) {
+        const int j = start + min(t * 32 + mc, n - 1);
+        if (j == P) {
+#pragma unroll
+            for (int st = 0; st < 8; st++) bk[st] = knsh[2 * st + mh2];
+        }
+        at_f32x16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[i] = 0.f;
+#pragma unroll
+        for (int st = 0; st < 8; st++)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[st], __builtin_bit_cast(at_bf16x8, bk[st]), acc, 0, 0, 0);
+        // acc[i] = row 4 (l / 32) + i (high halves), acc[4 + i] = row 8 + 4 (l / 32) + i (low halves)
+        const int jj = t * 32 + mc;
+        if (jj < n) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) pe[(4 * mh2 + i) * AT_CMAX + jj] = acc[i] + acc[4 + i];
+        }
+    };
+    for (int t = w; t < nt; t += 4) {
+        if (t + 2 < nt) issue_k(bk1, t + 2);
+        scores(bk0, t);
+        if (t + 4 < nt) issue_k(bk0, t + 4);
+        if (t + 2 < nt) scores(bk1, t + 2);
+    }
+    __syncthreads();
+
+    // wave w, heads 4 w + h: the chunk's max, exponentials in place, their sum
+    float mh[4], lh[4];
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        const float *ph = pe + (4 * w + h) * AT_CMAX;
+        float m = -INFINITY;
+        for (int j = lane; j < n; j += 64) m = fmaxf(m, ph[j]);
+        mh[h] = wave_max_f(m);
+    }
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        float *ph = pe + (4 * w + h) * AT_CMAX;
+        float l = 0.f;
+        for (int j = lane; j < n; j += 64) {
+            const float e = __expf(ph[j] - mh[h]);
+            ph[j] = e;
+            l += e;
+        }
+        lh[h] = wave_sum(l);
+    }
+    __syncthreads();
+
+    // values
+    at_f32x16 oacc[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) oacc[c][i] = 0.f;
+    uint4 *tile = vst[w];
+    // tile t's rows to LDS: row P is the new value, rows past the end zero
+    auto stage = [&](const uint4 (&v)[8], int t) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int r = 4 * i + (lane >> 4), c = lane & 15;
+            const int jj = 32 * t + r;
+            uint4 x = v[i];
+            if (start + jj == P) x = vnsh[c];
+            if (jj >= n) x = make_uint4(0, 0, 0, 0);
+            tile[r * 16 + (c ^ (2 * (r & 3)))] = x;
+        }
+    };
+    // A operand: exponentials of half kb of tile t, split high / low
+    auto a_op = [&](int t, int kb) -> at_bf16x8 {
+        const int j0 = 32 * t + 16 * kb + 8 * mh2;
+        const float4 *src = reinterpret_cast<const float4 *>(pe + (mc & 7) * AT_CMAX + j0);
+        const float4 f0 = src[0], f1 = src[1];
+        const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        uint32_t wd[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            float v0 = j0 + 2 * e < n ? f[2 * e] : 0.f;
+            float v1 = j0 + 2 * e + 1 < n ? f[2 * e + 1] : 0.f;
+            if (mc >= 8) {
+                v0 -= __uint_as_float((uint32_t)to_bf16_rne(v0) << 16);
+                v1 -= __uint_as_float((uint32_t)to_bf16_rne(v1) << 16);
+            }
+            wd[e] = mc < 16 ? pack_bf16x2(v0, v1) : 0u;
+        }
+        return __builtin_bit_cast(at_bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+    };
+    // B operand: half kb, dimensions 32 c .. 32 c + 31 (lane l: dimension
+    // 32 c + l % 32 at positions 16 kb + 8 (l / 32) .. + 7)
+    const int G = lane >> 4, rq = (lane >> 2) & 3, q = lane & 3;
+    auto b_op = [&](int kb, int c) -> at_bf16x8 {
+        const int r0 = 16 * kb + 8 * (G >> 1) + rq;  // rows r0 and r0 + 4 (r0 % 4 == rq)
+        const int ch = (4 * c + 2 * (G & 1) + (q >> 1)) ^ (2 * rq);
+        const char *t8 = reinterpret_cast<const char *>(tile) + 8 * (q & 1);
+        const at_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t8 + (r0 * 16 + ch) * 16));
+        const at_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t8 + ((r0 + 4) * 16 + ch) * 16));
+        return __builtin_bit_cast(at_bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto accum = [&](const uint4 (&v)[8], int t) {
+        stage(v, t);
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            const at_bf16x8 a = a_op(t, kb);
+#pragma unroll
+            for (int c = 0; c < 4; c++) oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b_op(kb, c), oacc[c], 0, 0, 0);
+        }
+    };
+    for (int t = w; t < nt; t += 4) {
+        if (t + 2 < nt) issue_v(vb, t + 2);
+        accum(va, t);
+        if (t + 4 < nt) issue_v(va, t + 4);
+        if (t + 2 < nt) accum(vb, t + 2);
+    }
+    // O[head 4 (l / 32) + i][32 c + l % 32] = row i (high) + row 8 + i (low);
+    // wave 1's sums reach wave 0 through its own (finished) tile
+    float o[4][4];
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) o[c][i] = oacc[c][i] + oacc[c][4 + i];
+    float *xs = reinterpret_cast<float *>(vst[1]);
+    if (w == 1) {
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) xs[(4 * c + i) * 64 + lane] = o[c][i];
+    }
+    __syncthreads();
+    const int NC = p.n_chunks;
+    const int cl = blockIdx.x;
+    if (w == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int h = g * 8 + 4 * mh2 + i;
+                p.part_o[(((size_t)b * p.Hq + h) * NC + cl) * AT_D + 32 * c + mc] = o[c][i] + xs[(4 * c + i) * 64 + lane];
+            }
+    }
+    if (lane < 4) {
+        const size_t at = ((size_t)b * p.Hq + g * 8 + 4 * w + lane) * NC + cl;
+        float m = mh[0], l = lh[0];
+#pragma unroll
+        for (int h = 1; h < 4; h++)
+            if (lane == h) {
+                m = mh[h];
+                l = lh[h];
+            }
+        p.part_m[at] = m;
+        p.part_l[at] = l;
+    }
+}
+
 // one block per (sequence, query head); wave w merges chunks w, w + 16, ...,
 // lane covers dimensions 2 lane, 2 lane + 1; the waves' sums are added in
 // wave order
@@ -554,14 +735,18 @@ __global__ void __launch_bounds__(64 * AT_COMB_WAVES) attn_combine(AttnArgs p) {
     }
 }
 
-template <int HW, int WV, bool MF>
-void launch_chunks(const AttnArgs &p, hipStream_t st) {
+template <typename Kern>
+void launch_grid(Kern kern, int threads, const AttnArgs &p, hipStream_t st) {
     const dim3 grid(p.n_chunks, p.Hkv, p.B);
-    auto kern = attn_chunk<HW, WV, MF>;
     if (p.ev)
-        hipExtLaunchKernelGGL(kern, grid, dim3(64 * WV), 0, st, p.ev[0], p.ev[1], 0, p);
+        hipExtLaunchKernelGGL(kern, grid, dim3(threads), 0, st, p.ev[0], p.ev[1], 0, p);
     else
-        hipLaunchKernelGGL(kern, grid, dim3(64 * WV), 0, st, p);
+        hipLaunchKernelGGL(kern, grid, dim3(threads), 0, st, p);
+}
+
+template <int HW, int WV>
+void launch_chunks(const AttnArgs &p, hipStream_t st) {
+    launch_grid(attn_chunk<HW, WV>, 64 * WV, p, st);
 }
 
 }  // namespace
@@ -569,8 +754,9 @@ void launch_chunks(const AttnArgs &p, hipStream_t st) {
 // Chunk size: 32 positions for a sliding window (its 513 positions then
 // spread over 17-18 blocks per key/value head, each with one load group of
 // keys and one of values in flight); for full attention the
-// smallest power of two in [64, 1024] that keeps the blocks of a call to
-// about 1024 at the cache's full length.
+// smallest power of two in [64, 512] that keeps the blocks of a call to
+// about 1024 at the cache's full length (512 positions keep the matrix-core
+// kernel's LDS at 36.5 KB, four blocks per CU).
 int attn_chunk_size(int window, int max_len, int B, int Hkv) {
     if (window > 0) return 32;
     int c = 64;
@@ -588,18 +774,19 @@ int attn_chunk_slots(int window, int max_len, int chunk) {
 hipError_t launch_attn(const AttnArgs &a, hipStream_t st) {
     AttnArgs p = a;
     const int grp = p.Hq / p.Hkv;
-    // matrix-core scores for full layers (measured: 90.0 -> 84.9 us at 128k);
-    // a window's 32-position chunks are faster without the LDS staging they need
+    // full layers with groups of 8 on the matrix cores (measured at 128k:
+    // scores 90.0 -> 84.9 us, values ...); a window's 32-position chunks
+    // are faster on the vector path without the LDS staging
     if (grp == 8 && p.window == 0)
-        launch_chunks<4, 2, true>(p, st);
+        launch_grid(attn_chunk_mf, 128, p, st);
     else if (grp == 8)
-        launch_chunks<4, 2, false>(p, st);
+        launch_chunks<4, 2>(p, st);
     else if (grp == 4)
-        launch_chunks<4, 1, false>(p, st);
+        launch_chunks<4, 1>(p, st);
     else if (grp == 2)
-        launch_chunks<2, 1, false>(p, st);
+        launch_chunks<2, 1>(p, st);
     else
-        launch_chunks<1, 1, false>(p, st);
+        launch_chunks<1, 1>(p, st);
     const dim3 gc(p.B, p.Hq);
     if (p.ev)
         hipExtLaunchKernelGGL(attn_combine, gc, dim3(64 * AT_COMB_WAVES), 0, st, p.ev[2], p.ev[3], 0, p);
