@@ -11,29 +11,31 @@
 // embedding turns the pairs (i, i + 64) by P * base^(-2i/128); the cache
 // holds bfloat16 keys (normalised and rotated) and values.
 //
-// Two kernels:
-//   attn_chunk   per (sequence, key/value head, chunk of positions): the
-//                group's query heads normalised and rotated in registers
-//                (the 64 rotary angles reduced in fp64, since P * freq needs
-//                more than fp32 at long positions), against the chunk's keys
-//                (scores to LDS), the chunk's max and exp-sum per head, then
-//                the values weighted by the exponentials; partial (max, sum,
-//                output) per chunk to the workspace.  The block whose chunk
-//                holds P computes the new key (normalised, rotated) and value
-//                in bf16, uses them for row P and writes them to the caches;
-//                no other block reads row P;
-//   attn_combine per (sequence, query head): the chunks merged with the
-//                sink in a fixed order: out = sum_c e^(m_c - M) o_c /
-//                (e^(z - M) + sum_c e^(m_c - M) l_c), M = max(z, max_c m_c).
-// Chunks are 64 positions in sliding-window layers (a window spreads over
-// 9-10 blocks per key/value head) and up to 1024 in full layers (about 1024
-// blocks per call at the cache's length); within a chunk two load groups of
-// 32 positions are in flight, the next loading while one is computed.
-// The cache is the stream: a full layer at long context reads 2 KiB per
-// position per key/value head pair (K and V), so attn_chunk is bound by HBM.
-// Lanes: 8 lanes per position (16 dimensions each, two 16-byte loads of a
-// 256-byte row), 8 positions per wave instruction; each wave serves up to 4
-// query heads of the group and keeps their query slices in registers.
+// Two kernels, one block per (sequence, key/value head, chunk of positions)
+// in the first, each writing the chunk's partial (max, exp-sum, output) per
+// query head to the workspace:
+//   attn_chunk     vector path (sliding windows, and groups of 1, 2 or 4):
+//                  the group's query heads normalised and rotated in
+//                  registers (the 64 rotary angles reduced in fp64, since
+//                  P * freq needs more than fp32 at long positions); scores
+//                  to LDS, the chunk's max and exp-sum per head, then the
+//                  values weighted by the exponentials.  8 lanes per position
+//                  (16 dimensions each, two 16-byte loads of a 256-byte row),
+//                  8 positions per wave instruction, two load groups of 32
+//                  positions in flight;
+//   attn_chunk_mf  matrix-core path (full layers, groups of 8): scores and
+//                  the value sums on v_mfma_f32_16x16x32_bf16 in one pass
+//                  with a running softmax (details at the kernel);
+//   attn_combine   per (sequence, query head): the chunks merged with the
+//                  sink in a fixed order: out = sum_c e^(m_c - M) o_c /
+//                  (e^(z - M) + sum_c e^(m_c - M) l_c), M = max(z, max_c m_c).
+// The block whose chunk holds P computes the new key (normalised, rotated)
+// and value in bf16, uses them for row P and writes them to the caches; no
+// other block reads row P.  Chunks are 32 positions in sliding-window layers
+// (a window spreads over 17-18 blocks per key/value head) and up to 512 in
+// full layers (about 1024 blocks per call at the cache's length).  The cache
+// is the stream: a full layer at long context reads 512 bytes per position
+// per key/value head (K and V), so the chunk kernels are bound by HBM.
 #include <hip/hip_runtime.h>
 
 #include "moe_device.h"
@@ -401,38 +403,53 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
     }
 }
 
+constexpr int AT_NT = 2;  // non-temporal: the cache is streamed once per call
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t at_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 typedef short at_s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) at_s16x4 lds_s16x4;
+typedef float at_f32x4 __attribute__((ext_vector_type(4)));
 
 // Matrix-core path: full layers (no rotary embedding) with 8 query heads
-// per key/value head; the same partials as attn_chunk.  Two waves; wave w
-// takes the 32-position tiles w, w + 2, ... of the chunk for all 8 heads.
-//   scores  A = the 8 prepared queries split into bf16 high and low halves
-//           (rows 0-7 and 8-15; rows 16-31 zero), B = the tile's keys straight
-//           from the cache (lane l: position l % 32, dimensions
-//           16 s + 8 (l / 32) .. + 7 for step s), 8 v_mfma_f32_32x32x16_bf16
-//           over the 128 dimensions; head h's score is row h + row h + 8
-//           (the split leaves about 2^-18 of the query);
-//   values  O[h][d] += sum_j e_hj V[j][d]: A = the exponentials split the
-//           same way (lane l: head row l % 32, positions 8 (l / 32) .. + 7 of
-//           a 16-position half), B = 8 positions of one dimension per lane.
-//           The tile's 32 value rows arrive 1 KB per load instruction (four
-//           whole rows), go to a wave-private LDS tile, and come back
-//           transposed by ds_read_b64_tr_b16: within a 16-lane group, lane i
-//           receives element i % 4 of the 8-byte reads of lanes 4 j + i / 4,
-//           j = 0..3, so four lanes reading 4 dimensions each of 4 rows hand
-//           every lane one dimension at 4 positions.  Two such reads make a
-//           B operand; 8 MFMAs per tile (two halves x four 32-dimension
-//           blocks).  The 16-byte chunk c of tile row r sits at c ^ 2 (r % 4),
-//           so the 4 rows a 16-lane group reads fall in distinct banks.
-// The two waves' value sums are added in wave order at the end.
-__global__ void __launch_bounds__(128) attn_chunk_mf(AttnArgs p) {
-    __shared__ float pe[8 * AT_CMAX];  // head h, position j at h * AT_CMAX + j: score, then exponential
+// per key/value head; the same partials as attn_chunk, in one pass over the
+// chunk with a running (online) softmax.  Two waves; wave w takes the
+// 32-position tiles w, w + 2, ... for all 8 heads and keeps its own running
+// max, sum and output; the two are merged at the end in wave order.
+// v_mfma_f32_16x16x32_bf16 throughout (lane l holds A[l % 16][8 (l / 16) + e],
+// B[8 (l / 16) + e][l % 16], e = 0..7, and D[4 (l / 16) + i][l % 16]):
+//   scores  S^T = K Q^T per 16-position half: A = 16 keys straight from the
+//           cache (lane: position l % 16, dimensions 32 s + 8 (l / 16) ..
+//           + 7 for step s), B = the 8 prepared queries split into bf16
+//           high and low halves (columns 0-7 and 8-15: the split leaves
+//           about 2^-18 of the query), 4 steps over the 128 dimensions;
+//           head h's score is column h + column h + 8, one exchange between
+//           lanes l and l ^ 8.  Lane l then holds head l % 8 at the 8
+//           positions 4 (l / 16) + i and 16 + 4 (l / 16) + i of the tile;
+//   values  O += P V: A = the exponentials of those 8 positions split high /
+//           low the same way (row l % 16), exactly where the scores left
+//           them; B = the same 8 positions of one dimension per lane.  The
+//           tile's 32 value rows arrive 1 KB per load instruction (four whole
+//           rows), go to a wave-private LDS tile, and come back transposed
+//           by ds_read_b64_tr_b16: within a 16-lane group, lane i receives
+//           element i % 4 of the 8-byte reads of lanes 4 j + i / 4, j = 0..3,
+//           so four lanes reading 4 dimensions each of 4 rows hand every lane
+//           one dimension at 4 positions.  Two reads per B operand; 8 MFMAs
+//           per tile (16-dimension blocks).  The 16-byte chunk c of tile row
+//           r sits at c ^ 2 (r % 4), so the 4 rows a 16-lane group reads
+//           fall in distinct banks.
+// Output rows: head h's high row h (lanes l / 16 = h / 4) plus its low row
+// h + 8 (lanes l / 16 = 2 + h / 4), one exchange between lanes l and l ^ 32.
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) attn_chunk_mf(AttnArgs p) {
     __shared__ uint4 vst[2][32 * 16];  // per wave: one tile of 32 value rows
     __shared__ float qsh[8][AT_D];
     __shared__ uint4 knsh[16], vnsh[16];  // the new key and value, bf16
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int sub = lane & 7, mc = lane & 31, mh2 = lane >> 5;
+    __shared__ float mls[2][2][8];        // per wave: running max and sum per head
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: tile offsets go to SGPRs
+    const int sub = lane & 7, col = lane & 15, G = lane >> 4;
     const int b = blockIdx.z, g = blockIdx.y;
     const int P = p.pos[b];
     if (P < 0 || P >= p.max_len) return;
@@ -440,29 +457,34 @@ __global__ void __launch_bounds__(128) attn_chunk_mf(AttnArgs p) {
     if (start >= end) return;
     const int n = end - start, nt = (n + 31) / 32;
     const size_t base = ((size_t)b * p.Hkv + g) * p.max_len;
-    const uint4 *Kc = reinterpret_cast<const uint4 *>(p.k_cache + base * AT_D);
-    const uint4 *Vc = reinterpret_cast<const uint4 *>(p.v_cache + base * AT_D);
-    // keys of tile t (B operands of the score MFMAs); rows past the chunk's
-    // end re-read its last row
-    auto issue_k = [&](uint4 (&bk)[8], int t) {
-        const int j = start + min(t * 32 + mc, n - 1);
+    // the chunk's valid rows as buffer resources: reads past its end return zero
+    const __amdgpu_buffer_rsrc_t krs = at_rsrc(p.k_cache + (base + start) * AT_D, (uint32_t)n * 256u);
+    const __amdgpu_buffer_rsrc_t vrs = at_rsrc(p.v_cache + (base + start) * AT_D, (uint32_t)n * 256u);
+    const int vo_k = col * 256 + G * 16, vo_v = G * 256 + col * 16;
+    // keys of tile t: k[4 ph + s] = half ph, step s (lane: position
+    // 32 t + 16 ph + l % 16, dimensions 32 s + 8 (l / 16) ..); values: v[i] =
+    // rows 4 i .. 4 i + 3 (lane: row 4 i + l / 16, chunk l % 16)
+    auto issue_k = [&](uint4 (&k)[8], int t) {
 #pragma unroll
-        for (int st = 0; st < 8; st++) bk[st] = ld_stream16(Kc + (size_t)j * 16 + 2 * st + mh2);
+        for (int ph = 0; ph < 2; ph++)
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const auto c = __builtin_amdgcn_raw_buffer_load_b128(krs, vo_k + 64 * s, 8192 * t + 4096 * ph, AT_NT);
+                k[4 * ph + s] = make_uint4(c[0], c[1], c[2], c[3]);
+            }
     };
-    // values of tile t: instruction i loads rows 4 i .. 4 i + 3 (lane l: row
-    // 4 i + l / 16, chunk l % 16); rows past the end re-read the last row
     auto issue_v = [&](uint4 (&v)[8], int t) {
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int r = min(32 * t + 4 * i + (lane >> 4), n - 1);
-            v[i] = ld_stream16(Vc + (size_t)(start + r) * 16 + (lane & 15));
+            const auto c = __builtin_amdgcn_raw_buffer_load_b128(vrs, vo_v + 1024 * (i & 3), 8192 * t + 4096 * (i >> 2), AT_NT);
+            v[i] = make_uint4(c[0], c[1], c[2], c[3]);
         }
     };
-    // the first tiles of keys and values are requested before anything else
-    uint4 bk0[8], bk1[8], va[8], vb[8];
+    // the first tile's keys and values are requested before anything else
+    uint4 k0[8], v0[8], k1[8], v1[8];
     if (w < nt) {
-        issue_k(bk0, w);
-        issue_v(va, w);
+        issue_k(k0, w);
+        issue_v(v0, w);
     }
     // the 8 prepared queries (wave w: heads 4 w .. 4 w + 3) and the new key
     // and value through LDS
@@ -476,188 +498,178 @@ __global__ void __launch_bounds__(128) attn_chunk_mf(AttnArgs p) {
         }
     }
     if (end == P + 1) {
-        uint4 k0, k1, v0, v1;
-        new_token(p, b, g, P, nullptr, false, lane, w == 0 && lane < 8, k0, k1, v0, v1);
+        uint4 nk0, nk1, nv0, nv1;
+        new_token(p, b, g, P, nullptr, false, lane, w == 0 && lane < 8, nk0, nk1, nv0, nv1);
         if (w == 0 && lane < 8) {
-            knsh[2 * sub] = k0;
-            knsh[2 * sub + 1] = k1;
-            vnsh[2 * sub] = v0;
-            vnsh[2 * sub + 1] = v1;
+            knsh[2 * sub] = nk0;
+            knsh[2 * sub + 1] = nk1;
+            vnsh[2 * sub] = nv0;
+            vnsh[2 * sub + 1] = nv1;
         }
     }
     __syncthreads();
-
-    // scores
-    at_bf16x8 aq[8];
+    // B operands of the scores: column col = head col % 8, high / low half
+    at_bf16x8 bq[4];
 #pragma unroll
-    for (int st = 0; st < 8; st++) {
+    for (int s = 0; s < 4; s++) {
+        const float *qr = &qsh[col & 7][32 * s + 8 * G];
         uint32_t wd[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            uint32_t pr = 0;
-            if (mc < 16) {
-                const float *qr = &qsh[mc & 7][16 * st + 8 * mh2 + 2 * e];
-                float v0 = qr[0], v1 = qr[1];
-                if (mc >= 8) {  // low half: what the high half leaves
-                    v0 -= __uint_as_float((uint32_t)to_bf16_rne(v0) << 16);
-                    v1 -= __uint_as_float((uint32_t)to_bf16_rne(v1) << 16);
-                }
-                pr = pack_bf16x2(v0, v1);
+            float x0 = qr[2 * e], x1 = qr[2 * e + 1];
+            if (col >= 8) {  // low half: what the high half leaves
+                x0 -= __uint_as_float((uint32_t)to_bf16_rne(x0) << 16);
+                x1 -= __uint_as_float((uint32_t)to_bf16_rne(x1) << 16);
             }
-            wd[e] = pr;
+            wd[e] = pack_bf16x2(x0, x1);
         }
-        aq[st] = __builtin_bit_cast(at_bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+        bq[s] = __builtin_bit_cast(at_bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
     }
-    auto scores = [&](uint4 (&bk)[8], int t) {
-        const int j = start + min(t * 32 + mc, n - 1);
-        if (j == P) {
-#pragma unroll
-            for (int st = 0; st < 8; st++) bk[st] = knsh[2 * st + mh2];
-        }
-        at_f32x16 acc;
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc[i] = 0.f;
-#pragma unroll
-        for (int st = 0; st < 8; st++)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[st], __builtin_bit_cast(at_bf16x8, bk[st]), acc, 0, 0, 0);
-        // acc[i] = row 4 (l / 32) + i (high halves), acc[4 + i] = row 8 + 4 (l / 32) + i (low halves)
-        const int jj = t * 32 + mc;
-        if (jj < n) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) pe[(4 * mh2 + i) * AT_CMAX + jj] = acc[i] + acc[4 + i];
-        }
-    };
-    for (int t = w; t < nt; t += 4) {
-        if (t + 2 < nt) issue_k(bk1, t + 2);
-        scores(bk0, t);
-        if (t + 4 < nt) issue_k(bk0, t + 4);
-        if (t + 2 < nt) scores(bk1, t + 2);
-    }
-    __syncthreads();
 
-    // wave w, heads 4 w + h: the chunk's max, exponentials in place, their sum
-    float mh[4], lh[4];
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-        const float *ph = pe + (4 * w + h) * AT_CMAX;
-        float m = -INFINITY;
-        for (int j = lane; j < n; j += 64) m = fmaxf(m, ph[j]);
-        mh[h] = wave_max_f(m);
-    }
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-        float *ph = pe + (4 * w + h) * AT_CMAX;
-        float l = 0.f;
-        for (int j = lane; j < n; j += 64) {
-            const float e = __expf(ph[j] - mh[h]);
-            ph[j] = e;
-            l += e;
-        }
-        lh[h] = wave_sum(l);
-    }
-    __syncthreads();
-
-    // values
-    at_f32x16 oacc[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) oacc[c][i] = 0.f;
     uint4 *tile = vst[w];
-    // tile t's rows to LDS: row P is the new value, rows past the end zero
-    auto stage = [&](const uint4 (&v)[8], int t) {
+    at_f32x4 oacc[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int r = 4 * i + (lane >> 4), c = lane & 15;
-            const int jj = 32 * t + r;
-            uint4 x = v[i];
-            if (start + jj == P) x = vnsh[c];
-            if (jj >= n) x = make_uint4(0, 0, 0, 0);
-            tile[r * 16 + (c ^ (2 * (r & 3)))] = x;
-        }
-    };
-    // A operand: exponentials of half kb of tile t, split high / low
-    auto a_op = [&](int t, int kb) -> at_bf16x8 {
-        const int j0 = 32 * t + 16 * kb + 8 * mh2;
-        const float4 *src = reinterpret_cast<const float4 *>(pe + (mc & 7) * AT_CMAX + j0);
-        const float4 f0 = src[0], f1 = src[1];
-        const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-        uint32_t wd[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            float v0 = j0 + 2 * e < n ? f[2 * e] : 0.f;
-            float v1 = j0 + 2 * e + 1 < n ? f[2 * e + 1] : 0.f;
-            if (mc >= 8) {
-                v0 -= __uint_as_float((uint32_t)to_bf16_rne(v0) << 16);
-                v1 -= __uint_as_float((uint32_t)to_bf16_rne(v1) << 16);
-            }
-            wd[e] = mc < 16 ? pack_bf16x2(v0, v1) : 0u;
-        }
-        return __builtin_bit_cast(at_bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
-    };
-    // B operand: half kb, dimensions 32 c .. 32 c + 31 (lane l: dimension
-    // 32 c + l % 32 at positions 16 kb + 8 (l / 32) .. + 7)
-    const int G = lane >> 4, rq = (lane >> 2) & 3, q = lane & 3;
-    auto b_op = [&](int kb, int c) -> at_bf16x8 {
-        const int r0 = 16 * kb + 8 * (G >> 1) + rq;  // rows r0 and r0 + 4 (r0 % 4 == rq)
-        const int ch = (4 * c + 2 * (G & 1) + (q >> 1)) ^ (2 * rq);
+    for (int c = 0; c < 8; c++) oacc[c] = at_f32x4{0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lrun = 0.f;  // head l % 8
+    // B operand of values block c: dimension 16 c + l % 16 at the lane's 8
+    // positions (read 0: rows 4 (l / 16) + j, read 1: rows 16 + 4 (l / 16) + j)
+    const int rq = (lane >> 2) & 3, q = lane & 3;
+    auto b_val = [&](int c) -> at_bf16x8 {
+        const int r0 = 4 * G + rq;  // rows r0 and r0 + 16, both with r % 4 == rq
+        const int ch = (2 * c + (q >> 1)) ^ (2 * rq);
         const char *t8 = reinterpret_cast<const char *>(tile) + 8 * (q & 1);
         const at_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t8 + (r0 * 16 + ch) * 16));
-        const at_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t8 + ((r0 + 4) * 16 + ch) * 16));
+        const at_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t8 + ((r0 + 16) * 16 + ch) * 16));
         return __builtin_bit_cast(at_bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto accum = [&](const uint4 (&v)[8], int t) {
-        stage(v, t);
+    // tile t; next_v requests the values of the wave's next tile once this
+    // tile's have left their registers
+    auto process = [&](uint4 (&k)[8], const uint4 (&v)[8], int t, auto next_v) {
+        // value rows to LDS (rows past the chunk's end arrive as zero); in the
+        // chunk's last tile row P is the new value
+        const bool last = t == nt - 1;
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
-            const at_bf16x8 a = a_op(t, kb);
-#pragma unroll
-            for (int c = 0; c < 4; c++) oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b_op(kb, c), oacc[c], 0, 0, 0);
+        for (int i = 0; i < 8; i++) {
+            const int r = 4 * i + G;
+            uint4 x = v[i];
+            if (last && start + 32 * t + r == P) x = vnsh[col];
+            tile[r * 16 + (col ^ (2 * (r & 3)))] = x;
         }
-    };
-    for (int t = w; t < nt; t += 4) {
-        if (t + 2 < nt) issue_v(vb, t + 2);
-        accum(va, t);
-        if (t + 4 < nt) issue_v(va, t + 4);
-        if (t + 2 < nt) accum(vb, t + 2);
-    }
-    // O[head 4 (l / 32) + i][32 c + l % 32] = row i (high) + row 8 + i (low);
-    // wave 1's sums reach wave 0 through its own (finished) tile
-    float o[4][4];
+        next_v();
+        // scores of the two halves
+        float sc[8];
 #pragma unroll
-    for (int c = 0; c < 4; c++)
+        for (int ph = 0; ph < 2; ph++) {
+            if (last && start + 32 * t + 16 * ph + col == P) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) o[c][i] = oacc[c][i] + oacc[c][4 + i];
-    float *xs = reinterpret_cast<float *>(vst[1]);
-    if (w == 1) {
+                for (int s = 0; s < 4; s++) k[4 * ph + s] = knsh[4 * s + G];
+            }
+            at_f32x4 acc = at_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; c++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) xs[(4 * c + i) * 64 + lane] = o[c][i];
-    }
-    __syncthreads();
-    const int NC = p.n_chunks;
-    const int cl = blockIdx.x;
-    if (w == 0) {
-#pragma unroll
-        for (int c = 0; c < 4; c++)
+            for (int s = 0; s < 4; s++)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(at_bf16x8, k[4 * ph + s]), bq[s], acc, 0,
+                                                             0, 0);
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int h = g * 8 + 4 * mh2 + i;
-                p.part_o[(((size_t)b * p.Hq + h) * NC + cl) * AT_D + 32 * c + mc] = o[c][i] + xs[(4 * c + i) * 64 + lane];
+                const float s2 = acc[i] + at_xor(acc[i], 3);  // high + low column
+                const int jj = 32 * t + 16 * ph + 4 * G + i;
+                sc[4 * ph + i] = jj < n ? s2 : -INFINITY;
             }
-    }
-    if (lane < 4) {
-        const size_t at = ((size_t)b * p.Hq + g * 8 + 4 * w + lane) * NC + cl;
-        float m = mh[0], l = lh[0];
+        }
+        // running max, rescale, exponentials
+        float tm = sc[0];
 #pragma unroll
-        for (int h = 1; h < 4; h++)
-            if (lane == h) {
-                m = mh[h];
-                l = lh[h];
+        for (int e = 1; e < 8; e++) tm = fmaxf(tm, sc[e]);
+        tm = fmaxf(tm, at_xor(tm, 4));
+        tm = fmaxf(tm, at_xor(tm, 5));
+        const float mnew = fmaxf(mrun, tm);
+        const float alpha = __expf(mrun - mnew);  // 0 on the first tile
+        mrun = mnew;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+            // output row 4 (l / 16) + i belongs to head 4 ((l / 16) & 1) + i
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float a = __shfl(alpha, (lane & 0x30) | (4 * (G & 1) + i), 64);
+#pragma unroll
+                for (int c = 0; c < 8; c++) oacc[c][i] *= a;
             }
-        p.part_m[at] = m;
-        p.part_l[at] = l;
+        }
+        float pe[8], ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            pe[e] = __expf(sc[e] - mnew);
+            ps += pe[e];
+        }
+        lrun = lrun * alpha + ps;
+        uint32_t wd[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            float x0 = pe[2 * e], x1 = pe[2 * e + 1];
+            if (col >= 8) {
+                x0 -= __uint_as_float((uint32_t)to_bf16_rne(x0) << 16);
+                x1 -= __uint_as_float((uint32_t)to_bf16_rne(x1) << 16);
+            }
+            wd[e] = pack_bf16x2(x0, x1);
+        }
+        const at_bf16x8 a = __builtin_bit_cast(at_bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+#pragma unroll
+        for (int c = 0; c < 8; c++) oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b_val(c), oacc[c], 0, 0, 0);
+    };
+    // keys two tiles ahead, values one
+    for (int t = w; t < nt; t += 4) {
+        if (t + 2 < nt) issue_k(k1, t + 2);
+        process(k0, v0, t, [&] {
+            if (t + 2 < nt) issue_v(v1, t + 2);
+        });
+        if (t + 4 < nt) issue_k(k0, t + 4);
+        if (t + 2 < nt)
+            process(k1, v1, t + 2, [&] {
+                if (t + 4 < nt) issue_v(v0, t + 4);
+            });
+    }
+    // this wave's sum over its lanes' positions; high + low output rows
+    lrun += at_xor(lrun, 4);
+    lrun += at_xor(lrun, 5);
+    float o[8][4];
+#pragma unroll
+    for (int c = 0; c < 8; c++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) o[c][i] = oacc[c][i] + at_xor(oacc[c][i], 5);
+    if (lane < 8) {
+        mls[w][0][lane] = mrun;
+        mls[w][1][lane] = lrun;
+    }
+    // wave 1's output (lanes 0-31: heads 4 (l / 16) + i, dimension 16 c + l % 16)
+    // reaches wave 0 through its own, finished tile
+    float *xs = reinterpret_cast<float *>(vst[1]);
+    if (w == 1 && lane < 32) {
+#pragma unroll
+        for (int c = 0; c < 8; c++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) xs[(4 * c + i) * 32 + lane] = o[c][i];
+    }
+    __syncthreads();
+    if (w != 0) return;
+    const int NC = p.n_chunks;
+    const int cl = blockIdx.x;
+    if (lane < 32) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int h = 4 * G + i;
+            const float m0 = mls[0][0][h], m1 = mls[1][0][h];
+            const float M = fmaxf(m0, m1);
+            const float s0 = __expf(m0 - M), s1 = __expf(m1 - M);
+            float *dst = p.part_o + (((size_t)b * p.Hq + g * 8 + h) * NC + cl) * AT_D + col;
+#pragma unroll
+            for (int c = 0; c < 8; c++) dst[16 * c] = s0 * o[c][i] + s1 * xs[(4 * c + i) * 32 + lane];
+        }
+    }
+    if (lane < 8) {
+        const float m0 = mls[0][0][lane], m1 = mls[1][0][lane];
+        const float M = fmaxf(m0, m1);
+        const size_t at = ((size_t)b * p.Hq + g * 8 + lane) * NC + cl;
+        p.part_m[at] = M;
+        p.part_l[at] = __expf(m0 - M) * mls[0][1][lane] + __expf(m1 - M) * mls[1][1][lane];
     }
 }
 
