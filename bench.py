@@ -116,9 +116,9 @@ COUNTER_TRAFFIC = {
     ("lm_head_q4_1_t1", "lm_head_kernel"): dict(source_digest="a0621f359d9319a6",
                                                 fetch_bytes=round(91654.3 * _FETCH_SCALE * 1024),
                                                 write_bytes=round(572.2 * _WRITE_SCALE * 1024)),
-    ("attn_full128k", "attn_chunk"): dict(source_digest="b8d3f2684d475380",
-                                          fetch_bytes=round(152520.2 * _FETCH_SCALE * 1024),
-                                          write_bytes=round(4610.1 * _WRITE_SCALE * 1024)),
+    ("attn_full128k", "attn_chunk"): dict(source_digest="eb0a2c2c80f6cac5",
+                                          fetch_bytes=round(131342.2 * _FETCH_SCALE * 1024),
+                                          write_bytes=round(2306.0 * _WRITE_SCALE * 1024)),
 }
 
 

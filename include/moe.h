@@ -299,8 +299,10 @@ moe_status moe_attn_workspace_size(const moe_attn_dims *dims, int32_t n_seqs, in
    positions per block of the first kernel, and *slots chunk partials per
    (sequence, query head) in the workspace (the combine kernel merges the
    slots a position range touches).  Sliding windows take 32-position
-   chunks; full layers the smallest power of two in [64, 512] that keeps a
-   call near 1024 blocks.  Same argument checks as moe_attn_workspace_size. */
+   chunks; full layers the smallest power of two in [64, 1024] that keeps a
+   call near 512 blocks with groups of 8 query heads (the matrix-core
+   kernel) and near 1024 blocks otherwise.  Same argument checks as
+   moe_attn_workspace_size. */
 moe_status moe_attn_chunk_plan(const moe_attn_dims *dims, int32_t n_seqs, int32_t max_len, int32_t *chunk,
                                int32_t *slots);
 

@@ -643,7 +643,7 @@ struct AttnWs {
 static AttnWs attn_ws(const moe_attn_dims &d, int B, int max_len) {
     AttnWs L{};
     const size_t nc = (size_t)moe::attn_chunk_slots(d.window, max_len,
-                                                    moe::attn_chunk_size(d.window, max_len, B, d.n_kv_heads));
+                                                    moe::attn_chunk_size(d.window, max_len, B, d.n_q_heads, d.n_kv_heads));
     size_t o = 0;
     auto take = [&](size_t bytes) {
         size_t at = o;
@@ -684,7 +684,7 @@ moe_status moe_attn_chunk_plan(const moe_attn_dims *d, int32_t n_seqs, int32_t m
                                int32_t *slots) {
     MOE_TRY(attn_check(d, n_seqs, max_len));
     if (!chunk || !slots) return fail(MOE_ERR_INVALID_ARG, "chunk or slots is NULL");
-    *chunk = moe::attn_chunk_size(d->window, max_len, n_seqs, d->n_kv_heads);
+    *chunk = moe::attn_chunk_size(d->window, max_len, n_seqs, d->n_q_heads, d->n_kv_heads);
     *slots = moe::attn_chunk_slots(d->window, max_len, *chunk);
     return ok();
 }
@@ -727,7 +727,7 @@ static moe_status attn_prepare(const moe_attn_dims *d, int32_t B, int32_t max_le
     a.Hkv = d->n_kv_heads;
     a.window = d->window;
     a.max_len = max_len;
-    a.chunk = moe::attn_chunk_size(d->window, max_len, B, d->n_kv_heads);
+    a.chunk = moe::attn_chunk_size(d->window, max_len, B, d->n_q_heads, d->n_kv_heads);
     a.n_chunks = moe::attn_chunk_slots(d->window, max_len, a.chunk);
     a.rope_base = d->rope_base;
     a.eps = d->norm_eps;

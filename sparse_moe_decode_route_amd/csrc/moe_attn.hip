@@ -32,8 +32,9 @@
 // The block whose chunk holds P computes the new key (normalised, rotated)
 // and value in bf16, uses them for row P and writes them to the caches; no
 // other block reads row P.  Chunks are 32 positions in sliding-window layers
-// (a window spreads over 17-18 blocks per key/value head) and up to 512 in
-// full layers (about 1024 blocks per call at the cache's length).  The cache
+// (a window spreads over 17-18 blocks per key/value head) and up to 1024 in
+// full layers (about 512 blocks per call at the cache's length on the
+// matrix-core path, 1024 on the vector path).  The cache
 // is the stream: a full layer at long context reads 512 bytes per position
 // per key/value head (K and V), so the chunk kernels are bound by HBM.
 #include <hip/hip_runtime.h>
@@ -49,7 +50,7 @@ typedef __bf16 at_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float at_f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int AT_D = 128;       // head size
-constexpr int AT_CMAX = 512;    // largest chunk (positions)
+constexpr int AT_CMAX = 1024;   // largest chunk (positions)
 constexpr int AT_UT = 4;        // tiles of 8 positions per load group
 constexpr int AT_COMB_WAVES = 16;
 
@@ -442,7 +443,7 @@ typedef float at_f32x4 __attribute__((ext_vector_type(4)));
 //           fall in distinct banks.
 // Output rows: head h's high row h (lanes l / 16 = h / 4) plus its low row
 // h + 8 (lanes l / 16 = 2 + h / 4), one exchange between lanes l and l ^ 32.
-__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) attn_chunk_mf(AttnArgs p) {
+__global__ void __launch_bounds__(128) attn_chunk_mf(AttnArgs p) {
     __shared__ uint4 vst[2][32 * 16];  // per wave: one tile of 32 value rows
     __shared__ float qsh[8][AT_D];
     __shared__ uint4 knsh[16], vnsh[16];  // the new key and value, bf16
@@ -765,16 +766,19 @@ void launch_chunks(const AttnArgs &p, hipStream_t st) {
 
 // Chunk size: 32 positions for a sliding window (its 513 positions then
 // spread over 17-18 blocks per key/value head, each with one load group of
-// keys and one of values in flight); for full attention the
-// smallest power of two in [64, 512] that keeps the blocks of a call to
-// about 1024 at the cache's full length (512 positions keep the matrix-core
-// kernel's LDS at 36.5 KB, four blocks per CU).
-int attn_chunk_size(int window, int max_len, int B, int Hkv) {
+// keys and one of values in flight).  Full attention: the smallest power of
+// two in [64, 1024] that keeps the blocks of a call at the cache's full
+// length to about 512 on the matrix-core path (one wave per SIMD, two blocks
+// per CU: every block resident at once) and about 1024 on the vector path.
+int attn_chunk_size(int window, int max_len, int B, int Hq, int Hkv) {
     if (window > 0) return 32;
+    const long long target = attn_uses_mfma(window, Hq, Hkv) ? 512 : 1024;
     int c = 64;
-    while (c < AT_CMAX && (long long)((max_len + c - 1) / c) * B * Hkv > 1024) c *= 2;
+    while (c < AT_CMAX && (long long)((max_len + c - 1) / c) * B * Hkv > target) c *= 2;
     return c;
 }
+
+bool attn_uses_mfma(int window, int Hq, int Hkv) { return window == 0 && Hq == 8 * Hkv; }
 
 int attn_chunk_slots(int window, int max_len, int chunk) {
     // a window of W positions spans at most ceil((W - 1) / chunk) + 1 chunks
@@ -787,9 +791,9 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t st) {
     AttnArgs p = a;
     const int grp = p.Hq / p.Hkv;
     // full layers with groups of 8 on the matrix cores (measured at 128k:
-    // scores 90.0 -> 84.9 us, values ...); a window's 32-position chunks
-    // are faster on the vector path without the LDS staging
-    if (grp == 8 && p.window == 0)
+    // 84.4 us on the vector path, 46.9 us here); a window's 32-position
+    // chunks are faster on the vector path without the LDS staging
+    if (attn_uses_mfma(p.window, p.Hq, p.Hkv))
         launch_grid(attn_chunk_mf, 128, p, st);
     else if (grp == 8)
         launch_chunks<4, 2>(p, st);

@@ -83,7 +83,7 @@ hipError_t launch_repack_q4_1_matrix(const uint8_t *canonical, uint8_t *packed, 
 // Decode attention (one new token per sequence), head size 128.
 struct AttnArgs {
     int B, Hq, Hkv, window, max_len;
-    int chunk;     // positions per chunk: attn_chunk_size(window, max_len, B, Hkv)
+    int chunk;     // positions per chunk: attn_chunk_size(window, max_len, B, Hq, Hkv)
     int n_chunks;  // chunk slots per (sequence, head): attn_chunk_slots(window, max_len, chunk)
     float rope_base, eps;
     double rope_freq[64];  // base^(-2i/128), i < 64 (host-computed in fp64)
@@ -95,7 +95,8 @@ struct AttnArgs {
     float *part_o;                // workspace [B, Hq, n_chunks, 128]
     hipEvent_t *ev;               // optional start/stop pairs for the 2 kernels
 };
-int attn_chunk_size(int window, int max_len, int B, int Hkv);
+bool attn_uses_mfma(int window, int Hq, int Hkv);
+int attn_chunk_size(int window, int max_len, int B, int Hq, int Hkv);
 int attn_chunk_slots(int window, int max_len, int chunk);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t st);
 

@@ -92,6 +92,13 @@ def test_attn_full_128k_context():
     _run(32, 4, 0, 131072, [131071], cfg_id=76, label="full 128k")
 
 
+def test_attn_full_long_ragged_chunk():
+    # 1024-position chunks: P = 100,003 leaves 676 positions in its chunk
+    # (21 full 32-position tiles and a ragged one, split unevenly over the
+    # chunk kernel's two waves)
+    _run(32, 4, 0, 131072, [100003], cfg_id=79, label="full long ragged")
+
+
 def test_attn_invalid_position_gives_nan_and_keeps_caches():
     a = gen.make_attn(2, 32, 4, 128, 64, cfg_id=77)
     d = gen.AttnInputs(*(t.to(_dev()) for t in (a.q, a.k_new, a.v_new, a.q_norm_w, a.k_norm_w, a.sinks,
