@@ -674,9 +674,10 @@ __global__ void __launch_bounds__(128) attn_chunk_mf(AttnArgs p) {
     }
 }
 
-// one block per (sequence, query head); wave w merges chunks w, w + 16, ...,
-// lane covers dimensions 2 lane, 2 lane + 1; the waves' sums are added in
-// wave order
+// one block per (sequence, query head); wave w merges chunks w, w + 16, ...
+// with a running max (one round of loads: four chunks in flight per wave),
+// lane covers dimensions 2 lane, 2 lane + 1; the waves' (max, sum, output)
+// and the sink are then merged in wave order
 __global__ void __launch_bounds__(64 * AT_COMB_WAVES) attn_combine(AttnArgs p) {
     __shared__ float red[AT_COMB_WAVES][2];
     __shared__ float2 ov[AT_COMB_WAVES][64];
@@ -696,20 +697,8 @@ __global__ void __launch_bounds__(64 * AT_COMB_WAVES) attn_combine(AttnArgs p) {
         const int c0 = (cf + k) * p.chunk;
         return max(c0, lo) < min(c0 + p.chunk, P + 1);
     };
-    const float z = p.sinks[h];
-    // M = max(z, max_c m_c): every lane of every wave takes part
-    float m = z;
-    for (int k = threadIdx.x; k < nc; k += 64 * AT_COMB_WAVES)
-        if (valid(k)) m = fmaxf(m, p.part_m[at + k]);
-    m = wave_max_f(m);
-    if (lane == 0) red[w][0] = m;
-    __syncthreads();
-    float M = red[0][0];
-#pragma unroll
-    for (int i = 1; i < AT_COMB_WAVES; i++) M = fmaxf(M, red[i][0]);
-    // this wave's chunks: sum of e^(m_c - M) l_c and of e^(m_c - M) o_c,
-    // four chunks' loads in flight at a time
-    float L = 0.f;
+    // this wave's chunks: running max m, sum L and output acc
+    float m = -INFINITY, L = 0.f;
     float2 acc = make_float2(0.f, 0.f);
     for (int k0 = w; k0 < nc; k0 += 4 * AT_COMB_WAVES) {
         float mk[4], lk[4];
@@ -725,23 +714,34 @@ __global__ void __launch_bounds__(64 * AT_COMB_WAVES) attn_combine(AttnArgs p) {
         for (int u = 0; u < 4; u++) {
             const int k = k0 + u * AT_COMB_WAVES;
             if (k >= nc || !valid(k)) continue;
-            const float e = __expf(mk[u] - M);
-            L = __builtin_fmaf(e, lk[u], L);
-            acc.x = __builtin_fmaf(e, vk[u].x, acc.x);
-            acc.y = __builtin_fmaf(e, vk[u].y, acc.y);
+            const float mn = fmaxf(m, mk[u]);
+            const float a = __expf(m - mn), e = __expf(mk[u] - mn);  // a = 0 for the first chunk
+            L = a * L + e * lk[u];
+            acc.x = a * acc.x + e * vk[u].x;
+            acc.y = a * acc.y + e * vk[u].y;
+            m = mn;
         }
     }
-    if (lane == 0) red[w][1] = L;
+    if (lane == 0) {
+        red[w][0] = m;
+        red[w][1] = L;
+    }
     ov[w][lane] = acc;
     __syncthreads();
     if (w == 0) {
+        // M = max(z, max_w m_w); waves without chunks carry m = -inf, weight 0
+        const float z = p.sinks[h];
+        float M = z;
+#pragma unroll
+        for (int i = 0; i < AT_COMB_WAVES; i++) M = fmaxf(M, red[i][0]);
         float Ls = __expf(z - M);
         float2 o = make_float2(0.f, 0.f);
 #pragma unroll
         for (int i = 0; i < AT_COMB_WAVES; i++) {
-            Ls += red[i][1];
-            o.x += ov[i][lane].x;
-            o.y += ov[i][lane].y;
+            const float e = __expf(red[i][0] - M);
+            Ls += e * red[i][1];
+            o.x += e * ov[i][lane].x;
+            o.y += e * ov[i][lane].y;
         }
         const float inv = 1.0f / Ls;
         reinterpret_cast<float2 *>(p.out + ((size_t)b * p.Hq + h) * AT_D)[lane] = make_float2(o.x * inv, o.y * inv);
