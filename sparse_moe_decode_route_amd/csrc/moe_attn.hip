@@ -19,10 +19,11 @@
 //                  registers (the 64 rotary angles reduced in fp64, since
 //                  P * freq needs more than fp32 at long positions); scores
 //                  to LDS, the chunk's max and exp-sum per head, then the
-//                  values weighted by the exponentials.  8 lanes per position
-//                  (16 dimensions each, two 16-byte loads of a 256-byte row),
-//                  8 positions per wave instruction, two load groups of 32
-//                  positions in flight;
+//                  values weighted by the exponentials.  8 lanes per position,
+//                  lane s holding dimensions 8 s .. + 7 and 64 + 8 s .. + 7
+//                  (two 16-byte loads, 128 contiguous bytes per 8 lanes; both
+//                  members of every rotary pair in one lane), 8 positions per
+//                  wave instruction, two load groups of 32 positions in flight;
 //   attn_chunk_mf  matrix-core path (full layers, groups of 8): scores and
 //                  the value sums on v_mfma_f32_16x16x32_bf16 in one pass
 //                  with a running softmax (details at the kernel);
@@ -99,11 +100,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)to_bf16_rne(lo) | ((uint32_t)to_bf16_rne(hi) << 16);
 }
 
-// This lane's 16 values (dimensions 16 sub .. 16 sub + 15) of one head:
-// RMSNorm over the head's 128 values (the 8 lanes of a position hold them),
-// gain, and the rotary turn of the pairs (i, i + 64) with cos / sin from cs;
-// the partner of a lane's values sits in lane ^ 4.
-__device__ __forceinline__ void head_prep(float (&x)[16], const float *gain, const float (*cs)[64], bool rope,
+// This lane's 16 values of one head: RMSNorm over the head's 128 values (the
+// 8 lanes of a position hold them), gain (this lane's 16 gain values in gv),
+// and the rotary turn of the pairs (i, i + 64) with cos / sin from cs.  The
+// turn needs the split layout (x[d] = dimension 8 sub + d, x[8 + d] =
+// dimension 64 + 8 sub + d), which keeps both members of a pair in the lane.
+__device__ __forceinline__ void head_prep(float (&x)[16], const float (&gv)[16], const float (*cs)[64], bool rope,
                                           float eps, int lane) {
     const int sub = lane & 7;
     float ss = 0.f;
@@ -114,15 +116,18 @@ __device__ __forceinline__ void head_prep(float (&x)[16], const float *gain, con
     ss += at_xor(ss, 2);
     const float inv = 1.0f / sqrtf(ss / (float)AT_D + eps);
 #pragma unroll
-    for (int d = 0; d < 16; d++) x[d] = x[d] * inv * gain[16 * sub + d];
+    for (int d = 0; d < 16; d++) x[d] = x[d] * inv * gv[d];
     if (rope) {
-        const bool high = sub >= 4;
-        const int i0 = 16 * (sub & 3);
+        const float4 *c4 = reinterpret_cast<const float4 *>(&cs[0][8 * sub]);
+        const float4 *s4 = reinterpret_cast<const float4 *>(&cs[1][8 * sub]);
+        const float4 ca = c4[0], cb = c4[1], sa = s4[0], sb = s4[1];
+        const float c[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+        const float sn[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
-        for (int d = 0; d < 16; d++) {
-            const float y = at_xor(x[d], 2);  // the partner value
-            const float c = cs[0][i0 + d], s = cs[1][i0 + d];
-            x[d] = high ? y * s + x[d] * c : x[d] * c - y * s;
+        for (int d = 0; d < 8; d++) {
+            const float lo = x[d], hi = x[8 + d];
+            x[d] = lo * c[d] - hi * sn[d];
+            x[8 + d] = hi * c[d] + lo * sn[d];
         }
     }
 }
@@ -159,13 +164,13 @@ __device__ __forceinline__ float tile_scores(const float (&qv)[HW][16], const ui
     return s;
 }
 
-// This lane's 16 values (dimensions 16 sub .. 16 sub + 15) of a 128-value
-// fp32 row.
-__device__ __forceinline__ void load16(const float *row, int sub, float (&x)[16]) {
-    const float4 *s = reinterpret_cast<const float4 *>(row + 16 * sub);
+// This lane's 16 values of a 128-value fp32 row: dimensions 16 sub ..
+// 16 sub + 15, or with split dimensions 8 sub .. + 7 then 64 + 8 sub .. + 7.
+__device__ __forceinline__ void load16(const float *row, int sub, float (&x)[16], bool split = false) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const float4 f = s[i];
+        const int o = split ? (i < 2 ? 8 * sub + 4 * i : 64 + 8 * sub + 4 * (i - 2)) : 16 * sub + 4 * i;
+        const float4 f = *reinterpret_cast<const float4 *>(row + o);
         x[4 * i] = f.x;
         x[4 * i + 1] = f.y;
         x[4 * i + 2] = f.z;
@@ -182,34 +187,49 @@ __device__ __forceinline__ uint4 pack8(const float (&x)[16], int o) {
 // scaled by 1/sqrt(128).  Every lane of the wave takes part.
 __device__ __forceinline__ void query16(const AttnArgs &p, int b, int h, const float (*cs)[64], bool rope, int lane,
                                         float (&x)[16]) {
+    float gv[16];
     load16(p.q + ((size_t)b * p.Hq + h) * AT_D, lane & 7, x);
-    head_prep(x, p.q_norm_w, cs, rope, p.eps, lane);
+    load16(p.q_norm_w, lane & 7, gv);
+    head_prep(x, gv, cs, rope, p.eps, lane);
 #pragma unroll
     for (int d = 0; d < 16; d++) x[d] *= 0.08838834764831845f;  // 1 / sqrt(128)
 }
 
 // The new token's key (normalised, rotated) and value for key/value head g
-// in bf16, this lane's 16 dimensions as two 16-byte chunks each; lanes with
-// write set store them to cache row P.  Every lane of the wave takes part.
-__device__ __forceinline__ void new_token(const AttnArgs &p, int b, int g, int P, const float (*cs)[64], bool rope,
-                                          int lane, bool write, uint4 &k0, uint4 &k1, uint4 &v0, uint4 &v1) {
+// in bf16 from the raw values in r, this lane's 16 dimensions (layout as
+// load16 with split) as two 16-byte chunks each; lanes with write set store
+// them to cache row P.  Every lane of the wave takes part.
+// raw new key, value and key-norm gains of key/value head g, this lane's 16
+// dimensions
+struct NewRaw {
+    float k[16], v[16], gk[16];
+};
+__device__ __forceinline__ void new_token_load(const AttnArgs &p, int b, int g, int lane, NewRaw &r, bool split) {
     const int sub = lane & 7;
-    float kx[16], vx[16];
-    load16(p.k_new + ((size_t)b * p.Hkv + g) * AT_D, sub, kx);
-    load16(p.v_new + ((size_t)b * p.Hkv + g) * AT_D, sub, vx);
-    head_prep(kx, p.k_norm_w, cs, rope, p.eps, lane);
+    load16(p.k_new + ((size_t)b * p.Hkv + g) * AT_D, sub, r.k, split);
+    load16(p.v_new + ((size_t)b * p.Hkv + g) * AT_D, sub, r.v, split);
+    load16(p.k_norm_w, sub, r.gk, split);
+}
+__device__ __forceinline__ void new_token(const AttnArgs &p, int b, int g, int P, const float (*cs)[64], bool rope,
+                                          int lane, bool write, NewRaw &r, bool split, uint4 &k0, uint4 &k1,
+                                          uint4 &v0, uint4 &v1) {
+    const int sub = lane & 7;
+    float(&kx)[16] = r.k;
+    const float(&vx)[16] = r.v;
+    head_prep(kx, r.gk, cs, rope, p.eps, lane);
     k0 = pack8(kx, 0);
     k1 = pack8(kx, 8);
     v0 = pack8(vx, 0);
     v1 = pack8(vx, 8);
     if (write) {
         const size_t row = (((size_t)b * p.Hkv + g) * p.max_len + P) * AT_D;
-        uint4 *kd = reinterpret_cast<uint4 *>(p.k_cache + row) + 2 * sub;
-        uint4 *vd = reinterpret_cast<uint4 *>(p.v_cache + row) + 2 * sub;
-        kd[0] = k0;
-        kd[1] = k1;
-        vd[0] = v0;
-        vd[1] = v1;
+        uint4 *kd = reinterpret_cast<uint4 *>(p.k_cache + row);
+        uint4 *vd = reinterpret_cast<uint4 *>(p.v_cache + row);
+        const int c0 = split ? sub : 2 * sub, c1 = split ? 8 + sub : 2 * sub + 1;  // 16-byte chunks
+        kd[c0] = k0;
+        kd[c1] = k1;
+        vd[c0] = v0;
+        vd[c1] = v1;
     }
 }
 
@@ -232,8 +252,9 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
     if (start >= end) return;
     const int h0 = g * (HW * WV) + w * HW;
     const size_t base = ((size_t)b * p.Hkv + g) * p.max_len;
-    const uint4 *K = reinterpret_cast<const uint4 *>(p.k_cache + base * AT_D) + 2 * sub;
-    const uint4 *V = reinterpret_cast<const uint4 *>(p.v_cache + base * AT_D) + 2 * sub;
+    // split layout: a lane reads 16-byte chunks sub and 8 + sub of a row
+    const uint4 *K = reinterpret_cast<const uint4 *>(p.k_cache + base * AT_D) + sub;
+    const uint4 *V = reinterpret_cast<const uint4 *>(p.v_cache + base * AT_D) + sub;
     const int n = end - start;
     const int ngrp = (n + 8 * AT_UT - 1) / (8 * AT_UT);  // load groups of AT_UT tiles
     // rows of group gi into (x, y); rows past the chunk's end re-read its last row
@@ -242,7 +263,7 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
         for (int u = 0; u < AT_UT; u++) {
             const int j = start + min((gi * AT_UT + u) * 8 + pg, n - 1);
             x[u] = ld_stream16(M + (size_t)j * 16);
-            y[u] = ld_stream16(M + (size_t)j * 16 + 1);
+            y[u] = ld_stream16(M + (size_t)j * 16 + 8);
         }
     };
     // the first groups of keys and values are requested before anything else
@@ -250,16 +271,27 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
     issue(K, xa, ya, 0);
     issue(V, va, vb, 0);
 
+    // then this wave's raw query heads, their gains, the new key and value
+    // (the chunk holding P) and the rotary frequencies: all requested before
+    // the rotary table is built
+    const bool rope = p.window > 0;
+    const double fr = rope && threadIdx.x < 64 ? p.rope_freq[threadIdx.x] : 0.0;
+    float qv[HW][16], gq[16];
+#pragma unroll
+    for (int h = 0; h < HW; h++) load16(p.q + ((size_t)b * p.Hq + h0 + h) * AT_D, sub, qv[h], true);
+    load16(p.q_norm_w, sub, gq, true);
+    const bool hasP = end == P + 1;
+    NewRaw nr;
+    if (hasP) new_token_load(p, b, g, lane, nr, true);
     // cos / sin of the 64 rotary angles P * freq_i: the product and its
     // reduction modulo 2 pi in fp64 (P * freq needs more than fp32 at long
     // positions), the reduced angle's sine and cosine in fp32
-    __shared__ float cs[2][64];
-    const bool rope = p.window > 0;
+    __shared__ __align__(16) float cs[2][64];  // read as float4
     if (rope) {
         if (threadIdx.x < 64) {
-            const double two_pi = 6.283185307179586476925286766559;
-            double ang = (double)P * p.rope_freq[threadIdx.x];
-            ang -= two_pi * floor(ang / two_pi);
+            const double two_pi = 6.283185307179586476925286766559, inv_two_pi = 0.15915494309189533576888376337251;
+            double ang = (double)P * fr;
+            ang -= two_pi * floor(ang * inv_two_pi);  // within rounding of [0, 2 pi)
             float sf, cf;
             sincosf((float)ang, &sf, &cf);
             cs[0][threadIdx.x] = cf;
@@ -267,15 +299,17 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
         }
         __syncthreads();
     }
-    // this wave's query heads
-    float qv[HW][16];
+    // this wave's query heads: normalised, rotated, scaled by 1/sqrt(128)
 #pragma unroll
-    for (int h = 0; h < HW; h++) query16(p, b, h0 + h, cs, rope, lane, qv[h]);
+    for (int h = 0; h < HW; h++) {
+        head_prep(qv[h], gq, cs, rope, p.eps, lane);
+#pragma unroll
+        for (int d = 0; d < 16; d++) qv[h][d] *= 0.08838834764831845f;  // 1 / sqrt(128)
+    }
     // the chunk holding P: the new key and value used in place of the cache
     // row P, which this block also writes
-    const bool hasP = end == P + 1;
     uint4 kn0 = make_uint4(0, 0, 0, 0), kn1 = kn0, vn0 = kn0, vn1 = kn0;
-    if (hasP) new_token(p, b, g, P, cs, rope, lane, w == 0 && pg == 0, kn0, kn1, vn0, vn1);
+    if (hasP) new_token(p, b, g, P, cs, rope, lane, w == 0 && pg == 0, nr, true, kn0, kn1, vn0, vn1);
     // row P of the first groups is the new key / value
 #pragma unroll
     for (int u = 0; u < AT_UT; u++) {
@@ -385,9 +419,13 @@ __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
     if (pg == 0) {
 #pragma unroll
         for (int h = 0; h < HW; h++) {
-            float4 *dst = reinterpret_cast<float4 *>(p.part_o + (((size_t)b * p.Hq + h0 + h) * NC + cl) * AT_D + 16 * sub);
+            float *dst = p.part_o + (((size_t)b * p.Hq + h0 + h) * NC + cl) * AT_D;
 #pragma unroll
-            for (int i = 0; i < 4; i++) dst[i] = make_float4(o[h][4 * i], o[h][4 * i + 1], o[h][4 * i + 2], o[h][4 * i + 3]);
+            for (int i = 0; i < 4; i++) {
+                const int o0 = i < 2 ? 8 * sub + 4 * i : 64 + 8 * sub + 4 * (i - 2);
+                *reinterpret_cast<float4 *>(dst + o0) =
+                    make_float4(o[h][4 * i], o[h][4 * i + 1], o[h][4 * i + 2], o[h][4 * i + 3]);
+            }
         }
     }
     if (lane < HW) {
@@ -500,7 +538,9 @@ __global__ void __launch_bounds__(128) attn_chunk_mf(AttnArgs p) {
     }
     if (end == P + 1) {
         uint4 nk0, nk1, nv0, nv1;
-        new_token(p, b, g, P, nullptr, false, lane, w == 0 && lane < 8, nk0, nk1, nv0, nv1);
+        NewRaw nr;
+        new_token_load(p, b, g, lane, nr, false);
+        new_token(p, b, g, P, nullptr, false, lane, w == 0 && lane < 8, nr, false, nk0, nk1, nv0, nv1);
         if (w == 0 && lane < 8) {
             knsh[2 * sub] = nk0;
             knsh[2 * sub + 1] = nk1;
