@@ -107,17 +107,17 @@ ATTN_SOURCES = ("moe_attn.hip", "moe_device.h", "moe_internal.h")
 _FETCH_SCALE = 262144.0 / 131085.2  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
 _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE KiB
 COUNTER_TRAFFIC = {
-    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="3c400d9417aae1b3",
+    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="caa2734f20dd3afc",
                                               fetch_bytes=round(3939.4 * _FETCH_SCALE * 1024),
                                               write_bytes=round(12.7 * _WRITE_SCALE * 1024)),
-    ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="c0646f2761c21c42",
-                                             fetch_bytes=round(227273.3 * _FETCH_SCALE * 1024),
-                                             write_bytes=round(28692.8 * _WRITE_SCALE * 1024)),
-    ("lm_head_q4_1_t1", "lm_head_kernel"): dict(source_digest="a0621f359d9319a6",
-                                                fetch_bytes=round(91654.3 * _FETCH_SCALE * 1024),
+    ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="9bc236c0b4662e31",
+                                             fetch_bytes=round(227174.8 * _FETCH_SCALE * 1024),
+                                             write_bytes=round(28694.4 * _WRITE_SCALE * 1024)),
+    ("lm_head_q4_1_t1", "lm_head_kernel"): dict(source_digest="676ef36934408841",
+                                                fetch_bytes=round(91654.2 * _FETCH_SCALE * 1024),
                                                 write_bytes=round(572.2 * _WRITE_SCALE * 1024)),
-    ("attn_full128k", "attn_chunk"): dict(source_digest="eb0a2c2c80f6cac5",
-                                          fetch_bytes=round(131342.2 * _FETCH_SCALE * 1024),
+    ("attn_full128k", "attn_chunk"): dict(source_digest="1a58abd52ba8cb8a",
+                                          fetch_bytes=round(131346.6 * _FETCH_SCALE * 1024),
                                           write_bytes=round(2306.0 * _WRITE_SCALE * 1024)),
 }
 
