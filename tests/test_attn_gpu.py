@@ -99,6 +99,14 @@ def test_attn_full_long_ragged_chunk():
     _run(32, 4, 0, 131072, [100003], cfg_id=79, label="full long ragged")
 
 
+def test_attn_full_groups_of_8_batch():
+    # matrix-core path with 2 key/value heads and 4 sequences: 512-position
+    # chunks here; P = 1023 ends a full chunk, 1024 starts one (1 position),
+    # 5000 leaves 393 (ragged), 19999 exactly one 32-position tile
+    _run(16, 2, 0, 20000, [19999, 5000, 1023, 1024], cfg_id=80, label="full groups of 8, batch 4")
+    assert B.attn_chunk_plan(B.attn_dims(16, 2, 0), 4, 20000) == (512, 40)
+
+
 def test_attn_invalid_position_gives_nan_and_keeps_caches():
     a = gen.make_attn(2, 32, 4, 128, 64, cfg_id=77)
     d = gen.AttnInputs(*(t.to(_dev()) for t in (a.q, a.k_new, a.v_new, a.q_norm_w, a.k_norm_w, a.sinks,
