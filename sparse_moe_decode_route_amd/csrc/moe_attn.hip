@@ -481,6 +481,9 @@ typedef float at_f32x4 __attribute__((ext_vector_type(4)));
 //           fall in distinct banks.
 // Output rows: head h's high row h (lanes l / 16 = h / 4) plus its low row
 // h + 8 (lanes l / 16 = 2 + h / 4), one exchange between lanes l and l ^ 32.
+// Registers: keys two tiles ahead, values one, the output in 32 accumulators:
+// one wave per SIMD without spills (a cap at two spills to scratch and runs
+// slower), so the chunk plan keeps a call near 512 blocks, two per CU.
 __global__ void __launch_bounds__(128) attn_chunk_mf(AttnArgs p) {
     __shared__ uint4 vst[2][32 * 16];  // per wave: one tile of 32 value rows
     __shared__ float qsh[8][AT_D];
