@@ -116,8 +116,8 @@ COUNTER_TRAFFIC = {
     ("lm_head_q4_1_t1", "lm_head_kernel"): dict(source_digest="676ef36934408841",
                                                 fetch_bytes=round(91654.2 * _FETCH_SCALE * 1024),
                                                 write_bytes=round(572.2 * _WRITE_SCALE * 1024)),
-    ("attn_full128k", "attn_chunk"): dict(source_digest="0b17e5631280f524",
-                                          fetch_bytes=round(131346.6 * _FETCH_SCALE * 1024),
+    ("attn_full128k", "attn_chunk"): dict(source_digest="6e7dd54d40665ef8",
+                                          fetch_bytes=round(131357.2 * _FETCH_SCALE * 1024),
                                           write_bytes=round(2306.0 * _WRITE_SCALE * 1024)),
 }
 

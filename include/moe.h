@@ -298,8 +298,9 @@ moe_status moe_attn_workspace_size(const moe_attn_dims *dims, int32_t n_seqs, in
 /* (host) the chunk plan moe_attn_decode uses for these sizes: *chunk
    positions per block of the first kernel, and *slots chunk partials per
    (sequence, query head) in the workspace (the combine kernel merges the
-   slots a position range touches).  Sliding windows take 32-position
-   chunks; full layers the smallest power of two in [64, 1024] that keeps a
+   slots a position range touches).  Sliding windows take 64-position
+   chunks with groups of 8 query heads (the matrix-core kernel) and 32
+   otherwise; full layers the smallest power of two in [64, 1024] that keeps a
    call near 512 blocks with groups of 8 query heads (the matrix-core
    kernel) and near 1024 blocks otherwise.  Same argument checks as
    moe_attn_workspace_size. */

@@ -14,7 +14,7 @@
 // Two kernels, one block per (sequence, key/value head, chunk of positions)
 // in the first, each writing the chunk's partial (max, exp-sum, output) per
 // query head to the workspace:
-//   attn_chunk     vector path (sliding windows, and groups of 1, 2 or 4):
+//   attn_chunk     vector path (groups of 1, 2 or 4 query heads per key/value head):
 //                  the group's query heads normalised and rotated in
 //                  registers (the 64 rotary angles reduced in fp64, since
 //                  P * freq needs more than fp32 at long positions); scores
@@ -24,17 +24,18 @@
 //                  (two 16-byte loads, 128 contiguous bytes per 8 lanes; both
 //                  members of every rotary pair in one lane), 8 positions per
 //                  wave instruction, two load groups of 32 positions in flight;
-//   attn_chunk_mf  matrix-core path (full layers, groups of 8): scores and
-//                  the value sums on v_mfma_f32_16x16x32_bf16 in one pass
-//                  with a running softmax (details at the kernel);
+//   attn_chunk_mf  matrix-core path (groups of 8, full and sliding-window
+//                  layers): scores and the value sums on
+//                  v_mfma_f32_16x16x32_bf16 in one pass with a running
+//                  softmax (details at the kernel);
 //   attn_combine   per (sequence, query head): the chunks merged with the
 //                  sink in a fixed order: out = sum_c e^(m_c - M) o_c /
 //                  (e^(z - M) + sum_c e^(m_c - M) l_c), M = max(z, max_c m_c).
 // The block whose chunk holds P computes the new key (normalised, rotated)
 // and value in bf16, uses them for row P and writes them to the caches; no
-// other block reads row P.  Chunks are 32 positions in sliding-window layers
-// (a window spreads over 17-18 blocks per key/value head) and up to 1024 in
-// full layers (about 512 blocks per call at the cache's length on the
+// other block reads row P.  Chunks are 64 positions in sliding-window layers
+// on the matrix-core path (32 on the vector path) and up to 1024 in full
+// layers (about 512 blocks per call at the cache's length on the
 // matrix-core path, 1024 on the vector path).  The cache
 // is the stream: a full layer at long context reads 512 bytes per position
 // per key/value head (K and V), so the chunk kernels are bound by HBM.
@@ -183,22 +184,6 @@ __device__ __forceinline__ uint4 pack8(const float (&x)[16], int o) {
                       pack_bf16x2(x[o + 6], x[o + 7]));
 }
 
-// Query head h of sequence b, this lane's 16 values: normalised, rotated,
-// scaled by 1/sqrt(128).  Every lane of the wave takes part.
-__device__ __forceinline__ void query16(const AttnArgs &p, int b, int h, const float (*cs)[64], bool rope, int lane,
-                                        float (&x)[16]) {
-    float gv[16];
-    load16(p.q + ((size_t)b * p.Hq + h) * AT_D, lane & 7, x);
-    load16(p.q_norm_w, lane & 7, gv);
-    head_prep(x, gv, cs, rope, p.eps, lane);
-#pragma unroll
-    for (int d = 0; d < 16; d++) x[d] *= 0.08838834764831845f;  // 1 / sqrt(128)
-}
-
-// The new token's key (normalised, rotated) and value for key/value head g
-// in bf16 from the raw values in r, this lane's 16 dimensions (layout as
-// load16 with split) as two 16-byte chunks each; lanes with write set store
-// them to cache row P.  Every lane of the wave takes part.
 // raw new key, value and key-norm gains of key/value head g, this lane's 16
 // dimensions
 struct NewRaw {
@@ -233,7 +218,7 @@ __device__ __forceinline__ void new_token(const AttnArgs &p, int b, int g, int P
     }
 }
 
-// Vector path (sliding windows; groups of 1, 2 and 4; 8 in windows): HW
+// Vector path (groups of 1, 2 and 4 query heads per key/value head): HW
 // query heads per wave, WV waves per block (HW * WV = group size).
 template <int HW, int WV>
 __global__ void __launch_bounds__(64 * WV) attn_chunk(AttnArgs p) {
@@ -452,9 +437,10 @@ typedef short at_s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) at_s16x4 lds_s16x4;
 typedef float at_f32x4 __attribute__((ext_vector_type(4)));
 
-// Matrix-core path: full layers (no rotary embedding) with 8 query heads
-// per key/value head; the same partials as attn_chunk, in one pass over the
-// chunk with a running (online) softmax.  Two waves; wave w takes the
+// Matrix-core path: 8 query heads per key/value head, full and sliding-window
+// layers (queries and the new key rotated on the split lane layout); the same
+// partials as attn_chunk, in one pass over the chunk with a running (online)
+// softmax.  Two waves; wave w takes the
 // 32-position tiles w, w + 2, ... for all 8 heads and keeps its own running
 // max, sum and output; the two are merged at the end in wave order.
 // v_mfma_f32_16x16x32_bf16 throughout (lane l holds A[l % 16][8 (l / 16) + e],
@@ -495,7 +481,9 @@ __global__ void __launch_bounds__(128) attn_chunk_mf(AttnArgs p) {
     const int b = blockIdx.z, g = blockIdx.y;
     const int P = p.pos[b];
     if (P < 0 || P >= p.max_len) return;
-    const int start = blockIdx.x * p.chunk, end = min(start + p.chunk, P + 1);  // [start, end)
+    const int lo = attn_lo(p, P);
+    const int c0 = (attn_first_chunk(p, P) + blockIdx.x) * p.chunk;
+    const int start = max(c0, lo), end = min(c0 + p.chunk, P + 1);  // [start, end)
     if (start >= end) return;
     const int n = end - start, nt = (n + 31) / 32;
     const size_t base = ((size_t)b * p.Hkv + g) * p.max_len;
@@ -528,27 +516,50 @@ __global__ void __launch_bounds__(128) attn_chunk_mf(AttnArgs p) {
         issue_k(k0, w);
         issue_v(v0, w);
     }
-    // the 8 prepared queries (wave w: heads 4 w .. 4 w + 3) and the new key
-    // and value through LDS
+    // this wave's raw query heads (4 w .. 4 w + 3), their gains, the new key
+    // and value (the chunk holding P) and the rotary frequencies, all requested
+    // before the rotary table is built (split layout: lane s holds dimensions
+    // 8 s .. + 7 and 64 + 8 s .. + 7)
+    const bool rope = p.window > 0;
+    const double fr = rope && threadIdx.x < 64 ? p.rope_freq[threadIdx.x] : 0.0;
+    float qx[4][16], gq[16];
+#pragma unroll
+    for (int h = 0; h < 4; h++) load16(p.q + ((size_t)b * p.Hq + g * 8 + 4 * w + h) * AT_D, sub, qx[h], true);
+    load16(p.q_norm_w, sub, gq, true);
+    const bool hasP = end == P + 1;
+    NewRaw nr;
+    if (hasP) new_token_load(p, b, g, lane, nr, true);
+    __shared__ __align__(16) float cs[2][64];  // read as float4
+    if (rope) {
+        if (threadIdx.x < 64) {
+            const double two_pi = 6.283185307179586476925286766559, inv_two_pi = 0.15915494309189533576888376337251;
+            double ang = (double)P * fr;
+            ang -= two_pi * floor(ang * inv_two_pi);  // within rounding of [0, 2 pi)
+            float sf, cf;
+            sincosf((float)ang, &sf, &cf);
+            cs[0][threadIdx.x] = cf;
+            cs[1][threadIdx.x] = sf;
+        }
+        __syncthreads();
+    }
+    // the 8 prepared queries and the new key and value through LDS
 #pragma unroll
     for (int h = 0; h < 4; h++) {
-        float x[16];
-        query16(p, b, g * 8 + 4 * w + h, nullptr, false, lane, x);
+        head_prep(qx[h], gq, cs, rope, p.eps, lane);
         if (lane < 8) {
 #pragma unroll
-            for (int d = 0; d < 16; d++) qsh[4 * w + h][16 * sub + d] = x[d];
+            for (int d = 0; d < 16; d++)
+                qsh[4 * w + h][d < 8 ? 8 * sub + d : 56 + 8 * sub + d] = qx[h][d] * 0.08838834764831845f;  // 1/sqrt(128)
         }
     }
-    if (end == P + 1) {
+    if (hasP) {
         uint4 nk0, nk1, nv0, nv1;
-        NewRaw nr;
-        new_token_load(p, b, g, lane, nr, false);
-        new_token(p, b, g, P, nullptr, false, lane, w == 0 && lane < 8, nr, false, nk0, nk1, nv0, nv1);
+        new_token(p, b, g, P, cs, rope, lane, w == 0 && lane < 8, nr, true, nk0, nk1, nv0, nv1);
         if (w == 0 && lane < 8) {
-            knsh[2 * sub] = nk0;
-            knsh[2 * sub + 1] = nk1;
-            vnsh[2 * sub] = nv0;
-            vnsh[2 * sub + 1] = nv1;
+            knsh[sub] = nk0;
+            knsh[8 + sub] = nk1;
+            vnsh[sub] = nv0;
+            vnsh[8 + sub] = nv1;
         }
     }
     __syncthreads();
@@ -807,21 +818,22 @@ void launch_chunks(const AttnArgs &p, hipStream_t st) {
 
 }  // namespace
 
-// Chunk size: 32 positions for a sliding window (its 513 positions then
-// spread over 17-18 blocks per key/value head, each with one load group of
-// keys and one of values in flight).  Full attention: the smallest power of
+// Chunk size: a sliding window takes 64 positions on the matrix-core path
+// (one tile per wave; 513 positions spread over 9-10 blocks per key/value
+// head; measured 11.7 us per layer against 11.6 for 32 and 13.5 for 128) and
+// 32 on the vector path (one load group of keys and one of values in flight).  Full attention: the smallest power of
 // two in [64, 1024] that keeps the blocks of a call at the cache's full
 // length to about 512 on the matrix-core path (one wave per SIMD, two blocks
 // per CU: every block resident at once) and about 1024 on the vector path.
 int attn_chunk_size(int window, int max_len, int B, int Hq, int Hkv) {
-    if (window > 0) return 32;
+    if (window > 0) return attn_uses_mfma(window, Hq, Hkv) ? 64 : 32;
     const long long target = attn_uses_mfma(window, Hq, Hkv) ? 512 : 1024;
     int c = 64;
     while (c < AT_CMAX && (long long)((max_len + c - 1) / c) * B * Hkv > target) c *= 2;
     return c;
 }
 
-bool attn_uses_mfma(int window, int Hq, int Hkv) { return window == 0 && Hq == 8 * Hkv; }
+bool attn_uses_mfma(int window, int Hq, int Hkv) { return Hq == 8 * Hkv; }
 
 int attn_chunk_slots(int window, int max_len, int chunk) {
     // a window of W positions spans at most ceil((W - 1) / chunk) + 1 chunks
@@ -833,9 +845,8 @@ int attn_chunk_slots(int window, int max_len, int chunk) {
 hipError_t launch_attn(const AttnArgs &a, hipStream_t st) {
     AttnArgs p = a;
     const int grp = p.Hq / p.Hkv;
-    // full layers with groups of 8 on the matrix cores (measured at 128k:
-    // 84.4 us on the vector path, 46.9 us here); a window's 32-position
-    // chunks are faster on the vector path without the LDS staging
+    // groups of 8 on the matrix cores (measured at 128k: 84.4 us on the
+    // vector path, 46.9 us here; windows of 513: 12.2 against 11.7 us)
     if (attn_uses_mfma(p.window, p.Hq, p.Hkv))
         launch_grid(attn_chunk_mf, 128, p, st);
     else if (grp == 8)

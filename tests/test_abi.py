@@ -181,11 +181,12 @@ def test_attn_checks(L):
 
 
 def test_attn_chunk_plan(L):
-    """Chunk plan: 32-position chunks for windows; for full layers the smallest
+    """Chunk plan: windows in 64-position chunks for groups of 8 (matrix-core
+    kernel), 32 otherwise; for full layers the smallest
     power of two in [64, 1024] keeping a call near 512 blocks for groups of 8
     (matrix-core kernel), near 1024 otherwise; the workspace
     holds one (max, sum, 128-value) partial per slot and query head."""
-    cases = (((32, 4, 513), 1, 8192, 32, 17), ((32, 4, 513), 1, 100, 32, 4), ((32, 4, 0), 1, 131072, 1024, 128),
+    cases = (((32, 4, 513), 1, 8192, 64, 9), ((32, 4, 513), 1, 100, 64, 2), ((16, 4, 513), 1, 8192, 32, 17), ((32, 4, 0), 1, 131072, 1024, 128),
              ((32, 4, 0), 1, 8192, 64, 128), ((32, 4, 0), 8, 131072, 1024, 128), ((32, 4, 0), 1, 1, 64, 1),
              ((16, 4, 0), 1, 131072, 512, 256), ((16, 4, 0), 1, 16384, 64, 256), ((32, 4, 0), 1, 16384, 128, 128))
     for (hq, hkv, win), nseq, ml, chunk, slots in cases:
