@@ -257,15 +257,27 @@ __device__ __forceinline__ void bn_gateup_finish(const DecodeParams &p, const WU
             }
         }
     }
+    // all RG x tokens x (gate, up) sums in one halving reduction: value
+    // k = (RG * NT) * (0 gate, 1 up) + NT * r + j ends in lanes l % PV == k,
+    // so lane NT * r + j holds the gate sum and its up sum sits PV / 2 lanes on
+    constexpr int NT = TWO ? 2 : 1, PV = 2 * RG * NT;
+    static_assert(PV == 4 || PV == 8 || PV == 16, "one exchange pairs the gate and up sums");
+    float v[PV];
 #pragma unroll
-    for (int r = 0; r < RG; r++) {
+    for (int r = 0; r < RG; r++)
 #pragma unroll
-        for (int j = 0; j < (TWO ? 2 : 1); j++) {
-            const float gs = wave_sum(ag[r][j]) * inv[j];
-            const float us = wave_sum(au[r][j]) * inv[j];
-            const int t = j == 0 ? ta : tb;
-            if (lane == 2 * r + j) p.h[((size_t)slot * p.T + t) * p.F + f0 + r] = silu_mul(gs, us);
+        for (int j = 0; j < NT; j++) {
+            v[NT * r + j] = ag[r][j];
+            v[RG * NT + NT * r + j] = au[r][j];
         }
+    const float red = wave_reduce_rows<PV>(v, lane);
+    const float up = xor_lane(red, PV == 16 ? 3 : PV == 8 ? 2 : 1);  // lane ^ (PV / 2)
+    const int k = lane % PV;
+    if (k < RG * NT) {
+        const int r = k / NT, j = k % NT;
+        const float sc = j == 0 ? inv[0] : inv[1];
+        const int t = j == 0 ? ta : tb;
+        if (lane == k) p.h[((size_t)slot * p.T + t) * p.F + f0 + r] = silu_mul(red * sc, up * sc);
     }
 }
 
