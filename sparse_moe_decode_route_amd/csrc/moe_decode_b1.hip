@@ -75,12 +75,19 @@ __device__ __forceinline__ void gateup_finish(const GateUp<FMT, UPLD, RG> &g, co
             au[r] += unit_dot<FMT>(g.wu[r][i], xv[i], g.tsu);
         }
     }
+    // the RG gate and RG up sums in one halving reduction: value k (gate r at
+    // k = r, up r at k = RG + r) ends in lanes l % (2 RG) == k, so lane r holds
+    // gate r and its up sum sits RG lanes on
+    static_assert(RG == 1 || RG == 2 || RG == 4, "one exchange pairs the gate and up sums");
+    float v[2 * RG];
 #pragma unroll
     for (int r = 0; r < RG; r++) {
-        const float gs = wave_sum(ag[r]);
-        const float us = wave_sum(au[r]);
-        if (lane == r) p.h[(size_t)slot * p.F + f0 + r] = silu_mul(gs, us);
+        v[r] = ag[r];
+        v[RG + r] = au[r];
     }
+    const float red = wave_reduce_rows<2 * RG>(v, lane);
+    const float up = xor_lane(red, RG == 4 ? 2 : RG == 2 ? 1 : 0);  // lane ^ RG
+    if (lane < RG) p.h[(size_t)slot * p.F + f0 + lane] = silu_mul(red, up);
 }
 
 // ---------------------------------------------------------------------------
