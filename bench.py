@@ -107,8 +107,8 @@ ATTN_SOURCES = ("moe_attn.hip", "moe_device.h", "moe_internal.h")
 _FETCH_SCALE = 262144.0 / 131085.2  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
 _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE KiB
 COUNTER_TRAFFIC = {
-    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="caa2734f20dd3afc",
-                                              fetch_bytes=round(3939.4 * _FETCH_SCALE * 1024),
+    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="a6637c8f6f343668",
+                                              fetch_bytes=round(3936.8 * _FETCH_SCALE * 1024),
                                               write_bytes=round(12.7 * _WRITE_SCALE * 1024)),
     ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="9bc236c0b4662e31",
                                              fetch_bytes=round(227174.8 * _FETCH_SCALE * 1024),
