@@ -88,6 +88,12 @@ def test_attn_long_positions_rotary_accuracy():
     _run(32, 4, 513, 131072, [131071, 100003], cfg_id=75, label="long swa")
 
 
+def test_attn_long_positions_rotary_vector_path():
+    # groups of 4 query heads run the vector kernel (groups of 8 the
+    # matrix-core one): its rotation on the split lane layout near 2^17
+    _run(16, 4, 513, 131072, [131071, 99999], cfg_id=81, label="long swa, groups of 4")
+
+
 def test_attn_full_128k_context():
     _run(32, 4, 0, 131072, [131071], cfg_id=76, label="full 128k")
 
