@@ -190,11 +190,12 @@ __global__ void __launch_bounds__(512) select_kernel(DecodeParams p) {
 #pragma unroll
             for (int t = 0; t < MAX_DECODE_T; t++) wt[t] = 0.f;
             if (e < p.E) {
+                // a repeated given index adds its slots' weights (slot order)
                 for (int t = 0; t < p.T; t++)
                     for (int i = 0; i < p.K; i++)
                         if (sel[t][i] == e) {
                             mask |= 1u << t;
-                            wt[t] = selw[t][i];
+                            wt[t] += selw[t][i];
                         }
             }
             const uint64_t bal = __ballot(mask != 0);

@@ -458,15 +458,23 @@ __global__ void __launch_bounds__(PF_THREADS) pf_scatter(PfParams p) {
     int r;
     float wt;
     if (j < p.K) {
-        const int e = p.idx[(size_t)t * p.K + j];
-        if (e < 0 || e >= p.E) {  // caller routing may hold invalid indices: no row
+        const int32_t *ti = p.idx + (size_t)t * p.K;
+        const int e = ti[j];
+        // caller routing may hold invalid indices (no row) or repeat an index:
+        // the token's first slot naming e owns the row and carries the weights
+        // of all its slots naming e, added in slot order; later ones get none
+        bool first = e >= 0 && e < p.E;
+        for (int k = 0; k < j; k++) first = first && ti[k] != e;
+        if (!first) {
             p.pos[i] = -1;
             return;
         }
         const size_t mi = (size_t)e * p.NW + (t >> 6);
         const unsigned long long below = (t & 63) ? ((1ull << (t & 63)) - 1ull) : 0ull;
         r = p.off[e] + p.wp[mi] + __popcll(p.mask[mi] & below);
-        wt = p.w[(size_t)t * p.K + j];
+        const float *tw = p.w + (size_t)t * p.K;
+        wt = tw[j];
+        for (int k = j + 1; k < p.K; k++) wt += ti[k] == e ? tw[k] : 0.f;
     } else {
         r = p.off[p.E + j - p.K] + t;
         wt = 1.f;

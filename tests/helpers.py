@@ -105,3 +105,19 @@ def lm_head_band(x: np.ndarray, w_dec: np.ndarray, block: int = 32) -> np.ndarra
     mag = a + 2.0 * np.repeat(bmax, block, axis=1)
     n = 48
     return 2.0 * n * U32 * (np.abs(x) @ mag.T)
+
+
+def check_chain_divergence(orc, layer, x_gpu_in: np.ndarray, x_orc_in: np.ndarray, band: float, top_k: int):
+    """At the first layer where a free-running oracle chain (fp64 from x_0) and
+    the GPU chain (fp32) select different experts, the difference must come
+    from the drift between their inputs to that layer: the oracle's own gap
+    between its k-th and (k+1)-th logit must lie within twice the largest
+    logit change that the drift causes, plus the fp32 band.  Returns
+    (gap, logit drift)."""
+    lg = orc.router_logits(layer, x_gpu_in)[0]
+    lo = orc.router_logits(layer, x_orc_in)[0]
+    drift = float(np.abs(lg - lo).max())
+    srt = np.sort(lo)[::-1]
+    gap = float(srt[top_k - 1] - srt[top_k])
+    assert gap <= 2.0 * drift + band, f"selection differs at a gap {gap} the input drift {drift} does not explain"
+    return gap, drift

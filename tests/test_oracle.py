@@ -613,3 +613,28 @@ def test_attn_head_norm_closed_form(orc):
     _, kc2, _ = orc.attn_decode(np.ones((1, 1, D)), np.full((1, 1, D), -3.7), np.zeros((1, 1, D)), np.ones(D), w,
                                 np.zeros(1), kc, kc.copy(), np.array([2]), window=0, eps=0.0)
     assert np.array_equal(_bf16_vals(kc2[0, 0, 2]), _bf16_vals(_bf16_bits(-w)))
+
+
+def test_attn_head_norm_epsilon_closed_form(orc):
+    # constant query c_q * 1 and key c_k * 1 with eps > 0: each normalises to
+    # c / sqrt(c^2 + eps) * w (eps inside the root, added to the mean square);
+    # at position 0 the only score is s = q . bf16(k) / sqrt(D), so the output
+    # is e^s / (e^s + e^z) * bf16(v)
+    D, eps = 16, 0.25
+    cq, ck = 0.5, -0.8
+    wq = np.linspace(0.5, 1.5, D)
+    wk = np.linspace(2.0, 1.0, D)
+    v = np.linspace(-1.0, 1.0, D)
+    z = 0.3
+    kc = np.zeros((1, 1, 4, D), dtype=np.uint16)
+    out, kc2, vc2 = orc.attn_decode(np.full((1, 1, D), cq), np.full((1, 1, D), ck), v[None, None, :], wq, wk,
+                                    np.array([z]), kc, kc.copy(), np.array([0]), window=0, eps=eps)
+    kh = ck / math.sqrt(ck * ck + eps) * wk
+    assert np.array_equal(_bf16_vals(kc2[0, 0, 0]), _bf16_vals(_bf16_bits(kh)))
+    qh = cq / math.sqrt(cq * cq + eps) * wq
+    s = float(qh @ _bf16_vals(_bf16_bits(kh))) / math.sqrt(D)
+    want = math.exp(s) / (math.exp(s) + math.exp(z)) * _bf16_vals(_bf16_bits(v))
+    assert np.allclose(out[0, 0], want, rtol=1e-13, atol=1e-15)
+    # the placements a misreading would give differ well beyond that tolerance
+    for wrong in (cq / (abs(cq) + eps), cq / math.sqrt(cq * cq) + eps):
+        assert abs(wrong - cq / math.sqrt(cq * cq + eps)) > 1e-2

@@ -50,6 +50,38 @@ def _x64(x: torch.Tensor) -> np.ndarray:
     return x.float().double().numpy()
 
 
+def _tile_boundary_rows(idx: np.ndarray, n_routed: int, n_shared: int, step: int = 64) -> np.ndarray:
+    """Tokens at the first and last row of every group of `step` rows of every
+    expert's row block (routed experts: the tokens that chose the expert, in
+    token order, as the permutation lays them out; shared experts: every
+    token), so that every grouped-GEMM tile of 64 or 128 rows, full or partial,
+    has its first and last row checked, and every expert with tokens at least
+    one row."""
+    T = idx.shape[0]
+    rows = set()
+    per_expert = [[] for _ in range(n_routed)]
+    for t in range(T):
+        for e in idx[t].tolist():
+            per_expert[e].append(t)
+    blocks = [toks for toks in per_expert if toks] + [list(range(T))] * (1 if n_shared else 0)
+    for toks in blocks:
+        for i in range(0, len(toks), step):
+            rows.add(toks[i])
+            rows.add(toks[min(i + step - 1, len(toks) - 1)])
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _oracle_rows_parallel(host, x64, idx, w, rows, workers: int = 8):
+    """oracle.experts_given over the listed rows, in chunks on host threads
+    (the oracle runs in C through ctypes, which releases the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    chunks = np.array_split(rows, max(1, min(workers, len(rows))))
+    def one(r):
+        return oracle.experts_given(host, x64[r], idx[r], w[r].astype(np.float64))
+    with ThreadPoolExecutor(max_workers=len(chunks)) as ex:
+        return np.concatenate(list(ex.map(one, chunks)))
+
+
 def _prefill_case(host, dev_layer, x: torch.Tensor, label: str, check_all_outputs=True, n_sample=0):
     dims = host.dims
     T = x.shape[0]
@@ -64,8 +96,13 @@ def _prefill_case(host, dev_layer, x: torch.Tensor, label: str, check_all_output
         oi[t], ow[t], _ = oracle.route(dims, logits[t])
     band = router_band_mfma(x64, _router64(host), x.dtype == torch.float32)
     n_exact, n_amb = check_routing(idx, w, logits, oi, ow, band)
-    rows = np.arange(T) if check_all_outputs else np.random.default_rng(0).choice(T, n_sample, replace=False)
-    oy = oracle.experts_given(host, x64[rows], idx[rows], w[rows].astype(np.float64))
+    if check_all_outputs:
+        rows = np.arange(T)
+    else:
+        # every tile's first and last row, every expert, plus a random sample
+        rnd = np.random.default_rng(0).choice(T, n_sample, replace=False)
+        rows = np.union1d(_tile_boundary_rows(idx, dims.n_routed, dims.n_shared), rnd)
+    oy = _oracle_rows_parallel(host, x64, idx, w, rows)
     err = rel_l2(y[rows], oy)
     print(f"[{label}] T={T} exact={n_exact} ambiguous={n_amb} checked rows={len(rows)} "
           f"max rel-L2 {err.max():.3e} mean {err.mean():.3e}")
@@ -113,7 +150,8 @@ def test_prefill_nvfp4_full_width():
 
 def test_prefill_4096_tokens_sampled():
     # the full prefill workload: 4096 bf16 tokens through one q4_1 layer with a
-    # Zipf(1.1) router prior; routing checked on every token, outputs on a sample
+    # Zipf(1.1) router prior; routing checked on every token, outputs on the
+    # first and last row of every tile of every expert plus a random sample
     dims = gen.WORKLOADS["c5_prefill_q4_1"]["dims"]
     host, dev = _layer(dims, cfg_id=5, zipf_s=1.1)
     idx, _ = _prefill_case(host, dev, _x(4096, dims.d_model, draw=0, bf16=True), "prefill 4096",
@@ -159,6 +197,10 @@ def test_expert_ffn_many_tokens_given_routing(wfmt):
     w = rng.random((T, 4)).astype(np.float32)
     idx[3, 1] = -1    # invalid indices select nothing
     idx[10, 0] = 16
+    idx[20, 3] = idx[20, 0]   # a repeated index contributes once per slot
+    idx[21, 2] = idx[21, 1]
+    idx[69, 1] = idx[69, 0]
+    idx[69, 3] = idx[69, 0]   # three slots naming one expert
     x = _x(T, 128, draw=9, bf16=False)
     y = B.expert_ffn_q4(dims, x.to(_dev()), dev.experts, dev.tensor_scale, torch.from_numpy(idx).to(_dev()),
                         torch.from_numpy(w).to(_dev()))
