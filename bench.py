@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--lm-cpu-seconds", type=float, default=10.0, help="minimum CPU baseline time (whole passes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=47, help="layers in the CPU baseline sample")
-    ap.add_argument("--cpu-tokens", type=int, default=8, help="tokens in the CPU baseline sample")
+    ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens in the one-thread CPU baseline sample")
+    ap.add_argument("--prefill-cpu-tokens", type=int, default=256, help="tokens in the prefill CPU baseline sample")
     ap.add_argument("--timed-calls", type=int, default=20,
                     help="eager stack calls with per-kernel dispatch events (the roofline's kernel timing)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -96,6 +97,8 @@ def source_digest(files=("moe_decode_b1.hip", "moe_decode.hip", "moe_device.h", 
 
 
 PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_device.h", "moe_internal.h")
+PERSIST_SOURCES = ("moe_stack_persist.hip", "moe_persist.h", "moe_device.h", "moe_internal.h")
+PS_LAYERS_PER_LAUNCH = 64  # layers per persistent-kernel launch (the library's limit)
 LM_HEAD_SOURCES = ("moe_lm_head.hip", "moe_device.h", "moe_internal.h")
 ATTN_SOURCES = ("moe_attn.hip", "moe_device.h", "moe_internal.h")
 
@@ -106,6 +109,11 @@ ATTN_SOURCES = ("moe_attn.hip", "moe_device.h", "moe_internal.h")
 # the kernel source digest it was taken on.
 _FETCH_SCALE = 262144.0 / 131085.2  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
 _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE KiB
+# MFMA utilisation of the prefill gate/up GEMM read from a rocprofv3 --pmc run
+# (SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE per dispatch); None until taken
+# on the current sources.
+PREFILL_MFMA_COUNTERS = None
+
 COUNTER_TRAFFIC = {
     ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="a6637c8f6f343668",
                                               fetch_bytes=round(3936.8 * _FETCH_SCALE * 1024),
@@ -163,7 +171,9 @@ def time_kernels(args, stack, xs, ws, dims, T):
     return {k: v / n for k, v in tot.items()}, float(np.mean(unions))
 
 
-def roofline(workload, dims, T, kernel_us, routed_union):
+def roofline(workload, dims, T, L, kernel_us, routed_union):
+    if "ps_stack" in kernel_us:
+        return roofline_persistent(workload, dims, L, kernel_us, routed_union)
     algo = kernel_algo_bytes(dims, T, routed_union)
     dom = max(kernel_us, key=lambda k: kernel_us[k])
     us = kernel_us[dom]
@@ -182,6 +192,32 @@ def roofline(workload, dims, T, kernel_us, routed_union):
                 per_kernel=kernels)
 
 
+def roofline_persistent(workload, dims, L, kernel_us, routed_union):
+    """The persistent kernel runs the whole batch-1 step: its algorithmic bytes
+    per launch are every layer's router, shared expert and routed union (the
+    layer's packed weights the method must read), the input token and the
+    output row; the launch time is its dispatch events' duration."""
+    from sparse_moe_decode_route_amd import inputs as gen
+    D, F, E, S = dims.d_model, dims.d_ff, dims.n_routed, dims.n_shared
+    eb = 2 * gen.matrix_bytes(F, D, dims.wfmt) + gen.matrix_bytes(D, F, dims.wfmt)
+    per_layer = E * D * 2 + (routed_union + S) * eb
+    launches = -(-L // PS_LAYERS_PER_LAUNCH)
+    algo = L * per_layer / launches + (D * 4 + D * 4) / launches
+    us = kernel_us["ps_stack"] * L / launches
+    achieved = algo / (us * 1e-6) / 1e9
+    tr = COUNTER_TRAFFIC.get((workload, "ps_stack"))
+    traffic = None
+    if tr is not None and tr["source_digest"] == source_digest(PERSIST_SOURCES):
+        traffic = tr["fetch_bytes"] + tr["write_bytes"]
+    return dict(bound="hbm", kernel="ps_stack", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, algo_bytes_per_launch=round(algo),
+                us_per_launch=round(us, 3), layers_per_launch=L // launches, launches_per_step=launches,
+                us_per_layer=round(kernel_us["ps_stack"], 4), clear_us_per_step=round(kernel_us["ps_clear"], 3),
+                timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream, mean over the eager "
+                       "timed calls",
+                per_kernel={k: dict(us=round(v, 3)) for k, v in kernel_us.items()})
+
+
 def bench_stack(args, wfmt: str, T: int):
     from sparse_moe_decode_route_amd import binding as B
     from sparse_moe_decode_route_amd import inputs as gen
@@ -194,7 +230,7 @@ def bench_stack(args, wfmt: str, T: int):
     log(f"stack of {L} layers ready in {time.time() - t0:.1f}s")
     stack = B.StackHandle(devs)
     eb = B.packed_expert_bytes(dims)
-    n_tok = args.warmup + args.steps + 1
+    n_tok = max(args.warmup + args.steps + 1, 2 * cpu_workers() + 1)
     xs = gen.make_hidden(cfg_id, n_tok * T, 2048, draw=777, device="cuda").reshape(n_tok, T, 2048)
     x_static = torch.empty((T, 2048), device="cuda")
     y_static = torch.empty((T, 2048), device="cuda")
@@ -226,13 +262,15 @@ def bench_stack(args, wfmt: str, T: int):
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(args.steps):
+    # one event between consecutive replays: the K step times, and their sum
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
         g.replay()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    step_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
     layer_tok_s = L * T / (ms * 1e-3)
     # the graph replayed the same arithmetic as the eager call: check the last replay against eager
     last = int(ctr.item()) - 1
@@ -247,6 +285,7 @@ def bench_stack(args, wfmt: str, T: int):
     workload = f"stack_{wfmt}_b{T}"
     kernel_us, routed_union = time_kernels(args, stack, xs, ws, dims, T)
     log(f"per-kernel us: {kernel_us}, routed union {routed_union:.2f}")
+    pct = {f"p{q}": round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)}
     out = dict(
         metric="MoE-layer decode tokens/s + achieved HBM GB/s (% of peak), 4-bit, batch 1",
         value=round(layer_tok_s, 1), unit="MoE-layer tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -259,31 +298,67 @@ def bench_stack(args, wfmt: str, T: int):
                     expert_bytes_per_layer=round(bytes_per_layer), router_bytes_per_layer=router_b,
                     expert_gbs=round(expert_gbs, 1), expert_frac_of_peak=round(expert_gbs / HBM_PEAK_GBS, 4),
                     step_gbs_incl_router=round(step_gbs, 1), graph_matches_eager=graph_matches_eager,
+                    step_ms_percentiles=pct, decode_path="persistent" if "ps_stack" in kernel_us else "kernels",
                     kernel_source_digest=source_digest()),
-        roofline=roofline(workload, dims, T, kernel_us, routed_union),
+        roofline=roofline(workload, dims, T, L, kernel_us, routed_union),
     )
     if want_cpu:
         out["cpu_baseline"] = cpu_baseline_stack(args, hosts, xs, dims, stack, ws)
     return out
 
 
-def cpu_baseline_stack(args, hosts, xs, dims, stack, ws):
-    """The oracle (fp64 plain C, one thread) on one token through the first cpu_layers layers."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers() -> int:
+    """Host threads for the all-core oracle timing: the host's cores, at most
+    16 (a GPU's share of a shared host)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _oracle_chains(hosts, xa):
+    """One fp64 oracle chain per token (rows of xa) through all hosts' layers."""
     import oracle
+    return oracle.stack_forward(hosts, xa)
+
+
+def cpu_baseline_stack(args, hosts, xs, dims, stack, ws):
+    """The oracle (fp64 plain C) on tokens through the stack's layers, each token
+    its own chain: one thread, then every worker thread running chains at once
+    (the oracle is C called through ctypes, which releases the interpreter
+    lock).  Also compares the GPU chain of the first token with the oracle's."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
     from sparse_moe_decode_route_amd import binding as B
     n = min(args.cpu_layers, len(hosts))
     nt = max(1, args.cpu_tokens)
-    xa = xs[:nt].reshape(nt, -1).cpu().double().numpy()
+    W = cpu_workers()
+    xa_all = xs[:max(nt, 2 * W)].reshape(-1, dims.d_model).cpu().double().numpy()
     oracle.lib()
+    # one thread
+    xa = xa_all[:nt]
     t0 = time.time()
-    y_all, ytr_all, itr_all = oracle.stack_forward(hosts[:n], xa)
-    dt = time.time() - t0
-    # parity below on the first token (the GPU chain of xs[0])
+    y_all, ytr_all, itr_all = _oracle_chains(hosts[:n], xa)
+    dt1 = time.time() - t0
+    # all workers: two chains per worker, one chain per call
+    xw = xa_all[:2 * W]
+    t0 = time.time()
+    with ThreadPoolExecutor(max_workers=W) as ex:
+        list(ex.map(lambda i: _oracle_chains(hosts[:n], xw[i:i + 1]), range(len(xw))))
+    dtw = time.time() - t0
+    # parity of the first token's chain: GPU stack over the same layers and token, end to
+    # end, and at the first layer whose selection differs, the oracle's fp64 logit gap
+    # between the k-th and (k+1)-th expert on the GPU's own input to that layer
     x0 = xa[:1]
     y, ytr, itr = y_all[:1], ytr_all[:, :1], itr_all[:, :1]
-    # parity of this sample: GPU stack over the same layers and token, end to end,
-    # and at the first layer whose selection differs, the oracle's fp64 logit gap
-    # between the k-th and (k+1)-th expert on the GPU's own input to that layer
     sub = B.StackHandle(stack.layers[:n])
     yg, ytr_g, ig = B.stack_decode(sub, xs[0].contiguous(), ws=ws, trace=True)
     torch.cuda.synchronize()
@@ -303,9 +378,12 @@ def cpu_baseline_stack(args, hosts, xs, dims, stack, ws):
         srt = np.sort(lg[0])[::-1]
         gap = float(srt[dims.top_k - 1] - srt[dims.top_k])
         tf_match = bool(np.array_equal(np.sort(oi[0]), np.sort(ig[first_diff][0])))
-    return dict(value=round(n * nt / dt, 3), unit="MoE-layer tok/s", cores=1, kind="oracle",
-                sample=f"{nt} tokens (independent chains) through {n} q4_1 layers (d_model 2048, d_ff 512, "
-                       f"256+1 experts), fp64 C, one thread, {dt:.1f}s",
+    return dict(value=round(n * len(xw) / dtw, 3), unit="MoE-layer tok/s", cores=W, kind="oracle",
+                sample=f"{len(xw)} tokens (independent chains, one per call) through {n} {dims.wfmt} layers "
+                       f"(d_model 2048, d_ff 512, 256+1 experts), fp64 C, {W} threads, {dtw:.1f}s",
+                cpu_model=cpu_model(), os_cpu_count=os.cpu_count(),
+                single_thread=dict(value=round(n * nt / dt1, 3), cores=1,
+                                   sample=f"{nt} tokens through {n} layers, one thread, {dt1:.1f}s"),
                 gpu_vs_oracle=dict(layers_same_routing=int(sum(same)), layers=n, first_divergent_layer=first_diff,
                                    oracle_topk_gap_at_divergence=gap,
                                    teacher_forced_selection_matches_at_divergence=tf_match,
@@ -324,6 +402,7 @@ def bench_prefill(args):
     B.repack_weights(dims, lay.experts, packed, dims.n_experts)
     torch.cuda.synchronize()
     dev = B.DeviceLayer(dims, lay.router, lay.router_bias, packed, None)
+    host = None if args.no_cpu else gen.Layer(dims, lay.router.cpu(), lay.router_bias.cpu(), lay.experts.cpu(), None)
     del lay
     x = gen.to_bf16(gen.make_hidden(5, T, 2048, draw=0, device="cuda"))
     ws = B.workspace(dims, T)
@@ -389,6 +468,7 @@ def bench_prefill(args):
     per_kernel["pf_gemm_down"]["tflops"] = round(fl_dn / (kus["pf_gemm_down"] * 1e-6) / 1e12, 1)
     rname = "pf_router_gemm" if "pf_router_gemm" in kus else "pf_logits"
     per_kernel[rname]["tflops"] = round(fl_rt / (kus[rname] * 1e-6) / 1e12, 1)
+    cpu = None if host is None else cpu_baseline_prefill(args, host, x)
     return dict(
         metric="MoE-layer prefill tokens/s (grouped GEMM on MFMA), 4-bit weights",
         value=round(T / (ms * 1e-3), 1), unit="tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -407,8 +487,29 @@ def bench_prefill(args):
                       unit="TFLOP/s", frac=round(ach / MFMA_FP16_PEAK_TFLOPS, 4), traffic=pf_traffic,
                       flops_per_launch=fl_gu, us_per_launch=round(kus[dom], 2),
                       timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream",
-                      per_kernel=per_kernel),
+                      per_kernel=per_kernel, mfma_counters=PREFILL_MFMA_COUNTERS),
+        cpu_baseline=cpu,
     )
+
+
+def cpu_baseline_prefill(args, host, x):
+    """The oracle (fp64 C) on the first --prefill-cpu-tokens tokens of the prefill
+    batch (same layer, routing by the oracle's own top-k), split over the worker
+    threads; reported as tokens/s."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    n = min(args.prefill_cpu_tokens, x.shape[0])
+    xa = x[:n].float().cpu().double().numpy()
+    W = cpu_workers()
+    oracle.lib()
+    chunks = np.array_split(np.arange(n), W)
+    t0 = time.time()
+    with ThreadPoolExecutor(max_workers=W) as ex:
+        list(ex.map(lambda r: oracle.layer_forward(host, xa[r]), [c for c in chunks if len(c)]))
+    dt = time.time() - t0
+    return dict(value=round(n / dt, 2), unit="tok/s", cores=W, kind="oracle",
+                sample=f"{n} of the 4096 bf16 tokens through the Zipf-skewed q4_1 layer, fp64 C, {W} threads, "
+                       f"{dt:.1f}s", cpu_model=cpu_model(), os_cpu_count=os.cpu_count())
 
 
 def bench_sweep(args):

@@ -109,7 +109,11 @@ moe_status moe_repack_weights(const moe_dims *dims, const void *canonical, void 
                               void *stream);
 
 /*
- * Router and selection.  For each token:
+ * Router and selection.  "Recursive Flint 40B-A2.5B" (orcarouter.ai blog),
+ * section "The architecture is a memory-bandwidth argument", sparsity
+ * bullet: every MoE layer routes each token to 6 of its 256 routed experts
+ * (the softmax gate and the renormalisation are readings; the pages name only
+ * the counts).  For each token:
  * logits = x Wr^T (+ bias) in fp32; softmax over n_routed; the top_k
  * experts by (logit descending, index ascending); renormalised weights.
  *   x          [n_tokens, d_model], fp32 (act = MOE_ACT_F32) or bf16
@@ -125,24 +129,35 @@ moe_status moe_route_topk(const moe_dims *dims, const void *x, int32_t act, int3
                           size_t ws_bytes, void *stream);
 
 /*
- * Expert FFN over given routing: for each token
+ * Expert FFN over given routing.  Same page and section as moe_route_topk:
+ * besides the routed experts one shared expert is always active, and decode
+ * time goes to moving the chosen experts' weights, so only those are read;
+ * section "The quantisation recipe is the most transferable part": the
+ * weights are 4-bit (q4_1, NVFP4).  For each token
  * y = sum_shared expert_s(x) + sum_i topk_w[i] * expert_{topk_idx[i]}(x),
  * streaming each distinct expert's 4-bit (or bf16) weights once per call and
- * applying it to all tokens that chose it.  Decode sizes: 1 <= n_tokens <= 8.
+ * applying it to all tokens that chose it.
+ * 1 <= n_tokens <= 65536: up to 8 tokens (up to 32 when the small-batch
+ * kernels fit the shape, see moe_layer_forward) take the decode GEMV path,
+ * more take the grouped GEMM of moe_layer_forward_prefill.
  *   experts      device layout; tensor_scale as in moe_layer_weights
- *   topk_idx     int32 [n_tokens, top_k], each in [0, n_routed), distinct per token
+ *   topk_idx     int32 [n_tokens, top_k], normally in [0, n_routed) and
+ *                distinct per token
  *   topk_w       fp32 [n_tokens, top_k]
  *   y            out fp32 [n_tokens, d_model]
  *   ws, ws_bytes workspace of at least moe_workspace_size(dims, n_tokens)
- * Indices outside [0, n_routed) select nothing (their slot contributes 0);
- * a repeated index counts once, with the weight of its last slot.
+ * Indices outside [0, n_routed) select nothing (their slot contributes 0).
+ * A repeated index contributes once per slot, as the sum above says: the
+ * expert is applied once with the sum of its slots' weights (added in slot
+ * order).
  */
 moe_status moe_expert_ffn_q4(const moe_dims *dims, const void *x, int32_t act, int32_t n_tokens,
                              const void *experts, const float *tensor_scale, const int32_t *topk_idx,
                              const float *topk_w, float *y, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Whole layer: route + expert FFN.  n_tokens <= 8 takes a decode path
+ * Whole layer: route + expert FFN, as defined by moe_route_topk and
+ * moe_expert_ffn_q4 (same page and section).  n_tokens <= 8 takes a decode path
  * (grouped GEMV over the union of chosen experts), and so does n_tokens <= 32
  * when the small-batch kernels fit the shape (d_model 2048 or 4096 with
  * 4-bit weights, 512 or 1024 with bf16; d_ff of 16 or 32 blocks, a multiple
@@ -165,7 +180,11 @@ moe_status moe_layer_forward_prefill(const moe_dims *dims, const moe_layer_weigh
                                      float *topk_w_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * A stack of n_layers layers: x_0 = x0 (fp32 [n_tokens, d_model]),
+ * A stack of decode layers.  Same page and section: 47 of the model's 49
+ * layers are MoE layers (also the layer table of the 648news.com page, section
+ * "MoE structure and recommended settings"); the RMS normalisation between
+ * layers, with unit gain and no residual, is a reading for independent
+ * synthetic layers.  x_0 = x0 (fp32 [n_tokens, d_model]),
  * y_l = layer_l(x_l), x_{l+1} = y_l / sqrt(mean(y_l^2) + 1e-6) per token;
  * y receives y_{n_layers-1}.  layers is a host array of n_layers structs.
  * y_trace fp32 [n_layers, n_tokens, d_model] and idx_trace int32
@@ -187,7 +206,9 @@ moe_status moe_stack_decode(const moe_dims *dims, int32_t n_layers, const moe_la
  *              kernel slot of a layer, averaged over the layers that ran it
  *              (-1 for a slot that never ran).
  *   n_kernels  (host) receives the number of slots used (3 on the batch-1
- *              path, 4 on the small-batch and general paths).
+ *              three-kernel path, 4 on the small-batch and general paths,
+ *              2 on the persistent path: the persistent kernel's time per
+ *              layer, and the clearing kernel's per call).
  *   names      (host, optional) receives the slots' kernel names separated
  *              by ';' (truncated to names_cap bytes, NUL-terminated).
  * Creates and destroys 8 * n_layers HIP events (n_layers <= 4096); not for
@@ -335,6 +356,34 @@ moe_status moe_attn_decode_timed(const moe_attn_dims *dims, int32_t n_seqs, int3
                                  const float *k_norm_w, const float *sinks, const int32_t *pos, uint16_t *k_cache,
                                  uint16_t *v_cache, float *out, void *ws, size_t ws_bytes, float *kernel_us,
                                  void *stream);
+
+/*
+ * (host) Batch-1 decode path of moe_layer_forward and moe_stack_decode,
+ * process-wide, for calls made after it returns:
+ *   MOE_PATH_AUTO     (default) the persistent kernel where it is built for
+ *                     the shape (q4_1 or NVFP4, d_model 2048, d_ff 512, one
+ *                     shared expert, top_k <= 6, n_routed <= 256, one block
+ *                     per CU fitting on 256 CUs), else three kernels per layer;
+ *   MOE_PATH_KERNELS  always three kernels per layer.
+ * The persistent kernel runs every layer of a stack in one dispatch (one per
+ * 64 layers) after a small clearing kernel: one block per CU, the layer's
+ * three global dependencies (logits, h, y) exchanged through mailboxes in the
+ * workspace, and the next layer's router row and shared expert loaded while
+ * the current layer runs.  Its waits are bounded: a wait that gives up ends
+ * the call with NaN outputs and an error that moe_decode_check reports.
+ */
+#define MOE_PATH_AUTO 0
+#define MOE_PATH_KERNELS 1
+moe_status moe_set_decode_path(int32_t path);
+
+/*
+ * (host) Whether the last batch-1 call that used this workspace on the
+ * persistent kernel finished its waits: MOE_OK, or MOE_ERR_HIP when a wait
+ * gave up (its outputs are NaN).  Copies the workspace's error word and
+ * synchronises `stream`.  Calls on other paths leave the word untouched.
+ */
+moe_status moe_decode_check(const moe_dims *dims, int32_t n_tokens, const void *ws, size_t ws_bytes,
+                            void *stream);
 
 /* (host) static description of a status code. */
 const char *moe_status_string(moe_status s);

@@ -25,8 +25,10 @@ ENTRY_POINTS = (
     "moe_expert_ffn_q4", "moe_layer_forward", "moe_layer_forward_prefill", "moe_stack_decode",
     "moe_stack_decode_timed", "moe_layer_forward_prefill_timed", "moe_lm_head_bytes", "moe_lm_head_repack",
     "moe_lm_head", "moe_lm_head_timed", "moe_attn_workspace_size", "moe_attn_chunk_plan", "moe_attn_decode", "moe_attn_decode_timed",
-    "moe_status_string", "moe_last_error",
+    "moe_set_decode_path", "moe_decode_check", "moe_status_string", "moe_last_error",
 )
+
+PATH_AUTO, PATH_KERNELS = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -103,6 +105,10 @@ def lib():
         L.moe_attn_decode.argtypes = [pa, i32, i32] + [vp] * 11 + [sz, vp]
         L.moe_attn_decode_timed.restype = ctypes.c_int
         L.moe_attn_decode_timed.argtypes = [pa, i32, i32] + [vp] * 11 + [sz, ctypes.POINTER(ctypes.c_float), vp]
+        L.moe_set_decode_path.restype = ctypes.c_int
+        L.moe_set_decode_path.argtypes = [i32]
+        L.moe_decode_check.restype = ctypes.c_int
+        L.moe_decode_check.argtypes = [pd, i32, vp, sz, vp]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_last_error.restype = ctypes.c_char_p
@@ -235,6 +241,17 @@ def layer_forward(layer: DeviceLayer, x: torch.Tensor, ws: Optional[torch.Tensor
 
 def layer_forward_prefill(layer: DeviceLayer, x: torch.Tensor, **kw):
     return layer_forward(layer, x, prefill=True, **kw)
+
+
+def set_decode_path(path: int):
+    """PATH_AUTO (persistent batch-1 kernel where built) or PATH_KERNELS."""
+    _check(lib().moe_set_decode_path(path))
+
+
+def decode_check(dims: gen.LayerDims, n_tokens: int, ws: torch.Tensor, stream=None):
+    """Raises MoeError if the last persistent-kernel call on ws gave up a wait."""
+    d = cdims(dims)
+    _check(lib().moe_decode_check(ctypes.byref(d), n_tokens, _ptr(ws), ws.numel(), _stream(stream)))
 
 
 class StackHandle:

@@ -6,11 +6,13 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
+#include "moe_persist.h"
 #include "moe_prefill.h"
 
 namespace {
@@ -62,7 +64,7 @@ bool decode_tokens(const moe_dims &d, int T) {
 
 // Decode-path workspace (n_tokens <= 32).
 struct DecodeWs {
-    size_t logits, idx, w, xbuf, xconv, meta, act_expert, act_mask, act_w, h, ybuf0, ybuf1, work, pairs, b1_list,
+    size_t logits, idx, w, xbuf, xconv, meta, act_expert, act_mask, act_w, h, ybuf0, ybuf1, work, pairs, b1_list, ps,
         total;
     int amax;
 };
@@ -91,6 +93,7 @@ DecodeWs decode_ws(const moe_dims &d, int T) {
     L.work = take((size_t)(d.n_shared * ((T + 1) / 2) + T * d.top_k) * 16);
     L.pairs = take((size_t)(d.n_shared * T + T * d.top_k) * 16);
     L.b1_list = take(8 * 16 * 4);
+    L.ps = take(moe::PS_WS_BYTES);
     L.total = o;
     return L;
 }
@@ -201,8 +204,63 @@ hipError_t launch_any(const moe::DecodeParams &p, hipStream_t st, int *path = nu
 const char *const kB1Names = "b1_route_shared;b1_topk_gateup;b1_down";
 const char *const kGenericNames = "phase_a_kernel;select_kernel;gateup_kernel;down_kernel";
 const char *const kBnNames = "bn_router;bn_select;bn_gateup;bn_down";
+const char *const kPsNames = "ps_stack;ps_clear";
+
+// Process-wide choice of the batch-1 decode path (moe_set_decode_path).
+int g_decode_path = MOE_PATH_AUTO;
+
+// Whether batch-1 calls of this shape take the persistent kernel.
+bool use_persistent(const moe_dims &d, int T) {
+    return T == 1 && g_decode_path == MOE_PATH_AUTO &&
+           moe::ps_supported(d.wfmt, d.d_model, d.d_ff, d.n_routed, d.n_shared, d.top_k);
+}
+
+// The persistent batch-1 path over n_layers layers (host array), x0 fp32
+// [D]: clear the mailboxes, then one launch per PS_MAX_LAYERS layers.  ev:
+// optional start/stop pairs, pair 0 for the clear and pair 1 + c for launch c.
+moe_status persistent_impl(const moe_dims &d, int n_layers, const moe_layer_weights *layers, const float *x0,
+                           float *y, float *y_trace, int32_t *idx_trace, float *w_trace, void *ws,
+                           const DecodeWs &L, hipStream_t st, hipEvent_t *ev) {
+    moe::PsParams p{};
+    p.D = d.d_model;
+    p.F = d.d_ff;
+    p.E = d.n_routed;
+    p.K = d.top_k;
+    p.last_layer = n_layers - 1;
+    p.expert_bytes = moe_packed_expert_bytes(&d);
+    p.x0 = x0;
+    p.y = y;
+    p.y_trace = y_trace;
+    p.idx_trace = idx_trace;
+    p.w_trace = w_trace;
+    // polls per wait before giving up: 2^18 (about 0.1 s); the environment
+    // variable MOE_PERSISTENT_SPIN_LIMIT lowers it so that tests can drive the
+    // give-up path with every kernel still ending normally
+    p.spin = 1 << 18;
+    if (const char *e = getenv("MOE_PERSISTENT_SPIN_LIMIT")) p.spin = std::max(0, std::min(p.spin, atoi(e)));
+    const size_t nslot = (size_t)moe::PS_BLOCKS * moe::PS_SLOT_WORDS;
+    p.mb_lg = at<unsigned long long>(ws, L.ps);
+    p.mb_h = p.mb_lg + nslot;
+    p.mb_y = p.mb_h + nslot;
+    p.ctrl = reinterpret_cast<uint32_t *>(p.mb_y + nslot);
+    MOE_TRY(hip_status(moe::ps_clear_launch(p, st, ev), "persistent clear launch"));
+    for (int c = 0, l0 = 0; l0 < n_layers; c++, l0 += moe::PS_MAX_LAYERS) {
+        p.l0 = l0;
+        p.n_layers = std::min(moe::PS_MAX_LAYERS, n_layers - l0);
+        for (int i = 0; i < p.n_layers; i++) {
+            const moe_layer_weights &w = layers[l0 + i];
+            p.layer[i] = moe::PsLayer{static_cast<const uint16_t *>(w.router), w.router_bias,
+                                      static_cast<const uint8_t *>(w.experts),
+                                      d.wfmt == MOE_W_NVFP4 ? w.tensor_scale : nullptr};
+        }
+        MOE_TRY(hip_status(moe::ps_launch(p, d.wfmt, st, ev ? ev + 2 * (1 + c) : nullptr), "persistent launch"));
+    }
+    return ok();
+}
 
 }  // namespace
+
+moe_status moe::set_error(moe_status s, const std::string &msg) { return fail(s, msg); }
 
 extern "C" {
 
@@ -351,6 +409,8 @@ moe_status moe_layer_forward(const moe_dims *d, const moe_layer_weights *w, cons
     p.want_router = 1;
     p.want_shared = 1;
     p.y = y;
+    if (use_persistent(*d, n_tokens))
+        return persistent_impl(*d, 1, w, p.x, y, nullptr, topk_idx_out, topk_w_out, ws, L, st, nullptr);
     return hip_status(launch_any(p, st), "layer launch");
 }
 
@@ -408,6 +468,10 @@ moe_status stack_impl(const moe_dims *d, int32_t n_layers, const moe_layer_weigh
     MOE_TRY(check_ptr(idx_trace, "idx_trace", false));
     MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
     const DecodeWs L = decode_ws(*d, n_tokens);
+    if (use_persistent(*d, n_tokens)) {
+        if (path) *path = 4;
+        return persistent_impl(*d, n_layers, layers, x0, y, y_trace, idx_trace, nullptr, ws, L, st, ev);
+    }
     const size_t TD = (size_t)n_tokens * d->d_model;
     const float *prev = nullptr;
     for (int l = 0; l < n_layers; l++) {
@@ -476,6 +540,26 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
     if (s != MOE_OK) {
         destroy();
         return s;
+    }
+    if (path == 4) {
+        // persistent kernel: its launches' time per layer, then the clear per call
+        double tot = 0.0;
+        const int chunks = (n_layers + moe::PS_MAX_LAYERS - 1) / moe::PS_MAX_LAYERS;
+        bool okt = true;
+        for (int c = 0; c < chunks; c++) {
+            float ms = 0.f;
+            okt &= hipEventElapsedTime(&ms, ev[2 * (1 + c)], ev[2 * (1 + c) + 1]) == hipSuccess;
+            tot += ms;
+        }
+        float ms_clear = 0.f;
+        okt &= hipEventElapsedTime(&ms_clear, ev[0], ev[1]) == hipSuccess;
+        destroy();
+        if (!okt) return fail(MOE_ERR_HIP, "event timing failed");
+        kernel_us[0] = (float)(tot / n_layers * 1e3);
+        kernel_us[1] = ms_clear * 1e3f;
+        *n_kernels = 2;
+        if (names && names_cap) snprintf(names, names_cap, "%s", kPsNames);
+        return ok();
     }
     const int slots = path == 1 ? 3 : 4;
     for (int k = 0; k < slots; k++) {
@@ -788,6 +872,27 @@ moe_status moe_attn_decode_timed(const moe_attn_dims *d, int32_t n_seqs, int32_t
     }
     for (auto &e : ev) (void)hipEventDestroy(e);
     return s == MOE_OK ? ok() : s;
+}
+
+moe_status moe_set_decode_path(int32_t path) {
+    if (path != MOE_PATH_AUTO && path != MOE_PATH_KERNELS)
+        return fail(MOE_ERR_INVALID_ARG, "path must be MOE_PATH_AUTO or MOE_PATH_KERNELS");
+    g_decode_path = path;
+    return ok();
+}
+
+moe_status moe_decode_check(const moe_dims *d, int32_t n_tokens, const void *ws, size_t ws_bytes, void *stream) {
+    MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
+    if (!decode_tokens(*d, n_tokens)) return ok();
+    const DecodeWs L = decode_ws(*d, n_tokens);
+    const size_t nslot = (size_t)moe::PS_BLOCKS * moe::PS_SLOT_WORDS;
+    const char *ctrl = static_cast<const char *>(ws) + L.ps + 3 * nslot * 8;
+    uint32_t flag = 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    MOE_TRY(hip_status(hipMemcpyAsync(&flag, ctrl, 4, hipMemcpyDeviceToHost, st), "error word copy"));
+    MOE_TRY(hip_status(hipStreamSynchronize(st), "stream synchronize"));
+    if (flag) return fail(MOE_ERR_HIP, "a wait of the persistent decode kernel gave up (outputs set to NaN)");
+    return ok();
 }
 
 const char *moe_status_string(moe_status s) {

@@ -1,10 +1,12 @@
-// Batch-1 decode path: three kernels per layer.
+// Batch-1 decode path: three kernels per layer (the persistent kernel of
+// moe_stack_persist.hip replaces it for the shapes that kernel is built for).
 //
 //   A  router logits (one wave per routed expert row) and the shared
 //      experts' h = silu(Wg x) * (Wu x) (one wave per pair of features).
-//   B  one wave per block computes the top-k of the logits (DPP argmax; no
-//      separate selection kernel) and shares it through LDS, then every
-//      wave computes h for two features of one chosen expert.
+//   B  every wave finds its own expert, the j-th largest logit (DPP argmax
+//      rounds, no barrier and no separate selection kernel), then computes h
+//      for two features of that expert; wave 0 of the first blocks also runs
+//      the full selection with weights for the routing outputs.
 //   C  down projection with the weighted combine: a block owns 8 output
 //      rows, its four waves split the active experts, h is staged in LDS,
 //      the four partial sums are added in a fixed order.

@@ -5,7 +5,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "../../include/moe.h"
+
 namespace moe {
+
+// Records msg for moe_last_error() on the calling thread and returns s.
+moe_status set_error(moe_status s, const std::string &msg);
 
 constexpr int MAX_DECODE_T = 8;   // batch-1, general and stack decode paths
 constexpr int MAX_BN_T = 32;      // small-batch path (regular shapes; token masks are 32 bits)
