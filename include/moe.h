@@ -170,6 +170,26 @@ moe_status moe_layer_forward(const moe_dims *dims, const moe_layer_weights *w, c
                              size_t ws_bytes, void *stream);
 
 /*
+ * moe_layer_forward without a caller workspace, for callers that cannot
+ * allocate device memory: code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (less ws and ws_bytes),
+ * kernels and results as moe_layer_forward.  The workspace is a static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES bytes, one copy per device, held
+ * until the process ends; its address is looked up on the first call on each
+ * device (the current device).  The call allocates nothing.  A call whose
+ * moe_workspace_size() exceeds the array returns MOE_ERR_WORKSPACE with
+ * nothing enqueued (at d_model 2048, d_ff 512, 256 + 1 experts, top-6 the
+ * decode path fits up to 32 tokens).  Every call on a device shares that
+ * device's array, which keeps the last call's contents: calls that overlap in
+ * time on one device (different streams or threads) race and give undefined
+ * results; calls ordered on one stream are safe.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+moe_status moe_layer_forward_noalloc(const moe_dims *dims, const moe_layer_weights *w, const void *x, int32_t act,
+                                     int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out,
+                                     void *stream);
+
+/*
  * Prefill path for any n_tokens: route all tokens, permute
  * (token, slot) pairs by expert (histogram, scan, scatter), run the experts
  * as a grouped GEMM on the matrix cores (fp16 operands, fp32 accumulate),

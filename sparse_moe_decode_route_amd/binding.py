@@ -22,7 +22,8 @@ MOE_OK = 0
 ACT_F32, ACT_BF16 = 0, 1
 ENTRY_POINTS = (
     "moe_packed_expert_bytes", "moe_workspace_size", "moe_repack_weights", "moe_route_topk",
-    "moe_expert_ffn_q4", "moe_layer_forward", "moe_layer_forward_prefill", "moe_stack_decode",
+    "moe_expert_ffn_q4", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_layer_forward_prefill",
+    "moe_stack_decode",
     "moe_stack_decode_timed", "moe_layer_forward_prefill_timed", "moe_lm_head_bytes", "moe_lm_head_repack",
     "moe_lm_head", "moe_lm_head_timed", "moe_attn_workspace_size", "moe_attn_chunk_plan", "moe_attn_decode", "moe_attn_decode_timed",
     "moe_set_decode_path", "moe_decode_check", "moe_status_string", "moe_last_error",
@@ -78,6 +79,8 @@ def lib():
         L.moe_layer_forward.argtypes = [pd, ctypes.POINTER(CLayerWeights), vp, i32, i32, vp, vp, vp, vp, sz, vp]
         L.moe_layer_forward_prefill.restype = ctypes.c_int
         L.moe_layer_forward_prefill.argtypes = L.moe_layer_forward.argtypes
+        L.moe_layer_forward_noalloc.restype = ctypes.c_int
+        L.moe_layer_forward_noalloc.argtypes = [pd, ctypes.POINTER(CLayerWeights), vp, i32, i32, vp, vp, vp, vp]
         L.moe_stack_decode.restype = ctypes.c_int
         L.moe_stack_decode.argtypes = [pd, i32, ctypes.POINTER(CLayerWeights), vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_stack_decode_timed.restype = ctypes.c_int
@@ -241,6 +244,17 @@ def layer_forward(layer: DeviceLayer, x: torch.Tensor, ws: Optional[torch.Tensor
 
 def layer_forward_prefill(layer: DeviceLayer, x: torch.Tensor, **kw):
     return layer_forward(layer, x, prefill=True, **kw)
+
+
+def layer_forward_noalloc(layer: DeviceLayer, x: torch.Tensor, y: torch.Tensor, idx: Optional[torch.Tensor] = None,
+                          w: Optional[torch.Tensor] = None, stream=None):
+    """moe_layer_forward_noalloc: the layer with the library's static scratch as
+    workspace; the caller passes every output buffer."""
+    d = cdims(layer.dims)
+    cw = layer.cstruct()
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(d), ctypes.byref(cw), _ptr(x), _act(x), x.shape[0], _ptr(y),
+                                           _ptr(idx), _ptr(w), _stream(stream)))
+    return y, idx, w
 
 
 def set_decode_path(path: int):
