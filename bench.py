@@ -38,6 +38,8 @@ def parse():
                     choices=["stack_q4_1_b1", "stack_nvfp4_b1", "stack_nvfp4_b8", "prefill_q4_1", "sweep_q4_1",
                              "lm_head_q4_1", "lm_head_nvfp4", "lm_head_bf16", "attn_swa", "attn_full128k"])
     ap.add_argument("--layers", type=int, default=47)
+    ap.add_argument("--decode-path", default="kernels", choices=["kernels", "persistent"],
+                    help="batch-1 decode path: three kernels per layer, or the persistent kernel where built")
     ap.add_argument("--lm-tokens", type=int, default=1, help="tokens per output-layer call (1..8)")
     ap.add_argument("--lm-cpu-rows", type=int, default=146_484, help="vocabulary rows in the CPU baseline sample")
     ap.add_argument("--lm-cpu-seconds", type=float, default=10.0, help="minimum CPU baseline time (whole passes)")
@@ -797,6 +799,7 @@ def main():
     sys.path.insert(0, root)
     from sparse_moe_decode_route_amd import binding as B
     B.lib()  # fails loudly if libmoe.so is missing
+    B.set_decode_path(B.PATH_PERSISTENT if args.decode_path == "persistent" else B.PATH_KERNELS)
     if args.workload == "stack_q4_1_b1":
         out = bench_stack(args, "q4_1", 1)
     elif args.workload == "stack_nvfp4_b1":

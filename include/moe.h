@@ -380,20 +380,22 @@ moe_status moe_attn_decode_timed(const moe_attn_dims *dims, int32_t n_seqs, int3
 /*
  * (host) Batch-1 decode path of moe_layer_forward and moe_stack_decode,
  * process-wide, for calls made after it returns:
- *   MOE_PATH_AUTO     (default) the persistent kernel where it is built for
- *                     the shape (q4_1 or NVFP4, d_model 2048, d_ff 512, one
- *                     shared expert, top_k <= 6, n_routed <= 256, one block
- *                     per CU fitting on 256 CUs), else three kernels per layer;
- *   MOE_PATH_KERNELS  always three kernels per layer.
+ *   MOE_PATH_KERNELS     (default) three kernels per layer;
+ *   MOE_PATH_PERSISTENT  the persistent kernel where it is built for the
+ *                        shape (q4_1 or NVFP4, d_model 2048, d_ff 512, one
+ *                        shared expert, top_k <= 6, n_routed <= 256, one block
+ *                        per CU fitting on 256 CUs), else three kernels.
  * The persistent kernel runs every layer of a stack in one dispatch (one per
  * 64 layers) after a small clearing kernel: one block per CU, the layer's
  * three global dependencies (logits, h, y) exchanged through mailboxes in the
  * workspace, and the next layer's router row and shared expert loaded while
- * the current layer runs.  Its waits are bounded: a wait that gives up ends
- * the call with NaN outputs and an error that moe_decode_check reports.
+ * the current layer runs.  On MI355X it is slower than three kernels per
+ * layer (the exchanges cost more than kernel boundaries), hence not the
+ * default.  Its waits are bounded: a wait that gives up ends the call with
+ * NaN outputs and an error that moe_decode_check reports.
  */
-#define MOE_PATH_AUTO 0
-#define MOE_PATH_KERNELS 1
+#define MOE_PATH_KERNELS 0
+#define MOE_PATH_PERSISTENT 1
 moe_status moe_set_decode_path(int32_t path);
 
 /*

@@ -207,11 +207,11 @@ const char *const kBnNames = "bn_router;bn_select;bn_gateup;bn_down";
 const char *const kPsNames = "ps_stack;ps_clear";
 
 // Process-wide choice of the batch-1 decode path (moe_set_decode_path).
-int g_decode_path = MOE_PATH_AUTO;
+int g_decode_path = MOE_PATH_KERNELS;
 
 // Whether batch-1 calls of this shape take the persistent kernel.
 bool use_persistent(const moe_dims &d, int T) {
-    return T == 1 && g_decode_path == MOE_PATH_AUTO &&
+    return T == 1 && g_decode_path == MOE_PATH_PERSISTENT &&
            moe::ps_supported(d.wfmt, d.d_model, d.d_ff, d.n_routed, d.n_shared, d.top_k);
 }
 
@@ -875,8 +875,8 @@ moe_status moe_attn_decode_timed(const moe_attn_dims *d, int32_t n_seqs, int32_t
 }
 
 moe_status moe_set_decode_path(int32_t path) {
-    if (path != MOE_PATH_AUTO && path != MOE_PATH_KERNELS)
-        return fail(MOE_ERR_INVALID_ARG, "path must be MOE_PATH_AUTO or MOE_PATH_KERNELS");
+    if (path != MOE_PATH_KERNELS && path != MOE_PATH_PERSISTENT)
+        return fail(MOE_ERR_INVALID_ARG, "path must be MOE_PATH_KERNELS or MOE_PATH_PERSISTENT");
     g_decode_path = path;
     return ok();
 }

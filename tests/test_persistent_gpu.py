@@ -20,7 +20,7 @@ from tests.helpers import REL_L2_TOL, check_routing, decode_band, rel_l2
 pytestmark = pytest.mark.gpu
 
 FP32_PATH_TOL = 5e-5
-PATHS = {"persistent": B.PATH_AUTO, "kernels": B.PATH_KERNELS}
+PATHS = {"persistent": B.PATH_PERSISTENT, "kernels": B.PATH_KERNELS}
 
 
 def _dev():
@@ -42,7 +42,7 @@ def _router64(host):
 def path(request):
     B.set_decode_path(PATHS[request.param])
     yield request.param
-    B.set_decode_path(B.PATH_AUTO)
+    B.set_decode_path(B.PATH_KERNELS)
 
 
 def _one(host, dl, x, label):
@@ -78,7 +78,7 @@ def test_paths_agree_on_routing_and_output():
         for name, code in PATHS.items():
             B.set_decode_path(code)
             outs[name] = B.layer_forward(dl, x)
-        B.set_decode_path(B.PATH_AUTO)
+        B.set_decode_path(B.PATH_KERNELS)
         torch.cuda.synchronize()
         (yp, ip, wp), (yk, ik, wk) = outs["persistent"], outs["kernels"]
         assert torch.equal(ip, ik)
@@ -86,8 +86,15 @@ def test_paths_agree_on_routing_and_output():
         assert float(rel_l2(yp.cpu().numpy(), yk.cpu().numpy()).max()) <= FP32_PATH_TOL
 
 
+@pytest.fixture
+def persistent():
+    B.set_decode_path(B.PATH_PERSISTENT)
+    yield
+    B.set_decode_path(B.PATH_KERNELS)
+
+
 @pytest.mark.parametrize("case", ["e64", "e64_equal_logits", "zipf_bias", "top4"])
-def test_persistent_shapes(case):
+def test_persistent_shapes(persistent, case):
     if case == "e64":
         host, dl = _layer(gen.LayerDims(2048, 512, n_routed=64, n_shared=1, top_k=6, wfmt="q4_1"), 61)
     elif case == "e64_equal_logits":
@@ -106,7 +113,7 @@ def test_persistent_shapes(case):
 
 
 @pytest.mark.parametrize("wfmt,L", [("nvfp4", 5), ("nvfp4", 66)])
-def test_persistent_stack_teacher_forced(wfmt, L):
+def test_persistent_stack_teacher_forced(persistent, wfmt, L):
     """L layers through the persistent path (66: two launches, 64 + 2 layers;
     the oracle checks layers 0-2 and 62-65 teacher-forced)."""
     dims = gen.LayerDims(2048, 512, wfmt=wfmt)
@@ -138,7 +145,7 @@ def test_persistent_stack_teacher_forced(wfmt, L):
         assert err <= FP32_PATH_TOL, (l, err)
 
 
-def test_persistent_stack_graph_replays_match_eager():
+def test_persistent_stack_graph_replays_match_eager(persistent):
     dims = gen.LayerDims(2048, 512, wfmt="q4_1")
     devs = [_layer(dims, 66, layer=l)[1] for l in range(3)]
     stack = B.StackHandle(devs)
@@ -164,7 +171,7 @@ def test_persistent_stack_graph_replays_match_eager():
         assert torch.equal(got, ref), i
 
 
-def test_persistent_give_up_path_sets_error_and_nan():
+def test_persistent_give_up_path_sets_error_and_nan(persistent):
     """A spin limit of 0 makes every wait that is not satisfied at its first
     poll give up: the call must end (no hang) with NaN outputs and an error
     from moe_decode_check; the next call with the normal limit is correct."""
