@@ -150,9 +150,8 @@ def kernel_algo_bytes(dims, T: int, routed_union: float):
     K = dims.top_k
     pairs = T * K + S * T  # (expert, token) rows of h
     bn = {"bn_router": E * D * 2 + T * D * 4 + T * E * 4,
-          "bn_select": T * E * 4,
-          "bn_gateup": (U + S) * 2 * gu + T * D * 4 + pairs * F * 4,
-          "bn_down": (U + S) * dn + pairs * F * 4 + T * D * 4}
+          "bn_gateup": (U + S) * 2 * gu + T * D * 4 + T * E * 4 + pairs * F * 4,
+          "bn_down": (U + S) * dn + pairs * F * 4 + T * D * 4 + T * E * 4}
     return {"b1_route_shared": a, "b1_topk_gateup": b, "b1_down": c,
             "phase_a_kernel": a, "select_kernel": T * E * 4, "gateup_kernel": b, "down_kernel": c, **bn}
 

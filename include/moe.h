@@ -226,7 +226,7 @@ moe_status moe_stack_decode(const moe_dims *dims, int32_t n_layers, const moe_la
  *              kernel slot of a layer, averaged over the layers that ran it
  *              (-1 for a slot that never ran).
  *   n_kernels  (host) receives the number of slots used (3 on the batch-1
- *              three-kernel path, 4 on the small-batch and general paths,
+ *              and small-batch paths, 4 on the general path,
  *              2 on the persistent path: the persistent kernel's time per
  *              layer, and the clearing kernel's per call).
  *   names      (host, optional) receives the slots' kernel names separated

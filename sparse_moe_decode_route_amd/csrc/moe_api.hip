@@ -203,7 +203,7 @@ hipError_t launch_any(const moe::DecodeParams &p, hipStream_t st, int *path = nu
 // Kernel names of one layer's slots, per path (slot order of MOE_LAUNCH).
 const char *const kB1Names = "b1_route_shared;b1_topk_gateup;b1_down";
 const char *const kGenericNames = "phase_a_kernel;select_kernel;gateup_kernel;down_kernel";
-const char *const kBnNames = "bn_router;bn_select;bn_gateup;bn_down";
+const char *const kBnNames = "bn_router;bn_gateup;bn_down";
 const char *const kPsNames = "ps_stack;ps_clear";
 
 // Process-wide choice of the batch-1 decode path (moe_set_decode_path).
@@ -561,7 +561,7 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
         if (names && names_cap) snprintf(names, names_cap, "%s", kPsNames);
         return ok();
     }
-    const int slots = path == 1 ? 3 : 4;
+    const int slots = path == 2 ? 4 : 3;
     for (int k = 0; k < slots; k++) {
         double tot = 0.0;
         int cnt = 0;

@@ -8,8 +8,8 @@
 //      for two features of that expert; wave 0 of the first blocks also runs
 //      the full selection with weights for the routing outputs.
 //   C  down projection with the weighted combine: a block owns 8 output
-//      rows, its four waves split the active experts, h is staged in LDS,
-//      the four partial sums are added in a fixed order.
+//      rows, each of its eight waves takes one active expert, h is staged in
+//      LDS, the waves' partial sums are added in a fixed order.
 //
 // Decode is bound by moving weights (the Flint 40B-A2.5B pages, "Recursive
 // Flint 40B-A2.5B", orcarouter.ai blog, section "The architecture is a
@@ -32,7 +32,7 @@ namespace {
 
 constexpr int B1_RG = 2;          // features (gate+up row pairs) per wave in A and B
 constexpr int B1_WAVES_B = 4;     // waves per block in B
-constexpr int B1_WAVES_C = 4;     // waves per block in C
+constexpr int B1_WAVES_C = 8;     // waves per block in C (one active slot each)
 constexpr int B1_RR = 2;          // output rows per lane group in C
 constexpr int B1_MAX_ACTIVE = 8;  // shared + routed slots
 constexpr int B1_SLOTS_PER_WAVE = B1_MAX_ACTIVE / B1_WAVES_C;
@@ -230,8 +230,9 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_B) b1_topk_gateup(DecodePar
 }
 
 // ---------------------------------------------------------------------------
-// C: down projection + combine; block = 4 waves over the same 8 rows, wave w
-// takes slots w and w + 4.
+// C: down projection + combine; block = 8 waves over the same 8 rows, wave w
+// takes slot w (two waves per SIMD keep a wave's LDS and FMA latencies
+// hidden behind the other's).
 // ---------------------------------------------------------------------------
 template <int FMT, int LPR_F>
 __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_C) b1_down(DecodeParams p) {

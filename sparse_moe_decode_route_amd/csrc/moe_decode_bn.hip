@@ -3,23 +3,27 @@
 // The layer is the same as on the batch-1 path (the Flint 40B-A2.5B pages,
 // "Recursive Flint 40B-A2.5B", orcarouter.ai blog, section "The architecture
 // is a memory-bandwidth argument": 256 routed experts, 6 chosen per token,
-// one shared expert; decode time is weight traffic).  With T tokens the
-// union of their chosen experts is read once per layer: expert e's weights
-// serve every token that chose it.
+// one shared expert; decode time is weight traffic).  Three kernels:
 //
 //   bn_router   router logits: one block per expert row, one wave per token
 //               (the batch-1 router's reduction per wave); in a stack
 //               x_t = y_t / rms(y_t) is never written: the router and gate/up
 //               kernels apply each token's 1/rms, computed from the loads they
 //               already make
-//   bn_select   per-token top-k, the expert union with token masks, and two
-//               work lists: (slot, token pair) items for gate/up and
-//               (slot, token) pairs for the down projection
-//   bn_gateup   one wave per (item, 2-4 features): weights and both tokens' x
-//               loaded before any arithmetic
-//   bn_down     8 output rows per block; wave t sums token t's down terms
-//               (its shared slots, then its selections in top-k order) in
-//               batches of 4 with every load of a batch in flight
+//   bn_gateup   one wave per (item, 2-4 features).  Items: each shared expert
+//               with a pair of tokens, then every (token t, selection j): the
+//               wave finds token t's j-th expert itself from the logits (the
+//               batch-1 selection rounds), so no selection kernel or work
+//               list sits between the router and the weight stream.  A
+//               routed expert chosen by several tokens is read once per token
+//               (at 8 tokens and 256 experts, 48 selections hit ~45 experts;
+//               repeats are served by L2)
+//   bn_down     8 output rows per block; wave t takes token t's selections
+//               (written by the gate/up wave of its first selection) and sums
+//               its down terms (its
+//               shared slots, then its selections in top-k order) in batches
+//               of 4 with every load of a batch in flight
+// h is kept per (token, slot of the token): [T][S + K][F].
 // No floating-point atomics; every sum has a fixed order.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -35,7 +39,6 @@ constexpr int BN_WAVES = 4;     // waves per block in gate/up
 constexpr int BN_RR = 2;        // output rows per lane group in down
 constexpr int BN_PB = 4;        // list entries per load batch in down
 constexpr int BN_MAXB = 3;      // batches per wave: a token's list has K + S <= 12 entries
-constexpr int BN_SEL_THREADS = 512;
 constexpr int BN_ROUTER_WAVES = 16;  // tokens per router block
 
 // ---------------------------------------------------------------------------
@@ -80,140 +83,6 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_ROUTER_WAVES) bn_router(DecodePar
     }
     const float sum = wave_sum(acc);
     if (lane == 0) p.logits[(size_t)t * p.E + e] = p.bias ? sum + p.bias[e] : sum;
-}
-
-// ---------------------------------------------------------------------------
-// bn_select: one block.  Wave w takes tokens w, w + 8, ...: their top-k (or reads the given
-// routing); the union of routed experts is compacted in ascending order after
-// the shared experts.  Work lists:
-//   work[i]  = {slot, token a, token b (or -1), expert}  for gate/up
-//   pairs[j] = {slot, token, coef bits, expert}         for down
-// meta = {active slots, items, pairs}.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(BN_SEL_THREADS) bn_select(DecodeParams p) {
-    __shared__ float coef[256][MAX_BN_T];  // routed expert x token: summed selection weights
-    __shared__ int sel_e[MAX_BN_T][8];     // token x selection: expert (-1: none)
-    __shared__ float sel_w[MAX_BN_T][8];
-    __shared__ int slot_of[256];               // routed expert -> active slot
-    __shared__ uint32_t emask[256];
-    __shared__ int wcnt[4];
-    __shared__ int act_e[256 + 4];
-    __shared__ uint32_t act_m[256 + 4];
-    __shared__ int n_items_s[256 + 4 + 1];
-    __shared__ int wtot_i[BN_SEL_THREADS / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int T = p.T, K = p.K, E = p.E, S = p.S;
-    if (tid < 256) emask[tid] = 0u;
-    for (int i = tid; i < 256 * MAX_BN_T; i += BN_SEL_THREADS) (&coef[0][0])[i] = 0.f;
-    __syncthreads();
-    for (int t = wave; t < T; t += BN_SEL_THREADS / 64) {
-        int e;
-        float wi;
-        if (p.route_given) {
-            e = lane < K ? p.idx[t * K + lane] : 0;
-            wi = lane < K ? p.w[t * K + lane] : 0.f;
-        } else {
-            wave_topk(p.logits + (size_t)t * E, E, K, &e, &wi);
-            if (lane < K) {
-                p.idx[t * K + lane] = e;
-                p.w[t * K + lane] = wi;
-                if (p.idx_out) p.idx_out[t * K + lane] = e;
-                if (p.w_out) p.w_out[t * K + lane] = wi;
-            }
-        }
-        const bool ok = lane < K && e >= 0 && e < E;  // invalid given indices select nothing
-        if (ok) atomicOr(&emask[e], 1u << t);
-        if (lane < K) {
-            sel_e[t][lane] = ok ? e : -1;
-            sel_w[t][lane] = wi;
-        }
-        // the token's weights per expert, added in selection order (a repeated
-        // given index adds its weights: the expert counted twice)
-        for (int k = 0; k < K; k++) {
-            const int ek = __shfl(e, k, 64);
-            const float wk = __shfl(wi, k, 64);
-            if (lane == 0 && ek >= 0 && ek < E) coef[ek][t] += wk;
-        }
-    }
-    __syncthreads();
-    // compaction of the routed union (threads 0..255 = experts, ascending)
-    const uint32_t m = tid < E ? emask[tid] : 0u;
-    const uint64_t bal = __ballot(m != 0u);
-    if (tid < 256 && lane == 0) wcnt[wave] = __popcll(bal);
-    __syncthreads();
-    int base = 0;
-    for (int w2 = 0; w2 < wave && w2 < 4; w2++) base += wcnt[w2];
-    const int n_routed = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-    const int n_act = S + n_routed;
-    if (tid < 256 && m != 0u) {
-        const int pos = S + base + __popcll(bal & ((1ull << lane) - 1ull));
-        act_e[pos] = tid;
-        act_m[pos] = m;
-        slot_of[tid] = pos;
-    }
-    if (tid < S) {
-        act_e[tid] = E + tid;
-        act_m[tid] = (T >= 32) ? 0xFFFFFFFFu : ((1u << T) - 1u);
-    }
-    __syncthreads();
-    // per-slot gate/up item counts and their exclusive scan (8 waves x 64 slots)
-    const int c_slot = tid < n_act ? __popc(act_m[tid]) : 0;
-    const int ci = (c_slot + 1) / 2;
-    const int inc_i = wave_incl_scan(ci);
-    if (lane == 63) wtot_i[wave] = inc_i;
-    __syncthreads();
-    int off_i = 0, tot_i = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < BN_SEL_THREADS / 64; w2++) {
-        off_i += w2 < wave ? wtot_i[w2] : 0;
-        tot_i += wtot_i[w2];
-    }
-    if (tid < n_act) {
-        n_items_s[tid] = off_i + inc_i - ci;
-        p.act_expert[tid] = act_e[tid];
-        p.act_mask[tid] = act_m[tid];
-    }
-    if (tid == 0) {
-        p.meta[0] = n_act;
-        p.meta[1] = tot_i;
-        p.meta[2] = T * (K + S);
-    }
-    // gate/up items past the last are marked empty (slot -1), so the gate/up
-    // kernel needs no count
-    const int max_items = S * ((T + 1) / 2) + T * K;
-    for (int i = tot_i + tid; i < max_items; i += BN_SEL_THREADS)
-        reinterpret_cast<int4 *>(p.work)[i] = make_int4(-1, 0, 0, 0);
-    // down-projection list per token t: entries t * (K + S) + j = its shared
-    // slots, then its selections in top-k order {slot, t, weight bits, expert};
-    // an invalid given index gives token -1 (adds nothing)
-    for (int i = tid; i < T * (K + S); i += BN_SEL_THREADS) {
-        const int t = i / (K + S), j = i % (K + S);
-        int4 q;
-        if (j < S) {
-            q = make_int4(j, t, __float_as_int(1.f), E + j);
-        } else {
-            const int e = sel_e[t][j - S];
-            q = e < 0 ? make_int4(0, -1, 0, 0) : make_int4(slot_of[e], t, __float_as_int(sel_w[t][j - S]), e);
-        }
-        reinterpret_cast<int4 *>(p.pairs)[i] = q;
-    }
-    // one thread per (slot, token): an even rank among the slot's selected
-    // tokens starts a gate/up item with the slot's next selected token (or none)
-    for (int i = tid; i < n_act * T; i += BN_SEL_THREADS) {
-        const int slot = i / T, t = i % T;
-        const int e = act_e[slot];
-        const uint32_t mk = act_m[slot];
-        const bool on = (mk >> t) & 1u;
-        const float c = !on ? 0.f : slot < S ? 1.f : coef[e][t];
-        p.act_w[slot * T + t] = c;
-        if (!on) continue;
-        const int rank = __popc(mk & ((1u << t) - 1u));
-        if ((rank & 1) == 0) {
-            const uint32_t later = mk & ~((2u << t) - 1u);
-            const int tb = later ? __builtin_ctz(later) : -1;
-            reinterpret_cast<int4 *>(p.work)[n_items_s[slot] + rank / 2] = make_int4(slot, t, tb, e);
-        }
-    }
 }
 
 // h for one work item from weights and x in registers: the wave holds the
@@ -277,13 +146,16 @@ __device__ __forceinline__ void bn_gateup_finish(const DecodeParams &p, const WU
         const int r = k / NT, j = k % NT;
         const float sc = j == 0 ? inv[0] : inv[1];
         const int t = j == 0 ? ta : tb;
-        if (lane == k) p.h[((size_t)slot * p.T + t) * p.F + f0 + r] = silu_mul(red * sc, up * sc);
+        if (lane == k) p.h[((size_t)t * (p.S + p.K) + slot) * p.F + f0 + r] = silu_mul(red * sc, up * sc);
     }
 }
 
 // ---------------------------------------------------------------------------
 // bn_gateup: wave gw -> item gw / (F / RG), features f0 .. f0 + RG - 1.
-// h[(slot * T + t) * F + f] = silu(Wg x_t)[f] * (Wu x_t)[f] for both tokens.
+// Items 0 .. S*ceil(T/2)-1: shared expert s with tokens 2i and 2i+1 (or 2i
+// alone); then item S*ceil(T/2) + K t + j: token t's j-th selection.
+// h[(t * (S + K) + slot) * F + f] = silu(Wg x_t)[f] * (Wu x_t)[f], slot = s
+// for shared expert s, S + j for selection j.
 // Weight loads first; the tokens' x rows go to LDS by contiguous loads of the
 // whole block and are read back per lane unit.
 // ---------------------------------------------------------------------------
@@ -295,9 +167,40 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
     const int per_item = p.F / RG;
     const int gw = blockIdx.x * BN_WAVES + wave;
     const int item = gw / per_item, f0 = (gw % per_item) * RG;
-    const int4 wk = reinterpret_cast<const int4 *>(p.work)[item];
-    if (wk.x < 0) return;  // past the last item
-    const int slot = wk.x, ta = wk.y, tb = wk.z < 0 ? wk.y : wk.z, expert = wk.w;
+    const int pairs = (p.T + 1) / 2, n_shared_items = p.S * pairs;
+    int slot, ta, tb, expert;
+    bool two, sel_wave = false;
+    float sel_lv[4];
+    if (item < n_shared_items) {
+        const int s2 = item / pairs, i = item % pairs;
+        slot = s2;
+        ta = 2 * i;
+        two = 2 * i + 1 < p.T;
+        tb = two ? 2 * i + 1 : ta;
+        expert = p.E + s2;
+    } else {
+        const int r = item - n_shared_items;
+        const int t = r / p.K, j = r % p.K;
+        if (t >= p.T) return;  // past the last item (uniform per block: its waves share the item)
+        slot = p.S + j;
+        ta = tb = t;
+        two = false;
+        if (p.route_given) {
+            expert = p.idx[t * p.K + j];
+            if (expert < 0 || expert >= p.E) return;  // an invalid given index selects nothing
+        } else {
+            float lv[4];
+            wave_topk_load(p.logits + (size_t)t * p.E, p.E, lv);
+            expert = wave_topk_nth(lv, p.E, j);
+            if (j == 0 && f0 == 0) {
+                // the item's first wave also writes token t's full selection
+                // with its weights, for the down kernel and the caller (after
+                // this wave's weight loads below are in flight)
+                sel_wave = true;
+                for (int k = 0; k < 4; k++) sel_lv[k] = lv[k];
+            }
+        }
+    }
     const uint8_t *eb = p.experts + (size_t)expert * p.expert_bytes;
     Mat mg{eb, p.F, p.D, p.tscale ? p.tscale[3 * expert + 0] : 1.f};
     Mat mu{eb + mat_bytes<FMT>(p.F, p.D), p.F, p.D, p.tscale ? p.tscale[3 * expert + 1] : 1.f};
@@ -312,6 +215,17 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
             wg[r][i] = load_unit<FMT>(mg, f0 + r, lane + MOE_WAVE * i);
             wu[r][i] = load_unit<FMT>(mu, f0 + r, lane + MOE_WAVE * i);
         }
+    if (sel_wave) {
+        int es;
+        float wi;
+        wave_topk_regs(sel_lv, p.E, p.K, &es, &wi);
+        if (lane < p.K) {
+            p.idx[ta * p.K + lane] = es;
+            p.w[ta * p.K + lane] = wi;
+            if (p.idx_out) p.idx_out[ta * p.K + lane] = es;
+            if (p.w_out) p.w_out[ta * p.K + lane] = wi;
+        }
+    }
     // the block's waves share the item (F / RG is a multiple of BN_WAVES):
     // its tokens' x rows are loaded once, 1 KB contiguous per wave-wide load
     const int nq = p.D / 4;  // 16-byte chunks per row
@@ -325,9 +239,9 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
         load_x_lds<FMT>(xa[i], xs[0], lane + MOE_WAVE * i);
         load_x_lds<FMT>(xb[i], xs[1], lane + MOE_WAVE * i);
     }
-    // a routed expert usually serves one token of the batch: the second
-    // token's arithmetic only runs for items that have one (uniform branch)
-    if (wk.z >= 0)
+    // the second token's arithmetic only runs for items that have one
+    // (uniform branch)
+    if (two)
         bn_gateup_finish<FMT, UPLD, RG, true>(p, wg, wu, xa, xb, mg.ts, mu.ts, scaled, slot, ta, tb, f0);
     else
         bn_gateup_finish<FMT, UPLD, RG, false>(p, wg, wu, xa, xb, mg.ts, mu.ts, scaled, slot, ta, tb, f0);
@@ -358,11 +272,24 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p
     const int D = p.D, F = p.F;
     const int r0 = blockIdx.x * ROWS + grp * BN_RR;
     const int KS = p.K + p.S;
-    // the token's list, loaded before any weight: lane j loads entry j, then
-    // every entry is read out as wave-uniform (scalar) values where it is used
-    // (no per-lane array of entries: indexed by the batch loop, it would live
-    // in scratch memory)
-    const int4 mine = reinterpret_cast<const int4 *>(p.pairs)[t * KS + min(lane, KS - 1)];
+    // the token's list (its shared slots, then its selections in top-k
+    // order): lane i
+    // holds entry i = {h row, valid, coef bits, expert}; every entry is then
+    // read out as wave-uniform (scalar) values where it is used (no per-lane
+    // array of entries: indexed by the batch loop, it would live in scratch)
+    // (the given routing, or the selection the gate/up kernel wrote)
+    const int es = lane < p.K ? p.idx[t * p.K + lane] : 0;
+    const float wi = lane < p.K ? p.w[t * p.K + lane] : 0.f;
+    int4 mine;
+    {
+        const int j = min(max(lane - p.S, 0), p.K - 1);
+        const int ej = __shfl(es, j, 64);
+        const float wj = __shfl(wi, j, 64);
+        const bool shared = lane < p.S;
+        const bool valid = shared || (ej >= 0 && ej < p.E);
+        mine = make_int4(t * KS + min(lane, KS - 1), valid ? t : -1, __float_as_int(shared ? 1.f : wj),
+                         shared ? p.E + lane : (valid ? ej : 0));
+    }
     auto entry = [&](int i) {
         const int j = min(i, KS - 1);
         return make_int4(__builtin_amdgcn_readlane(mine.x, j), __builtin_amdgcn_readlane(mine.y, j),
@@ -378,11 +305,15 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p
         WUnit wd[BN_PB][BN_RR];
         XUnit<FMT> hv[BN_PB];
         float coef[BN_PB], ts[BN_PB];
+        bool on[BN_PB];
 #pragma unroll
         for (int q = 0; q < BN_PB; q++) {
             const int j = bt * BN_PB + q;
             const int4 pr = entry(j);
-            coef[q] = (j < KS && pr.y >= 0) ? __int_as_float(pr.z) : 0.f;
+            // an entry past the list or of an invalid given index adds nothing
+            // (its h row was never written: selected out, not multiplied by 0)
+            on[q] = j < KS && pr.y >= 0;
+            coef[q] = __int_as_float(pr.z);
             const uint8_t *eb = p.experts + (size_t)pr.w * p.expert_bytes;
             Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, p.tscale ? p.tscale[3 * pr.w + 2] : 1.f};
             ts[q] = md.ts;
@@ -394,7 +325,7 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p
         uint4 hc[BN_PB][HLD];
 #pragma unroll
         for (int q = 0; q < BN_PB; q++) {
-            const uint4 *hsrc = reinterpret_cast<const uint4 *>(p.h + ((size_t)entry(bt * BN_PB + q).x * p.T + t) * F);
+            const uint4 *hsrc = reinterpret_cast<const uint4 *>(p.h + (size_t)entry(bt * BN_PB + q).x * F);
 #pragma unroll
             for (int i = 0; i < HLD; i++) hc[q][i] = hsrc[min(lane + MOE_WAVE * i, HCH - 1)];
         }
@@ -409,7 +340,10 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p
         for (int q = 0; q < BN_PB; q++) {
             load_x_lds<FMT>(hv[q], &hs[tw][q * HCH], sub);
 #pragma unroll
-            for (int r = 0; r < BN_RR; r++) acc[r] += coef[q] * unit_dot<FMT>(wd[q][r], hv[q], ts[q]);
+            for (int r = 0; r < BN_RR; r++) {
+                const float v = acc[r] + coef[q] * unit_dot<FMT>(wd[q][r], hv[q], ts[q]);
+                acc[r] = on[q] ? v : acc[r];
+            }
         }
     }
 #pragma unroll
@@ -425,11 +359,11 @@ hipError_t launch_bn_fmt(const DecodeParams &p, hipStream_t st) {
     constexpr int RG = UPLD == 1 ? 4 : 2;  // features per wave (register budget)
     const int max_items = S * ((p.T + 1) / 2) + p.T * p.K;
     const int waves_g = max_items * (p.F / RG);
-    MOE_LAUNCH(2, (bn_gateup<FMT, UPLD, RG>), dim3((waves_g + BN_WAVES - 1) / BN_WAVES), dim3(MOE_WAVE * BN_WAVES),
+    MOE_LAUNCH(1, (bn_gateup<FMT, UPLD, RG>), dim3((waves_g + BN_WAVES - 1) / BN_WAVES), dim3(MOE_WAVE * BN_WAVES),
                st, p);
     const int rows = (MOE_WAVE / LPR_F) * BN_RR;
     const int tg = (p.T + MAX_DECODE_T - 1) / MAX_DECODE_T;  // token groups of up to 8 waves
-    MOE_LAUNCH(3, (bn_down<FMT, LPR_F>), dim3((p.D + rows - 1) / rows, tg), dim3(MOE_WAVE * min(p.T, MAX_DECODE_T)),
+    MOE_LAUNCH(2, (bn_down<FMT, LPR_F>), dim3((p.D + rows - 1) / rows, tg), dim3(MOE_WAVE * min(p.T, MAX_DECODE_T)),
                st, p);
     return hipGetLastError();
 }
@@ -469,10 +403,9 @@ bool decode_bn_supported(int fmt, int D, int F, int E, int S) {
     return shape && E <= 256 && S <= 4 && D % 512 == 0 && (u == 1 || u == 2 || u == 4 || u == 8);
 }
 
-// Kernel slots: 0 logits, 1 select, 2 gate/up, 3 down.
+// Kernel slots: 0 logits, 1 gate/up, 2 down.
 hipError_t launch_decode_bn(const DecodeParams &p, hipStream_t st) {
     if (p.T < 1 || p.T > MAX_BN_T || p.E > 256 || p.S > 4 || !p.want_shared) return hipErrorNotSupported;
-    if (!p.work || !p.pairs) return hipErrorNotSupported;
     const bool ok = p.fmt == FMT_Q4_1 ? bn_shape_ok<FMT_Q4_1>(p)
                     : p.fmt == FMT_NVFP4 ? bn_shape_ok<FMT_NVFP4>(p)
                                          : bn_shape_ok<FMT_BF16>(p);
@@ -494,7 +427,6 @@ hipError_t launch_decode_bn(const DecodeParams &p, hipStream_t st) {
         }
 #undef BN_ROUTER
     }
-    MOE_LAUNCH(1, bn_select, dim3(1), dim3(BN_SEL_THREADS), st, p);
     if (p.fmt == FMT_Q4_1) return launch_bn_shape<FMT_Q4_1>(p, st);
     if (p.fmt == FMT_NVFP4) return launch_bn_shape<FMT_NVFP4>(p, st);
     return launch_bn_shape<FMT_BF16>(p, st);
