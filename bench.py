@@ -98,6 +98,7 @@ def source_digest(files=("moe_decode_b1.hip", "moe_decode.hip", "moe_device.h", 
     return h.hexdigest()[:16]
 
 
+BN_SOURCES = ("moe_decode_bn.hip", "moe_device.h", "moe_internal.h")
 PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_device.h", "moe_internal.h")
 PERSIST_SOURCES = ("moe_stack_persist.hip", "moe_persist.h", "moe_device.h", "moe_internal.h")
 PS_LAYERS_PER_LAUNCH = 64  # layers per persistent-kernel launch (the library's limit)
@@ -181,7 +182,8 @@ def roofline(workload, dims, T, L, kernel_us, routed_union):
     achieved = algo[dom] / (us * 1e-6) / 1e9
     tr = COUNTER_TRAFFIC.get((workload, dom))
     traffic = None
-    if tr is not None and tr["source_digest"] == source_digest():
+    digest = source_digest(BN_SOURCES) if dom.startswith("bn_") else source_digest()
+    if tr is not None and tr["source_digest"] == digest:
         traffic = tr["fetch_bytes"] + tr["write_bytes"]
     kernels = {k: dict(us_per_launch=round(v, 3), algo_bytes_per_launch=round(algo[k]),
                        gbs=round(algo[k] / (v * 1e-6) / 1e9, 1)) for k, v in kernel_us.items()}
@@ -189,7 +191,8 @@ def roofline(workload, dims, T, L, kernel_us, routed_union):
                 frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                 algo_bytes_per_launch=round(algo[dom]), us_per_launch=round(us, 3),
                 timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream, "
-                       "mean over every launch of the eager timed calls",
+                       "mean over every launch of the timed calls; each call's launches are "
+                       "enqueued behind a stream hold and then run back to back, as in a graph replay",
                 per_kernel=kernels)
 
 

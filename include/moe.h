@@ -135,8 +135,9 @@ moe_status moe_route_topk(const moe_dims *dims, const void *x, int32_t act, int3
  * section "The quantisation recipe is the most transferable part": the
  * weights are 4-bit (q4_1, NVFP4).  For each token
  * y = sum_shared expert_s(x) + sum_i topk_w[i] * expert_{topk_idx[i]}(x),
- * streaming each distinct expert's 4-bit (or bf16) weights once per call and
- * applying it to all tokens that chose it.
+ * reading from HBM only the chosen experts' 4-bit (or bf16) weights, each
+ * distinct expert once per call (repeated reads by further tokens are served
+ * by the caches).
  * 1 <= n_tokens <= 65536: up to 8 tokens (up to 32 when the small-batch
  * kernels fit the shape, see moe_layer_forward) take the decode GEMV path,
  * more take the grouped GEMM of moe_layer_forward_prefill.
@@ -158,7 +159,9 @@ moe_status moe_expert_ffn_q4(const moe_dims *dims, const void *x, int32_t act, i
 /*
  * Whole layer: route + expert FFN, as defined by moe_route_topk and
  * moe_expert_ffn_q4 (same page and section).  n_tokens <= 8 takes a decode path
- * (grouped GEMV over the union of chosen experts), and so does n_tokens <= 32
+ * (GEMV kernels that stream only the chosen experts' weights; an expert chosen
+ * by several tokens comes from HBM once, its other reads from cache), and so
+ * does n_tokens <= 32
  * when the small-batch kernels fit the shape (d_model 2048 or 4096 with
  * 4-bit weights, 512 or 1024 with bf16; d_ff of 16 or 32 blocks, a multiple
  * of 64; at least one shared expert); larger n_tokens take the prefill path

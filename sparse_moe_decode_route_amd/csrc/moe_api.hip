@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -258,6 +259,67 @@ moe_status persistent_impl(const moe_dims &d, int n_layers, const moe_layer_weig
     return ok();
 }
 
+// ---- launch gate of the timed entry points ----
+// The host enqueues event-bracketed launches more slowly than the GPU runs
+// them; left alone, every timed kernel would start after an idle gap that a
+// graph replay of the same launches does not have.  A one-wave kernel holds
+// the stream until the host has enqueued every timed launch behind it, so
+// that they then run back to back.  Its wait is bounded: it ends by itself
+// after GATE_MAX_TICKS of the 100 MHz real-time counter (0.2 s), so a store
+// that never arrives only delays the timed kernels.
+
+constexpr uint64_t GATE_MAX_TICKS = 20000000ull;
+
+__global__ void __launch_bounds__(64) hold_stream(uint32_t *flag, uint32_t seq, uint64_t max_ticks) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while ((int32_t)(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) - seq) < 0 &&
+           __builtin_amdgcn_s_memrealtime() - t0 < max_ticks)
+        __builtin_amdgcn_s_sleep(16);
+}
+
+// One gated timing call at a time per process: the flag word (pinned,
+// host-coherent, kept until the process ends) only ever grows.
+std::mutex g_gate_mu;
+uint32_t *g_gate_host = nullptr;
+uint32_t *g_gate_dev = nullptr;
+uint32_t g_gate_seq = 0;
+
+class StreamGate {
+  public:
+    // Enqueues the hold on st; without a flag word (allocation refused) the
+    // timed launches run ungated.
+    explicit StreamGate(hipStream_t st) : lk_(g_gate_mu) {
+        if (!g_gate_host) {
+            void *h = nullptr, *dptr = nullptr;
+            if (hipHostMalloc(&h, 256, hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess) {
+                (void)hipGetLastError();
+                return;
+            }
+            if (hipHostGetDevicePointer(&dptr, h, 0) != hipSuccess) {
+                (void)hipGetLastError();
+                (void)hipHostFree(h);
+                return;
+            }
+            g_gate_host = static_cast<uint32_t *>(h);
+            g_gate_dev = static_cast<uint32_t *>(dptr);
+            __atomic_store_n(g_gate_host, g_gate_seq, __ATOMIC_RELEASE);
+        }
+        seq_ = ++g_gate_seq;
+        hipLaunchKernelGGL(hold_stream, dim3(1), dim3(64), 0, st, g_gate_dev, seq_, GATE_MAX_TICKS);
+        if (hipGetLastError() != hipSuccess) seq_ = 0;
+    }
+    // Lets the held stream run (idempotent).
+    void release() {
+        if (seq_) __atomic_store_n(g_gate_host, seq_, __ATOMIC_RELEASE);
+        seq_ = 0;
+    }
+    ~StreamGate() { release(); }
+
+  private:
+    std::lock_guard<std::mutex> lk_;
+    uint32_t seq_ = 0;
+};
+
 }  // namespace
 
 moe_status moe::set_error(moe_status s, const std::string &msg) { return fail(s, msg); }
@@ -414,9 +476,9 @@ moe_status moe_layer_forward(const moe_dims *d, const moe_layer_weights *w, cons
     return hip_status(launch_any(p, st), "layer launch");
 }
 
-static moe_status prefill_impl(const moe_dims *d, const moe_layer_weights *w, const void *x, int32_t act,
-                               int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws,
-                               size_t ws_bytes, hipStream_t st, hipEvent_t *ev) {
+static moe_status prefill_check(const moe_dims *d, const moe_layer_weights *w, const void *x, int32_t act,
+                                int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                                size_t ws_bytes) {
     MOE_TRY(check_dims(d));
     if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown activation type");
     if (n_tokens < 1 || n_tokens > 65536) return fail(MOE_ERR_INVALID_ARG, "n_tokens must be in [1, 65536]");
@@ -427,7 +489,13 @@ static moe_status prefill_impl(const moe_dims *d, const moe_layer_weights *w, co
     MOE_TRY(check_ptr(y, "y"));
     MOE_TRY(check_ptr(topk_idx_out, "topk_idx_out", false));
     MOE_TRY(check_ptr(topk_w_out, "topk_w_out", false));
-    MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
+    return check_ws(d, n_tokens, ws, ws_bytes);
+}
+
+static moe_status prefill_impl(const moe_dims *d, const moe_layer_weights *w, const void *x, int32_t act,
+                               int32_t n_tokens, float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                               size_t ws_bytes, hipStream_t st, hipEvent_t *ev) {
+    MOE_TRY(prefill_check(d, w, x, act, n_tokens, y, topk_idx_out, topk_w_out, ws, ws_bytes));
     moe::PrefillArgs a = prefill_args(*d, x, act, n_tokens, ws);
     a.router = static_cast<const uint16_t *>(w->router);
     a.bias = w->router_bias;
@@ -453,9 +521,8 @@ namespace {
 
 // Shared body of the stack entry points; ev (optional) holds
 // n_layers * 2 * MAX_KERNEL_SLOTS events, *path receives the decode path.
-moe_status stack_impl(const moe_dims *d, int32_t n_layers, const moe_layer_weights *layers, const float *x0,
-                      int32_t n_tokens, float *y, float *y_trace, int32_t *idx_trace, void *ws, size_t ws_bytes,
-                      hipStream_t st, hipEvent_t *ev, int *path) {
+moe_status stack_check(const moe_dims *d, int32_t n_layers, const moe_layer_weights *layers, const float *x0,
+                       int32_t n_tokens, float *y, float *y_trace, int32_t *idx_trace, void *ws, size_t ws_bytes) {
     MOE_TRY(check_dims(d));
     if (n_layers < 1) return fail(MOE_ERR_INVALID_ARG, "n_layers must be >= 1");
     if (n_tokens < 1 || n_tokens > moe::MAX_DECODE_T)
@@ -466,7 +533,13 @@ moe_status stack_impl(const moe_dims *d, int32_t n_layers, const moe_layer_weigh
     MOE_TRY(check_ptr(y, "y"));
     MOE_TRY(check_ptr(y_trace, "y_trace", false));
     MOE_TRY(check_ptr(idx_trace, "idx_trace", false));
-    MOE_TRY(check_ws(d, n_tokens, ws, ws_bytes));
+    return check_ws(d, n_tokens, ws, ws_bytes);
+}
+
+moe_status stack_impl(const moe_dims *d, int32_t n_layers, const moe_layer_weights *layers, const float *x0,
+                      int32_t n_tokens, float *y, float *y_trace, int32_t *idx_trace, void *ws, size_t ws_bytes,
+                      hipStream_t st, hipEvent_t *ev, int *path) {
+    MOE_TRY(stack_check(d, n_layers, layers, x0, n_tokens, y, y_trace, idx_trace, ws, ws_bytes));
     const DecodeWs L = decode_ws(*d, n_tokens);
     if (use_persistent(*d, n_tokens)) {
         if (path) *path = 4;
@@ -520,6 +593,7 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
                                   size_t names_cap, void *stream) {
     if (!kernel_us || !n_kernels) return fail(MOE_ERR_INVALID_ARG, "kernel_us / n_kernels is NULL");
     if (n_layers < 1 || n_layers > 4096) return fail(MOE_ERR_INVALID_ARG, "n_layers must be in [1, 4096]");
+    MOE_TRY(stack_check(d, n_layers, layers, x0, n_tokens, y, nullptr, idx_trace, ws, ws_bytes));
     hipStream_t st = static_cast<hipStream_t>(stream);
     const size_t n_ev = (size_t)n_layers * 2 * moe::MAX_KERNEL_SLOTS;
     std::vector<hipEvent_t> ev(n_ev, nullptr);
@@ -534,8 +608,10 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
         }
     }
     int path = 0;
+    StreamGate gate(st);
     moe_status s = stack_impl(d, n_layers, layers, x0, n_tokens, y, nullptr, idx_trace, ws, ws_bytes, st,
                               ev.data(), &path);
+    gate.release();
     if (s == MOE_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(MOE_ERR_HIP, "stream synchronize failed");
     if (s != MOE_OK) {
         destroy();
@@ -589,6 +665,7 @@ moe_status moe_layer_forward_prefill_timed(const moe_dims *d, const moe_layer_we
                                            int32_t n_tokens, float *y, void *ws, size_t ws_bytes, float *kernel_us,
                                            int32_t *n_kernels, char *names, size_t names_cap, void *stream) {
     if (!kernel_us || !n_kernels) return fail(MOE_ERR_INVALID_ARG, "kernel_us / n_kernels is NULL");
+    MOE_TRY(prefill_check(d, w, x, act, n_tokens, y, nullptr, nullptr, ws, ws_bytes));
     hipEvent_t ev[2 * moe::PREFILL_SLOTS] = {};
     for (auto &e : ev) {
         if (hipEventCreate(&e) != hipSuccess) {
@@ -597,8 +674,10 @@ moe_status moe_layer_forward_prefill_timed(const moe_dims *d, const moe_layer_we
             return fail(MOE_ERR_HIP, "hipEventCreate failed");
         }
     }
+    StreamGate gate(static_cast<hipStream_t>(stream));
     moe_status s = prefill_impl(d, w, x, act, n_tokens, y, nullptr, nullptr, ws, ws_bytes,
                                 static_cast<hipStream_t>(stream), ev);
+    gate.release();
     if (s == MOE_OK && hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
         s = fail(MOE_ERR_HIP, "stream synchronize failed");
     if (s == MOE_OK) {
@@ -861,7 +940,9 @@ moe_status moe_attn_decode_timed(const moe_attn_dims *d, int32_t n_seqs, int32_t
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     a.ev = ev;
+    StreamGate gate(st);
     moe_status s = hip_status(moe::launch_attn(a, st), "attention launch");
+    gate.release();
     if (s == MOE_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(MOE_ERR_HIP, "stream synchronize failed");
     if (s == MOE_OK) {
         for (int k = 0; k < 2; k++) {

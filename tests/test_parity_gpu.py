@@ -261,6 +261,25 @@ def test_stack_graph_replays_match_eager():
         assert torch.equal(got, ref), i
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_stack_timed_matches_plain(T):
+    """The timed stack entry (launches held behind a stream gate, then run back
+    to back) computes exactly what the plain entry computes, and times every
+    kernel of the path."""
+    dims = gen.LayerDims(1024, 256, n_routed=32, n_shared=1, top_k=6, wfmt="q4_1")
+    devs = [_layer(dims, 45, layer=l)[1] for l in range(3)]
+    stack = B.StackHandle(devs)
+    x = gen.make_hidden(45, T, 1024, draw=7, device=_dev())
+    ws = B.workspace(dims, T)
+    ref, _, ritr = B.stack_decode(stack, x, ws=ws, trace=True)
+    torch.cuda.synchronize()
+    ref, ritr = ref.clone(), ritr.clone()
+    for _ in range(2):
+        y, itr, us = B.stack_decode_timed(stack, x, ws=ws, trace=True)
+        assert torch.equal(y, ref) and torch.equal(itr, ritr)
+        assert len(us) in (3, 4) and all(v > 0 for v in us.values()), us  # 4 on the general path
+
+
 # --------------------------------------------------------------------------- small-batch path (2-8 tokens)
 
 @pytest.mark.parametrize("dims,T", [

@@ -170,6 +170,17 @@ def test_prefill_deterministic():
     assert torch.equal(y1, y2) and torch.equal(i1, i2) and torch.equal(w1, w2)
 
 
+def test_prefill_timed_matches_plain():
+    dims = gen.LayerDims(256, 128, n_routed=64, n_shared=1, top_k=6, wfmt="q4_1")
+    host, dev = _layer(dims, cfg_id=22)
+    x = _x(300, 256, draw=2, bf16=True).to(_dev())
+    y1, _, _ = B.layer_forward(dev, x, prefill=True)
+    y2, us = B.layer_forward_prefill_timed(dev, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert len(us) == 7 and all(v > 0 for v in us.values()), us
+
+
 def test_route_topk_many_tokens():
     dims = gen.WORKLOADS["c2_layer_q4_1"]["dims"]
     host, dev = _layer(dims, cfg_id=5, zipf_s=1.1)
