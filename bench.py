@@ -51,6 +51,9 @@ def parse():
                     help="eager stack calls with per-kernel dispatch events (the roofline's kernel timing)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy five times (reference kernel for HBM counters)")
+    ap.add_argument("--rocprof-summary", metavar="CSV",
+                    help="summarise a rocprofv3 kernel_trace.csv or counter_collection.csv of this script per "
+                         "kernel, split at the first timed call (needs no GPU), and exit")
     return ap.parse_args()
 
 
@@ -789,8 +792,63 @@ def bench_attn(args, kind: str):
     )
 
 
+def _short_kernel_name(name: str) -> str:
+    """Kernel name without return type, namespaces and argument list."""
+    n = name.replace("void ", "").replace("moe::", "").replace("(anonymous namespace)::", "")
+    depth, out = 0, []
+    for ch in n:
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            break
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def _stats(v):
+    v = np.asarray(v, dtype=np.float64)
+    if v.size == 0:
+        return None
+    return dict(n=int(v.size), mean=round(float(v.mean()), 4), p10=round(float(np.percentile(v, 10)), 4),
+                p50=round(float(np.percentile(v, 50)), 4), p90=round(float(np.percentile(v, 90)), 4))
+
+
+def rocprof_summary(path: str) -> dict:
+    """Per-kernel summary of a rocprofv3 CSV written while this script ran.
+
+    Dispatches are split at the first hold_stream dispatch: before it, the
+    graph replays (and the untimed eager calls); from it on, the timed calls,
+    whose launches were enqueued behind the hold and ran back to back.  A
+    kernel_trace.csv gives durations in microseconds; a counter_collection.csv
+    gives each counter's value per dispatch."""
+    import csv
+    with open(path) as f:
+        rows = list(csv.DictReader(f))
+    counters = "Counter_Name" in (rows[0] if rows else {})
+    disp = {}
+    for r in rows:
+        d = disp.setdefault(int(r["Dispatch_Id"]), dict(k=_short_kernel_name(r["Kernel_Name"]),
+                                                        s=int(r["Start_Timestamp"]), e=int(r["End_Timestamp"]),
+                                                        c={}))
+        if counters:
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ds = sorted(disp.values(), key=lambda d: d["s"])
+    first_hold = next((d["s"] for d in ds if d["k"] == "hold_stream"), None)
+    per = {}
+    for d in ds:
+        ph = "graph" if first_hold is None or d["s"] < first_hold else "timed"
+        vals = d["c"] if counters else {"duration_us": (d["e"] - d["s"]) / 1e3}
+        for c, v in vals.items():
+            per.setdefault(d["k"], {}).setdefault(c, {"graph": [], "timed": []})[ph].append(v)
+    return {k: {c: dict(all=_stats(v["graph"] + v["timed"]), graph=_stats(v["graph"]), timed=_stats(v["timed"]))
+                for c, v in cs.items()} for k, cs in per.items()}
+
+
 def main():
     args = parse()
+    if args.rocprof_summary:
+        print(json.dumps(rocprof_summary(args.rocprof_summary), indent=1))
+        return
     if args.gpus != 1:
         print(json.dumps(dict(error=f"this build runs on one GPU only; --gpus {args.gpus} is not supported")))
         sys.exit(2)

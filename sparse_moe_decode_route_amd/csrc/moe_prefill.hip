@@ -750,6 +750,89 @@ __device__ __forceinline__ void pf_epilogue(const PfParams &p, const PfTile &til
     }
 }
 
+// pf_epilogue through LDS, for tiles of up to 128 rows: each wave writes its
+// results (the same fp32 arithmetic and fp16 rounding as pf_epilogue) to an
+// 8 KB LDS region of its own, token-major, and reads them back so that every
+// global store of a lane covers 16 contiguous bytes of one token's row and a
+// wave's store covers whole 64- or 128-byte row segments.  Stored directly
+// from the accumulator layout, one store instruction touches 32 rows of 16
+// bytes each, and the address unit's cost of those stores dominated the end
+// of every block.  The caller has waited for its copies into the region and
+// passed a workgroup barrier after the main loop's last reads of it.
+//   MODE 0: region [128 tokens][64 B]: the wave's 32 features of h; 16-byte
+//           chunk c of row t at slot c ^ ((t >> 2) & 3)
+//   MODE 1: region [64 tokens][128 B]: the wave's 64 output rows of O for
+//           token blocks 2 hb, 2 hb + 1 (two halves); chunk c of row t at
+//           slot c ^ (t & 7)
+template <int MODE>
+__device__ __forceinline__ void pf_epilogue_lds(const PfParams &p, const PfTile &tile, const f32x16_t (&acc)[2][4],
+                                                int r0, const bool (&sub_ok)[2], int g, int l32, int lane,
+                                                uint4 *region) {
+    uint8_t *rb = reinterpret_cast<uint8_t *>(region);
+    if (MODE == 0) {
+        if (!sub_ok[0]) return;
+        const float ts_g = p.tscale ? p.tscale[3 * tile.e + 0] : 1.f;
+        const float ts_u = p.tscale ? p.tscale[3 * tile.e + 1] : 1.f;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int t = 32 * b + l32;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                uint32_t pk[2];
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    const float g0 = acc[0][b][4 * q + 2 * i] * ts_g, u0 = acc[1][b][4 * q + 2 * i] * ts_u;
+                    const float g1 = acc[0][b][4 * q + 2 * i + 1] * ts_g, u1 = acc[1][b][4 * q + 2 * i + 1] * ts_u;
+                    const _Float16 h0 = (_Float16)silu_mul(g0, u0), h1 = (_Float16)silu_mul(g1, u1);
+                    pk[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                }
+                if (t < tile.rows)
+                    *reinterpret_cast<uint2 *>(rb + t * 64 + 16 * (q ^ ((t >> 2) & 3)) + 8 * g) = make_uint2(pk[0], pk[1]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int t = 16 * i + (lane >> 2), c = lane & 3;
+            if (t < tile.rows) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(rb + t * 64 + 16 * (c ^ ((t >> 2) & 3)));
+                *reinterpret_cast<uint4 *>(p.h + (size_t)(tile.row0 + t) * p.F + r0 + 8 * c) = v;
+            }
+        }
+    } else {
+        const float ts_d = p.tscale ? p.tscale[3 * tile.e + 2] : 1.f;
+        const int ROWS_A = p.D;
+#pragma unroll
+        for (int hb = 0; hb < 2; hb++) {
+#pragma unroll
+            for (int bb = 0; bb < 2; bb++) {
+                const int b = 2 * hb + bb, n = 32 * b + l32, t = 32 * bb + l32;
+                if (n >= tile.rows) continue;
+                const float c = p.perm_w[tile.row0 + n] * ts_d;
+#pragma unroll
+                for (int a = 0; a < 2; a++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const half2_t v01 = {(_Float16)(acc[a][b][4 * q + 0] * c), (_Float16)(acc[a][b][4 * q + 1] * c)};
+                        const half2_t v23 = {(_Float16)(acc[a][b][4 * q + 2] * c), (_Float16)(acc[a][b][4 * q + 3] * c)};
+                        *reinterpret_cast<uint2 *>(rb + t * 128 + 16 * ((4 * a + q) ^ (t & 7)) + 8 * g) =
+                            make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
+                    }
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int t = 8 * i + (lane >> 3), c = lane & 7, n = 64 * hb + t;
+                if (n < tile.rows && r0 + 8 * c < ROWS_A) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(rb + t * 128 + 16 * (c ^ (t & 7)));
+                    *reinterpret_cast<uint4 *>(p.o + (size_t)(tile.row0 + n) * p.D + r0 + 8 * c) = v;
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
 #endif  // __HIP_DEVICE_COMPILE__ (helpers of pf_gemm)
 
 // ---------------------------------------------------------------------------
@@ -1111,7 +1194,15 @@ _Pragma("unroll")                                                               
 #undef PQ_ISSUE_W2
 #undef PQ_ISSUE_X
 #undef PQ_READ_SC
-    pf_epilogue<MODE, NBLK>(p, tile, acc, r0, sub_ok, g, l32);
+    if constexpr (BM == 128) {
+        // the stages are free once every copy has landed and every wave is
+        // past its last step; wave w then takes token stage w as its region
+        wait_vmcnt<0>();
+        __syncthreads();
+        pf_epilogue_lds<MODE>(p, tile, acc, r0, sub_ok, g, l32, lane, PQ_XST(wave));
+    } else {
+        pf_epilogue<MODE, NBLK>(p, tile, acc, r0, sub_ok, g, l32);
+    }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 #undef PQ_XST

@@ -160,6 +160,41 @@ def test_prefill_4096_tokens_sampled():
     print(f"experts hit {np.count_nonzero(loads)}, max load {loads.max()}, min nonzero {loads[loads > 0].min()}")
 
 
+def test_prefill_maximum_tokens_sampled():
+    # the largest call the prefill path accepts, 65,536 bf16 tokens through the
+    # full q4_1 layer (Zipf(1.1) router prior): routing checked on every
+    # token, outputs on sampled tile boundaries and rows
+    dims = gen.WORKLOADS["c5_prefill_q4_1"]["dims"]
+    host, dev = _layer(dims, cfg_id=5, zipf_s=1.1)
+    T = 65536
+    x = _x(T, dims.d_model, draw=65, bf16=True)
+    y, idx, w = B.layer_forward(dev, x.to(_dev()), prefill=True)
+    torch.cuda.synchronize()
+    y, idx, w = y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    x64 = _x64(x)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=16) as ex:  # the oracle's C releases the interpreter lock
+        logits = np.concatenate(list(ex.map(lambda c: oracle.router_logits(host, c), np.array_split(x64, 64))))
+    oi = np.zeros((T, dims.top_k), dtype=np.int32)
+    ow = np.zeros((T, dims.top_k))
+    for t in range(T):
+        oi[t], ow[t], _ = oracle.route(dims, logits[t])
+    band = router_band_mfma(x64, _router64(host), False)
+    n_exact, n_amb = check_routing(idx, w, logits, oi, ow, band)
+    # outputs: the first and last row of 512 of the ~3,800 tiles (drawn at
+    # random, the shared expert's first and last tiles always), plus 64
+    # random rows
+    bnd = _tile_boundary_rows(idx, dims.n_routed, dims.n_shared, step=128)
+    rng = np.random.default_rng(1)
+    rows = np.union1d(rng.choice(bnd, min(1024, len(bnd)), replace=False),
+                      np.concatenate([rng.choice(T, 64, replace=False), [0, 127, T - 128, T - 1]]))
+    oy = _oracle_rows_parallel(host, x64, idx, w, rows, workers=16)
+    err = rel_l2(y[rows], oy)
+    print(f"[prefill max] T={T} exact={n_exact} ambiguous={n_amb} checked rows={len(rows)} "
+          f"max rel-L2 {err.max():.3e}")
+    assert np.all(err <= REL_L2_TOL) and err.max() <= FP16_PATH_GUARD, err.max()
+
+
 def test_prefill_deterministic():
     dims = gen.LayerDims(256, 128, n_routed=64, n_shared=1, top_k=6, wfmt="q4_1")
     host, dev = _layer(dims, cfg_id=22)
