@@ -701,6 +701,13 @@ __device__ __forceinline__ void rg_issue(const RgDma &d, uint4 *xs, uint4 *rs, i
 // the wave's row group a, m = 8 (j/4) + 4 g + j%4, n = 32 b + l32.
 //   MODE 0: h = silu(gate) * up (gate in a = 0, up in a = 1), fp16 rows of H
 //   MODE 1: O = coef * acc, fp16 rows of O
+// silu(g) * u for the fp16 h of the grouped GEMM: the reciprocal instruction
+// (within 1 ulp) in place of an IEEE division, whose correction steps cost
+// several times more; the result is rounded to fp16 (2^-11) right after.
+__device__ __forceinline__ float silu_mul_h(float g, float u) {
+    return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
 template <int MODE, int NBLK>
 __device__ __forceinline__ void pf_epilogue(const PfParams &p, const PfTile &tile, const f32x16_t (&acc)[2][NBLK], int r0,
                                             const bool (&sub_ok)[2], int g, int l32) {
@@ -720,7 +727,7 @@ __device__ __forceinline__ void pf_epilogue(const PfParams &p, const PfTile &til
                 for (int i = 0; i < 2; i++) {
                     const float g0 = acc[0][b][4 * q + 2 * i] * ts_g, u0 = acc[1][b][4 * q + 2 * i] * ts_u;
                     const float g1 = acc[0][b][4 * q + 2 * i + 1] * ts_g, u1 = acc[1][b][4 * q + 2 * i + 1] * ts_u;
-                    const _Float16 h0 = (_Float16)silu_mul(g0, u0), h1 = (_Float16)silu_mul(g1, u1);
+                    const _Float16 h0 = (_Float16)silu_mul_h(g0, u0), h1 = (_Float16)silu_mul_h(g1, u1);
                     pk[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
                 }
                 *reinterpret_cast<uint2 *>(hrow + 8 * q) = make_uint2(pk[0], pk[1]);
@@ -783,7 +790,7 @@ __device__ __forceinline__ void pf_epilogue_lds(const PfParams &p, const PfTile 
                 for (int i = 0; i < 2; i++) {
                     const float g0 = acc[0][b][4 * q + 2 * i] * ts_g, u0 = acc[1][b][4 * q + 2 * i] * ts_u;
                     const float g1 = acc[0][b][4 * q + 2 * i + 1] * ts_g, u1 = acc[1][b][4 * q + 2 * i + 1] * ts_u;
-                    const _Float16 h0 = (_Float16)silu_mul(g0, u0), h1 = (_Float16)silu_mul(g1, u1);
+                    const _Float16 h0 = (_Float16)silu_mul_h(g0, u0), h1 = (_Float16)silu_mul_h(g1, u1);
                     pk[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
                 }
                 if (t < tile.rows)
