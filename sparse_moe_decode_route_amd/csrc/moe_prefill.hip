@@ -393,12 +393,17 @@ __global__ void __launch_bounds__(PF_SCAN_THREADS) pf_scan(PfParams p) {
         for (int i = 0; i < EPW; i++) carry[i] = 0;
         for (int w0 = 0; w0 < p.NW; w0 += 64) {
             const int w = w0 + lane;
-            int c[EPW];
+            // every load issued before the first use, from clamped indices
+            // (a load under a condition gets a wait of its own)
+            unsigned long long mw[EPW];
 #pragma unroll
             for (int i = 0; i < EPW; i++) {
-                const int e = e0 + 16 * i;
-                c[i] = (e < p.E && w < p.NW) ? __popcll(p.mask[(uint32_t)(e * p.NW + w)]) : 0;
+                const int e = min(e0 + 16 * i, p.E - 1);
+                mw[i] = p.mask[(uint32_t)(e * p.NW + min(w, p.NW - 1))];
             }
+            int c[EPW];
+#pragma unroll
+            for (int i = 0; i < EPW; i++) c[i] = (e0 + 16 * i < p.E && w < p.NW) ? __popcll(mw[i]) : 0;
 #pragma unroll
             for (int i = 0; i < EPW; i++) {
                 const int e = e0 + 16 * i;
@@ -458,13 +463,25 @@ __global__ void __launch_bounds__(PF_THREADS) pf_scatter(PfParams p) {
     int r;
     float wt;
     if (j < p.K) {
+        // the token's whole index and weight rows in one round trip (top_k <= 8)
         const int32_t *ti = p.idx + (size_t)t * p.K;
-        const int e = ti[j];
+        const float *tw = p.w + (size_t)t * p.K;
+        int32_t tk[8];
+        float wk[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            tk[k] = ti[min(k, p.K - 1)];
+            wk[k] = tw[min(k, p.K - 1)];
+        }
+        int e = tk[0];
+#pragma unroll
+        for (int k = 1; k < 8; k++) e = k == j ? tk[k] : e;
         // caller routing may hold invalid indices (no row) or repeat an index:
         // the token's first slot naming e owns the row and carries the weights
         // of all its slots naming e, added in slot order; later ones get none
         bool first = e >= 0 && e < p.E;
-        for (int k = 0; k < j; k++) first = first && ti[k] != e;
+#pragma unroll
+        for (int k = 0; k < 8; k++) first = first && !(k < j && tk[k] == e);
         if (!first) {
             p.pos[i] = -1;
             return;
@@ -472,9 +489,9 @@ __global__ void __launch_bounds__(PF_THREADS) pf_scatter(PfParams p) {
         const size_t mi = (size_t)e * p.NW + (t >> 6);
         const unsigned long long below = (t & 63) ? ((1ull << (t & 63)) - 1ull) : 0ull;
         r = p.off[e] + p.wp[mi] + __popcll(p.mask[mi] & below);
-        const float *tw = p.w + (size_t)t * p.K;
-        wt = tw[j];
-        for (int k = j + 1; k < p.K; k++) wt += ti[k] == e ? tw[k] : 0.f;
+        wt = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; k++) wt += (k >= j && k < p.K && tk[k] == e) ? wk[k] : 0.f;
     } else {
         r = p.off[p.E + j - p.K] + t;
         wt = 1.f;
