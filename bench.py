@@ -113,26 +113,56 @@ ATTN_SOURCES = ("moe_attn.hip", "moe_device.h", "moe_internal.h")
 # script (one run per counter), each scaled by the same counter's reading for a
 # plain device copy of known size; keyed by (workload, kernel) and valid only for
 # the kernel source digest it was taken on.
-_FETCH_SCALE = 262144.0 / 131085.2  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
+_FETCH_SCALE = 262144.0 / 131083.5  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
 _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE KiB
-# MFMA utilisation of the prefill gate/up GEMM read from a rocprofv3 --pmc run
-# (SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE per dispatch); None until taken
-# on the current sources.
+# Matrix-core counters of the prefill GEMMs, per dispatch, from a rocprofv3
+# --pmc run of this script (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE,
+# SQ_INSTS_VALU_MFMA_MOPS_F16); valid only for the source digest they were
+# taken on.  The SQ counters sum over the chip's 1024 SIMDs (256 CUs x 4) and
+# GRBM_GUI_ACTIVE over its 8 XCDs, so utilisation = (busy / 1024) / (active / 8);
+# one MOP is 512 FLOPs of work issued to the matrix cores.
 PREFILL_MFMA_COUNTERS = None
 
+
+def prefill_mfma_counters(fl_gu: float, fl_dn: float):
+    """Counter-based MFMA utilisation of the two prefill GEMMs, or None when the
+    stored counters were taken on other kernel sources."""
+    c = PREFILL_MFMA_COUNTERS
+    if c is None or c["source_digest"] != source_digest(PREFILL_SOURCES):
+        return None
+    out = {}
+    for k, fl in (("pf_gemm_gateup", fl_gu), ("pf_gemm_down", fl_dn)):
+        v = c[k]
+        active = v["GRBM_GUI_ACTIVE"] / 8.0
+        out[k] = dict(mfma_busy_frac=round(v["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0 / active, 4),
+                      issued_flops=round(v["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512),
+                      algorithmic_flops=fl, padding_overhead=round(v["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / fl - 1, 4),
+                      clock_ghz=round(active / (v["duration_us"] * 1e3), 3), gui_active_cycles_per_xcd=round(active),
+                      counters=v)
+    return out
+
+
+def _traffic(digest: str, fetch_kib: float, write_kib: float) -> dict:
+    """A kernel's stored counter readings (KiB per dispatch, mean over the run) as bytes."""
+    return dict(source_digest=digest, fetch_bytes=round(fetch_kib * _FETCH_SCALE * 1024),
+                write_bytes=round(write_kib * _WRITE_SCALE * 1024))
+
+
 COUNTER_TRAFFIC = {
-    ("stack_q4_1_b1", "b1_topk_gateup"): dict(source_digest="a6637c8f6f343668",
-                                              fetch_bytes=round(3936.8 * _FETCH_SCALE * 1024),
-                                              write_bytes=round(12.7 * _WRITE_SCALE * 1024)),
-    ("prefill_q4_1", "pf_gemm_gateup"): dict(source_digest="9bc236c0b4662e31",
-                                             fetch_bytes=round(227174.8 * _FETCH_SCALE * 1024),
-                                             write_bytes=round(28694.4 * _WRITE_SCALE * 1024)),
-    ("lm_head_q4_1_t1", "lm_head_kernel"): dict(source_digest="676ef36934408841",
-                                                fetch_bytes=round(91654.2 * _FETCH_SCALE * 1024),
-                                                write_bytes=round(572.2 * _WRITE_SCALE * 1024)),
-    ("attn_full128k", "attn_chunk"): dict(source_digest="6e7dd54d40665ef8",
-                                          fetch_bytes=round(131357.2 * _FETCH_SCALE * 1024),
-                                          write_bytes=round(2306.0 * _WRITE_SCALE * 1024)),
+    # batch-1 q4_1 stack
+    ("stack_q4_1_b1", "b1_route_shared"): _traffic("2210e5c88176d58b", 1233.1659, 24.0),
+    ("stack_q4_1_b1", "b1_topk_gateup"): _traffic("2210e5c88176d58b", 3937.0461, 12.6691),
+    ("stack_q4_1_b1", "b1_down"): _traffic("2210e5c88176d58b", 2323.0305, 8.0),
+    # batch-8 NVFP4 stack
+    ("stack_nvfp4_b8", "bn_router"): _traffic("3f7cb9a941f7e6bf", 788.5061, 64.0),
+    ("stack_nvfp4_b8", "bn_gateup"): _traffic("3f7cb9a941f7e6bf", 26672.5574, 112.4276),
+    ("stack_nvfp4_b8", "bn_down"): _traffic("3f7cb9a941f7e6bf", 13565.2427, 64.0),
+    # 4096-token q4_1 prefill
+    ("prefill_q4_1", "pf_gemm_gateup"): _traffic("9bc236c0b4662e31", 227174.8, 28694.4),
+    # q4_1 output layer, 1 token
+    ("lm_head_q4_1_t1", "lm_head_kernel"): _traffic("73c3554f2833a25f", 91654.1802, 572.2188),
+    # full-attention layer at 128k positions
+    ("attn_full128k", "attn_chunk"): _traffic("2c11e0abd4e859cc", 131378.4219, 2306.0),
 }
 
 
@@ -183,13 +213,15 @@ def roofline(workload, dims, T, L, kernel_us, routed_union):
     dom = max(kernel_us, key=lambda k: kernel_us[k])
     us = kernel_us[dom]
     achieved = algo[dom] / (us * 1e-6) / 1e9
-    tr = COUNTER_TRAFFIC.get((workload, dom))
-    traffic = None
-    digest = source_digest(BN_SOURCES) if dom.startswith("bn_") else source_digest()
-    if tr is not None and tr["source_digest"] == digest:
-        traffic = tr["fetch_bytes"] + tr["write_bytes"]
+    def traffic_of(k):
+        tr = COUNTER_TRAFFIC.get((workload, k))
+        digest = source_digest(BN_SOURCES) if k.startswith("bn_") else source_digest()
+        return tr["fetch_bytes"] + tr["write_bytes"] if tr is not None and tr["source_digest"] == digest else None
+
+    traffic = traffic_of(dom)
     kernels = {k: dict(us_per_launch=round(v, 3), algo_bytes_per_launch=round(algo[k]),
-                       gbs=round(algo[k] / (v * 1e-6) / 1e9, 1)) for k, v in kernel_us.items()}
+                       gbs=round(algo[k] / (v * 1e-6) / 1e9, 1), traffic=traffic_of(k))
+               for k, v in kernel_us.items()}
     return dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                 algo_bytes_per_launch=round(algo[dom]), us_per_launch=round(us, 3),
@@ -494,7 +526,7 @@ def bench_prefill(args):
                       unit="TFLOP/s", frac=round(ach / MFMA_FP16_PEAK_TFLOPS, 4), traffic=pf_traffic,
                       flops_per_launch=fl_gu, us_per_launch=round(kus[dom], 2),
                       timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream",
-                      per_kernel=per_kernel, mfma_counters=PREFILL_MFMA_COUNTERS),
+                      per_kernel=per_kernel, mfma_counters=prefill_mfma_counters(fl_gu, fl_dn)),
         cpu_baseline=cpu,
     )
 
