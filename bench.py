@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=47, help="layers in the CPU baseline sample")
     ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens in the one-thread CPU baseline sample")
-    ap.add_argument("--prefill-cpu-tokens", type=int, default=256, help="tokens in the prefill CPU baseline sample")
+    ap.add_argument("--prefill-cpu-tokens", type=int, default=1024, help="tokens in the prefill CPU baseline sample")
     ap.add_argument("--timed-calls", type=int, default=20,
                     help="eager stack calls with per-kernel dispatch events (the roofline's kernel timing)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -90,14 +90,19 @@ def union_bytes(idx_trace: np.ndarray, dims, expert_bytes: int) -> float:
 
 
 def source_digest(files=("moe_decode_b1.hip", "moe_decode.hip", "moe_device.h", "moe_internal.h")) -> str:
-    """Digest of kernel sources (default: the decode kernels'): stored counter
-    readings apply only to the source they were taken on."""
+    """Digest of kernel sources (default: the decode kernels'), comments and
+    whitespace left out: stored counter readings apply only to the code they
+    were taken on."""
     import hashlib
+    import re
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_decode_route_amd", "csrc")
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(root, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(root, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -121,7 +126,14 @@ _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE K
 # taken on.  The SQ counters sum over the chip's 1024 SIMDs (256 CUs x 4) and
 # GRBM_GUI_ACTIVE over its 8 XCDs, so utilisation = (busy / 1024) / (active / 8);
 # one MOP is 512 FLOPs of work issued to the matrix cores.
-PREFILL_MFMA_COUNTERS = None
+PREFILL_MFMA_COUNTERS = dict(
+    source_digest="5ce359e33fe29017",
+    # means per dispatch over the 14 dispatches of each GEMM in one run
+    pf_gemm_gateup=dict(GRBM_GUI_ACTIVE=2431329.71, SQ_VALU_MFMA_BUSY_CYCLES=130285568.0,
+                        SQ_INSTS_VALU_MFMA_MOPS_F16=260571136.0, SQ_BUSY_CYCLES=8442673.43, duration_us=155.76),
+    pf_gemm_down=dict(GRBM_GUI_ACTIVE=1621104.07, SQ_VALU_MFMA_BUSY_CYCLES=65142784.0,
+                      SQ_INSTS_VALU_MFMA_MOPS_F16=130285568.0, SQ_BUSY_CYCLES=5546767.14, duration_us=93.95),
+)
 
 
 def prefill_mfma_counters(fl_gu: float, fl_dn: float):
@@ -150,19 +162,20 @@ def _traffic(digest: str, fetch_kib: float, write_kib: float) -> dict:
 
 COUNTER_TRAFFIC = {
     # batch-1 q4_1 stack
-    ("stack_q4_1_b1", "b1_route_shared"): _traffic("2210e5c88176d58b", 1233.1659, 24.0),
-    ("stack_q4_1_b1", "b1_topk_gateup"): _traffic("2210e5c88176d58b", 3937.0461, 12.6691),
-    ("stack_q4_1_b1", "b1_down"): _traffic("2210e5c88176d58b", 2323.0305, 8.0),
+    ("stack_q4_1_b1", "b1_route_shared"): _traffic("a245c119e9b3c9fb", 1233.1659, 24.0),
+    ("stack_q4_1_b1", "b1_topk_gateup"): _traffic("a245c119e9b3c9fb", 3937.0461, 12.6691),
+    ("stack_q4_1_b1", "b1_down"): _traffic("a245c119e9b3c9fb", 2323.0305, 8.0),
     # batch-8 NVFP4 stack
-    ("stack_nvfp4_b8", "bn_router"): _traffic("3f7cb9a941f7e6bf", 788.5061, 64.0),
-    ("stack_nvfp4_b8", "bn_gateup"): _traffic("3f7cb9a941f7e6bf", 26672.5574, 112.4276),
-    ("stack_nvfp4_b8", "bn_down"): _traffic("3f7cb9a941f7e6bf", 13565.2427, 64.0),
+    ("stack_nvfp4_b8", "bn_router"): _traffic("fb103a7a6ae54a32", 788.5061, 64.0),
+    ("stack_nvfp4_b8", "bn_gateup"): _traffic("fb103a7a6ae54a32", 26672.5574, 112.4276),
+    ("stack_nvfp4_b8", "bn_down"): _traffic("fb103a7a6ae54a32", 13565.2427, 64.0),
     # 4096-token q4_1 prefill
-    ("prefill_q4_1", "pf_gemm_gateup"): _traffic("9bc236c0b4662e31", 227174.8, 28694.4),
+    ("prefill_q4_1", "pf_gemm_gateup"): _traffic("5ce359e33fe29017", 227296.1927, 28676.0729),
+    ("prefill_q4_1", "pf_gemm_down"): _traffic("5ce359e33fe29017", 82041.125, 114688.0),
     # q4_1 output layer, 1 token
-    ("lm_head_q4_1_t1", "lm_head_kernel"): _traffic("73c3554f2833a25f", 91654.1802, 572.2188),
+    ("lm_head_q4_1_t1", "lm_head_kernel"): _traffic("b034d5cb4ad3291a", 91654.1802, 572.2188),
     # full-attention layer at 128k positions
-    ("attn_full128k", "attn_chunk"): _traffic("2c11e0abd4e859cc", 131378.4219, 2306.0),
+    ("attn_full128k", "attn_chunk"): _traffic("6dc9d335d181d254", 131378.4219, 2306.0),
 }
 
 
@@ -499,10 +512,14 @@ def bench_prefill(args):
     fl_all = fl_gu + fl_dn + fl_rt
     dom = "pf_gemm_gateup"
     ach = fl_gu / (kus[dom] * 1e-6) / 1e12
-    tr = COUNTER_TRAFFIC.get(("prefill_q4_1", dom))
-    pf_traffic = (tr["fetch_bytes"] + tr["write_bytes"]
-                  if tr is not None and tr["source_digest"] == source_digest(PREFILL_SOURCES) else None)
+    def pf_traffic_of(k):
+        tr = COUNTER_TRAFFIC.get(("prefill_q4_1", k))
+        return (tr["fetch_bytes"] + tr["write_bytes"]
+                if tr is not None and tr["source_digest"] == source_digest(PREFILL_SOURCES) else None)
+
+    pf_traffic = pf_traffic_of(dom)
     per_kernel = {k: dict(us_per_launch=round(v, 2)) for k, v in kus.items()}
+    per_kernel["pf_gemm_down"]["traffic"] = pf_traffic_of("pf_gemm_down")
     per_kernel["pf_gemm_gateup"]["tflops"] = round(fl_gu / (kus["pf_gemm_gateup"] * 1e-6) / 1e12, 1)
     per_kernel["pf_gemm_down"]["tflops"] = round(fl_dn / (kus["pf_gemm_down"] * 1e-6) / 1e12, 1)
     rname = "pf_router_gemm" if "pf_router_gemm" in kus else "pf_logits"
@@ -521,7 +538,8 @@ def bench_prefill(args):
                     layer_mfma_frac=round(fl_all / (ms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
                     experts_hit=int(np.count_nonzero(loads)), max_expert_load=int(loads.max()),
                     timing="HIP graph replay of one layer forward", eager_ms_per_step=round(ms_eager, 4),
-                    graph_matches_eager=graph_matches_eager),
+                    graph_matches_eager=graph_matches_eager,
+                    kernel_source_digest=source_digest(PREFILL_SOURCES)),
         roofline=dict(bound="mfma", kernel=dom, achieved=round(ach, 1), peak=MFMA_FP16_PEAK_TFLOPS,
                       unit="TFLOP/s", frac=round(ach / MFMA_FP16_PEAK_TFLOPS, 4), traffic=pf_traffic,
                       flops_per_launch=fl_gu, us_per_launch=round(kus[dom], 2),
@@ -852,7 +870,7 @@ def rocprof_summary(path: str) -> dict:
     graph replays (and the untimed eager calls); from it on, the timed calls,
     whose launches were enqueued behind the hold and ran back to back.  A
     kernel_trace.csv gives durations in microseconds; a counter_collection.csv
-    gives each counter's value per dispatch."""
+    gives each counter's value per dispatch, and the dispatch's duration."""
     import csv
     with open(path) as f:
         rows = list(csv.DictReader(f))
@@ -869,7 +887,7 @@ def rocprof_summary(path: str) -> dict:
     per = {}
     for d in ds:
         ph = "graph" if first_hold is None or d["s"] < first_hold else "timed"
-        vals = d["c"] if counters else {"duration_us": (d["e"] - d["s"]) / 1e3}
+        vals = dict(d["c"], duration_us=(d["e"] - d["s"]) / 1e3) if counters else {"duration_us": (d["e"] - d["s"]) / 1e3}
         for c, v in vals.items():
             per.setdefault(d["k"], {}).setdefault(c, {"graph": [], "timed": []})[ph].append(v)
     return {k: {c: dict(all=_stats(v["graph"] + v["timed"]), graph=_stats(v["graph"]), timed=_stats(v["timed"]))

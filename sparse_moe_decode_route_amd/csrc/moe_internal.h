@@ -15,7 +15,7 @@ namespace moe {
 moe_status set_error(moe_status s, const std::string &msg);
 
 constexpr int MAX_DECODE_T = 8;   // batch-1, general and stack decode paths
-constexpr int MAX_BN_T = 32;      // small-batch path (regular shapes; token masks are 32 bits)
+constexpr int MAX_BN_T = 32;      // small-batch path (regular shapes; the grouped GEMM is faster past 32 tokens)
 
 // Everything a decode-path kernel reads or writes (device pointers).
 struct DecodeParams {
