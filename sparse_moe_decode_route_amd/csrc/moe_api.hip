@@ -614,6 +614,7 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
     gate.release();
     if (s == MOE_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(MOE_ERR_HIP, "stream synchronize failed");
     if (s != MOE_OK) {
+        (void)hipStreamSynchronize(st);  // launches enqueued before the failure may still use the events
         destroy();
         return s;
     }
@@ -680,6 +681,7 @@ moe_status moe_layer_forward_prefill_timed(const moe_dims *d, const moe_layer_we
     gate.release();
     if (s == MOE_OK && hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
         s = fail(MOE_ERR_HIP, "stream synchronize failed");
+    if (s != MOE_OK) (void)hipStreamSynchronize(static_cast<hipStream_t>(stream));
     if (s == MOE_OK) {
         for (int k = 0; k < moe::PREFILL_SLOTS; k++) {
             float ms = 0.f;
@@ -944,6 +946,7 @@ moe_status moe_attn_decode_timed(const moe_attn_dims *d, int32_t n_seqs, int32_t
     moe_status s = hip_status(moe::launch_attn(a, st), "attention launch");
     gate.release();
     if (s == MOE_OK && hipStreamSynchronize(st) != hipSuccess) s = fail(MOE_ERR_HIP, "stream synchronize failed");
+    if (s != MOE_OK) (void)hipStreamSynchronize(st);
     if (s == MOE_OK) {
         for (int k = 0; k < 2; k++) {
             float ms = 0.f;

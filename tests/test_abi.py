@@ -107,6 +107,35 @@ def test_entry_points_validate_before_enqueue(L):
     assert b"n_experts" in L.moe_last_error()
 
 
+def test_timed_entry_points_validate_before_enqueue(L):
+    # the timed calls check their arguments before anything (the stream hold
+    # included) is enqueued: every call below fails validation on the host
+    d = _d()
+    fake = ctypes.c_void_p(0x10000)
+    w = B.CLayerWeights(0x10000, 0, 0x20000, 0)
+    us = (ctypes.c_float * 8)()
+    nk = ctypes.c_int32(0)
+    names = ctypes.create_string_buffer(64)
+    # no timing outputs
+    assert L.moe_stack_decode_timed(ctypes.byref(d), 1, ctypes.byref(w), fake, 1, fake, None, fake, 1 << 30,
+                                    None, ctypes.byref(nk), names, 64, None) == INVALID
+    # too many tokens for the stack, and no layers
+    assert L.moe_stack_decode_timed(ctypes.byref(d), 1, ctypes.byref(w), fake, 9, fake, None, fake, 1 << 30,
+                                    us, ctypes.byref(nk), names, 64, None) == INVALID
+    assert L.moe_stack_decode_timed(ctypes.byref(d), 0, ctypes.byref(w), fake, 1, fake, None, fake, 1 << 30,
+                                    us, ctypes.byref(nk), names, 64, None) == INVALID
+    # workspace too small
+    assert L.moe_stack_decode_timed(ctypes.byref(d), 1, ctypes.byref(w), fake, 1, fake, None, fake, 16,
+                                    us, ctypes.byref(nk), names, 64, None) == WORKSPACE
+    # prefill: NULL x, bad activation type, no timing outputs
+    assert L.moe_layer_forward_prefill_timed(ctypes.byref(d), ctypes.byref(w), None, 0, 64, fake, fake, 1 << 30,
+                                             us, ctypes.byref(nk), names, 64, None) == INVALID
+    assert L.moe_layer_forward_prefill_timed(ctypes.byref(d), ctypes.byref(w), fake, 7, 64, fake, fake, 1 << 30,
+                                             us, ctypes.byref(nk), names, 64, None) == UNSUPPORTED
+    assert L.moe_layer_forward_prefill_timed(ctypes.byref(d), ctypes.byref(w), fake, 0, 64, fake, fake, 1 << 30,
+                                             None, ctypes.byref(nk), names, 64, None) == INVALID
+
+
 def test_status_strings(L):
     for s in (0, -1, -2, -3, -4, -5):
         assert L.moe_status_string(s)
