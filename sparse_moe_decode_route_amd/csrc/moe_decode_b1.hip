@@ -261,24 +261,7 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_C) b1_down(DecodeParams p) 
     const int32_t *lst = p.b1_list + 16 * (blockIdx.x % p.b1_ncopy);
     const int my_e = lst[la];
     const float my_c = __int_as_float(lst[8 + la]);
-    // 2) every slot's h straight into LDS (global_load_lds: lane L of a wave
-    //    instruction writes 16 bytes at the instruction's LDS base + 16 L, so
-    //    each lane gathers the source for its padded position; pad positions
-    //    and slots past the active ones read h[0], a valid address)
-    const int wv = wave;
-#pragma unroll
-    for (int k = 0; k < NH; k++) {
-        const int pos = (k * B1_WAVES_C + wv) * MOE_WAVE + lane;
-        const int a = pos / (LPR_F * PU), r = pos % (LPR_F * PU);
-        const int u = r / PU, q = r % PU;
-        const bool real = (a < n_active) & (q < UE / 4);
-        const uint32_t off = real ? (uint32_t)(a * F + u * UE + q * 4) : 0u;  // 32-bit select, no branch
-        const float *src = p.h + off;
-        __builtin_amdgcn_global_load_lds((const void *)src,
-                                         (__attribute__((address_space(3))) void *)(hs4 + (k * B1_WAVES_C + wv) * MOE_WAVE),
-                                         16, 0, 0);
-    }
-    // 3) this wave's slots' down rows
+    // 2) this wave's slots' down rows (issued as soon as the list arrives)
     WUnit wd[B1_SLOTS_PER_WAVE][B1_RR];
     float ts[B1_SLOTS_PER_WAVE], coef[B1_SLOTS_PER_WAVE];
 #pragma unroll
@@ -291,6 +274,24 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_C) b1_down(DecodeParams p) 
         ts[q] = md.ts;
 #pragma unroll
         for (int r = 0; r < B1_RR; r++) wd[q][r] = load_unit<FMT>(md, min(r0 + r, D - 1), sub);
+    }
+    // 3) every slot's h straight into LDS (global_load_lds: lane L of a wave
+    //    instruction writes 16 bytes at the instruction's LDS base + 16 L, so
+    //    each lane gathers the source for its padded position; pad positions
+    //    and slots past the active ones read h[0], a valid address); issued
+    //    after the weight loads so that waiting for the list never waits for them
+    const int wv = wave;
+#pragma unroll
+    for (int k = 0; k < NH; k++) {
+        const int pos = (k * B1_WAVES_C + wv) * MOE_WAVE + lane;
+        const int a = pos / (LPR_F * PU), r = pos % (LPR_F * PU);
+        const int u = r / PU, q = r % PU;
+        const bool real = (a < n_active) & (q < UE / 4);
+        const uint32_t off = real ? (uint32_t)(a * F + u * UE + q * 4) : 0u;  // 32-bit select, no branch
+        const float *src = p.h + off;
+        __builtin_amdgcn_global_load_lds((const void *)src,
+                                         (__attribute__((address_space(3))) void *)(hs4 + (k * B1_WAVES_C + wv) * MOE_WAVE),
+                                         16, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0);  // h in LDS (and the weights) have arrived
     __syncthreads();
