@@ -162,9 +162,9 @@ def _traffic(digest: str, fetch_kib: float, write_kib: float) -> dict:
 
 COUNTER_TRAFFIC = {
     # batch-1 q4_1 stack
-    ("stack_q4_1_b1", "b1_route_shared"): _traffic("a245c119e9b3c9fb", 1233.1659, 24.0),
-    ("stack_q4_1_b1", "b1_topk_gateup"): _traffic("a245c119e9b3c9fb", 3937.0461, 12.6691),
-    ("stack_q4_1_b1", "b1_down"): _traffic("a245c119e9b3c9fb", 2323.0305, 8.0),
+    ("stack_q4_1_b1", "b1_route_shared"): _traffic("7ea1dc51669f28ab", 1233.1109, 24.0),
+    ("stack_q4_1_b1", "b1_topk_gateup"): _traffic("7ea1dc51669f28ab", 3936.9252, 12.6691),
+    ("stack_q4_1_b1", "b1_down"): _traffic("7ea1dc51669f28ab", 2323.0429, 8.0),
     # batch-8 NVFP4 stack
     ("stack_nvfp4_b8", "bn_router"): _traffic("fb103a7a6ae54a32", 788.5061, 64.0),
     ("stack_nvfp4_b8", "bn_gateup"): _traffic("fb103a7a6ae54a32", 26672.5574, 112.4276),
