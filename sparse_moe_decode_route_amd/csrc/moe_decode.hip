@@ -39,8 +39,8 @@ __device__ void gateup_unit(const DecodeParams &p, int slot, int expert, uint32_
     const int grp = lane / LPR, sub = lane % LPR;
     const int D = p.D, F = p.F;
     const uint8_t *eb = p.experts + (size_t)expert * p.expert_bytes;
-    Mat mg{eb, F, D, p.tscale ? p.tscale[3 * expert + 0] : 1.f};
-    Mat mu{eb + mat_bytes<FMT>(F, D), F, D, p.tscale ? p.tscale[3 * expert + 1] : 1.f};
+    Mat mg{eb, F, D, tensor_scale<FMT>(p.tscale, 3 * expert + 0)};
+    Mat mu{eb + mat_bytes<FMT>(F, D), F, D, tensor_scale<FMT>(p.tscale, 3 * expert + 1)};
     const int units = D / Unit<FMT>::E;
     const int fbase = f0 + grp * RG;
     float ag[RG][MAXT], au[RG][MAXT];
@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(MOE_WAVE) down_kernel(DecodeParams p) {
         const int e = p.act_expert[a];
         const uint32_t mask = p.act_mask[a];
         const uint8_t *eb = p.experts + (size_t)e * p.expert_bytes;
-        Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, p.tscale ? p.tscale[3 * e + 2] : 1.f};
+        Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, tensor_scale<FMT>(p.tscale, 3 * e + 2)};
         for (int u = sub; u < units; u += LPR_F) {
             WUnit wd[RR];
 #pragma unroll

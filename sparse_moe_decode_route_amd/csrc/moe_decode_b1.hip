@@ -48,8 +48,8 @@ template <int FMT, int UPLD, int RG>
 __device__ __forceinline__ void gateup_issue(GateUp<FMT, UPLD, RG> &g, const DecodeParams &p, int expert, int f0) {
     const int lane = threadIdx.x & (MOE_WAVE - 1);
     const uint8_t *eb = p.experts + (size_t)expert * p.expert_bytes;
-    Mat mg{eb, p.F, p.D, p.tscale ? p.tscale[3 * expert + 0] : 1.f};
-    Mat mu{eb + mat_bytes<FMT>(p.F, p.D), p.F, p.D, p.tscale ? p.tscale[3 * expert + 1] : 1.f};
+    Mat mg{eb, p.F, p.D, tensor_scale<FMT>(p.tscale, 3 * expert + 0)};
+    Mat mu{eb + mat_bytes<FMT>(p.F, p.D), p.F, p.D, tensor_scale<FMT>(p.tscale, 3 * expert + 1)};
     g.tsg = mg.ts;
     g.tsu = mu.ts;
 #pragma unroll
@@ -270,7 +270,7 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_C) b1_down(DecodeParams p) 
         const int e = __builtin_amdgcn_readlane(my_e, min(a, n_active - 1));
         coef[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_c), min(a, n_active - 1)));
         const uint8_t *eb = p.experts + (size_t)e * p.expert_bytes;
-        Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, p.tscale ? p.tscale[3 * e + 2] : 1.f};
+        Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, tensor_scale<FMT>(p.tscale, 3 * e + 2)};
         ts[q] = md.ts;
 #pragma unroll
         for (int r = 0; r < B1_RR; r++) wd[q][r] = load_unit<FMT>(md, min(r0 + r, D - 1), sub);

@@ -202,8 +202,8 @@ __global__ void __launch_bounds__(MOE_WAVE *BN_WAVES) bn_gateup(DecodeParams p) 
         }
     }
     const uint8_t *eb = p.experts + (size_t)expert * p.expert_bytes;
-    Mat mg{eb, p.F, p.D, p.tscale ? p.tscale[3 * expert + 0] : 1.f};
-    Mat mu{eb + mat_bytes<FMT>(p.F, p.D), p.F, p.D, p.tscale ? p.tscale[3 * expert + 1] : 1.f};
+    Mat mg{eb, p.F, p.D, tensor_scale<FMT>(p.tscale, 3 * expert + 0)};
+    Mat mu{eb + mat_bytes<FMT>(p.F, p.D), p.F, p.D, tensor_scale<FMT>(p.tscale, 3 * expert + 1)};
     const bool scaled = p.x_prev != nullptr;  // stack: x is the previous output, normalised here
     const float *xin = scaled ? p.x_prev : p.x;
     WUnit wg[RG][UPLD], wu[RG][UPLD];
@@ -315,7 +315,7 @@ __global__ void __launch_bounds__(MOE_WAVE *MAX_DECODE_T) bn_down(DecodeParams p
             on[q] = j < KS && pr.y >= 0;
             coef[q] = __int_as_float(pr.z);
             const uint8_t *eb = p.experts + (size_t)pr.w * p.expert_bytes;
-            Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, p.tscale ? p.tscale[3 * pr.w + 2] : 1.f};
+            Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, tensor_scale<FMT>(p.tscale, 3 * pr.w + 2)};
             ts[q] = md.ts;
 #pragma unroll
             for (int r = 0; r < BN_RR; r++) wd[q][r] = load_unit<FMT>(md, min(r0 + r, D - 1), sub);

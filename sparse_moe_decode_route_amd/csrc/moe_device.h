@@ -56,6 +56,15 @@ struct Mat {
     float ts;  // NVFP4 tensor scale (1 otherwise)
 };
 
+// Tensor scale i of an NVFP4 layer, 1 for the other formats.  The choice is
+// made at compile time (an NVFP4 call always carries its scales, which the
+// host checks): a load under a run-time condition gets a wait of its own, and
+// that wait would sit in front of the weight loads issued after it.
+template <int FMT>
+__device__ __forceinline__ float tensor_scale(const float *ts, int i) {
+    return FMT == FMT_NVFP4 ? ts[i] : 1.f;
+}
+
 template <int FMT>
 __device__ __forceinline__ size_t mat_bytes(int rows, int k) {
     if (FMT == FMT_BF16) return (size_t)rows * k * 2;

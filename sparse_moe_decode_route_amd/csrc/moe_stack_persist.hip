@@ -137,8 +137,8 @@ template <int FMT, int UPLD, int FPB>
 __device__ __forceinline__ void gu_load(GU<FMT, UPLD, FPB> &w, const uint8_t *experts, const float *tscale,
                                         size_t expert_bytes, int D, int F, int e, int f0, int lane) {
     const uint8_t *eb = experts + (size_t)e * expert_bytes;
-    Mat mg{eb, F, D, tscale ? tscale[3 * e + 0] : 1.f};
-    Mat mu{eb + mat_bytes<FMT>(F, D), F, D, tscale ? tscale[3 * e + 1] : 1.f};
+    Mat mg{eb, F, D, tensor_scale<FMT>(tscale, 3 * e + 0)};
+    Mat mu{eb + mat_bytes<FMT>(F, D), F, D, tensor_scale<FMT>(tscale, 3 * e + 1)};
     w.tg = mg.ts;
     w.tu = mu.ts;
 #pragma unroll
@@ -181,7 +181,7 @@ template <int FMT, int NDU, int UF>
 __device__ __forceinline__ void dn_load(DN<FMT, NDU> &d, const uint8_t *experts, const float *tscale,
                                         size_t expert_bytes, int D, int F, int e, int r0, int lane) {
     const uint8_t *eb = experts + (size_t)e * expert_bytes;
-    Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, tscale ? tscale[3 * e + 2] : 1.f};
+    Mat md{eb + 2 * mat_bytes<FMT>(F, D), D, F, tensor_scale<FMT>(tscale, 3 * e + 2)};
     d.ts = md.ts;
 #pragma unroll
     for (int k = 0; k < NDU; k++) {
