@@ -127,12 +127,12 @@ _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE K
 # GRBM_GUI_ACTIVE over its 8 XCDs, so utilisation = (busy / 1024) / (active / 8);
 # one MOP is 512 FLOPs of work issued to the matrix cores.
 PREFILL_MFMA_COUNTERS = dict(
-    source_digest="5ce359e33fe29017",
+    source_digest="a3d7b621146f8ab7",
     # means per dispatch over the 14 dispatches of each GEMM in one run
-    pf_gemm_gateup=dict(GRBM_GUI_ACTIVE=2431329.71, SQ_VALU_MFMA_BUSY_CYCLES=130285568.0,
-                        SQ_INSTS_VALU_MFMA_MOPS_F16=260571136.0, SQ_BUSY_CYCLES=8442673.43, duration_us=155.76),
-    pf_gemm_down=dict(GRBM_GUI_ACTIVE=1621104.07, SQ_VALU_MFMA_BUSY_CYCLES=65142784.0,
-                      SQ_INSTS_VALU_MFMA_MOPS_F16=130285568.0, SQ_BUSY_CYCLES=5546767.14, duration_us=93.95),
+    pf_gemm_gateup=dict(GRBM_GUI_ACTIVE=2417312.71, SQ_VALU_MFMA_BUSY_CYCLES=130285568.0,
+                        SQ_INSTS_VALU_MFMA_MOPS_F16=260571136.0, SQ_BUSY_CYCLES=8465129.0, duration_us=154.54),
+    pf_gemm_down=dict(GRBM_GUI_ACTIVE=1613752.57, SQ_VALU_MFMA_BUSY_CYCLES=65142784.0,
+                      SQ_INSTS_VALU_MFMA_MOPS_F16=130285568.0, SQ_BUSY_CYCLES=5553104.71, duration_us=93.83),
 )
 
 
@@ -162,20 +162,20 @@ def _traffic(digest: str, fetch_kib: float, write_kib: float) -> dict:
 
 COUNTER_TRAFFIC = {
     # batch-1 q4_1 stack
-    ("stack_q4_1_b1", "b1_route_shared"): _traffic("7ea1dc51669f28ab", 1233.1109, 24.0),
-    ("stack_q4_1_b1", "b1_topk_gateup"): _traffic("7ea1dc51669f28ab", 3936.9252, 12.6691),
-    ("stack_q4_1_b1", "b1_down"): _traffic("7ea1dc51669f28ab", 2323.0429, 8.0),
+    ("stack_q4_1_b1", "b1_route_shared"): _traffic("3873ae7b4315216b", 1233.1619, 24.0),
+    ("stack_q4_1_b1", "b1_topk_gateup"): _traffic("3873ae7b4315216b", 3937.0521, 12.6691),
+    ("stack_q4_1_b1", "b1_down"): _traffic("3873ae7b4315216b", 2323.0461, 8.0),
     # batch-8 NVFP4 stack
-    ("stack_nvfp4_b8", "bn_router"): _traffic("fb103a7a6ae54a32", 788.5061, 64.0),
-    ("stack_nvfp4_b8", "bn_gateup"): _traffic("fb103a7a6ae54a32", 26672.5574, 112.4276),
-    ("stack_nvfp4_b8", "bn_down"): _traffic("fb103a7a6ae54a32", 13565.2427, 64.0),
+    ("stack_nvfp4_b8", "bn_router"): _traffic("57c1d2057ded3856", 788.51, 64.0),
+    ("stack_nvfp4_b8", "bn_gateup"): _traffic("57c1d2057ded3856", 26673.5191, 112.4278),
+    ("stack_nvfp4_b8", "bn_down"): _traffic("57c1d2057ded3856", 13520.6781, 64.0),
     # 4096-token q4_1 prefill
-    ("prefill_q4_1", "pf_gemm_gateup"): _traffic("5ce359e33fe29017", 227296.1927, 28676.0729),
-    ("prefill_q4_1", "pf_gemm_down"): _traffic("5ce359e33fe29017", 82041.125, 114688.0),
+    ("prefill_q4_1", "pf_gemm_gateup"): _traffic("a3d7b621146f8ab7", 227413.3854, 28677.7604),
+    ("prefill_q4_1", "pf_gemm_down"): _traffic("a3d7b621146f8ab7", 82017.2969, 114688.0),
     # q4_1 output layer, 1 token
-    ("lm_head_q4_1_t1", "lm_head_kernel"): _traffic("b034d5cb4ad3291a", 91654.1802, 572.2188),
+    ("lm_head_q4_1_t1", "lm_head_kernel"): _traffic("c3b94d4e2367e0b5", 91654.112, 572.2188),
     # full-attention layer at 128k positions
-    ("attn_full128k", "attn_chunk"): _traffic("6dc9d335d181d254", 131378.4219, 2306.0),
+    ("attn_full128k", "attn_chunk"): _traffic("70abf60267263961", 131362.8772, 2306.0),
 }
 
 

@@ -225,6 +225,11 @@ moe_status moe_stack_decode(const moe_dims *dims, int32_t n_layers, const moe_la
  * pages time whole-model decode only (tokens/s on the two named machines);
  * this call gives the per-kernel split of the decode step that those
  * figures are made of.  Blocks the calling thread until the stack is done.
+ * The launches are enqueued behind a one-wave kernel that holds the stream
+ * until the host has enqueued all of them (at most 0.2 s), so that they run
+ * back to back as in a graph replay instead of each after an idle gap;
+ * timed calls of one process are serialised.  Results are those of
+ * moe_stack_decode, bit for bit.
  *   kernel_us  (host) float [4]: mean duration in microseconds of each
  *              kernel slot of a layer, averaged over the layers that ran it
  *              (-1 for a slot that never ran).
@@ -244,7 +249,8 @@ moe_status moe_stack_decode_timed(const moe_dims *dims, int32_t n_layers, const 
 
 /*
  * Measurement variant of moe_layer_forward_prefill (no routing outputs): the
- * same kernels, each launched with a start/stop event pair on its dispatch.
+ * same kernels, each launched with a start/stop event pair on its dispatch,
+ * held back and then run back to back as in moe_stack_decode_timed.
  * Blocks the calling thread until the layer is done.
  *   kernel_us  (host) float [7]: duration in microseconds of each kernel, in
  *              launch order (router logits, top-k, scan, scatter, gate/up
@@ -371,7 +377,8 @@ moe_status moe_attn_decode(const moe_attn_dims *dims, int32_t n_seqs, int32_t ma
                            void *ws, size_t ws_bytes, void *stream);
 
 /* Measurement variant: the same two kernels, each launched with a
-   start/stop event pair on its dispatch; kernel_us (host) float [2]
+   start/stop event pair on its dispatch, held back and then run back to
+   back as in moe_stack_decode_timed; kernel_us (host) float [2]
    receives their durations (chunks, combine) in microseconds.
    Blocks the calling thread; not for use under stream capture. */
 moe_status moe_attn_decode_timed(const moe_attn_dims *dims, int32_t n_seqs, int32_t max_len, const float *q,
