@@ -522,23 +522,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// 4 nibbles (bytes of t, each < 16) -> two fp16 pairs holding the integers:
-// v_perm_b32 places each byte under a 0x64 high byte, giving the fp16 value
-// 1024 + q exactly; subtracting 1024 is exact too.
+// 4 nibbles (bytes of t, each < 16) -> two fp16 pairs holding the integers,
+// one packed fp8 -> fp16 conversion per pair: a byte q < 16 read as OCP E4M3
+// is q * 2^-9 (exponent field 0 or 1), and the power-of-two scale 2^9 makes
+// it q exactly (one instruction per two weights, where placing each byte
+// under an fp16 exponent took a byte permute and a packed subtract).
 __device__ __forceinline__ void nib4_to_h(uint32_t t, half2_t &a, half2_t &b) {
-    const uint32_t p01 = __builtin_amdgcn_perm(0x64646464u, t, 0x04010400u);  // bytes t0, 64, t1, 64
-    const uint32_t p23 = __builtin_amdgcn_perm(0x64646464u, t, 0x04030402u);  // bytes t2, 64, t3, 64
-    const half2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-    a = __builtin_bit_cast(half2_t, p01) - k1024;
-    b = __builtin_bit_cast(half2_t, p23) - k1024;
-}
-
-// E2M1 code (4 bits) -> fp16 bits: sign, and the high byte of the fp16
-// encodings of {0, .5, 1, 1.5, 2, 3, 4, 6} packed in a 64-bit table
-__device__ __forceinline__ uint32_t e2m1_h(uint32_t c) {
-    constexpr unsigned long long kHi = 0x464442403E3C3800ull;
-    const uint32_t hi = (uint32_t)(kHi >> (8 * (c & 7u))) & 0xFFu;
-    return (hi << 8) | ((c & 8u) << 12);
+    a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t, 512.0f, false);  // bytes t0, t1
+    b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t, 512.0f, true);   // bytes t2, t3
 }
 
 // fragments for steps 0 and 1; NVFP4 values exclude the tensor scale
@@ -546,8 +537,11 @@ __device__ __forceinline__ uint32_t e2m1_h(uint32_t c) {
 template <int FMT>
 __device__ __forceinline__ void dequant_frag(const WRaw<FMT> &w, half8_t &s0, half8_t &s1) {
     if constexpr (FMT == FMT_Q4_1) {
-        const half2_t d2 = __builtin_bit_cast(half2_t, (w.dm & 0xFFFFu) * 0x10001u);
-        const half2_t m2 = __builtin_bit_cast(half2_t, (w.dm >> 16) * 0x10001u);
+        // {d, d} and {m, m}: the packed FMA takes them as halves of one
+        // register (operand selects), with no broadcast instructions
+        const half2_t dm = __builtin_bit_cast(half2_t, w.dm);
+        const half2_t d2 = __builtin_shufflevector(dm, dm, 0, 0);
+        const half2_t m2 = __builtin_shufflevector(dm, dm, 1, 1);
         const uint32_t wl[2] = {w.c.x, w.c.y};
 #pragma unroll
         for (int i = 0; i < 2; i++) {
@@ -562,12 +556,26 @@ __device__ __forceinline__ void dequant_frag(const WRaw<FMT> &w, half8_t &s0, ha
             s1[4 * i + 0] = a[0]; s1[4 * i + 1] = a[1]; s1[4 * i + 2] = b[0]; s1[4 * i + 3] = b[1];
         }
     } else if constexpr (FMT == FMT_NVFP4) {
+        // E2M1 pairs (one code byte each, low nibble first) by the hardware
+        // converter at scale 1 (exact), times the block's E4M3 scale: the
+        // product has at most 6 significant bits and lies in fp16's normal
+        // range, so it is exact too
         const _Float16 sc0 = (_Float16)e4m3_to_float(w.s & 0xFFu);
         const _Float16 sc1 = (_Float16)e4m3_to_float(w.s >> 8);
+        const half2_t k0 = {sc0, sc0}, k1 = {sc1, sc1};
+        // (the byte selector must be a literal)
+        const half2_t a[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.c0, 1.0f, 0) * k0,
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.c0, 1.0f, 1) * k0,
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.c0, 1.0f, 2) * k0,
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.c0, 1.0f, 3) * k0};
+        const half2_t b[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.c1, 1.0f, 0) * k1,
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.c1, 1.0f, 1) * k1,
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.c1, 1.0f, 2) * k1,
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.c1, 1.0f, 3) * k1};
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            s0[j] = __builtin_bit_cast(_Float16, (uint16_t)e2m1_h((w.c0 >> (4 * j)) & 0xFu)) * sc0;
-            s1[j] = __builtin_bit_cast(_Float16, (uint16_t)e2m1_h((w.c1 >> (4 * j)) & 0xFu)) * sc1;
+        for (int k = 0; k < 4; k++) {
+            s0[2 * k] = a[k][0]; s0[2 * k + 1] = a[k][1];
+            s1[2 * k] = b[k][0]; s1[2 * k + 1] = b[k][1];
         }
     } else {
         const uint32_t a[4] = {w.v0.x, w.v0.y, w.v0.z, w.v0.w};
@@ -1011,12 +1019,12 @@ __device__ __forceinline__ void pf_mfma_tokens(const _Float16 *stg, const half8_
 #endif
 
 // ---------------------------------------------------------------------------
-// pf_gemm_q4<MODE, BM>: pf_gemm for q4_1 weights on tiles of up to BM token
-// rows (128: two blocks per CU; 256: one block per CU with the accumulators
-// of 8 token blocks, so each dequantised weight feeds twice the MFMAs), with
-// the weight fragments of 4
-// consecutive 32-input steps copied at once (per row 64 B of codes and the
-// 16 B of 4 {d, m} pairs).  The address unit's cost of a wave-wide copy
+// pf_gemm_q4<FMT, MODE, BM>: pf_gemm for the 4-bit formats (q4_1, NVFP4) on
+// tiles of up to BM token rows (128: two blocks per CU; 256: one block per CU
+// with the accumulators of 8 token blocks, so each dequantised weight feeds
+// twice the MFMAs), with the weight fragments of 4 consecutive 32-input steps
+// copied at once (per row 64 B of codes, and the 16 B of 4 q4_1 {d, m} pairs
+// or the 8 B of 4 NVFP4 pairs of E4M3 block scales).  The address unit's cost of a wave-wide copy
 // grows with the cache lines it touches: 16 rows x 64 B costs well under
 // half of 64 rows x 16 B (measured on gfx950), and it dominated the
 // one-step weight copies.  Weight macro-stages are double-buffered and
@@ -1031,15 +1039,40 @@ constexpr int PQ_UNROLL = 16;                                   // steps per loo
 // chunk swizzle of a row in the code macro-stage (64-byte rows)
 __device__ __forceinline__ int pq_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
-template <int MODE, int BM>
+#if defined(__HIP_DEVICE_COMPILE__)
+// raw fragment of weight row `row`, step st of a macro buffer: the step's
+// 16 code bytes sit at chunk st ^ pq_swz(row) of the row; sc = the row's
+// scale word of that step (q4_1 {d, m}; NVFP4 the two E4M3 block scales)
+template <int FMT>
+__device__ __forceinline__ WRaw<FMT> pq_frag(const uint8_t *cb, int row, int st, int g, uint32_t sc) {
+    const uint8_t *q = cb + row * 64 + 16 * (st ^ pq_swz(row));
+    WRaw<FMT> w;
+    if constexpr (FMT == FMT_Q4_1) {
+        w.c = *reinterpret_cast<const uint2 *>(q + 8 * g);
+        w.dm = sc;
+    } else {
+        w.c0 = *reinterpret_cast<const uint32_t *>(q + 4 * g);
+        w.c1 = *reinterpret_cast<const uint32_t *>(q + 8 + 4 * g);
+        w.s = sc;
+    }
+    return w;
+}
+#endif
+
+template <int FMT, int MODE, int BM>
 __global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+    static_assert(FMT == FMT_Q4_1 || FMT == FMT_NVFP4, "4-bit formats");
     constexpr int NBLK = BM / 32;  // 32-row token blocks of a tile
     constexpr int XCH = BM / 64;   // token copies per thread per step
+    // copies per thread of a weight macro's first part (W1: scales + 2 code
+    // copies) and second part (W2: 2 code copies)
+    constexpr int W1N = FMT == FMT_Q4_1 ? 3 : 4, W2N = 2;
     __shared__ uint4 x0s[BM * 4], x1s[BM * 4], x2s[BM * 4], x3s[BM * 4];
     // codes: [256 rows][4 steps x 16 B], a row's step chunks XOR-swizzled by
     // pq_swz(row) (the 8-byte fragment reads of 32 rows then spread over the
-    // banks with the least conflict measured); scales: [256 rows][4 steps x {d, m}]
+    // banks with the least conflict measured); scales: [256 rows][4 steps x
+    // {d, m}] (q4_1) or [256 rows][4 steps x 2 E4M3] (NVFP4)
     // (one LDS object per macro buffer: codes, then scales at PQ_SOFF)
     __shared__ __attribute__((aligned(16))) uint8_t c0s[PQ_WBYTES], c1s[PQ_WBYTES];
 #define PQ_XST(st) ((st) == 0 ? x0s : (st) == 1 ? x1s : (st) == 2 ? x2s : x3s)
@@ -1054,7 +1087,7 @@ __global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfPa
     const int K = MODE == 0 ? p.D : p.F;
     const int ROWS_A = MODE == 0 ? p.F : p.D;
     const uint8_t *eb = p.experts + (size_t)tile.e * p.expert_bytes;
-    const uint32_t mb = (uint32_t)mat_bytes<FMT_Q4_1>(ROWS_A, K);  // bytes of one weight matrix
+    const uint32_t mb = (uint32_t)mat_bytes<FMT>(ROWS_A, K);  // bytes of one weight matrix
     // 32-row token blocks holding rows of the tile (the rest is padding)
     const int nb = __builtin_amdgcn_readfirstlane((tile.rows + 31) >> 5);
     const int r0 = MODE == 0 ? mt * 128 + 32 * wave : mt * 256 + 64 * wave;
@@ -1079,8 +1112,10 @@ __global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfPa
     // weight DMA over the block's matrices (gate then up, or down).  Stage
     // row q: MODE 0 gate row mt*128 + q (q < 128) or up row mt*128 + q - 128,
     // MODE 1 down row mt*256 + q.  Code slots i * 256 + tid hold row
-    // q = 64 i + tid / 4, step (tid & 3) ^ pq_swz(q) (= pq_swz(tid / 4)); scale
-    // slot tid holds row tid.
+    // q = 64 i + tid / 4, step (tid & 3) ^ pq_swz(q) (= pq_swz(tid / 4)).
+    // q4_1 scale slot tid (16 B) holds row tid; NVFP4 scale dword slots
+    // i * 256 + tid hold dword tid & 1 of row 128 i + tid / 2 (4-byte copies:
+    // a row's 8 bytes of a macro are only 8-byte aligned in the matrix).
     const __amdgpu_buffer_rsrc_t rw = buf_rsrc(MODE == 0 ? eb : eb + 2 * (size_t)mb, MODE == 0 ? 2 * mb : mb);
     auto wrow = [&](int q, uint32_t &mat) {
         mat = (MODE == 0 && q >= 128) ? mb : 0u;
@@ -1093,14 +1128,21 @@ __global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfPa
         const uint32_t ra = wrow(64 * i + (tid >> 2), mat);
         co[i] = mat + ra * (uint32_t)(K / 2) + 16 * ((tid & 3) ^ pq_swz(tid >> 2));
     }
-    uint32_t so;
-    {
+    uint32_t so[FMT == FMT_Q4_1 ? 1 : 2];
+    if constexpr (FMT == FMT_Q4_1) {
         uint32_t mat;
         const uint32_t ra = wrow(tid, mat);
-        so = mat + (uint32_t)ROWS_A * (K / 2) + ra * (uint32_t)(K / 32) * 4;
+        so[0] = mat + (uint32_t)ROWS_A * (K / 2) + ra * (uint32_t)(K / 32) * 4;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            uint32_t mat;
+            const uint32_t ra = wrow(128 * i + (tid >> 1), mat);
+            so[i] = mat + (uint32_t)ROWS_A * (K / 2) + ra * (uint32_t)(K / 16) + 4 * (tid & 1);
+        }
     }
     const int NK = K / 32, NM = (NK + PQ_MS - 1) / PQ_MS;
-    uint32_t sc0[PQ_MS], sc1[PQ_MS];  // {d, m} of the current macro, rows lrow0 and lrow1
+    uint32_t sc0[PQ_MS], sc1[PQ_MS];  // scale words of the current macro, rows lrow0 and lrow1
 
     f32x16_t acc[2][NBLK];
 #pragma unroll
@@ -1117,8 +1159,13 @@ __global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfPa
     do {                                                                                                           \
         uint8_t *cb_ = (b) == 0 ? c0s : c1s;                                                                       \
         uint8_t *sb_ = ((b) == 0 ? c0s : c1s) + PQ_SOFF;                                                           \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(sb_ + 16 * 64 * wave), 16, so, 4 * PQ_MS * (m), 0, \
-                                                 0);                                                               \
+        if constexpr (FMT == FMT_Q4_1) {                                                                           \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(sb_ + 16 * 64 * wave), 16, so[0],            \
+                                                     4 * PQ_MS * (m), 0, 0);                                       \
+        } else {                                                                                                   \
+            _Pragma("unroll") for (int i_ = 0; i_ < 2; i_++) __builtin_amdgcn_raw_ptr_buffer_load_lds(             \
+                rw, (lds_void *)(sb_ + 4 * (i_ * 256 + 64 * wave)), 4, so[i_], 2 * PQ_MS * (m), 0, 0);             \
+        }                                                                                                          \
         _Pragma("unroll") for (int i_ = 0; i_ < 2; i_++) __builtin_amdgcn_raw_ptr_buffer_load_lds(                 \
             rw, (lds_void *)(cb_ + 16 * (i_ * 256 + 64 * wave)), 16, co[i_], 16 * PQ_MS * (m), 0, 0);              \
     } while (0)
@@ -1136,10 +1183,17 @@ __global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfPa
 #define PQ_READ_SC(b)                                                                                              \
     do {                                                                                                           \
         const uint8_t *sb_ = ((b) == 0 ? c0s : c1s) + PQ_SOFF;                                                     \
-        const uint4 v0_ = *reinterpret_cast<const uint4 *>(sb_ + lrow0 * 16);                                      \
-        const uint4 v1_ = *reinterpret_cast<const uint4 *>(sb_ + lrow1 * 16);                                      \
-        sc0[0] = v0_.x; sc0[1] = v0_.y; sc0[2] = v0_.z; sc0[3] = v0_.w;                                            \
-        sc1[0] = v1_.x; sc1[1] = v1_.y; sc1[2] = v1_.z; sc1[3] = v1_.w;                                            \
+        if constexpr (FMT == FMT_Q4_1) {                                                                           \
+            const uint4 v0_ = *reinterpret_cast<const uint4 *>(sb_ + lrow0 * 16);                                  \
+            const uint4 v1_ = *reinterpret_cast<const uint4 *>(sb_ + lrow1 * 16);                                  \
+            sc0[0] = v0_.x; sc0[1] = v0_.y; sc0[2] = v0_.z; sc0[3] = v0_.w;                                        \
+            sc1[0] = v1_.x; sc1[1] = v1_.y; sc1[2] = v1_.z; sc1[3] = v1_.w;                                        \
+        } else {                                                                                                   \
+            const uint2 v0_ = *reinterpret_cast<const uint2 *>(sb_ + lrow0 * 8);                                   \
+            const uint2 v1_ = *reinterpret_cast<const uint2 *>(sb_ + lrow1 * 8);                                   \
+            sc0[0] = v0_.x & 0xFFFFu; sc0[1] = v0_.x >> 16; sc0[2] = v0_.y & 0xFFFFu; sc0[3] = v0_.y >> 16;        \
+            sc1[0] = v1_.x & 0xFFFFu; sc1[1] = v1_.x >> 16; sc1[2] = v1_.y & 0xFFFFu; sc1[3] = v1_.y >> 16;        \
+        }                                                                                                          \
     } while (0)
 
     PQ_ISSUE_W1(0, 0);
@@ -1153,23 +1207,16 @@ __global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfPa
     // weights of step 0 in MFMA operand form; each step then dequantises the
     // next step's weights while its own MFMAs run
     half8_t af[2][2];
-    {
-        WRaw<FMT_Q4_1> w0, w1;
-        w0.c = *reinterpret_cast<const uint2 *>(c0s + lrow0 * 64 + 16 * pq_swz(lrow0) + 8 * g);
-        w0.dm = sc0[0];
-        w1.c = *reinterpret_cast<const uint2 *>(c0s + lrow1 * 64 + 16 * pq_swz(lrow1) + 8 * g);
-        w1.dm = sc1[0];
-        dequant_frag<FMT_Q4_1>(w0, af[0][0], af[0][1]);
-        dequant_frag<FMT_Q4_1>(w1, af[1][0], af[1][1]);
-    }
+    dequant_frag<FMT>(pq_frag<FMT>(c0s, lrow0, 0, g, sc0[0]), af[0][0], af[0][1]);
+    dequant_frag<FMT>(pq_frag<FMT>(c0s, lrow1, 0, g, sc1[0]), af[1][0], af[1][1]);
 
     static_assert(PQ_UNROLL % (2 * PQ_MS) == 0 && PQ_UNROLL % PF_NS == 0 && PQ_MS == 4, "stage indices per trip");
     // The main loop, instantiated for tiles of at most 32 rows (the partial
     // tiles of most experts), of at most 128 and of up to BM rows: the
     // token-block count fixes the MFMAs of a step.  Step kb waits until
     // token stage kb has landed (only the copies of the two later steps may
-    // be pending: XCH token copies each, plus W1 (3) after a macro's first
-    // step and W2 (2) after its second); at a macro's last step it also waits
+    // be pending: XCH token copies each, plus W1 (W1N) after a macro's first
+    // step and W2 (W2N) after its second); at a macro's last step it also waits
     // for the next macro's W2, whose codes it dequantises for the next step.
     // The next macro's scales are read at that step too (its W1 copy came
     // before this step's token stage).
@@ -1183,9 +1230,9 @@ _Pragma("unroll")                                                               
             if (st == 0)                                                                                               \
                 wait_vmcnt<2 * XCH>();                                                                                 \
             else if (st == 1)                                                                                          \
-                wait_vmcnt<2 * XCH + 3>();                                                                             \
+                wait_vmcnt<2 * XCH + W1N>();                                                                           \
             else if (st == 2)                                                                                          \
-                wait_vmcnt<2 * XCH + 3 + 2>();                                                                         \
+                wait_vmcnt<2 * XCH + W1N + W2N>();                                                                     \
             else                                                                                                       \
                 wait_vmcnt<2 * XCH>();                                                                                 \
             pf_barrier();                                                                                              \
@@ -1197,13 +1244,8 @@ _Pragma("unroll")                                                               
             const int un = u + 1, stn = un % PQ_MS;                                                                    \
             if (stn == 0) PQ_READ_SC((un / PQ_MS) % 2);                                                                \
             const uint8_t *cb = (un / PQ_MS) % 2 == 0 ? c0s : c1s;                                                     \
-            WRaw<FMT_Q4_1> w0, w1;                                                                                     \
-            w0.c = *reinterpret_cast<const uint2 *>(cb + lrow0 * 64 + 16 * (stn ^ pq_swz(lrow0)) + 8 * g);             \
-            w0.dm = sc0[stn];                                                                                          \
-            w1.c = *reinterpret_cast<const uint2 *>(cb + lrow1 * 64 + 16 * (stn ^ pq_swz(lrow1)) + 8 * g);             \
-            w1.dm = sc1[stn];                                                                                          \
-            dequant_frag<FMT_Q4_1>(w0, af[0][0], af[0][1]);                                                            \
-            dequant_frag<FMT_Q4_1>(w1, af[1][0], af[1][1]);                                                            \
+            dequant_frag<FMT>(pq_frag<FMT>(cb, lrow0, stn, g, sc0[stn]), af[0][0], af[0][1]);                          \
+            dequant_frag<FMT>(pq_frag<FMT>(cb, lrow1, stn, g, sc1[stn]), af[1][0], af[1][1]);                          \
         }                                                                                                              \
     }
     if (nb == 1) {
@@ -1393,10 +1435,19 @@ unsigned pf_gemm_grid(int tiles_max, int MT) { return (unsigned)(8 * MT * ((tile
 template <int FMT>
 void launch_gemms(const PfParams &p, hipStream_t st) {
     const int mt0 = (p.F + 127) / 128, mt1 = (p.D + 255) / 256;
-    if constexpr (FMT == FMT_Q4_1) {
-        MOE_LAUNCH(4, (pf_gemm_q4<0, PQ_BM>), dim3(pf_gemm_grid(p.tiles_max, mt0)), dim3(PF_THREADS), st, p);
-        MOE_LAUNCH(5, (pf_gemm_q4<1, PQ_BM>), dim3(pf_gemm_grid(p.tiles_max, mt1)), dim3(PF_THREADS), st, p);
-    } else {
+    // pf_gemm_q4 copies a row's NVFP4 block scales of a macro-stage as two
+    // dwords, which must be 4-byte aligned in the matrix: K / 16 a multiple
+    // of 4 for both matrices (d_model and d_ff multiples of 64); other shapes
+    // take the one-step pipeline of pf_gemm
+    const bool macro = FMT == FMT_Q4_1 || (FMT == FMT_NVFP4 && p.D % 64 == 0 && p.F % 64 == 0);
+    if constexpr (FMT == FMT_Q4_1 || FMT == FMT_NVFP4) {
+        if (macro) {
+            MOE_LAUNCH(4, (pf_gemm_q4<FMT, 0, PQ_BM>), dim3(pf_gemm_grid(p.tiles_max, mt0)), dim3(PF_THREADS), st, p);
+            MOE_LAUNCH(5, (pf_gemm_q4<FMT, 1, PQ_BM>), dim3(pf_gemm_grid(p.tiles_max, mt1)), dim3(PF_THREADS), st, p);
+            return;
+        }
+    }
+    if constexpr (FMT != FMT_Q4_1) {
         MOE_LAUNCH(4, (pf_gemm<FMT, 0>), dim3(pf_gemm_grid(p.tiles_max, mt0)), dim3(PF_THREADS), st, p);
         MOE_LAUNCH(5, (pf_gemm<FMT, 1>), dim3(pf_gemm_grid(p.tiles_max, mt1)), dim3(PF_THREADS), st, p);
     }

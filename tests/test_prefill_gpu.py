@@ -127,6 +127,18 @@ def test_prefill_ragged_shapes(wfmt, T, bf16):
     _prefill_case(host, dev, _x(T, 96, draw=T, bf16=bf16), f"prefill ragged {wfmt} T={T}")
 
 
+@pytest.mark.parametrize("wfmt", ["q4_1", "nvfp4"])
+@pytest.mark.parametrize("T,bf16", [(77, True), (130, False)])
+def test_prefill_macro_stage_ragged_shapes(wfmt, T, bf16):
+    # d_model 192 and d_ff 320: the 4-bit GEMMs' weight macro-stages of 4
+    # reduction steps end part-way (6 and 10 steps), the last 128-feature and
+    # 256-row weight tiles are partial, and NVFP4 takes the macro-stage
+    # kernel (both sizes multiples of 64) rather than the one-step one
+    dims = gen.LayerDims(192, 320, n_routed=24, n_shared=1, top_k=4, wfmt=wfmt)
+    host, dev = _layer(dims, cfg_id=22)
+    _prefill_case(host, dev, _x(T, 192, draw=T, bf16=bf16), f"prefill macro ragged {wfmt} T={T}")
+
+
 def test_prefill_q4_1_zipf_full_width():
     dims = gen.WORKLOADS["c2_layer_q4_1"]["dims"]
     host, dev = _layer(dims, cfg_id=5, zipf_s=1.1)
