@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="stack_q4_1_b1",
-                    choices=["stack_q4_1_b1", "stack_nvfp4_b1", "stack_nvfp4_b8", "prefill_q4_1", "sweep_q4_1",
+                    choices=["stack_q4_1_b1", "stack_nvfp4_b1", "stack_nvfp4_b8", "prefill_q4_1", "prefill_nvfp4", "sweep_q4_1",
                              "lm_head_q4_1", "lm_head_nvfp4", "lm_head_bf16", "attn_swa", "attn_full128k"])
     ap.add_argument("--layers", type=int, default=47)
     ap.add_argument("--decode-path", default="kernels", choices=["kernels", "persistent"],
@@ -127,12 +127,12 @@ _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE K
 # GRBM_GUI_ACTIVE over its 8 XCDs, so utilisation = (busy / 1024) / (active / 8);
 # one MOP is 512 FLOPs of work issued to the matrix cores.
 PREFILL_MFMA_COUNTERS = dict(
-    source_digest="a3d7b621146f8ab7",
-    # means per dispatch over the 14 dispatches of each GEMM in one run
-    pf_gemm_gateup=dict(GRBM_GUI_ACTIVE=2417312.71, SQ_VALU_MFMA_BUSY_CYCLES=130285568.0,
-                        SQ_INSTS_VALU_MFMA_MOPS_F16=260571136.0, SQ_BUSY_CYCLES=8465129.0, duration_us=154.54),
-    pf_gemm_down=dict(GRBM_GUI_ACTIVE=1613752.57, SQ_VALU_MFMA_BUSY_CYCLES=65142784.0,
-                      SQ_INSTS_VALU_MFMA_MOPS_F16=130285568.0, SQ_BUSY_CYCLES=5553104.71, duration_us=93.83),
+    source_digest="88e0bbf19d33fe84",
+    # q4_1 layer: means per dispatch over the 14 dispatches of each GEMM in one run
+    pf_gemm_gateup=dict(GRBM_GUI_ACTIVE=2423730.14, SQ_VALU_MFMA_BUSY_CYCLES=130285568.0,
+                        SQ_INSTS_VALU_MFMA_MOPS_F16=260571136.0, SQ_BUSY_CYCLES=8467651.36, duration_us=152.31),
+    pf_gemm_down=dict(GRBM_GUI_ACTIVE=1605172.0, SQ_VALU_MFMA_BUSY_CYCLES=65142784.0,
+                      SQ_INSTS_VALU_MFMA_MOPS_F16=130285568.0, SQ_BUSY_CYCLES=5491608.71, duration_us=92.01),
 )
 
 
@@ -169,9 +169,11 @@ COUNTER_TRAFFIC = {
     ("stack_nvfp4_b8", "bn_router"): _traffic("57c1d2057ded3856", 788.51, 64.0),
     ("stack_nvfp4_b8", "bn_gateup"): _traffic("57c1d2057ded3856", 26673.5191, 112.4278),
     ("stack_nvfp4_b8", "bn_down"): _traffic("57c1d2057ded3856", 13520.6781, 64.0),
-    # 4096-token q4_1 prefill
-    ("prefill_q4_1", "pf_gemm_gateup"): _traffic("a3d7b621146f8ab7", 227413.3854, 28677.7604),
-    ("prefill_q4_1", "pf_gemm_down"): _traffic("a3d7b621146f8ab7", 82017.2969, 114688.0),
+    # 4096-token prefill, q4_1 and NVFP4
+    ("prefill_q4_1", "pf_gemm_gateup"): _traffic("88e0bbf19d33fe84", 226688.9219, 28677.2188),
+    ("prefill_q4_1", "pf_gemm_down"): _traffic("88e0bbf19d33fe84", 81872.3958, 114688.0),
+    ("prefill_nvfp4", "pf_gemm_gateup"): _traffic("88e0bbf19d33fe84", 232797.2969, 28676.1198),
+    ("prefill_nvfp4", "pf_gemm_down"): _traffic("88e0bbf19d33fe84", 75056.7448, 114688.0),
     # q4_1 output layer, 1 token
     ("lm_head_q4_1_t1", "lm_head_kernel"): _traffic("c3b94d4e2367e0b5", 91654.112, 572.2188),
     # full-attention layer at 128k positions
@@ -443,18 +445,21 @@ def cpu_baseline_stack(args, hosts, xs, dims, stack, ws):
                                    rel_l2_final=err))
 
 
-def bench_prefill(args):
-    """4096 bf16 tokens through one q4_1 layer with a Zipf(1.1) router prior."""
+def bench_prefill(args, wfmt="q4_1"):
+    """4096 bf16 tokens through one 4-bit layer (q4_1, or the same layer in
+    NVFP4) with a Zipf(1.1) router prior."""
     from sparse_moe_decode_route_amd import binding as B
     from sparse_moe_decode_route_amd import inputs as gen
-    dims = gen.LayerDims(2048, 512, wfmt="q4_1")
+    dims = gen.LayerDims(2048, 512, wfmt=wfmt)
     T = 4096
     lay = gen.make_layer(dims, cfg_id=5, layer=0, zipf_s=1.1, device="cuda")
     packed = torch.empty_like(lay.experts)
     B.repack_weights(dims, lay.experts, packed, dims.n_experts)
     torch.cuda.synchronize()
-    dev = B.DeviceLayer(dims, lay.router, lay.router_bias, packed, None)
-    host = None if args.no_cpu else gen.Layer(dims, lay.router.cpu(), lay.router_bias.cpu(), lay.experts.cpu(), None)
+    ts = lay.tensor_scale if wfmt == "nvfp4" else None
+    dev = B.DeviceLayer(dims, lay.router, lay.router_bias, packed, ts)
+    host = None if args.no_cpu else gen.Layer(dims, lay.router.cpu(), lay.router_bias.cpu(), lay.experts.cpu(),
+                                               None if ts is None else ts.cpu())
     del lay
     x = gen.to_bf16(gen.make_hidden(5, T, 2048, draw=0, device="cuda"))
     ws = B.workspace(dims, T)
@@ -513,7 +518,7 @@ def bench_prefill(args):
     dom = "pf_gemm_gateup"
     ach = fl_gu / (kus[dom] * 1e-6) / 1e12
     def pf_traffic_of(k):
-        tr = COUNTER_TRAFFIC.get(("prefill_q4_1", k))
+        tr = COUNTER_TRAFFIC.get((f"prefill_{wfmt}", k))
         return (tr["fetch_bytes"] + tr["write_bytes"]
                 if tr is not None and tr["source_digest"] == source_digest(PREFILL_SOURCES) else None)
 
@@ -530,9 +535,9 @@ def bench_prefill(args):
         value=round(T / (ms * 1e-3), 1), unit="tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f16",
         data="synthetic",
-        config=dict(workload="moe_prefill_q4_1_t4096: 4096 bf16 tokens (N(0,1) rounded) through one layer, d_model "
-                             "2048, d_ff 512, 256 routed + 1 shared, top-6, q4_1 experts, Zipf(1.1) router prior; "
-                             "MFMA operands fp16, fp32 accumulate",
+        config=dict(workload=f"moe_prefill_{wfmt}_t4096: 4096 bf16 tokens (N(0,1) rounded) through one layer, "
+                             f"d_model 2048, d_ff 512, 256 routed + 1 shared, top-6, {wfmt} experts, Zipf(1.1) "
+                             "router prior; MFMA operands fp16, fp32 accumulate",
                     global_batch=T, seq_len=T, parallelism="single-gpu",
                     flops_per_step=fl_all, layer_tflops=round(fl_all / (ms * 1e-3) / 1e12, 1),
                     layer_mfma_frac=round(fl_all / (ms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
@@ -544,7 +549,8 @@ def bench_prefill(args):
                       unit="TFLOP/s", frac=round(ach / MFMA_FP16_PEAK_TFLOPS, 4), traffic=pf_traffic,
                       flops_per_launch=fl_gu, us_per_launch=round(kus[dom], 2),
                       timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream",
-                      per_kernel=per_kernel, mfma_counters=prefill_mfma_counters(fl_gu, fl_dn)),
+                      per_kernel=per_kernel,
+                      mfma_counters=prefill_mfma_counters(fl_gu, fl_dn) if wfmt == "q4_1" else None),
         cpu_baseline=cpu,
     )
 
@@ -565,7 +571,7 @@ def cpu_baseline_prefill(args, host, x):
         list(ex.map(lambda r: oracle.layer_forward(host, xa[r]), [c for c in chunks if len(c)]))
     dt = time.time() - t0
     return dict(value=round(n / dt, 2), unit="tok/s", cores=W, kind="oracle",
-                sample=f"{n} of the 4096 bf16 tokens through the Zipf-skewed q4_1 layer, fp64 C, {W} threads, "
+                sample=f"{n} of the 4096 bf16 tokens through the Zipf-skewed {host.dims.wfmt} layer, fp64 C, {W} threads, "
                        f"{dt:.1f}s", cpu_model=cpu_model(), os_cpu_count=os.cpu_count())
 
 
@@ -923,7 +929,7 @@ def main():
     elif args.workload == "stack_nvfp4_b8":
         out = bench_stack(args, "nvfp4", 8)
     else:
-        out = bench_prefill(args)
+        out = bench_prefill(args, args.workload[len("prefill_"):])
     if args.copy_calibration:
         copy_calibration()
     print(json.dumps(out), flush=True)
