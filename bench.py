@@ -162,7 +162,7 @@ def _traffic(digest: str, fetch_kib: float, write_kib: float) -> dict:
 
 COUNTER_TRAFFIC = {
     # batch-1 q4_1 stack
-    ("stack_q4_1_b1", "b1_route_shared"): _traffic("3873ae7b4315216b", 1233.1619, 24.0),
+    ("stack_q4_1_b1", "b1_route"): _traffic("3873ae7b4315216b", 1233.1619, 24.0),
     ("stack_q4_1_b1", "b1_topk_gateup"): _traffic("3873ae7b4315216b", 3937.0521, 12.6691),
     ("stack_q4_1_b1", "b1_down"): _traffic("3873ae7b4315216b", 2323.0461, 8.0),
     # batch-8 NVFP4 stack
@@ -184,9 +184,10 @@ COUNTER_TRAFFIC = {
 def kernel_algo_bytes(dims, T: int, routed_union: float):
     """Algorithmic bytes one launch of each decode kernel must move.
 
-    Weights: packed bytes of the matrices the kernel reads (router bf16; gate
-    and up of the shared experts in the first kernel, of the routed union in
-    the gate/up kernel; down of every active expert in the last).  Activations:
+    Weights: packed bytes of the matrices the kernel reads (router bf16 in the
+    first kernel; gate and up of the routed union and the shared experts in
+    the batch-1 gate/up kernel, of the shared experts in the general path's
+    first kernel; down of every active expert in the last).  Activations:
     fp32 x in, logits, h and y as produced and consumed between kernels."""
     from sparse_moe_decode_route_amd import inputs as gen
     D, F, E, S = dims.d_model, dims.d_ff, dims.n_routed, dims.n_shared
@@ -195,13 +196,15 @@ def kernel_algo_bytes(dims, T: int, routed_union: float):
     U = routed_union
     a = E * D * 2 + S * 2 * gu + T * D * 4 + T * E * 4 + S * T * F * 4
     b = T * E * 4 + U * 2 * gu + T * D * 4 + U * T * F * 4
+    b1_a = E * D * 2 + T * D * 4 + T * E * 4
+    b1_b = T * E * 4 + (U + S) * 2 * gu + T * D * 4 + (U + S) * T * F * 4
     c = (U + S) * dn + (U + S) * T * F * 4 + T * D * 4
     K = dims.top_k
     pairs = T * K + S * T  # (expert, token) rows of h
     bn = {"bn_router": E * D * 2 + T * D * 4 + T * E * 4,
           "bn_gateup": (U + S) * 2 * gu + T * D * 4 + T * E * 4 + pairs * F * 4,
           "bn_down": (U + S) * dn + pairs * F * 4 + T * D * 4 + T * E * 4}
-    return {"b1_route_shared": a, "b1_topk_gateup": b, "b1_down": c,
+    return {"b1_route": b1_a, "b1_topk_gateup": b1_b, "b1_down": c,
             "phase_a_kernel": a, "select_kernel": T * E * 4, "gateup_kernel": b, "down_kernel": c, **bn}
 
 

@@ -202,7 +202,7 @@ hipError_t launch_any(const moe::DecodeParams &p, hipStream_t st, int *path = nu
 }
 
 // Kernel names of one layer's slots, per path (slot order of MOE_LAUNCH).
-const char *const kB1Names = "b1_route_shared;b1_topk_gateup;b1_down";
+const char *const kB1Names = "b1_route;b1_topk_gateup;b1_down";
 const char *const kGenericNames = "phase_a_kernel;select_kernel;gateup_kernel;down_kernel";
 const char *const kBnNames = "bn_router;bn_gateup;bn_down";
 const char *const kPsNames = "ps_stack;ps_clear";

@@ -1,12 +1,16 @@
 // Batch-1 decode path: three kernels per layer (the persistent kernel of
 // moe_stack_persist.hip replaces it for the shapes that kernel is built for).
 //
-//   A  router logits (one wave per routed expert row) and the shared
-//      experts' h = silu(Wg x) * (Wu x) (one wave per pair of features).
-//   B  every wave finds its own expert, the j-th largest logit (DPP argmax
-//      rounds, no barrier and no separate selection kernel), then computes h
-//      for two features of that expert; wave 0 of the first blocks also runs
-//      the full selection with weights for the routing outputs.
+//   A  router logits (one wave per routed expert row); in a stack each wave
+//      also applies the RMSNorm of the previous layer's output, and block 0
+//      writes the normalised x.
+//   B  h = silu(Wg x) * (Wu x), two features per wave, for every active
+//      expert: the shared experts' waves issue their loads at once (they do
+//      not depend on the routing, so they stream while the routed waves wait
+//      for the logits); every routed wave finds its own expert, the j-th
+//      largest logit (DPP argmax rounds, no barrier and no separate selection
+//      kernel); wave 0 of the first blocks also runs the full selection with
+//      weights for the routing outputs.
 //   C  down projection with the weighted combine: a block owns 8 output
 //      rows, each of its eight waves takes one active expert, h is staged in
 //      LDS, the waves' partial sums are added in a fixed order.
@@ -93,87 +97,75 @@ __device__ __forceinline__ void gateup_finish(const GateUp<FMT, UPLD, RG> &g, co
 }
 
 // ---------------------------------------------------------------------------
-// A: router rows + shared experts' gate/up (one wave per block)
+// A: router rows (one wave per block)
 // ---------------------------------------------------------------------------
-template <int FMT, int UPLR, int UPLD, bool SCALED>
-__global__ void __launch_bounds__(MOE_WAVE) b1_route_shared(DecodeParams p) {
+template <int UPLR, bool SCALED>
+__global__ void __launch_bounds__(MOE_WAVE) b1_route(DecodeParams p) {
     const int lane = threadIdx.x;
     constexpr bool scaled = SCALED;  // compile-time: no branch around loads
     const float *xin = scaled ? p.x_prev : p.x;
     float4 yr[2 * UPLR];
-    if ((int)blockIdx.x < p.E) {
-        // the rms partition is exactly this wave's router units: x = yr * xs
-        const int e = blockIdx.x;
-        load_rms_part<UPLR>(yr, xin);
-        Mat mr{(const uint8_t *)p.router, p.E, p.D, 1.f};
-        WUnit w[UPLR];
+    // the rms partition is exactly this wave's router units: x = yr * xs
+    const int e = blockIdx.x;
+    load_rms_part<UPLR>(yr, xin);
+    Mat mr{(const uint8_t *)p.router, p.E, p.D, 1.f};
+    WUnit w[UPLR];
 #pragma unroll
-        for (int i = 0; i < UPLR; i++) w[i] = load_unit<FMT_BF16>(mr, e, lane + MOE_WAVE * i);
-        __builtin_amdgcn_sched_barrier(0);
-        const float xs = scaled ? inv_rms_from<UPLR>(yr) : 1.f;
-        if (scaled && e == 0) {
-#pragma unroll
-            for (int i = 0; i < UPLR; i++) {
-                const float4 a = yr[2 * i], b = yr[2 * i + 1];
-                ((float4 *)p.xbuf)[2 * lane + 128 * i] = make_float4(a.x * xs, a.y * xs, a.z * xs, a.w * xs);
-                ((float4 *)p.xbuf)[2 * lane + 1 + 128 * i] = make_float4(b.x * xs, b.y * xs, b.z * xs, b.w * xs);
-            }
-        }
-        float acc = 0.f;
+    for (int i = 0; i < UPLR; i++) w[i] = load_unit<FMT_BF16>(mr, e, lane + MOE_WAVE * i);
+    __builtin_amdgcn_sched_barrier(0);
+    const float xs = scaled ? inv_rms_from<UPLR>(yr) : 1.f;
+    if (scaled && e == 0) {
 #pragma unroll
         for (int i = 0; i < UPLR; i++) {
-            XUnit<FMT_BF16> xv;
             const float4 a = yr[2 * i], b = yr[2 * i + 1];
-            xv.v[0] = a.x * xs;
-            xv.v[1] = a.y * xs;
-            xv.v[2] = a.z * xs;
-            xv.v[3] = a.w * xs;
-            xv.v[4] = b.x * xs;
-            xv.v[5] = b.y * xs;
-            xv.v[6] = b.z * xs;
-            xv.v[7] = b.w * xs;
-            xv.sum = 0.f;
-            acc += unit_dot<FMT_BF16>(w[i], xv, 1.f);
-        }
-        const float s = wave_sum(acc);
-        if (lane == 0) p.logits[e] = p.bias ? s + p.bias[e] : s;
-        return;
-    }
-    const int per_expert = p.F / B1_RG;
-    const int v = blockIdx.x - p.E;
-    const int s = v / per_expert, f0 = (v % per_expert) * B1_RG;
-    if (scaled) load_rms_part<UPLR>(yr, p.x_prev);
-    XUnit<FMT> xv[UPLD];
-#pragma unroll
-    for (int i = 0; i < UPLD; i++) load_x<FMT>(xv[i], xin, lane + MOE_WAVE * i);
-    GateUp<FMT, UPLD, B1_RG> g;
-    gateup_issue<FMT, UPLD, B1_RG>(g, p, p.E + s, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (scaled) {
-        const float xs = inv_rms_from<UPLR>(yr);
-#pragma unroll
-        for (int i = 0; i < UPLD; i++) {
-            float sum = 0.f;
-#pragma unroll
-            for (int k = 0; k < Unit<FMT>::E; k++) {
-                xv[i].v[k] *= xs;
-                sum += xv[i].v[k];
-            }
-            if (FMT == FMT_Q4_1) xv[i].sum = sum;
+            ((float4 *)p.xbuf)[2 * lane + 128 * i] = make_float4(a.x * xs, a.y * xs, a.z * xs, a.w * xs);
+            ((float4 *)p.xbuf)[2 * lane + 1 + 128 * i] = make_float4(b.x * xs, b.y * xs, b.z * xs, b.w * xs);
         }
     }
-    gateup_finish<FMT, UPLD, B1_RG>(g, p, s, f0, xv);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < UPLR; i++) {
+        XUnit<FMT_BF16> xv;
+        const float4 a = yr[2 * i], b = yr[2 * i + 1];
+        xv.v[0] = a.x * xs;
+        xv.v[1] = a.y * xs;
+        xv.v[2] = a.z * xs;
+        xv.v[3] = a.w * xs;
+        xv.v[4] = b.x * xs;
+        xv.v[5] = b.y * xs;
+        xv.v[6] = b.z * xs;
+        xv.v[7] = b.w * xs;
+        xv.sum = 0.f;
+        acc += unit_dot<FMT_BF16>(w[i], xv, 1.f);
+    }
+    const float s = wave_sum(acc);
+    if (lane == 0) p.logits[e] = p.bias ? s + p.bias[e] : s;
 }
 
 // ---------------------------------------------------------------------------
-// B: top-k in every wave, routed experts' gate/up
+// B: every active expert's gate/up; top-k in every routed wave
 // ---------------------------------------------------------------------------
 template <int FMT, int UPLD>
 __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_B) b1_topk_gateup(DecodeParams p) {
     const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
     const int per_expert = p.F / B1_RG;
     const int gw = blockIdx.x * B1_WAVES_B + wave;
+    // waves of routed slot j < K, then of shared expert j - K
     const int j = gw / per_expert, f0 = (gw % per_expert) * B1_RG;
+    const float *xin = p.x_prev ? p.xbuf : p.x;
+    if (j >= p.K) {
+        // a shared expert: no routing dependency, its loads go out at once
+        if (j >= p.K + p.S) return;
+        const int s = j - p.K;
+        GateUp<FMT, UPLD, B1_RG> g;
+        gateup_issue<FMT, UPLD, B1_RG>(g, p, p.E + s, f0);
+        XUnit<FMT> xv[UPLD];
+#pragma unroll
+        for (int i = 0; i < UPLD; i++) load_x<FMT>(xv[i], xin, lane + MOE_WAVE * i);
+        __builtin_amdgcn_sched_barrier(0);
+        gateup_finish<FMT, UPLD, B1_RG>(g, p, s, f0, xv);
+        return;
+    }
     float lv[4];
     wave_topk_load(p.logits, p.E, lv);
     int e = -1;
@@ -213,7 +205,6 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_B) b1_topk_gateup(DecodePar
             if (lane == 0) p.meta[0] = p.S + p.K;
         }
     }
-    if (j >= p.K) return;
     // every other wave finds its own expert (the j-th largest logit): no
     // barrier between the selection and the weight loads
     if (e < 0) e = wave_topk_nth(lv, p.E, j);
@@ -221,7 +212,6 @@ __global__ void __launch_bounds__(MOE_WAVE *B1_WAVES_B) b1_topk_gateup(DecodePar
     gateup_issue<FMT, UPLD, B1_RG>(g, p, e, f0);
     // x in the same round trip as the weights (loaded before the top-k, a
     // wait for the logits would also wait for these)
-    const float *xin = p.x_prev ? p.xbuf : p.x;
     XUnit<FMT> xv[UPLD];
 #pragma unroll
     for (int i = 0; i < UPLD; i++) load_x<FMT>(xv[i], xin, lane + MOE_WAVE * i);
@@ -346,12 +336,12 @@ hipError_t launch_fmt(const DecodeParams &pin, hipStream_t st, int uplr, int lpr
     DecodeParams p = pin;
     p.b1_ncopy = std::min(8, (p.K * (p.F / B1_RG) + B1_WAVES_B - 1) / B1_WAVES_B);
     const int per_expert = p.F / B1_RG;
-    const int grid_a = p.E + p.S * per_expert;
+    const int grid_a = p.E;
 #define MOE_A(U)                                                                          \
     if (p.x_prev)                                                                         \
-        MOE_LAUNCH(0, (b1_route_shared<FMT, U, UPLD, true>), dim3(grid_a), dim3(MOE_WAVE), st, p); \
+        MOE_LAUNCH(0, (b1_route<U, true>), dim3(grid_a), dim3(MOE_WAVE), st, p);          \
     else                                                                                  \
-        MOE_LAUNCH(0, (b1_route_shared<FMT, U, UPLD, false>), dim3(grid_a), dim3(MOE_WAVE), st, p);
+        MOE_LAUNCH(0, (b1_route<U, false>), dim3(grid_a), dim3(MOE_WAVE), st, p);
     switch (uplr) {
     case 1: MOE_A(1) break;
     case 2: MOE_A(2) break;
@@ -359,7 +349,7 @@ hipError_t launch_fmt(const DecodeParams &pin, hipStream_t st, int uplr, int lpr
     default: MOE_A(8) break;
     }
 #undef MOE_A
-    const int waves_b = p.K * per_expert;
+    const int waves_b = (p.K + p.S) * per_expert;
     const int grid_b = (waves_b + B1_WAVES_B - 1) / B1_WAVES_B;
     MOE_LAUNCH(1, (b1_topk_gateup<FMT, UPLD>), dim3(grid_b), dim3(MOE_WAVE * B1_WAVES_B), st, p);
     const int rows_per_block = (MOE_WAVE / lpr_f) * B1_RR;

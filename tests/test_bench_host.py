@@ -21,13 +21,13 @@ def test_batch1_algorithmic_bytes_per_launch():
     dims = gen.LayerDims(2048, 512, wfmt="q4_1")
     assert gen.matrix_bytes(512, 2048, "q4_1") == 655_360
     a = bench.kernel_algo_bytes(dims, 1, 6.0)
-    # router + shared gate/up + x + logits + h
-    assert a["b1_route_shared"] == 1_048_576 + 2 * 655_360 + 8_192 + 1_024 + 2_048
-    # logits + 6 experts' gate/up + x + h
-    assert a["b1_topk_gateup"] == 1_024 + 6 * 1_310_720 + 8_192 + 12_288
+    # router + x + logits
+    assert a["b1_route"] == 1_048_576 + 8_192 + 1_024
+    # logits + 7 experts' gate/up (6 routed, 1 shared) + x + h
+    assert a["b1_topk_gateup"] == 1_024 + 7 * 1_310_720 + 8_192 + 14_336
     # 7 experts' down + h + y
     assert a["b1_down"] == 7 * 655_360 + 14_336 + 8_192
-    assert a["b1_topk_gateup"] == 7_885_824 and a["b1_down"] == 4_610_048
+    assert a["b1_topk_gateup"] == 9_198_592 and a["b1_down"] == 4_610_048
 
 
 def test_small_batch_gateup_bytes_count_each_expert_once():
@@ -41,10 +41,10 @@ def test_small_batch_gateup_bytes_count_each_expert_once():
 
 def test_roofline_takes_the_longest_kernel():
     dims = gen.LayerDims(2048, 512, wfmt="q4_1")
-    us = {"b1_route_shared": 4.0, "b1_topk_gateup": 5.0, "b1_down": 4.5}
+    us = {"b1_route": 4.0, "b1_topk_gateup": 5.0, "b1_down": 4.5}
     r = bench.roofline("stack_q4_1_b1", dims, 1, 47, us, 6.0)
     assert r["kernel"] == "b1_topk_gateup" and r["bound"] == "hbm" and r["peak"] == 8000.0
-    assert r["achieved"] == pytest.approx(7_885_824 / 5e-6 / 1e9, rel=1e-4)
+    assert r["achieved"] == pytest.approx(9_198_592 / 5e-6 / 1e9, rel=1e-4)
     assert r["frac"] == pytest.approx(r["achieved"] / 8000.0, abs=1e-4)
 
 

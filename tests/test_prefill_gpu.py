@@ -160,13 +160,16 @@ def test_prefill_nvfp4_full_width():
     _prefill_case(host, dev, _x(96, dims.d_model, draw=5, bf16=True), "prefill nvfp4 T=96")
 
 
-def test_prefill_4096_tokens_sampled():
-    # the full prefill workload: 4096 bf16 tokens through one q4_1 layer with a
-    # Zipf(1.1) router prior; routing checked on every token, outputs on the
-    # first and last row of every tile of every expert plus a random sample
-    dims = gen.WORKLOADS["c5_prefill_q4_1"]["dims"]
+@pytest.mark.parametrize("wfmt", ["q4_1", "nvfp4"])
+def test_prefill_4096_tokens_sampled(wfmt):
+    # the full prefill workload: 4096 bf16 tokens through one 4-bit layer (the
+    # q4_1 layer, or the same layer in NVFP4) with a Zipf(1.1) router prior;
+    # routing checked on every token, outputs on the first and last row of
+    # every tile of every expert plus a random sample
+    dims = gen.LayerDims(2048, 512, wfmt=wfmt)
+    assert wfmt != "q4_1" or dims == gen.WORKLOADS["c5_prefill_q4_1"]["dims"]
     host, dev = _layer(dims, cfg_id=5, zipf_s=1.1)
-    idx, _ = _prefill_case(host, dev, _x(4096, dims.d_model, draw=0, bf16=True), "prefill 4096",
+    idx, _ = _prefill_case(host, dev, _x(4096, dims.d_model, draw=0, bf16=True), f"prefill 4096 {wfmt}",
                            check_all_outputs=False, n_sample=24)
     loads = np.bincount(idx.reshape(-1), minlength=dims.n_routed)
     print(f"experts hit {np.count_nonzero(loads)}, max load {loads.max()}, min nonzero {loads[loads > 0].min()}")
