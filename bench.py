@@ -162,9 +162,9 @@ def _traffic(digest: str, fetch_kib: float, write_kib: float) -> dict:
 
 COUNTER_TRAFFIC = {
     # batch-1 q4_1 stack
-    ("stack_q4_1_b1", "b1_route"): _traffic("3873ae7b4315216b", 1233.1619, 24.0),
-    ("stack_q4_1_b1", "b1_topk_gateup"): _traffic("3873ae7b4315216b", 3937.0521, 12.6691),
-    ("stack_q4_1_b1", "b1_down"): _traffic("3873ae7b4315216b", 2323.0461, 8.0),
+    ("stack_q4_1_b1", "b1_route"): _traffic("7d4ce39bbc3c9388", 563.0227, 16.0),
+    ("stack_q4_1_b1", "b1_topk_gateup"): _traffic("7d4ce39bbc3c9388", 4595.5831, 14.6691),
+    ("stack_q4_1_b1", "b1_down"): _traffic("7d4ce39bbc3c9388", 2325.5868, 8.0),
     # batch-8 NVFP4 stack
     ("stack_nvfp4_b8", "bn_router"): _traffic("57c1d2057ded3856", 788.51, 64.0),
     ("stack_nvfp4_b8", "bn_gateup"): _traffic("57c1d2057ded3856", 26673.5191, 112.4278),
