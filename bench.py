@@ -518,8 +518,13 @@ def bench_prefill(args, wfmt="q4_1"):
     fl_dn = rows * D * F * 2
     fl_rt = 2 * T * E * D
     fl_all = fl_gu + fl_dn + fl_rt
-    dom = "pf_gemm_gateup"
-    ach = fl_gu / (kus[dom] * 1e-6) / 1e12
+    # kernels that did not run report -1 (the down GEMM when it runs fused
+    # with the gate/up GEMM in one dispatch, pf_ffn)
+    kus = {k: v for k, v in kus.items() if v > 0}
+    fused = "pf_ffn" in kus
+    dom = "pf_ffn" if fused else "pf_gemm_gateup"
+    fl_dom = fl_gu + fl_dn if fused else fl_gu
+    ach = fl_dom / (kus[dom] * 1e-6) / 1e12
     def pf_traffic_of(k):
         tr = COUNTER_TRAFFIC.get((f"prefill_{wfmt}", k))
         return (tr["fetch_bytes"] + tr["write_bytes"]
@@ -527,9 +532,10 @@ def bench_prefill(args, wfmt="q4_1"):
 
     pf_traffic = pf_traffic_of(dom)
     per_kernel = {k: dict(us_per_launch=round(v, 2)) for k, v in kus.items()}
-    per_kernel["pf_gemm_down"]["traffic"] = pf_traffic_of("pf_gemm_down")
-    per_kernel["pf_gemm_gateup"]["tflops"] = round(fl_gu / (kus["pf_gemm_gateup"] * 1e-6) / 1e12, 1)
-    per_kernel["pf_gemm_down"]["tflops"] = round(fl_dn / (kus["pf_gemm_down"] * 1e-6) / 1e12, 1)
+    per_kernel[dom]["tflops"] = round(ach, 1)
+    if not fused:
+        per_kernel["pf_gemm_down"]["traffic"] = pf_traffic_of("pf_gemm_down")
+        per_kernel["pf_gemm_down"]["tflops"] = round(fl_dn / (kus["pf_gemm_down"] * 1e-6) / 1e12, 1)
     rname = "pf_router_gemm" if "pf_router_gemm" in kus else "pf_logits"
     per_kernel[rname]["tflops"] = round(fl_rt / (kus[rname] * 1e-6) / 1e12, 1)
     cpu = None if host is None else cpu_baseline_prefill(args, host, x)
@@ -550,7 +556,7 @@ def bench_prefill(args, wfmt="q4_1"):
                     kernel_source_digest=source_digest(PREFILL_SOURCES)),
         roofline=dict(bound="mfma", kernel=dom, achieved=round(ach, 1), peak=MFMA_FP16_PEAK_TFLOPS,
                       unit="TFLOP/s", frac=round(ach / MFMA_FP16_PEAK_TFLOPS, 4), traffic=pf_traffic,
-                      flops_per_launch=fl_gu, us_per_launch=round(kus[dom], 2),
+                      flops_per_launch=fl_dom, us_per_launch=round(kus[dom], 2),
                       timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream",
                       per_kernel=per_kernel,
                       mfma_counters=prefill_mfma_counters(fl_gu, fl_dn) if wfmt == "q4_1" else None),

@@ -689,7 +689,7 @@ moe_status moe_layer_forward_prefill_timed(const moe_dims *d, const moe_layer_we
         }
         (void)hipGetLastError();
         *n_kernels = moe::PREFILL_SLOTS;
-        if (names && names_cap) snprintf(names, names_cap, "%s", moe::prefill_names(act));
+        if (names && names_cap) snprintf(names, names_cap, "%s", moe::prefill_names(act, moe::prefill_fused(d->wfmt, d->d_model, d->d_ff)));
     }
     for (auto &e : ev) (void)hipEventDestroy(e);
     return s == MOE_OK ? ok() : s;

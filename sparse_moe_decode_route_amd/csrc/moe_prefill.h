@@ -31,7 +31,11 @@ struct PrefillArgs {
 // Kernel slots of the prefill path, in launch order (timing entry point);
 // names of the slots' kernels for tokens of type act (MOE_ACT_*).
 constexpr int PREFILL_SLOTS = 7;
-const char *prefill_names(int act);
+// Whether the 4-bit grouped GEMMs run fused in one dispatch (pf_ffn_q4) for
+// this format and shape.
+bool prefill_fused(int fmt, int D, int F);
+// Names of the prefill kernel slots (';'-separated), as timed.
+const char *prefill_names(int act, bool fused);
 
 size_t prefill_ws_bytes(int D, int F, int E, int S, int K, int T);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);

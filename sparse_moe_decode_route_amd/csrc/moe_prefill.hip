@@ -21,6 +21,9 @@
 //   pf_scatter  position of every (token, slot) pair in its expert's rows
 //   pf_gemm<0>  H = silu(X Wg^T) * (X Wu^T) per expert (fp16 H)
 //   pf_gemm<1>  O = coef * (H Wd^T) per expert (fp16 O, like H)
+//   pf_ffn_q4   (4-bit weights, in place of the two above) both GEMMs in
+//               one dispatch: a tile's down blocks start once its gate/up
+//               blocks have stored h
 //   pf_combine  y[t] = sum of t's rows of O in slot order
 // No floating-point atomics: integer/bitwise atomics only, so results do not
 // depend on scheduling.
@@ -39,7 +42,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int PF_BM = 128;          // rows (token slots) per tile of pf_gemm (and the bound of the tile count)
-constexpr int PQ_BM = 128;          // rows per tile of pf_gemm_q4
+constexpr int PQ_BM = 128;          // rows per tile of the 4-bit GEMMs (pf_ffn_q4)
 constexpr int PF_THREADS = 256;     // 4 waves
 constexpr int PF_MAX_TOPK = 8;
 
@@ -49,7 +52,7 @@ struct PfTile {
 
 // Workspace layout (byte offsets), shared by the host sizing and the launcher.
 struct PfWs {
-    size_t x16, logits, part, idx, w, mask, wp, off, tiles, meta, perm_tok, perm_w, pos, h, o, total;
+    size_t x16, logits, part, idx, w, mask, wp, off, tiles, meta, done, perm_tok, perm_w, pos, h, o, total;
     int NW, R, tiles_max, ksplit;
 };
 
@@ -83,6 +86,7 @@ PfWs pf_layout(int D, int F, int E, int S, int K, int T) {
     L.off = o; o = al(o + (size_t)(E + S + 1) * 4);
     L.tiles = o; o = al(o + (size_t)L.tiles_max * sizeof(PfTile));
     L.meta = o; o = al(o + 16 * 4);
+    L.done = o; o = al(o + (size_t)L.tiles_max * 4);
     L.perm_tok = o; o = al(o + (size_t)L.R * 4);
     L.perm_w = o; o = al(o + (size_t)L.R * 4);
     L.pos = o; o = al(o + (size_t)T * (K + S) * 4);
@@ -101,6 +105,7 @@ struct PfParams {
     int D, F, E, S, K, T, act, NW, R, tiles_max, want_x16;
     int ksplit;          // pf_router_gemm: reduction parts
     int BM;              // token rows per GEMM tile (tile table)
+    int g1;              // pf_ffn_q4: blocks of the gate/up role
     hipEvent_t *ev;
     size_t expert_bytes;
     const void *x;
@@ -122,6 +127,7 @@ struct PfParams {
     int32_t *off;
     PfTile *tiles;
     int32_t *meta;
+    int32_t *tile_done;  // pf_ffn_q4: gate/up blocks done per tile (zeroed by pf_scan)
     int32_t *perm_tok;
     float *perm_w;
     int32_t *pos;
@@ -383,6 +389,8 @@ __global__ void __launch_bounds__(PF_SCAN_THREADS) pf_scan(PfParams p) {
     __shared__ int tot_rows, tot_tiles;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_exp = p.E + p.S;
+    // the fused GEMM's per-tile counters start at zero on every call
+    for (int i = tid; i < p.tiles_max; i += PF_SCAN_THREADS) p.tile_done[i] = 0;
     // per routed expert (wave w: experts w, w + 16, ...): word prefixes, 64
     // words per pass; the words of the wave's 16 experts are loaded together
     // (32-bit element offsets from the scalar base keep one register per address)
@@ -431,6 +439,7 @@ __global__ void __launch_bounds__(PF_SCAN_THREADS) pf_scan(PfParams p) {
         p.off[n_exp] = tot_rows;
         p.meta[0] = n_full + tot_tiles;
         p.meta[1] = tot_rows;
+        p.meta[2] = n_full;
     }
     if (tid < n_exp) {
         for (int i = 0; i < my_full; i++) {
@@ -591,15 +600,21 @@ __device__ __forceinline__ void dequant_frag(const WRaw<FMT> &w, half8_t &s0, ha
 }
 
 // Block -> (tile, weight-row block) with an XCD-aware order.  Blocks go
-// round-robin to the 8 XCDs (block b to XCD b % 8); XCD x takes tiles x,
-// x + 8, x + 16, ... in table order, the MT blocks of a tile back to back, so
-// they share the tile's token rows in that XCD's L2, every XCD gets the same
-// share of full and partial tiles, and the table's partial tiles (last) fill
-// each XCD's tail.  Returns ti * MT + mt, or -1 past the last tile.
-__device__ __forceinline__ int xcd_tile_block(int b, int MT, int n_tiles) {
-    const int x = b & 7, j = b >> 3;
-    const int ti = x + 8 * (j / MT);
-    return ti < n_tiles ? ti * MT + j % MT : -1;
+// round-robin to the 8 XCDs (block b to XCD b % 8).  XCD x takes a
+// contiguous eighth of the full tiles, then a contiguous eighth of the partial
+// tiles (the table lists the full tiles first, in expert order), the MT
+// blocks of a tile back to back: an expert's full tiles then run on one or
+// two XCDs, which fetch its weights into their L2 once, the MT blocks of a
+// tile share its token rows in that L2, and every XCD gets as many full and
+// as many partial tiles as the others (to one), the partial ones filling its
+// tail.  Returns ti * MT + mt, or -1 past the XCD's last tile.
+__device__ __forceinline__ int xcd_tile_block(int b, int MT, int n_tiles, int n_full) {
+    const int x = b & 7, k = (b >> 3) / MT, mt = (b >> 3) % MT;
+    const int f0 = x * n_full / 8, nf = (x + 1) * n_full / 8 - f0;
+    if (k < nf) return (f0 + k) * MT + mt;
+    const int n_part = n_tiles - n_full;
+    const int p0 = x * n_part / 8, np = (x + 1) * n_part / 8 - p0;
+    return k - nf < np ? (n_full + p0 + k - nf) * MT + mt : -1;
 }
 
 // LDS bytes between consecutive lanes of a 2-byte buffer-to-LDS copy: each
@@ -891,7 +906,7 @@ __global__ void __launch_bounds__(PF_THREADS, 2) pf_gemm(PfParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int MT = MODE == 0 ? (p.F + 127) / 128 : (p.D + 255) / 256;
-    const int L = xcd_tile_block(blockIdx.x, MT, p.meta[0]);
+    const int L = xcd_tile_block(blockIdx.x, MT, p.meta[0], p.meta[2]);
     if (L < 0) return;
     const int ti = L / MT, mt = L % MT;
     const PfTile tile = p.tiles[ti];
@@ -1019,8 +1034,8 @@ __device__ __forceinline__ void pf_mfma_tokens(const _Float16 *stg, const half8_
 #endif
 
 // ---------------------------------------------------------------------------
-// pf_gemm_q4<FMT, MODE, BM>: pf_gemm for the 4-bit formats (q4_1, NVFP4) on
-// tiles of up to BM token rows (128: two blocks per CU; 256: one block per CU
+// pq_gemm_body<FMT, MODE, BM, FUSED>: pf_gemm for the 4-bit formats (q4_1,
+// NVFP4), run by pf_ffn_q4, on tiles of up to BM token rows (128: two blocks per CU; 256: one block per CU
 // with the accumulators of 8 token blocks, so each dequantised weight feeds
 // twice the MFMAs), with the weight fragments of 4 consecutive 32-input steps
 // copied at once (per row 64 B of codes, and the 16 B of 4 q4_1 {d, m} pairs
@@ -1059,8 +1074,49 @@ __device__ __forceinline__ WRaw<FMT> pq_frag(const uint8_t *cb, int row, int st,
 }
 #endif
 
-template <int FMT, int MODE, int BM>
-__global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+// Handover of h from the gate/up blocks of a tile to its down blocks inside
+// pf_ffn_q4.  Both run on the same XCD (see pf_ffn_q4), so h travels through
+// that XCD's L2, which needs no cache maintenance: a gate/up block waits until
+// its h stores have reached L2, then adds 1 + (its XCC id << 10) to the tile's
+// counter with an L2 atomic.  A down block's thread 0 polls the counter with
+// L1-bypassing loads for at most PF_SPIN_TICKS of the 100 MHz real-time
+// counter, then checks that every producer ran on its own XCC (the id field
+// must be target x its id).  A wait that gives up, or producers on another
+// XCC (whose L2 this block cannot see), return nonzero in every thread: the
+// block then writes NaN, so a broken handover shows as NaN outputs, never as
+// stale values or a hang.
+constexpr uint64_t PF_SPIN_TICKS = 2000000;  // 20 ms
+constexpr int PF_DONE_COUNT_BITS = 10;
+__device__ __forceinline__ int pf_xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15; }  // HW_REG_XCC_ID[3:0]
+__device__ __forceinline__ int pf_wait_tile(const int32_t *done, int target) {
+    int bad = 0;
+    if (threadIdx.x == 0) {
+        const int want_ids = target * pf_xcc_id();
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        int v;
+        while (((v = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) &
+                ((1 << PF_DONE_COUNT_BITS) - 1)) < target) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > PF_SPIN_TICKS) {
+                bad = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if ((v >> PF_DONE_COUNT_BITS) != want_ids) bad = 1;
+    }
+    return __syncthreads_or(bad);
+}
+#endif
+
+// Body of the 4-bit grouped GEMM for block `bid` of its role (MODE 0: gate/up,
+// MODE 1: down), over LDS stages that the kernel declares.  FUSED: the block
+// runs inside pf_ffn_q4, where a gate/up block counts its tile once its h
+// rows are stored and a down block waits for that count before it copies h
+// (its weight copies go out before the wait).
+template <int FMT, int MODE, int BM, bool FUSED>
+__device__ __forceinline__ void pq_gemm_body(const PfParams &p, int bid, uint4 *x0s, uint4 *x1s, uint4 *x2s,
+                                             uint4 *x3s, uint8_t *c0s, uint8_t *c1s) {
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(FMT == FMT_Q4_1 || FMT == FMT_NVFP4, "4-bit formats");
     constexpr int NBLK = BM / 32;  // 32-row token blocks of a tile
@@ -1068,19 +1124,12 @@ __global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfPa
     // copies per thread of a weight macro's first part (W1: scales + 2 code
     // copies) and second part (W2: 2 code copies)
     constexpr int W1N = FMT == FMT_Q4_1 ? 3 : 4, W2N = 2;
-    __shared__ uint4 x0s[BM * 4], x1s[BM * 4], x2s[BM * 4], x3s[BM * 4];
-    // codes: [256 rows][4 steps x 16 B], a row's step chunks XOR-swizzled by
-    // pq_swz(row) (the 8-byte fragment reads of 32 rows then spread over the
-    // banks with the least conflict measured); scales: [256 rows][4 steps x
-    // {d, m}] (q4_1) or [256 rows][4 steps x 2 E4M3] (NVFP4)
-    // (one LDS object per macro buffer: codes, then scales at PQ_SOFF)
-    __shared__ __attribute__((aligned(16))) uint8_t c0s[PQ_WBYTES], c1s[PQ_WBYTES];
 #define PQ_XST(st) ((st) == 0 ? x0s : (st) == 1 ? x1s : (st) == 2 ? x2s : x3s)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int MT = MODE == 0 ? (p.F + 127) / 128 : (p.D + 255) / 256;
-    const int L = xcd_tile_block(blockIdx.x, MT, p.meta[0]);
+    const int L = xcd_tile_block(bid, MT, p.meta[0], p.meta[2]);
     if (L < 0) return;
     const int ti = L / MT, mt = L % MT;
     const PfTile tile = p.tiles[ti];
@@ -1198,6 +1247,8 @@ __global__ void __launch_bounds__(PF_THREADS, BM == 128 ? 2 : 1) pf_gemm_q4(PfPa
 
     PQ_ISSUE_W1(0, 0);
     PQ_ISSUE_W2(0, 0);
+    int gave_up = 0;
+    if constexpr (FUSED && MODE == 1) gave_up = pf_wait_tile(p.tile_done + ti, (p.F + 127) / 128);
 #pragma unroll
     for (int s = 0; s < PF_NS - 1; s++) PQ_ISSUE_X(s, min(s, NK - 1));
     // macro 0 has landed once only the 3 token stages are pending
@@ -1260,6 +1311,14 @@ _Pragma("unroll")                                                               
 #undef PQ_ISSUE_W2
 #undef PQ_ISSUE_X
 #undef PQ_READ_SC
+    if (gave_up) {
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+#pragma unroll
+            for (int b = 0; b < NBLK; b++)
+#pragma unroll
+                for (int j = 0; j < 16; j++) acc[a][b][j] = __builtin_nanf("");
+    }
     if constexpr (BM == 128) {
         // the stages are free once every copy has landed and every wave is
         // past its last step; wave w then takes token stage w as its region
@@ -1269,9 +1328,45 @@ _Pragma("unroll")                                                               
     } else {
         pf_epilogue<MODE, NBLK>(p, tile, acc, r0, sub_ok, g, l32);
     }
+    if constexpr (FUSED && MODE == 0) {
+        // every wave's h stores have reached this XCD's L2 before the barrier;
+        // then one thread counts the tile's block with its XCC id
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_fetch_add(p.tile_done + ti, 1 + (pf_xcc_id() << PF_DONE_COUNT_BITS), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 #undef PQ_XST
+
+// pf_ffn_q4: both grouped GEMMs of a layer in one dispatch.  Blocks below
+// p.g1 are the gate/up GEMM's blocks, the rest the down GEMM's, each in the
+// block -> tile order of its own kernel; p.g1 is a multiple of 8, so the down
+// blocks of a tile run on the XCD that ran its gate/up blocks and read h
+// from that XCD's L2.  A down block waits only for the gate/up blocks of its
+// own tile, so the down GEMM fills the slots that the gate/up GEMM's last
+// blocks leave idle, without a kernel boundary between the two.  The wait
+// cannot deadlock: each XCD dispatches its blocks in order, so every gate/up
+// block is resident before any down block of its XCD, and gate/up blocks
+// never wait.
+template <int FMT>
+__global__ void __launch_bounds__(PF_THREADS, 2) pf_ffn_q4(PfParams p) {
+    // token stages: [128 rows][4 x 16 B]; weight macro buffers: codes [256
+    // rows][4 steps x 16 B], a row's step chunks XOR-swizzled by pq_swz(row)
+    // (the 8-byte fragment reads of 32 rows then spread over the banks with
+    // the least conflict measured), then scales at PQ_SOFF: [256 rows][4
+    // steps x {d, m}] (q4_1) or [256 rows][4 steps x 2 E4M3] (NVFP4).  One
+    // LDS object per stage and per macro buffer, so that the compiler's wait
+    // analysis tells a stage's copies from another stage's reads.
+    __shared__ uint4 x0s[PQ_BM * 4], x1s[PQ_BM * 4], x2s[PQ_BM * 4], x3s[PQ_BM * 4];
+    __shared__ __attribute__((aligned(16))) uint8_t c0s[PQ_WBYTES], c1s[PQ_WBYTES];
+    if ((int)blockIdx.x < p.g1)
+        pq_gemm_body<FMT, 0, PQ_BM, true>(p, blockIdx.x, x0s, x1s, x2s, x3s, c0s, c1s);
+    else
+        pq_gemm_body<FMT, 1, PQ_BM, true>(p, blockIdx.x - p.g1, x0s, x1s, x2s, x3s, c0s, c1s);
+}
 
 // ---------------------------------------------------------------------------
 // pf_router_gemm: router logits of bf16 tokens as a tiled GEMM on the matrix
@@ -1429,21 +1524,25 @@ __global__ void __launch_bounds__(PF_THREADS) pf_combine(PfParams p) {
 }
 
 // grid of the grouped GEMMs for at most tiles_max tiles of MT blocks (the
-// block -> tile order of xcd_tile_block)
-unsigned pf_gemm_grid(int tiles_max, int MT) { return (unsigned)(8 * MT * ((tiles_max + 7) / 8)); }
+// block -> tile order of xcd_tile_block: an XCD takes at most
+// ceil(full / 8) + ceil(partial / 8) <= ceil(tiles_max / 8) + 1 tiles)
+unsigned pf_gemm_grid(int tiles_max, int MT) { return (unsigned)(8 * MT * ((tiles_max + 7) / 8 + 1)); }
 
 template <int FMT>
 void launch_gemms(const PfParams &p, hipStream_t st) {
     const int mt0 = (p.F + 127) / 128, mt1 = (p.D + 255) / 256;
-    // pf_gemm_q4 copies a row's NVFP4 block scales of a macro-stage as two
+    // pf_ffn_q4 copies a row's NVFP4 block scales of a macro-stage as two
     // dwords, which must be 4-byte aligned in the matrix: K / 16 a multiple
     // of 4 for both matrices (d_model and d_ff multiples of 64); other shapes
     // take the one-step pipeline of pf_gemm
-    const bool macro = FMT == FMT_Q4_1 || (FMT == FMT_NVFP4 && p.D % 64 == 0 && p.F % 64 == 0);
+    const bool macro = prefill_fused(FMT, p.D, p.F);
     if constexpr (FMT == FMT_Q4_1 || FMT == FMT_NVFP4) {
         if (macro) {
-            MOE_LAUNCH(4, (pf_gemm_q4<FMT, 0, PQ_BM>), dim3(pf_gemm_grid(p.tiles_max, mt0)), dim3(PF_THREADS), st, p);
-            MOE_LAUNCH(5, (pf_gemm_q4<FMT, 1, PQ_BM>), dim3(pf_gemm_grid(p.tiles_max, mt1)), dim3(PF_THREADS), st, p);
+            // both GEMMs in one dispatch (pf_ffn_q4): gate/up blocks first
+            PfParams q = p;
+            q.g1 = (int)pf_gemm_grid(p.tiles_max, mt0);
+            const unsigned grid = (unsigned)q.g1 + pf_gemm_grid(p.tiles_max, mt1);
+            MOE_LAUNCH(4, pf_ffn_q4<FMT>, dim3(grid), dim3(PF_THREADS), st, q);
             return;
         }
     }
@@ -1455,7 +1554,15 @@ void launch_gemms(const PfParams &p, hipStream_t st) {
 
 }  // namespace
 
-const char *prefill_names(int act) {
+bool prefill_fused(int fmt, int D, int F) {
+    return fmt == FMT_Q4_1 || (fmt == FMT_NVFP4 && D % 64 == 0 && F % 64 == 0);
+}
+
+const char *prefill_names(int act, bool fused) {
+    // with the GEMMs fused, slot 4 is the fused kernel and slot 5 does not run
+    if (fused)
+        return act == MOE_ACT_F32 ? "pf_logits;pf_topk;pf_scan;pf_scatter;pf_ffn;pf_gemm_down;pf_combine"
+                                  : "pf_router_gemm;pf_topk;pf_scan;pf_scatter;pf_ffn;pf_gemm_down;pf_combine";
     return act == MOE_ACT_F32 ? "pf_logits;pf_topk;pf_scan;pf_scatter;pf_gemm_gateup;pf_gemm_down;pf_combine"
                               : "pf_router_gemm;pf_topk;pf_scan;pf_scatter;pf_gemm_gateup;pf_gemm_down;pf_combine";
 }
@@ -1485,6 +1592,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
     p.off = wsp<int32_t>(a.ws, L.off);
     p.tiles = wsp<PfTile>(a.ws, L.tiles);
     p.meta = wsp<int32_t>(a.ws, L.meta);
+    p.tile_done = wsp<int32_t>(a.ws, L.done);
     p.perm_tok = wsp<int32_t>(a.ws, L.perm_tok);
     p.perm_w = wsp<float>(a.ws, L.perm_w);
     p.pos = wsp<int32_t>(a.ws, L.pos);
