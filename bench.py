@@ -120,38 +120,40 @@ ATTN_SOURCES = ("moe_attn.hip", "moe_device.h", "moe_internal.h")
 # the kernel source digest it was taken on.
 _FETCH_SCALE = 262144.0 / 131083.5  # 256 MiB device copy: true KiB read / FETCH_SIZE KiB
 _WRITE_SCALE = 262144.0 / 262144.0  # same copy: true KiB written / WRITE_SIZE KiB
-# Matrix-core counters of the prefill GEMMs, per dispatch, from a rocprofv3
-# --pmc run of this script (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE,
-# SQ_INSTS_VALU_MFMA_MOPS_F16); valid only for the source digest they were
-# taken on.  The SQ counters sum over the chip's 1024 SIMDs (256 CUs x 4) and
-# GRBM_GUI_ACTIVE over its 8 XCDs, so utilisation = (busy / 1024) / (active / 8);
-# one MOP is 512 FLOPs of work issued to the matrix cores.
+# Matrix-core counters of the fused prefill GEMM kernel (gate/up and down in
+# one dispatch), per dispatch, from a rocprofv3 --pmc run of this script
+# (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_F16,
+# SQ_BUSY_CYCLES); valid only for the source digest they were taken on.  The SQ
+# counters sum over the chip's 1024 SIMDs (256 CUs x 4) and GRBM_GUI_ACTIVE over
+# its 8 XCDs, so utilisation = (busy / 1024) / (active / 8); one MOP is 512 FLOPs
+# of work issued to the matrix cores.
 PREFILL_MFMA_COUNTERS = dict(
-    source_digest="88e0bbf19d33fe84",
-    # q4_1 layer: means per dispatch over the 14 dispatches of each GEMM in one run
-    pf_gemm_gateup=dict(GRBM_GUI_ACTIVE=2423730.14, SQ_VALU_MFMA_BUSY_CYCLES=130285568.0,
-                        SQ_INSTS_VALU_MFMA_MOPS_F16=260571136.0, SQ_BUSY_CYCLES=8467651.36, duration_us=152.31),
-    pf_gemm_down=dict(GRBM_GUI_ACTIVE=1605172.0, SQ_VALU_MFMA_BUSY_CYCLES=65142784.0,
-                      SQ_INSTS_VALU_MFMA_MOPS_F16=130285568.0, SQ_BUSY_CYCLES=5491608.71, duration_us=92.01),
+    source_digest="b18198ac95672289",
+    # q4_1 layer: means per dispatch over the 4 timed dispatches of one run
+    pf_ffn=dict(GRBM_GUI_ACTIVE=3441111.75, SQ_VALU_MFMA_BUSY_CYCLES=195428352.0,
+                SQ_INSTS_VALU_MFMA_MOPS_F16=390856704.0, SQ_BUSY_CYCLES=12348378.25, duration_us=219.85),
 )
 
 
-def prefill_mfma_counters(fl_gu: float, fl_dn: float):
-    """Counter-based MFMA utilisation of the two prefill GEMMs, or None when the
-    stored counters were taken on other kernel sources."""
+def prefill_mfma_counters(flops: dict):
+    """Counter-based MFMA utilisation of the prefill GEMM kernels ({kernel:
+    algorithmic FLOPs per dispatch}), or None when the stored counters were
+    taken on other kernel sources."""
     c = PREFILL_MFMA_COUNTERS
     if c is None or c["source_digest"] != source_digest(PREFILL_SOURCES):
         return None
     out = {}
-    for k, fl in (("pf_gemm_gateup", fl_gu), ("pf_gemm_down", fl_dn)):
-        v = c[k]
+    for k, fl in flops.items():
+        v = c.get(k)
+        if v is None:
+            continue
         active = v["GRBM_GUI_ACTIVE"] / 8.0
         out[k] = dict(mfma_busy_frac=round(v["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0 / active, 4),
                       issued_flops=round(v["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512),
                       algorithmic_flops=fl, padding_overhead=round(v["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / fl - 1, 4),
                       clock_ghz=round(active / (v["duration_us"] * 1e3), 3), gui_active_cycles_per_xcd=round(active),
                       counters=v)
-    return out
+    return out or None
 
 
 def _traffic(digest: str, fetch_kib: float, write_kib: float) -> dict:
@@ -170,10 +172,9 @@ COUNTER_TRAFFIC = {
     ("stack_nvfp4_b8", "bn_gateup"): _traffic("57c1d2057ded3856", 26673.5191, 112.4278),
     ("stack_nvfp4_b8", "bn_down"): _traffic("57c1d2057ded3856", 13520.6781, 64.0),
     # 4096-token prefill, q4_1 and NVFP4
-    ("prefill_q4_1", "pf_gemm_gateup"): _traffic("88e0bbf19d33fe84", 226688.9219, 28677.2188),
-    ("prefill_q4_1", "pf_gemm_down"): _traffic("88e0bbf19d33fe84", 81872.3958, 114688.0),
-    ("prefill_nvfp4", "pf_gemm_gateup"): _traffic("88e0bbf19d33fe84", 232797.2969, 28676.1198),
-    ("prefill_nvfp4", "pf_gemm_down"): _traffic("88e0bbf19d33fe84", 75056.7448, 114688.0),
+    # (both GEMMs in one dispatch)
+    ("prefill_q4_1", "pf_ffn"): _traffic("b18198ac95672289", 219437.6, 143400.2),
+    ("prefill_nvfp4", "pf_ffn"): _traffic("b18198ac95672289", 207707.6, 143401.8),
     # q4_1 output layer, 1 token
     ("lm_head_q4_1_t1", "lm_head_kernel"): _traffic("c3b94d4e2367e0b5", 91654.112, 572.2188),
     # full-attention layer at 128k positions
@@ -559,7 +560,9 @@ def bench_prefill(args, wfmt="q4_1"):
                       flops_per_launch=fl_dom, us_per_launch=round(kus[dom], 2),
                       timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream",
                       per_kernel=per_kernel,
-                      mfma_counters=prefill_mfma_counters(fl_gu, fl_dn) if wfmt == "q4_1" else None),
+                      mfma_counters=(prefill_mfma_counters({dom: fl_dom} if fused else
+                                                           {"pf_gemm_gateup": fl_gu, "pf_gemm_down": fl_dn})
+                                     if wfmt == "q4_1" else None)),
         cpu_baseline=cpu,
     )
 

@@ -87,16 +87,17 @@ def test_prefill_mfma_counter_arithmetic(monkeypatch):
     digest = bench.source_digest(bench.PREFILL_SOURCES)
     v = dict(GRBM_GUI_ACTIVE=8 * 300_000.0, SQ_VALU_MFMA_BUSY_CYCLES=1024 * 120_000.0,
              SQ_INSTS_VALU_MFMA_MOPS_F16=250e6, duration_us=160.0)
-    monkeypatch.setattr(bench, "PREFILL_MFMA_COUNTERS",
-                        dict(source_digest=digest, pf_gemm_gateup=v, pf_gemm_down=v))
-    out = bench.prefill_mfma_counters(120e9, 60e9)
-    g = out["pf_gemm_gateup"]
+    monkeypatch.setattr(bench, "PREFILL_MFMA_COUNTERS", dict(source_digest=digest, pf_ffn=v))
+    out = bench.prefill_mfma_counters({"pf_ffn": 180e9})
+    g = out["pf_ffn"]
     assert g["mfma_busy_frac"] == pytest.approx(0.4)
     assert g["issued_flops"] == round(250e6 * 512)
+    assert g["padding_overhead"] == pytest.approx(250e6 * 512 / 180e9 - 1, abs=1e-4)
     assert g["clock_ghz"] == pytest.approx(300_000 / 160e3, abs=1e-3)
-    monkeypatch.setattr(bench, "PREFILL_MFMA_COUNTERS", dict(source_digest="stale", pf_gemm_gateup=v,
-                                                             pf_gemm_down=v))
-    assert bench.prefill_mfma_counters(120e9, 60e9) is None
+    # kernels without stored counters are left out
+    assert bench.prefill_mfma_counters({"pf_gemm_gateup": 120e9}) is None
+    monkeypatch.setattr(bench, "PREFILL_MFMA_COUNTERS", dict(source_digest="stale", pf_ffn=v))
+    assert bench.prefill_mfma_counters({"pf_ffn": 180e9}) is None
 
 
 def test_more_than_one_gpu_is_refused():
