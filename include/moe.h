@@ -255,6 +255,9 @@ moe_status moe_stack_decode_timed(const moe_dims *dims, int32_t n_layers, const 
  *   kernel_us  (host) float [7]: duration in microseconds of each kernel, in
  *              launch order (router logits, top-k, scan, scatter, gate/up
  *              GEMM, down GEMM, combine); -1 for a kernel that did not run.
+ *              q4_1 (and NVFP4 with d_model and d_ff multiples of 64) runs
+ *              both GEMMs in one kernel, named "pf_ffn" in the gate/up slot;
+ *              the down GEMM's slot then reports -1.
  *   n_kernels  (host) receives 7.
  *   names      (host, optional) receives the kernel names separated by ';'.
  * Creates and destroys 14 HIP events; not for use under stream capture.
