@@ -38,7 +38,7 @@ def parse():
                     choices=["stack_q4_1_b1", "stack_nvfp4_b1", "stack_nvfp4_b8", "prefill_q4_1", "prefill_nvfp4", "sweep_q4_1",
                              "lm_head_q4_1", "lm_head_nvfp4", "lm_head_bf16", "attn_swa", "attn_full128k"])
     ap.add_argument("--layers", type=int, default=47)
-    ap.add_argument("--decode-path", default="kernels", choices=["kernels", "persistent"],
+    ap.add_argument("--decode-path", default="kernels", choices=["kernels", "persistent", "xcd"],
                     help="batch-1 decode path: three kernels per layer, or the persistent kernel where built")
     ap.add_argument("--lm-tokens", type=int, default=1, help="tokens per output-layer call (1..8)")
     ap.add_argument("--lm-cpu-rows", type=int, default=146_484, help="vocabulary rows in the CPU baseline sample")
@@ -109,6 +109,7 @@ def source_digest(files=("moe_decode_b1.hip", "moe_decode.hip", "moe_device.h", 
 BN_SOURCES = ("moe_decode_bn.hip", "moe_device.h", "moe_internal.h")
 PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_device.h", "moe_internal.h")
 PERSIST_SOURCES = ("moe_stack_persist.hip", "moe_persist.h", "moe_device.h", "moe_internal.h")
+XCD_SOURCES = ("moe_decode_xcd.hip", "moe_xcd.h", "moe_device.h", "moe_internal.h")
 PS_LAYERS_PER_LAUNCH = 64  # layers per persistent-kernel launch (the library's limit)
 LM_HEAD_SOURCES = ("moe_lm_head.hip", "moe_device.h", "moe_internal.h")
 ATTN_SOURCES = ("moe_attn.hip", "moe_device.h", "moe_internal.h")
@@ -228,6 +229,8 @@ def time_kernels(args, stack, xs, ws, dims, T):
 def roofline(workload, dims, T, L, kernel_us, routed_union):
     if "ps_stack" in kernel_us:
         return roofline_persistent(workload, dims, L, kernel_us, routed_union)
+    if "xl_layer" in kernel_us:
+        return roofline_xcd(workload, dims, kernel_us, routed_union)
     algo = kernel_algo_bytes(dims, T, routed_union)
     dom = max(kernel_us, key=lambda k: kernel_us[k])
     us = kernel_us[dom]
@@ -274,6 +277,29 @@ def roofline_persistent(workload, dims, L, kernel_us, routed_union):
                 timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream, mean over the eager "
                        "timed calls",
                 per_kernel={k: dict(us=round(v, 3)) for k, v in kernel_us.items()})
+
+
+def roofline_xcd(workload, dims, kernel_us, routed_union):
+    """One kernel per layer (one expert per XCD): its algorithmic bytes per
+    launch are the layer's router, shared expert and routed union, the previous
+    layer's 8 partial outputs it adds and its own 8 partial outputs."""
+    from sparse_moe_decode_route_amd import inputs as gen
+    D, F, E, S = dims.d_model, dims.d_ff, dims.n_routed, dims.n_shared
+    eb = 2 * gen.matrix_bytes(F, D, dims.wfmt) + gen.matrix_bytes(D, F, dims.wfmt)
+    algo = E * D * 2 + (routed_union + S) * eb + 2 * 8 * D * 4
+    us = kernel_us["xl_layer"]
+    achieved = algo / (us * 1e-6) / 1e9
+    tr = COUNTER_TRAFFIC.get((workload, "xl_layer"))
+    traffic = None
+    if tr is not None and tr["source_digest"] == source_digest(XCD_SOURCES):
+        traffic = tr["fetch_bytes"] + tr["write_bytes"]
+    return dict(bound="hbm", kernel="xl_layer", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, algo_bytes_per_launch=round(algo),
+                us_per_launch=round(us, 3),
+                timing="HIP dispatch events (hipExtLaunchKernelGGL) on the launch stream, mean over every launch "
+                       "of the timed calls; each call's launches are enqueued behind a stream hold and then run "
+                       "back to back, as in a graph replay",
+                per_kernel={k: dict(us_per_launch=round(v, 3)) for k, v in kernel_us.items()})
 
 
 def bench_stack(args, wfmt: str, T: int):
@@ -356,7 +382,8 @@ def bench_stack(args, wfmt: str, T: int):
                     expert_bytes_per_layer=round(bytes_per_layer), router_bytes_per_layer=router_b,
                     expert_gbs=round(expert_gbs, 1), expert_frac_of_peak=round(expert_gbs / HBM_PEAK_GBS, 4),
                     step_gbs_incl_router=round(step_gbs, 1), graph_matches_eager=graph_matches_eager,
-                    step_ms_percentiles=pct, decode_path="persistent" if "ps_stack" in kernel_us else "kernels",
+                    step_ms_percentiles=pct, decode_path=("persistent" if "ps_stack" in kernel_us else
+                                 "xcd" if "xl_layer" in kernel_us else "kernels"),
                     kernel_source_digest=source_digest()),
         roofline=roofline(workload, dims, T, L, kernel_us, routed_union),
     )
@@ -927,7 +954,7 @@ def main():
     sys.path.insert(0, root)
     from sparse_moe_decode_route_amd import binding as B
     B.lib()  # fails loudly if libmoe.so is missing
-    B.set_decode_path(B.PATH_PERSISTENT if args.decode_path == "persistent" else B.PATH_KERNELS)
+    B.set_decode_path({"persistent": B.PATH_PERSISTENT, "xcd": B.PATH_XCD}.get(args.decode_path, B.PATH_KERNELS))
     if args.workload == "stack_q4_1_b1":
         out = bench_stack(args, "q4_1", 1)
     elif args.workload == "stack_nvfp4_b1":

@@ -406,15 +406,29 @@ moe_status moe_attn_decode_timed(const moe_attn_dims *dims, int32_t n_seqs, int3
  * layer (the exchanges cost more than kernel boundaries), hence not the
  * default.  Its waits are bounded: a wait that gives up ends the call with
  * NaN outputs and an error that moe_decode_check reports.
+ *   MOE_PATH_XCD         one kernel per layer where built for the shape (q4_1
+ *                        or NVFP4, d_model 2048, d_ff 512, 256 routed experts,
+ *                        top-6, one shared expert, a device of 256 CUs in 8
+ *                        XCDs), else three kernels.  Each XCD runs one active
+ *                        expert (XCD j < 6 the routed expert of rank j, which
+ *                        it selects from logits it computes itself; XCDs 6
+ *                        and 7 half of the shared expert each) and writes a
+ *                        partial output; the next layer's kernel adds the 8
+ *                        partials.  Its exchanges stay inside one XCD (its
+ *                        L2): barriers of the XCD's 32 blocks, bounded, and
+ *                        checked against the blocks' XCC ids; a barrier that
+ *                        gives up or sees another XCC ends the call with NaN
+ *                        outputs and an error that moe_decode_check reports.
  */
 #define MOE_PATH_KERNELS 0
 #define MOE_PATH_PERSISTENT 1
+#define MOE_PATH_XCD 2
 moe_status moe_set_decode_path(int32_t path);
 
 /*
  * (host) Whether the last batch-1 call that used this workspace on the
- * persistent kernel finished its waits: MOE_OK, or MOE_ERR_HIP when a wait
- * gave up (its outputs are NaN).  Copies the workspace's error word and
+ * persistent kernel (or the one-kernel-per-layer path) finished its waits:
+ * MOE_OK, or MOE_ERR_HIP when a wait gave up (its outputs are NaN).  Copies the workspace's error word and
  * synchronises `stream`.  Calls on other paths leave the word untouched.
  */
 moe_status moe_decode_check(const moe_dims *dims, int32_t n_tokens, const void *ws, size_t ws_bytes,

@@ -29,7 +29,7 @@ ENTRY_POINTS = (
     "moe_set_decode_path", "moe_decode_check", "moe_status_string", "moe_last_error",
 )
 
-PATH_KERNELS, PATH_PERSISTENT = 0, 1
+PATH_KERNELS, PATH_PERSISTENT, PATH_XCD = 0, 1, 2
 
 
 class MoeError(RuntimeError):
@@ -258,8 +258,9 @@ def layer_forward_noalloc(layer: DeviceLayer, x: torch.Tensor, y: torch.Tensor, 
 
 
 def set_decode_path(path: int):
-    """PATH_KERNELS (default: three kernels per layer) or PATH_PERSISTENT (the
-    persistent batch-1 kernel where built)."""
+    """PATH_KERNELS (default: three kernels per layer), PATH_PERSISTENT (the
+    persistent batch-1 kernel where built) or PATH_XCD (one kernel per layer,
+    one expert per XCD, where built)."""
     _check(lib().moe_set_decode_path(path))
 
 

@@ -13,6 +13,7 @@
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
+#include "moe_xcd.h"
 #include "moe_persist.h"
 #include "moe_prefill.h"
 
@@ -66,7 +67,7 @@ bool decode_tokens(const moe_dims &d, int T) {
 // Decode-path workspace (n_tokens <= 32).
 struct DecodeWs {
     size_t logits, idx, w, xbuf, xconv, meta, act_expert, act_mask, act_w, h, ybuf0, ybuf1, work, pairs, b1_list, ps,
-        total;
+        xl, total;
     int amax;
 };
 
@@ -95,6 +96,7 @@ DecodeWs decode_ws(const moe_dims &d, int T) {
     L.pairs = take((size_t)(d.n_shared * T + T * d.top_k) * 16);
     L.b1_list = take(8 * 16 * 4);
     L.ps = take(moe::PS_WS_BYTES);
+    L.xl = take(moe::xl_ws(d.d_model, d.d_ff, d.n_routed).total);
     L.total = o;
     return L;
 }
@@ -206,6 +208,7 @@ const char *const kB1Names = "b1_route;b1_topk_gateup;b1_down";
 const char *const kGenericNames = "phase_a_kernel;select_kernel;gateup_kernel;down_kernel";
 const char *const kBnNames = "bn_router;bn_gateup;bn_down";
 const char *const kPsNames = "ps_stack;ps_clear";
+const char *const kXlNames = "xl_layer;xl_reduce;xl_clear";
 
 // Process-wide choice of the batch-1 decode path (moe_set_decode_path).
 int g_decode_path = MOE_PATH_KERNELS;
@@ -214,6 +217,66 @@ int g_decode_path = MOE_PATH_KERNELS;
 bool use_persistent(const moe_dims &d, int T) {
     return T == 1 && g_decode_path == MOE_PATH_PERSISTENT &&
            moe::ps_supported(d.wfmt, d.d_model, d.d_ff, d.n_routed, d.n_shared, d.top_k);
+}
+
+// Whether batch-1 calls of this shape take one kernel per layer with one
+// expert per XCD.
+bool use_xcd(const moe_dims &d, int T) {
+    return T == 1 && g_decode_path == MOE_PATH_XCD &&
+           moe::xl_supported(d.wfmt, d.d_model, d.d_ff, d.n_routed, d.n_shared, d.top_k);
+}
+
+// The batch-1 path with one kernel per layer and one expert per XCD over
+// n_layers layers (host array), x0 fp32 [D]: a clear of the barrier counters
+// per XL_MAX_LAYERS layers, one kernel per layer (each adds the previous
+// layer's 8 partial outputs), and a final sum of the last layer's partials.
+// ev (optional): per layer MAX_KERNEL_SLOTS start/stop pairs; pair 0 times the
+// layer's kernel, pair 1 (last layer) the final sum, pair 2 a clear.
+moe_status xcd_impl(const moe_dims &d, int n_layers, const moe_layer_weights *layers, const float *x0, float *y,
+                    float *y_trace, int32_t *idx_trace, float *w_out, void *ws, const DecodeWs &L, hipStream_t st,
+                    hipEvent_t *ev) {
+    const moe::XlWs X = moe::xl_ws(d.d_model, d.d_ff, d.n_routed);
+    char *base = static_cast<char *>(ws) + L.xl;
+    float *part[2] = {reinterpret_cast<float *>(base + X.ypart0), reinterpret_cast<float *>(base + X.ypart1)};
+    int32_t *bar = reinterpret_cast<int32_t *>(base + X.bar);
+    // the error word is the persistent path's (ctrl[0]), so that
+    // moe_decode_check reports the last batch-1 call of either path
+    int32_t *err = at<int32_t>(ws, L.ps + 3 * (size_t)moe::PS_BLOCKS * moe::PS_SLOT_WORDS * 8);
+    const size_t D = (size_t)d.d_model;
+    moe::XlParams p{};
+    p.D = d.d_model;
+    p.F = d.d_ff;
+    p.E = d.n_routed;
+    p.K = d.top_k;
+    p.expert_bytes = moe_packed_expert_bytes(&d);
+    p.x0 = x0;
+    p.lg = reinterpret_cast<float *>(base + X.lg);
+    p.hb = reinterpret_cast<float *>(base + X.hb);
+    p.err = err;
+    for (int l = 0; l < n_layers; l++) {
+        hipEvent_t *lev = ev ? ev + (size_t)l * 2 * moe::MAX_KERNEL_SLOTS : nullptr;
+        if (l % moe::XL_MAX_LAYERS == 0)
+            MOE_TRY(hip_status(moe::xl_clear_launch(bar, err, l == 0, st, lev ? lev + 4 : nullptr), "clear launch"));
+        const moe_layer_weights &w = layers[l];
+        p.first = l == 0;
+        p.yin = l == 0 ? nullptr : part[(l - 1) & 1];
+        p.yout = part[l & 1];
+        p.y_prev = (l > 0 && y_trace) ? y_trace + (size_t)(l - 1) * D : nullptr;
+        p.router = static_cast<const uint16_t *>(w.router);
+        p.bias = w.router_bias;
+        p.experts = static_cast<const uint8_t *>(w.experts);
+        p.tscale = d.wfmt == MOE_W_NVFP4 ? w.tensor_scale : nullptr;
+        p.idx_out = idx_trace ? idx_trace + (size_t)l * d.top_k : nullptr;
+        p.w_out = n_layers == 1 ? w_out : nullptr;
+        p.bar = bar + (size_t)(l % moe::XL_MAX_LAYERS) * 2 * moe::XL_XCDS * moe::XL_LINE;
+        MOE_TRY(hip_status(moe::xl_layer_launch(p, d.wfmt, st, lev), "layer launch"));
+    }
+    hipEvent_t *last = ev ? ev + (size_t)(n_layers - 1) * 2 * moe::MAX_KERNEL_SLOTS + 2 : nullptr;
+    MOE_TRY(hip_status(moe::xl_reduce_launch(part[(n_layers - 1) & 1], y, d.d_model, st, last), "sum launch"));
+    if (y_trace)
+        MOE_TRY(hip_status(hipMemcpyAsync(y_trace + (size_t)(n_layers - 1) * D, y, D * 4, hipMemcpyDeviceToDevice, st),
+                           "trace copy"));
+    return ok();
 }
 
 // The persistent batch-1 path over n_layers layers (host array), x0 fp32
@@ -473,6 +536,7 @@ moe_status moe_layer_forward(const moe_dims *d, const moe_layer_weights *w, cons
     p.y = y;
     if (use_persistent(*d, n_tokens))
         return persistent_impl(*d, 1, w, p.x, y, nullptr, topk_idx_out, topk_w_out, ws, L, st, nullptr);
+    if (use_xcd(*d, n_tokens)) return xcd_impl(*d, 1, w, p.x, y, nullptr, topk_idx_out, topk_w_out, ws, L, st, nullptr);
     return hip_status(launch_any(p, st), "layer launch");
 }
 
@@ -544,6 +608,10 @@ moe_status stack_impl(const moe_dims *d, int32_t n_layers, const moe_layer_weigh
     if (use_persistent(*d, n_tokens)) {
         if (path) *path = 4;
         return persistent_impl(*d, n_layers, layers, x0, y, y_trace, idx_trace, nullptr, ws, L, st, ev);
+    }
+    if (use_xcd(*d, n_tokens)) {
+        if (path) *path = 5;
+        return xcd_impl(*d, n_layers, layers, x0, y, y_trace, idx_trace, nullptr, ws, L, st, ev);
     }
     const size_t TD = (size_t)n_tokens * d->d_model;
     const float *prev = nullptr;
@@ -638,7 +706,7 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
         if (names && names_cap) snprintf(names, names_cap, "%s", kPsNames);
         return ok();
     }
-    const int slots = path == 2 ? 4 : 3;
+    const int slots = path == 2 ? 4 : 3;  // the one-kernel-per-layer path (5): layer, final sum, clear
     for (int k = 0; k < slots; k++) {
         double tot = 0.0;
         int cnt = 0;
@@ -656,7 +724,7 @@ moe_status moe_stack_decode_timed(const moe_dims *d, int32_t n_layers, const moe
     destroy();
     *n_kernels = slots;
     if (names && names_cap) {
-        const char *src = path == 1 ? kB1Names : path == 3 ? kBnNames : kGenericNames;
+        const char *src = path == 1 ? kB1Names : path == 3 ? kBnNames : path == 5 ? kXlNames : kGenericNames;
         snprintf(names, names_cap, "%s", src);
     }
     return ok();
@@ -959,8 +1027,8 @@ moe_status moe_attn_decode_timed(const moe_attn_dims *d, int32_t n_seqs, int32_t
 }
 
 moe_status moe_set_decode_path(int32_t path) {
-    if (path != MOE_PATH_KERNELS && path != MOE_PATH_PERSISTENT)
-        return fail(MOE_ERR_INVALID_ARG, "path must be MOE_PATH_KERNELS or MOE_PATH_PERSISTENT");
+    if (path != MOE_PATH_KERNELS && path != MOE_PATH_PERSISTENT && path != MOE_PATH_XCD)
+        return fail(MOE_ERR_INVALID_ARG, "path must be MOE_PATH_KERNELS, MOE_PATH_PERSISTENT or MOE_PATH_XCD");
     g_decode_path = path;
     return ok();
 }
@@ -975,7 +1043,9 @@ moe_status moe_decode_check(const moe_dims *d, int32_t n_tokens, const void *ws,
     hipStream_t st = static_cast<hipStream_t>(stream);
     MOE_TRY(hip_status(hipMemcpyAsync(&flag, ctrl, 4, hipMemcpyDeviceToHost, st), "error word copy"));
     MOE_TRY(hip_status(hipStreamSynchronize(st), "stream synchronize"));
-    if (flag) return fail(MOE_ERR_HIP, "a wait of the persistent decode kernel gave up (outputs set to NaN)");
+    if (flag)
+        return fail(MOE_ERR_HIP, "a wait of the batch-1 decode kernels (persistent, or one kernel per layer) gave up "
+                                 "or crossed an XCD (outputs set to NaN)");
     return ok();
 }
 
