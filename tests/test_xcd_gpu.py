@@ -42,11 +42,13 @@ def xcd():
     B.set_decode_path(B.PATH_KERNELS)
 
 
-def _one(host, dl, x, label):
+def _one(host, dl, x, label, check=True):
     ws = B.workspace(host.dims, 1)
     y, idx, w = B.layer_forward(dl, x.to(_dev()), ws=ws)
     torch.cuda.synchronize()
-    B.decode_check(host.dims, 1, ws)
+    if check:
+        # the workspace's error word is written only by the paths with waits
+        B.decode_check(host.dims, 1, ws)
     y, idx, w = y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
     x64 = x.double().numpy()
     oi, ow, ol, _ = oracle.layer_forward(host, x64)
@@ -93,7 +95,7 @@ def test_xcd_unsupported_shape_falls_back(xcd):
     """64 routed experts: the path is not built for it, the call takes the
     three-kernel path and stays correct."""
     host, dl = _layer(gen.LayerDims(2048, 512, n_routed=64, n_shared=1, top_k=6, wfmt="q4_1"), 61)
-    _one(host, dl, gen.make_hidden(61, 1, 2048, draw=5), "xcd fallback e64")
+    _one(host, dl, gen.make_hidden(61, 1, 2048, draw=5), "xcd fallback e64", check=False)
 
 
 @pytest.mark.parametrize("wfmt,L", [("q4_1", 5), ("nvfp4", 66)])
