@@ -181,8 +181,9 @@ moe_status moe_layer_forward(const moe_dims *dims, const moe_layer_weights *w, c
  * until the process ends; its address is looked up on the first call on each
  * device (the current device).  The call allocates nothing.  A call whose
  * moe_workspace_size() exceeds the array returns MOE_ERR_WORKSPACE with
- * nothing enqueued (at d_model 2048, d_ff 512, 256 + 1 experts, top-6 the
- * decode path fits up to 32 tokens).  Every call on a device shares that
+ * nothing enqueued (at d_model 2048, d_ff 512, 256 + 1 experts, top-6 every
+ * call of up to 339 tokens fits: the decode paths up to 32 tokens, the
+ * grouped-GEMM path from 33 to 339).  Every call on a device shares that
  * device's array, which keeps the last call's contents: calls that overlap in
  * time on one device (different streams or threads) race and give undefined
  * results; calls ordered on one stream are safe.
