@@ -28,6 +28,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "moe_xcd.h"
@@ -230,14 +232,12 @@ __global__ void __launch_bounds__(XL_THREADS) xl_layer(XlParams p) {
     float *ydst;
     if (shared) {
         // ---- shared expert: h of its features, then its partial down rows ----
-        const int f_lo = (xcd - XL_K) * FSH;
         XUnit<FMT> xv;
         xl_x4<FMT>(xv, xs4, lane);
         float *hx = p.hb + (size_t)xcd * XL_F;
         xl_gateup<FMT, 1>(sg, su, sts_g, sts_u, xv, hx + 8 * q + wave, lane);
         bad |= xl_barrier(p.bar + (XL_XCDS + xcd) * XL_LINE, XL_BPX);
         ydst = p.yout + (size_t)xcd * XL_D + 64 * q + 8 * wave + lane / 8;
-        (void)f_lo;
         xl_down<FMT, 8, 1>(sd, sts_d, hx, bad ? __builtin_nanf("") : 1.f, ydst, lane);
     } else {
         // ---- routed XCD: 8 logits per block, all 256 through this XCD's L2 ----
@@ -337,9 +337,20 @@ hipError_t xl_launch(K kern, dim3 grid, dim3 block, hipStream_t st, hipEvent_t *
 bool xl_supported(int fmt, int D, int F, int E, int S, int K) {
     if ((fmt != FMT_Q4_1 && fmt != FMT_NVFP4) || D != XL_D || F != XL_F || E != XL_E || S != 1 || K != XL_K)
         return false;
-    int dev = 0, cus = 0, nb = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    // the device query once per (device, format): 0 unknown, 1 yes, 2 no
+    static std::atomic<int> known[64][2];
+    const int slot = fmt == FMT_Q4_1 ? 0 : 1;
+    if (dev >= 0 && dev < 64) {
+        const int k = known[dev][slot].load(std::memory_order_relaxed);
+        if (k) return k == 1;
+    }
+    int cus = 0, nb = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
         (void)hipGetLastError();
         return false;
     }
@@ -351,7 +362,9 @@ bool xl_supported(int fmt, int D, int F, int E, int S, int K) {
         return false;
     }
     // every block of the grid resident at once, 32 per XCD
-    return cus == XL_BLOCKS && nb >= 1;
+    const bool ok = cus == XL_BLOCKS && nb >= 1;
+    if (dev >= 0 && dev < 64) known[dev][slot].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok;
 }
 
 hipError_t xl_clear_launch(int32_t *bar, int32_t *err, bool clear_err, hipStream_t st, hipEvent_t *ev) {
