@@ -228,3 +228,15 @@ def test_attn_chunk_plan(L):
     c = ctypes.c_int32()
     assert L.moe_attn_chunk_plan(ctypes.byref(B.attn_dims(32, 4, 0)), 1, 8192, ctypes.byref(c), None) == INVALID
     assert L.moe_attn_chunk_plan(ctypes.byref(B.attn_dims(32, 4, 0)), 0, 8192, ctypes.byref(c), ctypes.byref(c)) == INVALID
+
+
+def test_decode_path_switch(L):
+    # the three batch-1 paths are accepted, anything else is refused (host only)
+    try:
+        for path in (B.PATH_PERSISTENT, B.PATH_XCD, B.PATH_KERNELS):
+            assert L.moe_set_decode_path(path) == OK
+        for bad in (-1, 3):
+            assert L.moe_set_decode_path(bad) == INVALID
+            assert b"MOE_PATH_XCD" in L.moe_last_error()
+    finally:
+        L.moe_set_decode_path(B.PATH_KERNELS)
