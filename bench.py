@@ -39,7 +39,8 @@ def parse():
                              "lm_head_q4_1", "lm_head_nvfp4", "lm_head_bf16", "attn_swa", "attn_full128k"])
     ap.add_argument("--layers", type=int, default=47)
     ap.add_argument("--decode-path", default="kernels", choices=["kernels", "persistent", "xcd"],
-                    help="batch-1 decode path: three kernels per layer, or the persistent kernel where built")
+                    help="batch-1 decode path: three kernels per layer, the persistent kernel, or one kernel per "
+                         "layer with one expert per XCD (the last two where built)")
     ap.add_argument("--lm-tokens", type=int, default=1, help="tokens per output-layer call (1..8)")
     ap.add_argument("--lm-cpu-rows", type=int, default=146_484, help="vocabulary rows in the CPU baseline sample")
     ap.add_argument("--lm-cpu-seconds", type=float, default=10.0, help="minimum CPU baseline time (whole passes)")
