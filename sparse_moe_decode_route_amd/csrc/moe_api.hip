@@ -250,6 +250,11 @@ moe_status xcd_impl(const moe_dims &d, int n_layers, const moe_layer_weights *la
     p.K = d.top_k;
     p.expert_bytes = moe_packed_expert_bytes(&d);
     p.x0 = x0;
+    // longest barrier wait: 20 ms of the 100 MHz real-time counter; the
+    // environment variable MOE_XCD_SPIN_TICKS lowers it so that tests can drive
+    // the give-up path with every kernel still ending normally
+    p.spin = 2000000u;
+    if (const char *e = getenv("MOE_XCD_SPIN_TICKS")) p.spin = (uint32_t)std::max(0, std::min((int)p.spin, atoi(e)));
     p.lg = reinterpret_cast<float *>(base + X.lg);
     p.hb = reinterpret_cast<float *>(base + X.hb);
     p.err = err;

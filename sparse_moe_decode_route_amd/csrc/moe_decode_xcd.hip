@@ -22,7 +22,7 @@
 // XCD-local barriers go through L2 atomics without cache maintenance.  Each
 // arrival carries the block's XCC id; a barrier whose arrivals came from
 // another XCC than the waiting block's (blocks not placed round-robin on the
-// XCDs), or that waits longer than 20 ms, sets the error word and makes the
+// XCDs), or that waits longer than its limit (20 ms), sets the error word and makes the
 // block write NaN, so a broken exchange never passes stale values or hangs.
 #include <hip/hip_fp16.h>
 #include <hip/hip_ext.h>
@@ -57,16 +57,16 @@ namespace {
 
 constexpr int XL_D = 2048, XL_F = 512, XL_E = 256, XL_K = 6;
 constexpr int XL_THREADS = MOE_WAVE * XL_WAVES;
-constexpr uint64_t XL_SPIN_TICKS = 2000000;  // 20 ms of the 100 MHz real-time counter
 constexpr int XL_ID_SHIFT = 8;               // barrier word: arrivals below, sum of XCC ids above
 
 __device__ __forceinline__ int xl_xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15; }  // HW_REG_XCC_ID
 
 // Barrier of the n blocks of one XCD on counter ctr.  Every wave's stores have
 // reached L2 before the block arrives; thread 0 then polls the counter with
-// L1-bypassing loads.  Returns nonzero (in every thread) if the wait gave up or
-// an arrival came from another XCC.
-__device__ __forceinline__ int xl_barrier(int32_t *ctr, int n) {
+// L1-bypassing loads for at most spin ticks of the 100 MHz real-time counter.
+// Returns nonzero (in every thread) if the wait gave up or an arrival came from
+// another XCC.
+__device__ __forceinline__ int xl_barrier(int32_t *ctr, int n, uint32_t spin) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int bad = 0;
@@ -77,7 +77,7 @@ __device__ __forceinline__ int xl_barrier(int32_t *ctr, int n) {
         int v;
         while (((v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & ((1 << XL_ID_SHIFT) - 1)) <
                n) {
-            if (__builtin_amdgcn_s_memrealtime() - t0 > XL_SPIN_TICKS) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > spin) {
                 bad = 1;
                 break;
             }
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(XL_THREADS) xl_layer(XlParams p) {
         xl_x4<FMT>(xv, xs4, lane);
         float *hx = p.hb + (size_t)xcd * XL_F;
         xl_gateup<FMT, 1>(sg, su, sts_g, sts_u, xv, hx + 8 * q + wave, lane);
-        bad |= xl_barrier(p.bar + (XL_XCDS + xcd) * XL_LINE, XL_BPX);
+        bad |= xl_barrier(p.bar + (XL_XCDS + xcd) * XL_LINE, XL_BPX, p.spin);
         ydst = p.yout + (size_t)xcd * XL_D + 64 * q + 8 * wave + lane / 8;
         xl_down<FMT, 8, 1>(sd, sts_d, hx, bad ? __builtin_nanf("") : 1.f, ydst, lane);
     } else {
@@ -262,7 +262,7 @@ __global__ void __launch_bounds__(XL_THREADS) xl_layer(XlParams p) {
             const int e = 8 * q + wave;
             if (lane == 0) p.lg[(size_t)xcd * XL_E + e] = p.bias ? s + p.bias[e] : s;
         }
-        bad |= xl_barrier(p.bar + xcd * XL_LINE, XL_BPX);
+        bad |= xl_barrier(p.bar + xcd * XL_LINE, XL_BPX, p.spin);
         // ---- top-k in every wave; this XCD's expert is rank xcd ----
         float lv[4];
         wave_topk_load(p.lg + (size_t)xcd * XL_E, XL_E, lv);
@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(XL_THREADS) xl_layer(XlParams p) {
         __builtin_amdgcn_sched_barrier(0);
         float *hx = p.hb + (size_t)xcd * XL_F;
         xl_gateup<FMT, 2>(wg, wu, mg.ts, mu.ts, xv, hx + f0, lane);
-        bad |= xl_barrier(p.bar + (XL_XCDS + xcd) * XL_LINE, XL_BPX);
+        bad |= xl_barrier(p.bar + (XL_XCDS + xcd) * XL_LINE, XL_BPX, p.spin);
         ydst = p.yout + (size_t)xcd * XL_D + r0;
         xl_down<FMT, 16, 2>(wd, md.ts, hx, bad ? __builtin_nanf("") : coef, ydst, lane);
     }

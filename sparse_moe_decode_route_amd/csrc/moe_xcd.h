@@ -23,6 +23,7 @@ XlWs xl_ws(int D, int F, int E);
 struct XlParams {
     int D, F, E, K;
     int first;             // 1: the layer's input is x0; 0: the previous layer's partials
+    uint32_t spin;         // longest barrier wait, in ticks of the 100 MHz real-time counter
     size_t expert_bytes;
     const float *x0;       // [D] (first layer)
     const float *yin;      // [8][D] partial outputs of the previous layer (else)

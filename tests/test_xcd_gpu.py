@@ -157,3 +157,34 @@ def test_xcd_stack_graph_replays_match_eager(xcd):
         torch.cuda.synchronize()
         assert torch.equal(got, ref), i
         B.decode_check(dims, 1, ws)
+
+
+def test_xcd_give_up_path_sets_error_and_nan(xcd):
+    """A barrier limit of 0 ticks makes every XCD barrier that is not complete
+    at its first poll give up: the call must end (no hang) with NaN outputs and
+    an error from moe_decode_check; the next call with the normal limit is
+    correct."""
+    import os
+    dims = gen.LayerDims(2048, 512, wfmt="q4_1")
+    host, dl = _layer(dims, 2)
+    x = gen.make_hidden(2, 1, 2048, draw=400).to(_dev())
+    ws = B.workspace(dims, 1)
+    os.environ["MOE_XCD_SPIN_TICKS"] = "0"
+    try:
+        y, _, _ = B.layer_forward(dl, x, ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["MOE_XCD_SPIN_TICKS"]
+    try:
+        B.decode_check(dims, 1, ws)
+        gave_up = False
+    except B.MoeError as e:
+        gave_up = True
+        assert "gave up" in str(e)
+    if gave_up:
+        assert torch.isnan(y).any()
+    y2, _, _ = B.layer_forward(dl, x, ws=ws)
+    torch.cuda.synchronize()
+    B.decode_check(dims, 1, ws)
+    assert not torch.isnan(y2).any()
+    print(f"[xcd give-up] first call gave up: {gave_up}")
