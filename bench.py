@@ -303,6 +303,48 @@ def roofline_xcd(workload, dims, kernel_us, routed_union):
                 per_kernel={k: dict(us_per_launch=round(v, 3)) for k, v in kernel_us.items()})
 
 
+def single_layer_times(args, dev, xs, ws, T, n_calls=47):
+    """One layer (the stack's first) called n_calls times back to back in one HIP
+    graph, each call on its own (not chained), per-call mean over the replays:
+    with a fresh token per call (the routed experts mostly come from HBM: the
+    layer's 506 MB exceed the 256 MB Infinity Cache), and warm, with the same
+    token on every call (no flush: its 7 experts' 13.8 MB and the router stay
+    on chip after the first call)."""
+    from sparse_moe_decode_route_amd import binding as B
+    one = B.StackHandle([dev])
+    y_static = torch.empty((T, 2048), device="cuda")
+    out = {}
+    for name, fresh in (("fresh_token_us", True), ("warm_same_token_us", False)):
+        xin = [xs[i if fresh else 0].contiguous() for i in range(n_calls)]
+
+        def calls():
+            for x in xin:
+                B.stack_decode(one, x, ws=ws, y=y_static)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            calls()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) * 1e3 / (reps * n_calls), 3)
+    out["timing"] = (f"{n_calls} calls of one layer (not chained) in one HIP graph, per-call mean over 20 "
+                     "replays")
+    return out
+
+
 def bench_stack(args, wfmt: str, T: int):
     from sparse_moe_decode_route_amd import binding as B
     from sparse_moe_decode_route_amd import inputs as gen
@@ -363,6 +405,8 @@ def bench_stack(args, wfmt: str, T: int):
     torch.cuda.synchronize()
     graph_matches_eager = bool(torch.equal(y_eager, y_static))
 
+    single = single_layer_times(args, devs[0], xs, ws, T) if T == 1 else None
+
     router_b = dims.n_routed * dims.d_model * 2
     algo_bytes_step = L * (bytes_per_layer + router_b)
     step_gbs = algo_bytes_step / (ms * 1e-3) / 1e9
@@ -383,7 +427,8 @@ def bench_stack(args, wfmt: str, T: int):
                     expert_bytes_per_layer=round(bytes_per_layer), router_bytes_per_layer=router_b,
                     expert_gbs=round(expert_gbs, 1), expert_frac_of_peak=round(expert_gbs / HBM_PEAK_GBS, 4),
                     step_gbs_incl_router=round(step_gbs, 1), graph_matches_eager=graph_matches_eager,
-                    step_ms_percentiles=pct, decode_path=("persistent" if "ps_stack" in kernel_us else
+                    step_ms_percentiles=pct, single_layer=single,
+                    decode_path=("persistent" if "ps_stack" in kernel_us else
                                  "xcd" if "xl_layer" in kernel_us else "kernels"),
                     kernel_source_digest=source_digest()),
         roofline=roofline(workload, dims, T, L, kernel_us, routed_union),
