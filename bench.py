@@ -315,7 +315,7 @@ def single_layer_times(args, dev, xs, ws, T, n_calls=47):
     y_static = torch.empty((T, 2048), device="cuda")
     out = {}
     for name, fresh in (("fresh_token_us", True), ("warm_same_token_us", False)):
-        xin = [xs[i if fresh else 0].contiguous() for i in range(n_calls)]
+        xin = [xs[i % xs.shape[0] if fresh else 0].contiguous() for i in range(n_calls)]
 
         def calls():
             for x in xin:
